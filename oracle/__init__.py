@@ -1,0 +1,192 @@
+"""CPU oracle for one rank's fused GEMV + one-shot AllReduce.
+
+TEST INFRASTRUCTURE.  Only the tests, the package smoke check and the
+benchmark's CPU-baseline leg may import this package.  It shares no code with
+the HIP library (`gemv_shot_all_amd`) and never imports it.
+
+The arithmetic lives in `gsa_oracle.c` (plain C, fp64); this module loads it
+with ctypes and adds numpy-facing wrappers plus a model of the signal-pad
+protocol state.  Sources followed (restated, not quoted):
+
+* fused GEMV + AllReduce operator -- "Overlapping Collective Communication
+  with Dependent Computation ... GPU-Initiated Intra-Kernel Networking"
+  (summary of "Optimizing Distributed ML Communication with Fused
+  Computation-Collective Operations"), Abstract;
+* row-parallel shard and one all-reduce at the end -- "Bay.Area.AI: Tensor and
+  2D Parallelism", Megatron MLP segment;
+* zero-initialised accumulator, every rank's buffer in rank order --
+  "PyTorch Symmetric Memory" documentation, writing-your-own-kernel section
+  (Triton one_shot_all_reduce_kernel);
+* fp32 accumulation of bf16 inputs -- same documentation, higher-precision
+  reduction section;
+* signal pad next to every symmetric allocation, sized by launched blocks
+  times world size, indexed by block -- same documentation, the
+  writing-your-own-kernel section and the set_signal_pad_size and
+  multimem_all_reduce_ entries of the API and op reference.
+
+Pins: every function here is checked against something other than itself in
+tests/test_oracle_pins.py (numpy fp64 matmul on tiny shapes, closed forms,
+hand-computed fp32 folds, shard-sum identity); tests/test_oracle_mutants.py
+plants mistakes in a copy of the C source and checks that a pin fails.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+# Protocol reading (the pages leave the granularity open): one flag per rank
+# per tile of 16 output rows (all batch columns), so a rank's row of the pad
+# holds ceil(N / 16) flags.  A simulated peer that has "published for every
+# call" holds the all-ones word.
+FLAG_TILE_ROWS = 16
+FLAG_PUBLISHED = 0xFFFFFFFF
+
+# The error bound every fp32 GPU result must meet against the fp64 value:
+# |err| <= 1e-5 * sum_k |A[n,k] x[b,k]| + 1e-6.
+BOUND_REL = 1e-5
+BOUND_ABS = 1e-6
+
+
+def _ptr(arr, ptype):
+    return arr.ctypes.data_as(ptype)
+
+
+class Oracle:
+    """ctypes view of one build of the oracle library."""
+
+    def __init__(self, path):
+        self.path = path
+        lib = ctypes.CDLL(path)
+        lib.gsa_oracle_gemv.argtypes = [_u16p, _u16p, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_int, _f64p, _f64p]
+        lib.gsa_oracle_gemv.restype = ctypes.c_int
+        lib.gsa_oracle_gemv_allreduce.argtypes = [
+            _u16p, _u16p, _f32p, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int, _f64p, _f64p, _f64p]
+        lib.gsa_oracle_gemv_allreduce.restype = ctypes.c_int
+        lib.gsa_oracle_fold_f32.argtypes = [_f32p, ctypes.c_int, ctypes.c_int64, _f32p]
+        lib.gsa_oracle_fold_f32.restype = None
+        self._lib = lib
+
+    def gemv(self, A, x):
+        """fp64 y[n, b] = sum_k A[n, k] x[b, k] and sum_k |A[n, k] x[b, k]|.
+
+        A: uint16 bf16 bits, N x Ks; x: uint16 bf16 bits, B x Ks.
+        """
+        A = np.ascontiguousarray(A, dtype=np.uint16)
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        N, Ks = A.shape
+        B, Ks2 = x.shape
+        if Ks2 != Ks:
+            raise ValueError("A and x disagree on the reduction length")
+        y = np.empty((N, B), np.float64)
+        a = np.empty((N, B), np.float64)
+        rc = self._lib.gsa_oracle_gemv(_ptr(A, _u16p), _ptr(x, _u16p), N, Ks, B,
+                                       _ptr(y, _f64p), _ptr(a, _f64p))
+        if rc != 0:
+            raise ValueError("oracle rejected the sizes")
+        return y, a
+
+    def gemv_allreduce(self, A, x, slots, rank):
+        """One rank's call: (y64, abs64, out64), each N x B float64.
+
+        slots: float32 W x N x B; row `rank` is ignored (the call publishes it).
+        """
+        A = np.ascontiguousarray(A, dtype=np.uint16)
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        slots = np.ascontiguousarray(slots, dtype=np.float32)
+        N, Ks = A.shape
+        B = x.shape[0]
+        W = slots.shape[0]
+        if x.shape[1] != Ks or slots.shape[1:] != (N, B):
+            raise ValueError("shape mismatch")
+        y = np.empty((N, B), np.float64)
+        a = np.empty((N, B), np.float64)
+        out = np.empty((N, B), np.float64)
+        rc = self._lib.gsa_oracle_gemv_allreduce(
+            _ptr(A, _u16p), _ptr(x, _u16p), _ptr(slots, _f32p), W, rank, N, Ks, B,
+            _ptr(y, _f64p), _ptr(a, _f64p), _ptr(out, _f64p))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return y, a, out
+
+    def fold_f32(self, slots):
+        """fp32 one-shot sum of the given slots in rank order from +0.0f."""
+        slots = np.ascontiguousarray(slots, dtype=np.float32)
+        W = slots.shape[0]
+        rest = slots.shape[1:]
+        nb = int(np.prod(rest)) if rest else 1
+        out = np.empty(rest, np.float32)
+        self._lib.gsa_oracle_fold_f32(_ptr(slots, _f32p), W, nb, _ptr(out, _f32p))
+        return out
+
+
+def bound(abs64):
+    """Allowed |fp32 result - fp64 value| for each element."""
+    return BOUND_REL * np.asarray(abs64, np.float64) + BOUND_ABS
+
+
+def flag_tiles(N):
+    """Number of flag tiles for N output rows."""
+    return (int(N) + FLAG_TILE_ROWS - 1) // FLAG_TILE_ROWS
+
+
+def pad_after_reset(W, N, published_mask):
+    """Logical W x T flag state right after a reset: published rows hold the
+    all-ones word, every other row holds 0."""
+    T = flag_tiles(N)
+    flags = np.zeros((W, T), np.uint32)
+    for p in range(W):
+        if (published_mask >> p) & 1:
+            flags[p, :] = FLAG_PUBLISHED
+    return flags
+
+
+def pad_after_calls(flags, rank, calls):
+    """State after `calls` calls by `rank` that each completed: a call whose
+    own flag read f publishes f + 1 (the call's epoch) on every tile of its
+    own row; peer rows are only read."""
+    flags = np.array(flags, np.uint32, copy=True)
+    flags[rank, :] = flags[rank, :] + np.uint32(calls)
+    return flags
+
+
+def expected_timeouts(flags_before, rank):
+    """Which (tile, peer) waits of one call cannot be satisfied, given the pad
+    before the call.  Epoch e_t = own flag + 1; the wait on peer p for tile t
+    needs flags[p][t] >= e_t.  Returns (timed_out_tiles, first) where first is
+    the lexicographically smallest (tile, peer) pair, or None."""
+    flags_before = np.asarray(flags_before, np.uint64)
+    W, T = flags_before.shape
+    epoch = flags_before[rank] + 1
+    tiles = []
+    first = None
+    for t in range(T):
+        missing = [p for p in range(W) if p != rank and flags_before[p, t] < epoch[t]]
+        if missing:
+            tiles.append(t)
+            if first is None:
+                first = (t, missing[0])
+    return tiles, first
+
+
+_default = None
+
+
+def load(path=None):
+    """Load the oracle library (building it first if it is not built)."""
+    global _default
+    if path is not None:
+        return Oracle(path)
+    if _default is None:
+        if not os.path.exists(_build.LIBRARY) or (
+                os.path.getmtime(_build.LIBRARY) < os.path.getmtime(_build.SOURCE)):
+            _build.build()
+        _default = Oracle(_build.LIBRARY)
+    return _default

@@ -1,0 +1,121 @@
+/*
+ * gsa_oracle.c -- CPU oracle for one rank's fused GEMV + one-shot AllReduce.
+ *
+ * TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT PATH.  Only the test suite, the
+ * package smoke check and the benchmark's CPU-baseline leg load this library.
+ * It shares no source, header, constant or helper with the HIP library; the
+ * two meet only at the seeded inputs.
+ *
+ * Plain, slow and meant to be checked by eye: fp64 accumulation, ascending
+ * loop order, no blocking, no threads, no vector tricks.
+ *
+ * What it computes (the sources it follows):
+ *  - "Overlapping Collective Communication with Dependent Computation ...
+ *    using GPU-Initiated Intra-Kernel Networking" (summary of Punniyamurthy
+ *    et al., "Optimizing Distributed ML Communication with Fused
+ *    Computation-Collective Operations"), Abstract: the fused GEMV + AllReduce
+ *    operator for Transformers.  One rank computes its partial product and the
+ *    partials of all ranks are summed.
+ *  - "Bay.Area.AI: Tensor and 2D Parallelism" talk, Megatron-style MLP
+ *    segment: a column-wise shard followed by a row-wise shard needs no
+ *    collective in between and one all-reduce at the end.  So rank r holds
+ *    the input-dimension slice A_r (N x K/W) of the weight and the matching
+ *    slice x_r of the activation, and its partial is y_r = A_r x_r.
+ *  - "PyTorch Symmetric Memory" documentation, section on writing your own
+ *    kernel (the Triton one_shot_all_reduce_kernel): the accumulator starts
+ *    at zero and the loop visits every rank's buffer in rank order 0..W-1,
+ *    the local one included.  The "PyTorch Symmetric Memory" talk says the
+ *    same (inner loop over all ranks, local or remote alike).
+ *  - "PyTorch Symmetric Memory" documentation, section on higher-precision
+ *    reduction: bf16 inputs are accumulated in fp32.  The oracle goes further
+ *    and accumulates in fp64, so it is the exact value up to fp64 rounding.
+ *
+ * Layouts (plain readings, the pages fix none): A_r is N x Ks row-major,
+ * x is B x Ks row-major (one token's activation slice is contiguous),
+ * slots are W x N x B with element (n, b) of rank r at r*N*B + n*B + b,
+ * outputs are N x B.  bf16 values arrive as their 16 raw bits.
+ */
+#include <stdint.h>
+#include <string.h>
+#include <math.h>
+
+/* A bf16 value is the upper half of an fp32 word: widening is exact. */
+static double bf16_bits_to_double(uint16_t bits)
+{
+    uint32_t word = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &word, sizeof f);
+    return (double)f;
+}
+
+/*
+ * y64[n*B+b]   = sum_k A_r[n][k] * x[b][k]          (fp64, ascending k)
+ * abs64[n*B+b] = sum_k |A_r[n][k] * x[b][k]|        (for the error bound)
+ * Returns 0, or -1 on a bad size.
+ */
+int gsa_oracle_gemv(const uint16_t *A_r, const uint16_t *x,
+                    int64_t N, int64_t Ks, int B,
+                    double *y64, double *abs64)
+{
+    if (N < 0 || Ks < 0 || B < 1)
+        return -1;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int b = 0; b < B; ++b) {
+            double sum = 0.0;
+            double sum_abs = 0.0;
+            for (int64_t k = 0; k < Ks; ++k) {
+                double a = bf16_bits_to_double(A_r[n * Ks + k]);
+                double v = bf16_bits_to_double(x[(int64_t)b * Ks + k]);
+                double p = a * v;
+                sum += p;
+                sum_abs += fabs(p);
+            }
+            y64[n * B + b] = sum;
+            abs64[n * B + b] = sum_abs;
+        }
+    }
+    return 0;
+}
+
+/*
+ * The whole call of rank `rank`: its partial y_r, then the one-shot sum
+ *   out64[i] = sum_{r=0..W-1} (r == rank ? y64[i] : slots[r][i])
+ * in ascending r, starting from 0.  Slot `rank` of the input is ignored: it
+ * is what the call itself publishes.
+ */
+int gsa_oracle_gemv_allreduce(const uint16_t *A_r, const uint16_t *x,
+                              const float *slots, int W, int rank,
+                              int64_t N, int64_t Ks, int B,
+                              double *y64, double *abs64, double *out64)
+{
+    if (W < 1 || rank < 0 || rank >= W)
+        return -1;
+    if (gsa_oracle_gemv(A_r, x, N, Ks, B, y64, abs64) != 0)
+        return -1;
+    int64_t NB = N * (int64_t)B;
+    for (int64_t i = 0; i < NB; ++i) {
+        double acc = 0.0;
+        for (int r = 0; r < W; ++r) {
+            double term = (r == rank) ? y64[i] : (double)slots[(int64_t)r * NB + i];
+            acc += term;
+        }
+        out64[i] = acc;
+    }
+    return 0;
+}
+
+/*
+ * The one-shot sum as fp32 arithmetic over given slots, in the pages' order:
+ *   acc = +0.0f; for r = 0..W-1: acc = fl32(acc + slots[r][i]); out[i] = acc
+ * Given the fp32 partials a GPU published, this result is unique, so it is
+ * the bit-exact reference for the reduction step.
+ */
+void gsa_oracle_fold_f32(const float *slots, int W, int64_t NB, float *out)
+{
+    for (int64_t i = 0; i < NB; ++i) {
+        float acc = 0.0f;
+        for (int r = 0; r < W; ++r)
+            acc = acc + slots[(int64_t)r * NB + i];
+        out[i] = acc;
+    }
+}

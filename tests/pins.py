@@ -1,0 +1,228 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each pin takes an `oracle.Oracle` and raises AssertionError on a mismatch.
+They are collected by test_oracle_pins.py (against the real oracle) and by
+test_oracle_mutants.py (against copies with planted mistakes, each of which
+must fail at least one pin).
+
+What pins what:
+  brute_force      GEMV, abs-sum and one-shot sum vs numpy fp64 matmul and
+                   numpy sums on tiny shapes (textbook routine, other order)
+  single_rank      W = 1: out equals the unsharded product
+  shard_sum        sum over shards of y_r equals the full product
+  identity         A = I gives y = x exactly
+  one_hot          x = e_j gives y = A[:, j] exactly
+  small_integers   integer-valued A, x: exact integer results (int64 matmul)
+  rank_order_exact own term is y, slot[rank] is ignored, peers enter once
+  bf16_decode      raw bits to value, incl. denormal and max finite
+  golden           hand-worked example in tests/golden/ (values by hand)
+  fold_*           fp32 fold: order, +0 start and fp32 rounding, by hand
+"""
+import json
+import os
+
+import numpy as np
+
+import gsa_inputs as gi
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _f64(bits):
+    return gi.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _close(a, b, rel, scale, what):
+    err = np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64))
+    lim = rel * np.asarray(scale, np.float64) + 1e-300
+    bad = ~(err <= lim)
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements off, max err {err.max():.3e}"
+
+
+def pin_brute_force(o):
+    rng = np.random.default_rng(1234)
+    for (N, Ks, B, W) in [(8, 8, 1, 1), (17, 24, 2, 2), (33, 40, 3, 3),
+                          (64, 64, 16, 8), (40, 56, 2, 8), (9, 16, 3, 2)]:
+        for rank in sorted({0, W - 1, W // 2}):
+            A = gi.bf16_bits(rng.normal(0, 0.5, (N, Ks)).astype(np.float32))
+            x = gi.bf16_bits(rng.normal(0, 1.0, (B, Ks)).astype(np.float32))
+            slots = rng.normal(0, 1, (W, N, B)).astype(np.float32)
+            slots[rank] = np.nan
+            y, a, out = o.gemv_allreduce(A, x, slots, rank)
+            Af, xf = _f64(A), _f64(x)
+            ref = Af @ xf.T
+            ref_abs = np.abs(Af) @ np.abs(xf).T
+            _close(y, ref, 1e-13, ref_abs, "y vs numpy")
+            _close(a, ref_abs, 1e-13, ref_abs, "abs vs numpy")
+            peers = [slots[r].astype(np.float64) for r in range(W) if r != rank]
+            ref_out = ref + (np.sum(peers, axis=0) if peers else 0.0)
+            scale = ref_abs + sum(np.abs(p) for p in peers) if peers else ref_abs
+            _close(out, ref_out, 1e-13, scale, "out vs numpy")
+
+
+def pin_single_rank(o):
+    rng = np.random.default_rng(7)
+    N, K, B = 24, 48, 3
+    A = gi.bf16_bits(rng.normal(0, 0.1, (N, K)).astype(np.float32))
+    x = gi.bf16_bits(rng.normal(0, 1, (B, K)).astype(np.float32))
+    slots = np.full((1, N, B), np.nan, np.float32)
+    y, a, out = o.gemv_allreduce(A, x, slots, 0)
+    assert np.array_equal(out, y), "W=1: out must equal y"
+    ref = _f64(A) @ _f64(x).T
+    _close(out, ref, 1e-13, np.abs(_f64(A)) @ np.abs(_f64(x)).T, "W=1 vs unsharded")
+
+
+def pin_shard_sum(o):
+    A, x = gi.make_full_inputs(32, 96, 2, sigma=0.3, seed=5)
+    ref = _f64(A) @ _f64(x).T
+    scale = np.abs(_f64(A)) @ np.abs(_f64(x)).T
+    for W in (2, 3, 4, 8):
+        total = np.zeros_like(ref)
+        for r in range(W):
+            Ar, xr = gi.shard(A, x, W, r)
+            y, _ = o.gemv(Ar, xr)
+            total += y
+        _close(total, ref, 1e-13, scale, f"shard sum W={W}")
+
+
+def pin_identity(o):
+    Ks = 24
+    one = gi.bf16_bits(np.array([1.0], np.float32))[0]
+    A = np.zeros((Ks, Ks), np.uint16)
+    A[np.arange(Ks), np.arange(Ks)] = one
+    rng = np.random.default_rng(3)
+    x = gi.bf16_bits(rng.normal(0, 1, (3, Ks)).astype(np.float32))
+    y, _ = o.gemv(A, x)
+    assert np.array_equal(y, _f64(x).T), "identity: y must equal x"
+
+
+def pin_one_hot(o):
+    rng = np.random.default_rng(4)
+    N, Ks, B = 20, 32, 4
+    A = gi.bf16_bits(rng.normal(0, 1, (N, Ks)).astype(np.float32))
+    one = gi.bf16_bits(np.array([1.0], np.float32))[0]
+    cols = [0, 5, 17, Ks - 1]
+    x = np.zeros((B, Ks), np.uint16)
+    for b, j in enumerate(cols):
+        x[b, j] = one
+    y, _ = o.gemv(A, x)
+    for b, j in enumerate(cols):
+        assert np.array_equal(y[:, b], _f64(A)[:, j]), f"one-hot column {j}"
+
+
+def pin_small_integers(o):
+    rng = np.random.default_rng(5)
+    N, Ks, B = 13, 40, 3
+    Ai = rng.integers(-4, 5, (N, Ks))
+    xi = rng.integers(-4, 5, (B, Ks))
+    A = gi.bf16_bits(Ai.astype(np.float32))
+    x = gi.bf16_bits(xi.astype(np.float32))
+    y, a = o.gemv(A, x)
+    assert np.array_equal(y, (Ai @ xi.T).astype(np.float64)), "integer products"
+    assert np.array_equal(a, (np.abs(Ai) @ np.abs(xi).T).astype(np.float64)), "integer abs"
+
+
+def pin_rank_order_exact(o):
+    # Integer-valued peers: every sum is exact, so only the choice of terms
+    # matters: y for the own rank, each peer slot once, slot[rank] ignored.
+    N, Ks, B, W = 4, 8, 2, 4
+    Ai = np.arange(N * Ks).reshape(N, Ks) % 5 - 2
+    xi = np.arange(B * Ks).reshape(B, Ks) % 3 - 1
+    A = gi.bf16_bits(Ai.astype(np.float32))
+    x = gi.bf16_bits(xi.astype(np.float32))
+    yi = Ai @ xi.T
+    for rank in range(W):
+        slots = np.empty((W, N, B), np.float32)
+        for r in range(W):
+            slots[r] = 1000.0 * (r + 1) + np.arange(N * B).reshape(N, B)
+        slots[rank] = np.nan
+        _, _, out = o.gemv_allreduce(A, x, slots, rank)
+        ref = yi.astype(np.float64)
+        for r in range(W):
+            if r != rank:
+                ref = ref + slots[r].astype(np.float64)
+        assert np.array_equal(out, ref), f"rank {rank}: wrong set of terms"
+
+
+def pin_bf16_decode(o):
+    cases = {0x3F80: 1.0, 0xC040: -3.0, 0x0080: 2.0 ** -126,
+             0x0001: 2.0 ** -133, 0x7F7F: float(np.float32(3.3895313892515355e38)),
+             0x8000: -0.0, 0x4049: 3.140625}
+    bits = np.array(list(cases.keys()), np.uint16)[:, None]
+    one = gi.bf16_bits(np.array([[1.0]], np.float32))
+    y, a = o.gemv(bits, one)
+    assert np.array_equal(y[:, 0], np.array(list(cases.values()))), f"decode {y[:, 0]}"
+
+
+def pin_golden(o):
+    with open(os.path.join(GOLDEN, "hand_worked_w2.json")) as f:
+        g = json.load(f)
+    A = gi.bf16_bits(np.array(g["A"], np.float32))
+    x = gi.bf16_bits(np.array(g["x"], np.float32))
+    slots = np.array(g["slots"], np.float32)
+    y, a, out = o.gemv_allreduce(A, x, slots, g["rank"])
+    assert np.array_equal(y, np.array(g["y"], np.float64)), "golden y"
+    assert np.array_equal(a, np.array(g["abs"], np.float64)), "golden abs"
+    assert np.array_equal(out, np.array(g["out"], np.float64)), "golden out"
+
+
+def _fold_bits(o, cols):
+    """Fold columns given as lists of float32 values (one per rank)."""
+    W = len(cols[0])
+    slots = np.array(cols, np.float32).T.reshape(W, len(cols)).copy()
+    return o.fold_f32(slots)
+
+
+def pin_fold_order(o):
+    big = float(2 ** 24)
+    # ((0 + 2^24) + 1) + 1 = 2^24 in fp32 (each +1 is a tie, kept even);
+    # the reverse order would give 2^24 + 2.
+    # ((0 + 1) + 2^24) - 2^24 = 0 (2^24 + 1 rounds to 2^24); reverse gives 1.
+    out = _fold_bits(o, [[big, 1.0, 1.0], [1.0, big, -big]])
+    assert out[0] == np.float32(big) and out[1] == np.float32(0.0), f"fold order {out}"
+
+
+def pin_fold_zero_start(o):
+    # The sum starts from +0.0: (+0) + (-0) = +0 in round-to-nearest.
+    out = _fold_bits(o, [[-0.0], [-0.0]])
+    assert not np.signbit(out).any(), "fold must start from +0.0"
+    out2 = _fold_bits(o, [[-0.0, -0.0, -0.0]])
+    assert not np.signbit(out2[0]), "fold must start from +0.0 (W=3)"
+
+
+def pin_fold_fp32(o):
+    # 1 + 2^-24 is a tie in fp32 and rounds to 1; fp64 would keep it.
+    # 1 + 3*2^-24 rounds up to 1 + 2^-22 (nearest).
+    out = _fold_bits(o, [[1.0, 2.0 ** -24], [1.0, 3 * 2.0 ** -24]])
+    assert out[0] == np.float32(1.0), f"fp32 tie: {out[0]!r}"
+    assert out[1] == np.float32(1.0 + 2.0 ** -22), f"fp32 rounding: {out[1]!r}"
+
+
+def pin_fold_matches_sequence(o):
+    # Random case, checked element-wise against numpy float32 scalar adds in
+    # rank order (numpy's float32 add is IEEE round-to-nearest).
+    rng = np.random.default_rng(11)
+    W, NB = 8, 257
+    slots = (rng.normal(0, 1, (W, NB)) * rng.choice([1e-3, 1, 1e3], (W, NB))).astype(np.float32)
+    out = o.fold_f32(slots)
+    for i in range(NB):
+        acc = np.float32(0.0)
+        for r in range(W):
+            acc = np.float32(acc + slots[r, i])
+        assert out[i].view(np.uint32) == acc.view(np.uint32), f"fold element {i}"
+
+
+PINS = [pin_brute_force, pin_single_rank, pin_shard_sum, pin_identity, pin_one_hot,
+        pin_small_integers, pin_rank_order_exact, pin_bf16_decode, pin_golden,
+        pin_fold_order, pin_fold_zero_start, pin_fold_fp32, pin_fold_matches_sequence]
+
+
+def failing_pins(o):
+    """Names of the pins that fail (or crash) for oracle build `o`."""
+    bad = []
+    for pin in PINS:
+        try:
+            pin(o)
+        except Exception as e:  # noqa: BLE001 - any failure counts
+            bad.append((pin.__name__, repr(e)[:200]))
+    return bad

@@ -1,0 +1,57 @@
+"""Plant plausible mistakes in a copy of the oracle's C source and check that
+at least one pin catches each of them.  Runs on the CPU only (gcc)."""
+import os
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+from tests import pins
+
+MUTANTS = {
+    "x_transposed": ("x[(int64_t)b * Ks + k]", "x[k * B + b]"),
+    "A_transposed": ("A_r[n * Ks + k]", "A_r[k * N + n]"),
+    "dropped_last_k": ("for (int64_t k = 0; k < Ks; ++k)", "for (int64_t k = 0; k < Ks - 1; ++k)"),
+    "wrong_sign": ("sum += p;", "sum -= p;"),
+    "abs_dropped": ("sum_abs += fabs(p);", "sum_abs += p;"),
+    "own_term_from_slot": ("(r == rank) ? y64[i] :", "(r == r + 1) ? y64[i] :"),
+    "own_term_dropped": ("(r == rank) ? y64[i] :", "(r == rank) ? 0.0 :"),
+    "peer_stride": ("? y64[i] : (double)slots[(int64_t)r * NB + i]",
+                    "? y64[i] : (double)slots[(int64_t)r * N + i]"),
+    "fold_stride": ("acc = acc + slots[(int64_t)r * NB + i]", "acc = acc + slots[(int64_t)r * W + i]"),
+    "y_index": ("y64[n * B + b] = sum;", "y64[(int64_t)b * N + n] = sum;"),
+    "bf16_shift": ("(uint32_t)bits << 16", "(uint32_t)bits << 15"),
+    "fold_reversed": ("for (int r = 0; r < W; ++r)\n            acc = acc + slots",
+                      "for (int r = W - 1; r >= 0; --r)\n            acc = acc + slots"),
+    "fold_starts_at_slot0": ("float acc = 0.0f;\n        for (int r = 0; r < W; ++r)",
+                             "float acc = slots[i];\n        for (int r = 1; r < W; ++r)"),
+    "fold_in_double": ("float acc = 0.0f;", "double acc = 0.0;"),
+    "out_skips_first_rank": ("for (int r = 0; r < W; ++r) {\n            double term",
+                             "for (int r = 1; r < W; ++r) {\n            double term"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(obuild.SOURCE) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, source, tmp_path):
+    old, new = MUTANTS[name]
+    assert source.count(old) == 1, f"mutation site for {name} not unique/found"
+    src = tmp_path / f"mutant_{name}.c"
+    src.write_text(source.replace(old, new))
+    lib = obuild.build(str(src), str(tmp_path / f"libmutant_{name}.so"),
+                       extra_flags=["-Wno-error"])
+    failed = pins.failing_pins(oracle.load(lib))
+    assert failed, f"no pin catches mutant {name}"
+
+
+def test_unmutated_copy_passes(source, tmp_path):
+    src = tmp_path / "copy.c"
+    src.write_text(source)
+    lib = obuild.build(str(src), str(tmp_path / "libcopy.so"))
+    assert pins.failing_pins(oracle.load(lib)) == []
+    assert os.path.exists(lib)
