@@ -1,0 +1,228 @@
+"""ctypes binding of libgsa.  Argument marshalling only: every step of the
+operation runs in the library's HIP kernels.  Names mirror include/gsa.h."""
+import ctypes
+import os
+
+LIBRARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgsa.so")
+
+# Values of include/gsa.h (tests check that these agree with the header).
+GSA_OK = 0
+GSA_EINVAL = -1
+GSA_ENOMEM = -2
+GSA_EHIP = -3
+GSA_ETIMEOUT = -4
+GSA_ESTATE = -5
+GSA_FLAG_PUBLISHED = 0xFFFFFFFF
+GSA_FLAG_TILE_ROWS = 16
+GSA_PAD_HEADER_WORDS = 16
+GSA_MAX_W = 8
+GSA_MAX_B = 16
+GSA_MAX_X_LDS_BYTES = 128 * 1024
+
+EXPORTS = ("gsa_symm_alloc", "gsa_symm_free", "gsa_symm_slots", "gsa_symm_signal_pad",
+           "gsa_signal_pad_row_stride", "gsa_signal_pad_reset", "gsa_gemv_allreduce",
+           "gsa_signal_pad_status", "gsa_set_wait_timeout_us", "gsa_strerror")
+
+
+class GsaError(RuntimeError):
+    """A GSA_E* code returned by the library."""
+
+    def __init__(self, code, what):
+        self.code = code
+        super().__init__(f"{what}: {_strerror(code)} ({code})")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library.  Raises if it has not been built: there is no
+    fallback implementation."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            raise ImportError(
+                f"{LIBRARY} is missing; build it with gemv_shot_all_amd.build.build() "
+                "(or __graft_entry__.build())")
+        L = ctypes.CDLL(LIBRARY)
+        vp, i64, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32
+        ci = ctypes.c_int
+        L.gsa_symm_alloc.argtypes = [ci, i64, ci, ctypes.POINTER(vp)]
+        L.gsa_symm_alloc.restype = ci
+        L.gsa_symm_free.argtypes = [vp]
+        L.gsa_symm_free.restype = ci
+        L.gsa_symm_slots.argtypes = [vp]
+        L.gsa_symm_slots.restype = vp
+        L.gsa_symm_signal_pad.argtypes = [vp]
+        L.gsa_symm_signal_pad.restype = vp
+        L.gsa_signal_pad_row_stride.argtypes = [i64]
+        L.gsa_signal_pad_row_stride.restype = i64
+        L.gsa_signal_pad_reset.argtypes = [vp, ci, i64, u32, vp]
+        L.gsa_signal_pad_reset.restype = ci
+        L.gsa_gemv_allreduce.argtypes = [vp, vp, vp, vp, vp, ci, ci, i64, i64, ci, vp]
+        L.gsa_gemv_allreduce.restype = ci
+        L.gsa_signal_pad_status.argtypes = [vp, vp, ctypes.POINTER(ci),
+                                            ctypes.POINTER(i64), ctypes.POINTER(ci)]
+        L.gsa_signal_pad_status.restype = ci
+        L.gsa_set_wait_timeout_us.argtypes = [u32]
+        L.gsa_set_wait_timeout_us.restype = ci
+        L.gsa_strerror.argtypes = [ci]
+        L.gsa_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _strerror(code):
+    try:
+        return lib().gsa_strerror(code).decode()
+    except ImportError:
+        return "library not loaded"
+
+
+def _check(rc, what):
+    if rc != GSA_OK:
+        raise GsaError(rc, what)
+
+
+def _ptr(t):
+    """Device address of a torch tensor (must be contiguous) or a raw int."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    """hipStream_t of `stream`: None means torch's current stream."""
+    if isinstance(stream, int):
+        return stream
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def gsa_symm_alloc(W, N, B):
+    h = ctypes.c_void_p()
+    _check(lib().gsa_symm_alloc(W, N, B, ctypes.byref(h)), "gsa_symm_alloc")
+    return h.value
+
+
+def gsa_symm_free(h):
+    _check(lib().gsa_symm_free(h), "gsa_symm_free")
+
+
+def gsa_symm_slots(h):
+    p = lib().gsa_symm_slots(h)
+    if not p:
+        raise GsaError(GSA_EINVAL, "gsa_symm_slots")
+    return p
+
+
+def gsa_symm_signal_pad(h):
+    p = lib().gsa_symm_signal_pad(h)
+    if not p:
+        raise GsaError(GSA_EINVAL, "gsa_symm_signal_pad")
+    return p
+
+
+def gsa_signal_pad_row_stride(N):
+    return lib().gsa_signal_pad_row_stride(N)
+
+
+def gsa_signal_pad_reset(pad, W, N, published_mask, stream=None):
+    _check(lib().gsa_signal_pad_reset(_ptr(pad), W, N, published_mask, _stream(stream)),
+           "gsa_signal_pad_reset")
+
+
+def gsa_gemv_allreduce(A_r, x, slots, pad, out, W, rank, N, K, B, stream=None):
+    _check(lib().gsa_gemv_allreduce(_ptr(A_r), _ptr(x), _ptr(slots), _ptr(pad), _ptr(out),
+                                    W, rank, N, K, B, _stream(stream)),
+           "gsa_gemv_allreduce")
+
+
+def gsa_signal_pad_status(pad, stream=None):
+    code, tile, peer = ctypes.c_int(), ctypes.c_int64(), ctypes.c_int()
+    _check(lib().gsa_signal_pad_status(_ptr(pad), _stream(stream), ctypes.byref(code),
+                                       ctypes.byref(tile), ctypes.byref(peer)),
+           "gsa_signal_pad_status")
+    return code.value, tile.value, peer.value
+
+
+def gsa_set_wait_timeout_us(us):
+    _check(lib().gsa_set_wait_timeout_us(us), "gsa_set_wait_timeout_us")
+
+
+def gsa_strerror(code):
+    return lib().gsa_strerror(code).decode()
+
+
+class _DeviceArray:
+    """Minimal __cuda_array_interface__ exporter for library-owned memory."""
+
+    def __init__(self, ptr, shape, typestr):
+        self.__cuda_array_interface__ = {
+            "shape": tuple(int(s) for s in shape), "typestr": typestr,
+            "data": (int(ptr), False), "version": 2, "strides": None}
+
+
+def device_view(ptr, shape, dtype):
+    """A torch tensor aliasing device memory at `ptr` (no copy, no ownership).
+    Used to fill and read the library-owned slots and signal pad."""
+    import numpy as np
+    import torch
+    typestr = {torch.float32: "<f4", torch.int32: "<i4", torch.uint8: "|u1",
+               torch.int64: "<i8"}[dtype]
+    del np
+    return torch.as_tensor(_DeviceArray(ptr, shape, typestr), device="cuda")
+
+
+class SymmBuffer:
+    """One symmetric buffer (W slots of N x B fp32 + signal pad), freed on
+    close().  Convenience wrapper over gsa_symm_alloc / gsa_symm_free."""
+
+    def __init__(self, W, N, B):
+        self.W, self.N, self.B = W, N, B
+        self.handle = gsa_symm_alloc(W, N, B)
+        self.slots = gsa_symm_slots(self.handle)
+        self.pad = gsa_symm_signal_pad(self.handle)
+        self.row_stride = gsa_signal_pad_row_stride(N)
+        self.tiles = (N + GSA_FLAG_TILE_ROWS - 1) // GSA_FLAG_TILE_ROWS
+
+    def slots_view(self):
+        """torch float32 view (W, N, B) of the slots."""
+        import torch
+        return device_view(self.slots, (self.W, self.N, self.B), torch.float32)
+
+    def pad_view(self):
+        """torch int32 view of the whole signal pad (header + W rows)."""
+        import torch
+        return device_view(self.pad, (GSA_PAD_HEADER_WORDS + self.W * self.row_stride,),
+                           torch.int32)
+
+    def flags(self):
+        """Host copy (numpy uint32, W x T) of the logical flag array."""
+        import numpy as np
+        raw = self.pad_view().cpu().numpy().view(np.uint32)
+        rows = raw[GSA_PAD_HEADER_WORDS:].reshape(self.W, self.row_stride)
+        return rows[:, :self.tiles].copy()
+
+    def reset(self, published_mask, stream=None):
+        gsa_signal_pad_reset(self.pad, self.W, self.N, published_mask, stream)
+
+    def status(self, stream=None):
+        return gsa_signal_pad_status(self.pad, stream)
+
+    def close(self):
+        if self.handle:
+            gsa_symm_free(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()

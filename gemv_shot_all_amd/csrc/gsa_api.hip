@@ -1,0 +1,270 @@
+// gsa_api.hip -- host side of libgsa: the C ABI declared in include/gsa.h.
+//
+// Symmetric buffer = W fp32 slots + signal pad in one device allocation, made
+// once at init (the PyTorch Symmetric Memory docs, API reference of empty():
+// a host-synchronous allocation meant for initialization, reused afterwards;
+// the writing-your-own-kernel section: a signal pad accompanies every
+// symmetric allocation).  A registry of live buffers lets every call check
+// that the slots/pad pointers belong together and match (W, N, B) in O(1),
+// like the constant-time is_symm_mem_tensor() check of the same API.
+
+#include <atomic>
+#include <mutex>
+#include <unordered_map>
+#include <unordered_set>
+
+#include "gsa_internal.h"
+
+struct gsa_symm {
+  int W;
+  int64_t N;
+  int B;
+  int64_t row_stride;
+  int64_t tiles;
+  size_t bytes;
+  void* base;
+  float* slots;
+  uint32_t* pad;
+  int device;
+};
+
+namespace {
+
+std::mutex g_mu;
+std::unordered_map<uintptr_t, gsa_symm*> g_by_slots;  // slots -> handle
+std::unordered_map<uintptr_t, gsa_symm*> g_by_pad;    // pad -> handle
+std::unordered_set<const void*> g_big_lds_ready;      // kernels opted in to > 64 KB LDS
+std::atomic<uint32_t> g_timeout_us{100000};
+std::unordered_map<int, uint64_t> g_clock_khz;        // device -> wall clock rate
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+int64_t tiles_of(int64_t N) { return (N + GSA_FLAG_TILE_ROWS - 1) / GSA_FLAG_TILE_ROWS; }
+
+gsa_symm* find_by_slots(const void* slots) {
+  auto it = g_by_slots.find((uintptr_t)slots);
+  return it == g_by_slots.end() ? nullptr : it->second;
+}
+gsa_symm* find_by_pad(const void* pad) {
+  auto it = g_by_pad.find((uintptr_t)pad);
+  return it == g_by_pad.end() ? nullptr : it->second;
+}
+
+// Live handles by address: a handle is never dereferenced before it is found
+// here, so a stale or foreign pointer yields GSA_EINVAL, not a fault.
+std::unordered_set<const gsa_symm*> g_handles;
+
+bool known(const gsa_symm* h) { return h && g_handles.count(h) != 0; }
+
+// Wall-clock ticks for `us` microseconds on the current device.
+int ticks_for(uint32_t us, uint64_t* ticks) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GSA_EHIP;
+  uint64_t khz;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_clock_khz.find(dev);
+    if (it != g_clock_khz.end()) {
+      khz = it->second;
+    } else {
+      int rate = 0;
+      if (hipDeviceGetAttribute(&rate, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+          rate <= 0)
+        return GSA_EHIP;
+      khz = (uint64_t)rate;
+      g_clock_khz[dev] = khz;
+    }
+  }
+  *ticks = (uint64_t)us * khz / 1000u + 1u;
+  return GSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t gsa_signal_pad_row_stride(int64_t N) {
+  if (N < 1) return -1;
+  return (int64_t)round_up((size_t)tiles_of(N), 64);
+}
+
+int gsa_symm_alloc(int W, int64_t N, int B, gsa_symm** out) {
+  if (!out || W < 1 || W > GSA_MAX_W || N < 1 || B < 1 || B > GSA_MAX_B) return GSA_EINVAL;
+  if (N > ((int64_t)1 << 40)) return GSA_EINVAL;
+  *out = nullptr;
+  const int64_t stride = gsa_signal_pad_row_stride(N);
+  const size_t slot_bytes = round_up((size_t)W * (size_t)N * (size_t)B * sizeof(float), kAlign);
+  const size_t pad_words = GSA_PAD_HEADER_WORDS + (size_t)W * (size_t)stride;
+  const size_t bytes = slot_bytes + round_up(pad_words * sizeof(uint32_t), kAlign);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GSA_EHIP;
+  void* base = nullptr;
+  if (hipMalloc(&base, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return GSA_ENOMEM;
+  }
+  uint32_t* pad = reinterpret_cast<uint32_t*>(static_cast<char*>(base) + slot_bytes);
+  uint32_t hdr[GSA_PAD_HEADER_WORDS] = {0};
+  hdr[gsa::kHdrTimeoutKey] = 0xFFFFFFFFu;
+  hdr[gsa::kHdrStateTile] = 0xFFFFFFFFu;
+  if (hipMemset(base, 0, bytes) != hipSuccess ||
+      hipMemcpy(pad, hdr, sizeof hdr, hipMemcpyHostToDevice) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(base);
+    return GSA_EHIP;
+  }
+  gsa_symm* h = new gsa_symm{W, N, B, stride, tiles_of(N), bytes, base,
+                             static_cast<float*>(base), pad, dev};
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_by_slots[(uintptr_t)h->slots] = h;
+  g_by_pad[(uintptr_t)h->pad] = h;
+  g_handles.insert(h);
+  *out = h;
+  return GSA_OK;
+}
+
+int gsa_symm_free(gsa_symm* h) {
+  if (!h) return GSA_OK;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!known(h)) return GSA_EINVAL;
+    g_by_slots.erase((uintptr_t)h->slots);
+    g_by_pad.erase((uintptr_t)h->pad);
+    g_handles.erase(h);
+  }
+  int prev = 0;
+  hipError_t e = hipGetDevice(&prev);
+  if (e == hipSuccess && prev != h->device) e = hipSetDevice(h->device);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipFree(h->base);
+  if (prev != h->device) (void)hipSetDevice(prev);
+  delete h;
+  return e == hipSuccess ? GSA_OK : GSA_EHIP;
+}
+
+float* gsa_symm_slots(const gsa_symm* h) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  return known(h) ? h->slots : nullptr;
+}
+
+uint32_t* gsa_symm_signal_pad(const gsa_symm* h) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  return known(h) ? h->pad : nullptr;
+}
+
+int gsa_signal_pad_reset(uint32_t* pad, int W, int64_t N, uint32_t published_mask,
+                         void* stream) {
+  if (!pad || W < 1 || W > GSA_MAX_W || N < 1) return GSA_EINVAL;
+  if (published_mask >> W) return GSA_EINVAL;
+  int64_t stride, tiles;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    gsa_symm* h = find_by_pad(pad);
+    if (!h || h->W != W || h->N != N) return GSA_EINVAL;
+    stride = h->row_stride;
+    tiles = h->tiles;
+  }
+  hipError_t e = gsa::launch_pad_reset(pad, W, (int)stride, (int)tiles, published_mask,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GSA_OK : GSA_EHIP;
+}
+
+int gsa_gemv_allreduce(const uint16_t* A_r, const uint16_t* x, float* slots, uint32_t* pad,
+                       float* out, int W, int rank, int64_t N, int64_t K, int B, void* stream) {
+  // Scalars first: these checks touch no HIP state.
+  if (W < 1 || W > GSA_MAX_W || rank < 0 || rank >= W) return GSA_EINVAL;
+  if (N < 1 || B < 1 || B > GSA_MAX_B || K < 1 || K % W != 0) return GSA_EINVAL;
+  const int64_t Ks = K / W;
+  if (Ks % 8 != 0 || Ks / 8 > (1 << 20)) return GSA_EINVAL;
+  if (tiles_of(N) > 0x7FFFFFFF / 8) return GSA_EINVAL;
+  if (!A_r || !x || !slots || !pad || !out) return GSA_EINVAL;
+  if (!aligned16(A_r) || !aligned16(x) || !aligned16(slots) || !aligned16(pad) ||
+      !aligned16(out))
+    return GSA_EINVAL;
+  const int C = (int)(Ks / 8);
+  gsa::Launch l;
+  if (!gsa::select_gemv_kernel(W, B, C, &l)) return GSA_EINVAL;
+
+  gsa::GemvArgs a;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    gsa_symm* h = find_by_slots(slots);
+    if (!h || h->pad != pad || h->W != W || h->N != N || h->B != B) return GSA_EINVAL;
+    a.row_stride = (int)h->row_stride;
+    a.tiles = (int)h->tiles;
+    if (l.lds_bytes > 65536 && !g_big_lds_ready.count(l.kernel)) {
+      // Opt in once to the largest dynamic LDS any shape of this kernel may use.
+      if (hipFuncSetAttribute(l.kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              GSA_MAX_X_LDS_BYTES + 16384) != hipSuccess) {
+        (void)hipGetLastError();
+      }
+      g_big_lds_ready.insert(l.kernel);
+    }
+  }
+  a.A = A_r;
+  a.x = x;
+  a.slots = slots;
+  a.pad = pad;
+  a.out = out;
+  a.N = N;
+  a.C = C;
+  a.B = B;
+  a.W = W;
+  a.rank = rank;
+  int rc = ticks_for(g_timeout_us.load(std::memory_order_relaxed), &a.timeout_ticks);
+  if (rc != GSA_OK) return rc;
+  hipError_t e = gsa::launch_gemv(l, a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return GSA_EHIP;
+  }
+  return GSA_OK;
+}
+
+int gsa_signal_pad_status(const uint32_t* pad, void* stream, int* code, int64_t* tile,
+                          int* peer) {
+  if (!pad || !code || !tile || !peer) return GSA_EINVAL;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!find_by_pad(pad)) return GSA_EINVAL;
+  }
+  uint32_t hdr[GSA_PAD_HEADER_WORDS];
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(hdr, pad, sizeof hdr, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return GSA_EHIP;
+  const uint32_t bits = hdr[gsa::kHdrErrorBits];
+  *code = (bits & gsa::kErrState) ? GSA_ESTATE : (bits & gsa::kErrTimeout) ? GSA_ETIMEOUT : GSA_OK;
+  const uint32_t key = hdr[gsa::kHdrTimeoutKey];
+  *tile = -1;
+  *peer = -1;
+  if (bits & gsa::kErrState) {
+    *tile = (int64_t)hdr[gsa::kHdrStateTile];
+  } else if (key != 0xFFFFFFFFu) {
+    *tile = (int64_t)(key / 8u);
+    *peer = (int)(key % 8u);
+  }
+  return GSA_OK;
+}
+
+int gsa_set_wait_timeout_us(uint32_t us) {
+  if (us == 0) return GSA_EINVAL;
+  g_timeout_us.store(us, std::memory_order_relaxed);
+  return GSA_OK;
+}
+
+const char* gsa_strerror(int code) {
+  switch (code) {
+    case GSA_OK: return "ok";
+    case GSA_EINVAL: return "invalid argument";
+    case GSA_ENOMEM: return "device allocation failed";
+    case GSA_EHIP: return "HIP runtime error";
+    case GSA_ETIMEOUT: return "signal-pad wait timed out";
+    case GSA_ESTATE: return "own flag row not usable (marked published or epochs exhausted)";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

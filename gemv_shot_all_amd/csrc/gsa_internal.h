@@ -1,0 +1,54 @@
+// gsa_internal.h -- declarations shared by the host side and the kernels of
+// libgsa.  Not part of the public ABI (that is include/gsa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gsa.h"
+
+namespace gsa {
+
+// Status words at the head of the signal pad.
+enum : int {
+  kHdrErrorBits = 0,   // atomicOr: kErrTimeout | kErrState
+  kHdrTimeoutKey = 1,  // atomicMin of tile * 8 + peer, 0xFFFFFFFF = none
+  kHdrStateTile = 2,   // atomicMin of the tile with a bad own flag row
+};
+enum : uint32_t { kErrTimeout = 1u, kErrState = 2u };
+
+// Everything one launch needs.  Built on the host per call, passed by value.
+struct GemvArgs {
+  const uint16_t* A;      // N x Ks bf16 bits
+  const uint16_t* x;      // B x Ks bf16 bits
+  float* slots;           // W x N x B fp32
+  uint32_t* pad;          // header + W flag rows
+  float* out;             // N x B fp32
+  int64_t N;
+  int C;                  // 16-byte chunks per row = Ks / 8
+  int B;
+  int W;
+  int rank;
+  int row_stride;         // words between flag rows
+  int tiles;              // ceil(N / 16)
+  uint64_t timeout_ticks; // device wall-clock ticks a wait may take
+};
+
+// A ready-to-launch kernel choice for one (B, C) shape.
+struct Launch {
+  const void* kernel;
+  unsigned block;         // threads per workgroup
+  size_t lds_bytes;       // dynamic LDS
+};
+
+// Pick the kernel for W ranks, batch B (1..16) and C chunks per row.  Returns
+// false if the shape exceeds the LDS staging bound.
+bool select_gemv_kernel(int W, int B, int C, Launch* out);
+// Dynamic LDS bytes the kernel chosen for (W, B, C) needs.
+size_t gemv_lds_bytes(int W, int B, int C);
+
+hipError_t launch_gemv(const Launch& l, const GemvArgs& a, hipStream_t s);
+hipError_t launch_pad_reset(uint32_t* pad, int W, int row_stride, int tiles,
+                            uint32_t published_mask, hipStream_t s);
+
+}  // namespace gsa

@@ -1,0 +1,144 @@
+/*
+ * gsa.h -- C ABI of libgsa: one rank's fused GEMV + one-shot AllReduce over
+ * a symmetric buffer, on one MI355X (gfx950).
+ *
+ * The operation (restated from the sources):
+ *   - "Overlapping Collective Communication with Dependent Computation ...
+ *     GPU-Initiated Intra-Kernel Networking" (summary of "Optimizing
+ *     Distributed ML Communication with Fused Computation-Collective
+ *     Operations"), Abstract: a GEMV fused with its AllReduce in one kernel;
+ *     each workgroup hands its finished share to the collective at once, and
+ *     scale-up results are written straight into peer memory.
+ *   - "Bay.Area.AI: Tensor and 2D Parallelism", Megatron MLP segment: the
+ *     row-parallel layer leaves a partial sum on every rank and one
+ *     all-reduce finishes it.  Rank r holds A_r, the input-dimension slice
+ *     (N x K/W) of the weight, and x_r, the matching activation slice.
+ *   - "PyTorch Symmetric Memory" documentation, writing-your-own-kernel
+ *     section: buffers of every rank are visible to the kernel, a signal pad
+ *     comes with every symmetric allocation, and the one-shot all-reduce sums
+ *     the buffers of ranks 0..W-1 in order from a zero accumulator.
+ *
+ * One call of gsa_gemv_allreduce on rank `rank`:
+ *   1. y_r[n][b] = sum_k A_r[n][k] x_r[b][k]   (bf16 in, fp32 accumulate)
+ *   2. slot[rank][n][b] = y_r[n][b]            (publish)
+ *   3. flag[rank][t] = e_t                     (release, per tile t)
+ *   4. wait flag[p][t] >= e_t for every p      (acquire, per tile, bounded)
+ *   5. out[n][b] = ((0 + s_0) + s_1) ... + s_{W-1}, s_r = slot[r][n][b],
+ *      fp32 round-to-nearest, s_rank being the value published in step 2.
+ * On one GPU the W-1 peer slots are ordinary device memory filled by the
+ * caller, and simulated peers are marked "published" in the signal pad.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked [device] are device addresses on the current HIP
+ *     device; [host] are host addresses.  Sizes are element counts.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Return value: GSA_OK or a negative GSA_E* code; no exceptions escape.
+ *   - Nothing here allocates on the call path except gsa_symm_alloc.
+ */
+#ifndef GSA_H
+#define GSA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GSA_OK        0
+#define GSA_EINVAL   (-1)  /* bad argument; nothing was launched            */
+#define GSA_ENOMEM   (-2)  /* device allocation failed                      */
+#define GSA_EHIP     (-3)  /* a HIP runtime call or a launch failed         */
+#define GSA_ETIMEOUT (-4)  /* a device-side flag wait expired (asynchronous) */
+#define GSA_ESTATE   (-5)  /* the caller's own flag row was marked published
+                              for every call, or its epoch is exhausted
+                              (asynchronous)                               */
+
+/* Flag value of a simulated peer: "published for every epoch". */
+#define GSA_FLAG_PUBLISHED 0xFFFFFFFFu
+/* Signal-pad protocol: one flag per rank per tile of 16 output rows (all
+ * batch columns).  T = ceil(N / 16) tiles. */
+#define GSA_FLAG_TILE_ROWS 16
+/* The pad starts with GSA_PAD_HEADER_WORDS status words, then W rows of
+ * flags, row r at word GSA_PAD_HEADER_WORDS + r * gsa_signal_pad_row_stride(N). */
+#define GSA_PAD_HEADER_WORDS 16
+#define GSA_MAX_W 8
+#define GSA_MAX_B 16
+/* Bytes of x staged in LDS per workgroup (B*K/W*2, with B rounded up to 16
+ * when B > 8 and one 16-byte pad per batch row) may not exceed this. */
+#define GSA_MAX_X_LDS_BYTES (128 * 1024)
+
+typedef struct gsa_symm gsa_symm; /* opaque host-side handle */
+
+/* Allocate one symmetric buffer: W fp32 slots of N x B (n-major) followed by
+ * the signal pad, as one device allocation on the current device, zeroed,
+ * every flag 0.  Host-blocking; meant for init time, not the call path (the
+ * PyTorch Symmetric Memory docs, API reference of empty(): allocate once and
+ * reuse).  1 <= W <= GSA_MAX_W, N >= 1, 1 <= B <= GSA_MAX_B.
+ * *out [host] receives the handle.  Errors: GSA_EINVAL, GSA_ENOMEM, GSA_EHIP. */
+int gsa_symm_alloc(int W, int64_t N, int B, gsa_symm **out);
+
+/* Free a handle and its device memory (host-blocking: synchronizes the
+ * device first).  NULL is a no-op.  Errors: GSA_EINVAL (unknown handle). */
+int gsa_symm_free(gsa_symm *h);
+
+/* [device] slot 0 of the buffer; slot r starts r*N*B floats later.  NULL for
+ * an unknown handle.  The library owns this memory. */
+float *gsa_symm_slots(const gsa_symm *h);
+
+/* [device] signal pad of the buffer (header + flags).  NULL if unknown. */
+uint32_t *gsa_symm_signal_pad(const gsa_symm *h);
+
+/* Words between consecutive rank rows of the pad for N rows (>= ceil(N/16),
+ * a multiple of 64).  Returns -1 for N < 1. */
+int64_t gsa_signal_pad_row_stride(int64_t N);
+
+/* Reset a pad: flag row p := GSA_FLAG_PUBLISHED if bit p of published_mask
+ * is set, else 0; status words cleared.  Stream-ordered (a small kernel), no
+ * host sync, no allocation.  `pad` [device] must come from
+ * gsa_symm_signal_pad of a buffer allocated with the same W and N.  The
+ * calling rank's bit must be clear before it calls gsa_gemv_allreduce.
+ * Errors: GSA_EINVAL, GSA_EHIP. */
+int gsa_signal_pad_reset(uint32_t *pad, int W, int64_t N, uint32_t published_mask,
+                         void *stream);
+
+/* One fused call on rank `rank` (steps 1-5 above), enqueued on `stream`.
+ *   A_r   [device] bf16 bits, N x Ks row-major (Ks = K/W, leading dim Ks)
+ *   x     [device] bf16 bits, this rank's activation slice, B x Ks row-major
+ *   slots [device] gsa_symm_slots of a buffer allocated with (W, N, B)
+ *   pad   [device] gsa_symm_signal_pad of the same buffer
+ *   out   [device] fp32 N x B (n-major); any device memory, written only
+ * Requires 1 <= W <= 8, 0 <= rank < W, K % W == 0, Ks % 8 == 0, N >= 1,
+ * 1 <= B <= 16, every pointer non-null and 16-byte aligned, and the x staging
+ * bound GSA_MAX_X_LDS_BYTES; otherwise GSA_EINVAL and nothing is launched.
+ * No host sync, no allocation.  All calls on one buffer must use one stream
+ * (flags are indexed by tile, not by stream).  Each tile's flag epoch is its
+ * own previous flag + 1, so at most 2^32 - 2 calls fit between resets.
+ * Device-side failures (a wait that exceeded the timeout, a bad own flag row)
+ * leave that tile's `out` rows unwritten and are reported by
+ * gsa_signal_pad_status.  Errors: GSA_EINVAL, GSA_EHIP (launch failed). */
+int gsa_gemv_allreduce(const uint16_t *A_r, const uint16_t *x, float *slots,
+                       uint32_t *pad, float *out, int W, int rank, int64_t N,
+                       int64_t K, int B, void *stream);
+
+/* Read the pad's status words after the work queued on `stream` has finished
+ * (synchronizes `stream`).  *code [host] := GSA_ESTATE if any call found its
+ * own flag row unusable (then *tile := the smallest such tile, *peer := -1),
+ * else GSA_ETIMEOUT if any wait expired (then *tile, *peer := the smallest
+ * (tile, peer) pair whose wait expired), else GSA_OK (*tile = *peer = -1).
+ * Words stay set until the next gsa_signal_pad_reset.
+ * Errors: GSA_EINVAL (unknown pad), GSA_EHIP. */
+int gsa_signal_pad_status(const uint32_t *pad, void *stream, int *code,
+                          int64_t *tile, int *peer);
+
+/* Device-side wait bound for later calls, in microseconds (default 100000).
+ * 0 is rejected with GSA_EINVAL. */
+int gsa_set_wait_timeout_us(uint32_t us);
+
+/* Static text for a GSA_* code. */
+const char *gsa_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSA_H */

@@ -1,0 +1,105 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point the
+header declares, agrees with the header's constants, and rejects bad
+arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gemv_shot_all_amd as gsa
+from gemv_shot_all_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gsa.h")
+
+
+def header_text():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", header_text(), flags=re.S)
+    return sorted(set(re.findall(r"\b(gsa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 10
+    L = ctypes.CDLL(_lib.LIBRARY)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in gsa.h but not exported"
+    assert sorted(_lib.EXPORTS) == names
+
+
+def test_constants_match_header():
+    text = header_text()
+    for name in ["GSA_OK", "GSA_EINVAL", "GSA_ENOMEM", "GSA_EHIP", "GSA_ETIMEOUT",
+                 "GSA_ESTATE", "GSA_FLAG_TILE_ROWS", "GSA_PAD_HEADER_WORDS", "GSA_MAX_W",
+                 "GSA_MAX_B"]:
+        m = re.search(rf"#define\s+{name}\s+\(?\s*(-?\d+)\s*\)?", text)
+        assert m, name
+        assert int(m.group(1)) == getattr(_lib, name), name
+    m = re.search(r"#define\s+GSA_FLAG_PUBLISHED\s+(0x[0-9A-Fa-f]+)u", text)
+    assert int(m.group(1), 16) == _lib.GSA_FLAG_PUBLISHED
+    m = re.search(r"#define\s+GSA_MAX_X_LDS_BYTES\s+\((\d+)\s*\*\s*(\d+)\)", text)
+    assert int(m.group(1)) * int(m.group(2)) == _lib.GSA_MAX_X_LDS_BYTES
+
+
+def test_strerror_covers_codes():
+    for code in (0, -1, -2, -3, -4, -5):
+        assert gsa.gsa_strerror(code) != "unknown error"
+    assert gsa.gsa_strerror(7) == "unknown error"
+
+
+def test_row_stride():
+    assert gsa.gsa_signal_pad_row_stride(0) == -1
+    assert gsa.gsa_signal_pad_row_stride(1) == 64
+    assert gsa.gsa_signal_pad_row_stride(1024) == 64
+    assert gsa.gsa_signal_pad_row_stride(1025) == 128
+    assert gsa.gsa_signal_pad_row_stride(8192) == 512
+
+
+P = 0x10000  # a 16-byte-aligned fake address: never dereferenced, rejected first
+
+
+@pytest.mark.parametrize("args", [
+    # (A, x, slots, pad, out, W, rank, N, K, B)
+    (P, P, P, P, P, 0, 0, 16, 64, 1),       # W < 1
+    (P, P, P, P, P, 9, 0, 16, 72, 1),       # W > 8
+    (P, P, P, P, P, 2, 2, 16, 64, 1),       # rank >= W
+    (P, P, P, P, P, 2, -1, 16, 64, 1),      # rank < 0
+    (P, P, P, P, P, 2, 0, 0, 64, 1),        # N < 1
+    (P, P, P, P, P, 3, 0, 16, 64, 1),       # K % W != 0
+    (P, P, P, P, P, 2, 0, 16, 36, 1),       # Ks % 8 != 0
+    (P, P, P, P, P, 2, 0, 16, 64, 0),       # B < 1
+    (P, P, P, P, P, 2, 0, 16, 64, 17),      # B > 16
+    (0, P, P, P, P, 2, 0, 16, 64, 1),       # null A
+    (P, P, P, P, 0, 2, 0, 16, 64, 1),       # null out
+    (P + 4, P, P, P, P, 2, 0, 16, 64, 1),   # misaligned A
+    (P, P + 8, P, P, P, 2, 0, 16, 64, 1),   # misaligned x
+    (P, P, P, P, P, 1, 0, 16, 8 * 8193, 16),  # x staging beyond the LDS bound
+    (P, P, P, P, P, 2, 0, 16, 64, 1),       # slots not from gsa_symm_alloc
+])
+def test_gemv_allreduce_rejects_bad_arguments(args):
+    rc = _lib.lib().gsa_gemv_allreduce(*args, None)
+    assert rc == gsa.GSA_EINVAL
+
+
+def test_other_entry_points_reject_bad_arguments():
+    L = _lib.lib()
+    h = ctypes.c_void_p()
+    assert L.gsa_symm_alloc(0, 16, 1, ctypes.byref(h)) == gsa.GSA_EINVAL
+    assert L.gsa_symm_alloc(2, 0, 1, ctypes.byref(h)) == gsa.GSA_EINVAL
+    assert L.gsa_symm_alloc(2, 16, 17, ctypes.byref(h)) == gsa.GSA_EINVAL
+    assert L.gsa_symm_alloc(2, 16, 1, None) == gsa.GSA_EINVAL
+    assert L.gsa_signal_pad_reset(P, 2, 16, 0, None) == gsa.GSA_EINVAL  # unknown pad
+    assert L.gsa_signal_pad_reset(P, 2, 16, 0b100, None) == gsa.GSA_EINVAL  # mask > W bits
+    c, t, p = ctypes.c_int(), ctypes.c_int64(), ctypes.c_int()
+    assert L.gsa_signal_pad_status(P, None, ctypes.byref(c), ctypes.byref(t),
+                                   ctypes.byref(p)) == gsa.GSA_EINVAL
+    assert L.gsa_set_wait_timeout_us(0) == gsa.GSA_EINVAL
+    assert L.gsa_symm_free(ctypes.c_void_p(P)) == gsa.GSA_EINVAL
+    assert L.gsa_symm_slots(ctypes.c_void_p(P)) is None
+    assert L.gsa_symm_free(None) == gsa.GSA_OK
