@@ -1,0 +1,272 @@
+"""Benchmark: µs per gemv_allreduce call and achieved HBM GB/s on one MI355X.
+
+One step = one fused call (GEMV of this rank's shard, publish, flag release,
+one-shot reduce) on one batch of resident inputs.  Inputs rotate over enough
+independent sets (>= 1 GiB in total) that every call reads A from HBM, not
+from the 256 MB Infinity Cache.
+
+The timed region replays a HIP graph of K calls (the way a decode loop issues
+them); a second, eager pass with an event pair around every launch gives the
+kernel's average duration, from which the roofline figure is computed.  The
+CPU oracle is timed on a bounded sample of the same workload.
+
+Prints one JSON line (rank 0, N = 1).
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import gsa_inputs as gi  # noqa: E402
+
+METRIC = "µs per gemv_allreduce call and achieved HBM GB/s (% of peak), 1 MI355X"
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_CONFIG = "c2"  # Llama-3-8B o_proj decode, W=8 N=4096 K=4096 B=1
+KERNEL_SOURCE = os.path.join(ROOT, "gemv_shot_all_amd", "csrc", "gemv_allreduce.hip")
+
+
+def alg_bytes(W, N, K, B):
+    """Bytes the method itself must move per call: A_r, x_r, the published
+    slot, the W-1 peer slots and out (flags excluded)."""
+    Ks = K // W
+    return 2 * N * Ks + 2 * B * Ks + 4 * N * B + 4 * (W - 1) * N * B + 4 * N * B
+
+
+def alg_flops(W, N, K, B):
+    Ks = K // W
+    return 2 * N * Ks * B + (W - 1) * N * B
+
+
+def kernel_source_digest():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_from_profile(cfg):
+    """HBM bytes per launch from the committed PMC summary for this workload,
+    or None if there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"gemv_allreduce_{cfg}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != kernel_source_digest():
+        return None
+    return float(m_b.group(1))
+
+
+class Sets:
+    """R independent input sets on the device, each with its own symmetric
+    buffer (peers published) and output."""
+
+    def __init__(self, d, rotate_bytes, max_sets=None):
+        import torch
+
+        import gemv_shot_all_amd as gsa
+        self.gsa = gsa
+        W, N, K, B = d["W"], d["N"], d["K"], d["B"]
+        self.W, self.N, self.K, self.B, self.rank = W, N, K, B, d["rank"]
+        foot = d["A"].nbytes + d["x"].nbytes + d["slots"].nbytes + 4 * N * B
+        R = max(1, -(-rotate_bytes // foot))
+        if max_sets:
+            R = min(R, max_sets)
+        self.R = R
+        A0 = torch.from_numpy(d["A"].view(np.int16)).cuda()
+        x0 = torch.from_numpy(d["x"].view(np.int16)).cuda()
+        s0 = torch.from_numpy(d["slots"]).cuda()
+        mask = ((1 << W) - 1) & ~(1 << self.rank)
+        self.A, self.x, self.out, self.bufs = [], [], [], []
+        for _ in range(R):
+            self.A.append(A0.clone())
+            self.x.append(x0.clone())
+            self.out.append(torch.full((N, B), float("nan"), dtype=torch.float32,
+                                       device="cuda"))
+            buf = gsa.SymmBuffer(W, N, B)
+            buf.slots_view().copy_(s0)
+            buf.reset(mask)
+            self.bufs.append(buf)
+        torch.cuda.synchronize()
+
+    def call(self, i):
+        j = i % self.R
+        b = self.bufs[j]
+        self.gsa.gsa_gemv_allreduce(self.A[j], self.x[j], b.slots, b.pad, self.out[j],
+                                    self.W, self.rank, self.N, self.K, self.B)
+
+    def close(self):
+        for b in self.bufs:
+            b.close()
+
+
+def check_parity(d, sets):
+    """Every set's result (the first R calls touched each set once) against
+    the oracle on set 0, and bit-equality of all sets with set 0."""
+    import oracle
+    out0 = sets.out[0].cpu().numpy()
+    slot0 = sets.bufs[0].slots_view().cpu().numpy()
+    y64, abs64, out64 = oracle.load().gemv_allreduce(d["A"], d["x"], d["slots"], d["rank"])
+    bnd = oracle.bound(abs64)
+    ok = bool(np.all(np.abs(out0 - out64) <= bnd) and
+              np.all(np.abs(slot0[d["rank"]] - y64) <= bnd))
+    for j in range(1, sets.R, max(1, sets.R // 8)):
+        ok = ok and np.array_equal(sets.out[j].cpu().numpy().view(np.uint32),
+                                   out0.view(np.uint32))
+    return ok, float(np.max(np.abs(out0 - out64) / bnd))
+
+
+def time_cpu_oracle(d, seconds):
+    """The oracle as it stands, single-threaded, on whole calls of the same
+    workload, for about `seconds` of CPU time.  Returns (µs per call, calls)."""
+    import oracle
+    o = oracle.load()
+    t0 = time.perf_counter()
+    o.gemv_allreduce(d["A"], d["x"], d["slots"], d["rank"])
+    one = time.perf_counter() - t0
+    n = max(1, int(seconds / max(one, 1e-6)))
+    t0 = time.perf_counter()
+    for _ in range(n):
+        o.gemv_allreduce(d["A"], d["x"], d["slots"], d["rank"])
+    el = time.perf_counter() - t0
+    return 1e6 * el / n, n
+
+
+def run_config(cfg, args):
+    import torch
+
+    d = gi.make_inputs(cfg, seed=args.seed, rank=0)
+    W, N, K, B = d["W"], d["N"], d["K"], d["B"]
+    sets = Sets(d, args.rotate_mib << 20 if not args.warm else 1, args.max_sets)
+    try:
+        # Warm-up; it also touches every set once, which the parity check reads.
+        for i in range(max(args.warmup, sets.R)):
+            sets.call(i)
+        torch.cuda.synchronize()
+        parity_ok, err_ratio = check_parity(d, sets)
+
+        # Eager pass: an event pair around every launch, on the launch stream.
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t_e0 = time.perf_counter()
+        for i in range(args.steps):
+            ev[i][0].record(stream)
+            sets.call(i)
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        eager_us = 1e6 * (time.perf_counter() - t_e0) / args.steps
+        durs = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3  # µs
+        kern_us = float(durs.mean())
+
+        # Timed region: replay of a graph holding K calls.
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(args.steps):
+                    sets.call(i)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        g.replay()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        us_per_call = 1e6 * el / args.steps
+        # The graph replays left every set in the same, correct state.
+        parity_after, _ = check_parity(d, sets)
+        parity_ok = parity_ok and parity_after
+    finally:
+        sets.close()
+
+    nbytes = alg_bytes(W, N, K, B)
+    achieved = nbytes / (kern_us * 1e-6) / 1e9
+    traffic = traffic_from_profile(cfg)
+    line = {
+        "metric": METRIC,
+        "value": round(us_per_call, 4),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_per_call / 1e3, 7),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": gi.CONFIGS[cfg]["name"], "id": cfg, "W": W, "rank": 0, "N": N,
+            "K": K, "B": B, "accumulate": "f32",
+            "inputs": "cold: rotated over %d resident sets" % sets.R if not args.warm
+                      else "warm: one set (Infinity-Cache resident, not HBM)",
+            "timing": "hipGraph replay of K calls between two device syncs",
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "alg_bytes_per_launch": nbytes,
+            "kernel_us_mean": round(kern_us, 4),
+            "kernel_us_p10_p50_p90": [round(float(np.percentile(durs, q)), 4)
+                                      for q in (10, 50, 90)],
+        },
+        "extra": {
+            "gbps_at_value": round(nbytes / (us_per_call * 1e-6) / 1e9, 1),
+            "eager_us_per_call": round(eager_us, 4),
+            "parity_ok": parity_ok,
+            "max_err_over_bound": err_ratio,
+            "alg_flops_per_call": alg_flops(W, N, K, B),
+        },
+    }
+    if args.cpu_seconds > 0:
+        cpu_us, ncalls = time_cpu_oracle(d, args.cpu_seconds)
+        line["cpu_baseline"] = {
+            "value": round(cpu_us, 2), "unit": "us/call", "cores": 1, "kind": "oracle",
+            "sample": f"{ncalls} whole calls of the {cfg} workload (fp64, single thread), "
+                      f"host {os.cpu_count()} logical CPUs",
+        }
+    else:
+        line["cpu_baseline"] = None
+    return line
+
+
+def main():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=200)
+    p.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(gi.CONFIGS))
+    p.add_argument("--all", action="store_true", help="one line per workload")
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--rotate-mib", type=int, default=1024,
+                   help="total size of the rotated input sets (MiB)")
+    p.add_argument("--max-sets", type=int, default=None)
+    p.add_argument("--warm", action="store_true", help="one resident set (cache-warm)")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="CPU-oracle timing budget (0 = skip)")
+    args = p.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the operator on one MI355X; "
+              "multi-GPU runs are not implemented (each rank would run this same "
+              "kernel on its own shard).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU (MI355X)", file=sys.stderr)
+        sys.exit(2)
+    cfgs = list(gi.CONFIGS) if args.all else [args.config]
+    for cfg in cfgs:
+        print(json.dumps(run_config(cfg, args)), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,7 +9,7 @@
 //   b. stages this rank's activation slice x (bf16) in LDS;
 //   c. streams its 16 rows of A_r with 128-bit loads and multiply-adds in
 //      fp32 (VALU bf16 dot2 for B <= 8, MFMA 16x16x32 for 8 < B <= 16);
-//   d. reduces lane partials with a fixed butterfly (or, for MFMA, a fixed
+//   d. reduces lane partials with a fixed DPP / lane-swap tree (or, for MFMA, a fixed
 //      cross-wave sum through LDS);
 //   e. publishes y into slot[rank], releases flag[rank][tile] = e, waits (if
 //      step a did not already see them) for every peer's flag >= e, and
@@ -24,6 +24,18 @@
 // fp32 accumulation of bf16 -- same documentation, higher-precision reduction.
 //
 // No value atomics and fixed reduction trees: repeated calls are bit-identical.
+//
+// Memory ordering of the signal-pad protocol.  Every access to shared
+// protocol state -- the published slot values, the peer slot values and the
+// flags -- is an agent-scope atomic (relaxed), which gfx950 performs at the
+// device coherence point, past the per-XCD L2 (sc1 loads and stores).  The
+// writer makes its slot stores complete (s_waitcnt vmcnt(0)) before the
+// workgroup barrier that precedes the flag store; the reader issues its slot
+// loads only after the flag load has returned a value >= the epoch (the loads
+// sit behind a branch on that value).  That orders data before flag without
+// an agent-scope fence, whose whole-L2 writeback (release) or invalidate
+// (acquire) per workgroup would cost several microseconds per call.  Across
+// GPUs the same scheme runs at system scope.
 
 #include "gsa_internal.h"
 
@@ -36,15 +48,10 @@ constexpr int kMaxW = GSA_MAX_W;
 // s_ctl[1] values: what the start-of-kernel poll found.
 enum : uint32_t { kMustWait = 0u, kPeersReady = 1u, kBadOwnRow = 2u };
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
-
-constexpr int pow2_ceil(int v) {
-  int p = 1;
-  while (p < v) p <<= 1;
-  return p;
-}
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -60,6 +67,18 @@ __device__ __forceinline__ float dot8(const uint4& a, const uint4& x, float acc)
   return acc;
 }
 
+// Buffer resource over `bytes` bytes at `base` (raw, stride 0).  Loads past
+// the end return zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes at byte offset voff + soff (voff per lane, soff uniform).
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ uint32_t* flag_ptr(const GemvArgs& a, int r, int64_t t) {
   return a.pad + GSA_PAD_HEADER_WORDS + (int64_t)r * a.row_stride + t;
 }
@@ -71,45 +90,73 @@ __device__ __forceinline__ uint32_t load_flag(const GemvArgs& a, int lane, int64
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void acquire_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+// Agent-scope (device-coherent) relaxed accesses for protocol state.
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_flag(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until at most N vector memory operations of this wave are still
+// outstanding (s_waitcnt vmcnt(N), expcnt and lgkmcnt untouched; gfx9
+// encoding: vmcnt bits [3:0] and [15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vm_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+// Wait until every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_vm_all() { wait_vm_le<0>(); }
 
-// Rank r's 16 x B tile of slot r lands at pe[(r * 16 + n) * B + b].  Rows
-// past N are clamped (their values are never used).  Every lane issues all
-// its loads before the first LDS write (ranks >= W are clamped to W-1 and
-// written to the sink at pe[W * 16 * B]).
-__device__ __forceinline__ void load_peer_tile(const GemvArgs& a, int lane, int64_t tile,
-                                               float* pe) {
+// Peer tiles: rank r's 16 x B tile of slot r lands at pe[(r * 16 + n) * B + b]
+// for every peer r != rank.  issue_peer_tile loads up to kPerLane values per
+// lane per peer into registers (rows past N are clamped to a valid address;
+// their values are never read); store_peer_tile writes them to LDS.  The peer
+// loop is unrolled over GSA_MAX_W with a uniform guard, so no load sits under
+// divergent control.
+constexpr int kPerLane = (kTileRows * GSA_MAX_B) / 64;  // 4
+
+__device__ __forceinline__ void issue_peer_tile(const GemvArgs& a, int lane, int64_t tile,
+                                                float (&v)[kMaxW][kPerLane]) {
   const int64_t NB = a.N * a.B;
-  const int tb = kTileRows * a.B;                // elements of one rank's tile
-  const int64_t first = tile * kTileRows * a.B;  // first element of the tile in a slot
+  const int per_lane = (kTileRows * a.B + 63) / 64;  // 1, 2 or 4
+  const int64_t first = tile * kTileRows * a.B;      // first element of the tile in a slot
   const int64_t last = NB - 1;
-  constexpr int kPerLane = (kTileRows * GSA_MAX_B) / 64;  // 4
-  float v[kMaxW][kPerLane];
 #pragma unroll
   for (int r = 0; r < kMaxW; ++r) {
-    const float* src = a.slots + min(r, a.W - 1) * NB;
+    if (r < a.W && r != a.rank) {
+      const float* src = a.slots + r * NB;
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) v[r][i] = src[min(first + lane + 64 * i, last)];
-  }
-  const int sink = a.W * tb;
-#pragma unroll
-  for (int r = 0; r < kMaxW; ++r) {
-#pragma unroll
-    for (int i = 0; i < kPerLane; ++i) {
-      const int e = lane + 64 * i;
-      pe[(r < a.W && e < tb) ? r * tb + e : sink] = v[r][i];
+      for (int i = 0; i < kPerLane; ++i)
+        if (i < per_lane) v[r][i] = load_coherent(&src[min(first + lane + 64 * i, last)]);
     }
   }
 }
 
-// The communication wave's part before the workgroup's second barrier: derive
-// the epoch from its own flag, check every peer's flag for this tile, and if
-// all have published, acquire and copy the peers' tiles into LDS.  Writes
-// s_ctl[0] = epoch and s_ctl[1] = kMustWait / kPeersReady / kBadOwnRow.
-__device__ __forceinline__ void comm_start(const GemvArgs& a, int lane, int64_t tile,
-                                           uint32_t fl, float* pe, uint32_t* s_ctl) {
+__device__ __forceinline__ void store_peer_tile(const GemvArgs& a, int lane,
+                                                const float (&v)[kMaxW][kPerLane], float* pe) {
+  const int tb = kTileRows * a.B;  // elements of one rank's tile
+  const int per_lane = (tb + 63) / 64;
+#pragma unroll
+  for (int r = 0; r < kMaxW; ++r) {
+    if (r < a.W && r != a.rank) {
+#pragma unroll
+      for (int i = 0; i < kPerLane; ++i) {
+        const int e = lane + 64 * i;
+        if (i < per_lane && e < tb) pe[r * tb + e] = v[r][i];
+      }
+    }
+  }
+}
+
+// The communication wave's start: derive the epoch from its own flag and
+// check every peer's flag for this tile.  Writes s_ctl[0] = epoch and
+// s_ctl[1] = kMustWait / kPeersReady / kBadOwnRow; returns s_ctl[1].
+__device__ __forceinline__ uint32_t comm_decide(const GemvArgs& a, int lane, int64_t tile,
+                                                uint32_t fl, uint32_t* s_ctl) {
   const uint32_t own = __builtin_amdgcn_readlane(fl, a.rank);
   if (own >= GSA_FLAG_PUBLISHED - 1u) {  // row marked published, or epochs exhausted
     if (lane == 0) {
@@ -117,19 +164,16 @@ __device__ __forceinline__ void comm_start(const GemvArgs& a, int lane, int64_t 
       atomicMin(a.pad + kHdrStateTile, (uint32_t)tile);
       s_ctl[1] = kBadOwnRow;
     }
-    return;
+    return kBadOwnRow;
   }
   const uint32_t epoch = own + 1u;
   const bool lane_ok = lane >= a.W || lane == a.rank || fl >= epoch;
   const bool ready = __ballot(!lane_ok) == 0;
-  if (ready) {
-    acquire_fence();
-    load_peer_tile(a, lane, tile, pe);
-  }
   if (lane == 0) {
     s_ctl[0] = epoch;
     s_ctl[1] = ready ? kPeersReady : kMustWait;
   }
+  return ready ? kPeersReady : kMustWait;
 }
 
 // Bounded wait for every peer's flag >= epoch.  On expiry records the
@@ -140,10 +184,7 @@ __device__ bool wait_peers(const GemvArgs& a, int lane, int64_t tile, uint32_t e
     const uint32_t f = load_flag(a, lane, tile);
     const bool lane_ok = lane >= a.W || lane == a.rank || f >= epoch;
     const uint64_t missing = __ballot(!lane_ok);
-    if (missing == 0) {
-      acquire_fence();
-      return true;
-    }
+    if (missing == 0) return true;
     if (wall_clock64() - start > a.timeout_ticks) {
       if (lane == 0) {
         const uint32_t peer = (uint32_t)(__ffsll((long long)missing) - 1);
@@ -156,27 +197,35 @@ __device__ bool wait_peers(const GemvArgs& a, int lane, int64_t tile, uint32_t e
   }
 }
 
-// The communication wave (the last wave of every workgroup).  It does the
-// signal-pad protocol so that its waits never hold up the A stream of the
-// compute waves.  Barrier schedule shared with the compute waves:
-//   B1 x staged | B2 partials + peer tile ready | B3 own slot published
-//   | B4 (only if the peers were not ready at B2) late peer tile ready.
+// The communication wave (the last wave of every workgroup) runs the
+// signal-pad protocol, so its round trips never hold up the A stream of the
+// compute waves.  A CU returns vector loads in issue order, so the flag load
+// goes out before the compute waves' x and A loads (barrier B0); the peer
+// loads it issues once the flags are back return right behind the A stream.
+// Barrier schedule shared with the compute waves:
+//   B0 flag load issued | B1 x staged by the compute waves | B2 partials
+//   final, peer tile in LDS if the peers were ready | B3 own slot published
+//   | B4 (only if the peers were not ready at the start) late peer tile in LDS.
 __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
                           uint32_t* s_ctl) {
   const uint32_t fl = load_flag(a, lane, tile);
+  __syncthreads();  // B0: the flag load is issued ahead of every x and A load
+  const uint32_t state = comm_decide(a, lane, tile, fl, s_ctl);
+  float v[kMaxW][kPerLane];
+  if (state == kPeersReady) issue_peer_tile(a, lane, tile, v);  // after the flags returned
   __syncthreads();  // B1
-  comm_start(a, lane, tile, fl, pe, s_ctl);
+  if (state == kPeersReady) store_peer_tile(a, lane, v, pe);
   __syncthreads();  // B2
-  const uint32_t state = s_ctl[1];
   if (state == kBadOwnRow) return;
   const uint32_t epoch = s_ctl[0];
-  __syncthreads();  // B3: the compute waves' slot stores precede this barrier
-  if (lane == 0)
-    __hip_atomic_store(flag_ptr(a, a.rank, tile), epoch, __ATOMIC_RELEASE,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();  // B3: the compute waves' slot stores completed before it
+  if (lane == 0) store_flag(flag_ptr(a, a.rank, tile), epoch);
   if (state == kPeersReady) return;
   const bool ok = wait_peers(a, lane, tile, epoch);
-  if (ok) load_peer_tile(a, lane, tile, pe);
+  if (ok) {
+    issue_peer_tile(a, lane, tile, v);  // after the flags returned
+    store_peer_tile(a, lane, v, pe);
+  }
   if (lane == 0) s_ctl[1] = ok ? kPeersReady : kMustWait;
   __syncthreads();  // B4
 }
@@ -208,13 +257,14 @@ __device__ void finish_after_b2(const GemvArgs& a, int64_t tile, const int (&n)[
   float* own_slot = a.slots + a.rank * NB;
 #pragma unroll
   for (int e = 0; e < OPL; ++e)
-    if (live[e]) own_slot[(row0 + n[e]) * a.B + b] = y[e];
+    if (live[e]) store_coherent(&own_slot[(row0 + n[e]) * a.B + b], y[e]);
   if (state == kPeersReady) {
 #pragma unroll
     for (int e = 0; e < OPL; ++e)
       if (live[e]) a.out[(row0 + n[e]) * a.B + b] = one_shot_sum(a, y[e], pe, n[e], b);
   }
-  __syncthreads();  // B3
+  wait_vm_all();    // the published values are at the coherence point ...
+  __syncthreads();  // B3 ... before the communication wave stores the flag
   if (state == kPeersReady) return;
   __syncthreads();  // B4
   if (s_ctl[1] != kPeersReady) return;  // wait expired: this tile's out rows stay unwritten
@@ -242,90 +292,112 @@ __device__ void mfma_finish(const GemvArgs& a, int64_t tile, int wave, int lane,
   finish_after_b2<4>(a, tile, n, b, live, y, pe, s_ctl);
 }
 
-// Butterfly reduction of P values over a group of G lanes (G, P powers of
-// two, P <= G).  Each step halves the values a lane keeps and the lanes it
-// spans; afterwards lane li holds the group total of value li / (G / P).
-template <int G, int P>
-__device__ __forceinline__ void butterfly(float* v, int li) {
-  if constexpr (G > 1) {
-    constexpr int OFF = G / 2;
-    if constexpr (P > 1) {
-      constexpr int H = P / 2;
-      const bool up = (li & OFF) != 0;
+// Sum of v over an aligned group of G lanes (G = 16, 32 or 64), returned in
+// every lane of the group, bit-identical across the group.  Within each
+// 16-lane row: DPP rotations by 8, 4, 2, 1 (lane i adds lane i+k mod 16; by
+// commutativity every lane ends with the same fixed tree).  Across rows:
+// v_permlane16_swap pairs rows 0-1 and 2-3, v_permlane32_swap pairs the two
+// halves; summing both swap outputs gives the pair total in every lane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(G == 16 || G == 32 || G == 64, "lane group of 16, 32 or 64");
+  v = v + dpp_f32<0x128>(v);  // row_ror:8
+  v = v + dpp_f32<0x124>(v);  // row_ror:4
+  v = v + dpp_f32<0x122>(v);  // row_ror:2
+  v = v + dpp_f32<0x121>(v);  // row_ror:1
+  if constexpr (G >= 32) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
+  }
+  if constexpr (G == 64) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    v = __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
+  }
+  return v;
+}
+
+// One A chunk (16 bytes) of each of the lane's R rows, at byte offset
+// voff[s] + soff, through the buffer resource over A.  Rows past N read
+// zeros; chunks past a row's end read the next row's data, which mac_chunk
+// pairs with a zero x chunk (A is finite), so no load is masked.
+template <int R>
+__device__ __forceinline__ void load_chunk(uint4 (&av)[R], __amdgpu_buffer_rsrc_t ra,
+                                           const uint32_t (&voff)[R], uint32_t soff) {
 #pragma unroll
-      for (int i = 0; i < H; ++i) {
-        const float send = up ? v[i] : v[i + H];
-        const float keep = up ? v[i + H] : v[i];
-        v[i] = keep + __shfl_xor(send, OFF);
-      }
-      butterfly<OFF, H>(v, li);
-    } else {
-      v[0] = v[0] + __shfl_xor(v[0], OFF);
-      butterfly<OFF, 1>(v, li);
+  for (int s = 0; s < R; ++s) av[s] = buf_load16(ra, voff[s], soff);
+}
+
+// acc[s][b] += <A chunk of row s, x chunk c of batch b>.  x chunks live at
+// lds_x[b * C + c]; lds_x[zidx] holds a zero chunk used for c >= C.
+template <bool MASKED, int B, int R>
+__device__ __forceinline__ void mac_chunk(float (&acc)[R][B], const uint4 (&av)[R],
+                                          const uint4* lds_x, int C, int zidx, int c) {
+  uint4 xv[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) xv[b] = lds_x[(MASKED && c >= C) ? zidx : b * C + c];
+#pragma unroll
+  for (int s = 0; s < R; ++s)
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[s][b] = dot8(av[s], xv[b], acc[s][b]);
+}
+
+// The lane's chunks j = 0, 1, ... (chunk li + j * G of each row) as a stream
+// with D chunks in flight: ring[j % D] holds chunk j, chunks 0..D-1 were
+// issued before the LDS barrier.  NCH > 0: exactly NCH chunks, fully
+// unrolled; NCH == 0: nch chunks, unrolled by D.
+template <bool MASKED, int NCH, int D, int B, int G, int R>
+__device__ __forceinline__ void valu_stream(float (&acc)[R][B], uint4 (&ring)[D][R],
+                                            __amdgpu_buffer_rsrc_t ra, const uint32_t (&voff)[R],
+                                            const uint4* lds_x, int C, int zidx, int li, int nch) {
+  if constexpr (NCH > 0) {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      mac_chunk<MASKED, B, R>(acc, ring[j % D], lds_x, C, zidx, li + j * G);
+      if (j + D < NCH) load_chunk<R>(ring[j % D], ra, voff, (uint32_t)((j + D) * G) * 16u);
     }
-  }
-}
-
-// A chunks [base + li + j*G] of rows rowc[0..R-1] (already clamped to N-1).
-// MASKED: chunks past the row end are clamped to a valid chunk; mac_pass pairs
-// them with a zero x chunk, so they add nothing (A is finite).
-template <bool MASKED, int CPL, int R, int G>
-__device__ __forceinline__ void load_a(uint4 (&av)[CPL][R], const uint4* Ag,
-                                       const int64_t (&rowc)[R], int C, int li, int base) {
+  } else {
+    for (int j0 = 0; j0 < nch; j0 += D) {
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const int c = base + li + j * G;
-    const int cc = MASKED ? min(c, C - 1) : c;
-#pragma unroll
-    for (int s = 0; s < R; ++s) av[j][s] = Ag[rowc[s] * C + cc];
-  }
-}
-
-// x chunks live at lds_x[b * C + c]; lds_x[B * C] holds a zero chunk.
-template <bool MASKED, int B, int R, int CPL, int G>
-__device__ __forceinline__ void mac_pass(float (&acc)[R][B], const uint4 (&av)[CPL][R],
-                                         const uint4* lds_x, int C, int li, int base) {
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) {
-    const int c = base + li + j * G;
-    uint4 xv[B];
-#pragma unroll
-    for (int b = 0; b < B; ++b) xv[b] = lds_x[(MASKED && c >= C) ? B * C : b * C + c];
-#pragma unroll
-    for (int s = 0; s < R; ++s)
-#pragma unroll
-      for (int b = 0; b < B; ++b) acc[s][b] = dot8(av[j][s], xv[b], acc[s][b]);
-  }
-}
-
-// Main loop of the VALU kernel: the first pass's A chunks are already in
-// registers; later passes load and accumulate.
-template <bool MASKED, int B, int G, int R, int CPL>
-__device__ __forceinline__ void valu_passes(float (&acc)[R][B], uint4 (&av)[CPL][R],
-                                            const uint4* Ag, const int64_t (&rowc)[R],
-                                            const uint4* lds_x, int C, int li) {
-  mac_pass<MASKED, B, R, CPL, G>(acc, av, lds_x, C, li, 0);
-  for (int base = G * CPL; base < C; base += G * CPL) {
-    load_a<MASKED, CPL, R, G>(av, Ag, rowc, C, li, base);
-    mac_pass<MASKED, B, R, CPL, G>(acc, av, lds_x, C, li, base);
+      for (int u = 0; u < D; ++u) {
+        const int j = j0 + u;
+        if (j < nch) {
+          mac_chunk<MASKED, B, R>(acc, ring[u], lds_x, C, zidx, li + j * G);
+          if (j + D < nch) load_chunk<R>(ring[u], ra, voff, (uint32_t)((j + D) * G) * 16u);
+        }
+      }
+    }
   }
 }
 
 // VALU path, B <= 8.  NW compute waves plus one communication wave.  Each
 // compute wave holds 64/G row groups of R rows; a row group of G lanes walks
-// one row in 16-byte chunks li, li+G, ...  CPL chunks per lane are loaded per
-// pass (the first pass before the LDS barrier, behind the x loads); XPT x
-// chunks per thread are staged through registers.  Chunk masking is only
-// compiled into the branch taken when C is not a multiple of G * CPL.
-// LDS: x chunks [b][c], one zero chunk, one sink chunk; then the peer tile.
-template <int B, int G, int R, int NW, int CPL, int XPT>
-__global__ __launch_bounds__((NW + 1) * 64) void gemv_ar_valu(GemvArgs a) {
+// one row in 16-byte chunks li, li+G, ... as a stream with D chunks in flight
+// per lane (the memory system accepts requests only as fast as it serves
+// them, so a wave that issued everything up front would sit blocked at issue
+// while its data arrives).  The compute waves first issue their share of x
+// (XPT chunks per thread, into registers) and the first D chunks of A, then
+// write x to LDS and pass the LDS barrier after only D chunks' worth of A
+// loads (the compiler interleaves the two; forcing every x load ahead of the
+// A loads measured slower, with all workgroups hitting the same x lines at
+// once).  WPE is the occupancy (waves per SIMD) the register budget must
+// allow.  NCH > 0 builds a fully unrolled instance for
+// exactly NCH chunks per lane; MASKED instances zero chunks past the row end.
+// LDS: x chunks [b][c], one zero chunk, one sink chunk, then the peer tile.
+template <int B, int G, int R, int NW, int NCH, int D, int XPT, int WPE, bool MASKED>
+__global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   constexpr int NT = NW * 64;
   constexpr int GPW = 64 / G;
   static_assert(NW * GPW * R == kTileRows, "one workgroup covers one flag tile");
   constexpr int V = R * B;
-  constexpr int P = pow2_ceil(V);
-  static_assert(P <= G, "butterfly needs P <= G");
+  static_assert(V <= G, "one owner lane per output of a row group");
 
   extern __shared__ uint4 lds_x[];
   __shared__ uint32_t s_ctl[2];
@@ -336,6 +408,7 @@ __global__ __launch_bounds__((NW + 1) * 64) void gemv_ar_valu(GemvArgs a) {
   const int64_t tile = blockIdx.x;
   const int C = a.C;
   const int xchunks = B * C;
+  const int zidx = xchunks;  // zero chunk; xchunks + 1 is the sink
   float* pe = reinterpret_cast<float*>(lds_x + xchunks + 2);
 
   if (wave == NW) {
@@ -347,22 +420,22 @@ __global__ __launch_bounds__((NW + 1) * 64) void gemv_ar_valu(GemvArgs a) {
   const int li = lane % G;
   const int nloc0 = (wave * GPW + grp) * R;  // first local row of this row group
   const int64_t row0 = tile * kTileRows + nloc0;
-  const bool masked = (C % (G * CPL)) != 0;
+  const int nch = NCH > 0 ? NCH : (C + G - 1) / G;
 
   const uint4* xg = reinterpret_cast<const uint4*>(a.x);
+  __syncthreads();  // B0
   uint4 xr[XPT];
 #pragma unroll
   for (int i = 0; i < XPT; ++i) xr[i] = xg[min(tid + i * NT, xchunks - 1)];
 
-  const uint4* Ag = reinterpret_cast<const uint4*>(a.A);
-  int64_t rowc[R];
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, (uint32_t)(a.N * C * 16));
+  uint32_t voff[R];
 #pragma unroll
-  for (int s = 0; s < R; ++s) rowc[s] = min(row0 + s, a.N - 1);
-  uint4 av[CPL][R];
-  if (masked)
-    load_a<true, CPL, R, G>(av, Ag, rowc, C, li, 0);
-  else
-    load_a<false, CPL, R, G>(av, Ag, rowc, C, li, 0);
+  for (int s = 0; s < R; ++s) voff[s] = ((uint32_t)(row0 + s) * (uint32_t)C + li) * 16u;
+  uint4 ring[D][R];
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+    if (NCH > 0 ? u < NCH : u < nch) load_chunk<R>(ring[u], ra, voff, (uint32_t)(u * G) * 16u);
 
 #pragma unroll
   for (int i = 0; i < XPT; ++i) {
@@ -370,7 +443,7 @@ __global__ __launch_bounds__((NW + 1) * 64) void gemv_ar_valu(GemvArgs a) {
     lds_x[idx < xchunks ? idx : xchunks + 1] = xr[i];  // out-of-range lanes: sink
   }
   for (int idx = tid + XPT * NT; idx < xchunks; idx += NT) lds_x[idx] = xg[idx];
-  if (tid == 0) lds_x[xchunks] = make_uint4(0u, 0u, 0u, 0u);  // zero chunk for masking
+  if (tid == 0) lds_x[zidx] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();  // B1
 
   float acc[R][B];
@@ -378,37 +451,34 @@ __global__ __launch_bounds__((NW + 1) * 64) void gemv_ar_valu(GemvArgs a) {
   for (int s = 0; s < R; ++s)
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[s][b] = 0.0f;
-  if (masked)
-    valu_passes<true, B, G, R, CPL>(acc, av, Ag, rowc, lds_x, C, li);
-  else
-    valu_passes<false, B, G, R, CPL>(acc, av, Ag, rowc, lds_x, C, li);
+  valu_stream<MASKED, NCH, D, B, G, R>(acc, ring, ra, voff, lds_x, C, zidx, li, nch);
 
-  float v[P];
+  // Every lane of the row group gets every total; lane li < V owns output
+  // li = s * B + b (row nloc0 + s, column b): consecutive floats of the slot.
+  float yv = 0.0f;
 #pragma unroll
-  for (int i = 0; i < P; ++i) v[i] = i < V ? acc[i / B][i % B] : 0.0f;
-  butterfly<G, P>(v, li);
-
-  // Lane li now holds value vidx = s * B + b of its row group.
-  const int vidx = li / (G / P);
-  const bool owner = (li % (G / P)) == 0 && vidx < V;
-  const int n[1] = {nloc0 + min(vidx, V - 1) / B};
-  const bool live[1] = {owner && tile * kTileRows + n[0] < a.N};
-  const float y[1] = {v[0]};
+  for (int i = 0; i < V; ++i) {
+    const float t = group_sum<G>(acc[i / B][i % B]);
+    yv = li == i ? t : yv;
+  }
+  const int vidx = min(li, V - 1);
+  const int n[1] = {nloc0 + vidx / B};
+  const bool live[1] = {li < V && tile * kTileRows + n[0] < a.N};
+  const float y[1] = {yv};
+  asm volatile("" ::"v"(yv));  // keep the GEMV ahead of B2 (it overlaps the peer loads)
   __syncthreads();  // B2
   finish_after_b2<1>(a, tile, n, vidx % B, live, y, pe, s_ctl);
 }
 
-// A operand chunks of k-steps s0..s0+SPW-1 for MFMA lane (row arowc, chunk
-// group kq).  MASKED: indices are clamped to a valid chunk; mfma_pass pairs
-// steps past s_end and chunks past the row with the zero x column.
-template <bool MASKED, int SPW>
-__device__ __forceinline__ void load_a_mfma(uint4 (&av)[SPW], const uint4* Ag, int64_t arowc,
-                                            int C, int kq, int s0) {
+// A operand chunks of k-steps s0..s0+SPW-1 for MFMA lane l: row (l & 15),
+// chunk 4 * step + (l >> 4); voff is the byte offset of that chunk at step 0.
+// Out-of-row and past-the-end chunks are harmless (see load_a); mfma_pass
+// pairs steps past s_end and chunks past the row with the zero x column.
+template <int SPW>
+__device__ __forceinline__ void load_a_mfma(uint4 (&av)[SPW], __amdgpu_buffer_rsrc_t ra,
+                                            uint32_t voff, int s0) {
 #pragma unroll
-  for (int u = 0; u < SPW; ++u) {
-    const int chunk = 4 * (s0 + u) + kq;
-    av[u] = Ag[arowc * C + (MASKED ? min(chunk, C - 1) : chunk)];
-  }
+  for (int u = 0; u < SPW; ++u) av[u] = buf_load16(ra, voff, (uint32_t)(s0 + u) * 64u);
 }
 
 // x chunk (batch xb, chunk c) at lds[xb * CP + c]; column C of every batch
@@ -429,12 +499,12 @@ __device__ __forceinline__ f32x4_t mfma_pass(f32x4_t acc, const uint4 (&av)[SPW]
 }
 
 template <bool MASKED, int SPW>
-__device__ __forceinline__ f32x4_t mfma_steps(uint4 (&av)[SPW], const uint4* Ag, int64_t arowc,
-                                              const uint4* lds, int CP, int C, int xb, int kq,
-                                              int s_begin, int s_end) {
+__device__ __forceinline__ f32x4_t mfma_steps(uint4 (&av)[SPW], __amdgpu_buffer_rsrc_t ra,
+                                              uint32_t voff, const uint4* lds, int CP, int C,
+                                              int xb, int kq, int s_begin, int s_end) {
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int s0 = s_begin; s0 < s_end; s0 += SPW) {
-    if (s0 != s_begin) load_a_mfma<MASKED, SPW>(av, Ag, arowc, C, kq, s0);
+    if (s0 != s_begin) load_a_mfma<SPW>(av, ra, voff, s0);
     acc = mfma_pass<MASKED, SPW>(acc, av, lds, CP, C, xb, kq, s0, s_end);
   }
   return acc;
@@ -476,6 +546,7 @@ __global__ __launch_bounds__((NW + 1) * 64) void gemv_ar_mfma(GemvArgs a) {
   const bool masked = (C % 4) != 0 || (steps % NW) != 0 || (per_wave % SPW) != 0;
 
   const uint4* xg = reinterpret_cast<const uint4*>(a.x);
+  __syncthreads();  // B0
   uint4 xr[XC][16];
 #pragma unroll
   for (int i = 0; i < XC; ++i) {
@@ -488,14 +559,11 @@ __global__ __launch_bounds__((NW + 1) * 64) void gemv_ar_mfma(GemvArgs a) {
     }
   }
 
-  const uint4* Ag = reinterpret_cast<const uint4*>(a.A);
-  const int64_t arowc = min(row0 + (lane & 15), a.N - 1);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, (uint32_t)(a.N * C * 16));
   const int kq = lane >> 4;
+  const uint32_t voff = ((uint32_t)(row0 + (lane & 15)) * (uint32_t)C + kq) * 16u;
   uint4 av[SPW];
-  if (masked)
-    load_a_mfma<true, SPW>(av, Ag, arowc, C, kq, s_begin);
-  else
-    load_a_mfma<false, SPW>(av, Ag, arowc, C, kq, s_begin);
+  load_a_mfma<SPW>(av, ra, voff, s_begin);
 
 #pragma unroll
   for (int i = 0; i < XC; ++i) {
@@ -514,9 +582,9 @@ __global__ __launch_bounds__((NW + 1) * 64) void gemv_ar_mfma(GemvArgs a) {
   const int xb = lane & 15;
   f32x4_t acc;
   if (masked)
-    acc = mfma_steps<true, SPW>(av, Ag, arowc, lds, CP, C, xb, kq, s_begin, s_end);
+    acc = mfma_steps<true, SPW>(av, ra, voff, lds, CP, C, xb, kq, s_begin, s_end);
   else
-    acc = mfma_steps<false, SPW>(av, Ag, arowc, lds, CP, C, xb, kq, s_begin, s_end);
+    acc = mfma_steps<false, SPW>(av, ra, voff, lds, CP, C, xb, kq, s_begin, s_end);
 
   if (wave > 0) {
 #pragma unroll
@@ -548,7 +616,6 @@ __global__ void pad_reset_kernel(uint32_t* pad, int W, int row_stride, uint32_t 
   pad[i] = v;
 }
 
-constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 constexpr int kMfmaWaves = 4;
 
 struct ValuChoice {
@@ -556,25 +623,36 @@ struct ValuChoice {
   int waves;  // compute waves (the communication wave comes on top)
 };
 
-// CMAX: largest C of the tier; XPT covers B * CMAX chunks (at most 8 per thread).
-template <int B, int G, int R, int NW, int CPL, int CMAX>
-ValuChoice valu_choice() {
-  constexpr int XPT0 = ceil_div(B * CMAX, NW * 64);
+constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// One tier: G lanes per row, R rows per row group, NW compute waves, D chunks
+// in flight per lane, occupancy WPE.  C == G * NCH gets the fully unrolled
+// exact instance; any other C the masked streaming instance.  XPT covers
+// B * G * NCH chunks of x (at most 8 per thread; the rest of a longer x is
+// staged by a plain loop).
+template <int B, int G, int R, int NW, int NCH, int D, int WPE>
+ValuChoice valu_tier(int C) {
+  constexpr int XPT0 = ceil_div(B * G * NCH, NW * 64);
   constexpr int XPT = XPT0 > 8 ? 8 : XPT0;
-  return {reinterpret_cast<const void*>(&gemv_ar_valu<B, G, R, NW, CPL, XPT>), NW};
+  constexpr int DE = D < NCH ? D : NCH;
+  const void* k;
+  if (C == G * NCH)
+    k = reinterpret_cast<const void*>(&gemv_ar_valu<B, G, R, NW, NCH, DE, XPT, WPE, false>);
+  else
+    k = reinterpret_cast<const void*>(&gemv_ar_valu<B, G, R, NW, 0, D, XPT, WPE, true>);
+  return {k, NW};
 }
 
 // VALU tiers by chunks per row C = Ks / 8 (every tier covers 16 rows per
 // workgroup, plus the communication wave):
-//   C <= 64 : 4 waves, a full wave per row, 4 rows per wave, 1 chunk per pass
-//   C <= 224: 4 waves, half a wave per row, 2 x 2 rows per wave, 7 chunks
-//   larger  : 8 waves, a full wave per row, 2 rows per wave, 7 chunks per
-//             pass (4 for B > 4, to stay within 168 VGPRs)
+//   C <= 64 : 4 waves, a full wave per row, 4 rows per wave
+//   C <= 224: 4 waves, half a wave per row, 2 x 2 rows per wave
+//   larger  : 8 waves, a full wave per row, 2 rows per wave
 template <int B>
 ValuChoice valu_kernel(int C) {
-  if (C <= 64) return valu_choice<B, 64, 4, 4, 1, 64>();
-  if (C <= 224) return valu_choice<B, 32, 2, 4, 7, 224>();
-  return valu_choice<B, 64, 2, 8, (B <= 4 ? 7 : 4), 448>();
+  if (C <= 64) return valu_tier<B, 64, 4, 4, 1, 1, 1>(C);
+  if (C <= 224) return valu_tier<B, 32, 2, 4, 7, 3, 1>(C);
+  return valu_tier<B, 64, 2, 8, 7, 3, 5>(C);
 }
 
 }  // namespace

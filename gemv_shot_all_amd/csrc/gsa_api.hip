@@ -183,6 +183,8 @@ int gsa_gemv_allreduce(const uint16_t* A_r, const uint16_t* x, float* slots, uin
   if (!aligned16(A_r) || !aligned16(x) || !aligned16(slots) || !aligned16(pad) ||
       !aligned16(out))
     return GSA_EINVAL;
+  // A_r is addressed through a 32-bit buffer resource.
+  if (N > ((int64_t)0x7FFFFFF0 / 2) / Ks) return GSA_EINVAL;
   const int C = (int)(Ks / 8);
   gsa::Launch l;
   if (!gsa::select_gemv_kernel(W, B, C, &l)) return GSA_EINVAL;

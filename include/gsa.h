@@ -108,8 +108,10 @@ int gsa_signal_pad_reset(uint32_t *pad, int W, int64_t N, uint32_t published_mas
  *   pad   [device] gsa_symm_signal_pad of the same buffer
  *   out   [device] fp32 N x B (n-major); any device memory, written only
  * Requires 1 <= W <= 8, 0 <= rank < W, K % W == 0, Ks % 8 == 0, N >= 1,
- * 1 <= B <= 16, every pointer non-null and 16-byte aligned, and the x staging
- * bound GSA_MAX_X_LDS_BYTES; otherwise GSA_EINVAL and nothing is launched.
+ * 1 <= B <= 16, N * Ks * 2 < 2^31 (A_r is addressed with 32-bit offsets),
+ * every pointer non-null and 16-byte aligned, and the x staging bound
+ * GSA_MAX_X_LDS_BYTES; otherwise GSA_EINVAL and nothing is launched.
+ * A_r must hold finite values (chunks past a row's end are paired with zeros).
  * No host sync, no allocation.  All calls on one buffer must use one stream
  * (flags are indexed by tile, not by stream).  Each tile's flag epoch is its
  * own previous flag + 1, so at most 2^32 - 2 calls fit between resets.
