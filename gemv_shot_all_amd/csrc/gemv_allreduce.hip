@@ -203,9 +203,13 @@ __device__ bool wait_peers(const GemvArgs& a, int lane, int64_t tile, uint32_t e
 // goes out before the compute waves' x and A loads (barrier B0); the peer
 // loads it issues once the flags are back return right behind the A stream.
 // Barrier schedule shared with the compute waves:
-//   B0 flag load issued | B1 x staged by the compute waves | B2 partials
-//   final, peer tile in LDS if the peers were ready | B3 own slot published
-//   | B4 (only if the peers were not ready at the start) late peer tile in LDS.
+//   B0 flag load issued | B1 x staged, decision in s_ctl | EXTRA barriers of
+//   the compute waves' own | B2 own slot published, and the peer tile in LDS
+//   if the peers were ready at the start (compute wave 0 then stores the
+//   flag) | B3 (only if they were not) late peer tile in LDS.
+// The peer loads stay in flight across B1: a workgroup barrier does not wait
+// for outstanding global loads.
+template <int EXTRA>
 __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
                           uint32_t* s_ctl) {
   const uint32_t fl = load_flag(a, lane, tile);
@@ -214,82 +218,71 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
   float v[kMaxW][kPerLane];
   if (state == kPeersReady) issue_peer_tile(a, lane, tile, v);  // after the flags returned
   __syncthreads();  // B1
+#pragma unroll
+  for (int i = 0; i < EXTRA; ++i) __syncthreads();
   if (state == kPeersReady) store_peer_tile(a, lane, v, pe);
   __syncthreads();  // B2
-  if (state == kBadOwnRow) return;
+  if (state != kMustWait) return;
   const uint32_t epoch = s_ctl[0];
-  __syncthreads();  // B3: the compute waves' slot stores completed before it
-  if (lane == 0) store_flag(flag_ptr(a, a.rank, tile), epoch);
-  if (state == kPeersReady) return;
-  const bool ok = wait_peers(a, lane, tile, epoch);
+  const bool ok = wait_peers(a, lane, tile, epoch);  // the own flag went out after B2
   if (ok) {
     issue_peer_tile(a, lane, tile, v);  // after the flags returned
     store_peer_tile(a, lane, v, pe);
   }
   if (lane == 0) s_ctl[1] = ok ? kPeersReady : kMustWait;
-  __syncthreads();  // B4
+  __syncthreads();  // B3
 }
 
 // out = ((0 + s_0) + s_1) ... + s_{W-1}; s_rank is this call's published y,
-// the others come from the peer tile in LDS (local row n, column b).
+// the others come from the peer tile in LDS (local row n, column b).  The W
+// peer values are read up front (indexes clamped into the tile) and ranks
+// r >= W add +0: the sum starts at +0 and a round-to-nearest sum is -0 only
+// if both terms are, so acc is never -0 and acc + 0 == acc exactly.
 __device__ __forceinline__ float one_shot_sum(const GemvArgs& a, float y, const float* pe, int n,
                                               int b) {
   const int tb = kTileRows * a.B;
+  const int idx = n * a.B + b;
+  float pv[kMaxW];
+#pragma unroll
+  for (int r = 0; r < kMaxW; ++r) pv[r] = pe[min(r, a.W - 1) * tb + idx];
   float acc = 0.0f;
 #pragma unroll
   for (int r = 0; r < kMaxW; ++r) {
-    if (r < a.W) acc = acc + (r == a.rank ? y : pe[r * tb + n * a.B + b]);
+    const float t = r == a.rank ? y : pv[r];
+    acc = acc + (r < a.W ? t : 0.0f);
   }
   return acc;
 }
 
-// Compute waves once their partials are final and barrier B2 has passed
-// (y[e] for local rows n[e], column b, owner lanes only): publish, (reduce),
-// B3, [B4, reduce].
+// Compute waves once y is final (y[e] for local rows n[e], column b; owner
+// lanes only), `state` being what the communication wave decided before B1:
+// publish y into slot[rank], B2, compute wave 0 releases the flag, [B3], out.
+// Every compute wave waits for its own slot stores to complete before B2, so
+// the flag store that follows B2 is ordered after all of them.
 template <int OPL>
-__device__ void finish_after_b2(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
-                                const bool (&live)[OPL], const float (&y)[OPL], const float* pe,
-                                const uint32_t* s_ctl) {
-  const uint32_t state = s_ctl[1];
-  if (state == kBadOwnRow) return;
+__device__ void publish_and_reduce(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
+                                   const bool (&live)[OPL], const float (&y)[OPL],
+                                   const float* pe, const uint32_t* s_ctl, uint32_t state,
+                                   bool flag_lane) {
   const int64_t NB = a.N * a.B;
   const int64_t row0 = tile * kTileRows;
   float* own_slot = a.slots + a.rank * NB;
-#pragma unroll
-  for (int e = 0; e < OPL; ++e)
-    if (live[e]) store_coherent(&own_slot[(row0 + n[e]) * a.B + b], y[e]);
-  if (state == kPeersReady) {
+  if (state != kBadOwnRow) {
 #pragma unroll
     for (int e = 0; e < OPL; ++e)
-      if (live[e]) a.out[(row0 + n[e]) * a.B + b] = one_shot_sum(a, y[e], pe, n[e], b);
+      if (live[e]) store_coherent(&own_slot[(row0 + n[e]) * a.B + b], y[e]);
   }
   wait_vm_all();    // the published values are at the coherence point ...
-  __syncthreads();  // B3 ... before the communication wave stores the flag
-  if (state == kPeersReady) return;
-  __syncthreads();  // B4
-  if (s_ctl[1] != kPeersReady) return;  // wait expired: this tile's out rows stay unwritten
+  __syncthreads();  // B2 ... in every compute wave
+  if (state == kBadOwnRow) return;
+  if (flag_lane) store_flag(flag_ptr(a, a.rank, tile), s_ctl[0]);
+  if (state == kMustWait) {
+    __syncthreads();  // B3
+    if (s_ctl[1] != kPeersReady) return;  // wait expired: this tile's out rows stay unwritten
+  }
 #pragma unroll
   for (int e = 0; e < OPL; ++e)
     if (live[e]) a.out[(row0 + n[e]) * a.B + b] = one_shot_sum(a, y[e], pe, n[e], b);
-}
-
-// MFMA epilogue: B2, wave 0 sums the compute waves' partials in wave order,
-// then publishes and reduces.
-template <int NW>
-__device__ void mfma_finish(const GemvArgs& a, int64_t tile, int wave, int lane,
-                            const int (&n)[4], int b, const bool (&live)[4], f32x4_t acc,
-                            const float* red, const float* pe, const uint32_t* s_ctl) {
-  __syncthreads();  // B2
-  float y[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) y[e] = acc[e];
-  if (wave == 0) {
-    for (int w = 1; w < NW; ++w) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = y[e] + red[((w - 1) * 4 + e) * 64 + lane];
-    }
-  }
-  finish_after_b2<4>(a, tile, n, b, live, y, pe, s_ctl);
 }
 
 // Sum of v over an aligned group of G lanes (G = 16, 32 or 64), returned in
@@ -412,7 +405,7 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   float* pe = reinterpret_cast<float*>(lds_x + xchunks + 2);
 
   if (wave == NW) {
-    comm_wave(a, lane, tile, pe, s_ctl);
+    comm_wave<0>(a, lane, tile, pe, s_ctl);
     return;
   }
 
@@ -445,6 +438,7 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   for (int idx = tid + XPT * NT; idx < xchunks; idx += NT) lds_x[idx] = xg[idx];
   if (tid == 0) lds_x[zidx] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();  // B1
+  const uint32_t state = s_ctl[1];
 
   float acc[R][B];
 #pragma unroll
@@ -465,9 +459,7 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   const int n[1] = {nloc0 + vidx / B};
   const bool live[1] = {li < V && tile * kTileRows + n[0] < a.N};
   const float y[1] = {yv};
-  asm volatile("" ::"v"(yv));  // keep the GEMV ahead of B2 (it overlaps the peer loads)
-  __syncthreads();  // B2
-  finish_after_b2<1>(a, tile, n, vidx % B, live, y, pe, s_ctl);
+  publish_and_reduce<1>(a, tile, n, vidx % B, live, y, pe, s_ctl, state, wave == 0 && lane == 0);
 }
 
 // A operand chunks of k-steps s0..s0+SPW-1 for MFMA lane l: row (l & 15),
@@ -517,9 +509,10 @@ __device__ __forceinline__ f32x4_t mfma_steps(uint4 (&av)[SPW], __amdgpu_buffer_
 // the signal-pad protocol.  Operand layout per lane l: A row (l & 15), B
 // column (l & 15), k-chunk (l >> 4) of the step's four 8-element chunks;
 // result rows 4*(l >> 4) + e, column (l & 15).
-// LDS: x [16][C + 1] chunks (column C zero); (NW-1) x 4 x 64 partials; peer tile.
+// LDS: x [16][C + 1] chunks (column C zero); NW 16 x 16 partials; peer tile.
 template <int NW, int SPW, int XC>
 __global__ __launch_bounds__((NW + 1) * 64) void gemv_ar_mfma(GemvArgs a) {
+  static_assert(NW * 4 == kTileRows, "each compute wave finishes 4 rows of the tile");
   constexpr int NT = NW * 64;
   extern __shared__ uint4 lds[];
   __shared__ uint32_t s_ctl[2];
@@ -531,10 +524,10 @@ __global__ __launch_bounds__((NW + 1) * 64) void gemv_ar_mfma(GemvArgs a) {
   const int C = a.C;
   const int CP = C + 1;  // padded LDS row: spreads the 16 batch rows over banks
   float* red = reinterpret_cast<float*>(lds + 16 * CP);
-  float* pe = red + (NW - 1) * 4 * 64;
+  float* pe = red + NW * kTileRows * 16;
 
   if (wave == NW) {
-    comm_wave(a, lane, tile, pe, s_ctl);
+    comm_wave<1>(a, lane, tile, pe, s_ctl);
     return;
   }
 
@@ -578,6 +571,7 @@ __global__ __launch_bounds__((NW + 1) * 64) void gemv_ar_mfma(GemvArgs a) {
   }
   if (tid < 16) lds[tid * CP + C] = make_uint4(0u, 0u, 0u, 0u);  // zero column
   __syncthreads();  // B1
+  const uint32_t state = s_ctl[1];
 
   const int xb = lane & 15;
   f32x4_t acc;
@@ -586,20 +580,22 @@ __global__ __launch_bounds__((NW + 1) * 64) void gemv_ar_mfma(GemvArgs a) {
   else
     acc = mfma_steps<false, SPW>(av, ra, voff, lds, CP, C, xb, kq, s_begin, s_end);
 
-  if (wave > 0) {
+  // Each wave's 16 x 16 partial goes to red[wave][n][b]; after the extra
+  // barrier wave w sums rows 4w .. 4w+3 over the waves in wave order (lane l:
+  // row 4w + (l >> 4), column l & 15) and publishes them.
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[((wave - 1) * 4 + e) * 64 + lane] = acc[e];
-  }
-  // B2 is inside compute_wave_finish; wave 0 reads the other partials after it.
-  const int b_own = min(lane & 15, a.B - 1);
-  int n[4];
-  bool live[4];
+  for (int e = 0; e < 4; ++e)
+    red[(wave * kTileRows + 4 * (lane >> 4) + e) * 16 + (lane & 15)] = acc[e];
+  __syncthreads();  // the extra barrier: every partial in LDS
+  const int nl = 4 * wave + (lane >> 4);
+  const int bl = lane & 15;
+  float y = red[nl * 16 + bl];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    n[e] = 4 * (lane >> 4) + e;
-    live[e] = wave == 0 && (lane & 15) < a.B && row0 + n[e] < a.N;
-  }
-  mfma_finish<NW>(a, tile, wave, lane, n, b_own, live, acc, red, pe, s_ctl);
+  for (int w = 1; w < NW; ++w) y = y + red[(w * kTileRows + nl) * 16 + bl];
+  const int n[1] = {nl};
+  const bool live[1] = {bl < a.B && row0 + nl < a.N};
+  const float yv[1] = {y};
+  publish_and_reduce<1>(a, tile, n, bl, live, yv, pe, s_ctl, state, wave == 0 && lane == 0);
 }
 
 __global__ void pad_reset_kernel(uint32_t* pad, int W, int row_stride, uint32_t mask) {
@@ -660,7 +656,7 @@ ValuChoice valu_kernel(int C) {
 size_t gemv_lds_bytes(int W, int B, int C) {
   const size_t peer_tile = ((size_t)W * kTileRows * B + 1) * sizeof(float);
   if (B <= 8) return ((size_t)B * C + 2) * 16 + peer_tile;
-  return (size_t)16 * (C + 1) * 16 + (size_t)(kMfmaWaves - 1) * 4 * 64 * sizeof(float) +
+  return (size_t)16 * (C + 1) * 16 + (size_t)kMfmaWaves * kTileRows * 16 * sizeof(float) +
          peer_tile;
 }
 
