@@ -67,15 +67,17 @@ __device__ __forceinline__ float dot8(const uint4& a, const uint4& x, float acc)
   return acc;
 }
 
-// Buffer resource over `bytes` bytes at `base` (raw, stride 0).  Loads past
-// the end return zeros instead of faulting.
+// Buffer resource over `bytes` bytes at `base` (raw, stride 0).  A load whose
+// per-lane offset is past the end returns zeros instead of touching memory.
+// The range check does not cover the uniform (SGPR) offset, so every offset
+// below goes into the per-lane one.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
-// 16 bytes at byte offset voff + soff (voff per lane, soff uniform).
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+// 16 bytes at byte offset off (per lane, range-checked).
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -203,13 +205,12 @@ __device__ bool wait_peers(const GemvArgs& a, int lane, int64_t tile, uint32_t e
 // goes out before the compute waves' x and A loads (barrier B0); the peer
 // loads it issues once the flags are back return right behind the A stream.
 // Barrier schedule shared with the compute waves:
-//   B0 flag load issued | B1 x staged, decision in s_ctl | EXTRA barriers of
-//   the compute waves' own | B2 own slot published, and the peer tile in LDS
-//   if the peers were ready at the start (compute wave 0 then stores the
-//   flag) | B3 (only if they were not) late peer tile in LDS.
+//   B0 flag load issued | B1 decision in s_ctl (the VALU kernels: x staged;
+//   the MFMA kernels: per-wave partials in LDS) | B2 own slot published, and
+//   the peer tile in LDS if the peers were ready at the start (compute wave 0
+//   then stores the flag) | B3 (only if they were not) late peer tile in LDS.
 // The peer loads stay in flight across B1: a workgroup barrier does not wait
 // for outstanding global loads.
-template <int EXTRA>
 __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
                           uint32_t* s_ctl) {
   const uint32_t fl = load_flag(a, lane, tile);
@@ -218,8 +219,6 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
   float v[kMaxW][kPerLane];
   if (state == kPeersReady) issue_peer_tile(a, lane, tile, v);  // after the flags returned
   __syncthreads();  // B1
-#pragma unroll
-  for (int i = 0; i < EXTRA; ++i) __syncthreads();
   if (state == kPeersReady) store_peer_tile(a, lane, v, pe);
   __syncthreads();  // B2
   if (state != kMustWait) return;
@@ -318,14 +317,15 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 // One A chunk (16 bytes) of each of the lane's R rows, at byte offset
-// voff[s] + soff, through the buffer resource over A.  Rows past N read
-// zeros; chunks past a row's end read the next row's data, which mac_chunk
-// pairs with a zero x chunk (A is finite), so no load is masked.
+// voff[s] + soff, through the buffer resource over A.  Rows past N, and the
+// last row's chunks past the end of A, read zeros; other chunks past a row's
+// end read the next row's data, which mac_chunk pairs with a zero x chunk (A
+// is finite), so no load is masked.
 template <int R>
 __device__ __forceinline__ void load_chunk(uint4 (&av)[R], __amdgpu_buffer_rsrc_t ra,
                                            const uint32_t (&voff)[R], uint32_t soff) {
 #pragma unroll
-  for (int s = 0; s < R; ++s) av[s] = buf_load16(ra, voff[s], soff);
+  for (int s = 0; s < R; ++s) av[s] = buf_load16(ra, voff[s] + soff);
 }
 
 // acc[s][b] += <A chunk of row s, x chunk c of batch b>.  x chunks live at
@@ -405,7 +405,7 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   float* pe = reinterpret_cast<float*>(lds_x + xchunks + 2);
 
   if (wave == NW) {
-    comm_wave<0>(a, lane, tile, pe, s_ctl);
+    comm_wave(a, lane, tile, pe, s_ctl);
     return;
   }
 
@@ -462,58 +462,54 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   publish_and_reduce<1>(a, tile, n, vidx % B, live, y, pe, s_ctl, state, wave == 0 && lane == 0);
 }
 
-// A operand chunks of k-steps s0..s0+SPW-1 for MFMA lane l: row (l & 15),
-// chunk 4 * step + (l >> 4); voff is the byte offset of that chunk at step 0.
-// Out-of-row and past-the-end chunks are harmless (see load_a); mfma_pass
-// pairs steps past s_end and chunks past the row with the zero x column.
-template <int SPW>
-__device__ __forceinline__ void load_a_mfma(uint4 (&av)[SPW], __amdgpu_buffer_rsrc_t ra,
-                                            uint32_t voff, int s0) {
+// MFMA epilogue: each wave's 16 x 16 partial goes to red[wave][n][b]; after
+// B1 wave w sums rows 4w .. 4w+3 over the waves in wave order (lane l: row
+// 4w + (l >> 4), column l & 15), publishes them and reduces.
+template <int NW>
+__device__ __forceinline__ void mfma_finish(const GemvArgs& a, int64_t tile, int wave, int lane,
+                                            f32x4_t acc, float* red, const float* pe,
+                                            const uint32_t* s_ctl) {
 #pragma unroll
-  for (int u = 0; u < SPW; ++u) av[u] = buf_load16(ra, voff, (uint32_t)(s0 + u) * 64u);
+  for (int e = 0; e < 4; ++e)
+    red[(wave * kTileRows + 4 * (lane >> 4) + e) * 16 + (lane & 15)] = acc[e];
+  __syncthreads();  // B1: every partial in LDS, the decision in s_ctl
+  const uint32_t state = s_ctl[1];
+  const int nl = 4 * wave + (lane >> 4);
+  const int bl = lane & 15;
+  float y = red[nl * 16 + bl];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) y = y + red[(w * kTileRows + nl) * 16 + bl];
+  const int n[1] = {nl};
+  const bool live[1] = {bl < a.B && tile * kTileRows + nl < a.N};
+  const float yv[1] = {y};
+  publish_and_reduce<1>(a, tile, n, bl, live, yv, pe, s_ctl, state, wave == 0 && lane == 0);
 }
 
-// x chunk (batch xb, chunk c) at lds[xb * CP + c]; column C of every batch
-// row is zero.
-template <bool MASKED, int SPW>
-__device__ __forceinline__ f32x4_t mfma_pass(f32x4_t acc, const uint4 (&av)[SPW],
-                                             const uint4* lds, int CP, int C, int xb, int kq,
-                                             int s0, int s_end) {
-#pragma unroll
-  for (int u = 0; u < SPW; ++u) {
-    const int chunk = 4 * (s0 + u) + kq;
-    const int cc = MASKED ? ((s0 + u < s_end && chunk < C) ? chunk : C) : chunk;
-    const uint4 xv = lds[xb * CP + cc];
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[u]),
-                                                  __builtin_bit_cast(bf16x8_t, xv), acc, 0, 0, 0);
-  }
-  return acc;
-}
-
-template <bool MASKED, int SPW>
-__device__ __forceinline__ f32x4_t mfma_steps(uint4 (&av)[SPW], __amdgpu_buffer_rsrc_t ra,
-                                              uint32_t voff, const uint4* lds, int CP, int C,
-                                              int xb, int kq, int s_begin, int s_end) {
-  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int s0 = s_begin; s0 < s_end; s0 += SPW) {
-    if (s0 != s_begin) load_a_mfma<SPW>(av, ra, voff, s0);
-    acc = mfma_pass<MASKED, SPW>(acc, av, lds, CP, C, xb, kq, s0, s_end);
-  }
-  return acc;
+// Copy 16 bytes per active lane from global memory straight into LDS: lane l
+// writes lds_base + 16 * l (lds_base is wave-uniform).  Completion is counted
+// by vmcnt like any other vector load.
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(
+      (const void __attribute__((address_space(1)))*)src,
+      (void __attribute__((address_space(3)))*)lds_base, 16, 0, 0);
 }
 
 // MFMA path, 8 < B <= 16 (batch padded to 16 with zeros).  The tile's 16 rows
 // form the A operand of v_mfma_f32_16x16x32_bf16, x (16 batches x 32 k) the
-// B operand from LDS.  The NW compute waves split the k-steps; their 16x16
-// fp32 partials are summed in wave order through LDS.  One more wave runs
-// the signal-pad protocol.  Operand layout per lane l: A row (l & 15), B
-// column (l & 15), k-chunk (l >> 4) of the step's four 8-element chunks;
-// result rows 4*(l >> 4) + e, column (l & 15).
+// B operand from LDS.  The NW compute waves split the k-steps (32 k each).
+// Each wave copies the x columns of its own k-steps from memory straight
+// into LDS (no registers, no barrier: it waits for its own copies), then
+// streams its A chunks with D steps in flight per lane.  Operand layout per
+// lane l: A row (l & 15), B column (l & 15), k-chunk (l >> 4) of the step's
+// four 8-element chunks; result rows 4*(l >> 4) + e, column (l & 15).  x
+// chunks past a row's end come from the zero column C, batch rows >= B are
+// zero; A chunks there read other data or zeros, which meet those zeros (A
+// is finite).  The per-wave 16 x 16 fp32 partials are summed in wave order
+// through LDS.  One more wave runs the signal-pad protocol.
 // LDS: x [16][C + 1] chunks (column C zero); NW 16 x 16 partials; peer tile.
-template <int NW, int SPW, int XC>
-__global__ __launch_bounds__((NW + 1) * 64) void gemv_ar_mfma(GemvArgs a) {
+template <int NW, int D>
+__global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs a) {
   static_assert(NW * 4 == kTileRows, "each compute wave finishes 4 rows of the tile");
-  constexpr int NT = NW * 64;
   extern __shared__ uint4 lds[];
   __shared__ uint32_t s_ctl[2];
 
@@ -522,12 +518,12 @@ __global__ __launch_bounds__((NW + 1) * 64) void gemv_ar_mfma(GemvArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t tile = blockIdx.x;
   const int C = a.C;
-  const int CP = C + 1;  // padded LDS row: spreads the 16 batch rows over banks
+  const int CP = C + 1;  // padded LDS row: the 16 batch rows of one chunk hit distinct banks
   float* red = reinterpret_cast<float*>(lds + 16 * CP);
   float* pe = red + NW * kTileRows * 16;
 
   if (wave == NW) {
-    comm_wave<1>(a, lane, tile, pe, s_ctl);
+    comm_wave(a, lane, tile, pe, s_ctl);
     return;
   }
 
@@ -535,67 +531,143 @@ __global__ __launch_bounds__((NW + 1) * 64) void gemv_ar_mfma(GemvArgs a) {
   const int steps = (C + 3) / 4;
   const int per_wave = (steps + NW - 1) / NW;
   const int s_begin = wave * per_wave;
-  const int s_end = min(steps, s_begin + per_wave);
-  const bool masked = (C % 4) != 0 || (steps % NW) != 0 || (per_wave % SPW) != 0;
+  const int n_steps = max(0, min(steps, s_begin + per_wave) - s_begin);
+  // This wave's chunks of every row: [c_begin, c_end), all < C.
+  const int c_begin = min(4 * s_begin, C);
+  const int c_end = min(4 * (s_begin + n_steps), C);
 
-  const uint4* xg = reinterpret_cast<const uint4*>(a.x);
   __syncthreads();  // B0
-  uint4 xr[XC][16];
+  // x columns [c_begin, c_end) of batch rows < B, 64 chunks per copy.
+  const uint4* xg = reinterpret_cast<const uint4*>(a.x);
+  for (int c0 = c_begin; c0 < c_end; c0 += 64) {
+    if (c0 + lane < c_end) {
+      for (int b = 0; b < a.B; ++b) lds_dma16(xg + (int64_t)b * C + c0 + lane, lds + b * CP + c0);
+    }
+  }
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, (uint32_t)(a.N * C * 16));
+  const int kq = lane >> 4;
+  const uint32_t a_row = ((uint32_t)(row0 + (lane & 15)) * (uint32_t)C + kq) * 16u;
+  const uint32_t kOutOfRange = 0x80000000u;  // past any A buffer: reads zeros
+  // A chunk of the wave's step j; steps past n_steps read zeros.  Every load
+  // is issued unconditionally, so the outstanding-load counts are static.
+  auto a_off = [&](int j) {
+    return j < n_steps ? a_row + (uint32_t)(s_begin + j) * 64u : kOutOfRange;
+  };
+  uint4 ring[D];
 #pragma unroll
-  for (int i = 0; i < XC; ++i) {
-    const int c = min(tid + i * NT, C - 1);
+  for (int u = 0; u < D; ++u) ring[u] = buf_load16(ra, a_off(u));
+  // This wave's x copies were issued before its D ring loads: once at most D
+  // loads are outstanding they have landed, before any other LDS access.
+  wait_vm_le<D>();
+  // Zeros this wave's steps may read: batch rows >= B and the column C.
+  for (int c = c_begin + lane; c < c_end; c += 64)
+    for (int b = a.B; b < 16; ++b) lds[b * CP + c] = make_uint4(0u, 0u, 0u, 0u);
+  if (lane < 16) lds[lane * CP + C] = make_uint4(0u, 0u, 0u, 0u);
+
+  // Whole blocks of D steps; a step past n_steps multiplies zeros from A by
+  // the zero column of x and adds +0 to an accumulator that is never -0.
+  // A block first reads its D x chunks from LDS, then each step runs its
+  // MFMA and refills its ring slot, in that order (the scheduling barrier
+  // keeps each refill next to its MFMA instead of letting a block's refills
+  // sink to its end).
+  const int xrow = (lane & 15) * CP;
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j0 = 0; j0 < n_steps; j0 += D) {
+    uint4 xv[D];
 #pragma unroll
-    for (int b = 0; b < 16; ++b) {
-      uint4 v = xg[min(b, a.B - 1) * C + c];
-      if (b >= a.B) v = make_uint4(0u, 0u, 0u, 0u);
-      xr[i][b] = v;
+    for (int u = 0; u < D; ++u) {
+      const int j = j0 + u;
+      const int chunk = 4 * (s_begin + j) + kq;
+      xv[u] = lds[xrow + (j < n_steps && chunk < C ? chunk : C)];
+    }
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ring[u]),
+                                                    __builtin_bit_cast(bf16x8_t, xv[u]), acc, 0,
+                                                    0, 0);
+      ring[u] = buf_load16(ra, a_off(j0 + u + D));
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
+  mfma_finish<NW>(a, tile, wave, lane, acc, red, pe, s_ctl);
+}
+
+// MFMA path for x beyond the LDS bound (8 < B <= 16, 16 * (C + 1) chunks over
+// GSA_MAX_X_LDS_BYTES): as gemv_ar_mfma, but the B operand is read from
+// memory (x stays in L2; rows >= B and chunks past a row's end read zeros
+// through out-of-range offsets), streamed with A, D steps in flight.  The
+// wave's steps start at a rotation that differs between the workgroups of
+// one XCD so that they do not all read the same lines of x at once.
+// LDS: NW 16 x 16 partials, then the peer tile.
+template <int NW, int D>
+__global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a) {
+  static_assert(NW * 4 == kTileRows, "each compute wave finishes 4 rows of the tile");
+  extern __shared__ uint4 lds[];
+  __shared__ uint32_t s_ctl[2];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t tile = blockIdx.x;
+  const int C = a.C;
+  float* red = reinterpret_cast<float*>(lds);
+  float* pe = red + NW * kTileRows * 16;
+
+  if (wave == NW) {
+    comm_wave(a, lane, tile, pe, s_ctl);
+    return;
+  }
+
+  const int64_t row0 = tile * kTileRows;
+  const int steps = (C + 3) / 4;
+  const int per_wave = (steps + NW - 1) / NW;
+  const int s_begin = wave * per_wave;
+  const int n_steps = max(0, min(steps, s_begin + per_wave) - s_begin);
+  const int rot = n_steps > 0 ? (int)((tile >> 3) % n_steps) : 0;
+
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, (uint32_t)(a.N * C * 16));
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(a.B * C * 16));
   const int kq = lane >> 4;
-  const uint32_t voff = ((uint32_t)(row0 + (lane & 15)) * (uint32_t)C + kq) * 16u;
-  uint4 av[SPW];
-  load_a_mfma<SPW>(av, ra, voff, s_begin);
+  const int l16 = lane & 15;
+  const uint32_t a_row = ((uint32_t)(row0 + l16) * (uint32_t)C + kq) * 16u;
+  const uint32_t x_row = ((uint32_t)l16 * (uint32_t)C + kq) * 16u;  // past x for l16 >= B
+  const uint32_t kOutOfRange = 0x80000000u;
+  // The wave's j-th step in its rotated order; steps past n_steps read zeros.
+  auto step_of = [&](int j) {
+    const int p = j + rot;
+    return s_begin + (p >= n_steps ? p - n_steps : p);
+  };
+  auto a_off = [&](int j) {
+    return j < n_steps ? a_row + (uint32_t)step_of(j) * 64u : kOutOfRange;
+  };
+  auto x_off = [&](int j) {
+    if (j >= n_steps) return kOutOfRange;
+    const int st = step_of(j);
+    return 4 * st + kq < C ? x_row + (uint32_t)st * 64u : kOutOfRange;
+  };
 
+  __syncthreads();  // B0
+  uint4 ra_ring[D], rx_ring[D];
 #pragma unroll
-  for (int i = 0; i < XC; ++i) {
-    const int c = tid + i * NT;
-    if (c >= C) continue;
-#pragma unroll
-    for (int b = 0; b < 16; ++b) lds[b * CP + c] = xr[i][b];
+  for (int u = 0; u < D; ++u) {
+    ra_ring[u] = buf_load16(ra, a_off(u));
+    rx_ring[u] = buf_load16(rx, x_off(u));
   }
-  for (int c = tid + XC * NT; c < C; c += NT) {
-    for (int b = 0; b < 16; ++b)
-      lds[b * CP + c] = b < a.B ? xg[b * C + c] : make_uint4(0u, 0u, 0u, 0u);
+
+  f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j0 = 0; j0 < n_steps; j0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ra_ring[u]),
+                                                    __builtin_bit_cast(bf16x8_t, rx_ring[u]),
+                                                    acc, 0, 0, 0);
+      ra_ring[u] = buf_load16(ra, a_off(j0 + u + D));
+      rx_ring[u] = buf_load16(rx, x_off(j0 + u + D));
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  if (tid < 16) lds[tid * CP + C] = make_uint4(0u, 0u, 0u, 0u);  // zero column
-  __syncthreads();  // B1
-  const uint32_t state = s_ctl[1];
-
-  const int xb = lane & 15;
-  f32x4_t acc;
-  if (masked)
-    acc = mfma_steps<true, SPW>(av, ra, voff, lds, CP, C, xb, kq, s_begin, s_end);
-  else
-    acc = mfma_steps<false, SPW>(av, ra, voff, lds, CP, C, xb, kq, s_begin, s_end);
-
-  // Each wave's 16 x 16 partial goes to red[wave][n][b]; after the extra
-  // barrier wave w sums rows 4w .. 4w+3 over the waves in wave order (lane l:
-  // row 4w + (l >> 4), column l & 15) and publishes them.
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-    red[(wave * kTileRows + 4 * (lane >> 4) + e) * 16 + (lane & 15)] = acc[e];
-  __syncthreads();  // the extra barrier: every partial in LDS
-  const int nl = 4 * wave + (lane >> 4);
-  const int bl = lane & 15;
-  float y = red[nl * 16 + bl];
-#pragma unroll
-  for (int w = 1; w < NW; ++w) y = y + red[(w * kTileRows + nl) * 16 + bl];
-  const int n[1] = {nl};
-  const bool live[1] = {bl < a.B && row0 + nl < a.N};
-  const float yv[1] = {y};
-  publish_and_reduce<1>(a, tile, n, bl, live, yv, pe, s_ctl, state, wave == 0 && lane == 0);
+  mfma_finish<NW>(a, tile, wave, lane, acc, red, pe, s_ctl);
 }
 
 __global__ void pad_reset_kernel(uint32_t* pad, int W, int row_stride, uint32_t mask) {
@@ -613,6 +685,9 @@ __global__ void pad_reset_kernel(uint32_t* pad, int W, int row_stride, uint32_t 
 }
 
 constexpr int kMfmaWaves = 4;
+
+// Whether the MFMA path stages x ([16][C + 1] chunks) in LDS.
+bool mfma_x_in_lds(int C) { return (size_t)16 * (C + 1) * 16 <= GSA_MAX_X_LDS_BYTES; }
 
 struct ValuChoice {
   const void* kernel;
@@ -655,15 +730,15 @@ ValuChoice valu_kernel(int C) {
 
 size_t gemv_lds_bytes(int W, int B, int C) {
   const size_t peer_tile = ((size_t)W * kTileRows * B + 1) * sizeof(float);
+  const size_t partials = (size_t)kMfmaWaves * kTileRows * 16 * sizeof(float);
   if (B <= 8) return ((size_t)B * C + 2) * 16 + peer_tile;
-  return (size_t)16 * (C + 1) * 16 + (size_t)kMfmaWaves * kTileRows * 16 * sizeof(float) +
-         peer_tile;
+  if (mfma_x_in_lds(C)) return (size_t)16 * (C + 1) * 16 + partials + peer_tile;
+  return partials + peer_tile;
 }
 
 bool select_gemv_kernel(int W, int B, int C, Launch* out) {
   if (W < 1 || W > GSA_MAX_W || B < 1 || B > GSA_MAX_B || C < 1) return false;
-  const size_t x_bytes = B <= 8 ? (size_t)B * C * 16 : (size_t)16 * (C + 1) * 16;
-  if (x_bytes > GSA_MAX_X_LDS_BYTES) return false;
+  if (B <= 8 && (size_t)B * C * 16 > GSA_MAX_X_LDS_BYTES) return false;  // x staged in LDS
   ValuChoice k{nullptr, kMfmaWaves};
   switch (B) {
     case 1: k = valu_kernel<1>(C); break;
@@ -675,7 +750,10 @@ bool select_gemv_kernel(int W, int B, int C, Launch* out) {
     case 7: k = valu_kernel<7>(C); break;
     case 8: k = valu_kernel<8>(C); break;
     default:
-      k = {reinterpret_cast<const void*>(&gemv_ar_mfma<kMfmaWaves, 16, 1>), kMfmaWaves};
+      k = mfma_x_in_lds(C)
+              ? ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma<kMfmaWaves, 8>), kMfmaWaves}
+              : ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma_xmem<kMfmaWaves, 8>),
+                           kMfmaWaves};
       break;
   }
   const unsigned block = (unsigned)(k.waves + 1) * 64;

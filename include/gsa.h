@@ -63,8 +63,9 @@ extern "C" {
 #define GSA_PAD_HEADER_WORDS 16
 #define GSA_MAX_W 8
 #define GSA_MAX_B 16
-/* Bytes of x staged in LDS per workgroup (B*K/W*2, with B rounded up to 16
- * when B > 8 and one 16-byte pad per batch row) may not exceed this. */
+/* For B <= 8 every workgroup stages x in LDS: B*K/W*2 bytes may not exceed
+ * this.  For B > 8 x is staged in LDS (16 batch rows of K/W*2 + 16 bytes)
+ * when that fits under this bound and read from memory otherwise. */
 #define GSA_MAX_X_LDS_BYTES (128 * 1024)
 
 typedef struct gsa_symm gsa_symm; /* opaque host-side handle */
@@ -109,8 +110,9 @@ int gsa_signal_pad_reset(uint32_t *pad, int W, int64_t N, uint32_t published_mas
  *   out   [device] fp32 N x B (n-major); any device memory, written only
  * Requires 1 <= W <= 8, 0 <= rank < W, K % W == 0, Ks % 8 == 0, N >= 1,
  * 1 <= B <= 16, N * Ks * 2 < 2^31 (A_r is addressed with 32-bit offsets),
- * every pointer non-null and 16-byte aligned, and the x staging bound
- * GSA_MAX_X_LDS_BYTES; otherwise GSA_EINVAL and nothing is launched.
+ * every pointer non-null and 16-byte aligned, and, for B <= 8 (x staged in
+ * LDS), B * Ks * 2 <= GSA_MAX_X_LDS_BYTES; otherwise GSA_EINVAL and nothing
+ * is launched.
  * A_r must hold finite values (chunks past a row's end are paired with zeros).
  * No host sync, no allocation.  All calls on one buffer must use one stream
  * (flags are indexed by tile, not by stream).  Each tile's flag epoch is its

@@ -79,7 +79,7 @@ P = 0x10000  # a 16-byte-aligned fake address: never dereferenced, rejected firs
     (P, P, P, P, 0, 2, 0, 16, 64, 1),       # null out
     (P + 4, P, P, P, P, 2, 0, 16, 64, 1),   # misaligned A
     (P, P + 8, P, P, P, 2, 0, 16, 64, 1),   # misaligned x
-    (P, P, P, P, P, 1, 0, 16, 8 * 8193, 16),  # x staging beyond the LDS bound
+    (P, P, P, P, P, 1, 0, 16, 8 * 8193, 8),   # B <= 8: x staging beyond the LDS bound
     (P, P, P, P, P, 2, 0, 16, 64, 1),       # slots not from gsa_symm_alloc
 ])
 def test_gemv_allreduce_rejects_bad_arguments(args):

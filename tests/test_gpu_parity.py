@@ -42,6 +42,9 @@ EDGE = [
     (2, 16, 8, 16, 0),        # MFMA, single chunk
     (8, 128, 4000, 12, 5),    # MFMA multi-pass, masked
     (1, 70, 256, 16, 0),      # MFMA, W = 1
+    (2, 32, 8192, 16, 1),     # MFMA, x 256 KB (read from memory, not staged)
+    (8, 40, 65536, 12, 3),    # MFMA, 1.5 MB of x, ragged N
+    (4, 24, 72, 10, 0),       # MFMA, C = 9: fewer k-steps than waves
     (8, 4096, 512, 6, 4),     # short tier, B = 6
     (8, 300, 1024, 7, 6),     # long tier, B = 7
 ]
