@@ -8,9 +8,12 @@ from the 256 MB Infinity Cache.
 The timed region replays a HIP graph of K calls (the way a decode loop issues
 them), bracketed by HIP events on the launch stream: the mean launch duration
 is the µs/call value and the denominator of the roofline figure (kernels of
-a graph run back to back, so this matches the kernel trace).  An eager pass
-of host-issued launches is reported beside it.  The CPU oracle is timed on a
-bounded sample of the same workload.
+a graph run back to back, so this matches the kernel trace).  Reported beside
+it: an eager pass of host-issued launches, a warm pass over one resident set
+(Infinity-Cache resident, not HBM), and the HBM read bandwidth a plain
+streaming-read kernel achieves over 1 GiB on the same GPU.  The CPU oracle
+is timed on a bounded sample of the same workload, on one thread and on all
+host cores (whole calls in parallel threads).
 
 Prints one JSON line (rank 0, N = 1).
 """
@@ -125,20 +128,91 @@ def check_parity(d, sets):
     return ok, float(np.max(np.abs(out0 - out64) / bnd))
 
 
-def time_cpu_oracle(d, seconds):
-    """The oracle as it stands, single-threaded, on whole calls of the same
-    workload, for about `seconds` of CPU time.  Returns (µs per call, calls)."""
+def time_cpu_oracle(d, seconds, threads=1):
+    """The oracle as it stands, on whole calls of the same workload, for about
+    `seconds` of wall time on `threads` threads (each runs whole calls; the
+    C oracle runs without the Python lock).  Returns (wall µs per call,
+    calls)."""
+    import threading
+
     import oracle
     o = oracle.load()
     t0 = time.perf_counter()
     o.gemv_allreduce(d["A"], d["x"], d["slots"], d["rank"])
     one = time.perf_counter() - t0
-    n = max(1, int(seconds / max(one, 1e-6)))
+    n = max(1, int(seconds / max(one, 1e-6)))  # calls per thread
+    def work():
+        for _ in range(n):
+            o.gemv_allreduce(d["A"], d["x"], d["slots"], d["rank"])
+    ts = [threading.Thread(target=work) for _ in range(threads)]
     t0 = time.perf_counter()
-    for _ in range(n):
-        o.gemv_allreduce(d["A"], d["x"], d["slots"], d["rank"])
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
     el = time.perf_counter() - t0
-    return 1e6 * el / n, n
+    return 1e6 * el / (n * threads), n * threads
+
+
+def host_threads():
+    """Threads the host offers this process (at most 16, the CPU share of one
+    GPU on a shared node)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def hbm_read_probe(gib=1, launches=20):
+    """Best HBM read bandwidth (GB/s) of the plain streaming-read kernel of
+    libgsa_probe.so over `gib` GiB, over a few grid sizes."""
+    import ctypes
+
+    import torch
+
+    from gemv_shot_all_amd import build as gbuild
+    if not os.path.exists(gbuild.PROBE_LIBRARY):
+        return None
+    L = ctypes.CDLL(gbuild.PROBE_LIBRARY)
+    L.gsa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                 ctypes.c_int, ctypes.c_void_p]
+    L.gsa_probe_read.restype = ctypes.c_int
+    nbytes = gib << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = None
+    for grid in (1024, 2048, 4096, 8192):
+        def launch():
+            rc = L.gsa_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid,
+                                  ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"gsa_probe_read: {rc}")
+        launch()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(launches):
+            launch()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        gbps = nbytes * launches / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+        best = gbps if best is None else max(best, gbps)
+    del buf, sink
+    return round(best, 1)
 
 
 def run_config(cfg, args):
@@ -187,6 +261,22 @@ def run_config(cfg, args):
         # The graph replays left every set in the same, correct state.
         parity_after, _ = check_parity(d, sets)
         parity_ok = parity_ok and parity_after
+
+        # Warm: the same number of calls on set 0 only (its inputs stay in
+        # the Infinity Cache and L2): not HBM, reported for reference.
+        gw = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(gw, stream=cap):
+                for _ in range(args.steps):
+                    sets.call(0)
+        gw.replay()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        gw.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        warm_us = 1e3 * ev0.elapsed_time(ev1) / args.steps
+        del g, gw
     finally:
         sets.close()
 
@@ -223,17 +313,23 @@ def run_config(cfg, args):
         "extra": {
             "wall_us_per_call": round(wall_us, 4),
             "eager_us_per_call": round(eager_us, 4),
+            "warm_us_per_call": round(warm_us, 4),
             "parity_ok": parity_ok,
             "max_err_over_bound": err_ratio,
             "alg_flops_per_call": alg_flops(W, N, K, B),
         },
     }
     if args.cpu_seconds > 0:
-        cpu_us, ncalls = time_cpu_oracle(d, args.cpu_seconds)
+        threads = host_threads()
+        st_us, st_calls = time_cpu_oracle(d, args.cpu_seconds / 2, threads=1)
+        mt_us, mt_calls = time_cpu_oracle(d, args.cpu_seconds / 2, threads=threads)
         line["cpu_baseline"] = {
-            "value": round(cpu_us, 2), "unit": "us/call", "cores": 1, "kind": "oracle",
-            "sample": f"{ncalls} whole calls of the {cfg} workload (fp64, single thread), "
-                      f"host {os.cpu_count()} logical CPUs",
+            "value": round(mt_us, 2), "unit": "us/call", "cores": threads, "kind": "oracle",
+            "sample": f"{mt_calls} whole calls of the {cfg} workload (fp64) on {threads} "
+                      f"threads in parallel, wall time per call; host: {os.cpu_count()} "
+                      f"logical CPUs, {cpu_model()}",
+            "single_thread_us_per_call": round(st_us, 2),
+            "single_thread_calls": st_calls,
         }
     else:
         line["cpu_baseline"] = None
@@ -252,8 +348,11 @@ def main():
                    help="total size of the rotated input sets (MiB)")
     p.add_argument("--max-sets", type=int, default=None)
     p.add_argument("--warm", action="store_true", help="one resident set (cache-warm)")
-    p.add_argument("--cpu-seconds", type=float, default=10.0,
-                   help="CPU-oracle timing budget (0 = skip)")
+    p.add_argument("--cpu-seconds", type=float, default=20.0,
+                   help="CPU-oracle wall-time budget, split between one thread and all "
+                        "host threads (0 = skip)")
+    p.add_argument("--no-probe", action="store_true",
+                   help="skip the 1 GiB streaming-read bandwidth reference")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB five times "
                         "(reference kernel for scaling HBM byte counters)")
@@ -277,9 +376,12 @@ def main():
             torch.mul(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    probe = hbm_read_probe() if not args.no_probe else None
     cfgs = list(gi.CONFIGS) if args.all else [args.config]
     for cfg in cfgs:
-        print(json.dumps(run_config(cfg, args)), flush=True)
+        line = run_config(cfg, args)
+        line["extra"]["hbm_read_probe_GBps"] = probe
+        print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

@@ -13,6 +13,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libgsa.so")
 SOURCES = ["gsa_api.hip", "gemv_allreduce.hip"]
+# The benchmark's achievable-bandwidth reference (include/gsa_probe.h).
+PROBE_LIBRARY = os.path.join(PKG, "libgsa_probe.so")
+PROBE_SOURCES = ["hbm_read_probe.hip"]
 ARCH = os.environ.get("GSA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [
@@ -26,15 +29,20 @@ def sources():
     return [os.path.join(CSRC, s) for s in SOURCES]
 
 
-def build(output=LIBRARY, extra_flags=()):
-    """Compile every HIP source into `output`; returns its path."""
+def _compile(srcs, output, extra_flags=()):
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     tmp = output + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC,
-           *sources(), "-o", tmp]
+    cmd = [hipcc, *HIPCC_FLAGS, *extra_flags, "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
     subprocess.run(cmd, check=True)
     os.replace(tmp, output)
     return output
+
+
+def build(output=LIBRARY, extra_flags=()):
+    """Compile the operator's HIP sources into `output` (and the benchmark's
+    read probe into its own library); returns the operator library's path."""
+    _compile([os.path.join(CSRC, s) for s in PROBE_SOURCES], PROBE_LIBRARY, extra_flags)
+    return _compile(sources(), output, extra_flags)
 
 
 def needs_build():

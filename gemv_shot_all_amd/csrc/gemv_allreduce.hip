@@ -722,7 +722,7 @@ ValuChoice valu_tier(int C) {
 template <int B>
 ValuChoice valu_kernel(int C) {
   if (C <= 64) return valu_tier<B, 64, 4, 4, 1, 1, 1>(C);
-  if (C <= 224) return valu_tier<B, 32, 2, 4, 7, 3, 1>(C);
+  if (C <= 224) return valu_tier<B, 32, 2, 4, 7, 4, 1>(C);
   return valu_tier<B, 64, 2, 8, 7, 3, 5>(C);
 }
 

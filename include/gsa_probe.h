@@ -1,0 +1,33 @@
+/* gsa_probe.h -- a measurement aid, not part of the operator.
+ *
+ * libgsa_probe.so holds one plain streaming-read kernel.  The benchmark runs
+ * it over >= 1 GiB of device memory to report the HBM read bandwidth a simple
+ * kernel achieves on the same GPU, beside the 8 TB/s datasheet peak that the
+ * operator's roofline figure is taken against.  It computes nothing the
+ * operator needs.
+ */
+#ifndef GSA_PROBE_H
+#define GSA_PROBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Read `bytes` bytes at device pointer `src` (16-byte aligned, bytes a
+ * multiple of 16, bytes / 16 < 2^31) with 128-bit loads, `grid` workgroups
+ * of 256 threads in a grid-stride loop, and fold them into one word per
+ * workgroup that is written to sink[blockIdx] only if it equals a value no
+ * input is expected to produce (so the loads cannot be optimised away).
+ * sink must hold `grid` uint32 words.  Enqueued on `stream` (a hipStream_t,
+ * NULL = default stream).  Returns 0, -1 (bad argument) or -3 (launch
+ * failed). */
+int gsa_probe_read(const void *src, size_t bytes, uint32_t *sink, int grid, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GSA_PROBE_H */
