@@ -19,6 +19,10 @@ protocol state.  Sources followed (restated, not quoted):
   (Triton one_shot_all_reduce_kernel);
 * fp32 accumulation of bf16 inputs -- same documentation, higher-precision
   reduction section;
+* bias then RMSNorm fused behind the all-reduce -- "PyTorch Symmetric Memory"
+  talk, real-model example (RMSNorm itself: its textbook definition, the
+  pages do not write it out); bf16 output of an fp32 accumulation -- the
+  documentation's higher-precision reduction section;
 * signal pad next to every symmetric allocation, sized by launched blocks
   times world size, indexed by block -- same documentation, the
   writing-your-own-kernel section and the set_signal_pad_size and
@@ -72,6 +76,13 @@ class Oracle:
         lib.gsa_oracle_gemv_allreduce.restype = ctypes.c_int
         lib.gsa_oracle_fold_f32.argtypes = [_f32p, ctypes.c_int, ctypes.c_int64, _f32p]
         lib.gsa_oracle_fold_f32.restype = None
+        lib.gsa_oracle_bias_rmsnorm.argtypes = [_f32p, _f32p, _f32p, ctypes.c_double,
+                                                ctypes.c_int64, ctypes.c_int, _f32p, _f64p,
+                                                _f64p]
+        lib.gsa_oracle_bias_rmsnorm.restype = ctypes.c_int
+        lib.gsa_oracle_scale_f32.argtypes = [_f32p, _f32p, _f32p, ctypes.c_int64, ctypes.c_int,
+                                             _f32p, _u16p]
+        lib.gsa_oracle_scale_f32.restype = None
         self._lib = lib
 
     def gemv(self, A, x):
@@ -115,6 +126,48 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle rejected the arguments")
         return y, a, out
+
+    def bias_rmsnorm(self, out, bias, w, eps):
+        """Bias then RMSNorm over rows, per column: (z fp32, inv64 fp64 per
+        column, y64 fp64).  out: N x B fp32; bias, w: N fp32 or None."""
+        out = np.ascontiguousarray(out, dtype=np.float32)
+        N, B = out.shape
+        args = []
+        for v in (bias, w):
+            if v is None:
+                args.append(None)
+            else:
+                v = np.ascontiguousarray(v, dtype=np.float32)
+                if v.shape != (N,):
+                    raise ValueError("bias / weight must hold N values")
+                args.append(v)
+        z = np.empty((N, B), np.float32)
+        inv = np.empty(B, np.float64)
+        y = np.empty((N, B), np.float64)
+        rc = self._lib.gsa_oracle_bias_rmsnorm(
+            _ptr(out, _f32p), None if args[0] is None else _ptr(args[0], _f32p),
+            None if args[1] is None else _ptr(args[1], _f32p), float(eps), N, B,
+            _ptr(z, _f32p), _ptr(inv, _f64p), _ptr(y, _f64p))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return z, inv, y
+
+    def scale_f32(self, z, inv, w):
+        """y = fl32(fl32(z * inv[b]) * w[n]) and its bf16 bits (RNE)."""
+        z = np.ascontiguousarray(z, dtype=np.float32)
+        N, B = z.shape
+        inv = np.ascontiguousarray(inv, dtype=np.float32)
+        if inv.shape != (B,):
+            raise ValueError("inv must hold B values")
+        wp = None
+        if w is not None:
+            w = np.ascontiguousarray(w, dtype=np.float32)
+            wp = _ptr(w, _f32p)
+        y = np.empty((N, B), np.float32)
+        yb = np.empty((N, B), np.uint16)
+        self._lib.gsa_oracle_scale_f32(_ptr(z, _f32p), _ptr(inv, _f32p), wp, N, B,
+                                       _ptr(y, _f32p), _ptr(yb, _u16p))
+        return y, yb
 
     def fold_f32(self, slots):
         """fp32 one-shot sum of the given slots in rank order from +0.0f."""

@@ -30,6 +30,15 @@
  *    reduction: bf16 inputs are accumulated in fp32.  The oracle goes further
  *    and accumulates in fp64, so it is the exact value up to fp64 rounding.
  *
+ *  - "PyTorch Symmetric Memory" talk, the real-model example near its end:
+ *    the all-reduce is followed by a bias addition (elementwise, so it joins
+ *    the reduction loop) and an RMSNorm, all in one kernel.  The pages do not
+ *    write RMSNorm out; gsa_oracle_bias_rmsnorm uses its textbook definition
+ *    over the hidden dimension (the N output rows of one token).
+ *  - "PyTorch Symmetric Memory" documentation, higher-precision reduction:
+ *    accumulate in fp32, hand the result back in the input precision (bf16),
+ *    which gsa_oracle_scale_f32 rounds to nearest, ties to even.
+ *
  * Layouts (plain readings, the pages fix none): A_r is N x Ks row-major,
  * x is B x Ks row-major (one token's activation slice is contiguous),
  * slots are W x N x B with element (n, b) of rank r at r*N*B + n*B + b,
@@ -117,5 +126,71 @@ void gsa_oracle_fold_f32(const float *slots, int W, int64_t NB, float *out)
         for (int r = 0; r < W; ++r)
             acc = acc + slots[(int64_t)r * NB + i];
         out[i] = acc;
+    }
+}
+
+/*
+ * The fused epilogue: bias, then RMSNorm over n, for every token column b.
+ *   z[n][b]   = fl32(out[n][b] + bias[n])                (bias NULL: 0)
+ *   inv64[b]  = 1 / sqrt((sum_n z[n][b]^2) / N + eps)    (fp64, ascending n)
+ *   y64[n][b] = z[n][b] * inv64[b] * w[n]                (fp64; w NULL: 1)
+ * out, z: N x B fp32; bias, w: N fp32.  Returns 0, or -1 on a bad size.
+ */
+int gsa_oracle_bias_rmsnorm(const float *out, const float *bias, const float *w,
+                            double eps, int64_t N, int B,
+                            float *z, double *inv64, double *y64)
+{
+    if (N < 1 || B < 1 || !(eps >= 0.0))
+        return -1;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int b = 0; b < B; ++b) {
+            float add = bias ? bias[n] : 0.0f;
+            z[n * B + b] = out[n * B + b] + add;
+        }
+    }
+    for (int b = 0; b < B; ++b) {
+        double ssq = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            double v = (double)z[n * B + b];
+            ssq += v * v;
+        }
+        inv64[b] = 1.0 / sqrt(ssq / (double)N + eps);
+    }
+    for (int64_t n = 0; n < N; ++n) {
+        double wn = w ? (double)w[n] : 1.0;
+        for (int b = 0; b < B; ++b)
+            y64[n * B + b] = (double)z[n * B + b] * inv64[b] * wn;
+    }
+    return 0;
+}
+
+/* fp32 to bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN. */
+static uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t lsb = (u >> 16) & 1u;
+    return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+/*
+ * The normalised output in fp32, given one 1/rms value per column, in the
+ * evaluation order y = fl32(fl32(z * inv[b]) * w[n]) (w NULL: the second
+ * product is skipped), plus its bf16 rounding.  Given the same inv, this
+ * result is unique.
+ */
+void gsa_oracle_scale_f32(const float *z, const float *inv, const float *w,
+                          int64_t N, int B, float *y, uint16_t *y_bf16)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        for (int b = 0; b < B; ++b) {
+            float v = z[n * B + b] * inv[b];
+            if (w)
+                v = v * w[n];
+            y[n * B + b] = v;
+            y_bf16[n * B + b] = f32_to_bf16_rne(v);
+        }
     }
 }

@@ -17,7 +17,15 @@ What pins what:
   bf16_decode      raw bits to value, incl. denormal and max finite
   golden           hand-worked example in tests/golden/ (values by hand)
   fold_*           fp32 fold: order, +0 start and fp32 rounding, by hand
+  rms_golden       bias + RMSNorm hand-worked example in tests/golden/
+  rms_*            RMSNorm closed forms and invariants: constant column,
+                   unit RMS at eps = 0, scale invariance, bias cancelling,
+                   independent columns
+  scale_exact      fp32 evaluation of the normalised output against exact
+                   rational arithmetic with IEEE round-to-nearest-even
+  bf16_rne         fp32 -> bf16 rounding, hand-chosen bit patterns
 """
+from fractions import Fraction
 import json
 import os
 
@@ -212,9 +220,152 @@ def pin_fold_matches_sequence(o):
         assert out[i].view(np.uint32) == acc.view(np.uint32), f"fold element {i}"
 
 
+def pin_rms_golden(o):
+    with open(os.path.join(GOLDEN, "rmsnorm_hand.json")) as f:
+        g = json.load(f)
+    z, inv, y = o.bias_rmsnorm(np.array(g["out"], np.float32), np.array(g["bias"], np.float32),
+                               np.array(g["weight"], np.float32), g["eps"])
+    assert np.array_equal(z, np.array(g["z"], np.float32)), f"golden z {z}"
+    _close(inv, g["inv"], 1e-15, np.abs(g["inv"]), "golden inv_rms")
+    _close(y, g["y"], 1e-15, np.abs(np.array(g["y"])) + 1e-300, "golden y")
+
+
+def pin_rms_constant_column(o):
+    # A column holding one value c everywhere: inv = 1 / sqrt(c^2 + eps).
+    N, eps = 37, 0.25
+    cs = np.array([3.0, -0.5, 1024.0], np.float32)
+    out = np.tile(cs, (N, 1))
+    z, inv, y = o.bias_rmsnorm(out, None, None, eps)
+    want = 1.0 / np.sqrt(cs.astype(np.float64) ** 2 + eps)
+    _close(inv, want, 1e-14, want, "constant-column inv_rms")
+    _close(y, np.tile(cs * want, (N, 1)), 1e-14, np.abs(np.tile(cs * want, (N, 1))),
+           "constant-column y")
+
+
+def pin_rms_unit_rms(o):
+    # eps = 0, no weight: every normalised column has mean square 1.
+    rng = np.random.default_rng(5)
+    out = rng.normal(0, 3, (50, 4)).astype(np.float32)
+    _, _, y = o.bias_rmsnorm(out, None, None, 0.0)
+    ms = (y ** 2).mean(axis=0)
+    assert np.all(np.abs(ms - 1.0) < 1e-12), f"unit RMS: {ms}"
+
+
+def pin_rms_scale_invariant(o):
+    # eps = 0: scaling a column by 4 (exact in fp32) leaves y unchanged, and
+    # scales inv by 1/4.
+    rng = np.random.default_rng(6)
+    out = rng.normal(0, 1, (33, 3)).astype(np.float32)
+    w = rng.normal(1, 0.1, 33).astype(np.float32)
+    _, inv1, y1 = o.bias_rmsnorm(out, None, w, 0.0)
+    _, inv4, y4 = o.bias_rmsnorm(out * np.float32(4), None, w, 0.0)
+    _close(y4, y1, 1e-13, np.abs(y1) + 1e-30, "scale invariance of y")
+    _close(inv4 * 4, inv1, 1e-14, inv1, "inv scales by 1/4")
+
+
+def pin_rms_bias_cancels(o):
+    # bias = -out on every row: z = 0, inv = 1/sqrt(eps), y = 0; and a bias
+    # that shifts a constant column by a known amount.
+    rng = np.random.default_rng(7)
+    out = rng.normal(0, 1, (20, 1)).astype(np.float32)
+    z, inv, y = o.bias_rmsnorm(out, -out[:, 0], None, 4.0)
+    assert np.all(z == 0) and np.all(y == 0), "bias = -out gives zeros"
+    assert inv[0] == 0.5, f"inv = 1/sqrt(eps) = 0.5, got {inv[0]}"
+    z2, inv2, _ = o.bias_rmsnorm(np.full((8, 1), 1.0, np.float32),
+                                 np.full(8, 2.0, np.float32), None, 0.0)
+    assert np.all(z2 == 3.0) and abs(inv2[0] - 1.0 / 3.0) < 1e-16, "bias shifts z"
+
+
+def pin_rms_columns_independent(o):
+    # Each token column is normalised on its own: permuting columns permutes
+    # the results, and columns do not leak into each other.
+    rng = np.random.default_rng(8)
+    out = rng.normal(0, 1, (24, 3)).astype(np.float32)
+    out[:, 1] *= 100.0
+    w = rng.normal(1, 0.2, 24).astype(np.float32)
+    _, inv, y = o.bias_rmsnorm(out, None, w, 1e-3)
+    perm = [2, 0, 1]
+    _, invp, yp = o.bias_rmsnorm(np.ascontiguousarray(out[:, perm]), None, w, 1e-3)
+    assert np.array_equal(invp, inv[perm]) and np.array_equal(yp, y[:, perm]), "column permutation"
+    for b in range(3):
+        _, i1, y1 = o.bias_rmsnorm(np.ascontiguousarray(out[:, b:b + 1]), None, w, 1e-3)
+        assert i1[0] == inv[b] and np.array_equal(y1[:, 0], y[:, b]), f"column {b} alone"
+
+
+def _rne_f32(q):
+    """The fp32 value nearest to the exact rational q (ties to even), for q in
+    the normal range: the IEEE rule restated on exact integers."""
+    if q == 0:
+        return 0.0
+    sign = -1 if q < 0 else 1
+    q = abs(q)
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    if Fraction(2) ** e > q:
+        e -= 1
+    m = q / Fraction(2) ** (e - 23)          # in [2^23, 2^24)
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * float(Fraction(fl) * Fraction(2) ** (e - 23))
+
+
+def pin_scale_exact(o):
+    # y = fl32(fl32(z * inv) * w): each product correctly rounded, in this
+    # order, checked with exact rational arithmetic.  Random values near 1
+    # make both roundings matter (and the other order differ on many).
+    rng = np.random.default_rng(9)
+    N, B = 64, 3
+    z = rng.uniform(0.5, 2.0, (N, B)).astype(np.float32)
+    inv = rng.uniform(0.5, 2.0, B).astype(np.float32)
+    w = rng.uniform(0.5, 2.0, N).astype(np.float32)
+    y, _ = o.scale_f32(z, inv, w)
+    for n in range(N):
+        for b in range(B):
+            t = _rne_f32(Fraction(float(z[n, b])) * Fraction(float(inv[b])))
+            want = _rne_f32(Fraction(t) * Fraction(float(w[n])))
+            assert float(y[n, b]) == want, f"scale ({n},{b}): {float(y[n, b])!r} vs {want!r}"
+    y0, _ = o.scale_f32(z, inv, None)
+    for n in range(N):
+        for b in range(B):
+            want = _rne_f32(Fraction(float(z[n, b])) * Fraction(float(inv[b])))
+            assert float(y0[n, b]) == want, f"scale without weight ({n},{b})"
+
+
+def pin_bf16_rne(o):
+    # fp32 bit pattern -> expected bf16 bits, chosen by hand.
+    cases = [
+        (0x3F800000, 0x3F80),  # 1.0
+        (0x3F808000, 0x3F80),  # 1 + 2^-8: halfway, ties to even (down)
+        (0x3F818000, 0x3F82),  # 1 + 3*2^-8: halfway, ties to even (up)
+        (0x3F808001, 0x3F81),  # just above halfway: up
+        (0x3F807FFF, 0x3F80),  # just below halfway: down
+        (0xC0200000, 0xC020),  # -2.5, exact
+        (0x7F7FFFFF, 0x7F80),  # largest finite fp32 rounds up to +inf
+        (0x7F800000, 0x7F80),  # +inf
+        (0x80000000, 0x8000),  # -0.0
+        (0x00000001, 0x0000),  # smallest denormal rounds to +0
+        (0x00010000, 0x0001),  # a bf16 denormal, exact
+    ]
+    bits = np.array([c[0] for c in cases], np.uint32)
+    z = bits.view(np.float32).reshape(-1, 1)
+    _, yb = o.scale_f32(z, np.ones(1, np.float32), None)
+    got = [int(v) for v in yb[:, 0]]
+    assert got == [c[1] for c in cases], f"bf16 rounding {[hex(v) for v in got]}"
+    # A quiet NaN with an all-ones payload: adding the rounding increment
+    # would carry into the sign and exponent; it must stay a NaN.
+    nan = np.array([[np.uint32(0x7FFFFFFF).view(np.float32)]])
+    _, ybn = o.scale_f32(nan, np.ones(1, np.float32), None)
+    v = int(ybn[0, 0])
+    assert (v & 0x7F80) == 0x7F80 and (v & 0x007F) != 0 and (v & 0x0040), \
+        f"NaN stays a quiet NaN, got {hex(v)}"
+
+
 PINS = [pin_brute_force, pin_single_rank, pin_shard_sum, pin_identity, pin_one_hot,
         pin_small_integers, pin_rank_order_exact, pin_bf16_decode, pin_golden,
-        pin_fold_order, pin_fold_zero_start, pin_fold_fp32, pin_fold_matches_sequence]
+        pin_fold_order, pin_fold_zero_start, pin_fold_fp32, pin_fold_matches_sequence,
+        pin_rms_golden, pin_rms_constant_column, pin_rms_unit_rms, pin_rms_scale_invariant,
+        pin_rms_bias_cancels, pin_rms_columns_independent, pin_scale_exact, pin_bf16_rne]
 
 
 def failing_pins(o):

@@ -28,6 +28,21 @@ MUTANTS = {
     "fold_in_double": ("float acc = 0.0f;", "double acc = 0.0;"),
     "out_skips_first_rank": ("for (int r = 0; r < W; ++r) {\n            double term",
                              "for (int r = 1; r < W; ++r) {\n            double term"),
+    "rms_mean_over_n_minus_1": ("sqrt(ssq / (double)N + eps)", "sqrt(ssq / (double)(N - 1) + eps)"),
+    "rms_eps_dropped": ("sqrt(ssq / (double)N + eps)", "sqrt(ssq / (double)N)"),
+    "rms_sqrt_dropped": ("1.0 / sqrt(ssq / (double)N + eps)", "1.0 / (ssq / (double)N + eps)"),
+    "rms_bias_subtracted": ("out[n * B + b] + add", "out[n * B + b] - add"),
+    "rms_weight_dropped": ("* inv64[b] * wn", "* inv64[b]"),
+    "rms_one_column": ("double v = (double)z[n * B + b];", "double v = (double)z[n * B];"),
+    "rms_z_in_double": ("float add = bias ? bias[n] : 0.0f;\n            z[n * B + b] = out[n * B + b] + add;",
+                        "float add = bias ? bias[n] : 0.0f;\n            z[n * B + b] = (float)((double)out[n * B + b] + (double)add + 1e-9);"),
+    "scale_other_order": ("float v = z[n * B + b] * inv[b];\n            if (w)\n                v = v * w[n];",
+                          "float v = w ? z[n * B + b] * (inv[b] * w[n]) : z[n * B + b] * inv[b];"),
+    "scale_in_double": ("float v = z[n * B + b] * inv[b];\n            if (w)\n                v = v * w[n];",
+                        "float v = (float)((double)z[n * B + b] * (double)inv[b] * (w ? (double)w[n] : 1.0));"),
+    "rne_truncates": ("return (uint16_t)((u + 0x7FFFu + lsb) >> 16);", "return (uint16_t)(u >> 16);"),
+    "rne_ties_away": ("return (uint16_t)((u + 0x7FFFu + lsb) >> 16);", "return (uint16_t)((u + 0x8000u) >> 16);"),
+    "nan_branch_dropped": ("if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0)\n        return (uint16_t)((u >> 16) | 0x0040u);\n", ""),
 }
 
 
