@@ -18,10 +18,20 @@ GSA_PAD_HEADER_WORDS = 16
 GSA_MAX_W = 8
 GSA_MAX_B = 16
 GSA_MAX_X_LDS_BYTES = 128 * 1024
+GSA_DTYPE_F32 = 0
+GSA_DTYPE_BF16 = 1
 
 EXPORTS = ("gsa_symm_alloc", "gsa_symm_free", "gsa_symm_slots", "gsa_symm_signal_pad",
            "gsa_signal_pad_row_stride", "gsa_signal_pad_reset", "gsa_gemv_allreduce",
-           "gsa_signal_pad_status", "gsa_set_wait_timeout_us", "gsa_strerror")
+           "gsa_gemv_allreduce_rmsnorm", "gsa_signal_pad_status", "gsa_set_wait_timeout_us",
+           "gsa_strerror")
+
+
+class gsa_epilogue(ctypes.Structure):
+    """struct gsa_epilogue of include/gsa.h."""
+    _fields_ = [("bias", ctypes.c_void_p), ("rms_weight", ctypes.c_void_p),
+                ("eps", ctypes.c_float), ("y_dtype", ctypes.c_int), ("y", ctypes.c_void_p),
+                ("inv_rms", ctypes.c_void_p)]
 
 
 class GsaError(RuntimeError):
@@ -61,6 +71,9 @@ def lib():
         L.gsa_signal_pad_reset.restype = ci
         L.gsa_gemv_allreduce.argtypes = [vp, vp, vp, vp, vp, ci, ci, i64, i64, ci, vp]
         L.gsa_gemv_allreduce.restype = ci
+        L.gsa_gemv_allreduce_rmsnorm.argtypes = [vp, vp, vp, vp, vp, ci, ci, i64, i64, ci,
+                                                 ctypes.POINTER(gsa_epilogue), vp]
+        L.gsa_gemv_allreduce_rmsnorm.restype = ci
         L.gsa_signal_pad_status.argtypes = [vp, vp, ctypes.POINTER(ci),
                                             ctypes.POINTER(i64), ctypes.POINTER(ci)]
         L.gsa_signal_pad_status.restype = ci
@@ -142,6 +155,28 @@ def gsa_gemv_allreduce(A_r, x, slots, pad, out, W, rank, N, K, B, stream=None):
     _check(lib().gsa_gemv_allreduce(_ptr(A_r), _ptr(x), _ptr(slots), _ptr(pad), _ptr(out),
                                     W, rank, N, K, B, _stream(stream)),
            "gsa_gemv_allreduce")
+
+
+def make_epilogue(y, bias=None, rms_weight=None, eps=1e-5, inv_rms=None):
+    """A gsa_epilogue for device tensors: y (N x B, float32 or bfloat16),
+    optional bias / rms_weight (N float32) and inv_rms (B float32)."""
+    import torch
+    if y.dtype == torch.float32:
+        dt = GSA_DTYPE_F32
+    elif y.dtype == torch.bfloat16:
+        dt = GSA_DTYPE_BF16
+    else:
+        raise ValueError("y must be float32 or bfloat16")
+    return gsa_epilogue(_ptr(bias), _ptr(rms_weight), float(eps), dt, _ptr(y), _ptr(inv_rms))
+
+
+def gsa_gemv_allreduce_rmsnorm(A_r, x, slots, pad, out, W, rank, N, K, B, ep, stream=None):
+    """ep: a gsa_epilogue (see make_epilogue), or None (rejected by the library)."""
+    _check(lib().gsa_gemv_allreduce_rmsnorm(_ptr(A_r), _ptr(x), _ptr(slots), _ptr(pad),
+                                            _ptr(out), W, rank, N, K, B,
+                                            None if ep is None else ctypes.byref(ep),
+                                            _stream(stream)),
+           "gsa_gemv_allreduce_rmsnorm")
 
 
 def gsa_signal_pad_status(pad, stream=None):

@@ -208,7 +208,9 @@ __device__ bool wait_peers(const GemvArgs& a, int lane, int64_t tile, uint32_t e
 //   B0 flag load issued | B1 decision in s_ctl (the VALU kernels: x staged;
 //   the MFMA kernels: per-wave partials in LDS) | B2 own slot published, and
 //   the peer tile in LDS if the peers were ready at the start (compute wave 0
-//   then stores the flag) | B3 (only if they were not) late peer tile in LDS.
+//   then stores the flag) | B3 (only if they were not) late peer tile in LDS
+//   | with the fused epilogue: E1, E2 and, in the workgroup that finishes
+//   last, E3 (see fused_epilogue).
 // The peer loads stay in flight across B1: a workgroup barrier does not wait
 // for outstanding global loads.
 __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
@@ -221,15 +223,21 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
   __syncthreads();  // B1
   if (state == kPeersReady) store_peer_tile(a, lane, v, pe);
   __syncthreads();  // B2
-  if (state != kMustWait) return;
-  const uint32_t epoch = s_ctl[0];
-  const bool ok = wait_peers(a, lane, tile, epoch);  // the own flag went out after B2
-  if (ok) {
-    issue_peer_tile(a, lane, tile, v);  // after the flags returned
-    store_peer_tile(a, lane, v, pe);
+  if (state == kMustWait) {
+    const uint32_t epoch = s_ctl[0];
+    const bool ok = wait_peers(a, lane, tile, epoch);  // the own flag went out after B2
+    if (ok) {
+      issue_peer_tile(a, lane, tile, v);  // after the flags returned
+      store_peer_tile(a, lane, v, pe);
+    }
+    if (lane == 0) s_ctl[1] = ok ? kPeersReady : kMustWait;
+    __syncthreads();  // B3
   }
-  if (lane == 0) s_ctl[1] = ok ? kPeersReady : kMustWait;
-  __syncthreads();  // B3
+  if (a.epi) {
+    __syncthreads();  // E1
+    __syncthreads();  // E2
+    if (s_ctl[2]) __syncthreads();  // E3 (last workgroup only)
+  }
 }
 
 // out = ((0 + s_0) + s_1) ... + s_{W-1}; s_rank is this call's published y,
@@ -253,19 +261,30 @@ __device__ __forceinline__ float one_shot_sum(const GemvArgs& a, float y, const 
   return acc;
 }
 
-// Compute waves once y is final (y[e] for local rows n[e], column b; owner
-// lanes only), `state` being what the communication wave decided before B1:
-// publish y into slot[rank], B2, compute wave 0 releases the flag, [B3], out.
+template <int OPL>
+__device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
+                               const bool (&own)[OPL], const bool (&live)[OPL],
+                               const float (&o)[OPL], bool ok, float* elds, uint32_t* s_ctl,
+                               int wave, int lane, int nt);
+
+// Compute waves once y is final (y[e] for local row n[e], column b, if own[e]:
+// every (row, column) of the tile has exactly one owner lane), `state` being
+// what the communication wave decided before B1: publish y into slot[rank],
+// B2, compute wave 0 releases the flag, [B3], out, [the fused epilogue].
 // Every compute wave waits for its own slot stores to complete before B2, so
-// the flag store that follows B2 is ordered after all of them.
+// the flag store that follows B2 is ordered after all of them.  nt: compute
+// threads of the workgroup.
 template <int OPL>
 __device__ void publish_and_reduce(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
-                                   const bool (&live)[OPL], const float (&y)[OPL],
-                                   const float* pe, const uint32_t* s_ctl, uint32_t state,
-                                   bool flag_lane) {
+                                   const bool (&own)[OPL], const float (&y)[OPL],
+                                   const float* pe, float* elds, uint32_t* s_ctl,
+                                   uint32_t state, int wave, int lane, int nt) {
   const int64_t NB = a.N * a.B;
   const int64_t row0 = tile * kTileRows;
   float* own_slot = a.slots + a.rank * NB;
+  bool live[OPL];
+#pragma unroll
+  for (int e = 0; e < OPL; ++e) live[e] = own[e] && row0 + n[e] < a.N;
   if (state != kBadOwnRow) {
 #pragma unroll
     for (int e = 0; e < OPL; ++e)
@@ -273,15 +292,26 @@ __device__ void publish_and_reduce(const GemvArgs& a, int64_t tile, const int (&
   }
   wait_vm_all();    // the published values are at the coherence point ...
   __syncthreads();  // B2 ... in every compute wave
-  if (state == kBadOwnRow) return;
-  if (flag_lane) store_flag(flag_ptr(a, a.rank, tile), s_ctl[0]);
+  bool ok = state != kBadOwnRow;
+  if (ok && wave == 0 && lane == 0) store_flag(flag_ptr(a, a.rank, tile), s_ctl[0]);
   if (state == kMustWait) {
     __syncthreads();  // B3
-    if (s_ctl[1] != kPeersReady) return;  // wait expired: this tile's out rows stay unwritten
+    ok = s_ctl[1] == kPeersReady;  // wait expired: this tile's out rows stay unwritten
   }
+  float o[OPL];
 #pragma unroll
-  for (int e = 0; e < OPL; ++e)
-    if (live[e]) a.out[(row0 + n[e]) * a.B + b] = one_shot_sum(a, y[e], pe, n[e], b);
+  for (int e = 0; e < OPL; ++e) {
+    o[e] = 0.0f;
+    if (ok && live[e]) {
+      o[e] = one_shot_sum(a, y[e], pe, n[e], b);
+      float* dst = &a.out[(row0 + n[e]) * a.B + b];
+      if (a.epi)
+        store_coherent(dst, o[e]);  // read back by the workgroup that finishes last
+      else
+        *dst = o[e];
+    }
+  }
+  if (a.epi) fused_epilogue<OPL>(a, tile, n, b, own, live, o, ok, elds, s_ctl, wave, lane, nt);
 }
 
 // Sum of v over an aligned group of G lanes (G = 16, 32 or 64), returned in
@@ -314,6 +344,110 @@ __device__ __forceinline__ float group_sum(float v) {
     v = __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
   }
   return v;
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even; a NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0)
+    return (uint16_t)((u >> 16) | 0x0040u);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// The fused epilogue: bias, then RMSNorm over the N rows of every token
+// column, then y in fp32 or bf16 ("PyTorch Symmetric Memory" talk, real-model
+// example: the bias addition joins the reduction loop and the RMSNorm runs in
+// the same kernel; RMSNorm by its textbook definition; bf16 output of an fp32
+// accumulation as in the documentation's higher-precision reduction).
+//   z = out + bias[n]; inv[b] = 1 / sqrtf(sum_n z^2 / N + eps);
+//   y = (z * inv[b]) * w[n]
+// The sum over n crosses workgroups: each tile sums its 16 squares per column
+// in row order, publishes the partial (coherent store), and counts itself
+// done in the pad header; the workgroup that completes the count folds the
+// partials in a fixed order (lane l takes tiles l, l + 64, ... in ascending
+// order, then a fixed lane tree), resets the count for the next call and
+// normalises every row.  A tile that failed (wait expired, bad own row)
+// contributes NaN, so y and inv come out NaN for that call.
+// Barriers: E1 (squares in LDS; every out store of the tile completed),
+// E2 (done count taken), E3 (last workgroup: inv in LDS).
+template <int OPL>
+__device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
+                               const bool (&own)[OPL], const bool (&live)[OPL],
+                               const float (&o)[OPL], bool ok, float* elds, uint32_t* s_ctl,
+                               int wave, int lane, int nt) {
+  float* zz = elds;           // [16 rows][16 columns] squares of z
+  float* s_inv = elds + 256;  // [16] 1 / rms per column
+  const int64_t row0 = tile * kTileRows;
+#pragma unroll
+  for (int e = 0; e < OPL; ++e) {
+    if (own[e]) {
+      float sq = 0.0f;  // rows past N add nothing
+      if (live[e]) {
+        const float z = o[e] + (a.bias ? a.bias[row0 + n[e]] : 0.0f);
+        sq = z * z;
+      }
+      zz[n[e] * 16 + b] = ok ? sq : __builtin_nanf("");
+    }
+  }
+  wait_vm_all();    // this wave's out stores are at the coherence point ...
+  __syncthreads();  // E1 ... in every compute wave, and the squares are in LDS
+  if (wave == 0) {
+    if (lane < a.B) {
+      float part = 0.0f;
+      for (int r = 0; r < kTileRows; ++r) part = part + zz[r * 16 + lane];
+      store_coherent(&a.ssq[tile * 16 + lane], part);
+    }
+    wait_vm_all();  // the partials are at the coherence point before the count
+    if (lane == 0) {
+      const uint32_t done =
+          __hip_atomic_fetch_add(&a.pad[kHdrEpiCount], 1u, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT) + 1u;
+      const uint32_t last = done == (uint32_t)a.tiles ? 1u : 0u;
+      if (last)  // every tile of this call has counted itself: ready for the next call
+        __hip_atomic_store(&a.pad[kHdrEpiCount], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_ctl[2] = last;
+    }
+  }
+  __syncthreads();  // E2
+  if (!s_ctl[2]) return;
+
+  // The last workgroup.  Its loads of partials and outputs are issued only
+  // after the count it took showed every tile done (they sit behind a branch
+  // on that value), and each tile made its stores complete before counting.
+  if (wave == 0) {
+    float acc[GSA_MAX_B];
+#pragma unroll
+    for (int c = 0; c < GSA_MAX_B; ++c) acc[c] = 0.0f;
+    for (int t = lane; t < a.tiles; t += 64) {
+#pragma unroll
+      for (int c = 0; c < GSA_MAX_B; ++c)
+        if (c < a.B) acc[c] = acc[c] + load_coherent(&a.ssq[(int64_t)t * 16 + c]);
+    }
+#pragma unroll
+    for (int c = 0; c < GSA_MAX_B; ++c) {
+      if (c < a.B) {
+        const float tot = group_sum<64>(acc[c]);
+        const float inv = 1.0f / sqrtf(tot / (float)a.N + a.eps);
+        if (lane == 0) {
+          s_inv[c] = inv;
+          if (a.inv_rms) a.inv_rms[c] = inv;
+        }
+      }
+    }
+  }
+  __syncthreads();  // E3
+  const int64_t NB = a.N * a.B;
+  for (int64_t i = (int64_t)wave * 64 + lane; i < NB; i += nt) {
+    const int64_t r = i / a.B;
+    const int c = (int)(i - r * a.B);
+    const float z = load_coherent(&a.out[i]) + (a.bias ? a.bias[r] : 0.0f);
+    float v = z * s_inv[c];
+    if (a.rms_w) v = v * a.rms_w[r];
+    if (a.y_bf16)
+      static_cast<uint16_t*>(a.y)[i] = bf16_rne(v);
+    else
+      static_cast<float*>(a.y)[i] = v;
+  }
 }
 
 // One A chunk (16 bytes) of each of the lane's R rows, at byte offset
@@ -393,7 +527,7 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   static_assert(V <= G, "one owner lane per output of a row group");
 
   extern __shared__ uint4 lds_x[];
-  __shared__ uint32_t s_ctl[2];
+  __shared__ uint32_t s_ctl[4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -403,6 +537,7 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   const int xchunks = B * C;
   const int zidx = xchunks;  // zero chunk; xchunks + 1 is the sink
   float* pe = reinterpret_cast<float*>(lds_x + xchunks + 2);
+  float* elds = pe + a.W * kTileRows * B + 1;  // the epilogue's LDS
 
   if (wave == NW) {
     comm_wave(a, lane, tile, pe, s_ctl);
@@ -457,9 +592,9 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   }
   const int vidx = min(li, V - 1);
   const int n[1] = {nloc0 + vidx / B};
-  const bool live[1] = {li < V && tile * kTileRows + n[0] < a.N};
+  const bool own[1] = {li < V};
   const float y[1] = {yv};
-  publish_and_reduce<1>(a, tile, n, vidx % B, live, y, pe, s_ctl, state, wave == 0 && lane == 0);
+  publish_and_reduce<1>(a, tile, n, vidx % B, own, y, pe, elds, s_ctl, state, wave, lane, NT);
 }
 
 // MFMA epilogue: each wave's 16 x 16 partial goes to red[wave][n][b]; after
@@ -468,7 +603,7 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
 template <int NW>
 __device__ __forceinline__ void mfma_finish(const GemvArgs& a, int64_t tile, int wave, int lane,
                                             f32x4_t acc, float* red, const float* pe,
-                                            const uint32_t* s_ctl) {
+                                            float* elds, uint32_t* s_ctl) {
 #pragma unroll
   for (int e = 0; e < 4; ++e)
     red[(wave * kTileRows + 4 * (lane >> 4) + e) * 16 + (lane & 15)] = acc[e];
@@ -480,9 +615,9 @@ __device__ __forceinline__ void mfma_finish(const GemvArgs& a, int64_t tile, int
 #pragma unroll
   for (int w = 1; w < NW; ++w) y = y + red[(w * kTileRows + nl) * 16 + bl];
   const int n[1] = {nl};
-  const bool live[1] = {bl < a.B && tile * kTileRows + nl < a.N};
+  const bool own[1] = {bl < a.B};
   const float yv[1] = {y};
-  publish_and_reduce<1>(a, tile, n, bl, live, yv, pe, s_ctl, state, wave == 0 && lane == 0);
+  publish_and_reduce<1>(a, tile, n, bl, own, yv, pe, elds, s_ctl, state, wave, lane, NW * 64);
 }
 
 // Copy 16 bytes per active lane from global memory straight into LDS: lane l
@@ -511,7 +646,7 @@ template <int NW, int D>
 __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs a) {
   static_assert(NW * 4 == kTileRows, "each compute wave finishes 4 rows of the tile");
   extern __shared__ uint4 lds[];
-  __shared__ uint32_t s_ctl[2];
+  __shared__ uint32_t s_ctl[4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -521,6 +656,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs a) {
   const int CP = C + 1;  // padded LDS row: the 16 batch rows of one chunk hit distinct banks
   float* red = reinterpret_cast<float*>(lds + 16 * CP);
   float* pe = red + NW * kTileRows * 16;
+  float* elds = pe + a.W * kTileRows * a.B + 1;  // the epilogue's LDS
 
   if (wave == NW) {
     comm_wave(a, lane, tile, pe, s_ctl);
@@ -590,7 +726,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs a) {
     }
   }
 
-  mfma_finish<NW>(a, tile, wave, lane, acc, red, pe, s_ctl);
+  mfma_finish<NW>(a, tile, wave, lane, acc, red, pe, elds, s_ctl);
 }
 
 // MFMA path for x beyond the LDS bound (8 < B <= 16, 16 * (C + 1) chunks over
@@ -604,7 +740,7 @@ template <int NW, int D>
 __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a) {
   static_assert(NW * 4 == kTileRows, "each compute wave finishes 4 rows of the tile");
   extern __shared__ uint4 lds[];
-  __shared__ uint32_t s_ctl[2];
+  __shared__ uint32_t s_ctl[4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -613,6 +749,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a
   const int C = a.C;
   float* red = reinterpret_cast<float*>(lds);
   float* pe = red + NW * kTileRows * 16;
+  float* elds = pe + a.W * kTileRows * a.B + 1;  // the epilogue's LDS
 
   if (wave == NW) {
     comm_wave(a, lane, tile, pe, s_ctl);
@@ -667,7 +804,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  mfma_finish<NW>(a, tile, wave, lane, acc, red, pe, s_ctl);
+  mfma_finish<NW>(a, tile, wave, lane, acc, red, pe, elds, s_ctl);
 }
 
 __global__ void pad_reset_kernel(uint32_t* pad, int W, int row_stride, uint32_t mask) {
@@ -728,15 +865,17 @@ ValuChoice valu_kernel(int C) {
 
 }  // namespace
 
-size_t gemv_lds_bytes(int W, int B, int C) {
-  const size_t peer_tile = ((size_t)W * kTileRows * B + 1) * sizeof(float);
+size_t gemv_lds_bytes(int W, int B, int C, bool epi) {
+  // The peer tile, then (with the epilogue) 16 x 16 squares and 16 1/rms.
+  const size_t tail = ((size_t)W * kTileRows * B + 1) * sizeof(float) +
+                      (epi ? (size_t)(256 + 16) * sizeof(float) : 0);
   const size_t partials = (size_t)kMfmaWaves * kTileRows * 16 * sizeof(float);
-  if (B <= 8) return ((size_t)B * C + 2) * 16 + peer_tile;
-  if (mfma_x_in_lds(C)) return (size_t)16 * (C + 1) * 16 + partials + peer_tile;
-  return partials + peer_tile;
+  if (B <= 8) return ((size_t)B * C + 2) * 16 + tail;
+  if (mfma_x_in_lds(C)) return (size_t)16 * (C + 1) * 16 + partials + tail;
+  return partials + tail;
 }
 
-bool select_gemv_kernel(int W, int B, int C, Launch* out) {
+bool select_gemv_kernel(int W, int B, int C, bool epi, Launch* out) {
   if (W < 1 || W > GSA_MAX_W || B < 1 || B > GSA_MAX_B || C < 1) return false;
   if (B <= 8 && (size_t)B * C * 16 > GSA_MAX_X_LDS_BYTES) return false;  // x staged in LDS
   ValuChoice k{nullptr, kMfmaWaves};
@@ -757,7 +896,7 @@ bool select_gemv_kernel(int W, int B, int C, Launch* out) {
       break;
   }
   const unsigned block = (unsigned)(k.waves + 1) * 64;
-  *out = {k.kernel, block, gemv_lds_bytes(W, B, C)};
+  *out = {k.kernel, block, gemv_lds_bytes(W, B, C, epi)};
   return true;
 }
 

@@ -9,6 +9,7 @@
 // like the constant-time is_symm_mem_tensor() check of the same API.
 
 #include <atomic>
+#include <cmath>
 #include <mutex>
 #include <unordered_map>
 #include <unordered_set>
@@ -25,6 +26,7 @@ struct gsa_symm {
   void* base;
   float* slots;
   uint32_t* pad;
+  float* ssq;  // the fused epilogue's per-tile partial sums (tiles x 16 fp32)
   int device;
 };
 
@@ -97,7 +99,9 @@ int gsa_symm_alloc(int W, int64_t N, int B, gsa_symm** out) {
   const int64_t stride = gsa_signal_pad_row_stride(N);
   const size_t slot_bytes = round_up((size_t)W * (size_t)N * (size_t)B * sizeof(float), kAlign);
   const size_t pad_words = GSA_PAD_HEADER_WORDS + (size_t)W * (size_t)stride;
-  const size_t bytes = slot_bytes + round_up(pad_words * sizeof(uint32_t), kAlign);
+  const size_t pad_bytes = round_up(pad_words * sizeof(uint32_t), kAlign);
+  const size_t ssq_bytes = round_up((size_t)tiles_of(N) * 16 * sizeof(float), kAlign);
+  const size_t bytes = slot_bytes + pad_bytes + ssq_bytes;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return GSA_EHIP;
   void* base = nullptr;
@@ -115,8 +119,9 @@ int gsa_symm_alloc(int W, int64_t N, int B, gsa_symm** out) {
     (void)hipFree(base);
     return GSA_EHIP;
   }
+  float* ssq = reinterpret_cast<float*>(static_cast<char*>(base) + slot_bytes + pad_bytes);
   gsa_symm* h = new gsa_symm{W, N, B, stride, tiles_of(N), bytes, base,
-                             static_cast<float*>(base), pad, dev};
+                             static_cast<float*>(base), pad, ssq, dev};
   std::lock_guard<std::mutex> lk(g_mu);
   g_by_slots[(uintptr_t)h->slots] = h;
   g_by_pad[(uintptr_t)h->pad] = h;
@@ -171,8 +176,16 @@ int gsa_signal_pad_reset(uint32_t* pad, int W, int64_t N, uint32_t published_mas
   return e == hipSuccess ? GSA_OK : GSA_EHIP;
 }
 
-int gsa_gemv_allreduce(const uint16_t* A_r, const uint16_t* x, float* slots, uint32_t* pad,
-                       float* out, int W, int rank, int64_t N, int64_t K, int B, void* stream) {
+}  // extern "C"
+
+namespace {
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Both entry points: validate, fill the launch arguments, enqueue one kernel.
+int enqueue_call(const uint16_t* A_r, const uint16_t* x, float* slots, uint32_t* pad,
+                 float* out, int W, int rank, int64_t N, int64_t K, int B,
+                 const gsa_epilogue* ep, void* stream) {
   // Scalars first: these checks touch no HIP state.
   if (W < 1 || W > GSA_MAX_W || rank < 0 || rank >= W) return GSA_EINVAL;
   if (N < 1 || B < 1 || B > GSA_MAX_B || K < 1 || K % W != 0) return GSA_EINVAL;
@@ -185,9 +198,19 @@ int gsa_gemv_allreduce(const uint16_t* A_r, const uint16_t* x, float* slots, uin
     return GSA_EINVAL;
   // A_r is addressed through a 32-bit buffer resource.
   if (N > ((int64_t)0x7FFFFFF0 / 2) / Ks) return GSA_EINVAL;
+  if (ep) {
+    if (!ep->y || (ep->y_dtype != GSA_DTYPE_F32 && ep->y_dtype != GSA_DTYPE_BF16))
+      return GSA_EINVAL;
+    if (!aligned(ep->y, ep->y_dtype == GSA_DTYPE_F32 ? 4 : 2)) return GSA_EINVAL;
+    if ((ep->bias && !aligned(ep->bias, 4)) || (ep->rms_weight && !aligned(ep->rms_weight, 4)) ||
+        (ep->inv_rms && !aligned(ep->inv_rms, 4)))
+      return GSA_EINVAL;
+    if (!std::isfinite(ep->eps) || ep->eps < 0.0f) return GSA_EINVAL;
+    if (N > ((int64_t)1 << 24)) return GSA_EINVAL;  // N is exact as a float divisor
+  }
   const int C = (int)(Ks / 8);
   gsa::Launch l;
-  if (!gsa::select_gemv_kernel(W, B, C, &l)) return GSA_EINVAL;
+  if (!gsa::select_gemv_kernel(W, B, C, ep != nullptr, &l)) return GSA_EINVAL;
 
   gsa::GemvArgs a;
   {
@@ -196,6 +219,7 @@ int gsa_gemv_allreduce(const uint16_t* A_r, const uint16_t* x, float* slots, uin
     if (!h || h->pad != pad || h->W != W || h->N != N || h->B != B) return GSA_EINVAL;
     a.row_stride = (int)h->row_stride;
     a.tiles = (int)h->tiles;
+    a.ssq = h->ssq;
     if (l.lds_bytes > 65536 && !g_big_lds_ready.count(l.kernel)) {
       // Opt in once to the largest dynamic LDS any shape of this kernel may use.
       if (hipFuncSetAttribute(l.kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -215,6 +239,13 @@ int gsa_gemv_allreduce(const uint16_t* A_r, const uint16_t* x, float* slots, uin
   a.B = B;
   a.W = W;
   a.rank = rank;
+  a.epi = ep ? 1 : 0;
+  a.y_bf16 = ep && ep->y_dtype == GSA_DTYPE_BF16 ? 1 : 0;
+  a.eps = ep ? ep->eps : 0.0f;
+  a.bias = ep ? ep->bias : nullptr;
+  a.rms_w = ep ? ep->rms_weight : nullptr;
+  a.y = ep ? ep->y : nullptr;
+  a.inv_rms = ep ? ep->inv_rms : nullptr;
   int rc = ticks_for(g_timeout_us.load(std::memory_order_relaxed), &a.timeout_ticks);
   if (rc != GSA_OK) return rc;
   hipError_t e = gsa::launch_gemv(l, a, static_cast<hipStream_t>(stream));
@@ -223,6 +254,22 @@ int gsa_gemv_allreduce(const uint16_t* A_r, const uint16_t* x, float* slots, uin
     return GSA_EHIP;
   }
   return GSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gsa_gemv_allreduce(const uint16_t* A_r, const uint16_t* x, float* slots, uint32_t* pad,
+                       float* out, int W, int rank, int64_t N, int64_t K, int B, void* stream) {
+  return enqueue_call(A_r, x, slots, pad, out, W, rank, N, K, B, nullptr, stream);
+}
+
+int gsa_gemv_allreduce_rmsnorm(const uint16_t* A_r, const uint16_t* x, float* slots,
+                               uint32_t* pad, float* out, int W, int rank, int64_t N, int64_t K,
+                               int B, const gsa_epilogue* ep, void* stream) {
+  if (!ep) return GSA_EINVAL;
+  return enqueue_call(A_r, x, slots, pad, out, W, rank, N, K, B, ep, stream);
 }
 
 int gsa_signal_pad_status(const uint32_t* pad, void* stream, int* code, int64_t* tile,

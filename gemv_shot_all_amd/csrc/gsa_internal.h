@@ -14,6 +14,7 @@ enum : int {
   kHdrErrorBits = 0,   // atomicOr: kErrTimeout | kErrState
   kHdrTimeoutKey = 1,  // atomicMin of tile * 8 + peer, 0xFFFFFFFF = none
   kHdrStateTile = 2,   // atomicMin of the tile with a bad own flag row
+  kHdrEpiCount = 3,    // epilogue: tiles of the running call that are done (0 between calls)
 };
 enum : uint32_t { kErrTimeout = 1u, kErrState = 2u };
 
@@ -32,6 +33,16 @@ struct GemvArgs {
   int row_stride;         // words between flag rows
   int tiles;              // ceil(N / 16)
   uint64_t timeout_ticks; // device wall-clock ticks a wait may take
+  // Fused epilogue (bias, RMSNorm over rows, y in fp32 or bf16); epi == 0:
+  // none, and the fields below are unused.
+  int epi;
+  int y_bf16;
+  float eps;
+  const float* bias;      // N fp32 or null
+  const float* rms_w;     // N fp32 or null
+  void* y;                // N x B
+  float* inv_rms;         // B fp32 or null
+  float* ssq;             // tiles x 16 fp32 partial sums of squares (library scratch)
 };
 
 // A ready-to-launch kernel choice for one (B, C) shape.
@@ -41,11 +52,12 @@ struct Launch {
   size_t lds_bytes;       // dynamic LDS
 };
 
-// Pick the kernel for W ranks, batch B (1..16) and C chunks per row.  Returns
-// false if the shape exceeds the LDS staging bound.
-bool select_gemv_kernel(int W, int B, int C, Launch* out);
-// Dynamic LDS bytes the kernel chosen for (W, B, C) needs.
-size_t gemv_lds_bytes(int W, int B, int C);
+// Pick the kernel for W ranks, batch B (1..16) and C chunks per row (with
+// the epilogue's extra LDS if epi).  Returns false if the shape exceeds the
+// LDS staging bound.
+bool select_gemv_kernel(int W, int B, int C, bool epi, Launch* out);
+// Dynamic LDS bytes the kernel chosen for (W, B, C, epi) needs.
+size_t gemv_lds_bytes(int W, int B, int C, bool epi);
 
 hipError_t launch_gemv(const Launch& l, const GemvArgs& a, hipStream_t s);
 hipError_t launch_pad_reset(uint32_t* pad, int W, int row_stride, int tiles,

@@ -124,6 +124,43 @@ int gsa_gemv_allreduce(const uint16_t *A_r, const uint16_t *x, float *slots,
                        uint32_t *pad, float *out, int W, int rank, int64_t N,
                        int64_t K, int B, void *stream);
 
+/* Output element types of the fused epilogue. */
+#define GSA_DTYPE_F32 0
+#define GSA_DTYPE_BF16 1
+
+/* What gsa_gemv_allreduce_rmsnorm does after the one-shot sum.  The
+ * "PyTorch Symmetric Memory" talk's real-model example follows the
+ * all-reduce with a bias addition (elementwise, so it joins the reduction
+ * loop) and an RMSNorm, all in one kernel; RMSNorm is taken by its textbook
+ * definition over the hidden dimension, i.e. the N output rows of a token:
+ *   z[n][b]  = out[n][b] + bias[n]                     (fp32)
+ *   inv[b]   = 1 / sqrtf(sum_n z[n][b]^2 / N + eps)     (fp32)
+ *   y[n][b]  = (z[n][b] * inv[b]) * rms_weight[n]       (fp32, then y_dtype)
+ * A bf16 y is rounded to nearest, ties to even (an fp32 accumulation handed
+ * back in bf16, as in the documentation's higher-precision reduction). */
+typedef struct gsa_epilogue {
+  const float *bias;       /* [device] N fp32, or NULL: no bias */
+  const float *rms_weight; /* [device] N fp32, or NULL: weight 1 */
+  float eps;               /* finite, >= 0 (eps = 0 and an all-zero column give NaN) */
+  int y_dtype;             /* GSA_DTYPE_F32 or GSA_DTYPE_BF16 */
+  void *y;                 /* [device] N x B (n-major), naturally aligned, written */
+  float *inv_rms;          /* [device] B fp32 written with inv[b], or NULL */
+} gsa_epilogue;
+
+/* gsa_gemv_allreduce (same arguments, same contract, `out` written as
+ * there), followed in the same kernel by the epilogue `ep` [host, read
+ * before return].  The sum over n crosses tiles: each tile publishes its
+ * partial sums of squares, counts itself done in the pad header, and the
+ * tile that completes the count folds the partials in a fixed order and
+ * normalises all N rows, so repeated calls are bit-identical.  If any tile
+ * of the call failed (see gsa_signal_pad_status), y and inv_rms are NaN.
+ * Requires N <= 2^24 in addition.  Errors: GSA_EINVAL (also: ep or y NULL,
+ * unknown y_dtype, misaligned pointer, eps negative or not finite),
+ * GSA_EHIP. */
+int gsa_gemv_allreduce_rmsnorm(const uint16_t *A_r, const uint16_t *x, float *slots,
+                               uint32_t *pad, float *out, int W, int rank, int64_t N,
+                               int64_t K, int B, const gsa_epilogue *ep, void *stream);
+
 /* Read the pad's status words after the work queued on `stream` has finished
  * (synchronizes `stream`).  *code [host] := GSA_ESTATE if any call found its
  * own flag row unusable (then *tile := the smallest such tile, *peer := -1),

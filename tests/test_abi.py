@@ -87,6 +87,30 @@ def test_gemv_allreduce_rejects_bad_arguments(args):
     assert rc == gsa.GSA_EINVAL
 
 
+def test_rmsnorm_entry_point_rejects_bad_arguments():
+    L = _lib.lib()
+    good = (P, P, P, P, P, 2, 0, 16, 64, 1)
+
+    def ep(**kw):
+        e = _lib.gsa_epilogue(None, None, 1e-5, gsa.GSA_DTYPE_F32, P, None)
+        for k, v in kw.items():
+            setattr(e, k, v)
+        return ctypes.byref(e)
+
+    assert L.gsa_gemv_allreduce_rmsnorm(*good, None, None) == gsa.GSA_EINVAL  # no epilogue
+    for bad in [dict(y=None), dict(y_dtype=2), dict(y_dtype=-1), dict(eps=-1.0),
+                dict(eps=float("nan")), dict(eps=float("inf")), dict(y=P + 2),
+                dict(bias=P + 2), dict(rms_weight=P + 1), dict(inv_rms=P + 3)]:
+        assert L.gsa_gemv_allreduce_rmsnorm(*good, ep(**bad), None) == gsa.GSA_EINVAL, bad
+    # a bf16 y only needs 2-byte alignment; everything valid but the fake
+    # slots still fails the buffer registry check
+    assert L.gsa_gemv_allreduce_rmsnorm(*good, ep(y=P + 2, y_dtype=gsa.GSA_DTYPE_BF16),
+                                        None) == gsa.GSA_EINVAL
+    # N > 2^24 with the epilogue
+    big = (P, P, P, P, P, 1, 0, (1 << 24) + 1, 8, 1)
+    assert L.gsa_gemv_allreduce_rmsnorm(*big, ep(), None) == gsa.GSA_EINVAL
+
+
 def test_other_entry_points_reject_bad_arguments():
     L = _lib.lib()
     h = ctypes.c_void_p()

@@ -1,0 +1,211 @@
+"""GPU parity of the fused epilogue (bias, RMSNorm over rows, fp32 or bf16 y)
+through the C ABI (gsa_gemv_allreduce_rmsnorm), against the CPU oracle.
+
+Per call: `out` meets the usual bar (bound vs fp64, bit-exact rank-order
+fold of the slots read back); inv_rms is within an a-priori bound of the fp64
+value computed from z = fl32(out + bias); y is bit-identical to the fp32
+evaluation (z * inv) * w given the kernel's inv_rms (and its bf16 rounding).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gemv_shot_all_amd as gsa
+import gsa_inputs as gi
+import oracle
+from tests.gpu_util import Run, all_but, check_against_oracle
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -24
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def inv_rel_bound(N):
+    """Relative bound on the kernel's fp32 1/rms: the sum of squares runs 16
+    sequential adds per tile, ceil(T/64) per lane of the fold and a 6-level
+    lane tree (depth d), after one rounding per square; then a division by
+    N, the +eps, the square root (which halves the relative error) and the
+    reciprocal each round once."""
+    T = (N + 15) // 16
+    d = 16 + math.ceil(T / 64) + 6
+    return ((d + 3) / 2 + 3) * U
+
+
+class EpiRun:
+    def __init__(self, d, rank=None, bias=True, weight=True, eps=1e-5, y_dtype=torch.float32,
+                 seed=0, published_mask=None):
+        self.d = d
+        self.rank = d["rank"] if rank is None else rank
+        self.slots_in = d["slots"].copy()
+        self.r = Run(d["A"], d["x"], self.slots_in, self.rank, published_mask)
+        N, B = self.r.N, self.r.B
+        rng = np.random.default_rng(seed + 77)
+        self.bias = rng.normal(0, 0.5, N).astype(np.float32) if bias else None
+        self.w = rng.normal(1, 0.1, N).astype(np.float32) if weight else None
+        self.eps = eps
+        self.bias_t = None if self.bias is None else torch.from_numpy(self.bias).cuda()
+        self.w_t = None if self.w is None else torch.from_numpy(self.w).cuda()
+        self.y = torch.full((N, B), float("nan"), dtype=y_dtype, device="cuda")
+        self.inv = torch.full((B,), float("nan"), dtype=torch.float32, device="cuda")
+        self.ep = gsa.make_epilogue(self.y, self.bias_t, self.w_t, eps, self.inv)
+
+    def call(self):
+        r = self.r
+        gsa.gsa_gemv_allreduce_rmsnorm(r.A, r.x, r.buf.slots, r.buf.pad, r.out, r.W, self.rank,
+                                       r.N, r.K, r.B, self.ep)
+
+    def results(self):
+        out, slots, flags, status = self.r.results()
+        y = self.y.cpu()
+        y = (y.view(torch.int16).numpy().view(np.uint16) if self.y.dtype == torch.bfloat16
+             else y.numpy())
+        hdr = self.r.buf.pad_view()[:gsa.GSA_PAD_HEADER_WORDS].cpu().numpy()
+        return out, slots, y, self.inv.cpu().numpy(), status, hdr
+
+    def close(self):
+        self.r.close()
+
+
+def check_epilogue(er, out, slots_out, y, inv, what):
+    d = er.d
+    check_against_oracle(d["A"], d["x"], er.slots_in, er.rank, out, slots_out, what)
+    o = oracle.load()
+    z, inv64, y64 = o.bias_rmsnorm(out, er.bias, er.w, er.eps)
+    rel = inv_rel_bound(out.shape[0])
+    err = np.abs(inv.astype(np.float64) - inv64) / inv64
+    assert np.all(err <= rel), f"{what}: inv_rms rel err {err.max():.3g} > {rel:.3g}"
+    y32, ybf = o.scale_f32(z, inv, er.w)
+    if y.dtype == np.uint16:
+        assert np.array_equal(y, ybf), f"{what}: bf16 y differs from RNE of (z*inv)*w"
+    else:
+        assert np.array_equal(y.view(np.uint32), y32.view(np.uint32)), (
+            f"{what}: y differs from (z*inv)*w given the kernel's inv_rms")
+        # and close to the fp64 value
+        lim = np.abs(y64) * (rel + 3 * U) + 1e-30
+        assert np.all(np.abs(y.astype(np.float64) - y64) <= lim), f"{what}: y vs fp64"
+
+
+def run_epi_and_check(d, what, **kw):
+    er = EpiRun(d, **kw)
+    try:
+        er.call()
+        out, sl, y, inv, status, hdr = er.results()
+    finally:
+        er.close()
+    assert status == (gsa.GSA_OK, -1, -1), f"{what}: status {status}"
+    assert hdr[3] == 0, f"{what}: done count not reset ({hdr[3]})"
+    check_epilogue(er, out, sl, y, inv, what)
+
+
+@pytest.mark.parametrize("cfg", ["c1", "c2", "c3b4", "c4", "c5"])
+@pytest.mark.parametrize("ydt", ["f32", "bf16"])
+def test_config_epilogue(cfg, ydt):
+    _say(f"[epilogue] config {cfg} y={ydt}")
+    d = gi.make_inputs(cfg, seed=0, rank=0)
+    run_epi_and_check(d, f"{cfg}/{ydt}",
+                      y_dtype=torch.float32 if ydt == "f32" else torch.bfloat16)
+
+
+EDGE = [
+    # (W, N, Ks, B, rank, bias, weight, eps)
+    (2, 1000, 512, 1, 1, True, True, 1e-6),      # ragged N
+    (8, 17, 512, 3, 7, True, False, 1e-5),       # 2 tiles, the second with one row
+    (1, 1, 8, 1, 0, False, False, 1e-3),         # one row
+    (4, 50, 2048, 9, 3, False, True, 0.0),       # MFMA, ragged, eps = 0
+    (4, 4000, 256, 16, 1, True, True, 1e-5),     # MFMA, 250 tiles: several per fold lane
+    (8, 8192 + 16 * 65, 64, 2, 5, True, True, 1e-5),  # 577 tiles, short rows
+]
+
+
+@pytest.mark.parametrize("W,N,Ks,B,rank,bias,weight,eps", EDGE)
+def test_edge_epilogue(W, N, Ks, B, rank, bias, weight, eps):
+    _say(f"[epilogue] edge W={W} N={N} Ks={Ks} B={B} bias={bias} weight={weight} eps={eps}")
+    d = gi.make_shard_inputs(W, N, Ks, B, sigma=0.02, seed=3, cfg_id=3000 + N + B, rank=rank)
+    run_epi_and_check(d, f"W={W} N={N} Ks={Ks} B={B}", bias=bias, weight=weight, eps=eps)
+
+
+def test_repeats_bit_identical_and_mixed_with_plain_calls():
+    """Three epilogue calls with plain calls in between: the done count goes
+    back to 0 after each, y and inv_rms are bit-identical every time."""
+    _say("[epilogue] repeats")
+    d = gi.make_inputs("c2", seed=4, rank=0)
+    er = EpiRun(d, seed=4)
+    try:
+        ys, invs = [], []
+        for i in range(3):
+            er.call()
+            er.r.call()  # a plain call on the same buffer
+            out, sl, y, inv, status, hdr = er.results()
+            assert status == (gsa.GSA_OK, -1, -1) and hdr[3] == 0
+            ys.append(y.copy())
+            invs.append(inv.copy())
+        check_epilogue(er, out, sl, ys[-1], invs[-1], "repeats")
+    finally:
+        er.close()
+    for i in range(1, 3):
+        assert np.array_equal(ys[i].view(np.uint32), ys[0].view(np.uint32))
+        assert np.array_equal(invs[i].view(np.uint32), invs[0].view(np.uint32))
+
+
+def test_timeout_poisons_y_then_recovers():
+    """A withheld peer: the waits expire, y and inv_rms come out NaN, the
+    done count is back to 0; after a reset with the peer published the next
+    call is correct."""
+    _say("[epilogue] timeout")
+    W, rank = 4, 1
+    d = gi.make_shard_inputs(W, 64, 256, 2, seed=12, rank=rank)
+    gsa.gsa_set_wait_timeout_us(200)
+    try:
+        er = EpiRun(d, rank=rank, published_mask=all_but(W, rank) & ~(1 << 2))
+        try:
+            er.call()
+            out, sl, y, inv, status, hdr = er.results()
+            assert status[0] == gsa.GSA_ETIMEOUT
+            assert np.isnan(y).all() and np.isnan(inv).all(), "a failed call must poison y"
+            assert hdr[3] == 0, "done count reset even when tiles failed"
+            er.r.buf.reset(all_but(W, rank))
+            er.y.fill_(float("nan"))
+            er.r.out.fill_(float("nan"))
+            er.call()
+            out, sl, y, inv, status, hdr = er.results()
+            assert status == (gsa.GSA_OK, -1, -1)
+            check_epilogue(er, out, sl, y, inv, "after recovery")
+        finally:
+            er.close()
+    finally:
+        gsa.gsa_set_wait_timeout_us(100000)
+
+
+def test_graph_replays_match_eager():
+    """Calls captured in a HIP graph (the done count resets inside every
+    call): every replay gives the eager result, bit for bit."""
+    _say("[epilogue] graph replays")
+    d = gi.make_inputs("c3b4", seed=5, rank=0)
+    er = EpiRun(d, seed=5, y_dtype=torch.bfloat16)
+    try:
+        er.call()
+        out0, sl0, y0, inv0, status, hdr = er.results()
+        check_epilogue(er, out0, sl0, y0, inv0, "eager")
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for _ in range(3):
+                    er.call()
+        for rep in range(3):
+            er.y.fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            out, sl, y, inv, status, hdr = er.results()
+            assert status == (gsa.GSA_OK, -1, -1) and hdr[3] == 0
+            assert np.array_equal(y, y0) and np.array_equal(inv.view(np.uint32),
+                                                            inv0.view(np.uint32)), f"replay {rep}"
+    finally:
+        er.close()
