@@ -38,11 +38,13 @@ DEFAULT_CONFIG = "c2"  # Llama-3-8B o_proj decode, W=8 N=4096 K=4096 B=1
 KERNEL_SOURCE = os.path.join(ROOT, "gemv_shot_all_amd", "csrc", "gemv_allreduce.hip")
 
 
-def alg_bytes(W, N, K, B):
+def alg_bytes(W, N, K, B, epilogue=False):
     """Bytes the method itself must move per call: A_r, x_r, the published
-    slot, the W-1 peer slots and out (flags excluded)."""
+    slot, the W-1 peer slots and out (flags excluded); with the fused
+    epilogue also the bias and RMSNorm weight (N fp32 each) and y (bf16)."""
     Ks = K // W
-    return 2 * N * Ks + 2 * B * Ks + 4 * N * B + 4 * (W - 1) * N * B + 4 * N * B
+    base = 2 * N * Ks + 2 * B * Ks + 4 * N * B + 4 * (W - 1) * N * B + 4 * N * B
+    return base + (8 * N + 2 * N * B if epilogue else 0)
 
 
 def alg_flops(W, N, K, B):
@@ -73,13 +75,14 @@ class Sets:
     """R independent input sets on the device, each with its own symmetric
     buffer (peers published) and output."""
 
-    def __init__(self, d, rotate_bytes, max_sets=None):
+    def __init__(self, d, rotate_bytes, max_sets=None, epilogue=False):
         import torch
 
         import gemv_shot_all_amd as gsa
         self.gsa = gsa
         W, N, K, B = d["W"], d["N"], d["K"], d["B"]
         self.W, self.N, self.K, self.B, self.rank = W, N, K, B, d["rank"]
+        self.epilogue = epilogue
         foot = d["A"].nbytes + d["x"].nbytes + d["slots"].nbytes + 4 * N * B
         R = max(1, -(-rotate_bytes // foot))
         if max_sets:
@@ -99,13 +102,31 @@ class Sets:
             buf.slots_view().copy_(s0)
             buf.reset(mask)
             self.bufs.append(buf)
+        self.eps = []
+        if epilogue:
+            # bias ~ N(0, 0.5), RMSNorm weight ~ N(1, 0.1), eps 1e-5, y in bf16
+            rng = np.random.default_rng(1234)
+            bias = torch.from_numpy(rng.normal(0, 0.5, N).astype(np.float32)).cuda()
+            w = torch.from_numpy(rng.normal(1, 0.1, N).astype(np.float32)).cuda()
+            self.epi_tensors = []
+            for _ in range(R):
+                t = (bias.clone(), w.clone(),
+                     torch.empty((N, B), dtype=torch.bfloat16, device="cuda"),
+                     torch.empty(B, dtype=torch.float32, device="cuda"))
+                self.epi_tensors.append(t)
+                self.eps.append(gsa.make_epilogue(t[2], t[0], t[1], 1e-5, t[3]))
         torch.cuda.synchronize()
 
     def call(self, i):
         j = i % self.R
         b = self.bufs[j]
-        self.gsa.gsa_gemv_allreduce(self.A[j], self.x[j], b.slots, b.pad, self.out[j],
-                                    self.W, self.rank, self.N, self.K, self.B)
+        if self.epilogue:
+            self.gsa.gsa_gemv_allreduce_rmsnorm(self.A[j], self.x[j], b.slots, b.pad,
+                                                self.out[j], self.W, self.rank, self.N, self.K,
+                                                self.B, self.eps[j])
+        else:
+            self.gsa.gsa_gemv_allreduce(self.A[j], self.x[j], b.slots, b.pad, self.out[j],
+                                        self.W, self.rank, self.N, self.K, self.B)
 
     def close(self):
         for b in self.bufs:
@@ -115,6 +136,8 @@ class Sets:
 def check_parity(d, sets):
     """Every set's result (the first R calls touched each set once) against
     the oracle on set 0, and bit-equality of all sets with set 0."""
+    import torch
+
     import oracle
     out0 = sets.out[0].cpu().numpy()
     slot0 = sets.bufs[0].slots_view().cpu().numpy()
@@ -125,6 +148,15 @@ def check_parity(d, sets):
     for j in range(1, sets.R, max(1, sets.R // 8)):
         ok = ok and np.array_equal(sets.out[j].cpu().numpy().view(np.uint32),
                                    out0.view(np.uint32))
+    if sets.epilogue:
+        # y: the RNE bf16 of (z * inv) * w given the kernel's inv_rms, and
+        # inv_rms close to the fp64 value.
+        bias, w, y, inv = (t.cpu() for t in sets.epi_tensors[0])
+        o = oracle.load()
+        z, inv64, _ = o.bias_rmsnorm(out0, bias.numpy(), w.numpy(), 1e-5)
+        _, ybf = o.scale_f32(z, inv.numpy(), w.numpy())
+        ok = ok and np.array_equal(y.view(torch.int16).numpy().view(np.uint16), ybf)
+        ok = ok and bool(np.all(np.abs(inv.numpy() - inv64) <= 1e-5 * inv64))
     return ok, float(np.max(np.abs(out0 - out64) / bnd))
 
 
@@ -220,7 +252,7 @@ def run_config(cfg, args):
 
     d = gi.make_inputs(cfg, seed=args.seed, rank=0)
     W, N, K, B = d["W"], d["N"], d["K"], d["B"]
-    sets = Sets(d, args.rotate_mib << 20 if not args.warm else 1, args.max_sets)
+    sets = Sets(d, args.rotate_mib << 20 if not args.warm else 1, args.max_sets, args.epilogue)
     try:
         # Warm-up; it also touches every set once, which the parity check reads.
         for i in range(max(args.warmup, sets.R)):
@@ -280,9 +312,9 @@ def run_config(cfg, args):
     finally:
         sets.close()
 
-    nbytes = alg_bytes(W, N, K, B)
+    nbytes = alg_bytes(W, N, K, B, args.epilogue)
     achieved = nbytes / (us_per_call * 1e-6) / 1e9
-    traffic = traffic_from_profile(cfg)
+    traffic = None if args.epilogue else traffic_from_profile(cfg)
     line = {
         "metric": METRIC,
         "value": round(us_per_call, 4),
@@ -302,6 +334,8 @@ def run_config(cfg, args):
             "inputs": "cold: rotated over %d resident sets" % sets.R if not args.warm
                       else "warm: one set (Infinity-Cache resident, not HBM)",
             "timing": "hipGraph replay of K calls between two device syncs",
+            "epilogue": ("bias + RMSNorm over rows (eps 1e-5), y in bf16" if args.epilogue
+                         else "none"),
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
@@ -351,6 +385,8 @@ def main():
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="CPU-oracle wall-time budget, split between one thread and all "
                         "host threads (0 = skip)")
+    p.add_argument("--epilogue", action="store_true",
+                   help="time gsa_gemv_allreduce_rmsnorm (bias + RMSNorm, y in bf16) instead")
     p.add_argument("--no-probe", action="store_true",
                    help="skip the 1 GiB streaming-read bandwidth reference")
     p.add_argument("--copy-calibration-mib", type=int, default=0,

@@ -209,14 +209,22 @@ __device__ bool wait_peers(const GemvArgs& a, int lane, int64_t tile, uint32_t e
 //   the MFMA kernels: per-wave partials in LDS) | B2 own slot published, and
 //   the peer tile in LDS if the peers were ready at the start (compute wave 0
 //   then stores the flag) | B3 (only if they were not) late peer tile in LDS
-//   | with the fused epilogue: E1, E2 and, in the workgroup that finishes
-//   last, E3 (see fused_epilogue).
+//   | with the fused epilogue: E1, E2 and maybe E3, E4 (see fused_epilogue).
 // The peer loads stay in flight across B1: a workgroup barrier does not wait
 // for outstanding global loads.
+// With the epilogue the communication wave also counts the tile started (at
+// entry) and, once its protocol work is done, looks whether every tile of the
+// call has started (s_ctl[3]); s_epi_k gets the call's index.
 __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
-                          uint32_t* s_ctl) {
+                          uint32_t* s_ctl, unsigned long long* s_epi_k) {
   const uint32_t fl = load_flag(a, lane, tile);
   __syncthreads();  // B0: the flag load is issued ahead of every x and A load
+  // Count the tile started; the value is used only after the protocol work.
+  unsigned long long* started =
+      reinterpret_cast<unsigned long long*>(a.pad + kHdrEpiStart);
+  unsigned long long before = 0;
+  if (a.epi && lane == 0)
+    before = __hip_atomic_fetch_add(started, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t state = comm_decide(a, lane, tile, fl, s_ctl);
   float v[kMaxW][kPerLane];
   if (state == kPeersReady) issue_peer_tile(a, lane, tile, v);  // after the flags returned
@@ -234,9 +242,20 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
     __syncthreads();  // B3
   }
   if (a.epi) {
+    if (lane == 0) {
+      const unsigned long long k = before / (unsigned)a.tiles;
+      const unsigned long long all = (k + 1ull) * (unsigned)a.tiles;
+      const unsigned long long now =
+          __hip_atomic_load(started, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *s_epi_k = k;
+      s_ctl[3] = now >= all ? 1u : 0u;
+    }
     __syncthreads();  // E1
     __syncthreads();  // E2
-    if (s_ctl[2]) __syncthreads();  // E3 (last workgroup only)
+    if (s_ctl[3] || s_ctl[2]) {
+      __syncthreads();  // E3
+      __syncthreads();  // E4
+    }
   }
 }
 
@@ -261,11 +280,11 @@ __device__ __forceinline__ float one_shot_sum(const GemvArgs& a, float y, const 
   return acc;
 }
 
-template <int OPL>
+template <int BM, int OPL>
 __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
                                const bool (&own)[OPL], const bool (&live)[OPL],
                                const float (&o)[OPL], bool ok, float* elds, uint32_t* s_ctl,
-                               int wave, int lane, int nt);
+                               const unsigned long long* s_epi_k, int wave, int lane, int nt);
 
 // Compute waves once y is final (y[e] for local row n[e], column b, if own[e]:
 // every (row, column) of the tile has exactly one owner lane), `state` being
@@ -274,11 +293,12 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
 // Every compute wave waits for its own slot stores to complete before B2, so
 // the flag store that follows B2 is ordered after all of them.  nt: compute
 // threads of the workgroup.
-template <int OPL>
+template <int BM, int OPL>
 __device__ void publish_and_reduce(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
                                    const bool (&own)[OPL], const float (&y)[OPL],
                                    const float* pe, float* elds, uint32_t* s_ctl,
-                                   uint32_t state, int wave, int lane, int nt) {
+                                   const unsigned long long* s_epi_k, uint32_t state, int wave,
+                                   int lane, int nt) {
   const int64_t NB = a.N * a.B;
   const int64_t row0 = tile * kTileRows;
   float* own_slot = a.slots + a.rank * NB;
@@ -311,7 +331,8 @@ __device__ void publish_and_reduce(const GemvArgs& a, int64_t tile, const int (&
         *dst = o[e];
     }
   }
-  if (a.epi) fused_epilogue<OPL>(a, tile, n, b, own, live, o, ok, elds, s_ctl, wave, lane, nt);
+  if (a.epi)
+    fused_epilogue<BM, OPL>(a, tile, n, b, own, live, o, ok, elds, s_ctl, s_epi_k, wave, lane, nt);
 }
 
 // Sum of v over an aligned group of G lanes (G = 16, 32 or 64), returned in
@@ -354,6 +375,59 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// 1 / rms per column from every tile's published partials, computed by the
+// compute waves of the last tile in a fixed order: thread j (nt threads)
+// takes tiles j, j + nt, ... in ascending order, each wave sums its lanes
+// with the fixed lane tree, and the waves' sums are added in wave order.
+// Result in s_inv[0..B).  Contains the barrier E3.  BM >= B bounds the
+// registers it holds (the epilogue runs where the GEMV's registers are free,
+// and must not raise the kernel's register count).
+template <int BM>
+__device__ void fold_inv_rms(const GemvArgs& a, int wave, int lane, int nt, float* wsum,
+                             float* s_inv) {
+  float acc[BM];
+#pragma unroll
+  for (int c = 0; c < BM; ++c) acc[c] = 0.0f;
+  // The partials of two tiles are loaded before they are added.
+  for (int t0 = wave * 64 + lane; t0 < a.tiles; t0 += 2 * nt) {
+    float pv[2][BM];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = min(t0 + u * nt, a.tiles - 1);
+#pragma unroll
+      for (int c = 0; c < BM; ++c)
+        pv[u][c] = c < a.B ? load_coherent(&a.ssq[(int64_t)t * kEpiRecordWords + c]) : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (t0 + u * nt < a.tiles) {
+#pragma unroll
+        for (int c = 0; c < BM; ++c) acc[c] = acc[c] + pv[u][c];
+      }
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < BM; ++c) {
+    if (c < a.B) {
+      const float ws = group_sum<64>(acc[c]);
+      if (lane == 0) wsum[wave * 16 + c] = ws;
+    }
+  }
+  __syncthreads();  // E3: every wave's sums in LDS
+  if (wave == 0 && lane < a.B) {
+    float tot = 0.0f;
+    for (int w = 0; w < nt / 64; ++w) tot = tot + wsum[w * 16 + lane];
+    s_inv[lane] = 1.0f / sqrtf(tot / (float)a.N + a.eps);
+  }
+}
+
+__device__ __forceinline__ void store_y(const GemvArgs& a, int64_t i, float v) {
+  if (a.y_bf16)
+    static_cast<uint16_t*>(a.y)[i] = bf16_rne(v);
+  else
+    static_cast<float*>(a.y)[i] = v;
+}
+
 // The fused epilogue: bias, then RMSNorm over the N rows of every token
 // column, then y in fp32 or bf16 ("PyTorch Symmetric Memory" talk, real-model
 // example: the bias addition joins the reduction loop and the RMSNorm runs in
@@ -361,92 +435,160 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 // accumulation as in the documentation's higher-precision reduction).
 //   z = out + bias[n]; inv[b] = 1 / sqrtf(sum_n z^2 / N + eps);
 //   y = (z * inv[b]) * w[n]
-// The sum over n crosses workgroups: each tile sums its 16 squares per column
-// in row order, publishes the partial (coherent store), and counts itself
-// done in the pad header; the workgroup that completes the count folds the
-// partials in a fixed order (lane l takes tiles l, l + 64, ... in ascending
-// order, then a fixed lane tree), resets the count for the next call and
-// normalises every row.  A tile that failed (wait expired, bad own row)
-// contributes NaN, so y and inv come out NaN for that call.
-// Barriers: E1 (squares in LDS; every out store of the tile completed),
-// E2 (done count taken), E3 (last workgroup: inv in LDS).
-template <int OPL>
+// The sum over n crosses workgroups.  Each tile sums its 16 squares per
+// column in row order and publishes the partials (coherent stores) in its
+// record, then adds one to a 64-bit done count in the pad header.  Both this
+// count and the started count (taken at entry) only grow, so call k is
+// complete when they reach (k + 1) * tiles.  The tile whose add completes
+// the done count folds every partial (fold_inv_rms), publishes inv and then
+// a flag holding k + 1 (after the inv stores completed).
+//  - A tile that saw every tile of its call started (s_ctl[3], looked up by
+//    the communication wave) may wait: every other tile is resident or done
+//    and finishes on its own.  It marks its record with k + 1, waits
+//    (bounded) for the flag, reads inv and normalises its own rows from
+//    registers.
+//  - Any other tile marks 0 and leaves; the last tile also normalises the
+//    rows of every tile not marked k + 1, re-reading out (stored coherently
+//    for this).
+// A tile that failed (wait expired, bad own row) contributes NaN, so y comes
+// out NaN for that call.  Barriers: E1 (squares in LDS, out stores
+// completed), E2 (count taken), then, in the last tile and in waiting tiles,
+// E3 (wave sums in LDS, or the flag seen) and E4 (inv in LDS).
+template <int BM, int OPL>
 __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
                                const bool (&own)[OPL], const bool (&live)[OPL],
                                const float (&o)[OPL], bool ok, float* elds, uint32_t* s_ctl,
-                               int wave, int lane, int nt) {
-  float* zz = elds;           // [16 rows][16 columns] squares of z
-  float* s_inv = elds + 256;  // [16] 1 / rms per column
+                               const unsigned long long* s_epi_k, int wave, int lane, int nt) {
+  float* zz = elds;            // [16 rows][16 columns] squares of z
+  float* s_inv = elds + 256;   // [16] 1 / rms per column
+  float* wsum = elds + 272;    // [8 waves][16 columns] the fold's wave sums
   const int64_t row0 = tile * kTileRows;
+  float z[OPL];
 #pragma unroll
   for (int e = 0; e < OPL; ++e) {
+    z[e] = 0.0f;
     if (own[e]) {
       float sq = 0.0f;  // rows past N add nothing
       if (live[e]) {
-        const float z = o[e] + (a.bias ? a.bias[row0 + n[e]] : 0.0f);
-        sq = z * z;
+        z[e] = o[e] + (a.bias ? a.bias[row0 + n[e]] : 0.0f);
+        sq = z[e] * z[e];
       }
       zz[n[e] * 16 + b] = ok ? sq : __builtin_nanf("");
     }
   }
   wait_vm_all();    // this wave's out stores are at the coherence point ...
   __syncthreads();  // E1 ... in every compute wave, and the squares are in LDS
+  const unsigned long long k = *s_epi_k;
+  const unsigned long long target = (k + 1ull) * (unsigned)a.tiles;
+  const uint32_t mark = (uint32_t)(k + 1ull);
+  const bool waits = s_ctl[3] != 0;
+  unsigned long long* done = reinterpret_cast<unsigned long long*>(a.pad + kHdrEpiCount);
+  float* rec = a.ssq + tile * kEpiRecordWords;
+  float* inv_pub = a.ssq + (int64_t)a.tiles * kEpiRecordWords;  // [16] inv, then the flag
+  uint32_t* inv_flag = reinterpret_cast<uint32_t*>(inv_pub + 16);
   if (wave == 0) {
     if (lane < a.B) {
       float part = 0.0f;
       for (int r = 0; r < kTileRows; ++r) part = part + zz[r * 16 + lane];
-      store_coherent(&a.ssq[tile * 16 + lane], part);
+      store_coherent(&rec[lane], part);
     }
-    wait_vm_all();  // the partials are at the coherence point before the count
+    if (lane == 16)
+      __hip_atomic_store(reinterpret_cast<uint32_t*>(rec + 16), waits ? mark : 0u,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_vm_all();  // the record is at the coherence point before the count
     if (lane == 0) {
-      const uint32_t done =
-          __hip_atomic_fetch_add(&a.pad[kHdrEpiCount], 1u, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT) + 1u;
-      const uint32_t last = done == (uint32_t)a.tiles ? 1u : 0u;
-      if (last)  // every tile of this call has counted itself: ready for the next call
-        __hip_atomic_store(&a.pad[kHdrEpiCount], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_ctl[2] = last;
+      const unsigned long long before =
+          __hip_atomic_fetch_add(done, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_ctl[2] = before + 1ull == target ? 1u : 0u;
     }
   }
   __syncthreads();  // E2
-  if (!s_ctl[2]) return;
+  const bool last = s_ctl[2] != 0;
+  if (!last && !waits) return;
 
-  // The last workgroup.  Its loads of partials and outputs are issued only
-  // after the count it took showed every tile done (they sit behind a branch
-  // on that value), and each tile made its stores complete before counting.
-  if (wave == 0) {
-    float acc[GSA_MAX_B];
-#pragma unroll
-    for (int c = 0; c < GSA_MAX_B; ++c) acc[c] = 0.0f;
-    for (int t = lane; t < a.tiles; t += 64) {
-#pragma unroll
-      for (int c = 0; c < GSA_MAX_B; ++c)
-        if (c < a.B) acc[c] = acc[c] + load_coherent(&a.ssq[(int64_t)t * 16 + c]);
+  if (last) {
+    // Every tile has published: fold, then publish inv and the flag.
+    fold_inv_rms<BM>(a, wave, lane, nt, wsum, s_inv);  // contains E3
+    if (wave == 0) {
+      if (lane < a.B) {
+        store_coherent(&inv_pub[lane], s_inv[lane]);
+        if (a.inv_rms) a.inv_rms[lane] = s_inv[lane];
+      }
+      wait_vm_all();  // inv at the coherence point before the flag
+      if (lane == 0)
+        __hip_atomic_store(inv_flag, mark, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-#pragma unroll
-    for (int c = 0; c < GSA_MAX_B; ++c) {
-      if (c < a.B) {
-        const float tot = group_sum<64>(acc[c]);
-        const float inv = 1.0f / sqrtf(tot / (float)a.N + a.eps);
-        if (lane == 0) {
-          s_inv[c] = inv;
-          if (a.inv_rms) a.inv_rms[c] = inv;
+  } else {
+    if (wave == 0 && lane == 0) {
+      bool seen = true;
+      const uint64_t start = wall_clock64();
+      // Other tiles may still be in their bounded peer waits: allow twice that.
+      while (__hip_atomic_load(inv_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != mark) {
+        if (wall_clock64() - start > 2 * a.timeout_ticks + 1000000ull) {
+          atomicOr(a.pad + kHdrErrorBits, kErrEpiWait);
+          atomicMin(a.pad + kHdrEpiWaitTile, (uint32_t)tile);
+          seen = false;
+          break;
         }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      s_ctl[1] = seen ? 1u : 0u;  // the protocol state is no longer needed
+    }
+    __syncthreads();  // E3: the flag seen (or the wait expired)
+    // inv is loaded only after the flag showed it published.
+    if (wave == 0 && lane < a.B)
+      s_inv[lane] = s_ctl[1] ? load_coherent(&inv_pub[lane]) : __builtin_nanf("");
+  }
+  __syncthreads();  // E4: inv in LDS
+  if (waits) {
+#pragma unroll
+    for (int e = 0; e < OPL; ++e) {
+      if (live[e]) {
+        float v = z[e] * s_inv[b];
+        if (a.rms_w) v = v * a.rms_w[row0 + n[e]];
+        if (!ok) v = __builtin_nanf("");
+        store_y(a, (row0 + n[e]) * a.B + b, v);
       }
     }
   }
-  __syncthreads();  // E3
+  if (!last) return;
+
+  // The last tile: the rows of every tile not marked k + 1 (in the common
+  // case, where every tile saw all tiles started, there are none).  Thread j
+  // takes tiles j, j + nt, ...; a tile's outputs go four at a time, all
+  // loads of a batch before its stores.  The loads of marks and outputs are
+  // issued only after the count this tile took showed every tile done (they
+  // sit behind a branch on that value).
+  constexpr int kBatch = 4;
   const int64_t NB = a.N * a.B;
-  for (int64_t i = (int64_t)wave * 64 + lane; i < NB; i += nt) {
-    const int64_t r = i / a.B;
-    const int c = (int)(i - r * a.B);
-    const float z = load_coherent(&a.out[i]) + (a.bias ? a.bias[r] : 0.0f);
-    float v = z * s_inv[c];
-    if (a.rms_w) v = v * a.rms_w[r];
-    if (a.y_bf16)
-      static_cast<uint16_t*>(a.y)[i] = bf16_rne(v);
-    else
-      static_cast<float*>(a.y)[i] = v;
+  for (int t = wave * 64 + lane; t < a.tiles; t += nt) {
+    const uint32_t m = __hip_atomic_load(
+        reinterpret_cast<const uint32_t*>(a.ssq + (int64_t)t * kEpiRecordWords + 16),
+        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (m == mark) continue;
+    const int64_t lo = (int64_t)t * kTileRows * a.B;
+    const int64_t hi = min(NB, lo + (int64_t)kTileRows * a.B);
+    for (int64_t i0 = lo; i0 < hi; i0 += kBatch) {
+      float ov[kBatch], bv[kBatch], wv[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int64_t i = min(i0 + u, hi - 1);
+        const int64_t r = i / a.B;
+        ov[u] = load_coherent(&a.out[i]);
+        bv[u] = a.bias ? a.bias[r] : 0.0f;
+        wv[u] = a.rms_w ? a.rms_w[r] : 1.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int64_t i = i0 + u;
+        if (i < hi) {
+          const int c = (int)(i % a.B);
+          float v = (ov[u] + bv[u]) * s_inv[c];
+          if (a.rms_w) v = v * wv[u];
+          store_y(a, i, v);
+        }
+      }
+    }
   }
 }
 
@@ -528,6 +670,7 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
 
   extern __shared__ uint4 lds_x[];
   __shared__ uint32_t s_ctl[4];
+  __shared__ unsigned long long s_epi_k;  // the epilogue's call index
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -540,7 +683,7 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   float* elds = pe + a.W * kTileRows * B + 1;  // the epilogue's LDS
 
   if (wave == NW) {
-    comm_wave(a, lane, tile, pe, s_ctl);
+    comm_wave(a, lane, tile, pe, s_ctl, &s_epi_k);
     return;
   }
 
@@ -594,7 +737,8 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   const int n[1] = {nloc0 + vidx / B};
   const bool own[1] = {li < V};
   const float y[1] = {yv};
-  publish_and_reduce<1>(a, tile, n, vidx % B, own, y, pe, elds, s_ctl, state, wave, lane, NT);
+  publish_and_reduce<B, 1>(a, tile, n, vidx % B, own, y, pe, elds, s_ctl, &s_epi_k, state, wave,
+                           lane, NT);
 }
 
 // MFMA epilogue: each wave's 16 x 16 partial goes to red[wave][n][b]; after
@@ -603,7 +747,8 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
 template <int NW>
 __device__ __forceinline__ void mfma_finish(const GemvArgs& a, int64_t tile, int wave, int lane,
                                             f32x4_t acc, float* red, const float* pe,
-                                            float* elds, uint32_t* s_ctl) {
+                                            float* elds, uint32_t* s_ctl,
+                                            const unsigned long long* s_epi_k) {
 #pragma unroll
   for (int e = 0; e < 4; ++e)
     red[(wave * kTileRows + 4 * (lane >> 4) + e) * 16 + (lane & 15)] = acc[e];
@@ -617,7 +762,8 @@ __device__ __forceinline__ void mfma_finish(const GemvArgs& a, int64_t tile, int
   const int n[1] = {nl};
   const bool own[1] = {bl < a.B};
   const float yv[1] = {y};
-  publish_and_reduce<1>(a, tile, n, bl, own, yv, pe, elds, s_ctl, state, wave, lane, NW * 64);
+  publish_and_reduce<GSA_MAX_B, 1>(a, tile, n, bl, own, yv, pe, elds, s_ctl, s_epi_k, state,
+                                   wave, lane, NW * 64);
 }
 
 // Copy 16 bytes per active lane from global memory straight into LDS: lane l
@@ -647,6 +793,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs a) {
   static_assert(NW * 4 == kTileRows, "each compute wave finishes 4 rows of the tile");
   extern __shared__ uint4 lds[];
   __shared__ uint32_t s_ctl[4];
+  __shared__ unsigned long long s_epi_k;  // the epilogue's call index
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -659,7 +806,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs a) {
   float* elds = pe + a.W * kTileRows * a.B + 1;  // the epilogue's LDS
 
   if (wave == NW) {
-    comm_wave(a, lane, tile, pe, s_ctl);
+    comm_wave(a, lane, tile, pe, s_ctl, &s_epi_k);
     return;
   }
 
@@ -726,7 +873,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs a) {
     }
   }
 
-  mfma_finish<NW>(a, tile, wave, lane, acc, red, pe, elds, s_ctl);
+  mfma_finish<NW>(a, tile, wave, lane, acc, red, pe, elds, s_ctl, &s_epi_k);
 }
 
 // MFMA path for x beyond the LDS bound (8 < B <= 16, 16 * (C + 1) chunks over
@@ -741,6 +888,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a
   static_assert(NW * 4 == kTileRows, "each compute wave finishes 4 rows of the tile");
   extern __shared__ uint4 lds[];
   __shared__ uint32_t s_ctl[4];
+  __shared__ unsigned long long s_epi_k;  // the epilogue's call index
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -752,7 +900,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a
   float* elds = pe + a.W * kTileRows * a.B + 1;  // the epilogue's LDS
 
   if (wave == NW) {
-    comm_wave(a, lane, tile, pe, s_ctl);
+    comm_wave(a, lane, tile, pe, s_ctl, &s_epi_k);
     return;
   }
 
@@ -804,16 +952,18 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  mfma_finish<NW>(a, tile, wave, lane, acc, red, pe, elds, s_ctl);
+  mfma_finish<NW>(a, tile, wave, lane, acc, red, pe, elds, s_ctl, &s_epi_k);
 }
 
-__global__ void pad_reset_kernel(uint32_t* pad, int W, int row_stride, uint32_t mask) {
+__global__ void pad_reset_kernel(uint32_t* pad, int W, int row_stride, uint32_t mask,
+                                 uint32_t* epi_flag) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i == 0) *epi_flag = 0u;  // the epilogue's published-inv flag restarts with the counts
   const int64_t total = GSA_PAD_HEADER_WORDS + (int64_t)W * row_stride;
   if (i >= total) return;
   uint32_t v;
   if (i < GSA_PAD_HEADER_WORDS) {
-    v = (i == kHdrTimeoutKey || i == kHdrStateTile) ? 0xFFFFFFFFu : 0u;
+    v = (i == kHdrTimeoutKey || i == kHdrStateTile || i == kHdrEpiWaitTile) ? 0xFFFFFFFFu : 0u;
   } else {
     const int r = (int)((i - GSA_PAD_HEADER_WORDS) / row_stride);
     v = ((mask >> r) & 1u) ? GSA_FLAG_PUBLISHED : 0u;
@@ -866,9 +1016,10 @@ ValuChoice valu_kernel(int C) {
 }  // namespace
 
 size_t gemv_lds_bytes(int W, int B, int C, bool epi) {
-  // The peer tile, then (with the epilogue) 16 x 16 squares and 16 1/rms.
+  // The peer tile, then (with the epilogue) 16 x 16 squares, 16 1/rms and
+  // up to 8 waves x 16 partial sums.
   const size_t tail = ((size_t)W * kTileRows * B + 1) * sizeof(float) +
-                      (epi ? (size_t)(256 + 16) * sizeof(float) : 0);
+                      (epi ? (size_t)(256 + 16 + 8 * 16) * sizeof(float) : 0);
   const size_t partials = (size_t)kMfmaWaves * kTileRows * 16 * sizeof(float);
   if (B <= 8) return ((size_t)B * C + 2) * 16 + tail;
   if (mfma_x_in_lds(C)) return (size_t)16 * (C + 1) * 16 + partials + tail;
@@ -906,13 +1057,14 @@ hipError_t launch_gemv(const Launch& l, const GemvArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_pad_reset(uint32_t* pad, int W, int row_stride, int tiles,
-                            uint32_t published_mask, hipStream_t s) {
-  (void)tiles;
+                            uint32_t published_mask, float* epi_scratch, hipStream_t s) {
+  uint32_t* epi_flag =
+      reinterpret_cast<uint32_t*>(epi_scratch + (int64_t)tiles * kEpiRecordWords + 16);
   const int64_t total = GSA_PAD_HEADER_WORDS + (int64_t)W * row_stride;
   const unsigned block = 256;
   const unsigned grid = (unsigned)((total + block - 1) / block);
   hipLaunchKernelGGL(pad_reset_kernel, dim3(grid), dim3(block), 0, s, pad, W, row_stride,
-                     published_mask);
+                     published_mask, epi_flag);
   return hipGetLastError();
 }
 

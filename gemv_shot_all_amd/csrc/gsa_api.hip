@@ -100,7 +100,9 @@ int gsa_symm_alloc(int W, int64_t N, int B, gsa_symm** out) {
   const size_t slot_bytes = round_up((size_t)W * (size_t)N * (size_t)B * sizeof(float), kAlign);
   const size_t pad_words = GSA_PAD_HEADER_WORDS + (size_t)W * (size_t)stride;
   const size_t pad_bytes = round_up(pad_words * sizeof(uint32_t), kAlign);
-  const size_t ssq_bytes = round_up((size_t)tiles_of(N) * 16 * sizeof(float), kAlign);
+  // The epilogue's scratch: one record per tile, then 1/rms and its flag.
+  const size_t ssq_bytes =
+      round_up(((size_t)tiles_of(N) + 1) * gsa::kEpiRecordWords * sizeof(float), kAlign);
   const size_t bytes = slot_bytes + pad_bytes + ssq_bytes;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return GSA_EHIP;
@@ -113,6 +115,7 @@ int gsa_symm_alloc(int W, int64_t N, int B, gsa_symm** out) {
   uint32_t hdr[GSA_PAD_HEADER_WORDS] = {0};
   hdr[gsa::kHdrTimeoutKey] = 0xFFFFFFFFu;
   hdr[gsa::kHdrStateTile] = 0xFFFFFFFFu;
+  hdr[gsa::kHdrEpiWaitTile] = 0xFFFFFFFFu;
   if (hipMemset(base, 0, bytes) != hipSuccess ||
       hipMemcpy(pad, hdr, sizeof hdr, hipMemcpyHostToDevice) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
@@ -164,15 +167,17 @@ int gsa_signal_pad_reset(uint32_t* pad, int W, int64_t N, uint32_t published_mas
   if (!pad || W < 1 || W > GSA_MAX_W || N < 1) return GSA_EINVAL;
   if (published_mask >> W) return GSA_EINVAL;
   int64_t stride, tiles;
+  float* epi_scratch;
   {
     std::lock_guard<std::mutex> lk(g_mu);
     gsa_symm* h = find_by_pad(pad);
     if (!h || h->W != W || h->N != N) return GSA_EINVAL;
     stride = h->row_stride;
     tiles = h->tiles;
+    epi_scratch = h->ssq;
   }
   hipError_t e = gsa::launch_pad_reset(pad, W, (int)stride, (int)tiles, published_mask,
-                                       static_cast<hipStream_t>(stream));
+                                       epi_scratch, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? GSA_OK : GSA_EHIP;
 }
 
@@ -285,7 +290,9 @@ int gsa_signal_pad_status(const uint32_t* pad, void* stream, int* code, int64_t*
       hipStreamSynchronize(s) != hipSuccess)
     return GSA_EHIP;
   const uint32_t bits = hdr[gsa::kHdrErrorBits];
-  *code = (bits & gsa::kErrState) ? GSA_ESTATE : (bits & gsa::kErrTimeout) ? GSA_ETIMEOUT : GSA_OK;
+  *code = (bits & gsa::kErrState) ? GSA_ESTATE
+          : (bits & (gsa::kErrTimeout | gsa::kErrEpiWait)) ? GSA_ETIMEOUT
+                                                          : GSA_OK;
   const uint32_t key = hdr[gsa::kHdrTimeoutKey];
   *tile = -1;
   *peer = -1;
@@ -294,6 +301,8 @@ int gsa_signal_pad_status(const uint32_t* pad, void* stream, int* code, int64_t*
   } else if (key != 0xFFFFFFFFu) {
     *tile = (int64_t)(key / 8u);
     *peer = (int)(key % 8u);
+  } else if (bits & gsa::kErrEpiWait) {
+    *tile = (int64_t)hdr[gsa::kHdrEpiWaitTile];
   }
   return GSA_OK;
 }

@@ -14,9 +14,14 @@ enum : int {
   kHdrErrorBits = 0,   // atomicOr: kErrTimeout | kErrState
   kHdrTimeoutKey = 1,  // atomicMin of tile * 8 + peer, 0xFFFFFFFF = none
   kHdrStateTile = 2,   // atomicMin of the tile with a bad own flag row
-  kHdrEpiCount = 3,    // epilogue: tiles of the running call that are done (0 between calls)
+  kHdrEpiCount = 4,    // epilogue: 64-bit count of finished tiles over all calls (words 4, 5)
+  kHdrEpiWaitTile = 6, // atomicMin of a tile whose epilogue wait expired, 0xFFFFFFFF = none
+  kHdrEpiStart = 8,    // epilogue: 64-bit count of started tiles over all calls (words 8, 9)
 };
-enum : uint32_t { kErrTimeout = 1u, kErrState = 2u };
+// The epilogue's per-tile record in the scratch: 16 partial sums (one per
+// column), then the call mark (uint32) at word 16.
+constexpr int kEpiRecordWords = 32;
+enum : uint32_t { kErrTimeout = 1u, kErrState = 2u, kErrEpiWait = 4u };
 
 // Everything one launch needs.  Built on the host per call, passed by value.
 struct GemvArgs {
@@ -42,7 +47,7 @@ struct GemvArgs {
   const float* rms_w;     // N fp32 or null
   void* y;                // N x B
   float* inv_rms;         // B fp32 or null
-  float* ssq;             // tiles x 16 fp32 partial sums of squares (library scratch)
+  float* ssq;             // tiles x kEpiRecordWords: partial sums of squares + mark (scratch)
 };
 
 // A ready-to-launch kernel choice for one (B, C) shape.
@@ -60,7 +65,9 @@ bool select_gemv_kernel(int W, int B, int C, bool epi, Launch* out);
 size_t gemv_lds_bytes(int W, int B, int C, bool epi);
 
 hipError_t launch_gemv(const Launch& l, const GemvArgs& a, hipStream_t s);
+// Also clears the fused epilogue's published-inv flag in epi_scratch (the
+// buffer's tiles x kEpiRecordWords records, then inv and the flag).
 hipError_t launch_pad_reset(uint32_t* pad, int W, int row_stride, int tiles,
-                            uint32_t published_mask, hipStream_t s);
+                            uint32_t published_mask, float* epi_scratch, hipStream_t s);
 
 }  // namespace gsa

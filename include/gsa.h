@@ -94,7 +94,8 @@ uint32_t *gsa_symm_signal_pad(const gsa_symm *h);
 int64_t gsa_signal_pad_row_stride(int64_t N);
 
 /* Reset a pad: flag row p := GSA_FLAG_PUBLISHED if bit p of published_mask
- * is set, else 0; status words cleared.  Stream-ordered (a small kernel), no
+ * is set, else 0; status words and the fused epilogue's counts cleared (and
+ * its library-held scratch made ready for them).  Stream-ordered (a small kernel), no
  * host sync, no allocation.  `pad` [device] must come from
  * gsa_symm_signal_pad of a buffer allocated with the same W and N.  The
  * calling rank's bit must be clear before it calls gsa_gemv_allreduce.
@@ -150,10 +151,16 @@ typedef struct gsa_epilogue {
 /* gsa_gemv_allreduce (same arguments, same contract, `out` written as
  * there), followed in the same kernel by the epilogue `ep` [host, read
  * before return].  The sum over n crosses tiles: each tile publishes its
- * partial sums of squares, counts itself done in the pad header, and the
- * tile that completes the count folds the partials in a fixed order and
- * normalises all N rows, so repeated calls are bit-identical.  If any tile
- * of the call failed (see gsa_signal_pad_status), y and inv_rms are NaN.
+ * partial sums of squares and counts itself done in the pad header (a count
+ * that only grows, cleared by gsa_signal_pad_reset); 1/rms is the fold of
+ * the partials in one fixed order, so repeated calls are bit-identical.
+ * When the whole grid fits on the GPU at once (the occupancy the library
+ * queries), every tile waits for the count, folds and normalises its own
+ * rows; otherwise the tile that completes the count normalises all N rows.
+ * Both give the same bits.  The tile-side wait is bounded (twice the
+ * timeout of gsa_set_wait_timeout_us); if it expires, gsa_signal_pad_status
+ * reports GSA_ETIMEOUT with that tile and peer -1.  If any tile of the call
+ * failed, y and inv_rms are NaN.
  * Requires N <= 2^24 in addition.  Errors: GSA_EINVAL (also: ep or y NULL,
  * unknown y_dtype, misaligned pointer, eps negative or not finite),
  * GSA_EHIP. */

@@ -92,6 +92,13 @@ def check_epilogue(er, out, slots_out, y, inv, what):
         assert np.all(np.abs(y.astype(np.float64) - y64) <= lim), f"{what}: y vs fp64"
 
 
+def done_count(hdr, word=4):
+    """The epilogue's 64-bit count of finished tiles (pad header words 4-5;
+    word=8: the count of started tiles, words 8-9)."""
+    h = hdr.astype(np.int64) & 0xFFFFFFFF
+    return int(h[word]) | (int(h[word + 1]) << 32)
+
+
 def run_epi_and_check(d, what, **kw):
     er = EpiRun(d, **kw)
     try:
@@ -100,7 +107,8 @@ def run_epi_and_check(d, what, **kw):
     finally:
         er.close()
     assert status == (gsa.GSA_OK, -1, -1), f"{what}: status {status}"
-    assert hdr[3] == 0, f"{what}: done count not reset ({hdr[3]})"
+    assert done_count(hdr) == er.r.buf.tiles, f"{what}: done count {done_count(hdr)}"
+    assert done_count(hdr, 8) == er.r.buf.tiles, f"{what}: started count"
     check_epilogue(er, out, sl, y, inv, what)
 
 
@@ -121,6 +129,8 @@ EDGE = [
     (4, 50, 2048, 9, 3, False, True, 0.0),       # MFMA, ragged, eps = 0
     (4, 4000, 256, 16, 1, True, True, 1e-5),     # MFMA, 250 tiles: several per fold lane
     (8, 8192 + 16 * 65, 64, 2, 5, True, True, 1e-5),  # 577 tiles, short rows
+    (2, 65536, 64, 1, 0, True, True, 1e-5),     # 4096 tiles: more than fit at once
+    (2, 16 * 6000 + 5, 64, 3, 1, True, False, 1e-4),  # 6001 tiles, ragged
 ]
 
 
@@ -132,8 +142,9 @@ def test_edge_epilogue(W, N, Ks, B, rank, bias, weight, eps):
 
 
 def test_repeats_bit_identical_and_mixed_with_plain_calls():
-    """Three epilogue calls with plain calls in between: the done count goes
-    back to 0 after each, y and inv_rms are bit-identical every time."""
+    """Three epilogue calls with plain calls in between: the done count grows
+    by the tile count with every epilogue call (plain calls leave it alone),
+    y and inv_rms are bit-identical every time."""
     _say("[epilogue] repeats")
     d = gi.make_inputs("c2", seed=4, rank=0)
     er = EpiRun(d, seed=4)
@@ -143,7 +154,8 @@ def test_repeats_bit_identical_and_mixed_with_plain_calls():
             er.call()
             er.r.call()  # a plain call on the same buffer
             out, sl, y, inv, status, hdr = er.results()
-            assert status == (gsa.GSA_OK, -1, -1) and hdr[3] == 0
+            assert status == (gsa.GSA_OK, -1, -1)
+            assert done_count(hdr) == (i + 1) * er.r.buf.tiles
             ys.append(y.copy())
             invs.append(inv.copy())
         check_epilogue(er, out, sl, ys[-1], invs[-1], "repeats")
@@ -155,9 +167,9 @@ def test_repeats_bit_identical_and_mixed_with_plain_calls():
 
 
 def test_timeout_poisons_y_then_recovers():
-    """A withheld peer: the waits expire, y and inv_rms come out NaN, the
-    done count is back to 0; after a reset with the peer published the next
-    call is correct."""
+    """A withheld peer: the waits expire, y and inv_rms come out NaN, yet
+    every tile still counts itself done; after a reset with the peer
+    published the next call is correct."""
     _say("[epilogue] timeout")
     W, rank = 4, 1
     d = gi.make_shard_inputs(W, 64, 256, 2, seed=12, rank=rank)
@@ -169,7 +181,7 @@ def test_timeout_poisons_y_then_recovers():
             out, sl, y, inv, status, hdr = er.results()
             assert status[0] == gsa.GSA_ETIMEOUT
             assert np.isnan(y).all() and np.isnan(inv).all(), "a failed call must poison y"
-            assert hdr[3] == 0, "done count reset even when tiles failed"
+            assert done_count(hdr) == er.r.buf.tiles, "every tile counts itself, failed or not"
             er.r.buf.reset(all_but(W, rank))
             er.y.fill_(float("nan"))
             er.r.out.fill_(float("nan"))
@@ -184,8 +196,8 @@ def test_timeout_poisons_y_then_recovers():
 
 
 def test_graph_replays_match_eager():
-    """Calls captured in a HIP graph (the done count resets inside every
-    call): every replay gives the eager result, bit for bit."""
+    """Calls captured in a HIP graph (no host-held state: the done count
+    only grows): every replay gives the eager result, bit for bit."""
     _say("[epilogue] graph replays")
     d = gi.make_inputs("c3b4", seed=5, rank=0)
     er = EpiRun(d, seed=5, y_dtype=torch.bfloat16)
@@ -204,7 +216,8 @@ def test_graph_replays_match_eager():
             g.replay()
             torch.cuda.synchronize()
             out, sl, y, inv, status, hdr = er.results()
-            assert status == (gsa.GSA_OK, -1, -1) and hdr[3] == 0
+            assert status == (gsa.GSA_OK, -1, -1)
+            assert done_count(hdr) == (4 + 3 * rep) * er.r.buf.tiles
             assert np.array_equal(y, y0) and np.array_equal(inv.view(np.uint32),
                                                             inv0.view(np.uint32)), f"replay {rep}"
     finally:
