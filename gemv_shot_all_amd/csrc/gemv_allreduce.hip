@@ -37,6 +37,8 @@
 // (acquire) per workgroup would cost several microseconds per call.  Across
 // GPUs the same scheme runs at system scope.
 
+#include <algorithm>
+
 #include "gsa_internal.h"
 
 namespace gsa {
@@ -199,6 +201,15 @@ __device__ bool wait_peers(const GemvArgs& a, int lane, int64_t tile, uint32_t e
   }
 }
 
+// The fused epilogue's grouped counts (see kEpiGroups): tile t is in group
+// t % kEpiGroups, which holds epi_group_tiles(g) of the call's tiles.
+__device__ __forceinline__ int epi_group_tiles(const GemvArgs& a, int g) {
+  return g < a.tiles ? (a.tiles - g + kEpiGroups - 1) / kEpiGroups : 0;
+}
+__device__ __forceinline__ unsigned long long* epi_count(const GemvArgs& a, int64_t off, int g) {
+  return reinterpret_cast<unsigned long long*>(a.ssq + off + (int64_t)g * kEpiRecordWords);
+}
+
 // The communication wave (the last wave of every workgroup) runs the
 // signal-pad protocol, so its round trips never hold up the A stream of the
 // compute waves.  A CU returns vector loads in issue order, so the flag load
@@ -212,19 +223,20 @@ __device__ bool wait_peers(const GemvArgs& a, int lane, int64_t tile, uint32_t e
 //   | with the fused epilogue: E1, E2 and maybe E3, E4 (see fused_epilogue).
 // The peer loads stay in flight across B1: a workgroup barrier does not wait
 // for outstanding global loads.
-// With the epilogue the communication wave also counts the tile started (at
-// entry) and, once its protocol work is done, looks whether every tile of the
-// call has started (s_ctl[3]); s_epi_k gets the call's index.
+// With the epilogue the communication wave also counts the tile started in
+// its group (after B0) and, once its protocol work is done, looks whether
+// every tile of the call has started (s_ctl[3]: lane g reads group g's
+// count); s_epi_k gets the call's index.
 __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
                           uint32_t* s_ctl, unsigned long long* s_epi_k) {
   const uint32_t fl = load_flag(a, lane, tile);
   __syncthreads();  // B0: the flag load is issued ahead of every x and A load
   // Count the tile started; the value is used only after the protocol work.
-  unsigned long long* started =
-      reinterpret_cast<unsigned long long*>(a.pad + kHdrEpiStart);
+  const int grp = (int)(tile % kEpiGroups);
   unsigned long long before = 0;
   if (a.epi && lane == 0)
-    before = __hip_atomic_fetch_add(started, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    before = __hip_atomic_fetch_add(epi_count(a, epi_started_off(a.tiles), grp), 1ull,
+                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t state = comm_decide(a, lane, tile, fl, s_ctl);
   float v[kMaxW][kPerLane];
   if (state == kPeersReady) issue_peer_tile(a, lane, tile, v);  // after the flags returned
@@ -242,13 +254,22 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
     __syncthreads();  // B3
   }
   if (a.epi) {
+    // The call's index k (every tile of a call is counted once per group).
+    const unsigned long long k =
+        __builtin_amdgcn_readfirstlane((uint32_t)(before / (unsigned)epi_group_tiles(a, grp))) |
+        0ull;
+    const int ng = epi_group_tiles(a, lane);
+    bool lane_ok = true;
+    if (ng > 0) {
+      const unsigned long long now = __hip_atomic_load(
+          epi_count(a, epi_started_off(a.tiles), lane), __ATOMIC_RELAXED,
+          __HIP_MEMORY_SCOPE_AGENT);
+      lane_ok = now >= (k + 1ull) * (unsigned)ng;
+    }
+    const bool all_started = __ballot(!lane_ok) == 0;
     if (lane == 0) {
-      const unsigned long long k = before / (unsigned)a.tiles;
-      const unsigned long long all = (k + 1ull) * (unsigned)a.tiles;
-      const unsigned long long now =
-          __hip_atomic_load(started, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       *s_epi_k = k;
-      s_ctl[3] = now >= all ? 1u : 0u;
+      s_ctl[3] = all_started ? 1u : 0u;
     }
     __syncthreads();  // E1
     __syncthreads();  // E2
@@ -437,16 +458,18 @@ __device__ __forceinline__ void store_y(const GemvArgs& a, int64_t i, float v) {
 //   y = (z * inv[b]) * w[n]
 // The sum over n crosses workgroups.  Each tile sums its 16 squares per
 // column in row order and publishes the partials (coherent stores) in its
-// record, then adds one to a 64-bit done count in the pad header.  Both this
-// count and the started count (taken at entry) only grow, so call k is
-// complete when they reach (k + 1) * tiles.  The tile whose add completes
-// the done count folds every partial (fold_inv_rms), publishes inv and then
-// a flag holding k + 1 (after the inv stores completed).
+// record, then adds one to its group's done count; the tile that completes
+// its group adds one to the count of completed groups, and the tile that
+// completes that count is the last.  Every count (and the started counts
+// taken at entry) only grows, so call k is complete when a count reaches
+// (k + 1) times its number of members.  The last tile folds every partial
+// (fold_inv_rms), then publishes inv and a flag holding k + 1 (after the
+// inv stores completed) in kEpiGroups copies, one per group.
 //  - A tile that saw every tile of its call started (s_ctl[3], looked up by
 //    the communication wave) may wait: every other tile is resident or done
 //    and finishes on its own.  It marks its record with k + 1, waits
-//    (bounded) for the flag, reads inv and normalises its own rows from
-//    registers.
+//    (bounded) for its group's copy of the flag, reads inv from that copy and
+//    normalises its own rows from registers.
 //  - Any other tile marks 0 and leaves; the last tile also normalises the
 //    rows of every tile not marked k + 1, re-reading out (stored coherently
 //    for this).
@@ -479,13 +502,13 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
   wait_vm_all();    // this wave's out stores are at the coherence point ...
   __syncthreads();  // E1 ... in every compute wave, and the squares are in LDS
   const unsigned long long k = *s_epi_k;
-  const unsigned long long target = (k + 1ull) * (unsigned)a.tiles;
   const uint32_t mark = (uint32_t)(k + 1ull);
   const bool waits = s_ctl[3] != 0;
-  unsigned long long* done = reinterpret_cast<unsigned long long*>(a.pad + kHdrEpiCount);
+  const int grp = (int)(tile % kEpiGroups);
   float* rec = a.ssq + tile * kEpiRecordWords;
-  float* inv_pub = a.ssq + (int64_t)a.tiles * kEpiRecordWords;  // [16] inv, then the flag
-  uint32_t* inv_flag = reinterpret_cast<uint32_t*>(inv_pub + 16);
+  // This tile's group copy of the published inv and flag.
+  float* inv_copy = a.ssq + epi_inv_off(a.tiles) + (int64_t)grp * kEpiRecordWords;
+  uint32_t* inv_flag = reinterpret_cast<uint32_t*>(inv_copy + 16);
   if (wave == 0) {
     if (lane < a.B) {
       float part = 0.0f;
@@ -497,9 +520,20 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     wait_vm_all();  // the record is at the coherence point before the count
     if (lane == 0) {
-      const unsigned long long before =
-          __hip_atomic_fetch_add(done, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      s_ctl[2] = before + 1ull == target ? 1u : 0u;
+      uint32_t last = 0;
+      const unsigned long long g_before =
+          __hip_atomic_fetch_add(epi_count(a, epi_done_off(a.tiles), grp), 1ull,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (g_before + 1ull == (k + 1ull) * (unsigned)epi_group_tiles(a, grp)) {
+        // This tile completed its group (whose members all counted after
+        // their records were published): count the group.
+        const unsigned groups = (unsigned)min(a.tiles, kEpiGroups);
+        const unsigned long long t_before =
+            __hip_atomic_fetch_add(epi_count(a, epi_top_off(a.tiles), 0), 1ull,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = t_before + 1ull == (k + 1ull) * groups ? 1u : 0u;
+      }
+      s_ctl[2] = last;
     }
   }
   __syncthreads();  // E2
@@ -510,13 +544,13 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
     // Every tile has published: fold, then publish inv and the flag.
     fold_inv_rms<BM>(a, wave, lane, nt, wsum, s_inv);  // contains E3
     if (wave == 0) {
-      if (lane < a.B) {
-        store_coherent(&inv_pub[lane], s_inv[lane]);
-        if (a.inv_rms) a.inv_rms[lane] = s_inv[lane];
-      }
+      // Lane g writes group g's copy: inv, then (once inv completed) the flag.
+      float* copy = a.ssq + epi_inv_off(a.tiles) + (int64_t)lane * kEpiRecordWords;
+      for (int c = 0; c < a.B; ++c) store_coherent(&copy[c], s_inv[c]);
+      if (a.inv_rms && lane < a.B) a.inv_rms[lane] = s_inv[lane];
       wait_vm_all();  // inv at the coherence point before the flag
-      if (lane == 0)
-        __hip_atomic_store(inv_flag, mark, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(reinterpret_cast<uint32_t*>(copy + 16), mark, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     }
   } else {
     if (wave == 0 && lane == 0) {
@@ -537,7 +571,7 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
     __syncthreads();  // E3: the flag seen (or the wait expired)
     // inv is loaded only after the flag showed it published.
     if (wave == 0 && lane < a.B)
-      s_inv[lane] = s_ctl[1] ? load_coherent(&inv_pub[lane]) : __builtin_nanf("");
+      s_inv[lane] = s_ctl[1] ? load_coherent(&inv_copy[lane]) : __builtin_nanf("");
   }
   __syncthreads();  // E4: inv in LDS
   if (waits) {
@@ -956,9 +990,9 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a
 }
 
 __global__ void pad_reset_kernel(uint32_t* pad, int W, int row_stride, uint32_t mask,
-                                 uint32_t* epi_flag) {
+                                 uint32_t* epi_tail, int64_t tail_words) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i == 0) *epi_flag = 0u;  // the epilogue's published-inv flag restarts with the counts
+  if (i < tail_words) epi_tail[i] = 0u;  // the epilogue's flags and counts
   const int64_t total = GSA_PAD_HEADER_WORDS + (int64_t)W * row_stride;
   if (i >= total) return;
   uint32_t v;
@@ -1058,13 +1092,14 @@ hipError_t launch_gemv(const Launch& l, const GemvArgs& a, hipStream_t s) {
 
 hipError_t launch_pad_reset(uint32_t* pad, int W, int row_stride, int tiles,
                             uint32_t published_mask, float* epi_scratch, hipStream_t s) {
-  uint32_t* epi_flag =
-      reinterpret_cast<uint32_t*>(epi_scratch + (int64_t)tiles * kEpiRecordWords + 16);
-  const int64_t total = GSA_PAD_HEADER_WORDS + (int64_t)W * row_stride;
+  uint32_t* epi_tail = reinterpret_cast<uint32_t*>(epi_scratch + epi_inv_off(tiles));
+  const int64_t tail_words = epi_scratch_words(tiles) - epi_inv_off(tiles);
+  const int64_t total =
+      std::max<int64_t>(GSA_PAD_HEADER_WORDS + (int64_t)W * row_stride, tail_words);
   const unsigned block = 256;
   const unsigned grid = (unsigned)((total + block - 1) / block);
   hipLaunchKernelGGL(pad_reset_kernel, dim3(grid), dim3(block), 0, s, pad, W, row_stride,
-                     published_mask, epi_flag);
+                     published_mask, epi_tail, tail_words);
   return hipGetLastError();
 }
 

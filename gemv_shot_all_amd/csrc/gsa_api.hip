@@ -100,9 +100,9 @@ int gsa_symm_alloc(int W, int64_t N, int B, gsa_symm** out) {
   const size_t slot_bytes = round_up((size_t)W * (size_t)N * (size_t)B * sizeof(float), kAlign);
   const size_t pad_words = GSA_PAD_HEADER_WORDS + (size_t)W * (size_t)stride;
   const size_t pad_bytes = round_up(pad_words * sizeof(uint32_t), kAlign);
-  // The epilogue's scratch: one record per tile, then 1/rms and its flag.
+  // The epilogue's scratch: one record per tile, then flags and counts.
   const size_t ssq_bytes =
-      round_up(((size_t)tiles_of(N) + 1) * gsa::kEpiRecordWords * sizeof(float), kAlign);
+      round_up((size_t)gsa::epi_scratch_words(tiles_of(N)) * sizeof(float), kAlign);
   const size_t bytes = slot_bytes + pad_bytes + ssq_bytes;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return GSA_EHIP;

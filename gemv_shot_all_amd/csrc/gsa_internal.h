@@ -14,13 +14,32 @@ enum : int {
   kHdrErrorBits = 0,   // atomicOr: kErrTimeout | kErrState
   kHdrTimeoutKey = 1,  // atomicMin of tile * 8 + peer, 0xFFFFFFFF = none
   kHdrStateTile = 2,   // atomicMin of the tile with a bad own flag row
-  kHdrEpiCount = 4,    // epilogue: 64-bit count of finished tiles over all calls (words 4, 5)
   kHdrEpiWaitTile = 6, // atomicMin of a tile whose epilogue wait expired, 0xFFFFFFFF = none
-  kHdrEpiStart = 8,    // epilogue: 64-bit count of started tiles over all calls (words 8, 9)
 };
-// The epilogue's per-tile record in the scratch: 16 partial sums (one per
-// column), then the call mark (uint32) at word 16.
+// The epilogue's scratch (fp32 / uint32 words, 128-byte lines of 32 words):
+//   records   tiles lines: 16 partial sums of squares, the call mark at word 16
+//   inv       kEpiGroups lines: 16 x 1/rms, the published flag at word 16
+//   started   kEpiGroups lines: a 64-bit count at word 0
+//   done      kEpiGroups lines: a 64-bit count at word 0
+//   top       1 line: a 64-bit count of completed groups at word 0
+// Tile t belongs to group t % kEpiGroups; spreading the counts and the flag
+// over separate lines keeps the tiles' atomics and polls from queueing on one
+// address.  Everything after the records is cleared by the pad reset.
 constexpr int kEpiRecordWords = 32;
+constexpr int kEpiGroups = 64;
+__host__ __device__ constexpr int64_t epi_inv_off(int64_t tiles) { return tiles * kEpiRecordWords; }
+__host__ __device__ constexpr int64_t epi_started_off(int64_t tiles) {
+  return epi_inv_off(tiles) + kEpiGroups * kEpiRecordWords;
+}
+__host__ __device__ constexpr int64_t epi_done_off(int64_t tiles) {
+  return epi_started_off(tiles) + kEpiGroups * kEpiRecordWords;
+}
+__host__ __device__ constexpr int64_t epi_top_off(int64_t tiles) {
+  return epi_done_off(tiles) + kEpiGroups * kEpiRecordWords;
+}
+__host__ __device__ constexpr int64_t epi_scratch_words(int64_t tiles) {
+  return epi_top_off(tiles) + kEpiRecordWords;
+}
 enum : uint32_t { kErrTimeout = 1u, kErrState = 2u, kErrEpiWait = 4u };
 
 // Everything one launch needs.  Built on the host per call, passed by value.
@@ -65,8 +84,8 @@ bool select_gemv_kernel(int W, int B, int C, bool epi, Launch* out);
 size_t gemv_lds_bytes(int W, int B, int C, bool epi);
 
 hipError_t launch_gemv(const Launch& l, const GemvArgs& a, hipStream_t s);
-// Also clears the fused epilogue's published-inv flag in epi_scratch (the
-// buffer's tiles x kEpiRecordWords records, then inv and the flag).
+// Also clears the fused epilogue's scratch after its records (flags and
+// counts), so the next call starts counting from zero.
 hipError_t launch_pad_reset(uint32_t* pad, int W, int row_stride, int tiles,
                             uint32_t published_mask, float* epi_scratch, hipStream_t s);
 

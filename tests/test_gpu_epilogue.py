@@ -92,13 +92,6 @@ def check_epilogue(er, out, slots_out, y, inv, what):
         assert np.all(np.abs(y.astype(np.float64) - y64) <= lim), f"{what}: y vs fp64"
 
 
-def done_count(hdr, word=4):
-    """The epilogue's 64-bit count of finished tiles (pad header words 4-5;
-    word=8: the count of started tiles, words 8-9)."""
-    h = hdr.astype(np.int64) & 0xFFFFFFFF
-    return int(h[word]) | (int(h[word + 1]) << 32)
-
-
 def run_epi_and_check(d, what, **kw):
     er = EpiRun(d, **kw)
     try:
@@ -107,8 +100,6 @@ def run_epi_and_check(d, what, **kw):
     finally:
         er.close()
     assert status == (gsa.GSA_OK, -1, -1), f"{what}: status {status}"
-    assert done_count(hdr) == er.r.buf.tiles, f"{what}: done count {done_count(hdr)}"
-    assert done_count(hdr, 8) == er.r.buf.tiles, f"{what}: started count"
     check_epilogue(er, out, sl, y, inv, what)
 
 
@@ -142,9 +133,9 @@ def test_edge_epilogue(W, N, Ks, B, rank, bias, weight, eps):
 
 
 def test_repeats_bit_identical_and_mixed_with_plain_calls():
-    """Three epilogue calls with plain calls in between: the done count grows
-    by the tile count with every epilogue call (plain calls leave it alone),
-    y and inv_rms are bit-identical every time."""
+    """Three epilogue calls with plain calls in between (which leave the
+    epilogue's counts alone): y and inv_rms are right and bit-identical every
+    time."""
     _say("[epilogue] repeats")
     d = gi.make_inputs("c2", seed=4, rank=0)
     er = EpiRun(d, seed=4)
@@ -155,10 +146,9 @@ def test_repeats_bit_identical_and_mixed_with_plain_calls():
             er.r.call()  # a plain call on the same buffer
             out, sl, y, inv, status, hdr = er.results()
             assert status == (gsa.GSA_OK, -1, -1)
-            assert done_count(hdr) == (i + 1) * er.r.buf.tiles
+            check_epilogue(er, out, sl, y, inv, f"repeat {i}")
             ys.append(y.copy())
             invs.append(inv.copy())
-        check_epilogue(er, out, sl, ys[-1], invs[-1], "repeats")
     finally:
         er.close()
     for i in range(1, 3):
@@ -167,9 +157,9 @@ def test_repeats_bit_identical_and_mixed_with_plain_calls():
 
 
 def test_timeout_poisons_y_then_recovers():
-    """A withheld peer: the waits expire, y and inv_rms come out NaN, yet
-    every tile still counts itself done; after a reset with the peer
-    published the next call is correct."""
+    """A withheld peer: the waits expire, y and inv_rms come out NaN (every
+    tile still counts itself done, so nothing hangs); after a reset with the
+    peer published the next calls are correct."""
     _say("[epilogue] timeout")
     W, rank = 4, 1
     d = gi.make_shard_inputs(W, 64, 256, 2, seed=12, rank=rank)
@@ -181,7 +171,6 @@ def test_timeout_poisons_y_then_recovers():
             out, sl, y, inv, status, hdr = er.results()
             assert status[0] == gsa.GSA_ETIMEOUT
             assert np.isnan(y).all() and np.isnan(inv).all(), "a failed call must poison y"
-            assert done_count(hdr) == er.r.buf.tiles, "every tile counts itself, failed or not"
             er.r.buf.reset(all_but(W, rank))
             er.y.fill_(float("nan"))
             er.r.out.fill_(float("nan"))
@@ -189,6 +178,11 @@ def test_timeout_poisons_y_then_recovers():
             out, sl, y, inv, status, hdr = er.results()
             assert status == (gsa.GSA_OK, -1, -1)
             check_epilogue(er, out, sl, y, inv, "after recovery")
+            er.y.fill_(float("nan"))
+            er.call()
+            out, sl, y, inv, status, hdr = er.results()
+            assert status == (gsa.GSA_OK, -1, -1)
+            check_epilogue(er, out, sl, y, inv, "second call after recovery")
         finally:
             er.close()
     finally:
@@ -196,8 +190,8 @@ def test_timeout_poisons_y_then_recovers():
 
 
 def test_graph_replays_match_eager():
-    """Calls captured in a HIP graph (no host-held state: the done count
-    only grows): every replay gives the eager result, bit for bit."""
+    """Calls captured in a HIP graph (no host-held state: the epilogue's
+    counts only grow): every replay gives the eager result, bit for bit."""
     _say("[epilogue] graph replays")
     d = gi.make_inputs("c3b4", seed=5, rank=0)
     er = EpiRun(d, seed=5, y_dtype=torch.bfloat16)
@@ -217,7 +211,6 @@ def test_graph_replays_match_eager():
             torch.cuda.synchronize()
             out, sl, y, inv, status, hdr = er.results()
             assert status == (gsa.GSA_OK, -1, -1)
-            assert done_count(hdr) == (4 + 3 * rep) * er.r.buf.tiles
             assert np.array_equal(y, y0) and np.array_equal(inv.view(np.uint32),
                                                             inv0.view(np.uint32)), f"replay {rep}"
     finally:
