@@ -23,6 +23,8 @@ protocol state.  Sources followed (restated, not quoted):
   talk, real-model example (RMSNorm itself: its textbook definition, the
   pages do not write it out); bf16 output of an fp32 accumulation -- the
   documentation's higher-precision reduction section;
+* two-shot variant (reduce-scatter of an owned chunk, then all-gather) --
+  the documentation's op reference of two_shot_all_reduce_;
 * signal pad next to every symmetric allocation, sized by launched blocks
   times world size, indexed by block -- same documentation, the
   writing-your-own-kernel section and the set_signal_pad_size and
@@ -83,6 +85,11 @@ class Oracle:
         lib.gsa_oracle_scale_f32.argtypes = [_f32p, _f32p, _f32p, ctypes.c_int64, ctypes.c_int,
                                              _f32p, _u16p]
         lib.gsa_oracle_scale_f32.restype = None
+        lib.gsa_oracle_two_shot_chunk_rows.argtypes = [ctypes.c_int64, ctypes.c_int]
+        lib.gsa_oracle_two_shot_chunk_rows.restype = ctypes.c_int64
+        lib.gsa_oracle_two_shot.argtypes = [_f32p, _f32p, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int64, ctypes.c_int, _f32p, _f32p]
+        lib.gsa_oracle_two_shot.restype = None
         self._lib = lib
 
     def gemv(self, A, x):
@@ -168,6 +175,25 @@ class Oracle:
         self._lib.gsa_oracle_scale_f32(_ptr(z, _f32p), _ptr(inv, _f32p), wp, N, B,
                                        _ptr(y, _f32p), _ptr(yb, _u16p))
         return y, yb
+
+    def two_shot_chunk_rows(self, N, W):
+        """Rows per rank's chunk in the two-shot variant (whole 16-row tiles)."""
+        return int(self._lib.gsa_oracle_two_shot_chunk_rows(N, W))
+
+    def two_shot(self, slots, gathered, rank):
+        """(out, mine): out rows of the own chunk = fp32 rank-order fold of the
+        slots, other rows = gathered; mine = the own chunk's published values
+        (NaN elsewhere).  slots: W x N x B fp32; gathered: N x B fp32."""
+        slots = np.ascontiguousarray(slots, dtype=np.float32)
+        W, N, B = slots.shape
+        gathered = np.ascontiguousarray(gathered, dtype=np.float32)
+        if gathered.shape != (N, B):
+            raise ValueError("gathered must be N x B")
+        out = np.empty((N, B), np.float32)
+        mine = np.full((N, B), np.nan, np.float32)
+        self._lib.gsa_oracle_two_shot(_ptr(slots, _f32p), _ptr(gathered, _f32p), W, rank, N, B,
+                                      _ptr(out, _f32p), _ptr(mine, _f32p))
+        return out, mine
 
     def fold_f32(self, slots):
         """fp32 one-shot sum of the given slots in rank order from +0.0f."""

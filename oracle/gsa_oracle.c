@@ -35,6 +35,12 @@
  *    the reduction loop) and an RMSNorm, all in one kernel.  The pages do not
  *    write RMSNorm out; gsa_oracle_bias_rmsnorm uses its textbook definition
  *    over the hidden dimension (the N output rows of one token).
+ *  - "PyTorch Symmetric Memory" documentation, op reference of
+ *    two_shot_all_reduce_ (a two-stage all-reduce; the talk mentions a
+ *    two-shot version too): read as reduce-scatter then all-gather.  Rank p
+ *    owns one tile-aligned chunk of the rows, sums it over all ranks in rank
+ *    order from zero (the one-shot rule) and publishes it; every rank copies
+ *    the other chunks from their owners (gsa_oracle_two_shot).
  *  - "PyTorch Symmetric Memory" documentation, higher-precision reduction:
  *    accumulate in fp32, hand the result back in the input precision (bf16),
  *    which gsa_oracle_scale_f32 rounds to nearest, ties to even.
@@ -191,6 +197,51 @@ void gsa_oracle_scale_f32(const float *z, const float *inv, const float *w,
                 v = v * w[n];
             y[n * B + b] = v;
             y_bf16[n * B + b] = f32_to_bf16_rne(v);
+        }
+    }
+}
+
+/*
+ * Rows owned by each rank in the two-shot variant: chunks of
+ * chunk_rows = ceil(ceil(N / W) / 16) * 16 rows (whole 16-row tiles), rank p
+ * owning rows [p * chunk_rows, min(N, (p + 1) * chunk_rows)); rows past
+ * W * chunk_rows cannot occur.  Returns chunk_rows.
+ */
+int64_t gsa_oracle_two_shot_chunk_rows(int64_t N, int W)
+{
+    int64_t per_rank = (N + W - 1) / W;
+    return (per_rank + 15) / 16 * 16;
+}
+
+/*
+ * Two-shot all-reduce at one rank's share, given the slots as published
+ * (W x N x B fp32, the calling rank's own slot included) and what every
+ * rank published as its reduced chunk (`gathered`, N x B: rows of chunk p
+ * hold rank p's values; the calling rank's rows are ignored):
+ *   rows of the own chunk:   out = fp32 fold of the W slots in rank order
+ *                            from +0 (as gsa_oracle_fold_f32), also the
+ *                            chunk this rank publishes (mine)
+ *   rows of chunk p != rank: out = gathered (rank p's published values)
+ * out, mine: N x B fp32 (mine is written only on the own chunk's rows).
+ */
+void gsa_oracle_two_shot(const float *slots, const float *gathered, int W, int rank,
+                         int64_t N, int B, float *out, float *mine)
+{
+    int64_t cr = gsa_oracle_two_shot_chunk_rows(N, W);
+    int64_t NB = N * (int64_t)B;
+    for (int64_t n = 0; n < N; ++n) {
+        int64_t owner = n / cr;
+        for (int b = 0; b < B; ++b) {
+            int64_t i = n * B + b;
+            if (owner == rank) {
+                float acc = 0.0f;
+                for (int r = 0; r < W; ++r)
+                    acc = acc + slots[(int64_t)r * NB + i];
+                out[i] = acc;
+                mine[i] = acc;
+            } else {
+                out[i] = gathered[i];
+            }
         }
     }
 }

@@ -24,6 +24,9 @@ What pins what:
   scale_exact      fp32 evaluation of the normalised output against exact
                    rational arithmetic with IEEE round-to-nearest-even
   bf16_rne         fp32 -> bf16 rounding, hand-chosen bit patterns
+  two_shot_*       chunk partition (hand values and its defining properties),
+                   ownership of every row for every rank against numpy
+                   float32 sums in rank order and plain copies
 """
 from fractions import Fraction
 import json
@@ -361,11 +364,51 @@ def pin_bf16_rne(o):
         f"NaN stays a quiet NaN, got {hex(v)}"
 
 
+def pin_two_shot_chunks(o):
+    # Hand values: ceil(N / W) rounded up to whole 16-row tiles.
+    for N, W, want in [(4096, 8, 512), (17, 8, 16), (1000, 3, 336), (33, 2, 32), (1, 1, 16),
+                       (16384, 8, 2048), (8192, 4, 2048), (4097, 8, 528)]:
+        got = o.two_shot_chunk_rows(N, W)
+        assert got == want, f"chunk rows N={N} W={W}: {got} != {want}"
+    # Defining properties on a sweep: a multiple of 16, every row owned, and
+    # the smallest such size.
+    for N in (1, 15, 16, 17, 100, 1023, 4096, 5000):
+        for W in range(1, 9):
+            cr = o.two_shot_chunk_rows(N, W)
+            per = -(-N // W)
+            assert cr % 16 == 0 and cr >= per and cr - 16 < per and W * cr >= N, (N, W, cr)
+
+
+def pin_two_shot_rows(o):
+    # For every rank: rows of its chunk hold the float32 rank-order sum of
+    # the slots (numpy scalar adds), every other row a copy of gathered.
+    rng = np.random.default_rng(13)
+    W, N, B = 3, 70, 2
+    slots = rng.normal(0, 1, (W, N, B)).astype(np.float32)
+    gathered = rng.normal(0, 1, (N, B)).astype(np.float32)
+    cr = -(-(-(-N // W)) // 16) * 16
+    for rank in range(W):
+        out, mine = o.two_shot(slots, gathered, rank)
+        for n in range(N):
+            own = rank * cr <= n < (rank + 1) * cr
+            for b in range(B):
+                if own:
+                    acc = np.float32(0.0)
+                    for r in range(W):
+                        acc = np.float32(acc + slots[r, n, b])
+                    assert out[n, b].view(np.uint32) == acc.view(np.uint32), (rank, n, b)
+                    assert mine[n, b].view(np.uint32) == acc.view(np.uint32), (rank, n, b)
+                else:
+                    assert out[n, b].view(np.uint32) == gathered[n, b].view(np.uint32), (rank, n, b)
+                    assert np.isnan(mine[n, b]), (rank, n, b)
+
+
 PINS = [pin_brute_force, pin_single_rank, pin_shard_sum, pin_identity, pin_one_hot,
         pin_small_integers, pin_rank_order_exact, pin_bf16_decode, pin_golden,
         pin_fold_order, pin_fold_zero_start, pin_fold_fp32, pin_fold_matches_sequence,
         pin_rms_golden, pin_rms_constant_column, pin_rms_unit_rms, pin_rms_scale_invariant,
-        pin_rms_bias_cancels, pin_rms_columns_independent, pin_scale_exact, pin_bf16_rne]
+        pin_rms_bias_cancels, pin_rms_columns_independent, pin_scale_exact, pin_bf16_rne,
+        pin_two_shot_chunks, pin_two_shot_rows]
 
 
 def failing_pins(o):

@@ -18,14 +18,15 @@ MUTANTS = {
     "own_term_dropped": ("(r == rank) ? y64[i] :", "(r == rank) ? 0.0 :"),
     "peer_stride": ("? y64[i] : (double)slots[(int64_t)r * NB + i]",
                     "? y64[i] : (double)slots[(int64_t)r * N + i]"),
-    "fold_stride": ("acc = acc + slots[(int64_t)r * NB + i]", "acc = acc + slots[(int64_t)r * W + i]"),
+    "fold_stride": ("            acc = acc + slots[(int64_t)r * NB + i];\n        out[i] = acc;",
+                    "            acc = acc + slots[(int64_t)r * W + i];\n        out[i] = acc;"),
     "y_index": ("y64[n * B + b] = sum;", "y64[(int64_t)b * N + n] = sum;"),
     "bf16_shift": ("(uint32_t)bits << 16", "(uint32_t)bits << 15"),
     "fold_reversed": ("for (int r = 0; r < W; ++r)\n            acc = acc + slots",
                       "for (int r = W - 1; r >= 0; --r)\n            acc = acc + slots"),
     "fold_starts_at_slot0": ("float acc = 0.0f;\n        for (int r = 0; r < W; ++r)",
                              "float acc = slots[i];\n        for (int r = 1; r < W; ++r)"),
-    "fold_in_double": ("float acc = 0.0f;", "double acc = 0.0;"),
+    "fold_in_double": ("        float acc = 0.0f;\n        for", "        double acc = 0.0;\n        for"),
     "out_skips_first_rank": ("for (int r = 0; r < W; ++r) {\n            double term",
                              "for (int r = 1; r < W; ++r) {\n            double term"),
     "rms_mean_over_n_minus_1": ("sqrt(ssq / (double)N + eps)", "sqrt(ssq / (double)(N - 1) + eps)"),
@@ -42,6 +43,14 @@ MUTANTS = {
                         "float v = (float)((double)z[n * B + b] * (double)inv[b] * (w ? (double)w[n] : 1.0));"),
     "rne_truncates": ("return (uint16_t)((u + 0x7FFFu + lsb) >> 16);", "return (uint16_t)(u >> 16);"),
     "rne_ties_away": ("return (uint16_t)((u + 0x7FFFu + lsb) >> 16);", "return (uint16_t)((u + 0x8000u) >> 16);"),
+    "two_shot_no_tile_round": ("return (per_rank + 15) / 16 * 16;", "return per_rank;"),
+    "two_shot_round_down": ("return (per_rank + 15) / 16 * 16;", "return per_rank / 16 * 16 + 16 * (per_rank < 16);"),
+    "two_shot_owner_off_by_one": ("int64_t owner = n / cr;", "int64_t owner = (n + 1) / cr;"),
+    "two_shot_copies_slot": ("out[i] = gathered[i];", "out[i] = slots[(int64_t)rank * NB + i];"),
+    "two_shot_fold_reversed": ("for (int r = 0; r < W; ++r)\n                    acc = acc + slots",
+                               "for (int r = W - 1; r >= 0; --r)\n                    acc = acc + slots"),
+    "two_shot_skips_own": ("for (int r = 0; r < W; ++r)\n                    acc = acc + slots",
+                           "for (int r = 0; r < W; ++r)\n                    if (r != rank) acc = acc + slots"),
     "nan_branch_dropped": ("if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0)\n        return (uint16_t)((u >> 16) | 0x0040u);\n", ""),
 }
 
