@@ -1,4 +1,4 @@
-"""gemv_shot_all_amd: one rank's fused GEMV + one-shot AllReduce on MI355X.
+"""gemv_shot_all_amd: one rank's fused GEMV + AllReduce (one-shot or two-shot) on MI355X.
 
 The operation runs in hand-written HIP kernels inside libgsa.so (C ABI in
 include/gsa.h).  This package is its thin Python binding; PyTorch supplies
@@ -9,6 +9,7 @@ from ._lib import (  # noqa: F401
     EXPORTS, GSA_DTYPE_BF16, GSA_DTYPE_F32, GSA_EHIP, GSA_EINVAL, GSA_ENOMEM, GSA_ESTATE,
     GSA_ETIMEOUT, GSA_FLAG_PUBLISHED, GSA_FLAG_TILE_ROWS, GSA_MAX_B, GSA_MAX_W,
     GSA_MAX_X_LDS_BYTES, GSA_OK, GSA_PAD_HEADER_WORDS, GsaError, SymmBuffer, device_view,
-    gsa_epilogue, gsa_gemv_allreduce, gsa_gemv_allreduce_rmsnorm, gsa_set_wait_timeout_us,
-    gsa_signal_pad_reset, gsa_signal_pad_row_stride, gsa_signal_pad_status, gsa_strerror,
-    gsa_symm_alloc, gsa_symm_free, gsa_symm_signal_pad, gsa_symm_slots, lib, make_epilogue)
+    gsa_epilogue, gsa_gemv_allreduce, gsa_gemv_allreduce_rmsnorm, gsa_gemv_allreduce_two_shot,
+    gsa_set_wait_timeout_us, gsa_signal_pad_reset, gsa_signal_pad_row_stride,
+    gsa_signal_pad_status, gsa_strerror, gsa_symm_alloc, gsa_symm_free, gsa_symm_gathered,
+    gsa_symm_signal_pad, gsa_symm_slots, lib, make_epilogue)

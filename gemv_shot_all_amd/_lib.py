@@ -22,9 +22,9 @@ GSA_DTYPE_F32 = 0
 GSA_DTYPE_BF16 = 1
 
 EXPORTS = ("gsa_symm_alloc", "gsa_symm_free", "gsa_symm_slots", "gsa_symm_signal_pad",
-           "gsa_signal_pad_row_stride", "gsa_signal_pad_reset", "gsa_gemv_allreduce",
-           "gsa_gemv_allreduce_rmsnorm", "gsa_signal_pad_status", "gsa_set_wait_timeout_us",
-           "gsa_strerror")
+           "gsa_symm_gathered", "gsa_signal_pad_row_stride", "gsa_signal_pad_reset",
+           "gsa_gemv_allreduce", "gsa_gemv_allreduce_two_shot", "gsa_gemv_allreduce_rmsnorm",
+           "gsa_signal_pad_status", "gsa_set_wait_timeout_us", "gsa_strerror")
 
 
 class gsa_epilogue(ctypes.Structure):
@@ -65,12 +65,17 @@ def lib():
         L.gsa_symm_slots.restype = vp
         L.gsa_symm_signal_pad.argtypes = [vp]
         L.gsa_symm_signal_pad.restype = vp
+        L.gsa_symm_gathered.argtypes = [vp]
+        L.gsa_symm_gathered.restype = vp
         L.gsa_signal_pad_row_stride.argtypes = [i64]
         L.gsa_signal_pad_row_stride.restype = i64
         L.gsa_signal_pad_reset.argtypes = [vp, ci, i64, u32, vp]
         L.gsa_signal_pad_reset.restype = ci
         L.gsa_gemv_allreduce.argtypes = [vp, vp, vp, vp, vp, ci, ci, i64, i64, ci, vp]
         L.gsa_gemv_allreduce.restype = ci
+        L.gsa_gemv_allreduce_two_shot.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, i64, i64, ci,
+                                                  vp]
+        L.gsa_gemv_allreduce_two_shot.restype = ci
         L.gsa_gemv_allreduce_rmsnorm.argtypes = [vp, vp, vp, vp, vp, ci, ci, i64, i64, ci,
                                                  ctypes.POINTER(gsa_epilogue), vp]
         L.gsa_gemv_allreduce_rmsnorm.restype = ci
@@ -142,6 +147,13 @@ def gsa_symm_signal_pad(h):
     return p
 
 
+def gsa_symm_gathered(h):
+    p = lib().gsa_symm_gathered(h)
+    if not p:
+        raise GsaError(GSA_EINVAL, "gsa_symm_gathered")
+    return p
+
+
 def gsa_signal_pad_row_stride(N):
     return lib().gsa_signal_pad_row_stride(N)
 
@@ -155,6 +167,14 @@ def gsa_gemv_allreduce(A_r, x, slots, pad, out, W, rank, N, K, B, stream=None):
     _check(lib().gsa_gemv_allreduce(_ptr(A_r), _ptr(x), _ptr(slots), _ptr(pad), _ptr(out),
                                     W, rank, N, K, B, _stream(stream)),
            "gsa_gemv_allreduce")
+
+
+def gsa_gemv_allreduce_two_shot(A_r, x, slots, pad, gathered, out, W, rank, N, K, B,
+                                stream=None):
+    _check(lib().gsa_gemv_allreduce_two_shot(_ptr(A_r), _ptr(x), _ptr(slots), _ptr(pad),
+                                             _ptr(gathered), _ptr(out), W, rank, N, K, B,
+                                             _stream(stream)),
+           "gsa_gemv_allreduce_two_shot")
 
 
 def make_epilogue(y, bias=None, rms_weight=None, eps=1e-5, inv_rms=None):
@@ -216,14 +236,16 @@ def device_view(ptr, shape, dtype):
 
 
 class SymmBuffer:
-    """One symmetric buffer (W slots of N x B fp32 + signal pad), freed on
-    close().  Convenience wrapper over gsa_symm_alloc / gsa_symm_free."""
+    """One symmetric buffer (W slots of N x B fp32, signal pad, the two-shot
+    variant's gathered chunks), freed on close().  Convenience wrapper over
+    gsa_symm_alloc / gsa_symm_free."""
 
     def __init__(self, W, N, B):
         self.W, self.N, self.B = W, N, B
         self.handle = gsa_symm_alloc(W, N, B)
         self.slots = gsa_symm_slots(self.handle)
         self.pad = gsa_symm_signal_pad(self.handle)
+        self.gathered = gsa_symm_gathered(self.handle)
         self.row_stride = gsa_signal_pad_row_stride(N)
         self.tiles = (N + GSA_FLAG_TILE_ROWS - 1) // GSA_FLAG_TILE_ROWS
 
@@ -232,18 +254,30 @@ class SymmBuffer:
         import torch
         return device_view(self.slots, (self.W, self.N, self.B), torch.float32)
 
-    def pad_view(self):
-        """torch int32 view of the whole signal pad (header + W rows)."""
+    def gathered_view(self):
+        """torch float32 view (N, B) of the gathered chunks."""
         import torch
-        return device_view(self.pad, (GSA_PAD_HEADER_WORDS + self.W * self.row_stride,),
+        return device_view(self.gathered, (self.N, self.B), torch.float32)
+
+    def pad_view(self):
+        """torch int32 view of the whole signal pad (header + 2W flag rows)."""
+        import torch
+        return device_view(self.pad, (GSA_PAD_HEADER_WORDS + 2 * self.W * self.row_stride,),
                            torch.int32)
 
-    def flags(self):
-        """Host copy (numpy uint32, W x T) of the logical flag array."""
+    def _flag_rows(self, first):
         import numpy as np
         raw = self.pad_view().cpu().numpy().view(np.uint32)
-        rows = raw[GSA_PAD_HEADER_WORDS:].reshape(self.W, self.row_stride)
-        return rows[:, :self.tiles].copy()
+        rows = raw[GSA_PAD_HEADER_WORDS:].reshape(2 * self.W, self.row_stride)
+        return rows[first:first + self.W, :self.tiles].copy()
+
+    def flags(self):
+        """Host copy (numpy uint32, W x T) of the slot flags."""
+        return self._flag_rows(0)
+
+    def flags2(self):
+        """Host copy (numpy uint32, W x T) of the reduced-chunk flags."""
+        return self._flag_rows(self.W)
 
     def reset(self, published_mask, stream=None):
         gsa_signal_pad_reset(self.pad, self.W, self.N, published_mask, stream)

@@ -86,6 +86,15 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 __device__ __forceinline__ uint32_t* flag_ptr(const GemvArgs& a, int r, int64_t t) {
   return a.pad + GSA_PAD_HEADER_WORDS + (int64_t)r * a.row_stride + t;
 }
+// Two-shot: rank r's reduced-chunk flag for tile t (pad row W + r).
+__device__ __forceinline__ uint32_t* flag2_ptr(const GemvArgs& a, int r, int64_t t) {
+  return a.pad + GSA_PAD_HEADER_WORDS + (int64_t)(a.W + r) * a.row_stride + t;
+}
+// The rank that reduces tile t: the calling rank, or in the two-shot variant
+// the owner of the tile's chunk.
+__device__ __forceinline__ int tile_owner(const GemvArgs& a, int64_t t) {
+  return a.two_shot ? (int)min((int64_t)(a.W - 1), t * GSA_FLAG_TILE_ROWS / a.chunk_rows) : a.rank;
+}
 
 // Lane p reads flag[min(p, W-1)][t] (no divergent loads: every lane reads a
 // valid word; lanes >= W are ignored by the callers).
@@ -129,6 +138,20 @@ __device__ __forceinline__ void issue_peer_tile(const GemvArgs& a, int lane, int
   const int per_lane = (kTileRows * a.B + 63) / 64;  // 1, 2 or 4
   const int64_t first = tile * kTileRows * a.B;      // first element of the tile in a slot
   const int64_t last = NB - 1;
+  const int owner = tile_owner(a, tile);
+  if (owner != a.rank) {
+    // Two-shot, a chunk another rank reduces: its published values, kept at
+    // the owner's slot of the peer tile.
+#pragma unroll
+    for (int r = 0; r < kMaxW; ++r) {
+      if (r == owner) {
+#pragma unroll
+        for (int i = 0; i < kPerLane; ++i)
+          if (i < per_lane) v[r][i] = load_coherent(&a.gathered[min(first + lane + 64 * i, last)]);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int r = 0; r < kMaxW; ++r) {
     if (r < a.W && r != a.rank) {
@@ -140,13 +163,14 @@ __device__ __forceinline__ void issue_peer_tile(const GemvArgs& a, int lane, int
   }
 }
 
-__device__ __forceinline__ void store_peer_tile(const GemvArgs& a, int lane,
+__device__ __forceinline__ void store_peer_tile(const GemvArgs& a, int lane, int64_t tile,
                                                 const float (&v)[kMaxW][kPerLane], float* pe) {
   const int tb = kTileRows * a.B;  // elements of one rank's tile
   const int per_lane = (tb + 63) / 64;
+  const int owner = tile_owner(a, tile);
 #pragma unroll
   for (int r = 0; r < kMaxW; ++r) {
-    if (r < a.W && r != a.rank) {
+    if (owner != a.rank ? r == owner : (r < a.W && r != a.rank)) {
 #pragma unroll
       for (int i = 0; i < kPerLane; ++i) {
         const int e = lane + 64 * i;
@@ -171,7 +195,12 @@ __device__ __forceinline__ uint32_t comm_decide(const GemvArgs& a, int lane, int
     return kBadOwnRow;
   }
   const uint32_t epoch = own + 1u;
-  const bool lane_ok = lane >= a.W || lane == a.rank || fl >= epoch;
+  const int owner = tile_owner(a, tile);
+  bool lane_ok = lane >= a.W || lane == a.rank || fl >= epoch;
+  if (owner != a.rank)  // two-shot: only the owner's reduced chunk is needed
+    lane_ok = lane != 0 ||
+              __hip_atomic_load(flag2_ptr(a, owner, tile), __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT) >= epoch;
   const bool ready = __ballot(!lane_ok) == 0;
   if (lane == 0) {
     s_ctl[0] = epoch;
@@ -184,9 +213,17 @@ __device__ __forceinline__ uint32_t comm_decide(const GemvArgs& a, int lane, int
 // smallest missing peer of this tile in the pad header.
 __device__ bool wait_peers(const GemvArgs& a, int lane, int64_t tile, uint32_t epoch) {
   const uint64_t start = wall_clock64();
+  const int owner = tile_owner(a, tile);
   for (;;) {
-    const uint32_t f = load_flag(a, lane, tile);
-    const bool lane_ok = lane >= a.W || lane == a.rank || f >= epoch;
+    bool lane_ok;
+    if (owner != a.rank) {  // two-shot: the owner's reduced-chunk flag
+      const uint32_t f2 = __hip_atomic_load(flag2_ptr(a, owner, tile), __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+      lane_ok = lane != owner || f2 >= epoch;
+    } else {
+      const uint32_t f = load_flag(a, lane, tile);
+      lane_ok = lane >= a.W || lane == a.rank || f >= epoch;
+    }
     const uint64_t missing = __ballot(!lane_ok);
     if (missing == 0) return true;
     if (wall_clock64() - start > a.timeout_ticks) {
@@ -220,7 +257,9 @@ __device__ __forceinline__ unsigned long long* epi_count(const GemvArgs& a, int6
 //   the MFMA kernels: per-wave partials in LDS) | B2 own slot published, and
 //   the peer tile in LDS if the peers were ready at the start (compute wave 0
 //   then stores the flag) | B3 (only if they were not) late peer tile in LDS
-//   | with the fused epilogue: E1, E2 and maybe E3, E4 (see fused_epilogue).
+//   | two-shot, own chunk: B5 (reduced chunk published; compute wave 0 then
+//   stores the reduced-chunk flag) | with the fused epilogue: E1, E2 and
+//   maybe E3, E4 (see fused_epilogue).
 // The peer loads stay in flight across B1: a workgroup barrier does not wait
 // for outstanding global loads.
 // With the epilogue the communication wave also counts the tile started in
@@ -241,18 +280,19 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
   float v[kMaxW][kPerLane];
   if (state == kPeersReady) issue_peer_tile(a, lane, tile, v);  // after the flags returned
   __syncthreads();  // B1
-  if (state == kPeersReady) store_peer_tile(a, lane, v, pe);
+  if (state == kPeersReady) store_peer_tile(a, lane, tile, v, pe);
   __syncthreads();  // B2
   if (state == kMustWait) {
     const uint32_t epoch = s_ctl[0];
     const bool ok = wait_peers(a, lane, tile, epoch);  // the own flag went out after B2
     if (ok) {
       issue_peer_tile(a, lane, tile, v);  // after the flags returned
-      store_peer_tile(a, lane, v, pe);
+      store_peer_tile(a, lane, tile, v, pe);
     }
     if (lane == 0) s_ctl[1] = ok ? kPeersReady : kMustWait;
     __syncthreads();  // B3
   }
+  if (a.two_shot && tile_owner(a, tile) == a.rank) __syncthreads();  // B5
   if (a.epi) {
     // The call's index k (every tile of a call is counted once per group).
     const unsigned long long k =
@@ -339,18 +379,29 @@ __device__ void publish_and_reduce(const GemvArgs& a, int64_t tile, const int (&
     __syncthreads();  // B3
     ok = s_ctl[1] == kPeersReady;  // wait expired: this tile's out rows stay unwritten
   }
+  const int owner = tile_owner(a, tile);
   float o[OPL];
 #pragma unroll
   for (int e = 0; e < OPL; ++e) {
     o[e] = 0.0f;
     if (ok && live[e]) {
-      o[e] = one_shot_sum(a, y[e], pe, n[e], b);
-      float* dst = &a.out[(row0 + n[e]) * a.B + b];
+      const int64_t i = (row0 + n[e]) * a.B + b;
+      if (owner == a.rank) {
+        o[e] = one_shot_sum(a, y[e], pe, n[e], b);
+        if (a.two_shot) store_coherent(&a.gathered[i], o[e]);  // this rank's reduced chunk
+      } else {
+        o[e] = pe[owner * kTileRows * a.B + n[e] * a.B + b];  // the owner's reduced chunk
+      }
       if (a.epi)
-        store_coherent(dst, o[e]);  // read back by the workgroup that finishes last
+        store_coherent(&a.out[i], o[e]);  // read back by the workgroup that finishes last
       else
-        *dst = o[e];
+        a.out[i] = o[e];
     }
+  }
+  if (a.two_shot && owner == a.rank) {
+    wait_vm_all();    // the reduced chunk is at the coherence point ...
+    __syncthreads();  // B5 ... in every compute wave
+    if (ok && wave == 0 && lane == 0) store_flag(flag2_ptr(a, a.rank, tile), s_ctl[0]);
   }
   if (a.epi)
     fused_epilogue<BM, OPL>(a, tile, n, b, own, live, o, ok, elds, s_ctl, s_epi_k, wave, lane, nt);
@@ -993,13 +1044,15 @@ __global__ void pad_reset_kernel(uint32_t* pad, int W, int row_stride, uint32_t 
                                  uint32_t* epi_tail, int64_t tail_words) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < tail_words) epi_tail[i] = 0u;  // the epilogue's flags and counts
-  const int64_t total = GSA_PAD_HEADER_WORDS + (int64_t)W * row_stride;
+  // Header, then 2W flag rows: rank r's slot flags (row r) and reduced-chunk
+  // flags of the two-shot variant (row W + r).
+  const int64_t total = GSA_PAD_HEADER_WORDS + 2 * (int64_t)W * row_stride;
   if (i >= total) return;
   uint32_t v;
   if (i < GSA_PAD_HEADER_WORDS) {
     v = (i == kHdrTimeoutKey || i == kHdrStateTile || i == kHdrEpiWaitTile) ? 0xFFFFFFFFu : 0u;
   } else {
-    const int r = (int)((i - GSA_PAD_HEADER_WORDS) / row_stride);
+    const int r = (int)((i - GSA_PAD_HEADER_WORDS) / row_stride) % W;
     v = ((mask >> r) & 1u) ? GSA_FLAG_PUBLISHED : 0u;
   }
   pad[i] = v;
@@ -1095,7 +1148,7 @@ hipError_t launch_pad_reset(uint32_t* pad, int W, int row_stride, int tiles,
   uint32_t* epi_tail = reinterpret_cast<uint32_t*>(epi_scratch + epi_inv_off(tiles));
   const int64_t tail_words = epi_scratch_words(tiles) - epi_inv_off(tiles);
   const int64_t total =
-      std::max<int64_t>(GSA_PAD_HEADER_WORDS + (int64_t)W * row_stride, tail_words);
+      std::max<int64_t>(GSA_PAD_HEADER_WORDS + 2 * (int64_t)W * row_stride, tail_words);
   const unsigned block = 256;
   const unsigned grid = (unsigned)((total + block - 1) / block);
   hipLaunchKernelGGL(pad_reset_kernel, dim3(grid), dim3(block), 0, s, pad, W, row_stride,

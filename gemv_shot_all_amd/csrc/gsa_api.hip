@@ -26,7 +26,8 @@ struct gsa_symm {
   void* base;
   float* slots;
   uint32_t* pad;
-  float* ssq;  // the fused epilogue's per-tile partial sums (tiles x 16 fp32)
+  float* gathered;  // the two-shot variant's reduced chunks (N x B fp32)
+  float* ssq;       // the fused epilogue's scratch
   int device;
 };
 
@@ -98,12 +99,13 @@ int gsa_symm_alloc(int W, int64_t N, int B, gsa_symm** out) {
   *out = nullptr;
   const int64_t stride = gsa_signal_pad_row_stride(N);
   const size_t slot_bytes = round_up((size_t)W * (size_t)N * (size_t)B * sizeof(float), kAlign);
-  const size_t pad_words = GSA_PAD_HEADER_WORDS + (size_t)W * (size_t)stride;
+  const size_t pad_words = GSA_PAD_HEADER_WORDS + 2 * (size_t)W * (size_t)stride;
+  const size_t gathered_bytes = round_up((size_t)N * (size_t)B * sizeof(float), kAlign);
   const size_t pad_bytes = round_up(pad_words * sizeof(uint32_t), kAlign);
   // The epilogue's scratch: one record per tile, then flags and counts.
   const size_t ssq_bytes =
       round_up((size_t)gsa::epi_scratch_words(tiles_of(N)) * sizeof(float), kAlign);
-  const size_t bytes = slot_bytes + pad_bytes + ssq_bytes;
+  const size_t bytes = slot_bytes + pad_bytes + gathered_bytes + ssq_bytes;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return GSA_EHIP;
   void* base = nullptr;
@@ -122,9 +124,11 @@ int gsa_symm_alloc(int W, int64_t N, int B, gsa_symm** out) {
     (void)hipFree(base);
     return GSA_EHIP;
   }
-  float* ssq = reinterpret_cast<float*>(static_cast<char*>(base) + slot_bytes + pad_bytes);
+  float* gathered = reinterpret_cast<float*>(static_cast<char*>(base) + slot_bytes + pad_bytes);
+  float* ssq = reinterpret_cast<float*>(static_cast<char*>(base) + slot_bytes + pad_bytes +
+                                        gathered_bytes);
   gsa_symm* h = new gsa_symm{W, N, B, stride, tiles_of(N), bytes, base,
-                             static_cast<float*>(base), pad, ssq, dev};
+                             static_cast<float*>(base), pad, gathered, ssq, dev};
   std::lock_guard<std::mutex> lk(g_mu);
   g_by_slots[(uintptr_t)h->slots] = h;
   g_by_pad[(uintptr_t)h->pad] = h;
@@ -162,6 +166,11 @@ uint32_t* gsa_symm_signal_pad(const gsa_symm* h) {
   return known(h) ? h->pad : nullptr;
 }
 
+float* gsa_symm_gathered(const gsa_symm* h) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  return known(h) ? h->gathered : nullptr;
+}
+
 int gsa_signal_pad_reset(uint32_t* pad, int W, int64_t N, uint32_t published_mask,
                          void* stream) {
   if (!pad || W < 1 || W > GSA_MAX_W || N < 1) return GSA_EINVAL;
@@ -189,7 +198,7 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 
 // Both entry points: validate, fill the launch arguments, enqueue one kernel.
 int enqueue_call(const uint16_t* A_r, const uint16_t* x, float* slots, uint32_t* pad,
-                 float* out, int W, int rank, int64_t N, int64_t K, int B,
+                 float* gathered, float* out, int W, int rank, int64_t N, int64_t K, int B,
                  const gsa_epilogue* ep, void* stream) {
   // Scalars first: these checks touch no HIP state.
   if (W < 1 || W > GSA_MAX_W || rank < 0 || rank >= W) return GSA_EINVAL;
@@ -222,6 +231,7 @@ int enqueue_call(const uint16_t* A_r, const uint16_t* x, float* slots, uint32_t*
     std::lock_guard<std::mutex> lk(g_mu);
     gsa_symm* h = find_by_slots(slots);
     if (!h || h->pad != pad || h->W != W || h->N != N || h->B != B) return GSA_EINVAL;
+    if (gathered && h->gathered != gathered) return GSA_EINVAL;
     a.row_stride = (int)h->row_stride;
     a.tiles = (int)h->tiles;
     a.ssq = h->ssq;
@@ -244,6 +254,10 @@ int enqueue_call(const uint16_t* A_r, const uint16_t* x, float* slots, uint32_t*
   a.B = B;
   a.W = W;
   a.rank = rank;
+  a.two_shot = gathered ? 1 : 0;
+  a.gathered = gathered;
+  a.chunk_rows = (int)(((N + W - 1) / W + GSA_FLAG_TILE_ROWS - 1) / GSA_FLAG_TILE_ROWS *
+                       GSA_FLAG_TILE_ROWS);
   a.epi = ep ? 1 : 0;
   a.y_bf16 = ep && ep->y_dtype == GSA_DTYPE_BF16 ? 1 : 0;
   a.eps = ep ? ep->eps : 0.0f;
@@ -267,14 +281,21 @@ extern "C" {
 
 int gsa_gemv_allreduce(const uint16_t* A_r, const uint16_t* x, float* slots, uint32_t* pad,
                        float* out, int W, int rank, int64_t N, int64_t K, int B, void* stream) {
-  return enqueue_call(A_r, x, slots, pad, out, W, rank, N, K, B, nullptr, stream);
+  return enqueue_call(A_r, x, slots, pad, nullptr, out, W, rank, N, K, B, nullptr, stream);
+}
+
+int gsa_gemv_allreduce_two_shot(const uint16_t* A_r, const uint16_t* x, float* slots,
+                                uint32_t* pad, float* gathered, float* out, int W, int rank,
+                                int64_t N, int64_t K, int B, void* stream) {
+  if (!gathered || !aligned16(gathered)) return GSA_EINVAL;
+  return enqueue_call(A_r, x, slots, pad, gathered, out, W, rank, N, K, B, nullptr, stream);
 }
 
 int gsa_gemv_allreduce_rmsnorm(const uint16_t* A_r, const uint16_t* x, float* slots,
                                uint32_t* pad, float* out, int W, int rank, int64_t N, int64_t K,
                                int B, const gsa_epilogue* ep, void* stream) {
   if (!ep) return GSA_EINVAL;
-  return enqueue_call(A_r, x, slots, pad, out, W, rank, N, K, B, ep, stream);
+  return enqueue_call(A_r, x, slots, pad, nullptr, out, W, rank, N, K, B, ep, stream);
 }
 
 int gsa_signal_pad_status(const uint32_t* pad, void* stream, int* code, int64_t* tile,

@@ -57,6 +57,13 @@ struct GemvArgs {
   int row_stride;         // words between flag rows
   int tiles;              // ceil(N / 16)
   uint64_t timeout_ticks; // device wall-clock ticks a wait may take
+  // Two-shot variant: rank p owns rows [p * chunk_rows, (p + 1) * chunk_rows)
+  // (whole tiles), reduces them into gathered (N x B) and raises its
+  // reduced-chunk flag (pad row W + p); other rows are copied from their
+  // owner's gathered rows once its flag shows the epoch.
+  int two_shot;
+  int chunk_rows;
+  float* gathered;
   // Fused epilogue (bias, RMSNorm over rows, y in fp32 or bf16); epi == 0:
   // none, and the fields below are unused.
   int epi;

@@ -14,7 +14,8 @@ bf16 slice of the activation, W-1 peer slots of N x B fp32 partial sums):
   c4   W=8 N=8192 K=28672 B=4   A~N(0,0.015)  70B-class MLP down_proj
   c5   W=4 N=8192 K=8192  B=16  A~N(0,0.02)   skinny GEMM (matrix-core path)
 
-x ~ N(0, 1); peer slots ~ N(0, 1) fp32.  No weights or datasets are used:
+x ~ N(0, 1); peer slots ~ N(0, 1) fp32; for the two-shot variant the other
+ranks' reduced chunks ~ N(0, 1) fp32.  No weights or datasets are used:
 these draws stand in for the layer shapes named above.
 """
 import numpy as np
@@ -91,6 +92,15 @@ def make_inputs(cfg, seed=0, rank=0):
     d = make_shard_inputs(W, N, K // W, B, c["sigma"], seed, c["cfg_id"] * 16 + B, rank)
     d["sigma"] = c["sigma"]
     return d
+
+
+def make_gathered(N, B, seed=0, cfg_id=0):
+    """Stand-in for the reduced chunks other ranks publish in the two-shot
+    variant: float32 N x B ~ N(0, 1).  (The rows of the calling rank's own
+    chunk are overwritten by the call; tests fill them with the sentinel.)"""
+    ss = np.random.SeedSequence([int(seed), int(cfg_id), 2])
+    g = np.random.Generator(np.random.PCG64(ss))
+    return g.normal(0.0, 1.0, size=(N, B)).astype(np.float32)
 
 
 def make_full_inputs(N, K, B, sigma=0.02, seed=0, cfg_id=99):

@@ -58,8 +58,10 @@ extern "C" {
 /* Signal-pad protocol: one flag per rank per tile of 16 output rows (all
  * batch columns).  T = ceil(N / 16) tiles. */
 #define GSA_FLAG_TILE_ROWS 16
-/* The pad starts with GSA_PAD_HEADER_WORDS status words, then W rows of
- * flags, row r at word GSA_PAD_HEADER_WORDS + r * gsa_signal_pad_row_stride(N). */
+/* The pad starts with GSA_PAD_HEADER_WORDS status words, then 2W rows of
+ * flags, row r at word GSA_PAD_HEADER_WORDS + r * gsa_signal_pad_row_stride(N):
+ * rows 0..W-1 hold each rank's slot flags, rows W..2W-1 each rank's
+ * reduced-chunk flags of the two-shot variant. */
 #define GSA_PAD_HEADER_WORDS 16
 #define GSA_MAX_W 8
 #define GSA_MAX_B 16
@@ -89,12 +91,17 @@ float *gsa_symm_slots(const gsa_symm *h);
 /* [device] signal pad of the buffer (header + flags).  NULL if unknown. */
 uint32_t *gsa_symm_signal_pad(const gsa_symm *h);
 
+/* [device] the two-shot variant's gathered chunks: N x B fp32 (n-major), the
+ * rows of rank p's chunk holding what rank p published as its reduced chunk
+ * (on one GPU the caller fills the other ranks' rows).  NULL if unknown. */
+float *gsa_symm_gathered(const gsa_symm *h);
+
 /* Words between consecutive rank rows of the pad for N rows (>= ceil(N/16),
  * a multiple of 64).  Returns -1 for N < 1. */
 int64_t gsa_signal_pad_row_stride(int64_t N);
 
-/* Reset a pad: flag row p := GSA_FLAG_PUBLISHED if bit p of published_mask
- * is set, else 0; status words and the fused epilogue's counts cleared (and
+/* Reset a pad: flag rows p and W + p := GSA_FLAG_PUBLISHED if bit p of
+ * published_mask is set, else 0; status words and the fused epilogue's counts cleared (and
  * its library-held scratch made ready for them).  Stream-ordered (a small kernel), no
  * host sync, no allocation.  `pad` [device] must come from
  * gsa_symm_signal_pad of a buffer allocated with the same W and N.  The
@@ -124,6 +131,24 @@ int gsa_signal_pad_reset(uint32_t *pad, int W, int64_t N, uint32_t published_mas
 int gsa_gemv_allreduce(const uint16_t *A_r, const uint16_t *x, float *slots,
                        uint32_t *pad, float *out, int W, int rank, int64_t N,
                        int64_t K, int B, void *stream);
+
+/* The two-stage variant of the same operator: the documentation's op
+ * reference lists a two-stage all-reduce (two_shot_all_reduce_) beside the
+ * one-shot one, read here as reduce-scatter then all-gather.  Each rank owns
+ * one chunk of ceil(ceil(N / W) / 16) * 16 rows (whole tiles; rank p owns
+ * rows [p * chunk, (p + 1) * chunk)).  A call computes and publishes y_r and
+ * the slot flags as gsa_gemv_allreduce does; for the rows of its own chunk it
+ * waits for every rank's slot flag, writes out = the rank-order sum from zero
+ * (the one-shot rule, same bits) and publishes it into `gathered` with its
+ * reduced-chunk flag (pad row W + rank); for every other row it waits for
+ * the owner's reduced-chunk flag and copies the owner's `gathered` rows into
+ * out.  Per rank this reads (W - 1) chunks of peer slots plus W - 1 peer
+ * chunks, instead of W - 1 whole slots.  `gathered` [device] must be
+ * gsa_symm_gathered of the same buffer; everything else as gsa_gemv_allreduce.
+ * Errors: GSA_EINVAL, GSA_EHIP. */
+int gsa_gemv_allreduce_two_shot(const uint16_t *A_r, const uint16_t *x, float *slots,
+                                uint32_t *pad, float *gathered, float *out, int W, int rank,
+                                int64_t N, int64_t K, int B, void *stream);
 
 /* Output element types of the fused epilogue. */
 #define GSA_DTYPE_F32 0

@@ -111,6 +111,24 @@ def test_rmsnorm_entry_point_rejects_bad_arguments():
     assert L.gsa_gemv_allreduce_rmsnorm(*big, ep(), None) == gsa.GSA_EINVAL
 
 
+def test_two_shot_entry_point_rejects_bad_arguments():
+    L = _lib.lib()
+    A, x, slots, pad, out = P, P, P, P, P
+    good = (2, 0, 16, 64, 1)
+    # no gathered buffer, a misaligned one, one that is not the buffer's own
+    assert L.gsa_gemv_allreduce_two_shot(A, x, slots, pad, None, out, *good, None) == (
+        gsa.GSA_EINVAL)
+    assert L.gsa_gemv_allreduce_two_shot(A, x, slots, pad, P + 4, out, *good, None) == (
+        gsa.GSA_EINVAL)
+    assert L.gsa_gemv_allreduce_two_shot(A, x, slots, pad, P, out, *good, None) == (
+        gsa.GSA_EINVAL)
+    # the plain call's argument checks apply too
+    for bad in [(2, 2, 16, 64, 1), (3, 0, 16, 64, 1), (2, 0, 16, 64, 17), (2, 0, 0, 64, 1)]:
+        assert L.gsa_gemv_allreduce_two_shot(A, x, slots, pad, P, out, *bad, None) == (
+            gsa.GSA_EINVAL), bad
+    assert L.gsa_symm_gathered(ctypes.c_void_p(P)) is None
+
+
 def test_other_entry_points_reject_bad_arguments():
     L = _lib.lib()
     h = ctypes.c_void_p()
