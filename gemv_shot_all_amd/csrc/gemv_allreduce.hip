@@ -91,9 +91,14 @@ __device__ __forceinline__ uint32_t* flag2_ptr(const GemvArgs& a, int r, int64_t
   return a.pad + GSA_PAD_HEADER_WORDS + (int64_t)(a.W + r) * a.row_stride + t;
 }
 // The rank that reduces tile t: the calling rank, or in the two-shot variant
-// the owner of the tile's chunk.
+// (TS) the owner of the tile's chunk.  The kernels take TS as a template
+// argument so that the one-shot instances carry none of this code.
+template <bool TS>
 __device__ __forceinline__ int tile_owner(const GemvArgs& a, int64_t t) {
-  return a.two_shot ? (int)min((int64_t)(a.W - 1), t * GSA_FLAG_TILE_ROWS / a.chunk_rows) : a.rank;
+  if constexpr (TS)
+    return min(a.W - 1, (int)((uint32_t)t / (uint32_t)a.chunk_tiles));
+  else
+    return a.rank;
 }
 
 // Lane p reads flag[min(p, W-1)][t] (no divergent loads: every lane reads a
@@ -132,30 +137,21 @@ __device__ __forceinline__ void wait_vm_all() { wait_vm_le<0>(); }
 // divergent control.
 constexpr int kPerLane = (kTileRows * GSA_MAX_B) / 64;  // 4
 
+template <bool TS>
 __device__ __forceinline__ void issue_peer_tile(const GemvArgs& a, int lane, int64_t tile,
                                                 float (&v)[kMaxW][kPerLane]) {
   const int64_t NB = a.N * a.B;
   const int per_lane = (kTileRows * a.B + 63) / 64;  // 1, 2 or 4
   const int64_t first = tile * kTileRows * a.B;      // first element of the tile in a slot
   const int64_t last = NB - 1;
-  const int owner = tile_owner(a, tile);
-  if (owner != a.rank) {
-    // Two-shot, a chunk another rank reduces: its published values, kept at
-    // the owner's slot of the peer tile.
-#pragma unroll
-    for (int r = 0; r < kMaxW; ++r) {
-      if (r == owner) {
-#pragma unroll
-        for (int i = 0; i < kPerLane; ++i)
-          if (i < per_lane) v[r][i] = load_coherent(&a.gathered[min(first + lane + 64 * i, last)]);
-      }
-    }
-    return;
-  }
+  const int owner = tile_owner<TS>(a, tile);
+  // Two-shot, a chunk another rank reduces: its published values, held in
+  // v[0] (store_peer_tile puts them at the owner's place in the peer tile).
+  const bool copy = TS && owner != a.rank;
 #pragma unroll
   for (int r = 0; r < kMaxW; ++r) {
-    if (r < a.W && r != a.rank) {
-      const float* src = a.slots + r * NB;
+    if (copy ? r == 0 : (r < a.W && r != a.rank)) {
+      const float* src = copy ? a.gathered : a.slots + r * NB;
 #pragma unroll
       for (int i = 0; i < kPerLane; ++i)
         if (i < per_lane) v[r][i] = load_coherent(&src[min(first + lane + 64 * i, last)]);
@@ -163,18 +159,21 @@ __device__ __forceinline__ void issue_peer_tile(const GemvArgs& a, int lane, int
   }
 }
 
+template <bool TS>
 __device__ __forceinline__ void store_peer_tile(const GemvArgs& a, int lane, int64_t tile,
                                                 const float (&v)[kMaxW][kPerLane], float* pe) {
   const int tb = kTileRows * a.B;  // elements of one rank's tile
   const int per_lane = (tb + 63) / 64;
-  const int owner = tile_owner(a, tile);
+  const int owner = tile_owner<TS>(a, tile);
+  const bool copy = TS && owner != a.rank;  // v[0] holds the owner's values
 #pragma unroll
   for (int r = 0; r < kMaxW; ++r) {
-    if (owner != a.rank ? r == owner : (r < a.W && r != a.rank)) {
+    if (copy ? r == 0 : (r < a.W && r != a.rank)) {
+      float* dst = pe + (copy ? owner : r) * tb;
 #pragma unroll
       for (int i = 0; i < kPerLane; ++i) {
         const int e = lane + 64 * i;
-        if (i < per_lane && e < tb) pe[r * tb + e] = v[r][i];
+        if (i < per_lane && e < tb) dst[e] = v[r][i];
       }
     }
   }
@@ -183,6 +182,7 @@ __device__ __forceinline__ void store_peer_tile(const GemvArgs& a, int lane, int
 // The communication wave's start: derive the epoch from its own flag and
 // check every peer's flag for this tile.  Writes s_ctl[0] = epoch and
 // s_ctl[1] = kMustWait / kPeersReady / kBadOwnRow; returns s_ctl[1].
+template <bool TS>
 __device__ __forceinline__ uint32_t comm_decide(const GemvArgs& a, int lane, int64_t tile,
                                                 uint32_t fl, uint32_t* s_ctl) {
   const uint32_t own = __builtin_amdgcn_readlane(fl, a.rank);
@@ -195,9 +195,9 @@ __device__ __forceinline__ uint32_t comm_decide(const GemvArgs& a, int lane, int
     return kBadOwnRow;
   }
   const uint32_t epoch = own + 1u;
-  const int owner = tile_owner(a, tile);
+  const int owner = tile_owner<TS>(a, tile);
   bool lane_ok = lane >= a.W || lane == a.rank || fl >= epoch;
-  if (owner != a.rank)  // two-shot: only the owner's reduced chunk is needed
+  if (TS && owner != a.rank)  // two-shot: only the owner's reduced chunk is needed
     lane_ok = lane != 0 ||
               __hip_atomic_load(flag2_ptr(a, owner, tile), __ATOMIC_RELAXED,
                                 __HIP_MEMORY_SCOPE_AGENT) >= epoch;
@@ -211,12 +211,13 @@ __device__ __forceinline__ uint32_t comm_decide(const GemvArgs& a, int lane, int
 
 // Bounded wait for every peer's flag >= epoch.  On expiry records the
 // smallest missing peer of this tile in the pad header.
+template <bool TS>
 __device__ bool wait_peers(const GemvArgs& a, int lane, int64_t tile, uint32_t epoch) {
   const uint64_t start = wall_clock64();
-  const int owner = tile_owner(a, tile);
+  const int owner = tile_owner<TS>(a, tile);
   for (;;) {
     bool lane_ok;
-    if (owner != a.rank) {  // two-shot: the owner's reduced-chunk flag
+    if (TS && owner != a.rank) {  // two-shot: the owner's reduced-chunk flag
       const uint32_t f2 = __hip_atomic_load(flag2_ptr(a, owner, tile), __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
       lane_ok = lane != owner || f2 >= epoch;
@@ -266,6 +267,7 @@ __device__ __forceinline__ unsigned long long* epi_count(const GemvArgs& a, int6
 // its group (after B0) and, once its protocol work is done, looks whether
 // every tile of the call has started (s_ctl[3]: lane g reads group g's
 // count); s_epi_k gets the call's index.
+template <bool TS>
 __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
                           uint32_t* s_ctl, unsigned long long* s_epi_k) {
   const uint32_t fl = load_flag(a, lane, tile);
@@ -276,23 +278,23 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
   if (a.epi && lane == 0)
     before = __hip_atomic_fetch_add(epi_count(a, epi_started_off(a.tiles), grp), 1ull,
                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint32_t state = comm_decide(a, lane, tile, fl, s_ctl);
+  const uint32_t state = comm_decide<TS>(a, lane, tile, fl, s_ctl);
   float v[kMaxW][kPerLane];
-  if (state == kPeersReady) issue_peer_tile(a, lane, tile, v);  // after the flags returned
+  if (state == kPeersReady) issue_peer_tile<TS>(a, lane, tile, v);  // after the flags returned
   __syncthreads();  // B1
-  if (state == kPeersReady) store_peer_tile(a, lane, tile, v, pe);
+  if (state == kPeersReady) store_peer_tile<TS>(a, lane, tile, v, pe);
   __syncthreads();  // B2
   if (state == kMustWait) {
     const uint32_t epoch = s_ctl[0];
-    const bool ok = wait_peers(a, lane, tile, epoch);  // the own flag went out after B2
+    const bool ok = wait_peers<TS>(a, lane, tile, epoch);  // the own flag went out after B2
     if (ok) {
-      issue_peer_tile(a, lane, tile, v);  // after the flags returned
-      store_peer_tile(a, lane, tile, v, pe);
+      issue_peer_tile<TS>(a, lane, tile, v);  // after the flags returned
+      store_peer_tile<TS>(a, lane, tile, v, pe);
     }
     if (lane == 0) s_ctl[1] = ok ? kPeersReady : kMustWait;
     __syncthreads();  // B3
   }
-  if (a.two_shot && tile_owner(a, tile) == a.rank) __syncthreads();  // B5
+  if (TS && tile_owner<TS>(a, tile) == a.rank) __syncthreads();  // B5
   if (a.epi) {
     // The call's index k (every tile of a call is counted once per group).
     const unsigned long long k =
@@ -354,8 +356,8 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
 // Every compute wave waits for its own slot stores to complete before B2, so
 // the flag store that follows B2 is ordered after all of them.  nt: compute
 // threads of the workgroup.
-template <int BM, int OPL>
-__device__ void publish_and_reduce(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
+template <int BM, int OPL, bool TS>
+__device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
                                    const bool (&own)[OPL], const float (&y)[OPL],
                                    const float* pe, float* elds, uint32_t* s_ctl,
                                    const unsigned long long* s_epi_k, uint32_t state, int wave,
@@ -379,16 +381,16 @@ __device__ void publish_and_reduce(const GemvArgs& a, int64_t tile, const int (&
     __syncthreads();  // B3
     ok = s_ctl[1] == kPeersReady;  // wait expired: this tile's out rows stay unwritten
   }
-  const int owner = tile_owner(a, tile);
+  const int owner = tile_owner<TS>(a, tile);
   float o[OPL];
 #pragma unroll
   for (int e = 0; e < OPL; ++e) {
     o[e] = 0.0f;
     if (ok && live[e]) {
       const int64_t i = (row0 + n[e]) * a.B + b;
-      if (owner == a.rank) {
+      if (!TS || owner == a.rank) {
         o[e] = one_shot_sum(a, y[e], pe, n[e], b);
-        if (a.two_shot) store_coherent(&a.gathered[i], o[e]);  // this rank's reduced chunk
+        if (TS) store_coherent(&a.gathered[i], o[e]);  // this rank's reduced chunk
       } else {
         o[e] = pe[owner * kTileRows * a.B + n[e] * a.B + b];  // the owner's reduced chunk
       }
@@ -398,7 +400,7 @@ __device__ void publish_and_reduce(const GemvArgs& a, int64_t tile, const int (&
         a.out[i] = o[e];
     }
   }
-  if (a.two_shot && owner == a.rank) {
+  if (TS && owner == a.rank) {
     wait_vm_all();    // the reduced chunk is at the coherence point ...
     __syncthreads();  // B5 ... in every compute wave
     if (ok && wave == 0 && lane == 0) store_flag(flag2_ptr(a, a.rank, tile), s_ctl[0]);
@@ -745,7 +747,7 @@ __device__ __forceinline__ void valu_stream(float (&acc)[R][B], uint4 (&ring)[D]
 // allow.  NCH > 0 builds a fully unrolled instance for
 // exactly NCH chunks per lane; MASKED instances zero chunks past the row end.
 // LDS: x chunks [b][c], one zero chunk, one sink chunk, then the peer tile.
-template <int B, int G, int R, int NW, int NCH, int D, int XPT, int WPE, bool MASKED>
+template <int B, int G, int R, int NW, int NCH, int D, int XPT, int WPE, bool MASKED, bool TS>
 __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   constexpr int NT = NW * 64;
   constexpr int GPW = 64 / G;
@@ -768,7 +770,7 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   float* elds = pe + a.W * kTileRows * B + 1;  // the epilogue's LDS
 
   if (wave == NW) {
-    comm_wave(a, lane, tile, pe, s_ctl, &s_epi_k);
+    comm_wave<TS>(a, lane, tile, pe, s_ctl, &s_epi_k);
     return;
   }
 
@@ -822,14 +824,14 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   const int n[1] = {nloc0 + vidx / B};
   const bool own[1] = {li < V};
   const float y[1] = {yv};
-  publish_and_reduce<B, 1>(a, tile, n, vidx % B, own, y, pe, elds, s_ctl, &s_epi_k, state, wave,
-                           lane, NT);
+  publish_and_reduce<B, 1, TS>(a, tile, n, vidx % B, own, y, pe, elds, s_ctl, &s_epi_k, state,
+                               wave, lane, NT);
 }
 
 // MFMA epilogue: each wave's 16 x 16 partial goes to red[wave][n][b]; after
 // B1 wave w sums rows 4w .. 4w+3 over the waves in wave order (lane l: row
 // 4w + (l >> 4), column l & 15), publishes them and reduces.
-template <int NW>
+template <int NW, bool TS>
 __device__ __forceinline__ void mfma_finish(const GemvArgs& a, int64_t tile, int wave, int lane,
                                             f32x4_t acc, float* red, const float* pe,
                                             float* elds, uint32_t* s_ctl,
@@ -847,8 +849,8 @@ __device__ __forceinline__ void mfma_finish(const GemvArgs& a, int64_t tile, int
   const int n[1] = {nl};
   const bool own[1] = {bl < a.B};
   const float yv[1] = {y};
-  publish_and_reduce<GSA_MAX_B, 1>(a, tile, n, bl, own, yv, pe, elds, s_ctl, s_epi_k, state,
-                                   wave, lane, NW * 64);
+  publish_and_reduce<GSA_MAX_B, 1, TS>(a, tile, n, bl, own, yv, pe, elds, s_ctl, s_epi_k, state,
+                                       wave, lane, NW * 64);
 }
 
 // Copy 16 bytes per active lane from global memory straight into LDS: lane l
@@ -873,7 +875,7 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
 // is finite).  The per-wave 16 x 16 fp32 partials are summed in wave order
 // through LDS.  One more wave runs the signal-pad protocol.
 // LDS: x [16][C + 1] chunks (column C zero); NW 16 x 16 partials; peer tile.
-template <int NW, int D>
+template <int NW, int D, bool TS>
 __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs a) {
   static_assert(NW * 4 == kTileRows, "each compute wave finishes 4 rows of the tile");
   extern __shared__ uint4 lds[];
@@ -891,7 +893,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs a) {
   float* elds = pe + a.W * kTileRows * a.B + 1;  // the epilogue's LDS
 
   if (wave == NW) {
-    comm_wave(a, lane, tile, pe, s_ctl, &s_epi_k);
+    comm_wave<TS>(a, lane, tile, pe, s_ctl, &s_epi_k);
     return;
   }
 
@@ -958,7 +960,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs a) {
     }
   }
 
-  mfma_finish<NW>(a, tile, wave, lane, acc, red, pe, elds, s_ctl, &s_epi_k);
+  mfma_finish<NW, TS>(a, tile, wave, lane, acc, red, pe, elds, s_ctl, &s_epi_k);
 }
 
 // MFMA path for x beyond the LDS bound (8 < B <= 16, 16 * (C + 1) chunks over
@@ -968,7 +970,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs a) {
 // wave's steps start at a rotation that differs between the workgroups of
 // one XCD so that they do not all read the same lines of x at once.
 // LDS: NW 16 x 16 partials, then the peer tile.
-template <int NW, int D>
+template <int NW, int D, bool TS>
 __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a) {
   static_assert(NW * 4 == kTileRows, "each compute wave finishes 4 rows of the tile");
   extern __shared__ uint4 lds[];
@@ -985,7 +987,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a
   float* elds = pe + a.W * kTileRows * a.B + 1;  // the epilogue's LDS
 
   if (wave == NW) {
-    comm_wave(a, lane, tile, pe, s_ctl, &s_epi_k);
+    comm_wave<TS>(a, lane, tile, pe, s_ctl, &s_epi_k);
     return;
   }
 
@@ -1037,7 +1039,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  mfma_finish<NW>(a, tile, wave, lane, acc, red, pe, elds, s_ctl, &s_epi_k);
+  mfma_finish<NW, TS>(a, tile, wave, lane, acc, red, pe, elds, s_ctl, &s_epi_k);
 }
 
 __global__ void pad_reset_kernel(uint32_t* pad, int W, int row_stride, uint32_t mask,
@@ -1075,16 +1077,16 @@ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // exact instance; any other C the masked streaming instance.  XPT covers
 // B * G * NCH chunks of x (at most 8 per thread; the rest of a longer x is
 // staged by a plain loop).
-template <int B, int G, int R, int NW, int NCH, int D, int WPE>
+template <int B, int G, int R, int NW, int NCH, int D, int WPE, bool TS>
 ValuChoice valu_tier(int C) {
   constexpr int XPT0 = ceil_div(B * G * NCH, NW * 64);
   constexpr int XPT = XPT0 > 8 ? 8 : XPT0;
   constexpr int DE = D < NCH ? D : NCH;
   const void* k;
   if (C == G * NCH)
-    k = reinterpret_cast<const void*>(&gemv_ar_valu<B, G, R, NW, NCH, DE, XPT, WPE, false>);
+    k = reinterpret_cast<const void*>(&gemv_ar_valu<B, G, R, NW, NCH, DE, XPT, WPE, false, TS>);
   else
-    k = reinterpret_cast<const void*>(&gemv_ar_valu<B, G, R, NW, 0, D, XPT, WPE, true>);
+    k = reinterpret_cast<const void*>(&gemv_ar_valu<B, G, R, NW, 0, D, XPT, WPE, true, TS>);
   return {k, NW};
 }
 
@@ -1093,11 +1095,31 @@ ValuChoice valu_tier(int C) {
 //   C <= 64 : 4 waves, a full wave per row, 4 rows per wave
 //   C <= 224: 4 waves, half a wave per row, 2 x 2 rows per wave
 //   larger  : 8 waves, a full wave per row, 2 rows per wave
-template <int B>
+template <int B, bool TS>
 ValuChoice valu_kernel(int C) {
-  if (C <= 64) return valu_tier<B, 64, 4, 4, 1, 1, 1>(C);
-  if (C <= 224) return valu_tier<B, 32, 2, 4, 7, 4, 1>(C);
-  return valu_tier<B, 64, 2, 8, 7, 3, 5>(C);
+  if (C <= 64) return valu_tier<B, 64, 4, 4, 1, 1, 1, TS>(C);
+  if (C <= 224) return valu_tier<B, 32, 2, 4, 7, 4, 1, TS>(C);
+  return valu_tier<B, 64, 2, 8, 7, 3, 5, TS>(C);
+}
+
+template <bool TS>
+ValuChoice pick_kernel(int B, int C) {
+  switch (B) {
+    case 1: return valu_kernel<1, TS>(C);
+    case 2: return valu_kernel<2, TS>(C);
+    case 3: return valu_kernel<3, TS>(C);
+    case 4: return valu_kernel<4, TS>(C);
+    case 5: return valu_kernel<5, TS>(C);
+    case 6: return valu_kernel<6, TS>(C);
+    case 7: return valu_kernel<7, TS>(C);
+    case 8: return valu_kernel<8, TS>(C);
+    default:
+      return mfma_x_in_lds(C)
+                 ? ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma<kMfmaWaves, 8, TS>),
+                              kMfmaWaves}
+                 : ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma_xmem<kMfmaWaves, 8, TS>),
+                              kMfmaWaves};
+  }
 }
 
 }  // namespace
@@ -1113,26 +1135,11 @@ size_t gemv_lds_bytes(int W, int B, int C, bool epi) {
   return partials + tail;
 }
 
-bool select_gemv_kernel(int W, int B, int C, bool epi, Launch* out) {
+bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, Launch* out) {
   if (W < 1 || W > GSA_MAX_W || B < 1 || B > GSA_MAX_B || C < 1) return false;
   if (B <= 8 && (size_t)B * C * 16 > GSA_MAX_X_LDS_BYTES) return false;  // x staged in LDS
-  ValuChoice k{nullptr, kMfmaWaves};
-  switch (B) {
-    case 1: k = valu_kernel<1>(C); break;
-    case 2: k = valu_kernel<2>(C); break;
-    case 3: k = valu_kernel<3>(C); break;
-    case 4: k = valu_kernel<4>(C); break;
-    case 5: k = valu_kernel<5>(C); break;
-    case 6: k = valu_kernel<6>(C); break;
-    case 7: k = valu_kernel<7>(C); break;
-    case 8: k = valu_kernel<8>(C); break;
-    default:
-      k = mfma_x_in_lds(C)
-              ? ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma<kMfmaWaves, 8>), kMfmaWaves}
-              : ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma_xmem<kMfmaWaves, 8>),
-                           kMfmaWaves};
-      break;
-  }
+  if (epi && two_shot) return false;  // separate entry points
+  const ValuChoice k = two_shot ? pick_kernel<true>(B, C) : pick_kernel<false>(B, C);
   const unsigned block = (unsigned)(k.waves + 1) * 64;
   *out = {k.kernel, block, gemv_lds_bytes(W, B, C, epi)};
   return true;

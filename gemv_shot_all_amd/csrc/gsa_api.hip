@@ -224,7 +224,8 @@ int enqueue_call(const uint16_t* A_r, const uint16_t* x, float* slots, uint32_t*
   }
   const int C = (int)(Ks / 8);
   gsa::Launch l;
-  if (!gsa::select_gemv_kernel(W, B, C, ep != nullptr, &l)) return GSA_EINVAL;
+  if (!gsa::select_gemv_kernel(W, B, C, ep != nullptr, gathered != nullptr, &l))
+    return GSA_EINVAL;
 
   gsa::GemvArgs a;
   {
@@ -254,10 +255,8 @@ int enqueue_call(const uint16_t* A_r, const uint16_t* x, float* slots, uint32_t*
   a.B = B;
   a.W = W;
   a.rank = rank;
-  a.two_shot = gathered ? 1 : 0;
   a.gathered = gathered;
-  a.chunk_rows = (int)(((N + W - 1) / W + GSA_FLAG_TILE_ROWS - 1) / GSA_FLAG_TILE_ROWS *
-                       GSA_FLAG_TILE_ROWS);
+  a.chunk_tiles = (int)(((N + W - 1) / W + GSA_FLAG_TILE_ROWS - 1) / GSA_FLAG_TILE_ROWS);
   a.epi = ep ? 1 : 0;
   a.y_bf16 = ep && ep->y_dtype == GSA_DTYPE_BF16 ? 1 : 0;
   a.eps = ep ? ep->eps : 0.0f;

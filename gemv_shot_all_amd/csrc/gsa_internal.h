@@ -57,12 +57,11 @@ struct GemvArgs {
   int row_stride;         // words between flag rows
   int tiles;              // ceil(N / 16)
   uint64_t timeout_ticks; // device wall-clock ticks a wait may take
-  // Two-shot variant: rank p owns rows [p * chunk_rows, (p + 1) * chunk_rows)
-  // (whole tiles), reduces them into gathered (N x B) and raises its
-  // reduced-chunk flag (pad row W + p); other rows are copied from their
-  // owner's gathered rows once its flag shows the epoch.
-  int two_shot;
-  int chunk_rows;
+  // Two-shot variant (the kernels' TS instances): rank p owns tiles
+  // [p * chunk_tiles, (p + 1) * chunk_tiles), reduces them into gathered
+  // (N x B) and raises its reduced-chunk flag (pad row W + p); other rows are
+  // copied from their owner's gathered rows once its flag shows the epoch.
+  int chunk_tiles;
   float* gathered;
   // Fused epilogue (bias, RMSNorm over rows, y in fp32 or bf16); epi == 0:
   // none, and the fields below are unused.
@@ -86,7 +85,7 @@ struct Launch {
 // Pick the kernel for W ranks, batch B (1..16) and C chunks per row (with
 // the epilogue's extra LDS if epi).  Returns false if the shape exceeds the
 // LDS staging bound.
-bool select_gemv_kernel(int W, int B, int C, bool epi, Launch* out);
+bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, Launch* out);
 // Dynamic LDS bytes the kernel chosen for (W, B, C, epi) needs.
 size_t gemv_lds_bytes(int W, int B, int C, bool epi);
 
