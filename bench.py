@@ -260,7 +260,7 @@ def hbm_read_probe(gib=1, launches=20):
     sink = torch.zeros(1 << 16, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
     best = None
-    for grid in (1024, 2048, 4096, 8192):
+    for grid in (256, 512, 1024, 2048, 4096, 8192):
         def launch():
             rc = L.gsa_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(), grid,
                                   ctypes.c_void_p(stream.cuda_stream))

@@ -77,8 +77,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
-// 16 bytes at byte offset off (per lane, range-checked).
+// 16 bytes at byte offset off (per lane, range-checked).  Cache policy 2 is
+// the non-temporal hint (nt): A is streamed once per call, and a plain
+// streaming read reaches markedly more HBM bandwidth with it on MI355X.
+#ifndef GSA_A_CPOL
+#define GSA_A_CPOL 2
+#endif
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, GSA_A_CPOL);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// The same without the hint, for x (read by every workgroup: kept cached).
+__device__ __forceinline__ uint4 buf_load16_cached(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
@@ -1024,7 +1034,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a
 #pragma unroll
   for (int u = 0; u < D; ++u) {
     ra_ring[u] = buf_load16(ra, a_off(u));
-    rx_ring[u] = buf_load16(rx, x_off(u));
+    rx_ring[u] = buf_load16_cached(rx, x_off(u));
   }
 
   f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -1035,7 +1045,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a
                                                     __builtin_bit_cast(bf16x8_t, rx_ring[u]),
                                                     acc, 0, 0, 0);
       ra_ring[u] = buf_load16(ra, a_off(j0 + u + D));
-      rx_ring[u] = buf_load16(rx, x_off(j0 + u + D));
+      rx_ring[u] = buf_load16_cached(rx, x_off(j0 + u + D));
       __builtin_amdgcn_sched_barrier(0);
     }
   }

@@ -8,19 +8,29 @@ namespace {
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
-__global__ __launch_bounds__(256) void read_probe(const uint4* __restrict__ src, int64_t n,
-                                                  uint32_t* sink) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+constexpr int kBlock = 256;
+constexpr int kUnroll = 8;  // 16-byte loads in flight per thread
+
+// Workgroup g reads the contiguous chunks [g * seg, min((g + 1) * seg, n))
+// (16 bytes each), kUnroll coalesced loads per thread per step, with the
+// non-temporal hint (a streaming read; measured the fastest form on MI355X).
+__global__ __launch_bounds__(kBlock) void read_probe(const u32x4_t* __restrict__ src, int64_t n,
+                                                     int64_t seg, uint32_t* sink) {
+  const int64_t begin = (int64_t)blockIdx.x * seg;
+  const int64_t end = begin + seg < n ? begin + seg : n;
   uint32_t acc = 0;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const uint4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^
-           d.z ^ d.w;
+  int64_t base = begin;
+  for (; base + kUnroll * kBlock <= end; base += kUnroll * kBlock) {
+    u32x4_t v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      v[u] = __builtin_nontemporal_load(src + base + u * kBlock + threadIdx.x);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < n; i += stride) {
-    const uint4 a = src[i];
-    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  for (int64_t i = base + threadIdx.x; i < end; i += kBlock) {
+    const u32x4_t v = __builtin_nontemporal_load(src + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
 }
@@ -32,8 +42,10 @@ extern "C" int gsa_probe_read(const void* src, size_t bytes, uint32_t* sink, int
   if (!src || !sink || grid < 1 || bytes % 16 != 0 || bytes / 16 >= ((size_t)1 << 31) ||
       ((uintptr_t)src & 15) != 0)
     return -1;
-  hipLaunchKernelGGL(read_probe, dim3((unsigned)grid), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), static_cast<const uint4*>(src),
-                     (int64_t)(bytes / 16), sink);
+  const int64_t n = (int64_t)(bytes / 16);
+  const int64_t seg = (n + grid - 1) / grid;
+  hipLaunchKernelGGL(read_probe, dim3((unsigned)grid), dim3(kBlock), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const u32x4_t*>(src), n, seg,
+                     sink);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }

@@ -17,8 +17,9 @@ extern "C" {
 #endif
 
 /* Read `bytes` bytes at device pointer `src` (16-byte aligned, bytes a
- * multiple of 16, bytes / 16 < 2^31) with 128-bit loads, `grid` workgroups
- * of 256 threads in a grid-stride loop, and fold them into one word per
+ * multiple of 16, bytes / 16 < 2^31) with non-temporal 128-bit loads, `grid`
+ * workgroups of 256 threads, each over one contiguous segment of about
+ * bytes / grid bytes, eight loads in flight per thread, and fold them into one word per
  * workgroup that is written to sink[blockIdx] only if it equals a value no
  * input is expected to produce (so the loads cannot be optimised away).
  * sink must hold `grid` uint32 words.  Enqueued on `stream` (a hipStream_t,
