@@ -69,10 +69,16 @@ def kernel_source_digest():
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def traffic_from_profile(cfg):
+def profile_name(cfg, epilogue=False, two_shot=False):
+    """Base name of the committed rocprofv3 summaries for a bench line."""
+    variant = "_rmsnorm" if epilogue else "_two_shot" if two_shot else ""
+    return f"gemv_allreduce{variant}_{cfg}"
+
+
+def traffic_from_profile(cfg, epilogue=False, two_shot=False):
     """HBM bytes per launch from the committed PMC summary for this workload,
     or None if there is none or the kernel source changed since."""
-    path = os.path.join(ROOT, "profiles", f"gemv_allreduce_{cfg}_pmc.md")
+    path = os.path.join(ROOT, "profiles", profile_name(cfg, epilogue, two_shot) + "_pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -349,7 +355,7 @@ def run_config(cfg, args):
 
     nbytes = alg_bytes(W, N, K, B, args.epilogue, args.two_shot)
     achieved = nbytes / (us_per_call * 1e-6) / 1e9
-    traffic = None if args.epilogue or args.two_shot else traffic_from_profile(cfg)
+    traffic = traffic_from_profile(cfg, args.epilogue, args.two_shot)
     line = {
         "metric": METRIC,
         "value": round(us_per_call, 4),
