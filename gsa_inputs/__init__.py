@@ -48,9 +48,13 @@ def bf16_bits(values):
     f = np.ascontiguousarray(values, dtype=np.float32)
     if not np.all(np.isfinite(f)):
         raise ValueError("bf16_bits needs finite values")
-    u = f.view(np.uint32).astype(np.uint64)
-    u = u + 0x7FFF + ((u >> 16) & 1)
-    return (u >> 16).astype(np.uint16)
+    u = f.view(np.uint32)
+    # finite words are at most 0xFF7FFFFF, so the sum stays below 2^32
+    r = (u >> 16) & 1
+    r += 0x7FFF
+    r += u
+    r >>= 16
+    return r.astype(np.uint16)
 
 
 def bf16_bits_to_f32(bits):
@@ -117,3 +121,95 @@ def shard(A, x, W, r):
     Ks = K // W
     return (np.ascontiguousarray(A[:, r * Ks:(r + 1) * Ks]),
             np.ascontiguousarray(x[:, r * Ks:(r + 1) * Ks]))
+
+
+# ---------------------------------------------------------------------------
+# Mixture-of-experts workloads: the expert down-projection fused with the
+# combine all-to-all, at one rank's share.  W ranks hold ne experts each
+# (global expert g = rank * ne + e); every rank has T tokens, each routed to
+# top_k distinct experts drawn uniformly; an expert accepts at most
+# `capacity` tokens per call (assignments past it are dropped, in rank and
+# token order).  Weights ~ N(0, sigma), dispatched token rows ~ N(0, 1), bf16.
+#
+#   m0  W=4 ne=4  H=256  F=128  top-2 of 16,  T=8   small case
+#   m1  W=8 ne=16 H=2048 F=768  top-8 of 128, T=16  Qwen3-30B-A3B-like down_proj
+#   m2  W=8 ne=32 H=7168 F=2048 top-8 of 256, T=16  DeepSeek-V3-like down_proj
+MOE_CONFIGS = {
+    "m0": dict(cfg_id=20, W=4, ne=4, H=256, F=128, top_k=2, T=8, capacity=16, sigma=0.05,
+               name="small MoE, W=4 ne=4 H=256 F=128 top-2 of 16, 8 tokens per rank"),
+    "m1": dict(cfg_id=21, W=8, ne=16, H=2048, F=768, top_k=8, T=16, capacity=16, sigma=0.02,
+               name="Qwen3-30B-A3B-like MoE down_proj, W=8 ne=16 H=2048 F=768 top-8 of 128, "
+                    "16 tokens per rank"),
+    "m2": dict(cfg_id=22, W=8, ne=32, H=7168, F=2048, top_k=8, T=16, capacity=16, sigma=0.02,
+               name="DeepSeek-V3-like MoE down_proj, W=8 ne=32 H=7168 F=2048 top-8 of 256, "
+                    "16 tokens per rank"),
+}
+
+
+def moe_routing(W, ne, T, top_k, capacity, seed=0, cfg_id=0):
+    """Seeded routing of every rank's T tokens: counts[s][g] = tokens of rank
+    s accepted by global expert g (int64, W x W*ne)."""
+    E = W * ne
+    ss = np.random.SeedSequence([int(seed), int(cfg_id), 7])
+    g = np.random.Generator(np.random.PCG64(ss))
+    load = np.zeros(E, np.int64)
+    counts = np.zeros((W, E), np.int64)
+    for s in range(W):
+        for _ in range(T):
+            experts = np.argsort(g.random(E))[:top_k]
+            for ex in experts:
+                if load[ex] < capacity:
+                    load[ex] += 1
+                    counts[s, ex] += 1
+    return counts
+
+
+def make_moe_inputs(cfg, seed=0, rank=0, gap=0):
+    """One rank's inputs for a MoE workload (see MOE_CONFIGS).
+
+    Returns a dict with
+      X        uint16 rows_in x F   dispatched token rows (bf16 bits), laid
+                                    out expert-major then source-rank-major,
+                                    `gap` unused rows after every segment
+      Wd       uint16 ne x H x F    the rank's expert weights (bf16 bits)
+      length   int32 ne x W         rows of source rank s for local expert e
+      in_off   int32 ne x W         first row of that segment in X
+      dst_off  int32 W x ne         first row of that segment in rank s's
+                                    combine buffer (rank s's rows ordered by
+                                    global expert)
+      bufs     float32 W x rows_out x H: every rank's combine buffer before
+               the call: rows of other ranks' experts ~ N(0, 1) (as if their
+               owners had pushed them), this rank's rows NaN sentinel
+    """
+    c = MOE_CONFIGS[cfg] if isinstance(cfg, str) else cfg
+    W, ne, H, F = c["W"], c["ne"], c["H"], c["F"]
+    counts = moe_routing(W, ne, c["T"], c["top_k"], c["capacity"], seed, c["cfg_id"])
+    length = np.zeros((ne, W), np.int32)
+    in_off = np.zeros((ne, W), np.int32)
+    dst_off = np.zeros((W, ne), np.int32)
+    row = 0
+    for e in range(ne):
+        for s in range(W):
+            length[e, s] = counts[s, rank * ne + e]
+            in_off[e, s] = row
+            row += int(length[e, s]) + gap
+    rows_in = max(row, 1)
+    rows_out = c["T"] * c["top_k"]
+    for s in range(W):
+        before = np.concatenate([[0], np.cumsum(counts[s])])
+        for e in range(ne):
+            dst_off[s, e] = before[rank * ne + e]
+    ss = np.random.SeedSequence([int(seed), int(c["cfg_id"]), int(rank), 8])
+    gw, gx, gb = [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(3)]
+    w32 = gw.standard_normal(size=(ne, H, F), dtype=np.float32)
+    w32 *= np.float32(c["sigma"])
+    Wd = bf16_bits(w32)
+    del w32
+    X = bf16_bits(gx.standard_normal(size=(rows_in, F), dtype=np.float32))
+    bufs = gb.normal(0.0, 1.0, size=(W, rows_out, H)).astype(np.float32)
+    for s in range(W):
+        for e in range(ne):
+            o, n = int(dst_off[s, e]), int(length[e, s])
+            bufs[s, o:o + n] = sentinel((n, H))
+    return dict(X=X, Wd=Wd, length=length, in_off=in_off, dst_off=dst_off, bufs=bufs, W=W,
+                ne=ne, H=H, F=F, rows_in=rows_in, rows_out=rows_out, rank=rank, counts=counts)

@@ -1,4 +1,4 @@
-"""CPU oracle for one rank's fused GEMV + one-shot AllReduce.
+"""CPU oracle for one rank's fused GEMV + AllReduce (and the MoE GEMM + combine).
 
 TEST INFRASTRUCTURE.  Only the tests, the package smoke check and the
 benchmark's CPU-baseline leg may import this package.  It shares no code with
@@ -25,6 +25,11 @@ protocol state.  Sources followed (restated, not quoted):
   documentation's higher-precision reduction section;
 * two-shot variant (reduce-scatter of an owned chunk, then all-gather) --
   the documentation's op reference of two_shot_all_reduce_;
+* GEMM + All-to-All for mixture-of-experts -- the fused-operators page,
+  Abstract; the expert-major dispatch layout and the combine that sends each
+  segment back to its source rank at an offset it chose -- the
+  documentation's op reference of all_to_all_vdev_2d and
+  all_to_all_vdev_2d_offset;
 * signal pad next to every symmetric allocation, sized by launched blocks
   times world size, indexed by block -- same documentation, the
   writing-your-own-kernel section and the set_signal_pad_size and
@@ -90,6 +95,13 @@ class Oracle:
         lib.gsa_oracle_two_shot.argtypes = [_f32p, _f32p, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_int64, ctypes.c_int, _f32p, _f32p]
         lib.gsa_oracle_two_shot.restype = None
+        _i32p = ctypes.POINTER(ctypes.c_int32)
+        lib.gsa_oracle_moe_combine.argtypes = [
+            _u16p, _u16p, _i32p, _i32p, _i32p, ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _f64p, _f64p,
+            ctypes.POINTER(ctypes.c_uint8)]
+        lib.gsa_oracle_moe_combine.restype = ctypes.c_int
+        self._i32p = _i32p
         self._lib = lib
 
     def gemv(self, A, x):
@@ -194,6 +206,34 @@ class Oracle:
         self._lib.gsa_oracle_two_shot(_ptr(slots, _f32p), _ptr(gathered, _f32p), W, rank, N, B,
                                       _ptr(out, _f32p), _ptr(mine, _f32p))
         return out, mine
+
+    def moe_combine(self, X, Wd, length, in_off, dst_off, W, rows_out):
+        """Expert products placed by the combine all-to-all, at one rank's
+        share: (y64, abs64, written) with y64 / abs64 float64 W x rows_out x H
+        (NaN where no segment lands) and written uint8 W x rows_out.
+
+        X: uint16 bf16 bits rows_in x F; Wd: uint16 ne x H x F; length and
+        in_off: int ne x W; dst_off: int W x ne.  Raises ValueError on a
+        segment out of range (-1) or two segments on one row (-2)."""
+        X = np.ascontiguousarray(X, dtype=np.uint16)
+        Wd = np.ascontiguousarray(Wd, dtype=np.uint16)
+        ne, H, F = Wd.shape
+        rows_in = X.shape[0]
+        if X.shape[1] != F:
+            raise ValueError("X and Wd disagree on F")
+        length = np.ascontiguousarray(length, dtype=np.int32).reshape(ne, W)
+        in_off = np.ascontiguousarray(in_off, dtype=np.int32).reshape(ne, W)
+        dst_off = np.ascontiguousarray(dst_off, dtype=np.int32).reshape(W, ne)
+        y = np.full((W, rows_out, H), np.nan)
+        a = np.full((W, rows_out, H), np.nan)
+        written = np.zeros((W, rows_out), np.uint8)
+        rc = self._lib.gsa_oracle_moe_combine(
+            _ptr(X, _u16p), _ptr(Wd, _u16p), _ptr(length, self._i32p), _ptr(in_off, self._i32p),
+            _ptr(dst_off, self._i32p), W, ne, H, F, rows_in, rows_out, _ptr(y, _f64p),
+            _ptr(a, _f64p), written.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)))
+        if rc != 0:
+            raise ValueError(f"oracle rejected the segments ({rc})")
+        return y, a, written
 
     def fold_f32(self, slots):
         """fp32 one-shot sum of the given slots in rank order from +0.0f."""

@@ -45,6 +45,17 @@
  *    accumulate in fp32, hand the result back in the input precision (bf16),
  *    which gsa_oracle_scale_f32 rounds to nearest, ties to even.
  *
+ *  - "Overlapping Collective Communication ..." (the fused-operators page),
+ *    Abstract: a third fused operator, GEMM + All-to-All for mixture-of-
+ *    experts models.  "PyTorch Symmetric Memory" documentation, op reference
+ *    of all_to_all_vdev_2d and all_to_all_vdev_2d_offset: the dispatch
+ *    shuffle lays tokens out expert-major (each local expert's segments from
+ *    source ranks 0..W-1), with splits and offsets given on the device; the
+ *    combine is its inverse, sending every segment back to its source rank
+ *    at an offset that rank chose.  gsa_oracle_moe_combine computes each
+ *    local expert's product of its dispatched rows with its weight and
+ *    places every result row where the combine puts it.
+ *
  * Layouts (plain readings, the pages fix none): A_r is N x Ks row-major,
  * x is B x Ks row-major (one token's activation slice is contiguous),
  * slots are W x N x B with element (n, b) of rank r at r*N*B + n*B + b,
@@ -244,4 +255,58 @@ void gsa_oracle_two_shot(const float *slots, const float *gathered, int W, int r
             }
         }
     }
+}
+
+/*
+ * Mixture-of-experts down-projection fused with the combine all-to-all, at
+ * one rank's share.  This rank holds ne experts; expert e's weight Wd[e] is
+ * H x F (H output features of F inputs, row-major).  The dispatched rows X
+ * (rows_in x F) hold, for local expert e and source rank s, len[e*W + s] rows
+ * starting at row in_off[e*W + s].  Row i of that segment goes back to rank
+ * s as row dst_off[s*ne + e] + i of its combine buffer (rows_out x H):
+ *   y64[(s*rows_out + dst_off[s*ne+e] + i)*H + n]
+ *       = sum_k X[in_off[e*W+s] + i][k] * Wd[e][n][k]      (fp64, ascending k)
+ *   abs64[...] = sum_k |X[..][k] * Wd[e][n][k]|            (for the error bound)
+ *   written[s*rows_out + row] = 1 for every row a segment fills.
+ * Other entries are left as the caller set them.  Returns 0; -1 if a length
+ * or offset is negative or a segment leaves X or a combine buffer; -2 if two
+ * segments fill the same row of a combine buffer.
+ */
+int gsa_oracle_moe_combine(const uint16_t *X, const uint16_t *Wd, const int32_t *len,
+                           const int32_t *in_off, const int32_t *dst_off, int W, int ne,
+                           int64_t H, int64_t F, int64_t rows_in, int64_t rows_out,
+                           double *y64, double *abs64, uint8_t *written)
+{
+    if (W < 1 || ne < 1 || H < 1 || F < 1)
+        return -1;
+    for (int s = 0; s < W; ++s) {
+        for (int e = 0; e < ne; ++e) {
+            int64_t n_rows = len[e * W + s];
+            int64_t src = in_off[e * W + s];
+            int64_t dst = dst_off[s * ne + e];
+            if (n_rows < 0 || src < 0 || dst < 0 || src + n_rows > rows_in ||
+                dst + n_rows > rows_out)
+                return -1;
+            for (int64_t i = 0; i < n_rows; ++i) {
+                int64_t orow = (int64_t)s * rows_out + dst + i;
+                if (written[orow])
+                    return -2;
+                written[orow] = 1;
+                const uint16_t *xr = X + (src + i) * F;
+                for (int64_t n = 0; n < H; ++n) {
+                    const uint16_t *wr = Wd + ((int64_t)e * H + n) * F;
+                    double acc = 0.0;
+                    double acc_abs = 0.0;
+                    for (int64_t k = 0; k < F; ++k) {
+                        double q = bf16_bits_to_double(xr[k]) * bf16_bits_to_double(wr[k]);
+                        acc += q;
+                        acc_abs += fabs(q);
+                    }
+                    y64[orow * H + n] = acc;
+                    abs64[orow * H + n] = acc_abs;
+                }
+            }
+        }
+    }
+    return 0;
 }

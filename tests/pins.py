@@ -27,6 +27,11 @@ What pins what:
   two_shot_*       chunk partition (hand values and its defining properties),
                    ownership of every row for every rank against numpy
                    float32 sums in rank order and plain copies
+  moe_*            the MoE product + combine placement: numpy fp64 matmul of
+                   every segment placed by slicing, identity weights (rows
+                   move exactly), one-hot rows (pick a weight column), a
+                   hand-worked golden file, rejection of overlapping and
+                   out-of-range segments
 """
 from fractions import Fraction
 import json
@@ -403,12 +408,136 @@ def pin_two_shot_rows(o):
                     assert np.isnan(mine[n, b]), (rank, n, b)
 
 
+def _moe_call(o, d):
+    return o.moe_combine(d["X"], d["Wd"], d["length"], d["in_off"], d["dst_off"], d["W"],
+                         d["rows_out"])
+
+
+def _tiny_moe(seed, W=3, ne=2, H=5, F=7, max_len=3, gap=1):
+    """Random tiny MoE call: random segment lengths (zeros included), gaps
+    between segments in X, destinations packed in rank s's buffer in global
+    expert order with a random start."""
+    rng = np.random.default_rng(seed)
+    length = rng.integers(0, max_len + 1, size=(ne, W)).astype(np.int32)
+    in_off = np.zeros((ne, W), np.int32)
+    row = 0
+    for e in range(ne):
+        for s in range(W):
+            in_off[e, s] = row
+            row += int(length[e, s]) + gap
+    dst_off = np.zeros((W, ne), np.int32)
+    rows_out = 0
+    for s in range(W):
+        at = int(rng.integers(0, 3))
+        for e in range(ne):
+            dst_off[s, e] = at
+            at += int(length[e, s])
+        rows_out = max(rows_out, at + 1)
+    X = gi.bf16_bits(rng.normal(0, 1, size=(max(row, 1), F)).astype(np.float32))
+    Wd = gi.bf16_bits(rng.normal(0, 1, size=(ne, H, F)).astype(np.float32))
+    return dict(X=X, Wd=Wd, length=length, in_off=in_off, dst_off=dst_off, W=W, ne=ne, H=H, F=F,
+                rows_out=rows_out)
+
+
+def pin_moe_numpy(o):
+    # Against numpy float64 matmul of each segment, placed by plain slicing.
+    for seed in range(4):
+        d = _tiny_moe(seed)
+        y, a, written = _moe_call(o, d)
+        want = np.full_like(y, np.nan)
+        wabs = np.full_like(y, np.nan)
+        X = gi.bf16_bits_to_f32(d["X"]).astype(np.float64)
+        Wd = gi.bf16_bits_to_f32(d["Wd"]).astype(np.float64)
+        for e in range(d["ne"]):
+            for s in range(d["W"]):
+                n, src, dst = d["length"][e, s], d["in_off"][e, s], d["dst_off"][s, e]
+                seg = X[src:src + n]
+                want[s, dst:dst + n] = seg @ Wd[e].T
+                wabs[s, dst:dst + n] = np.abs(seg) @ np.abs(Wd[e]).T
+        assert np.array_equal(np.isnan(y), np.isnan(want)), "rows placed differently"
+        m = ~np.isnan(want)
+        assert np.allclose(y[m], want[m], rtol=1e-12, atol=1e-12), "moe values"
+        assert np.allclose(a[m], wabs[m], rtol=1e-12, atol=1e-12), "moe abs sums"
+        assert int(written.sum()) == int(d["length"].sum()), "rows written"
+
+
+def pin_moe_identity(o):
+    # Identity weights (H = F): every destination row is its source X row,
+    # exactly; rows are told apart by their values.
+    d = _tiny_moe(11, W=4, ne=3, H=6, F=6)
+    eye = gi.bf16_bits(np.eye(6, dtype=np.float32))
+    d["Wd"] = np.stack([eye] * d["ne"])
+    y, a, written = _moe_call(o, d)
+    X = gi.bf16_bits_to_f32(d["X"]).astype(np.float64)
+    for s in range(d["W"]):
+        for e in range(d["ne"]):
+            for i in range(int(d["length"][e, s])):
+                src = int(d["in_off"][e, s]) + i
+                dst = int(d["dst_off"][s, e]) + i
+                assert np.array_equal(y[s, dst], X[src]), (s, e, i)
+
+
+def pin_moe_one_hot(o):
+    # A one-hot source row picks one input column of the expert's weight.
+    d = _tiny_moe(12, W=2, ne=2, H=4, F=5, max_len=2, gap=0)
+    F = d["F"]
+    rows = d["X"].shape[0]
+    hot = [(r * 3 + 1) % F for r in range(rows)]
+    X = np.zeros((rows, F), np.float32)
+    X[np.arange(rows), hot] = 1.0
+    d["X"] = gi.bf16_bits(X)
+    y, a, written = _moe_call(o, d)
+    Wd = gi.bf16_bits_to_f32(d["Wd"]).astype(np.float64)
+    for s in range(d["W"]):
+        for e in range(d["ne"]):
+            for i in range(int(d["length"][e, s])):
+                src = int(d["in_off"][e, s]) + i
+                dst = int(d["dst_off"][s, e]) + i
+                assert np.array_equal(y[s, dst], Wd[e][:, hot[src]]), (s, e, i)
+
+
+def pin_moe_golden(o):
+    with open(os.path.join(GOLDEN, "moe_hand.json")) as f:
+        g = json.load(f)
+    X = gi.bf16_bits(np.array(g["X"], np.float32))
+    Wd = gi.bf16_bits(np.array(g["Wd"], np.float32))
+    y, a, written = o.moe_combine(X, Wd, np.array(g["length"]), np.array(g["in_off"]),
+                                  np.array(g["dst_off"]), g["W"], g["rows_out"])
+    for key, row in g["expect"].items():
+        s, r = map(int, key.split(","))
+        assert np.array_equal(y[s, r], np.array(row)), f"golden moe {key}"
+        assert np.array_equal(a[s, r], np.array(g["expect_abs"][key])), f"golden moe abs {key}"
+    assert int(written.sum()) == len(g["expect"]), "golden moe rows written"
+
+
+def pin_moe_rejects(o):
+    # Two segments on one destination row, and a segment past the buffer.
+    d = _tiny_moe(13, W=2, ne=2, H=3, F=4, max_len=2, gap=0)
+    d["length"][:] = 1
+    d["in_off"] = np.arange(4, dtype=np.int32).reshape(2, 2)
+    d["X"] = d["X"][:1].repeat(4, axis=0)
+    d["dst_off"] = np.array([[0, 0], [0, 1]], np.int32)  # rank 0: both experts on row 0
+    d["rows_out"] = 2
+    try:
+        _moe_call(o, d)
+        raise AssertionError("overlap not rejected")
+    except ValueError as e:
+        assert "(-2)" in str(e), e
+    d["dst_off"] = np.array([[0, 1], [0, 2]], np.int32)  # rank 1, expert 1: row 2 of 2
+    try:
+        _moe_call(o, d)
+        raise AssertionError("out-of-range segment not rejected")
+    except ValueError as e:
+        assert "(-1)" in str(e), e
+
+
 PINS = [pin_brute_force, pin_single_rank, pin_shard_sum, pin_identity, pin_one_hot,
         pin_small_integers, pin_rank_order_exact, pin_bf16_decode, pin_golden,
         pin_fold_order, pin_fold_zero_start, pin_fold_fp32, pin_fold_matches_sequence,
         pin_rms_golden, pin_rms_constant_column, pin_rms_unit_rms, pin_rms_scale_invariant,
         pin_rms_bias_cancels, pin_rms_columns_independent, pin_scale_exact, pin_bf16_rne,
-        pin_two_shot_chunks, pin_two_shot_rows]
+        pin_two_shot_chunks, pin_two_shot_rows, pin_moe_numpy, pin_moe_identity,
+        pin_moe_one_hot, pin_moe_golden, pin_moe_rejects]
 
 
 def failing_pins(o):

@@ -51,6 +51,19 @@ MUTANTS = {
                                "for (int r = W - 1; r >= 0; --r)\n                    acc = acc + slots"),
     "two_shot_skips_own": ("for (int r = 0; r < W; ++r)\n                    acc = acc + slots",
                            "for (int r = 0; r < W; ++r)\n                    if (r != rank) acc = acc + slots"),
+    "moe_weight_transposed": ("bf16_bits_to_double(xr[k]) * bf16_bits_to_double(wr[k])",
+                              "bf16_bits_to_double(xr[k]) * bf16_bits_to_double(Wd[(int64_t)e * H * F + (k % H) * F + n % F])"),
+    "moe_expert_ignored": ("const uint16_t *wr = Wd + ((int64_t)e * H + n) * F;",
+                           "const uint16_t *wr = Wd + ((int64_t)0 * H + n) * F;"),
+    "moe_len_transposed": ("int64_t n_rows = len[e * W + s];", "int64_t n_rows = len[(s * ne + e) % (W * ne)];"),
+    "moe_in_off_transposed": ("int64_t src = in_off[e * W + s];", "int64_t src = in_off[(s * ne + e) % (W * ne)];"),
+    "moe_dst_transposed": ("int64_t dst = dst_off[s * ne + e];", "int64_t dst = dst_off[(e * W + s) % (W * ne)];"),
+    "moe_dropped_last_row": ("for (int64_t i = 0; i < n_rows; ++i) {", "for (int64_t i = 0; i < n_rows - 1; ++i) {"),
+    "moe_dropped_last_k": ("for (int64_t k = 0; k < F; ++k) {", "for (int64_t k = 0; k < F - 1; ++k) {"),
+    "moe_dest_rank_ignored": ("int64_t orow = (int64_t)s * rows_out + dst + i;", "int64_t orow = dst + i;"),
+    "moe_first_row_only": ("const uint16_t *xr = X + (src + i) * F;", "const uint16_t *xr = X + src * F;"),
+    "moe_abs_dropped": ("acc_abs += fabs(q);", "acc_abs += q;"),
+    "moe_overlap_unchecked": ("if (written[orow])\n                    return -2;\n", ""),
     "nan_branch_dropped": ("if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0)\n        return (uint16_t)((u >> 16) | 0x0040u);\n", ""),
 }
 
