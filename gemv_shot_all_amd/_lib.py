@@ -12,6 +12,7 @@ GSA_ENOMEM = -2
 GSA_EHIP = -3
 GSA_ETIMEOUT = -4
 GSA_ESTATE = -5
+GSA_ESPLIT = -6
 GSA_FLAG_PUBLISHED = 0xFFFFFFFF
 GSA_FLAG_TILE_ROWS = 16
 GSA_PAD_HEADER_WORDS = 16
@@ -20,11 +21,15 @@ GSA_MAX_B = 16
 GSA_MAX_X_LDS_BYTES = 128 * 1024
 GSA_DTYPE_F32 = 0
 GSA_DTYPE_BF16 = 1
+GSA_MOE_MAX_TOKENS = 16
+GSA_MOE_MAX_F = 4088
 
 EXPORTS = ("gsa_symm_alloc", "gsa_symm_free", "gsa_symm_slots", "gsa_symm_signal_pad",
            "gsa_symm_gathered", "gsa_signal_pad_row_stride", "gsa_signal_pad_reset",
            "gsa_gemv_allreduce", "gsa_gemv_allreduce_two_shot", "gsa_gemv_allreduce_rmsnorm",
-           "gsa_signal_pad_status", "gsa_set_wait_timeout_us", "gsa_strerror")
+           "gsa_signal_pad_status", "gsa_set_wait_timeout_us", "gsa_strerror",
+           "gsa_a2a_pad_words", "gsa_a2a_alloc", "gsa_a2a_free", "gsa_a2a_buffers",
+           "gsa_a2a_signal_pads", "gsa_a2a_reset", "gsa_moe_gemm_all_to_all", "gsa_a2a_status")
 
 
 class gsa_epilogue(ctypes.Structure):
@@ -86,6 +91,24 @@ def lib():
         L.gsa_set_wait_timeout_us.restype = ci
         L.gsa_strerror.argtypes = [ci]
         L.gsa_strerror.restype = ctypes.c_char_p
+        L.gsa_a2a_pad_words.argtypes = [ci, ci, i64]
+        L.gsa_a2a_pad_words.restype = i64
+        L.gsa_a2a_alloc.argtypes = [ci, ci, i64, i64, ctypes.POINTER(vp)]
+        L.gsa_a2a_alloc.restype = ci
+        L.gsa_a2a_free.argtypes = [vp]
+        L.gsa_a2a_free.restype = ci
+        L.gsa_a2a_buffers.argtypes = [vp]
+        L.gsa_a2a_buffers.restype = vp
+        L.gsa_a2a_signal_pads.argtypes = [vp]
+        L.gsa_a2a_signal_pads.restype = vp
+        L.gsa_a2a_reset.argtypes = [vp, ci, ci, i64, u32, vp]
+        L.gsa_a2a_reset.restype = ci
+        L.gsa_moe_gemm_all_to_all.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, i64, i64, i64,
+                                              i64, vp]
+        L.gsa_moe_gemm_all_to_all.restype = ci
+        L.gsa_a2a_status.argtypes = [vp, ci, vp, ctypes.POINTER(ci), ctypes.POINTER(i64),
+                                     ctypes.POINTER(ci)]
+        L.gsa_a2a_status.restype = ci
         _lib = L
     return _lib
 
@@ -295,3 +318,96 @@ class SymmBuffer:
 
     def __exit__(self, *exc):
         self.close()
+
+
+# --- mixture of experts: expert GEMM fused with the combine all-to-all ---
+
+def gsa_a2a_pad_words(W, ne, H):
+    return lib().gsa_a2a_pad_words(W, ne, H)
+
+
+def gsa_a2a_alloc(W, ne, H, rows_out):
+    h = ctypes.c_void_p()
+    _check(lib().gsa_a2a_alloc(W, ne, H, rows_out, ctypes.byref(h)), "gsa_a2a_alloc")
+    return h.value
+
+
+def gsa_a2a_free(h):
+    _check(lib().gsa_a2a_free(h), "gsa_a2a_free")
+
+
+def gsa_a2a_buffers(h):
+    p = lib().gsa_a2a_buffers(h)
+    if not p:
+        raise GsaError(GSA_EINVAL, "gsa_a2a_buffers")
+    return p
+
+
+def gsa_a2a_signal_pads(h):
+    p = lib().gsa_a2a_signal_pads(h)
+    if not p:
+        raise GsaError(GSA_EINVAL, "gsa_a2a_signal_pads")
+    return p
+
+
+def gsa_a2a_reset(pads, W, ne, H, published_mask, stream=None):
+    _check(lib().gsa_a2a_reset(_ptr(pads), W, ne, H, published_mask, _stream(stream)),
+           "gsa_a2a_reset")
+
+
+def gsa_moe_gemm_all_to_all(X, Wd, splits, dst_off, bufs, pads, W, rank, ne, H, F, rows_in,
+                            rows_out, stream=None):
+    _check(lib().gsa_moe_gemm_all_to_all(_ptr(X), _ptr(Wd), _ptr(splits), _ptr(dst_off),
+                                         _ptr(bufs), _ptr(pads), W, rank, ne, H, F, rows_in,
+                                         rows_out, _stream(stream)),
+           "gsa_moe_gemm_all_to_all")
+
+
+def gsa_a2a_status(pads, rank, stream=None):
+    """(code, tile, peer) of rank `rank`'s pad; synchronizes the stream."""
+    c, t, p = ctypes.c_int(), ctypes.c_int64(), ctypes.c_int()
+    _check(lib().gsa_a2a_status(_ptr(pads), rank, _stream(stream), ctypes.byref(c),
+                                ctypes.byref(t), ctypes.byref(p)), "gsa_a2a_status")
+    return c.value, t.value, p.value
+
+
+class A2ABuffer:
+    """W combine buffers (rows_out x H fp32 each) and W signal pads, freed on
+    close().  Convenience wrapper over gsa_a2a_alloc / gsa_a2a_free."""
+
+    def __init__(self, W, ne, H, rows_out):
+        self.W, self.ne, self.H, self.rows_out = W, ne, H, rows_out
+        self.handle = gsa_a2a_alloc(W, ne, H, rows_out)
+        self.bufs = gsa_a2a_buffers(self.handle)
+        self.pads = gsa_a2a_signal_pads(self.handle)
+        self.pad_words = gsa_a2a_pad_words(W, ne, H)
+        self.row_stride = gsa_signal_pad_row_stride(H)
+        self.tiles = (H + GSA_FLAG_TILE_ROWS - 1) // GSA_FLAG_TILE_ROWS
+
+    def bufs_view(self):
+        """torch float32 view (W, rows_out, H) of the combine buffers."""
+        import torch
+        return device_view(self.bufs, (self.W, self.rows_out, self.H), torch.float32)
+
+    def pads_view(self):
+        """torch int32 view (W, pad_words) of the signal pads."""
+        import torch
+        return device_view(self.pads, (self.W, self.pad_words), torch.int32)
+
+    def flags(self):
+        """Host copy (numpy uint32, W pads x W sources x ne x tiles)."""
+        import numpy as np
+        raw = self.pads_view().cpu().numpy().view(np.uint32)
+        rows = raw[:, GSA_PAD_HEADER_WORDS:].reshape(self.W, self.W, self.ne, self.row_stride)
+        return rows[..., :self.tiles].copy()
+
+    def reset(self, published_mask, stream=None):
+        gsa_a2a_reset(self.pads, self.W, self.ne, self.H, published_mask, stream)
+
+    def status(self, rank, stream=None):
+        return gsa_a2a_status(self.pads, rank, stream)
+
+    def close(self):
+        if self.handle:
+            gsa_a2a_free(self.handle)
+            self.handle = None

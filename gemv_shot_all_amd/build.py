@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libgsa.so")
-SOURCES = ["gsa_api.hip", "gemv_allreduce.hip"]
+SOURCES = ["gsa_api.hip", "gemv_allreduce.hip", "moe_a2a.hip"]
 # The benchmark's achievable-bandwidth reference (include/gsa_probe.h).
 PROBE_LIBRARY = os.path.join(PKG, "libgsa_probe.so")
 PROBE_SOURCES = ["hbm_read_probe.hip"]
@@ -49,7 +49,8 @@ def needs_build():
     if not os.path.exists(LIBRARY):
         return True
     t = os.path.getmtime(LIBRARY)
-    deps = sources() + [os.path.join(CSRC, "gsa_internal.h"), os.path.join(INCLUDE, "gsa.h")]
+    deps = sources() + [os.path.join(CSRC, "gsa_internal.h"), os.path.join(CSRC, "gsa_device.h"),
+                        os.path.join(INCLUDE, "gsa.h")]
     return any(os.path.getmtime(d) > t for d in deps)
 
 

@@ -31,6 +31,21 @@ struct gsa_symm {
   int device;
 };
 
+// The MoE GEMM + combine all-to-all: W combine buffers and W pads in one
+// device allocation.
+struct gsa_a2a {
+  int W;
+  int ne;
+  int64_t H;
+  int64_t rows_out;
+  int64_t row_stride;
+  int64_t pad_words;
+  void* base;
+  float* bufs;
+  uint32_t* pads;
+  int device;
+};
+
 namespace {
 
 std::mutex g_mu;
@@ -60,6 +75,10 @@ gsa_symm* find_by_pad(const void* pad) {
 std::unordered_set<const gsa_symm*> g_handles;
 
 bool known(const gsa_symm* h) { return h && g_handles.count(h) != 0; }
+
+std::unordered_set<const gsa_a2a*> g_a2a;                  // live MoE handles
+std::unordered_map<uintptr_t, gsa_a2a*> g_a2a_by_pads;     // pads -> handle
+bool known(const gsa_a2a* h) { return h && g_a2a.count(h) != 0; }
 
 // Wall-clock ticks for `us` microseconds on the current device.
 int ticks_for(uint32_t us, uint64_t* ticks) {
@@ -333,6 +352,173 @@ int gsa_set_wait_timeout_us(uint32_t us) {
   return GSA_OK;
 }
 
+int64_t gsa_a2a_pad_words(int W, int ne, int64_t H) {
+  if (W < 1 || W > GSA_MAX_W || ne < 1 || ne > 256 || H < 1 || H > ((int64_t)1 << 30)) return -1;
+  return GSA_PAD_HEADER_WORDS + (int64_t)W * ne * gsa_signal_pad_row_stride(H);
+}
+
+int gsa_a2a_alloc(int W, int ne, int64_t H, int64_t rows_out, gsa_a2a** out) {
+  if (!out) return GSA_EINVAL;
+  *out = nullptr;
+  const int64_t pad_words = gsa_a2a_pad_words(W, ne, H);
+  if (pad_words < 0 || rows_out < 1) return GSA_EINVAL;
+  if ((int64_t)W * rows_out > ((int64_t)1 << 40) / H) return GSA_EINVAL;
+  const size_t buf_bytes = round_up((size_t)W * rows_out * H * sizeof(float), kAlign);
+  const size_t pad_bytes = round_up((size_t)W * pad_words * sizeof(uint32_t), kAlign);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GSA_EHIP;
+  void* base = nullptr;
+  if (hipMalloc(&base, buf_bytes + pad_bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    return GSA_ENOMEM;
+  }
+  if (hipMemset(base, 0, buf_bytes + pad_bytes) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(base);
+    return GSA_EHIP;
+  }
+  uint32_t* pads = reinterpret_cast<uint32_t*>(static_cast<char*>(base) + buf_bytes);
+  gsa_a2a* h = new gsa_a2a{W, ne, H, rows_out, gsa_signal_pad_row_stride(H), pad_words, base,
+                           static_cast<float*>(base), pads, dev};
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_a2a.insert(h);
+  g_a2a_by_pads[(uintptr_t)pads] = h;
+  *out = h;
+  return GSA_OK;
+}
+
+int gsa_a2a_free(gsa_a2a* h) {
+  if (!h) return GSA_OK;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!known(h)) return GSA_EINVAL;
+    g_a2a_by_pads.erase((uintptr_t)h->pads);
+    g_a2a.erase(h);
+  }
+  int prev = 0;
+  hipError_t e = hipGetDevice(&prev);
+  if (e == hipSuccess && prev != h->device) e = hipSetDevice(h->device);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipFree(h->base);
+  if (prev != h->device) (void)hipSetDevice(prev);
+  delete h;
+  return e == hipSuccess ? GSA_OK : GSA_EHIP;
+}
+
+float* gsa_a2a_buffers(const gsa_a2a* h) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  return known(h) ? h->bufs : nullptr;
+}
+
+uint32_t* gsa_a2a_signal_pads(const gsa_a2a* h) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  return known(h) ? h->pads : nullptr;
+}
+
+int gsa_a2a_reset(uint32_t* pads, int W, int ne, int64_t H, uint32_t published_mask,
+                  void* stream) {
+  if (!pads || W < 1 || W > GSA_MAX_W || (published_mask >> W)) return GSA_EINVAL;
+  int64_t stride, pad_words;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_a2a_by_pads.find((uintptr_t)pads);
+    if (it == g_a2a_by_pads.end()) return GSA_EINVAL;
+    const gsa_a2a* h = it->second;
+    if (h->W != W || h->ne != ne || h->H != H) return GSA_EINVAL;
+    stride = h->row_stride;
+    pad_words = h->pad_words;
+  }
+  hipError_t e = gsa::launch_a2a_reset(pads, W, ne, (int)stride, pad_words, published_mask,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? GSA_OK : GSA_EHIP;
+}
+
+int gsa_moe_gemm_all_to_all(const uint16_t* X, const uint16_t* Wd, const int32_t* splits,
+                            const int32_t* dst_off, float* bufs, uint32_t* pads, int W,
+                            int rank, int ne, int64_t H, int64_t F, int64_t rows_in,
+                            int64_t rows_out, void* stream) {
+  // Scalars first: these checks touch no HIP state.
+  if (W < 1 || W > GSA_MAX_W || rank < 0 || rank >= W || ne < 1 || ne > 256) return GSA_EINVAL;
+  if (H < 1 || F < 8 || F % 8 != 0 || F > GSA_MOE_MAX_F || rows_in < 1 || rows_out < 1)
+    return GSA_EINVAL;
+  if (H * F * 2 >= ((int64_t)1 << 31)) return GSA_EINVAL;  // one expert through a buffer resource
+  if (rows_in > ((int64_t)1 << 40) / F) return GSA_EINVAL;
+  if (!X || !Wd || !splits || !dst_off || !bufs || !pads) return GSA_EINVAL;
+  if (!aligned16(X) || !aligned16(Wd) || !aligned16(bufs) || !aligned16(pads) ||
+      ((uintptr_t)splits & 3u) || ((uintptr_t)dst_off & 3u))
+    return GSA_EINVAL;
+  gsa::MoeArgs a;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_a2a_by_pads.find((uintptr_t)pads);
+    if (it == g_a2a_by_pads.end()) return GSA_EINVAL;
+    const gsa_a2a* h = it->second;
+    if (h->bufs != bufs || h->W != W || h->ne != ne || h->H != H || h->rows_out != rows_out)
+      return GSA_EINVAL;
+    a.row_stride = (int)h->row_stride;
+    a.pad_words = h->pad_words;
+  }
+  a.X = X;
+  a.Wd = Wd;
+  a.splits = splits;
+  a.dst_off = dst_off;
+  a.bufs = bufs;
+  a.pads = pads;
+  a.W = W;
+  a.rank = rank;
+  a.ne = ne;
+  a.C = (int)(F / 8);
+  a.tiles = (int)tiles_of(H);
+  a.H = H;
+  a.F = F;
+  a.rows_in = rows_in;
+  a.rows_out = rows_out;
+  int rc = ticks_for(g_timeout_us.load(std::memory_order_relaxed), &a.timeout_ticks);
+  if (rc != GSA_OK) return rc;
+  hipError_t e = gsa::launch_moe(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return GSA_EHIP;
+  }
+  return GSA_OK;
+}
+
+int gsa_a2a_status(const uint32_t* pads, int rank, void* stream, int* code, int64_t* tile,
+                   int* peer) {
+  if (!pads || !code || !tile || !peer) return GSA_EINVAL;
+  int64_t pad_words;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_a2a_by_pads.find((uintptr_t)pads);
+    if (it == g_a2a_by_pads.end() || rank < 0 || rank >= it->second->W) return GSA_EINVAL;
+    pad_words = it->second->pad_words;
+  }
+  uint32_t hdr[GSA_PAD_HEADER_WORDS];
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(hdr, pads + (int64_t)rank * pad_words, sizeof hdr, hipMemcpyDeviceToHost,
+                     s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return GSA_EHIP;
+  const uint32_t bits = hdr[gsa::kHdrErrorBits];
+  *tile = -1;
+  *peer = -1;
+  if (bits & gsa::kErrSplit) {
+    *code = GSA_ESPLIT;
+    *tile = (int64_t)hdr[gsa::kHdrSplitExpert];
+  } else if (bits & gsa::kErrState) {
+    *code = GSA_ESTATE;
+    *tile = (int64_t)hdr[gsa::kHdrStateTile];
+  } else if (bits & gsa::kErrTimeout) {
+    *code = GSA_ETIMEOUT;
+    const uint32_t key = hdr[gsa::kHdrTimeoutKey];
+    *tile = (int64_t)(key / 8u);
+    *peer = (int)(key % 8u);
+  } else {
+    *code = GSA_OK;
+  }
+  return GSA_OK;
+}
+
 const char* gsa_strerror(int code) {
   switch (code) {
     case GSA_OK: return "ok";
@@ -341,6 +527,8 @@ const char* gsa_strerror(int code) {
     case GSA_EHIP: return "HIP runtime error";
     case GSA_ETIMEOUT: return "signal-pad wait timed out";
     case GSA_ESTATE: return "own flag row not usable (marked published or epochs exhausted)";
+    case GSA_ESPLIT: return "a split or offset on the device is out of range, or an expert got "
+                            "more tokens than it takes";
     default: return "unknown error";
   }
 }

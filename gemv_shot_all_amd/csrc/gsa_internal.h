@@ -15,6 +15,7 @@ enum : int {
   kHdrTimeoutKey = 1,  // atomicMin of tile * 8 + peer, 0xFFFFFFFF = none
   kHdrStateTile = 2,   // atomicMin of the tile with a bad own flag row
   kHdrEpiWaitTile = 6, // atomicMin of a tile whose epilogue wait expired, 0xFFFFFFFF = none
+  kHdrSplitExpert = 7, // MoE: atomicMin of a local expert with a bad split table
 };
 // The epilogue's scratch (fp32 / uint32 words, 128-byte lines of 32 words):
 //   records   tiles lines: 16 partial sums of squares, the call mark at word 16
@@ -40,7 +41,7 @@ __host__ __device__ constexpr int64_t epi_top_off(int64_t tiles) {
 __host__ __device__ constexpr int64_t epi_scratch_words(int64_t tiles) {
   return epi_top_off(tiles) + kEpiRecordWords;
 }
-enum : uint32_t { kErrTimeout = 1u, kErrState = 2u, kErrEpiWait = 4u };
+enum : uint32_t { kErrTimeout = 1u, kErrState = 2u, kErrEpiWait = 4u, kErrSplit = 8u };
 
 // Everything one launch needs.  Built on the host per call, passed by value.
 struct GemvArgs {
@@ -94,5 +95,25 @@ hipError_t launch_gemv(const Launch& l, const GemvArgs& a, hipStream_t s);
 // counts), so the next call starts counting from zero.
 hipError_t launch_pad_reset(uint32_t* pad, int W, int row_stride, int tiles,
                             uint32_t published_mask, float* epi_scratch, hipStream_t s);
+
+// The MoE GEMM + combine all-to-all (moe_a2a.hip).
+struct MoeArgs {
+  const uint16_t* X;        // rows_in x F bf16 bits
+  const uint16_t* Wd;       // ne x H x F bf16 bits
+  const int32_t* splits;    // 2 x ne x W: lengths, then offsets in X
+  const int32_t* dst_off;   // W x ne
+  float* bufs;              // W x rows_out x H fp32
+  uint32_t* pads;           // W pads of pad_words words
+  int W, rank, ne;
+  int C;                    // F / 8 (16-byte chunks per row)
+  int tiles;                // ceil(H / 16)
+  int row_stride;           // words between flag rows
+  int64_t H, F, rows_in, rows_out, pad_words;
+  uint64_t timeout_ticks;
+};
+size_t moe_lds_bytes(int C);
+hipError_t launch_moe(const MoeArgs& a, hipStream_t s);
+hipError_t launch_a2a_reset(uint32_t* pads, int W, int ne, int row_stride, int64_t pad_words,
+                            uint32_t published_mask, hipStream_t s);
 
 }  // namespace gsa

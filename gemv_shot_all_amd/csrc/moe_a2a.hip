@@ -1,0 +1,268 @@
+// moe_a2a.hip -- a mixture-of-experts down-projection fused with the combine
+// all-to-all, at one rank's share, for gfx950.
+//
+// Rank `rank` holds ne experts.  Workgroup (e, t) owns local expert e and
+// output features [16 t, 16 t + 16).  Inside one launch it
+//   a. reads the expert's split table (one segment per source rank), checks
+//      it, and lays out its M <= 16 tokens: token j's row in X and the row
+//      of its source rank's combine buffer that receives it;
+//   b. copies the tokens' rows of X into LDS (each compute wave its own
+//      k-slice, straight from memory with LDS DMA) and streams the tile's 16
+//      weight rows with v_mfma_f32_16x16x32_bf16 (weights as the A operand,
+//      tokens as the B operand, fp32 accumulation), the waves' partials
+//      summed in wave order;
+//   c. stores each token's 16 results into its source rank's combine buffer,
+//      waits for the stores, raises flag (rank, e, t) in every rank's pad,
+//      and waits (bounded) for flag (p, e, t) of every other rank p in its
+//      own pad.
+//
+// Sources (restated): a GEMM fused with an All-to-All for mixture-of-
+// experts models, each workgroup handing its finished results to the
+// collective at once and writing them straight into the destination's
+// memory -- "Overlapping Collective Communication with Dependent Computation
+// ... GPU-Initiated Intra-Kernel Networking", Abstract.  The dispatch layout
+// (expert-major, source ranks in order, splits and offsets on the device)
+// and the combine back to the source ranks -- "PyTorch Symmetric Memory"
+// documentation, op reference of all_to_all_vdev_2d and
+// all_to_all_vdev_2d_offset.  fp32 accumulation of bf16 -- same
+// documentation, higher-precision reduction.
+//
+// Memory ordering as in the GEMV kernels: result rows and flags are
+// agent-scope (sc1) accesses; every result store of the workgroup completes
+// (s_waitcnt vmcnt(0), then a barrier) before its flags are stored.
+
+#include "gsa_device.h"
+#include "gsa_internal.h"
+
+namespace gsa {
+namespace {
+
+constexpr int kTok = GSA_MOE_MAX_TOKENS;  // the MFMA B operand's 16 columns
+constexpr int kWaves = 4;                 // compute waves per workgroup
+constexpr int kRing = 8;                  // weight steps in flight per lane
+static_assert(kTok == 16, "one 16 x 16 x 32 MFMA tile of tokens");
+
+__device__ __forceinline__ uint32_t* moe_flag(const MoeArgs& a, int pad, int src, int e, int t) {
+  return a.pads + (int64_t)pad * a.pad_words + GSA_PAD_HEADER_WORDS +
+         (int64_t)(src * a.ne + e) * a.row_stride + t;
+}
+
+// Every other rank's flag (p, e, t) in the own pad >= epoch, bounded by the
+// timeout; on expiry the smallest missing rank is recorded (wave 0 only).
+__device__ void moe_wait_peers(const MoeArgs& a, int lane, int e, int t, uint32_t epoch) {
+  uint32_t* own_pad = a.pads + (int64_t)a.rank * a.pad_words;
+  const uint64_t start = wall_clock64();
+  for (;;) {
+    const uint32_t f = __hip_atomic_load(moe_flag(a, a.rank, min(lane, a.W - 1), e, t),
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool lane_ok = lane >= a.W || lane == a.rank || f >= epoch;
+    const uint64_t missing = __ballot(!lane_ok);
+    if (missing == 0) return;
+    if (wall_clock64() - start > a.timeout_ticks) {
+      if (lane == 0) {
+        const uint32_t peer = (uint32_t)(__ffsll((long long)missing) - 1);
+        atomicOr(own_pad + kHdrErrorBits, kErrTimeout);
+        atomicMin(own_pad + kHdrTimeoutKey, (uint32_t)(e * a.tiles + t) * 8u + peer);
+      }
+      return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// LDS (dynamic): x [16][C + 1] chunks (column C and rows >= M zero), the
+// waves' 16 x 16 partials, the results token-major [16][16].
+__global__ __launch_bounds__(kWaves * 64) void moe_gemm_a2a(MoeArgs a) {
+  extern __shared__ uint4 lds[];
+  __shared__ int64_t s_xrow[kTok];  // token j: its row of X
+  __shared__ int64_t s_dst[kTok];   // token j: first element of its combine row
+  __shared__ uint32_t s_ctl[4];     // epoch, ok, M
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int e = (int)(blockIdx.x / (unsigned)a.tiles);
+  const int t = (int)(blockIdx.x % (unsigned)a.tiles);
+  const int C = a.C;
+  const int CP = C + 1;  // padded LDS row: the 16 token rows of one chunk hit distinct banks
+  float* red = reinterpret_cast<float*>(lds + 16 * CP);
+  float* yt = red + kWaves * 256;
+  uint32_t* own_pad = a.pads + (int64_t)a.rank * a.pad_words;
+
+  if (wave == 0) {
+    // Lane s < W: source rank s's segment (every lane reads a valid entry).
+    const int s = min(lane, a.W - 1);
+    const int64_t len = a.splits[e * a.W + s];
+    const int64_t ioff = a.splits[(int64_t)a.ne * a.W + e * a.W + s];
+    const int64_t doff = a.dst_off[(int64_t)s * a.ne + e];
+    const bool bad = lane < a.W && (len < 0 || ioff < 0 || doff < 0 || len > kTok ||
+                                    ioff + len > a.rows_in || doff + len > a.rows_out);
+    const int mine = (lane < a.W && !bad) ? (int)len : 0;
+    int before = 0, M = 0;  // rows of the lanes below this one, and in total
+    for (int r = 0; r < a.W; ++r) {
+      const int lr = __builtin_amdgcn_readlane(mine, r);
+      before += r < lane ? lr : 0;
+      M += lr;
+    }
+    const bool splits_ok = __ballot(bad) == 0 && M <= kTok;
+    const uint32_t own = __hip_atomic_load(moe_flag(a, a.rank, a.rank, e, t), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    const bool own_ok = own < GSA_FLAG_PUBLISHED - 1u;  // not marked published, not exhausted
+    if (splits_ok && own_ok && lane < a.W) {
+      for (int i = 0; i < mine; ++i) {
+        s_xrow[before + i] = ioff + i;
+        s_dst[before + i] = ((int64_t)lane * a.rows_out + doff + i) * a.H;
+      }
+    }
+    if (lane == 0) {
+      if (!splits_ok) {
+        atomicOr(own_pad + kHdrErrorBits, kErrSplit);
+        atomicMin(own_pad + kHdrSplitExpert, (uint32_t)e);
+      }
+      if (!own_ok) {
+        atomicOr(own_pad + kHdrErrorBits, kErrState);
+        atomicMin(own_pad + kHdrStateTile, (uint32_t)(e * a.tiles + t));
+      }
+      s_ctl[0] = own + 1u;
+      s_ctl[1] = (splits_ok && own_ok) ? 1u : 0u;
+      s_ctl[2] = (uint32_t)M;
+    }
+  }
+  __syncthreads();  // B0: token table and decision in LDS
+  if (s_ctl[1] == 0u) return;
+  const int M = (int)s_ctl[2];
+
+  if (M > 0) {
+    const int steps = (C + 3) / 4;
+    const int per_wave = (steps + kWaves - 1) / kWaves;
+    const int s_begin = wave * per_wave;
+    const int n_steps = max(0, min(steps, s_begin + per_wave) - s_begin);
+    const int c_begin = min(4 * s_begin, C);
+    const int c_end = min(4 * (s_begin + n_steps), C);
+
+    // This wave's k-slice of every token row, straight into LDS.
+    const uint4* xg = reinterpret_cast<const uint4*>(a.X);
+    for (int c0 = c_begin; c0 < c_end; c0 += 64) {
+      if (c0 + lane < c_end) {
+        for (int j = 0; j < M; ++j) lds_dma16(xg + s_xrow[j] * C + c0 + lane, lds + j * CP + c0);
+      }
+    }
+    const uint16_t* w_e = a.Wd + (int64_t)e * a.H * a.F;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(w_e, (uint32_t)(a.H * a.F * 2));
+    const int kq = lane >> 4;
+    const uint32_t a_row = ((uint32_t)(t * 16 + (lane & 15)) * (uint32_t)C + kq) * 16u;
+    const uint32_t kOutOfRange = 0x80000000u;  // past any weight: reads zeros
+    // Weight chunk of the wave's step j; steps past n_steps (and rows past H)
+    // read zeros.  Every load is issued unconditionally, so the
+    // outstanding-load counts are static.
+    auto a_off = [&](int j) {
+      return j < n_steps ? a_row + (uint32_t)(s_begin + j) * 64u : kOutOfRange;
+    };
+    uint4 ring[kRing];
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) ring[u] = buf_load16(ra, a_off(u));
+    // The x copies went out before the ring loads: once at most kRing loads
+    // are outstanding they have landed.
+    wait_vm_le<kRing>();
+    for (int c = c_begin + lane; c < c_end; c += 64)
+      for (int j = M; j < kTok; ++j) lds[j * CP + c] = make_uint4(0u, 0u, 0u, 0u);
+    if (lane < kTok) lds[lane * CP + C] = make_uint4(0u, 0u, 0u, 0u);
+
+    const int xrow = (lane & 15) * CP;
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j0 = 0; j0 < n_steps; j0 += kRing) {
+      uint4 xv[kRing];
+#pragma unroll
+      for (int u = 0; u < kRing; ++u) {
+        const int j = j0 + u;
+        const int chunk = 4 * (s_begin + j) + kq;
+        xv[u] = lds[xrow + (j < n_steps && chunk < C ? chunk : C)];
+      }
+#pragma unroll
+      for (int u = 0; u < kRing; ++u) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ring[u]),
+                                                      __builtin_bit_cast(bf16x8_t, xv[u]), acc, 0,
+                                                      0, 0);
+        ring[u] = buf_load16(ra, a_off(j0 + u + kRing));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // Partials: feature 4 * (lane >> 4) + q, token lane & 15.
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      red[(wave * 16 + 4 * (lane >> 4) + q) * 16 + (lane & 15)] = acc[q];
+    __syncthreads();  // B1
+    {
+      const int nl = 4 * wave + (lane >> 4);
+      const int bl = lane & 15;
+      float y = red[nl * 16 + bl];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) y = y + red[(w * 16 + nl) * 16 + bl];
+      yt[bl * 16 + nl] = y;
+    }
+    __syncthreads();  // B2: results token-major
+    // Thread (j, n): token j's feature 16 t + n; 16 threads write one row's
+    // 64 contiguous bytes.
+    const int j = tid >> 4;
+    const int n = tid & 15;
+    const int64_t feat = (int64_t)t * 16 + n;
+    if (j < M && feat < a.H) store_coherent(&a.bufs[s_dst[j] + feat], yt[j * 16 + n]);
+  }
+  wait_vm_all();    // this wave's result rows are at the coherence point ...
+  __syncthreads();  // B3 ... in every wave
+  if (wave == 0) {
+    const uint32_t epoch = s_ctl[0];
+    if (lane < a.W) store_flag(moe_flag(a, lane, a.rank, e, t), epoch);
+    moe_wait_peers(a, lane, e, t, epoch);
+  }
+}
+
+__global__ void a2a_reset_kernel(uint32_t* pads, int ne, int row_stride, int64_t pad_words,
+                                 int64_t total, uint32_t mask) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int64_t w = i % pad_words;  // word within its pad
+  uint32_t v;
+  if (w < GSA_PAD_HEADER_WORDS) {
+    v = (w == kHdrTimeoutKey || w == kHdrStateTile || w == kHdrEpiWaitTile ||
+         w == kHdrSplitExpert)
+            ? 0xFFFFFFFFu
+            : 0u;
+  } else {
+    const int src = (int)((w - GSA_PAD_HEADER_WORDS) / row_stride) / ne;
+    v = ((mask >> src) & 1u) ? GSA_FLAG_PUBLISHED : 0u;
+  }
+  pads[i] = v;
+}
+
+}  // namespace
+
+size_t moe_lds_bytes(int C) {
+  return (size_t)16 * (C + 1) * 16 + (size_t)(kWaves * 256 + 256) * sizeof(float);
+}
+
+hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
+  const size_t lds = moe_lds_bytes(a.C);
+  if (lds > 65536) {
+    // Opt in to the largest dynamic LDS this kernel may use (cheap, idempotent).
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_gemm_a2a),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)moe_lds_bytes(GSA_MOE_MAX_F / 8));
+    if (e != hipSuccess) return e;
+  }
+  const unsigned grid = (unsigned)(a.ne * a.tiles);
+  hipLaunchKernelGGL(moe_gemm_a2a, dim3(grid), dim3(kWaves * 64), lds, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_a2a_reset(uint32_t* pads, int W, int ne, int row_stride, int64_t pad_words,
+                            uint32_t published_mask, hipStream_t s) {
+  const int64_t total = (int64_t)W * pad_words;
+  const unsigned block = 256;
+  const unsigned grid = (unsigned)((total + block - 1) / block);
+  hipLaunchKernelGGL(a2a_reset_kernel, dim3(grid), dim3(block), 0, s, pads, ne, row_stride,
+                     pad_words, total, published_mask);
+  return hipGetLastError();
+}
+
+}  // namespace gsa

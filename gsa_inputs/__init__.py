@@ -165,7 +165,18 @@ def moe_routing(W, ne, T, top_k, capacity, seed=0, cfg_id=0):
 
 
 def make_moe_inputs(cfg, seed=0, rank=0, gap=0):
-    """One rank's inputs for a MoE workload (see MOE_CONFIGS).
+    """One rank's inputs for a MoE workload (see MOE_CONFIGS): the seeded
+    routing of moe_routing, then make_moe_from_counts."""
+    c = MOE_CONFIGS[cfg] if isinstance(cfg, str) else cfg
+    counts = moe_routing(c["W"], c["ne"], c["T"], c["top_k"], c["capacity"], seed, c["cfg_id"])
+    return make_moe_from_counts(counts, c["ne"], c["H"], c["F"], c["sigma"], seed, c["cfg_id"],
+                                rank, gap, rows_out=c["T"] * c["top_k"])
+
+
+def make_moe_from_counts(counts, ne, H, F, sigma=0.02, seed=0, cfg_id=0, rank=0, gap=0,
+                         rows_out=None):
+    """One rank's inputs given counts[s][g] (tokens of rank s accepted by
+    global expert g, W x W*ne).
 
     Returns a dict with
       X        uint16 rows_in x F   dispatched token rows (bf16 bits), laid
@@ -181,9 +192,8 @@ def make_moe_inputs(cfg, seed=0, rank=0, gap=0):
                the call: rows of other ranks' experts ~ N(0, 1) (as if their
                owners had pushed them), this rank's rows NaN sentinel
     """
-    c = MOE_CONFIGS[cfg] if isinstance(cfg, str) else cfg
-    W, ne, H, F = c["W"], c["ne"], c["H"], c["F"]
-    counts = moe_routing(W, ne, c["T"], c["top_k"], c["capacity"], seed, c["cfg_id"])
+    counts = np.asarray(counts, np.int64)
+    W = counts.shape[0]
     length = np.zeros((ne, W), np.int32)
     in_off = np.zeros((ne, W), np.int32)
     dst_off = np.zeros((W, ne), np.int32)
@@ -194,15 +204,16 @@ def make_moe_inputs(cfg, seed=0, rank=0, gap=0):
             in_off[e, s] = row
             row += int(length[e, s]) + gap
     rows_in = max(row, 1)
-    rows_out = c["T"] * c["top_k"]
+    if rows_out is None:
+        rows_out = max(1, int(counts.sum(axis=1).max()))
     for s in range(W):
         before = np.concatenate([[0], np.cumsum(counts[s])])
         for e in range(ne):
             dst_off[s, e] = before[rank * ne + e]
-    ss = np.random.SeedSequence([int(seed), int(c["cfg_id"]), int(rank), 8])
+    ss = np.random.SeedSequence([int(seed), int(cfg_id), int(rank), 8])
     gw, gx, gb = [np.random.Generator(np.random.PCG64(s)) for s in ss.spawn(3)]
     w32 = gw.standard_normal(size=(ne, H, F), dtype=np.float32)
-    w32 *= np.float32(c["sigma"])
+    w32 *= np.float32(sigma)
     Wd = bf16_bits(w32)
     del w32
     X = bf16_bits(gx.standard_normal(size=(rows_in, F), dtype=np.float32))

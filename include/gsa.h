@@ -52,6 +52,9 @@ extern "C" {
 #define GSA_ESTATE   (-5)  /* the caller's own flag row was marked published
                               for every call, or its epoch is exhausted
                               (asynchronous)                               */
+#define GSA_ESPLIT   (-6)  /* a split or offset read on the device was out of
+                              range, or an expert got more tokens than
+                              GSA_MOE_MAX_TOKENS (asynchronous)            */
 
 /* Flag value of a simulated peer: "published for every epoch". */
 #define GSA_FLAG_PUBLISHED 0xFFFFFFFFu
@@ -209,6 +212,99 @@ int gsa_set_wait_timeout_us(uint32_t us);
 
 /* Static text for a GSA_* code. */
 const char *gsa_strerror(int code);
+
+/* ------------------------------------------------------------------------
+ * Mixture of experts: an expert's down-projection GEMM fused with the
+ * combine all-to-all, at one rank's share.
+ *
+ * The fused-operators page names GEMM + All-to-All for mixture-of-experts
+ * models beside GEMV + AllReduce; the symmetric-memory documentation's op
+ * reference (all_to_all_vdev_2d, all_to_all_vdev_2d_offset) fixes the data
+ * movement: the dispatch leaves each rank's tokens expert-major (for local
+ * expert e, the segments of source ranks 0..W-1), splits and offsets live on
+ * the device, and the combine sends every segment back to its source rank at
+ * an offset that rank chose.  Here rank `rank` holds ne experts (global
+ * expert rank * ne + e); for each local expert e and each 16-feature tile t
+ * one workgroup multiplies the expert's dispatched rows by the tile's 16
+ * weight rows (bf16 in, fp32 accumulation), stores each result row straight
+ * into its source rank's combine buffer, raises flag (rank, e, t) in that
+ * rank's signal pad, and then waits (bounded) for flag (p, e, t) of every
+ * other rank p in its own pad: when the call's work has finished, this
+ * rank's combine buffer holds every expert's rows for its tokens.
+ *
+ * On one GPU the W combine buffers and W pads of a gsa_a2a allocation stand
+ * for the W ranks' symmetric buffers: this rank writes its rows into all of
+ * them, and the other ranks' rows in its own buffer are filled by the
+ * caller, their flags marked published by gsa_a2a_reset.
+ * ---------------------------------------------------------------------- */
+
+/* Tokens one local expert may take per call (its capacity). */
+#define GSA_MOE_MAX_TOKENS 16
+/* Largest input width F of the expert GEMM (the dispatched rows of one
+ * expert are staged in LDS). */
+#define GSA_MOE_MAX_F 4088
+
+typedef struct gsa_a2a gsa_a2a;
+
+/* Words of one signal pad: GSA_PAD_HEADER_WORDS status words, then W * ne
+ * flag rows of gsa_signal_pad_row_stride(H) words; row p * ne + e holds the
+ * flags of source rank p's local expert e, one per 16-feature tile.  -1 on a
+ * bad argument. */
+int64_t gsa_a2a_pad_words(int W, int ne, int64_t H);
+
+/* Allocate (zeroed, host-blocking, init time) W combine buffers of
+ * rows_out x H fp32 (rank s's buffer at s * rows_out * H, row-major) and W
+ * signal pads.  1 <= W <= GSA_MAX_W, 1 <= ne <= 256, H >= 1,
+ * 1 <= rows_out, W * rows_out * H < 2^40.  *out [host] := the handle.
+ * Errors: GSA_EINVAL, GSA_ENOMEM, GSA_EHIP. */
+int gsa_a2a_alloc(int W, int ne, int64_t H, int64_t rows_out, gsa_a2a **out);
+/* Free a handle (synchronizes its device first).  NULL is a no-op. */
+int gsa_a2a_free(gsa_a2a *h);
+/* [device] the W combine buffers, or NULL for an unknown handle. */
+float *gsa_a2a_buffers(const gsa_a2a *h);
+/* [device] the W signal pads (pad s at s * gsa_a2a_pad_words(W, ne, H)). */
+uint32_t *gsa_a2a_signal_pads(const gsa_a2a *h);
+
+/* Reset every pad of the allocation on `stream`: status words cleared; flag
+ * row p * ne + e := GSA_FLAG_PUBLISHED if bit p of published_mask is set,
+ * else 0.  Errors: GSA_EINVAL (unknown pads or mismatched sizes), GSA_EHIP. */
+int gsa_a2a_reset(uint32_t *pads, int W, int ne, int64_t H, uint32_t published_mask,
+                  void *stream);
+
+/* One call of rank `rank` (asynchronous on `stream`, one kernel, no
+ * allocation, no host sync):
+ *   X      [device] bf16 bits, rows_in x F: the dispatched rows
+ *   Wd     [device] bf16 bits, ne x H x F: expert e's weight, H output
+ *          features of F inputs, row-major
+ *   splits [device] int32, 2 x ne x W: splits[e * W + s] = rows of source
+ *          rank s for local expert e, splits[ne * W + e * W + s] = the first
+ *          of them in X (gaps between segments are allowed)
+ *   dst_off [device] int32, W x ne: dst_off[s * ne + e] = the first row of
+ *          that segment in rank s's combine buffer
+ *   bufs, pads: gsa_a2a_buffers / gsa_a2a_signal_pads of one allocation of
+ *          (W, ne, H, rows_out)
+ * Row i of segment (e, s) of the result, sum_k X[row][k] * Wd[e][n][k] in
+ * fp32, goes to row dst_off[s * ne + e] + i of buffer s.  Each local expert
+ * may take at most GSA_MOE_MAX_TOKENS rows per call; experts with none skip
+ * their weights.  Host-checked: sizes (F % 8 == 0, F <= GSA_MOE_MAX_F,
+ * H * F * 2 < 2^31), 16-byte alignment of X, Wd, bufs, pads, 4-byte
+ * alignment of splits and dst_off.  Device-checked: every split and offset
+ * (a bad table sets GSA_ESPLIT for that expert, which then writes nothing
+ * and raises no flag).  Flags carry epochs like gsa_gemv_allreduce (own row
+ * of the own pad + 1).  Errors: GSA_EINVAL, GSA_EHIP; GSA_ETIMEOUT,
+ * GSA_ESTATE and GSA_ESPLIT later through gsa_a2a_status. */
+int gsa_moe_gemm_all_to_all(const uint16_t *X, const uint16_t *Wd, const int32_t *splits,
+                            const int32_t *dst_off, float *bufs, uint32_t *pads, int W,
+                            int rank, int ne, int64_t H, int64_t F, int64_t rows_in,
+                            int64_t rows_out, void *stream);
+
+/* Status of rank `rank`'s pad after the work queued on `stream` (synchronizes
+ * it): *code := GSA_ESPLIT (then *tile := the smallest bad local expert),
+ * else GSA_ESTATE (*tile := smallest e * tiles + t with an unusable own
+ * row), else GSA_ETIMEOUT (*tile, *peer := smallest expired (e * tiles + t,
+ * peer)), else GSA_OK (*tile = *peer = -1).  Errors: GSA_EINVAL, GSA_EHIP. */
+int gsa_a2a_status(const uint32_t *pads, int rank, void *stream, int *code, int64_t *tile,
+                   int *peer);
 
 #ifdef __cplusplus
 }

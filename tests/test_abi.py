@@ -36,8 +36,8 @@ def test_library_exports_every_declared_symbol():
 def test_constants_match_header():
     text = header_text()
     for name in ["GSA_OK", "GSA_EINVAL", "GSA_ENOMEM", "GSA_EHIP", "GSA_ETIMEOUT",
-                 "GSA_ESTATE", "GSA_FLAG_TILE_ROWS", "GSA_PAD_HEADER_WORDS", "GSA_MAX_W",
-                 "GSA_MAX_B"]:
+                 "GSA_ESTATE", "GSA_ESPLIT", "GSA_FLAG_TILE_ROWS", "GSA_PAD_HEADER_WORDS",
+                 "GSA_MAX_W", "GSA_MAX_B", "GSA_MOE_MAX_TOKENS", "GSA_MOE_MAX_F"]:
         m = re.search(rf"#define\s+{name}\s+\(?\s*(-?\d+)\s*\)?", text)
         assert m, name
         assert int(m.group(1)) == getattr(_lib, name), name
@@ -48,7 +48,7 @@ def test_constants_match_header():
 
 
 def test_strerror_covers_codes():
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         assert gsa.gsa_strerror(code) != "unknown error"
     assert gsa.gsa_strerror(7) == "unknown error"
 
@@ -127,6 +127,43 @@ def test_two_shot_entry_point_rejects_bad_arguments():
         assert L.gsa_gemv_allreduce_two_shot(A, x, slots, pad, P, out, *bad, None) == (
             gsa.GSA_EINVAL), bad
     assert L.gsa_symm_gathered(ctypes.c_void_p(P)) is None
+
+
+def test_moe_entry_points_reject_bad_arguments():
+    L = _lib.lib()
+    assert L.gsa_a2a_pad_words(0, 1, 16) == -1
+    assert L.gsa_a2a_pad_words(2, 0, 16) == -1
+    assert L.gsa_a2a_pad_words(2, 1, 0) == -1
+    assert L.gsa_a2a_pad_words(2, 3, 100) == gsa.GSA_PAD_HEADER_WORDS + 2 * 3 * 64
+    h = ctypes.c_void_p()
+    assert L.gsa_a2a_alloc(0, 1, 16, 4, ctypes.byref(h)) == gsa.GSA_EINVAL
+    assert L.gsa_a2a_alloc(2, 257, 16, 4, ctypes.byref(h)) == gsa.GSA_EINVAL
+    assert L.gsa_a2a_alloc(2, 1, 16, 0, ctypes.byref(h)) == gsa.GSA_EINVAL
+    assert L.gsa_a2a_alloc(2, 1, 16, 4, None) == gsa.GSA_EINVAL
+    assert L.gsa_a2a_free(ctypes.c_void_p(P)) == gsa.GSA_EINVAL
+    assert L.gsa_a2a_buffers(ctypes.c_void_p(P)) is None
+    assert L.gsa_a2a_signal_pads(ctypes.c_void_p(P)) is None
+    assert L.gsa_a2a_reset(P, 2, 1, 16, 0, None) == gsa.GSA_EINVAL  # unknown pads
+    c, t, p = ctypes.c_int(), ctypes.c_int64(), ctypes.c_int()
+    assert L.gsa_a2a_status(P, 0, None, ctypes.byref(c), ctypes.byref(t),
+                            ctypes.byref(p)) == gsa.GSA_EINVAL
+    # (X, Wd, splits, dst_off, bufs, pads, W, rank, ne, H, F, rows_in, rows_out)
+    good = [P, P, P, P, P, P, 2, 0, 2, 64, 128, 8, 8]
+    bad_cases = [
+        (6, 0), (6, 9), (7, 2), (7, -1), (8, 0), (8, 257),   # W, rank, ne
+        (9, 0), (10, 0), (10, 12), (10, 4096), (11, 0), (12, 0),  # H, F, rows_in, rows_out
+        (0, 0), (1, 0), (2, 0), (3, 0), (4, 0), (5, 0),      # null pointers
+        (0, P + 8), (1, P + 4), (4, P + 4), (5, P + 8), (2, P + 2), (3, P + 1),  # alignment
+    ]
+    for i, v in bad_cases:
+        args = list(good)
+        args[i] = v
+        assert L.gsa_moe_gemm_all_to_all(*args, None) == gsa.GSA_EINVAL, (i, v)
+    big = list(good)
+    big[9], big[10] = 1 << 20, 1024  # H * F * 2 = 2^31: one expert past a buffer resource
+    assert L.gsa_moe_gemm_all_to_all(*big, None) == gsa.GSA_EINVAL
+    # every argument valid but the pads are not from gsa_a2a_alloc
+    assert L.gsa_moe_gemm_all_to_all(*good, None) == gsa.GSA_EINVAL
 
 
 def test_other_entry_points_reject_bad_arguments():
