@@ -15,7 +15,10 @@ streaming-read kernel achieves over 1 GiB on the same GPU.  The CPU oracle
 is timed on a bounded sample of the same workload, on one thread and on all
 host cores (whole calls in parallel threads).
 
-Prints one JSON line (rank 0, N = 1).
+`--config m0|m1|m2` (or `--all-moe`) times the mixture-of-experts GEMM fused
+with the combine all-to-all instead, on the same principles.
+
+Prints one JSON line per workload (rank 0, N = 1).
 """
 import argparse
 import hashlib
@@ -36,6 +39,8 @@ METRIC = "µs per gemv_allreduce call and achieved HBM GB/s (% of peak), 1 MI355
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_CONFIG = "c2"  # Llama-3-8B o_proj decode, W=8 N=4096 K=4096 B=1
 KERNEL_SOURCE = os.path.join(ROOT, "gemv_shot_all_amd", "csrc", "gemv_allreduce.hip")
+MOE_KERNEL_SOURCE = os.path.join(ROOT, "gemv_shot_all_amd", "csrc", "moe_a2a.hip")
+MOE_METRIC = "µs per MoE GEMM + combine all-to-all call and achieved HBM GB/s (% of peak), 1 MI355X"
 
 
 def two_shot_chunk_rows(N, W):
@@ -64,8 +69,8 @@ def alg_flops(W, N, K, B):
     return 2 * N * Ks * B + (W - 1) * N * B
 
 
-def kernel_source_digest():
-    with open(KERNEL_SOURCE, "rb") as f:
+def kernel_source_digest(path=KERNEL_SOURCE):
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
@@ -75,16 +80,17 @@ def profile_name(cfg, epilogue=False, two_shot=False):
     return f"gemv_allreduce{variant}_{cfg}"
 
 
-def traffic_from_profile(cfg, epilogue=False, two_shot=False):
+def traffic_from_profile(cfg, epilogue=False, two_shot=False, name=None, source=KERNEL_SOURCE):
     """HBM bytes per launch from the committed PMC summary for this workload,
     or None if there is none or the kernel source changed since."""
-    path = os.path.join(ROOT, "profiles", profile_name(cfg, epilogue, two_shot) + "_pmc.md")
+    name = name or profile_name(cfg, epilogue, two_shot)
+    path = os.path.join(ROOT, "profiles", name + "_pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_sha or not m_b or m_sha.group(1) != kernel_source_digest():
+    if not m_sha or not m_b or m_sha.group(1) != kernel_source_digest(source):
         return None
     return float(m_b.group(1))
 
@@ -412,13 +418,205 @@ def run_config(cfg, args):
     return line
 
 
+def moe_alg_bytes(d):
+    """Bytes the MoE call must move: the weights of every local expert that
+    has tokens (2 H F each), its dispatched rows (2 F per token) and the
+    result rows pushed to the combine buffers (4 H per token); split tables
+    and flags excluded."""
+    M = d["length"].sum(axis=1)
+    H, F = d["H"], d["F"]
+    return int((M > 0).sum()) * 2 * H * F + int(M.sum()) * (2 * F + 4 * H)
+
+
+class MoeSets:
+    """R independent MoE input sets on the device, each with its own combine
+    buffers and pads (peers published)."""
+
+    def __init__(self, d, rotate_bytes, max_sets=None):
+        import torch
+
+        import gemv_shot_all_amd as gsa
+        self.gsa, self.d = gsa, d
+        foot = d["Wd"].nbytes + d["X"].nbytes + d["bufs"].nbytes
+        R = max(1, -(-rotate_bytes // foot))
+        if max_sets:
+            R = min(R, max_sets)
+        self.R = R
+        Wd0 = torch.from_numpy(d["Wd"].view(np.int16)).cuda()
+        X0 = torch.from_numpy(d["X"].view(np.int16)).cuda()
+        b0 = torch.from_numpy(d["bufs"]).cuda()
+        splits = torch.from_numpy(np.concatenate([d["length"].ravel(),
+                                                  d["in_off"].ravel()]).astype(np.int32)).cuda()
+        dst = torch.from_numpy(d["dst_off"].astype(np.int32).ravel()).cuda()
+        W, rank = d["W"], d["rank"]
+        mask = ((1 << W) - 1) & ~(1 << rank)
+        self.Wd, self.X, self.splits, self.dst, self.bufs = [], [], [], [], []
+        for _ in range(R):
+            self.Wd.append(Wd0.clone())
+            self.X.append(X0.clone())
+            self.splits.append(splits.clone())
+            self.dst.append(dst.clone())
+            buf = gsa.A2ABuffer(W, d["ne"], d["H"], d["rows_out"])
+            buf.bufs_view().copy_(b0)
+            buf.reset(mask)
+            self.bufs.append(buf)
+        del Wd0
+        torch.cuda.synchronize()
+
+    def call(self, i):
+        j = i % self.R
+        d, b = self.d, self.bufs[j]
+        self.gsa.gsa_moe_gemm_all_to_all(self.X[j], self.Wd[j], self.splits[j], self.dst[j],
+                                         b.bufs, b.pads, d["W"], d["rank"], d["ne"], d["H"],
+                                         d["F"], d["rows_in"], d["rows_out"])
+
+    def check_consistency(self):
+        """Every set's combine buffers bit-identical to set 0's, finite where
+        the combine writes; every set's status OK."""
+        out0 = self.bufs[0].bufs_view().cpu().numpy()
+        ok = bool(np.all(np.isfinite(out0)))
+        for j in range(self.R):
+            ok = ok and self.bufs[j].status(self.d["rank"]) == (0, -1, -1)
+        for j in range(1, self.R, max(1, self.R // 8)):
+            ok = ok and np.array_equal(self.bufs[j].bufs_view().cpu().numpy().view(np.uint32),
+                                       out0.view(np.uint32))
+        return ok
+
+    def close(self):
+        for b in self.bufs:
+            b.close()
+
+
+def time_cpu_oracle_moe(d, seconds, threads=1):
+    """The oracle's moe_combine on whole calls, as time_cpu_oracle."""
+    import threading
+
+    import oracle
+    o = oracle.load()
+
+    def one_call():
+        o.moe_combine(d["X"], d["Wd"], d["length"], d["in_off"], d["dst_off"], d["W"],
+                      d["rows_out"])
+    t0 = time.perf_counter()
+    one_call()
+    one = time.perf_counter() - t0
+    n = max(1, int(seconds / max(one, 1e-6)))
+
+    def work():
+        for _ in range(n):
+            one_call()
+    ts = [threading.Thread(target=work) for _ in range(threads)]
+    t0 = time.perf_counter()
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    el = time.perf_counter() - t0
+    return 1e6 * el / (n * threads), n * threads
+
+
+def run_moe_config(cfg, args):
+    import torch
+
+    d = gi.make_moe_inputs(cfg, seed=args.seed, rank=0)
+    sets = MoeSets(d, args.rotate_mib << 20 if not args.warm else 1, args.max_sets)
+    try:
+        for i in range(max(args.warmup, sets.R)):
+            sets.call(i)
+        torch.cuda.synchronize()
+        consistent = sets.check_consistency()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(args.steps):
+                    sets.call(i)
+        g.replay()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall_us = 1e6 * (time.perf_counter() - t0) / args.steps
+        us_per_call = 1e3 * ev0.elapsed_time(ev1) / args.steps
+        consistent = consistent and sets.check_consistency()
+        del g
+    finally:
+        R = sets.R
+        sets.close()
+    nbytes = moe_alg_bytes(d)
+    achieved = nbytes / (us_per_call * 1e-6) / 1e9
+    name = f"moe_gemm_all_to_all_{cfg}"
+    c = gi.MOE_CONFIGS[cfg]
+    M = d["length"].sum(axis=1)
+    line = {
+        "metric": MOE_METRIC,
+        "value": round(us_per_call, 4),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us_per_call / 1e3, 7),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": c["name"], "id": cfg, "W": d["W"], "rank": 0, "ne": d["ne"],
+            "H": d["H"], "F": d["F"], "top_k": c["top_k"], "tokens_per_rank": c["T"],
+            "tokens_received": int(M.sum()), "experts_with_tokens": int((M > 0).sum()),
+            "accumulate": "f32", "out": "f32",
+            "inputs": "cold: rotated over %d resident sets" % R if not args.warm
+                      else "warm: one set (Infinity-Cache resident, not HBM)",
+            "timing": "hipGraph replay of K calls between two device syncs",
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic_from_profile(cfg, name=name, source=MOE_KERNEL_SOURCE),
+            "alg_bytes_per_launch": nbytes,
+            "launch_us_mean": round(us_per_call, 4),
+        },
+        "extra": {
+            "wall_us_per_call": round(wall_us, 4),
+            "sets_consistent": consistent,
+            "alg_flops_per_call": int(2 * d["H"] * d["F"] * M.sum()),
+        },
+    }
+    if args.cpu_seconds > 0:
+        threads = host_threads()
+        st_us, st_calls = time_cpu_oracle_moe(d, args.cpu_seconds / 2, threads=1)
+        mt_us, mt_calls = time_cpu_oracle_moe(d, args.cpu_seconds / 2, threads=threads)
+        line["cpu_baseline"] = {
+            "value": round(mt_us, 2), "unit": "us/call", "cores": threads, "kind": "oracle",
+            "sample": f"{mt_calls} whole calls of the {cfg} workload (fp64) on {threads} "
+                      f"threads in parallel, wall time per call; host: {os.cpu_count()} "
+                      f"logical CPUs, {cpu_model()}",
+            "single_thread_us_per_call": round(st_us, 2),
+            "single_thread_calls": st_calls,
+        }
+    else:
+        line["cpu_baseline"] = None
+    return line
+
+
 def main():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=200)
-    p.add_argument("--config", default=DEFAULT_CONFIG, choices=sorted(gi.CONFIGS))
+    p.add_argument("--config", default=DEFAULT_CONFIG,
+                   choices=sorted(gi.CONFIGS) + sorted(gi.MOE_CONFIGS),
+                   help="a GEMV + AllReduce workload, or m0/m1/m2 for the MoE GEMM + "
+                        "combine all-to-all")
     p.add_argument("--all", action="store_true", help="one line per workload")
+    p.add_argument("--all-moe", action="store_true", help="one line per MoE workload")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--rotate-mib", type=int, default=1024,
                    help="total size of the rotated input sets (MiB)")
@@ -460,9 +658,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     probe = hbm_read_probe() if not args.no_probe else None
-    cfgs = list(gi.CONFIGS) if args.all else [args.config]
+    cfgs = list(gi.CONFIGS) if args.all else [] if args.all_moe else [args.config]
+    if args.all_moe:
+        cfgs += list(gi.MOE_CONFIGS)
     for cfg in cfgs:
-        line = run_config(cfg, args)
+        line = run_moe_config(cfg, args) if cfg in gi.MOE_CONFIGS else run_config(cfg, args)
         line["extra"]["hbm_read_probe_GBps"] = probe
         print(json.dumps(line), flush=True)
 
