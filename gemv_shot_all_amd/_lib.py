@@ -411,3 +411,9 @@ class A2ABuffer:
         if self.handle:
             gsa_a2a_free(self.handle)
             self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
