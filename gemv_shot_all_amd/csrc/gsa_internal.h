@@ -111,7 +111,6 @@ struct MoeArgs {
   int64_t H, F, rows_in, rows_out, pad_words;
   uint64_t timeout_ticks;
 };
-size_t moe_lds_bytes(int C);
 hipError_t launch_moe(const MoeArgs& a, hipStream_t s);
 hipError_t launch_a2a_reset(uint32_t* pads, int W, int ne, int row_stride, int64_t pad_words,
                             uint32_t published_mask, hipStream_t s);

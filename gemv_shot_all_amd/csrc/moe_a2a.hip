@@ -1,20 +1,20 @@
 // moe_a2a.hip -- a mixture-of-experts down-projection fused with the combine
 // all-to-all, at one rank's share, for gfx950.
 //
-// Rank `rank` holds ne experts.  Workgroup (e, t) owns local expert e and
-// output features [16 t, 16 t + 16).  Inside one launch it
+// Rank `rank` holds ne experts.  A workgroup owns local expert e and TPW
+// consecutive 16-feature tiles t0 .. t0 + TPW - 1.  Inside one launch it
 //   a. reads the expert's split table (one segment per source rank), checks
 //      it, and lays out its M <= 16 tokens: token j's row in X and the row
 //      of its source rank's combine buffer that receives it;
 //   b. copies the tokens' rows of X into LDS (each compute wave its own
-//      k-slice, straight from memory with LDS DMA) and streams the tile's 16
-//      weight rows with v_mfma_f32_16x16x32_bf16 (weights as the A operand,
-//      tokens as the B operand, fp32 accumulation), the waves' partials
-//      summed in wave order;
-//   c. stores each token's 16 results into its source rank's combine buffer,
-//      waits for the stores, raises flag (rank, e, t) in every rank's pad,
-//      and waits (bounded) for flag (p, e, t) of every other rank p in its
-//      own pad.
+//      k-slice, straight from memory with LDS DMA) and streams each tile's
+//      16 weight rows with v_mfma_f32_16x16x32_bf16 (weights as the A
+//      operand, tokens as the B operand, fp32 accumulation), the waves'
+//      partials summed in wave order;
+//   c. stores each token's results into its source rank's combine buffer,
+//      waits for the stores, raises flag (rank, e, t) of each tile in every
+//      rank's pad, and waits (bounded) for flag (p, e, t) of every other
+//      rank p in its own pad.
 //
 // Sources (restated): a GEMM fused with an All-to-All for mixture-of-
 // experts models, each workgroup handing its finished results to the
@@ -39,7 +39,6 @@ namespace {
 
 constexpr int kTok = GSA_MOE_MAX_TOKENS;  // the MFMA B operand's 16 columns
 constexpr int kWaves = 4;                 // compute waves per workgroup
-constexpr int kRing = 8;                  // weight steps in flight per lane
 static_assert(kTok == 16, "one 16 x 16 x 32 MFMA tile of tokens");
 
 __device__ __forceinline__ uint32_t* moe_flag(const MoeArgs& a, int pad, int src, int e, int t) {
@@ -47,22 +46,28 @@ __device__ __forceinline__ uint32_t* moe_flag(const MoeArgs& a, int pad, int src
          (int64_t)(src * a.ne + e) * a.row_stride + t;
 }
 
-// Every other rank's flag (p, e, t) in the own pad >= epoch, bounded by the
-// timeout; on expiry the smallest missing rank is recorded (wave 0 only).
-__device__ void moe_wait_peers(const MoeArgs& a, int lane, int e, int t, uint32_t epoch) {
+// Every other rank's flag (p, e, t0 + q) in the own pad >= the tile's epoch
+// for the nt tiles of a workgroup (lane 8 q + p), bounded by the timeout; on
+// expiry the smallest missing (tile, rank) is recorded (wave 0 only).
+__device__ void moe_wait_peers(const MoeArgs& a, int lane, int e, int t0, int nt,
+                               const uint32_t* epochs) {
   uint32_t* own_pad = a.pads + (int64_t)a.rank * a.pad_words;
   const uint64_t start = wall_clock64();
+  const int q = min(lane >> 3, nt - 1);   // lane 8 q + p: tile t0 + q, peer p
+  const int p = min(lane & 7, a.W - 1);
+  const int t = t0 + q;
+  const uint32_t epoch = epochs[q];
   for (;;) {
-    const uint32_t f = __hip_atomic_load(moe_flag(a, a.rank, min(lane, a.W - 1), e, t),
+    const uint32_t f = __hip_atomic_load(moe_flag(a, a.rank, p, e, t),
                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool lane_ok = lane >= a.W || lane == a.rank || f >= epoch;
+    const bool lane_ok = (lane >> 3) >= nt || (lane & 7) >= a.W || p == a.rank || f >= epoch;
     const uint64_t missing = __ballot(!lane_ok);
     if (missing == 0) return;
     if (wall_clock64() - start > a.timeout_ticks) {
       if (lane == 0) {
-        const uint32_t peer = (uint32_t)(__ffsll((long long)missing) - 1);
+        const uint32_t bit = (uint32_t)(__ffsll((long long)missing) - 1);
         atomicOr(own_pad + kHdrErrorBits, kErrTimeout);
-        atomicMin(own_pad + kHdrTimeoutKey, (uint32_t)(e * a.tiles + t) * 8u + peer);
+        atomicMin(own_pad + kHdrTimeoutKey, (uint32_t)(e * a.tiles + t0 + (int)(bit >> 3)) * 8u + (bit & 7u));
       }
       return;
     }
@@ -71,22 +76,28 @@ __device__ void moe_wait_peers(const MoeArgs& a, int lane, int e, int t, uint32_
 }
 
 // LDS (dynamic): x [16][C + 1] chunks (column C and rows >= M zero), the
-// waves' 16 x 16 partials, the results token-major [16][16].
+// waves' 16 x (16 TPW) partials, the results token-major [16][16 TPW].
+// TPW: 16-feature tiles per workgroup (each x chunk read from LDS serves TPW
+// MFMAs); RING: weight steps in flight per lane.
+template <int TPW, int RING>
 __global__ __launch_bounds__(kWaves * 64) void moe_gemm_a2a(MoeArgs a) {
   extern __shared__ uint4 lds[];
   __shared__ int64_t s_xrow[kTok];  // token j: its row of X
   __shared__ int64_t s_dst[kTok];   // token j: first element of its combine row
-  __shared__ uint32_t s_ctl[4];     // epoch, ok, M
+  __shared__ uint32_t s_ctl[4];     // -, ok, M
+  __shared__ uint32_t s_ep[TPW];    // epoch of each tile
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int e = (int)(blockIdx.x / (unsigned)a.tiles);
-  const int t = (int)(blockIdx.x % (unsigned)a.tiles);
+  const int groups = (a.tiles + TPW - 1) / TPW;
+  const int e = (int)(blockIdx.x / (unsigned)groups);
+  const int t0 = (int)(blockIdx.x % (unsigned)groups) * TPW;
+  const int nt = min(TPW, a.tiles - t0);
   const int C = a.C;
   const int CP = C + 1;  // padded LDS row: the 16 token rows of one chunk hit distinct banks
   float* red = reinterpret_cast<float*>(lds + 16 * CP);
-  float* yt = red + kWaves * 256;
+  float* yt = red + kWaves * 256 * TPW;
   uint32_t* own_pad = a.pads + (int64_t)a.rank * a.pad_words;
 
   if (wave == 0) {
@@ -105,15 +116,18 @@ __global__ __launch_bounds__(kWaves * 64) void moe_gemm_a2a(MoeArgs a) {
       M += lr;
     }
     const bool splits_ok = __ballot(bad) == 0 && M <= kTok;
-    const uint32_t own = __hip_atomic_load(moe_flag(a, a.rank, a.rank, e, t), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-    const bool own_ok = own < GSA_FLAG_PUBLISHED - 1u;  // not marked published, not exhausted
+    const uint32_t own = __hip_atomic_load(moe_flag(a, a.rank, a.rank, e, t0 + min(lane, nt - 1)),
+                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // tiles whose own flag row is marked published or has its epochs exhausted
+    const uint64_t own_bad = __ballot(lane < nt && own >= GSA_FLAG_PUBLISHED - 1u);
+    const bool own_ok = own_bad == 0;
     if (splits_ok && own_ok && lane < a.W) {
       for (int i = 0; i < mine; ++i) {
         s_xrow[before + i] = ioff + i;
         s_dst[before + i] = ((int64_t)lane * a.rows_out + doff + i) * a.H;
       }
     }
+    if (lane < nt) s_ep[lane] = own + 1u;
     if (lane == 0) {
       if (!splits_ok) {
         atomicOr(own_pad + kHdrErrorBits, kErrSplit);
@@ -121,9 +135,9 @@ __global__ __launch_bounds__(kWaves * 64) void moe_gemm_a2a(MoeArgs a) {
       }
       if (!own_ok) {
         atomicOr(own_pad + kHdrErrorBits, kErrState);
-        atomicMin(own_pad + kHdrStateTile, (uint32_t)(e * a.tiles + t));
+        atomicMin(own_pad + kHdrStateTile,
+                  (uint32_t)(e * a.tiles + t0 + __ffsll((long long)own_bad) - 1));
       }
-      s_ctl[0] = own + 1u;
       s_ctl[1] = (splits_ok && own_ok) ? 1u : 0u;
       s_ctl[2] = (uint32_t)M;
     }
@@ -150,70 +164,82 @@ __global__ __launch_bounds__(kWaves * 64) void moe_gemm_a2a(MoeArgs a) {
     const uint16_t* w_e = a.Wd + (int64_t)e * a.H * a.F;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(w_e, (uint32_t)(a.H * a.F * 2));
     const int kq = lane >> 4;
-    const uint32_t a_row = ((uint32_t)(t * 16 + (lane & 15)) * (uint32_t)C + kq) * 16u;
+    const uint32_t a_row = ((uint32_t)(t0 * 16 + (lane & 15)) * (uint32_t)C + kq) * 16u;
+    const uint32_t tile_bytes = 16u * (uint32_t)C * 16u;
     const uint32_t kOutOfRange = 0x80000000u;  // past any weight: reads zeros
-    // Weight chunk of the wave's step j; steps past n_steps (and rows past H)
-    // read zeros.  Every load is issued unconditionally, so the
-    // outstanding-load counts are static.
-    auto a_off = [&](int j) {
-      return j < n_steps ? a_row + (uint32_t)(s_begin + j) * 64u : kOutOfRange;
+    auto a_off = [&](int j, int q) {
+      return j < n_steps ? a_row + (uint32_t)q * tile_bytes + (uint32_t)(s_begin + j) * 64u : kOutOfRange;
     };
-    uint4 ring[kRing];
+    uint4 ring[RING][TPW];
 #pragma unroll
-    for (int u = 0; u < kRing; ++u) ring[u] = buf_load16(ra, a_off(u));
-    // The x copies went out before the ring loads: once at most kRing loads
+    for (int u = 0; u < RING; ++u)
+#pragma unroll
+      for (int q = 0; q < TPW; ++q) ring[u][q] = buf_load16(ra, a_off(u, q));
+    // The x copies went out before the ring loads: once at most RING loads
     // are outstanding they have landed.
-    wait_vm_le<kRing>();
+    wait_vm_le<RING * TPW>();
     for (int c = c_begin + lane; c < c_end; c += 64)
       for (int j = M; j < kTok; ++j) lds[j * CP + c] = make_uint4(0u, 0u, 0u, 0u);
     if (lane < kTok) lds[lane * CP + C] = make_uint4(0u, 0u, 0u, 0u);
 
     const int xrow = (lane & 15) * CP;
-    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int j0 = 0; j0 < n_steps; j0 += kRing) {
-      uint4 xv[kRing];
+    f32x4_t acc[TPW];
 #pragma unroll
-      for (int u = 0; u < kRing; ++u) {
+    for (int q = 0; q < TPW; ++q) acc[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j0 = 0; j0 < n_steps; j0 += RING) {
+      uint4 xv[RING];
+#pragma unroll
+      for (int u = 0; u < RING; ++u) {
         const int j = j0 + u;
         const int chunk = 4 * (s_begin + j) + kq;
         xv[u] = lds[xrow + (j < n_steps && chunk < C ? chunk : C)];
       }
 #pragma unroll
-      for (int u = 0; u < kRing; ++u) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ring[u]),
-                                                      __builtin_bit_cast(bf16x8_t, xv[u]), acc, 0,
-                                                      0, 0);
-        ring[u] = buf_load16(ra, a_off(j0 + u + kRing));
+      for (int u = 0; u < RING; ++u) {
+#pragma unroll
+        for (int q = 0; q < TPW; ++q) {
+          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ring[u][q]),
+                                                           __builtin_bit_cast(bf16x8_t, xv[u]),
+                                                           acc[q], 0, 0, 0);
+          ring[u][q] = buf_load16(ra, a_off(j0 + u + RING, q));
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
     // Partials: feature 4 * (lane >> 4) + q, token lane & 15.
+    // red[wave][q*16 + feature][token]
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      red[(wave * 16 + 4 * (lane >> 4) + q) * 16 + (lane & 15)] = acc[q];
+    for (int q = 0; q < TPW; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        red[(wave * 16 * TPW + q * 16 + 4 * (lane >> 4) + r) * 16 + (lane & 15)] = acc[q][r];
     __syncthreads();  // B1
-    {
-      const int nl = 4 * wave + (lane >> 4);
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) {
+      const int nl = q * 16 + 4 * wave + (lane >> 4);
       const int bl = lane & 15;
       float y = red[nl * 16 + bl];
 #pragma unroll
-      for (int w = 1; w < kWaves; ++w) y = y + red[(w * 16 + nl) * 16 + bl];
-      yt[bl * 16 + nl] = y;
+      for (int w = 1; w < kWaves; ++w) y = y + red[(w * 16 * TPW + nl) * 16 + bl];
+      yt[bl * 16 * TPW + nl] = y;
     }
     __syncthreads();  // B2: results token-major
-    // Thread (j, n): token j's feature 16 t + n; 16 threads write one row's
-    // 64 contiguous bytes.
     const int j = tid >> 4;
     const int n = tid & 15;
-    const int64_t feat = (int64_t)t * 16 + n;
-    if (j < M && feat < a.H) store_coherent(&a.bufs[s_dst[j] + feat], yt[j * 16 + n]);
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) {
+      const int64_t feat = (int64_t)(t0 + q) * 16 + n;
+      if (j < M && q < nt && feat < a.H)
+        store_coherent(&a.bufs[s_dst[j] + feat], yt[j * 16 * TPW + q * 16 + n]);
+    }
   }
   wait_vm_all();    // this wave's result rows are at the coherence point ...
   __syncthreads();  // B3 ... in every wave
   if (wave == 0) {
-    const uint32_t epoch = s_ctl[0];
-    if (lane < a.W) store_flag(moe_flag(a, lane, a.rank, e, t), epoch);
-    moe_wait_peers(a, lane, e, t, epoch);
+    // lane 8 q + d: tile t0 + q's flag in pad d
+    if ((lane >> 3) < nt && (lane & 7) < a.W)
+      store_flag(moe_flag(a, lane & 7, a.rank, e, t0 + (lane >> 3)), s_ep[lane >> 3]);
+    moe_wait_peers(a, lane, e, t0, nt, s_ep);
   }
 }
 
@@ -237,22 +263,39 @@ __global__ void a2a_reset_kernel(uint32_t* pads, int ne, int row_stride, int64_t
 
 }  // namespace
 
-size_t moe_lds_bytes(int C) {
-  return (size_t)16 * (C + 1) * 16 + (size_t)(kWaves * 256 + 256) * sizeof(float);
+namespace {
+
+template <int TPW>
+size_t lds_bytes(int C) {
+  return (size_t)16 * (C + 1) * 16 + (size_t)(kWaves * 256 * TPW + 256 * TPW) * sizeof(float);
 }
 
-hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
-  const size_t lds = moe_lds_bytes(a.C);
+template <int TPW, int RING>
+hipError_t launch(const MoeArgs& a, hipStream_t s) {
+  const size_t lds = lds_bytes<TPW>(a.C);
   if (lds > 65536) {
-    // Opt in to the largest dynamic LDS this kernel may use (cheap, idempotent).
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&moe_gemm_a2a),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)moe_lds_bytes(GSA_MOE_MAX_F / 8));
+    // Opt in to the largest dynamic LDS this instance may use (cheap, idempotent).
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&moe_gemm_a2a<TPW, RING>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes<TPW>(GSA_MOE_MAX_F / 8));
     if (e != hipSuccess) return e;
   }
-  const unsigned grid = (unsigned)(a.ne * a.tiles);
-  hipLaunchKernelGGL(moe_gemm_a2a, dim3(grid), dim3(kWaves * 64), lds, s, a);
+  const unsigned grid = (unsigned)(a.ne * ((a.tiles + TPW - 1) / TPW));
+  hipLaunchKernelGGL((moe_gemm_a2a<TPW, RING>), dim3(grid), dim3(kWaves * 64), lds, s, a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+// Tiles per workgroup by the width F of the expert: narrow experts take four
+// 16-feature tiles per workgroup, wide ones two, so that each workgroup
+// streams about 100-130 KB of weights and its fixed costs (split table, token
+// staging, store acknowledgement, flags) are spread over more bytes.
+// Measured on the Qwen3-30B-A3B-like (F = 768) and DeepSeek-V3-like
+// (F = 2048) shapes: one tile per workgroup 21.7 / 236 us, two 18.7 / 205,
+// four 17.0 / 230.
+hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
+  return a.F <= 1024 ? launch<4, 4>(a, s) : launch<2, 8>(a, s);
 }
 
 hipError_t launch_a2a_reset(uint32_t* pads, int W, int ne, int row_stride, int64_t pad_words,

@@ -137,6 +137,8 @@ EDGE = [
     (1, 4, 48, 256, 0, [16, 1, 0, 7], 0),   # one rank
     (8, 1, 1000, 136, 3, [9], 0),           # ragged C, one expert per rank
     (3, 5, 33, 32, 2, [0], 0),              # no tokens at all
+    (2, 2, 48, 2048, 1, [16, 2], 0),        # wide experts: two tiles per workgroup, 3 tiles
+    (4, 2, 80, 1024, 3, [5], 1),            # four tiles per workgroup, 5 tiles
 ]
 
 
