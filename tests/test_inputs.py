@@ -36,3 +36,54 @@ def test_distribution_roughly_as_stated():
     assert abs(A.std() - 0.02) < 5e-4 and abs(A.mean()) < 5e-4
     x = gi.bf16_bits_to_f32(d["x"])
     assert abs(x.std() - 1.0) < 0.1
+
+
+def test_moe_routing_respects_top_k_and_capacity():
+    c = gi.MOE_CONFIGS["m1"]
+    counts = gi.moe_routing(c["W"], c["ne"], c["T"], c["top_k"], c["capacity"], seed=0,
+                            cfg_id=c["cfg_id"])
+    E = c["W"] * c["ne"]
+    assert counts.shape == (c["W"], E)
+    # every expert takes at most its capacity; no token is counted twice for
+    # one expert, so a rank sends at most T tokens to any expert
+    assert counts.sum(axis=0).max() <= c["capacity"]
+    assert counts.max() <= c["T"]
+    # each rank routes T * top_k assignments before capacity drops
+    assert np.all(counts.sum(axis=1) <= c["T"] * c["top_k"])
+    again = gi.moe_routing(c["W"], c["ne"], c["T"], c["top_k"], c["capacity"], seed=0,
+                           cfg_id=c["cfg_id"])
+    assert np.array_equal(counts, again)
+
+
+def test_moe_layout_is_expert_major_and_combine_ordered():
+    rng = np.random.default_rng(5)
+    W, ne = 3, 2
+    counts = rng.integers(0, 4, size=(W, W * ne))
+    for rank in range(W):
+        d = gi.make_moe_from_counts(counts, ne, H=8, F=16, seed=1, rank=rank, gap=1)
+        # dispatch layout: local expert e, then source rank s, `gap` rows apart
+        row = 0
+        for e in range(ne):
+            for s in range(W):
+                assert d["length"][e, s] == counts[s, rank * ne + e]
+                assert d["in_off"][e, s] == row
+                row += int(d["length"][e, s]) + 1
+        # combine layout: rank s's rows ordered by global expert
+        for s in range(W):
+            for e in range(ne):
+                g = rank * ne + e
+                assert d["dst_off"][s, e] == counts[s, :g].sum()
+        # this rank's destination rows start as the sentinel, the rest finite
+        mine = np.zeros(d["bufs"].shape[:2], bool)
+        for s in range(W):
+            for e in range(ne):
+                o, n = int(d["dst_off"][s, e]), int(d["length"][e, s])
+                mine[s, o:o + n] = True
+        assert np.isnan(d["bufs"][mine]).all() and np.isfinite(d["bufs"][~mine]).all()
+
+
+def test_gathered_generator_shape_and_determinism():
+    a = gi.make_gathered(100, 3, seed=1, cfg_id=2)
+    b = gi.make_gathered(100, 3, seed=1, cfg_id=2)
+    assert a.shape == (100, 3) and a.dtype == np.float32
+    assert np.array_equal(a, b) and np.isfinite(a).all()
