@@ -10,7 +10,9 @@ from ._lib import (  # noqa: F401
     A2ABuffer, GSA_ESPLIT, GSA_MOE_MAX_F, GSA_MOE_MAX_TOKENS, EXPORTS, gsa_a2a_alloc,
     gsa_a2a_buffers, gsa_a2a_free, gsa_a2a_pad_words, gsa_a2a_reset, gsa_a2a_signal_pads,
     gsa_a2a_status, gsa_moe_gemm_all_to_all, GSA_DTYPE_BF16, GSA_DTYPE_F32, GSA_EHIP, GSA_EINVAL, GSA_ENOMEM, GSA_ESTATE,
-    GSA_ETIMEOUT, GSA_FLAG_PUBLISHED, GSA_FLAG_TILE_ROWS, GSA_MAX_B, GSA_MAX_W,
+    GSA_ETIMEOUT, GSA_FLAG_PUBLISHED, GSA_FLAG_GROUP_TILES, GSA_FLAG_GROUP_WORDS,
+    GSA_FLAG_TILE_ROWS, flag_word,
+    GSA_MOE_TILE_ROWS, GSA_MAX_B, GSA_MAX_W,
     GSA_MAX_X_LDS_BYTES, GSA_OK, GSA_PAD_HEADER_WORDS, GsaError, SymmBuffer, device_view,
     gsa_epilogue, gsa_gemv_allreduce, gsa_gemv_allreduce_rmsnorm, gsa_gemv_allreduce_two_shot,
     gsa_set_wait_timeout_us, gsa_signal_pad_reset, gsa_signal_pad_row_stride,

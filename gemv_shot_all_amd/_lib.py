@@ -14,7 +14,10 @@ GSA_ETIMEOUT = -4
 GSA_ESTATE = -5
 GSA_ESPLIT = -6
 GSA_FLAG_PUBLISHED = 0xFFFFFFFF
-GSA_FLAG_TILE_ROWS = 16
+GSA_FLAG_TILE_ROWS = 4
+GSA_FLAG_GROUP_TILES = 4
+GSA_FLAG_GROUP_WORDS = 32
+GSA_MOE_TILE_ROWS = 16
 GSA_PAD_HEADER_WORDS = 16
 GSA_MAX_W = 8
 GSA_MAX_B = 16
@@ -181,6 +184,12 @@ def gsa_signal_pad_row_stride(N):
     return lib().gsa_signal_pad_row_stride(N)
 
 
+def flag_word(t):
+    """Word of flag tile t (int or numpy array) within a rank's row of the
+    pad: groups of GSA_FLAG_GROUP_TILES flags, GSA_FLAG_GROUP_WORDS apart."""
+    return (t // GSA_FLAG_GROUP_TILES) * GSA_FLAG_GROUP_WORDS + t % GSA_FLAG_GROUP_TILES
+
+
 def gsa_signal_pad_reset(pad, W, N, published_mask, stream=None):
     _check(lib().gsa_signal_pad_reset(_ptr(pad), W, N, published_mask, _stream(stream)),
            "gsa_signal_pad_reset")
@@ -292,7 +301,7 @@ class SymmBuffer:
         import numpy as np
         raw = self.pad_view().cpu().numpy().view(np.uint32)
         rows = raw[GSA_PAD_HEADER_WORDS:].reshape(2 * self.W, self.row_stride)
-        return rows[first:first + self.W, :self.tiles].copy()
+        return rows[first:first + self.W, flag_word(np.arange(self.tiles))].copy()
 
     def flags(self):
         """Host copy (numpy uint32, W x T) of the slot flags."""
@@ -381,8 +390,8 @@ class A2ABuffer:
         self.bufs = gsa_a2a_buffers(self.handle)
         self.pads = gsa_a2a_signal_pads(self.handle)
         self.pad_words = gsa_a2a_pad_words(W, ne, H)
-        self.row_stride = gsa_signal_pad_row_stride(H)
-        self.tiles = (H + GSA_FLAG_TILE_ROWS - 1) // GSA_FLAG_TILE_ROWS
+        self.row_stride = (self.pad_words - GSA_PAD_HEADER_WORDS) // (W * ne)
+        self.tiles = (H + GSA_MOE_TILE_ROWS - 1) // GSA_MOE_TILE_ROWS
 
     def bufs_view(self):
         """torch float32 view (W, rows_out, H) of the combine buffers."""

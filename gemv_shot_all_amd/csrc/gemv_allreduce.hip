@@ -1,19 +1,22 @@
 // gemv_allreduce.hip -- the fused GEMV + one-shot AllReduce kernels for gfx950.
 //
-// One workgroup owns one flag tile: 16 output rows x all B batch columns.
-// Inside one launch it
-//   a. reads its own flag (epoch e = flag + 1) and polls the peers' flags
-//      for its tile; if every peer has already published (always the case
-//      for simulated peers) it acquires and prefetches the peer slots so
-//      their latency hides under the A stream;
+// One workgroup owns one tile of TR output rows x all B batch columns: TR = 4
+// (the plain one-shot call on short rows) or 16 (everything else).  The
+// signal pad holds one flag per rank per flag tile of 4 rows, so a workgroup
+// raises and waits on TR / 4 flags.  Inside one launch it
+//   a. reads its own flags (epoch e = flag + 1 per flag tile) and polls the
+//      peers' flags for its rows; if every peer has already published (always
+//      the case for simulated peers) it acquires and prefetches the peer slots
+//      so their latency hides under the A stream;
 //   b. stages this rank's activation slice x (bf16) in LDS;
 //   c. streams its 16 rows of A_r with 128-bit loads and multiply-adds in
 //      fp32 (VALU bf16 dot2 for B <= 8, MFMA 16x16x32 for 8 < B <= 16);
 //   d. reduces lane partials with a fixed DPP / lane-swap tree (or, for MFMA, a fixed
 //      cross-wave sum through LDS);
-//   e. publishes y into slot[rank], releases flag[rank][tile] = e, waits (if
-//      step a did not already see them) for every peer's flag >= e, and
-//      writes out = ((0 + s_0) + s_1) ... + s_{W-1} in rank order.
+//   e. publishes y into slot[rank], releases flag[rank][f] = e for each of
+//      its flag tiles f, waits (if step a did not already see them) for every
+//      peer's flag >= e, and writes out = ((0 + s_0) + s_1) ... + s_{W-1} in
+//      rank order (rows of a flag tile whose wait expired stay unwritten).
 //
 // Sources (restated): fused GEMV + AllReduce with per-workgroup hand-off of
 // finished results -- "Overlapping Collective Communication with Dependent
@@ -45,11 +48,54 @@
 namespace gsa {
 namespace {
 
-constexpr int kTileRows = GSA_FLAG_TILE_ROWS;
+constexpr int kFlagRows = GSA_FLAG_TILE_ROWS;  // rows per flag tile (4)
+constexpr int kBigTile = 16;                   // rows of the MFMA / epilogue / two-shot tiles
 constexpr int kMaxW = GSA_MAX_W;
+static_assert(kBigTile % kFlagRows == 0 && kBigTile / kFlagRows * kMaxW <= 64,
+              "one communication-wave lane per (flag tile, rank) of a workgroup");
 
-// s_ctl[1] values: what the start-of-kernel poll found.
+// Workgroup LDS control words:
+//   s_ctl[0] after a late wait: bit q set if flag tile q of the workgroup is complete
+//   s_ctl[1] what the start-of-kernel poll found (kMustWait / kPeersReady /
+//            kBadOwnRow), after a late wait kPeersReady if every flag tile is complete
+//   s_ctl[2], s_ctl[3] the fused epilogue's (see fused_epilogue)
+//   s_ctl[4 + q] the epoch of flag tile q
+constexpr int kCtlWords = 8;
 enum : uint32_t { kMustWait = 0u, kPeersReady = 1u, kBadOwnRow = 2u };
+
+// The workgroup tile of this block.  The dispatcher deals consecutive block
+// ids to the XCDs in turn (block b runs on XCD b % 8).  With XM the tiles go
+// to the XCDs in contiguous runs instead, so the slot, out and flag lines of
+// neighbouring tiles are written from one XCD (one L2); measured on the
+// shorter rows, where those stores weigh most (8B down_proj shape 4.95
+// against 5.08 us per call), and not taken on the longer rows or by MFMA
+// (slightly slower there).
+constexpr uint32_t kXcds = 8;
+template <bool XM>
+__device__ __forceinline__ int64_t block_tile() {
+  const uint32_t b = blockIdx.x;
+  if constexpr (!XM) {
+    return b;
+  } else {
+    const uint32_t T = gridDim.x, x = b % kXcds, k = b / kXcds;
+    const uint32_t per = T / kXcds, rem = T % kXcds;
+    return (int64_t)(x * per + min(x, rem) + k);  // a bijection of [0, T)
+  }
+}
+
+// The flag tiles [f0, f0 + nf) of workgroup tile `tile` of TR rows (the last
+// workgroup may cover fewer than TR / 4 of the ceil(N / 4) flag tiles).
+struct FlagSpan {
+  int64_t f0;
+  int nf;
+};
+template <int TR>
+__device__ __forceinline__ FlagSpan flag_span(const GemvArgs& a, int64_t tile) {
+  constexpr int FPW = TR / kFlagRows;
+  const int64_t f0 = tile * FPW;
+  const int64_t nflags = (a.N + kFlagRows - 1) / kFlagRows;
+  return {f0, (int)min((int64_t)FPW, nflags - f0)};
+}
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -65,16 +111,22 @@ __device__ __forceinline__ float dot8(const uint4& a, const uint4& x, float acc)
   return acc;
 }
 
+// Word of flag tile t within a rank's row: groups of 4 flag tiles (one
+// 16-row tile), one group per 128-byte line.
+__device__ __forceinline__ int64_t flag_word(int64_t t) {
+  return (t / GSA_FLAG_GROUP_TILES) * GSA_FLAG_GROUP_WORDS + t % GSA_FLAG_GROUP_TILES;
+}
 __device__ __forceinline__ uint32_t* flag_ptr(const GemvArgs& a, int r, int64_t t) {
-  return a.pad + GSA_PAD_HEADER_WORDS + (int64_t)r * a.row_stride + t;
+  return a.pad + GSA_PAD_HEADER_WORDS + (int64_t)r * a.row_stride + flag_word(t);
 }
 // Two-shot: rank r's reduced-chunk flag for tile t (pad row W + r).
 __device__ __forceinline__ uint32_t* flag2_ptr(const GemvArgs& a, int r, int64_t t) {
-  return a.pad + GSA_PAD_HEADER_WORDS + (int64_t)(a.W + r) * a.row_stride + t;
+  return a.pad + GSA_PAD_HEADER_WORDS + (int64_t)(a.W + r) * a.row_stride + flag_word(t);
 }
-// The rank that reduces tile t: the calling rank, or in the two-shot variant
-// (TS) the owner of the tile's chunk.  The kernels take TS as a template
-// argument so that the one-shot instances carry none of this code.
+// The rank that reduces workgroup tile t: the calling rank, or in the
+// two-shot variant (TS, 16-row tiles only) the owner of the tile's chunk.
+// The kernels take TS as a template argument so that the one-shot instances
+// carry none of this code.
 template <bool TS>
 __device__ __forceinline__ int tile_owner(const GemvArgs& a, int64_t t) {
   if constexpr (TS)
@@ -83,27 +135,42 @@ __device__ __forceinline__ int tile_owner(const GemvArgs& a, int64_t t) {
     return a.rank;
 }
 
-// Lane p reads flag[min(p, W-1)][t] (no divergent loads: every lane reads a
-// valid word; lanes >= W are ignored by the callers).
-__device__ __forceinline__ uint32_t load_flag(const GemvArgs& a, int lane, int64_t t) {
-  return __hip_atomic_load(flag_ptr(a, min(lane, a.W - 1), t), __ATOMIC_RELAXED,
+// The communication wave's flag lanes: lane l stands for rank p = l % 8 of
+// the workgroup's flag tile q = l / 8 (lanes past the span, p >= W or
+// q >= nf, are clamped to a valid word and ignored by the callers; no load
+// sits under divergent control, and no division delays the first load).
+__device__ __forceinline__ int lane_q(const FlagSpan& fs, int lane) {
+  return min(lane >> 3, fs.nf - 1);
+}
+__device__ __forceinline__ bool lane_in_span(const GemvArgs& a, const FlagSpan& fs, int lane) {
+  return (lane & 7) < a.W && (lane >> 3) < fs.nf;
+}
+__device__ __forceinline__ uint32_t load_flag(const GemvArgs& a, const FlagSpan& fs, int lane) {
+  return __hip_atomic_load(flag_ptr(a, min(lane & 7, a.W - 1), fs.f0 + lane_q(fs, lane)),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Two-shot: lane q < nf reads the owner's reduced-chunk flag of flag tile q.
+__device__ __forceinline__ uint32_t load_flag2(const GemvArgs& a, const FlagSpan& fs, int owner,
+                                               int lane) {
+  return __hip_atomic_load(flag2_ptr(a, owner, fs.f0 + min(lane, fs.nf - 1)), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Peer tiles: rank r's 16 x B tile of slot r lands at pe[(r * 16 + n) * B + b]
+// Peer tiles: rank r's TR x B tile of slot r lands at pe[(r * TR + n) * B + b]
 // for every peer r != rank.  issue_peer_tile loads up to kPerLane values per
 // lane per peer into registers (rows past N are clamped to a valid address;
 // their values are never read); store_peer_tile writes them to LDS.  The peer
 // loop is unrolled over GSA_MAX_W with a uniform guard, so no load sits under
 // divergent control.
-constexpr int kPerLane = (kTileRows * GSA_MAX_B) / 64;  // 4
+template <int TR>
+constexpr int kPerLane = (TR * GSA_MAX_B + 63) / 64;  // 4 (TR = 16) or 1 (TR = 4)
 
-template <bool TS>
+template <bool TS, int TR>
 __device__ __forceinline__ void issue_peer_tile(const GemvArgs& a, int lane, int64_t tile,
-                                                float (&v)[kMaxW][kPerLane]) {
+                                                float (&v)[kMaxW][kPerLane<TR>]) {
   const int64_t NB = a.N * a.B;
-  const int per_lane = (kTileRows * a.B + 63) / 64;  // 1, 2 or 4
-  const int64_t first = tile * kTileRows * a.B;      // first element of the tile in a slot
+  const int per_lane = (TR * a.B + 63) / 64;  // 1, 2 or 4
+  const int64_t first = tile * TR * a.B;      // first element of the tile in a slot
   const int64_t last = NB - 1;
   const int owner = tile_owner<TS>(a, tile);
   // Two-shot, a chunk another rank reduces: its published values, held in
@@ -114,16 +181,16 @@ __device__ __forceinline__ void issue_peer_tile(const GemvArgs& a, int lane, int
     if (copy ? r == 0 : (r < a.W && r != a.rank)) {
       const float* src = copy ? a.gathered : a.slots + r * NB;
 #pragma unroll
-      for (int i = 0; i < kPerLane; ++i)
+      for (int i = 0; i < kPerLane<TR>; ++i)
         if (i < per_lane) v[r][i] = load_coherent(&src[min(first + lane + 64 * i, last)]);
     }
   }
 }
 
-template <bool TS>
+template <bool TS, int TR>
 __device__ __forceinline__ void store_peer_tile(const GemvArgs& a, int lane, int64_t tile,
-                                                const float (&v)[kMaxW][kPerLane], float* pe) {
-  const int tb = kTileRows * a.B;  // elements of one rank's tile
+                                                const float (&v)[kMaxW][kPerLane<TR>], float* pe) {
+  const int tb = TR * a.B;  // elements of one rank's tile
   const int per_lane = (tb + 63) / 64;
   const int owner = tile_owner<TS>(a, tile);
   const bool copy = TS && owner != a.rank;  // v[0] holds the owner's values
@@ -132,7 +199,7 @@ __device__ __forceinline__ void store_peer_tile(const GemvArgs& a, int lane, int
     if (copy ? r == 0 : (r < a.W && r != a.rank)) {
       float* dst = pe + (copy ? owner : r) * tb;
 #pragma unroll
-      for (int i = 0; i < kPerLane; ++i) {
+      for (int i = 0; i < kPerLane<TR>; ++i) {
         const int e = lane + 64 * i;
         if (i < per_lane && e < tb) dst[e] = v[r][i];
       }
@@ -140,61 +207,76 @@ __device__ __forceinline__ void store_peer_tile(const GemvArgs& a, int lane, int
   }
 }
 
-// The communication wave's start: derive the epoch from its own flag and
-// check every peer's flag for this tile.  Writes s_ctl[0] = epoch and
-// s_ctl[1] = kMustWait / kPeersReady / kBadOwnRow; returns s_ctl[1].
+// The communication wave's start: derive each flag tile's epoch from its own
+// flag and check every peer's flag for it.  Writes s_ctl[4 + q] = epoch of
+// flag tile q and s_ctl[1] = kMustWait / kPeersReady / kBadOwnRow; returns
+// s_ctl[1].  A workgroup with an unusable own flag (marked published, or its
+// epochs exhausted) records the first such flag tile and does nothing else.
 template <bool TS>
 __device__ __forceinline__ uint32_t comm_decide(const GemvArgs& a, int lane, int64_t tile,
-                                                uint32_t fl, uint32_t* s_ctl) {
-  const uint32_t own = __builtin_amdgcn_readlane(fl, a.rank);
-  if (own >= GSA_FLAG_PUBLISHED - 1u) {  // row marked published, or epochs exhausted
+                                                const FlagSpan& fs, uint32_t fl, uint32_t* s_ctl) {
+  const int q = lane_q(fs, lane);
+  const int p = lane & 7;
+  const bool in_span = lane_in_span(a, fs, lane);
+  const uint32_t own = __shfl(fl, q * 8 + a.rank);  // the own flag of this lane's flag tile
+  const uint64_t bad = __ballot(in_span && own >= GSA_FLAG_PUBLISHED - 1u);
+  if (bad != 0) {
     if (lane == 0) {
       atomicOr(a.pad + kHdrErrorBits, kErrState);
-      atomicMin(a.pad + kHdrStateTile, (uint32_t)tile);
+      atomicMin(a.pad + kHdrStateTile,
+                (uint32_t)(fs.f0 + ((__ffsll((long long)bad) - 1) >> 3)));
       s_ctl[1] = kBadOwnRow;
     }
     return kBadOwnRow;
   }
   const uint32_t epoch = own + 1u;
+  if (in_span && p == a.rank) s_ctl[4 + q] = epoch;
   const int owner = tile_owner<TS>(a, tile);
-  bool lane_ok = lane >= a.W || lane == a.rank || fl >= epoch;
-  if (TS && owner != a.rank)  // two-shot: only the owner's reduced chunk is needed
-    lane_ok = lane != 0 ||
-              __hip_atomic_load(flag2_ptr(a, owner, tile), __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT) >= epoch;
-  const bool ready = __ballot(!lane_ok) == 0;
-  if (lane == 0) {
-    s_ctl[0] = epoch;
-    s_ctl[1] = ready ? kPeersReady : kMustWait;
+  bool lane_ok = !in_span || p == a.rank || fl >= epoch;
+  if (TS && owner != a.rank) {  // two-shot: only the owner's reduced chunk is needed
+    const uint32_t e2 = __shfl(fl, min(lane, fs.nf - 1) * 8 + a.rank) + 1u;
+    const uint32_t f2 = load_flag2(a, fs, owner, lane);  // every lane loads a valid word
+    lane_ok = lane >= fs.nf || f2 >= e2;
   }
+  const bool ready = __ballot(!lane_ok) == 0;
+  if (lane == 0) s_ctl[1] = ready ? kPeersReady : kMustWait;
   return ready ? kPeersReady : kMustWait;
 }
 
-// Bounded wait for every peer's flag >= epoch.  On expiry records the
-// smallest missing peer of this tile in the pad header.
+// Bounded wait for every peer's flag >= the epoch of each of the workgroup's
+// flag tiles.  Returns the mask of complete flag tiles (bit q); on expiry
+// records the smallest missing (flag tile, peer) in the pad header.
 template <bool TS>
-__device__ bool wait_peers(const GemvArgs& a, int lane, int64_t tile, uint32_t epoch) {
+__device__ uint32_t wait_peers(const GemvArgs& a, int lane, int64_t tile, const FlagSpan& fs,
+                               const uint32_t* s_ctl) {
   const uint64_t start = wall_clock64();
   const int owner = tile_owner<TS>(a, tile);
+  const bool copy = TS && owner != a.rank;  // two-shot: the owner's reduced-chunk flags
+  const int q = copy ? min(lane, fs.nf - 1) : lane_q(fs, lane);
+  const bool in_span = copy ? lane < fs.nf : lane_in_span(a, fs, lane);
+  const int p = lane & 7;
+  const uint32_t epoch = s_ctl[4 + q];
+  const uint32_t all = (1u << fs.nf) - 1u;
   for (;;) {
-    bool lane_ok;
-    if (TS && owner != a.rank) {  // two-shot: the owner's reduced-chunk flag
-      const uint32_t f2 = __hip_atomic_load(flag2_ptr(a, owner, tile), __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-      lane_ok = lane != owner || f2 >= epoch;
-    } else {
-      const uint32_t f = load_flag(a, lane, tile);
-      lane_ok = lane >= a.W || lane == a.rank || f >= epoch;
-    }
+    // Every lane loads a valid word; lanes outside the span are ignored.
+    const uint32_t f = copy ? load_flag2(a, fs, owner, lane) : load_flag(a, fs, lane);
+    const bool lane_ok = !in_span || (!copy && p == a.rank) || f >= epoch;
     const uint64_t missing = __ballot(!lane_ok);
-    if (missing == 0) return true;
+    if (missing == 0) return all;
     if (wall_clock64() - start > a.timeout_ticks) {
-      if (lane == 0) {
-        const uint32_t peer = (uint32_t)(__ffsll((long long)missing) - 1);
-        atomicOr(a.pad + kHdrErrorBits, kErrTimeout);
-        atomicMin(a.pad + kHdrTimeoutKey, (uint32_t)tile * 8u + peer);
+      uint32_t failed = 0;
+      for (int f = 0; f < fs.nf; ++f) {
+        const uint64_t lanes = copy ? (1ull << f) : (0xFFull << (8 * f));
+        if (missing & lanes) failed |= 1u << f;
       }
-      return false;
+      if (lane == 0) {
+        const int l = __ffsll((long long)missing) - 1;
+        const int64_t f = fs.f0 + (copy ? l : l >> 3);
+        const uint32_t peer = copy ? (uint32_t)owner : (uint32_t)(l & 7);
+        atomicOr(a.pad + kHdrErrorBits, kErrTimeout);
+        atomicMin(a.pad + kHdrTimeoutKey, (uint32_t)f * 8u + peer);
+      }
+      return all & ~failed;
     }
     __builtin_amdgcn_s_sleep(2);
   }
@@ -217,10 +299,11 @@ __device__ __forceinline__ unsigned long long* epi_count(const GemvArgs& a, int6
 // Barrier schedule shared with the compute waves:
 //   B0 flag load issued | B1 decision in s_ctl (the VALU kernels: x staged;
 //   the MFMA kernels: per-wave partials in LDS) | B2 own slot published, and
-//   the peer tile in LDS if the peers were ready at the start (compute wave 0
-//   then stores the flag) | B3 (only if they were not) late peer tile in LDS
-//   | two-shot, own chunk: B5 (reduced chunk published; compute wave 0 then
-//   stores the reduced-chunk flag) | with the fused epilogue: E1, E2 and
+//   the peer tile in LDS if the peers were ready at the start (lanes of
+//   compute wave 0 then store the workgroup's flags) | B3 (only if they were
+//   not) late peer tile in LDS | two-shot, own chunk: B5 (reduced chunk
+//   published; compute wave 0 then stores the reduced-chunk flags) | with the
+//   fused epilogue: E1, E2 and
 //   maybe E3, E4 (see fused_epilogue).
 // The peer loads stay in flight across B1: a workgroup barrier does not wait
 // for outstanding global loads.
@@ -228,35 +311,41 @@ __device__ __forceinline__ unsigned long long* epi_count(const GemvArgs& a, int6
 // its group (after B0) and, once its protocol work is done, looks whether
 // every tile of the call has started (s_ctl[3]: lane g reads group g's
 // count); s_epi_k gets the call's index.
-template <bool TS>
+template <bool TS, int TR>
 __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
                           uint32_t* s_ctl, unsigned long long* s_epi_k) {
-  const uint32_t fl = load_flag(a, lane, tile);
-  __syncthreads();  // B0: the flag load is issued ahead of every x and A load
+  const FlagSpan fs = flag_span<TR>(a, tile);
+  const uint32_t fl = load_flag(a, fs, lane);
+  __syncthreads();  // B0: the flag loads are issued ahead of every x and A load
   // Count the tile started; the value is used only after the protocol work.
+  constexpr bool kEpi = TR == kBigTile;  // the epilogue runs on 16-row tiles only
   const int grp = (int)(tile % kEpiGroups);
   unsigned long long before = 0;
-  if (a.epi && lane == 0)
+  if (kEpi && a.epi && lane == 0)
     before = __hip_atomic_fetch_add(epi_count(a, epi_started_off(a.tiles), grp), 1ull,
                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint32_t state = comm_decide<TS>(a, lane, tile, fl, s_ctl);
-  float v[kMaxW][kPerLane];
-  if (state == kPeersReady) issue_peer_tile<TS>(a, lane, tile, v);  // after the flags returned
+  const uint32_t state = comm_decide<TS>(a, lane, tile, fs, fl, s_ctl);
+  float v[kMaxW][kPerLane<TR>];
+  if (state == kPeersReady) issue_peer_tile<TS, TR>(a, lane, tile, v);  // after the flags returned
   __syncthreads();  // B1
-  if (state == kPeersReady) store_peer_tile<TS>(a, lane, tile, v, pe);
+  if (state == kPeersReady) store_peer_tile<TS, TR>(a, lane, tile, v, pe);
   __syncthreads();  // B2
   if (state == kMustWait) {
-    const uint32_t epoch = s_ctl[0];
-    const bool ok = wait_peers<TS>(a, lane, tile, epoch);  // the own flag went out after B2
-    if (ok) {
-      issue_peer_tile<TS>(a, lane, tile, v);  // after the flags returned
-      store_peer_tile<TS>(a, lane, tile, v, pe);
+    // The own flags went out after B2.
+    const uint32_t done = wait_peers<TS>(a, lane, tile, fs, s_ctl);
+    if (done != 0) {
+      // After the flags returned; rows of incomplete flag tiles are never read.
+      issue_peer_tile<TS, TR>(a, lane, tile, v);
+      store_peer_tile<TS, TR>(a, lane, tile, v, pe);
     }
-    if (lane == 0) s_ctl[1] = ok ? kPeersReady : kMustWait;
+    if (lane == 0) {
+      s_ctl[0] = done;
+      s_ctl[1] = done == (1u << fs.nf) - 1u ? kPeersReady : kMustWait;
+    }
     __syncthreads();  // B3
   }
   if (TS && tile_owner<TS>(a, tile) == a.rank) __syncthreads();  // B5
-  if (a.epi) {
+  if (kEpi && a.epi) {
     // The call's index k (every tile of a call is counted once per group).
     const unsigned long long k =
         __builtin_amdgcn_readfirstlane((uint32_t)(before / (unsigned)epi_group_tiles(a, grp))) |
@@ -288,9 +377,10 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
 // peer values are read up front (indexes clamped into the tile) and ranks
 // r >= W add +0: the sum starts at +0 and a round-to-nearest sum is -0 only
 // if both terms are, so acc is never -0 and acc + 0 == acc exactly.
+template <int TR>
 __device__ __forceinline__ float one_shot_sum(const GemvArgs& a, float y, const float* pe, int n,
                                               int b) {
-  const int tb = kTileRows * a.B;
+  const int tb = TR * a.B;
   const int idx = n * a.B + b;
   float pv[kMaxW];
 #pragma unroll
@@ -307,24 +397,27 @@ __device__ __forceinline__ float one_shot_sum(const GemvArgs& a, float y, const 
 template <int BM, int OPL>
 __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
                                const bool (&own)[OPL], const bool (&live)[OPL],
-                               const float (&o)[OPL], bool ok, float* elds, uint32_t* s_ctl,
-                               const unsigned long long* s_epi_k, int wave, int lane, int nt);
+                               const float (&o)[OPL], const bool (&ok)[OPL], float* elds,
+                               uint32_t* s_ctl, const unsigned long long* s_epi_k, int wave,
+                               int lane, int nt);
 
 // Compute waves once y is final (y[e] for local row n[e], column b, if own[e]:
 // every (row, column) of the tile has exactly one owner lane), `state` being
 // what the communication wave decided before B1: publish y into slot[rank],
-// B2, compute wave 0 releases the flag, [B3], out, [the fused epilogue].
-// Every compute wave waits for its own slot stores to complete before B2, so
-// the flag store that follows B2 is ordered after all of them.  nt: compute
-// threads of the workgroup.
-template <int BM, int OPL, bool TS>
+// B2, lanes of compute wave 0 release the workgroup's flags, [B3], out (rows
+// of complete flag tiles), [the fused epilogue].  Every compute wave waits
+// for its own slot stores to complete before B2, so the flag stores that
+// follow B2 are ordered after all of them.  nt: compute threads of the
+// workgroup.
+template <int BM, int OPL, bool TS, int TR>
 __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
                                    const bool (&own)[OPL], const float (&y)[OPL],
                                    const float* pe, float* elds, uint32_t* s_ctl,
                                    const unsigned long long* s_epi_k, uint32_t state, int wave,
                                    int lane, int nt) {
   const int64_t NB = a.N * a.B;
-  const int64_t row0 = tile * kTileRows;
+  const int64_t row0 = tile * TR;
+  const FlagSpan fs = flag_span<TR>(a, tile);
   float* own_slot = a.slots + a.rank * NB;
   bool live[OPL];
 #pragma unroll
@@ -336,24 +429,28 @@ __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t ti
   }
   wait_vm_all();    // the published values are at the coherence point ...
   __syncthreads();  // B2 ... in every compute wave
-  bool ok = state != kBadOwnRow;
-  if (ok && wave == 0 && lane == 0) store_flag(flag_ptr(a, a.rank, tile), s_ctl[0]);
+  if (state != kBadOwnRow && wave == 0 && lane < fs.nf)
+    store_flag(flag_ptr(a, a.rank, fs.f0 + lane), s_ctl[4 + lane]);
+  uint32_t done = state == kBadOwnRow ? 0u : ~0u;  // complete flag tiles
   if (state == kMustWait) {
     __syncthreads();  // B3
-    ok = s_ctl[1] == kPeersReady;  // wait expired: this tile's out rows stay unwritten
+    done = s_ctl[0];  // a wait expired: those flag tiles' out rows stay unwritten
   }
+  bool ok[OPL];
+#pragma unroll
+  for (int e = 0; e < OPL; ++e) ok[e] = ((done >> (n[e] / kFlagRows)) & 1u) != 0;
   const int owner = tile_owner<TS>(a, tile);
   float o[OPL];
 #pragma unroll
   for (int e = 0; e < OPL; ++e) {
     o[e] = 0.0f;
-    if (ok && live[e]) {
+    if (ok[e] && live[e]) {
       const int64_t i = (row0 + n[e]) * a.B + b;
       if (!TS || owner == a.rank) {
-        o[e] = one_shot_sum(a, y[e], pe, n[e], b);
+        o[e] = one_shot_sum<TR>(a, y[e], pe, n[e], b);
         if (TS) store_coherent(&a.gathered[i], o[e]);  // this rank's reduced chunk
       } else {
-        o[e] = pe[owner * kTileRows * a.B + n[e] * a.B + b];  // the owner's reduced chunk
+        o[e] = pe[owner * TR * a.B + n[e] * a.B + b];  // the owner's reduced chunk
       }
       if (a.epi)
         store_coherent(&a.out[i], o[e]);  // read back by the workgroup that finishes last
@@ -364,10 +461,14 @@ __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t ti
   if (TS && owner == a.rank) {
     wait_vm_all();    // the reduced chunk is at the coherence point ...
     __syncthreads();  // B5 ... in every compute wave
-    if (ok && wave == 0 && lane == 0) store_flag(flag2_ptr(a, a.rank, tile), s_ctl[0]);
+    if (wave == 0 && lane < fs.nf && ((done >> lane) & 1u))
+      store_flag(flag2_ptr(a, a.rank, fs.f0 + lane), s_ctl[4 + lane]);
   }
-  if (a.epi)
-    fused_epilogue<BM, OPL>(a, tile, n, b, own, live, o, ok, elds, s_ctl, s_epi_k, wave, lane, nt);
+  if constexpr (TR == kBigTile) {
+    if (a.epi)
+      fused_epilogue<BM, OPL>(a, tile, n, b, own, live, o, ok, elds, s_ctl, s_epi_k, wave, lane,
+                              nt);
+  }
 }
 
 // Sum of v over an aligned group of G lanes (G = 16, 32 or 64), returned in
@@ -487,19 +588,20 @@ __device__ __forceinline__ void store_y(const GemvArgs& a, int64_t i, float v) {
 //  - Any other tile marks 0 and leaves; the last tile also normalises the
 //    rows of every tile not marked k + 1, re-reading out (stored coherently
 //    for this).
-// A tile that failed (wait expired, bad own row) contributes NaN, so y comes
-// out NaN for that call.  Barriers: E1 (squares in LDS, out stores
+// A row that failed (its flag tile's wait expired, or a bad own row)
+// contributes NaN, so y comes out NaN for that call.  Barriers: E1 (squares in LDS, out stores
 // completed), E2 (count taken), then, in the last tile and in waiting tiles,
 // E3 (wave sums in LDS, or the flag seen) and E4 (inv in LDS).
 template <int BM, int OPL>
 __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
                                const bool (&own)[OPL], const bool (&live)[OPL],
-                               const float (&o)[OPL], bool ok, float* elds, uint32_t* s_ctl,
-                               const unsigned long long* s_epi_k, int wave, int lane, int nt) {
+                               const float (&o)[OPL], const bool (&ok)[OPL], float* elds,
+                               uint32_t* s_ctl, const unsigned long long* s_epi_k, int wave,
+                               int lane, int nt) {
   float* zz = elds;            // [16 rows][16 columns] squares of z
   float* s_inv = elds + 256;   // [16] 1 / rms per column
   float* wsum = elds + 272;    // [8 waves][16 columns] the fold's wave sums
-  const int64_t row0 = tile * kTileRows;
+  const int64_t row0 = tile * kBigTile;
   float z[OPL];
 #pragma unroll
   for (int e = 0; e < OPL; ++e) {
@@ -510,7 +612,7 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
         z[e] = o[e] + (a.bias ? a.bias[row0 + n[e]] : 0.0f);
         sq = z[e] * z[e];
       }
-      zz[n[e] * 16 + b] = ok ? sq : __builtin_nanf("");
+      zz[n[e] * 16 + b] = ok[e] ? sq : __builtin_nanf("");
     }
   }
   wait_vm_all();    // this wave's out stores are at the coherence point ...
@@ -526,7 +628,7 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
   if (wave == 0) {
     if (lane < a.B) {
       float part = 0.0f;
-      for (int r = 0; r < kTileRows; ++r) part = part + zz[r * 16 + lane];
+      for (int r = 0; r < kBigTile; ++r) part = part + zz[r * 16 + lane];
       store_coherent(&rec[lane], part);
     }
     if (lane == 16)
@@ -574,7 +676,7 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
       while (__hip_atomic_load(inv_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != mark) {
         if (wall_clock64() - start > 2 * a.timeout_ticks + 1000000ull) {
           atomicOr(a.pad + kHdrErrorBits, kErrEpiWait);
-          atomicMin(a.pad + kHdrEpiWaitTile, (uint32_t)tile);
+          atomicMin(a.pad + kHdrEpiWaitTile, (uint32_t)(tile * (kBigTile / kFlagRows)));
           seen = false;
           break;
         }
@@ -594,7 +696,7 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
       if (live[e]) {
         float v = z[e] * s_inv[b];
         if (a.rms_w) v = v * a.rms_w[row0 + n[e]];
-        if (!ok) v = __builtin_nanf("");
+        if (!ok[e]) v = __builtin_nanf("");
         store_y(a, (row0 + n[e]) * a.B + b, v);
       }
     }
@@ -614,8 +716,8 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
         reinterpret_cast<const uint32_t*>(a.ssq + (int64_t)t * kEpiRecordWords + 16),
         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (m == mark) continue;
-    const int64_t lo = (int64_t)t * kTileRows * a.B;
-    const int64_t hi = min(NB, lo + (int64_t)kTileRows * a.B);
+    const int64_t lo = (int64_t)t * kBigTile * a.B;
+    const int64_t hi = min(NB, lo + (int64_t)kBigTile * a.B);
     for (int64_t i0 = lo; i0 < hi; i0 += kBatch) {
       float ov[kBatch], bv[kBatch], wv[kBatch];
 #pragma unroll
@@ -707,38 +809,43 @@ __device__ __forceinline__ void valu_stream(float (&acc)[R][B], uint4 (&ring)[D]
 // once).  WPE is the occupancy (waves per SIMD) the register budget must
 // allow.  NCH > 0 builds a fully unrolled instance for
 // exactly NCH chunks per lane; MASKED instances zero chunks past the row end.
+// TR = NW * (64 / G) * R rows per workgroup (4 or 16; the two-shot variant and
+// the fused epilogue run on 16).  XM: XCD-contiguous tile order (block_tile).
 // LDS: x chunks [b][c], one zero chunk, one sink chunk, then the peer tile.
-template <int B, int G, int R, int NW, int NCH, int D, int XPT, int WPE, bool MASKED, bool TS>
+template <int B, int G, int R, int NW, int NCH, int D, int XPT, int WPE, bool MASKED, bool TS,
+          bool XM>
 __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   constexpr int NT = NW * 64;
   constexpr int GPW = 64 / G;
-  static_assert(NW * GPW * R == kTileRows, "one workgroup covers one flag tile");
+  constexpr int TR = NW * GPW * R;
+  static_assert(TR == kBigTile || (TR == kFlagRows && !TS),
+                "16-row tiles, or 4-row tiles of the plain one-shot call");
   constexpr int V = R * B;
   static_assert(V <= G, "one owner lane per output of a row group");
 
   extern __shared__ uint4 lds_x[];
-  __shared__ uint32_t s_ctl[4];
+  __shared__ uint32_t s_ctl[kCtlWords];
   __shared__ unsigned long long s_epi_k;  // the epilogue's call index
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t tile = blockIdx.x;
+  const int64_t tile = block_tile<XM>();
   const int C = a.C;
   const int xchunks = B * C;
   const int zidx = xchunks;  // zero chunk; xchunks + 1 is the sink
   float* pe = reinterpret_cast<float*>(lds_x + xchunks + 2);
-  float* elds = pe + a.W * kTileRows * B + 1;  // the epilogue's LDS
+  float* elds = pe + a.W * TR * B + 1;  // the epilogue's LDS
 
   if (wave == NW) {
-    comm_wave<TS>(a, lane, tile, pe, s_ctl, &s_epi_k);
+    comm_wave<TS, TR>(a, lane, tile, pe, s_ctl, &s_epi_k);
     return;
   }
 
   const int grp = lane / G;
   const int li = lane % G;
   const int nloc0 = (wave * GPW + grp) * R;  // first local row of this row group
-  const int64_t row0 = tile * kTileRows + nloc0;
+  const int64_t row0 = tile * TR + nloc0;
   const int nch = NCH > 0 ? NCH : (C + G - 1) / G;
 
   const uint4* xg = reinterpret_cast<const uint4*>(a.x);
@@ -785,8 +892,8 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   const int n[1] = {nloc0 + vidx / B};
   const bool own[1] = {li < V};
   const float y[1] = {yv};
-  publish_and_reduce<B, 1, TS>(a, tile, n, vidx % B, own, y, pe, elds, s_ctl, &s_epi_k, state,
-                               wave, lane, NT);
+  publish_and_reduce<B, 1, TS, TR>(a, tile, n, vidx % B, own, y, pe, elds, s_ctl, &s_epi_k,
+                                   state, wave, lane, NT);
 }
 
 // MFMA epilogue: each wave's 16 x 16 partial goes to red[wave][n][b]; after
@@ -799,19 +906,19 @@ __device__ __forceinline__ void mfma_finish(const GemvArgs& a, int64_t tile, int
                                             const unsigned long long* s_epi_k) {
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    red[(wave * kTileRows + 4 * (lane >> 4) + e) * 16 + (lane & 15)] = acc[e];
+    red[(wave * kBigTile + 4 * (lane >> 4) + e) * 16 + (lane & 15)] = acc[e];
   __syncthreads();  // B1: every partial in LDS, the decision in s_ctl
   const uint32_t state = s_ctl[1];
   const int nl = 4 * wave + (lane >> 4);
   const int bl = lane & 15;
   float y = red[nl * 16 + bl];
 #pragma unroll
-  for (int w = 1; w < NW; ++w) y = y + red[(w * kTileRows + nl) * 16 + bl];
+  for (int w = 1; w < NW; ++w) y = y + red[(w * kBigTile + nl) * 16 + bl];
   const int n[1] = {nl};
   const bool own[1] = {bl < a.B};
   const float yv[1] = {y};
-  publish_and_reduce<GSA_MAX_B, 1, TS>(a, tile, n, bl, own, yv, pe, elds, s_ctl, s_epi_k, state,
-                                       wave, lane, NW * 64);
+  publish_and_reduce<GSA_MAX_B, 1, TS, kBigTile>(a, tile, n, bl, own, yv, pe, elds, s_ctl,
+                                                 s_epi_k, state, wave, lane, NW * 64);
 }
 
 // MFMA path, 8 < B <= 16 (batch padded to 16 with zeros).  The tile's 16 rows
@@ -829,9 +936,9 @@ __device__ __forceinline__ void mfma_finish(const GemvArgs& a, int64_t tile, int
 // LDS: x [16][C + 1] chunks (column C zero); NW 16 x 16 partials; peer tile.
 template <int NW, int D, bool TS>
 __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs a) {
-  static_assert(NW * 4 == kTileRows, "each compute wave finishes 4 rows of the tile");
+  static_assert(NW * 4 == kBigTile, "each compute wave finishes 4 rows of the tile");
   extern __shared__ uint4 lds[];
-  __shared__ uint32_t s_ctl[4];
+  __shared__ uint32_t s_ctl[kCtlWords];
   __shared__ unsigned long long s_epi_k;  // the epilogue's call index
 
   const int tid = threadIdx.x;
@@ -841,15 +948,15 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs a) {
   const int C = a.C;
   const int CP = C + 1;  // padded LDS row: the 16 batch rows of one chunk hit distinct banks
   float* red = reinterpret_cast<float*>(lds + 16 * CP);
-  float* pe = red + NW * kTileRows * 16;
-  float* elds = pe + a.W * kTileRows * a.B + 1;  // the epilogue's LDS
+  float* pe = red + NW * kBigTile * 16;
+  float* elds = pe + a.W * kBigTile * a.B + 1;  // the epilogue's LDS
 
   if (wave == NW) {
-    comm_wave<TS>(a, lane, tile, pe, s_ctl, &s_epi_k);
+    comm_wave<TS, kBigTile>(a, lane, tile, pe, s_ctl, &s_epi_k);
     return;
   }
 
-  const int64_t row0 = tile * kTileRows;
+  const int64_t row0 = tile * kBigTile;
   const int steps = (C + 3) / 4;
   const int per_wave = (steps + NW - 1) / NW;
   const int s_begin = wave * per_wave;
@@ -924,9 +1031,9 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs a) {
 // LDS: NW 16 x 16 partials, then the peer tile.
 template <int NW, int D, bool TS>
 __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a) {
-  static_assert(NW * 4 == kTileRows, "each compute wave finishes 4 rows of the tile");
+  static_assert(NW * 4 == kBigTile, "each compute wave finishes 4 rows of the tile");
   extern __shared__ uint4 lds[];
-  __shared__ uint32_t s_ctl[4];
+  __shared__ uint32_t s_ctl[kCtlWords];
   __shared__ unsigned long long s_epi_k;  // the epilogue's call index
 
   const int tid = threadIdx.x;
@@ -935,15 +1042,15 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a
   const int64_t tile = blockIdx.x;
   const int C = a.C;
   float* red = reinterpret_cast<float*>(lds);
-  float* pe = red + NW * kTileRows * 16;
-  float* elds = pe + a.W * kTileRows * a.B + 1;  // the epilogue's LDS
+  float* pe = red + NW * kBigTile * 16;
+  float* elds = pe + a.W * kBigTile * a.B + 1;  // the epilogue's LDS
 
   if (wave == NW) {
-    comm_wave<TS>(a, lane, tile, pe, s_ctl, &s_epi_k);
+    comm_wave<TS, kBigTile>(a, lane, tile, pe, s_ctl, &s_epi_k);
     return;
   }
 
-  const int64_t row0 = tile * kTileRows;
+  const int64_t row0 = tile * kBigTile;
   const int steps = (C + 3) / 4;
   const int per_wave = (steps + NW - 1) / NW;
   const int s_begin = wave * per_wave;
@@ -1019,7 +1126,8 @@ bool mfma_x_in_lds(int C) { return (size_t)16 * (C + 1) * 16 <= GSA_MAX_X_LDS_BY
 
 struct ValuChoice {
   const void* kernel;
-  int waves;  // compute waves (the communication wave comes on top)
+  int waves;      // compute waves (the communication wave comes on top)
+  int tile_rows;  // rows per workgroup
 };
 
 constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -1029,59 +1137,68 @@ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // exact instance; any other C the masked streaming instance.  XPT covers
 // B * G * NCH chunks of x (at most 8 per thread; the rest of a longer x is
 // staged by a plain loop).
-template <int B, int G, int R, int NW, int NCH, int D, int WPE, bool TS>
+template <int B, int G, int R, int NW, int NCH, int D, int WPE, bool TS, bool XM>
 ValuChoice valu_tier(int C) {
   constexpr int XPT0 = ceil_div(B * G * NCH, NW * 64);
   constexpr int XPT = XPT0 > 8 ? 8 : XPT0;
   constexpr int DE = D < NCH ? D : NCH;
   const void* k;
   if (C == G * NCH)
-    k = reinterpret_cast<const void*>(&gemv_ar_valu<B, G, R, NW, NCH, DE, XPT, WPE, false, TS>);
+    k = reinterpret_cast<const void*>(
+        &gemv_ar_valu<B, G, R, NW, NCH, DE, XPT, WPE, false, TS, XM>);
   else
-    k = reinterpret_cast<const void*>(&gemv_ar_valu<B, G, R, NW, 0, D, XPT, WPE, true, TS>);
-  return {k, NW};
+    k = reinterpret_cast<const void*>(&gemv_ar_valu<B, G, R, NW, 0, D, XPT, WPE, true, TS, XM>);
+  return {k, NW, NW * (64 / G) * R};
 }
 
-// VALU tiers by chunks per row C = Ks / 8 (every tier covers 16 rows per
-// workgroup, plus the communication wave):
-//   C <= 64 : 4 waves, a full wave per row, 4 rows per wave
-//   C <= 224: 4 waves, half a wave per row, 2 x 2 rows per wave
-//   larger  : 8 waves, a full wave per row, 2 rows per wave
+// VALU tiers by chunks per row C = Ks / 8 (plus the communication wave):
+//   C <= 64, plain one-shot call: 4 rows per workgroup, 1 wave, half a wave
+//            per row, 2 x 2 rows (more, smaller workgroups: on the Llama-3-8B
+//            o_proj shape 4.05 against 4.49 us per call with 16-row tiles)
+//   C <= 64 : 16 rows, 4 waves, a full wave per row, 4 rows per wave
+//   C <= 224: 16 rows, 4 waves, half a wave per row, 2 x 2 rows per wave
+//   larger  : 16 rows, 8 waves, a full wave per row, 2 rows per wave
+// (4-row tiles on the longer rows measured slower: 5.4-5.5 against 5.25 us on
+// the 8B down_proj shape, 14.9 against 12.3 us on the 70B-class one.)  Tiles
+// of rows up to C = 224 go to the XCDs in contiguous runs (block_tile).
 template <int B, bool TS>
-ValuChoice valu_kernel(int C) {
-  if (C <= 64) return valu_tier<B, 64, 4, 4, 1, 1, 1, TS>(C);
-  if (C <= 224) return valu_tier<B, 32, 2, 4, 7, 4, 1, TS>(C);
-  return valu_tier<B, 64, 2, 8, 7, 3, 5, TS>(C);
+ValuChoice valu_kernel(int C, bool small_tiles) {
+  if constexpr (!TS) {
+    if (small_tiles && C <= 64) return valu_tier<B, 32, 2, 1, 2, 2, 1, false, true>(C);
+  }
+  if (C <= 64) return valu_tier<B, 64, 4, 4, 1, 1, 1, TS, true>(C);
+  if (C <= 224) return valu_tier<B, 32, 2, 4, 7, 4, 1, TS, true>(C);
+  return valu_tier<B, 64, 2, 8, 7, 3, 5, TS, false>(C);
 }
 
 template <bool TS>
-ValuChoice pick_kernel(int B, int C) {
+ValuChoice pick_kernel(int B, int C, bool small_tiles) {
   switch (B) {
-    case 1: return valu_kernel<1, TS>(C);
-    case 2: return valu_kernel<2, TS>(C);
-    case 3: return valu_kernel<3, TS>(C);
-    case 4: return valu_kernel<4, TS>(C);
-    case 5: return valu_kernel<5, TS>(C);
-    case 6: return valu_kernel<6, TS>(C);
-    case 7: return valu_kernel<7, TS>(C);
-    case 8: return valu_kernel<8, TS>(C);
+    case 1: return valu_kernel<1, TS>(C, small_tiles);
+    case 2: return valu_kernel<2, TS>(C, small_tiles);
+    case 3: return valu_kernel<3, TS>(C, small_tiles);
+    case 4: return valu_kernel<4, TS>(C, small_tiles);
+    case 5: return valu_kernel<5, TS>(C, small_tiles);
+    case 6: return valu_kernel<6, TS>(C, small_tiles);
+    case 7: return valu_kernel<7, TS>(C, small_tiles);
+    case 8: return valu_kernel<8, TS>(C, small_tiles);
     default:
       return mfma_x_in_lds(C)
                  ? ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma<kMfmaWaves, 8, TS>),
-                              kMfmaWaves}
+                              kMfmaWaves, kBigTile}
                  : ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma_xmem<kMfmaWaves, 8, TS>),
-                              kMfmaWaves};
+                              kMfmaWaves, kBigTile};
   }
 }
 
 }  // namespace
 
-size_t gemv_lds_bytes(int W, int B, int C, bool epi) {
+size_t gemv_lds_bytes(int W, int B, int C, bool epi, int tile_rows) {
   // The peer tile, then (with the epilogue) 16 x 16 squares, 16 1/rms and
   // up to 8 waves x 16 partial sums.
-  const size_t tail = ((size_t)W * kTileRows * B + 1) * sizeof(float) +
+  const size_t tail = ((size_t)W * tile_rows * B + 1) * sizeof(float) +
                       (epi ? (size_t)(256 + 16 + 8 * 16) * sizeof(float) : 0);
-  const size_t partials = (size_t)kMfmaWaves * kTileRows * 16 * sizeof(float);
+  const size_t partials = (size_t)kMfmaWaves * kBigTile * 16 * sizeof(float);
   if (B <= 8) return ((size_t)B * C + 2) * 16 + tail;
   if (mfma_x_in_lds(C)) return (size_t)16 * (C + 1) * 16 + partials + tail;
   return partials + tail;
@@ -1091,9 +1208,11 @@ bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, Launch* ou
   if (W < 1 || W > GSA_MAX_W || B < 1 || B > GSA_MAX_B || C < 1) return false;
   if (B <= 8 && (size_t)B * C * 16 > GSA_MAX_X_LDS_BYTES) return false;  // x staged in LDS
   if (epi && two_shot) return false;  // separate entry points
-  const ValuChoice k = two_shot ? pick_kernel<true>(B, C) : pick_kernel<false>(B, C);
+  const bool small_tiles = !epi && !two_shot;  // 4-row tiles only for the plain call
+  const ValuChoice k =
+      two_shot ? pick_kernel<true>(B, C, false) : pick_kernel<false>(B, C, small_tiles);
   const unsigned block = (unsigned)(k.waves + 1) * 64;
-  *out = {k.kernel, block, gemv_lds_bytes(W, B, C, epi)};
+  *out = {k.kernel, block, gemv_lds_bytes(W, B, C, epi, k.tile_rows), k.tile_rows};
   return true;
 }
 

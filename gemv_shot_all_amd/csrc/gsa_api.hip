@@ -59,7 +59,14 @@ constexpr size_t kAlign = 256;
 
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+// Flag tiles of the GEMV pad (4 rows each), 16-row tiles (the fused
+// epilogue's records, the two-shot chunks), MoE feature tiles.
 int64_t tiles_of(int64_t N) { return (N + GSA_FLAG_TILE_ROWS - 1) / GSA_FLAG_TILE_ROWS; }
+int64_t big_tiles_of(int64_t N) {
+  return (N + gsa::kBigTileRows - 1) / gsa::kBigTileRows;
+}
+int64_t moe_tiles_of(int64_t H) { return (H + GSA_MOE_TILE_ROWS - 1) / GSA_MOE_TILE_ROWS; }
+int64_t moe_row_stride(int64_t H) { return (int64_t)round_up((size_t)moe_tiles_of(H), 64); }
 
 gsa_symm* find_by_slots(const void* slots) {
   auto it = g_by_slots.find((uintptr_t)slots);
@@ -109,7 +116,8 @@ extern "C" {
 
 int64_t gsa_signal_pad_row_stride(int64_t N) {
   if (N < 1) return -1;
-  return (int64_t)round_up((size_t)tiles_of(N), 64);
+  const int64_t groups = (tiles_of(N) + GSA_FLAG_GROUP_TILES - 1) / GSA_FLAG_GROUP_TILES;
+  return (int64_t)round_up((size_t)groups * GSA_FLAG_GROUP_WORDS, 64);
 }
 
 int gsa_symm_alloc(int W, int64_t N, int B, gsa_symm** out) {
@@ -121,9 +129,9 @@ int gsa_symm_alloc(int W, int64_t N, int B, gsa_symm** out) {
   const size_t pad_words = GSA_PAD_HEADER_WORDS + 2 * (size_t)W * (size_t)stride;
   const size_t gathered_bytes = round_up((size_t)N * (size_t)B * sizeof(float), kAlign);
   const size_t pad_bytes = round_up(pad_words * sizeof(uint32_t), kAlign);
-  // The epilogue's scratch: one record per tile, then flags and counts.
+  // The epilogue's scratch: one record per 16-row tile, then flags and counts.
   const size_t ssq_bytes =
-      round_up((size_t)gsa::epi_scratch_words(tiles_of(N)) * sizeof(float), kAlign);
+      round_up((size_t)gsa::epi_scratch_words(big_tiles_of(N)) * sizeof(float), kAlign);
   const size_t bytes = slot_bytes + pad_bytes + gathered_bytes + ssq_bytes;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return GSA_EHIP;
@@ -146,7 +154,7 @@ int gsa_symm_alloc(int W, int64_t N, int B, gsa_symm** out) {
   float* gathered = reinterpret_cast<float*>(static_cast<char*>(base) + slot_bytes + pad_bytes);
   float* ssq = reinterpret_cast<float*>(static_cast<char*>(base) + slot_bytes + pad_bytes +
                                         gathered_bytes);
-  gsa_symm* h = new gsa_symm{W, N, B, stride, tiles_of(N), bytes, base,
+  gsa_symm* h = new gsa_symm{W, N, B, stride, big_tiles_of(N), bytes, base,
                              static_cast<float*>(base), pad, gathered, ssq, dev};
   std::lock_guard<std::mutex> lk(g_mu);
   g_by_slots[(uintptr_t)h->slots] = h;
@@ -253,7 +261,7 @@ int enqueue_call(const uint16_t* A_r, const uint16_t* x, float* slots, uint32_t*
     if (!h || h->pad != pad || h->W != W || h->N != N || h->B != B) return GSA_EINVAL;
     if (gathered && h->gathered != gathered) return GSA_EINVAL;
     a.row_stride = (int)h->row_stride;
-    a.tiles = (int)h->tiles;
+    a.tiles = (int)((N + l.tile_rows - 1) / l.tile_rows);  // == h->tiles for 16-row tiles
     a.ssq = h->ssq;
     if (l.lds_bytes > 65536 && !g_big_lds_ready.count(l.kernel)) {
       // Opt in once to the largest dynamic LDS any shape of this kernel may use.
@@ -275,7 +283,7 @@ int enqueue_call(const uint16_t* A_r, const uint16_t* x, float* slots, uint32_t*
   a.W = W;
   a.rank = rank;
   a.gathered = gathered;
-  a.chunk_tiles = (int)(((N + W - 1) / W + GSA_FLAG_TILE_ROWS - 1) / GSA_FLAG_TILE_ROWS);
+  a.chunk_tiles = (int)big_tiles_of((N + W - 1) / W);  // whole 16-row tiles per rank
   a.epi = ep ? 1 : 0;
   a.y_bf16 = ep && ep->y_dtype == GSA_DTYPE_BF16 ? 1 : 0;
   a.eps = ep ? ep->eps : 0.0f;
@@ -354,7 +362,7 @@ int gsa_set_wait_timeout_us(uint32_t us) {
 
 int64_t gsa_a2a_pad_words(int W, int ne, int64_t H) {
   if (W < 1 || W > GSA_MAX_W || ne < 1 || ne > 256 || H < 1 || H > ((int64_t)1 << 30)) return -1;
-  return GSA_PAD_HEADER_WORDS + (int64_t)W * ne * gsa_signal_pad_row_stride(H);
+  return GSA_PAD_HEADER_WORDS + (int64_t)W * ne * moe_row_stride(H);
 }
 
 int gsa_a2a_alloc(int W, int ne, int64_t H, int64_t rows_out, gsa_a2a** out) {
@@ -378,7 +386,7 @@ int gsa_a2a_alloc(int W, int ne, int64_t H, int64_t rows_out, gsa_a2a** out) {
     return GSA_EHIP;
   }
   uint32_t* pads = reinterpret_cast<uint32_t*>(static_cast<char*>(base) + buf_bytes);
-  gsa_a2a* h = new gsa_a2a{W, ne, H, rows_out, gsa_signal_pad_row_stride(H), pad_words, base,
+  gsa_a2a* h = new gsa_a2a{W, ne, H, rows_out, moe_row_stride(H), pad_words, base,
                            static_cast<float*>(base), pads, dev};
   std::lock_guard<std::mutex> lk(g_mu);
   g_a2a.insert(h);
@@ -468,7 +476,7 @@ int gsa_moe_gemm_all_to_all(const uint16_t* X, const uint16_t* Wd, const int32_t
   a.rank = rank;
   a.ne = ne;
   a.C = (int)(F / 8);
-  a.tiles = (int)tiles_of(H);
+  a.tiles = (int)moe_tiles_of(H);
   a.H = H;
   a.F = F;
   a.rows_in = rows_in;

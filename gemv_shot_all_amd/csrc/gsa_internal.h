@@ -56,10 +56,10 @@ struct GemvArgs {
   int W;
   int rank;
   int row_stride;         // words between flag rows
-  int tiles;              // ceil(N / 16)
+  int tiles;              // workgroup tiles: ceil(N / tile rows of the kernel)
   uint64_t timeout_ticks; // device wall-clock ticks a wait may take
-  // Two-shot variant (the kernels' TS instances): rank p owns tiles
-  // [p * chunk_tiles, (p + 1) * chunk_tiles), reduces them into gathered
+  // Two-shot variant (the kernels' TS instances, 16-row tiles): rank p owns
+  // tiles [p * chunk_tiles, (p + 1) * chunk_tiles), reduces them into gathered
   // (N x B) and raises its reduced-chunk flag (pad row W + p); other rows are
   // copied from their owner's gathered rows once its flag shows the epoch.
   int chunk_tiles;
@@ -76,19 +76,24 @@ struct GemvArgs {
   float* ssq;             // tiles x kEpiRecordWords: partial sums of squares + mark (scratch)
 };
 
+// Rows per flag tile of the pad (GSA_FLAG_TILE_ROWS) and per workgroup of the
+// kernels that run the fused epilogue, the two-shot variant and MFMA.
+constexpr int kBigTileRows = 16;
+
 // A ready-to-launch kernel choice for one (B, C) shape.
 struct Launch {
   const void* kernel;
   unsigned block;         // threads per workgroup
   size_t lds_bytes;       // dynamic LDS
+  int tile_rows;          // output rows per workgroup (4 or 16)
 };
 
 // Pick the kernel for W ranks, batch B (1..16) and C chunks per row (with
 // the epilogue's extra LDS if epi).  Returns false if the shape exceeds the
 // LDS staging bound.
 bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, Launch* out);
-// Dynamic LDS bytes the kernel chosen for (W, B, C, epi) needs.
-size_t gemv_lds_bytes(int W, int B, int C, bool epi);
+// Dynamic LDS bytes a kernel of tile_rows rows per workgroup needs for (W, B, C, epi).
+size_t gemv_lds_bytes(int W, int B, int C, bool epi, int tile_rows);
 
 hipError_t launch_gemv(const Launch& l, const GemvArgs& a, hipStream_t s);
 // Also clears the fused epilogue's scratch after its records (flags and

@@ -58,11 +58,22 @@ extern "C" {
 
 /* Flag value of a simulated peer: "published for every epoch". */
 #define GSA_FLAG_PUBLISHED 0xFFFFFFFFu
-/* Signal-pad protocol: one flag per rank per tile of 16 output rows (all
- * batch columns).  T = ceil(N / 16) tiles. */
-#define GSA_FLAG_TILE_ROWS 16
+/* Signal-pad protocol: one flag per rank per flag tile of 4 output rows (all
+ * batch columns).  T = ceil(N / 4) flag tiles.  A workgroup computes 4 or 16
+ * rows (chosen from K/W and B), so it raises and waits on 1 or 4 flags. */
+#define GSA_FLAG_TILE_ROWS 4
+/* Within a rank's row the flags come in groups of GSA_FLAG_GROUP_TILES
+ * consecutive flag tiles (16 rows), one group per GSA_FLAG_GROUP_WORDS words
+ * (128 bytes): flag tile t sits at word (t / 4) * 32 + t % 4.  A 16-row
+ * workgroup's flags share one line, and neighbouring workgroups' flags do
+ * not. */
+#define GSA_FLAG_GROUP_TILES 4
+#define GSA_FLAG_GROUP_WORDS 32
+/* The MoE combine's flags cover tiles of 16 output features. */
+#define GSA_MOE_TILE_ROWS 16
 /* The pad starts with GSA_PAD_HEADER_WORDS status words, then 2W rows of
- * flags, row r at word GSA_PAD_HEADER_WORDS + r * gsa_signal_pad_row_stride(N):
+ * flags, row r at word GSA_PAD_HEADER_WORDS + r * gsa_signal_pad_row_stride(N)
+ * (flag tile t of the row at word (t / 4) * 32 + t % 4 of it):
  * rows 0..W-1 hold each rank's slot flags, rows W..2W-1 each rank's
  * reduced-chunk flags of the two-shot variant. */
 #define GSA_PAD_HEADER_WORDS 16
@@ -99,8 +110,9 @@ uint32_t *gsa_symm_signal_pad(const gsa_symm *h);
  * (on one GPU the caller fills the other ranks' rows).  NULL if unknown. */
 float *gsa_symm_gathered(const gsa_symm *h);
 
-/* Words between consecutive rank rows of the pad for N rows (>= ceil(N/16),
- * a multiple of 64).  Returns -1 for N < 1. */
+/* Words between consecutive rank rows of the pad for N rows
+ * (ceil(ceil(N / 4) / 4) groups of 32 words, rounded up to a multiple of 64).
+ * Returns -1 for N < 1. */
 int64_t gsa_signal_pad_row_stride(int64_t N);
 
 /* Reset a pad: flag rows p and W + p := GSA_FLAG_PUBLISHED if bit p of
@@ -126,11 +138,12 @@ int gsa_signal_pad_reset(uint32_t *pad, int W, int64_t N, uint32_t published_mas
  * is launched.
  * A_r must hold finite values (chunks past a row's end are paired with zeros).
  * No host sync, no allocation.  All calls on one buffer must use one stream
- * (flags are indexed by tile, not by stream).  Each tile's flag epoch is its
+ * (flags are indexed by tile, not by stream).  Each flag tile's epoch is its
  * own previous flag + 1, so at most 2^32 - 2 calls fit between resets.
- * Device-side failures (a wait that exceeded the timeout, a bad own flag row)
- * leave that tile's `out` rows unwritten and are reported by
- * gsa_signal_pad_status.  Errors: GSA_EINVAL, GSA_EHIP (launch failed). */
+ * Device-side failures leave `out` rows unwritten and are reported by
+ * gsa_signal_pad_status: a wait that exceeded the timeout, the rows of that
+ * flag tile; an unusable own flag, every row of its workgroup (which then
+ * raises none of its flags).  Errors: GSA_EINVAL, GSA_EHIP (launch failed). */
 int gsa_gemv_allreduce(const uint16_t *A_r, const uint16_t *x, float *slots,
                        uint32_t *pad, float *out, int W, int rank, int64_t N,
                        int64_t K, int B, void *stream);
@@ -138,8 +151,8 @@ int gsa_gemv_allreduce(const uint16_t *A_r, const uint16_t *x, float *slots,
 /* The two-stage variant of the same operator: the documentation's op
  * reference lists a two-stage all-reduce (two_shot_all_reduce_) beside the
  * one-shot one, read here as reduce-scatter then all-gather.  Each rank owns
- * one chunk of ceil(ceil(N / W) / 16) * 16 rows (whole tiles; rank p owns
- * rows [p * chunk, (p + 1) * chunk)).  A call computes and publishes y_r and
+ * one chunk of ceil(ceil(N / W) / 16) * 16 rows (whole 16-row workgroup
+ * tiles; rank p owns rows [p * chunk, (p + 1) * chunk)).  A call computes and publishes y_r and
  * the slot flags as gsa_gemv_allreduce does; for the rows of its own chunk it
  * waits for every rank's slot flag, writes out = the rank-order sum from zero
  * (the one-shot rule, same bits) and publishes it into `gathered` with its
@@ -187,7 +200,7 @@ typedef struct gsa_epilogue {
  * rows; otherwise the tile that completes the count normalises all N rows.
  * Both give the same bits.  The tile-side wait is bounded (twice the
  * timeout of gsa_set_wait_timeout_us); if it expires, gsa_signal_pad_status
- * reports GSA_ETIMEOUT with that tile and peer -1.  If any tile of the call
+ * reports GSA_ETIMEOUT with that tile's first flag tile and peer -1.  If any tile of the call
  * failed, y and inv_rms are NaN.
  * Requires N <= 2^24 in addition.  Errors: GSA_EINVAL (also: ep or y NULL,
  * unknown y_dtype, misaligned pointer, eps negative or not finite),
@@ -198,9 +211,10 @@ int gsa_gemv_allreduce_rmsnorm(const uint16_t *A_r, const uint16_t *x, float *sl
 
 /* Read the pad's status words after the work queued on `stream` has finished
  * (synchronizes `stream`).  *code [host] := GSA_ESTATE if any call found its
- * own flag row unusable (then *tile := the smallest such tile, *peer := -1),
- * else GSA_ETIMEOUT if any wait expired (then *tile, *peer := the smallest
- * (tile, peer) pair whose wait expired), else GSA_OK (*tile = *peer = -1).
+ * own flag row unusable (then *tile := the smallest such flag tile, *peer :=
+ * -1), else GSA_ETIMEOUT if any wait expired (then *tile, *peer := the
+ * smallest (flag tile, peer) pair whose wait expired), else GSA_OK (*tile =
+ * *peer = -1).
  * Words stay set until the next gsa_signal_pad_reset.
  * Errors: GSA_EINVAL (unknown pad), GSA_EHIP. */
 int gsa_signal_pad_status(const uint32_t *pad, void *stream, int *code,
@@ -247,9 +261,10 @@ const char *gsa_strerror(int code);
 typedef struct gsa_a2a gsa_a2a;
 
 /* Words of one signal pad: GSA_PAD_HEADER_WORDS status words, then W * ne
- * flag rows of gsa_signal_pad_row_stride(H) words; row p * ne + e holds the
- * flags of source rank p's local expert e, one per 16-feature tile.  -1 on a
- * bad argument. */
+ * flag rows of S = (pad words - GSA_PAD_HEADER_WORDS) / (W * ne) words
+ * (ceil(H / GSA_MOE_TILE_ROWS) rounded up to a multiple of 64); row
+ * p * ne + e holds the flags of source rank p's local expert e, one per
+ * 16-feature tile.  -1 on a bad argument. */
 int64_t gsa_a2a_pad_words(int W, int ne, int64_t H);
 
 /* Allocate (zeroed, host-blocking, init time) W combine buffers of

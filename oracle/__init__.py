@@ -52,10 +52,10 @@ _f32p = ctypes.POINTER(ctypes.c_float)
 _f64p = ctypes.POINTER(ctypes.c_double)
 
 # Protocol reading (the pages leave the granularity open): one flag per rank
-# per tile of 16 output rows (all batch columns), so a rank's row of the pad
-# holds ceil(N / 16) flags.  A simulated peer that has "published for every
+# per flag tile of 4 output rows (all batch columns), so a rank's row of the
+# pad holds ceil(N / 4) flags.  A simulated peer that has "published for every
 # call" holds the all-ones word.
-FLAG_TILE_ROWS = 16
+FLAG_TILE_ROWS = 4
 FLAG_PUBLISHED = 0xFFFFFFFF
 
 # The error bound every fp32 GPU result must meet against the fp64 value:

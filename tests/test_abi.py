@@ -36,7 +36,10 @@ def test_library_exports_every_declared_symbol():
 def test_constants_match_header():
     text = header_text()
     for name in ["GSA_OK", "GSA_EINVAL", "GSA_ENOMEM", "GSA_EHIP", "GSA_ETIMEOUT",
-                 "GSA_ESTATE", "GSA_ESPLIT", "GSA_FLAG_TILE_ROWS", "GSA_PAD_HEADER_WORDS",
+                 "GSA_ESTATE", "GSA_ESPLIT", "GSA_FLAG_TILE_ROWS", "GSA_FLAG_GROUP_TILES",
+                 "GSA_FLAG_GROUP_WORDS",
+                 "GSA_MOE_TILE_ROWS",
+                 "GSA_PAD_HEADER_WORDS",
                  "GSA_MAX_W", "GSA_MAX_B", "GSA_MOE_MAX_TOKENS", "GSA_MOE_MAX_F"]:
         m = re.search(rf"#define\s+{name}\s+\(?\s*(-?\d+)\s*\)?", text)
         assert m, name
@@ -55,10 +58,13 @@ def test_strerror_covers_codes():
 
 def test_row_stride():
     assert gsa.gsa_signal_pad_row_stride(0) == -1
+    # one flag per 4 rows, groups of 4 flags 32 words apart, rounded up to 64 words
     assert gsa.gsa_signal_pad_row_stride(1) == 64
-    assert gsa.gsa_signal_pad_row_stride(1024) == 64
-    assert gsa.gsa_signal_pad_row_stride(1025) == 128
-    assert gsa.gsa_signal_pad_row_stride(8192) == 512
+    assert gsa.gsa_signal_pad_row_stride(32) == 64
+    assert gsa.gsa_signal_pad_row_stride(33) == 128
+    assert gsa.gsa_signal_pad_row_stride(8192) == 16384
+    # flag tile t at word (t // 4) * 32 + t % 4 of a rank's row
+    assert [int(gsa.flag_word(t)) for t in range(10)] == [0, 1, 2, 3, 32, 33, 34, 35, 64, 65]
 
 
 P = 0x10000  # a 16-byte-aligned fake address: never dereferenced, rejected first

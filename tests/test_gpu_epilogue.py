@@ -135,7 +135,9 @@ def test_edge_epilogue(W, N, Ks, B, rank, bias, weight, eps):
 def test_repeats_bit_identical_and_mixed_with_plain_calls():
     """Three epilogue calls with plain calls in between (which leave the
     epilogue's counts alone): y and inv_rms are right and bit-identical every
-    time."""
+    time.  (On this shape the plain call runs 4-row workgroups and the
+    epilogue call 16-row ones, so their partial sums may round differently:
+    each call's results are checked right after it.)"""
     _say("[epilogue] repeats")
     d = gi.make_inputs("c2", seed=4, rank=0)
     er = EpiRun(d, seed=4)
@@ -143,12 +145,16 @@ def test_repeats_bit_identical_and_mixed_with_plain_calls():
         ys, invs = [], []
         for i in range(3):
             er.call()
-            er.r.call()  # a plain call on the same buffer
             out, sl, y, inv, status, hdr = er.results()
             assert status == (gsa.GSA_OK, -1, -1)
             check_epilogue(er, out, sl, y, inv, f"repeat {i}")
             ys.append(y.copy())
             invs.append(inv.copy())
+            er.r.out.fill_(float("nan"))
+            er.r.call()  # a plain call on the same buffer
+            out, sl, _, status = er.r.results()
+            assert status == (gsa.GSA_OK, -1, -1)
+            check_against_oracle(d["A"], d["x"], er.slots_in, 0, out, sl, f"plain {i}")
     finally:
         er.close()
     for i in range(1, 3):
@@ -213,5 +219,36 @@ def test_graph_replays_match_eager():
             assert status == (gsa.GSA_OK, -1, -1)
             assert np.array_equal(y, y0) and np.array_equal(inv.view(np.uint32),
                                                             inv0.view(np.uint32)), f"replay {rep}"
+    finally:
+        er.close()
+
+
+@pytest.mark.parametrize("K", [256, 6400])
+def test_plain_and_epilogue_calls_share_a_buffer(K):
+    """Plain calls (4-row workgroups on short rows) and epilogue calls (16-row
+    workgroups) alternate on one buffer: every call raises each 4-row flag
+    tile once, so the epochs stay in step and every result is right."""
+    _say(f"[epilogue] plain and epilogue calls on one buffer, K={K}")
+    W, rank = 4, 2
+    d = gi.make_shard_inputs(W, 200, K, 3, seed=21, rank=rank)
+    er = EpiRun(d, rank=rank, seed=21)
+    try:
+        for i, kind in enumerate(["plain", "epilogue", "plain", "epilogue", "plain"]):
+            er.r.out.fill_(float("nan"))
+            if kind == "plain":
+                er.r.call()
+                out, sl, flags, status = er.r.results()
+                assert status == (gsa.GSA_OK, -1, -1), (kind, i, status)
+                check_against_oracle(d["A"], d["x"], er.slots_in, rank, out, sl, f"{kind} {i}")
+            else:
+                er.y.fill_(float("nan"))
+                er.call()
+                out, sl, y, inv, status, hdr = er.results()
+                assert status == (gsa.GSA_OK, -1, -1), (kind, i, status)
+                check_epilogue(er, out, sl, y, inv, f"{kind} {i}")
+                flags = er.r.buf.flags()
+            expect = oracle.pad_after_calls(oracle.pad_after_reset(W, 200, all_but(W, rank)),
+                                            rank, i + 1)
+            assert np.array_equal(flags, expect), f"{kind} {i}: flag state"
     finally:
         er.close()

@@ -203,19 +203,24 @@ def test_timeout_reports_missing_peer_and_skips_out():
     assert np.array_equal(flags, oracle.pad_after_calls(before, rank, 1))
 
 
-def test_timeout_single_tile():
-    """One flag word of peer 2 overwritten with 0 from the host: only that
-    tile times out; every other tile is correct."""
-    _say("[protocol] timeout, one tile withheld")
+@pytest.mark.parametrize("K,t_bad", [
+    (128, 3),    # short rows: 4-row workgroups, one flag tile each
+    (3200, 5),   # longer rows: 16-row workgroups; flag tile 5 is the second of its workgroup
+    (128, 19),   # the last flag tile
+])
+def test_timeout_single_tile(K, t_bad):
+    """One flag word of peer 2 overwritten with 0 from the host: only the rows
+    of that flag tile stay unwritten, whatever the workgroup size; every other
+    row is correct."""
+    _say(f"[protocol] timeout, one flag tile withheld, K={K} t={t_bad}")
     W, rank, N, B = 4, 0, 80, 3
-    d = gi.make_shard_inputs(W, N, 128, B, seed=11, rank=rank)
+    d = gi.make_shard_inputs(W, N, K, B, seed=11, rank=rank)
     gsa.gsa_set_wait_timeout_us(200)
     try:
         r = Run(d["A"], d["x"], d["slots"].copy(), rank)
         try:
-            t_bad = 3
             pad = r.buf.pad_view()
-            pad[gsa.GSA_PAD_HEADER_WORDS + 2 * r.buf.row_stride + t_bad] = 0
+            pad[gsa.GSA_PAD_HEADER_WORDS + 2 * r.buf.row_stride + gsa.flag_word(t_bad)] = 0
             torch.cuda.synchronize()
             r.call()
             out, sl, flags, status = r.results()
@@ -224,7 +229,8 @@ def test_timeout_single_tile():
     finally:
         gsa.gsa_set_wait_timeout_us(100000)
     assert status == (gsa.GSA_ETIMEOUT, t_bad, 2)
-    rows = slice(16 * t_bad, min(N, 16 * (t_bad + 1)))
+    ft = oracle.FLAG_TILE_ROWS
+    rows = slice(ft * t_bad, min(N, ft * (t_bad + 1)))
     assert np.isnan(out[rows]).all()
     mask = np.ones(N, bool)
     mask[rows] = False

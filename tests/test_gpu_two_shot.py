@@ -35,7 +35,7 @@ def own_rows(N, W, rank):
 def own_tiles(N, W, rank):
     rows = own_rows(N, W, rank)
     T = oracle.flag_tiles(N)
-    return [t for t in range(T) if rows.start <= 16 * t < rows.stop]
+    return [t for t in range(T) if rows.start <= oracle.FLAG_TILE_ROWS * t < rows.stop]
 
 
 class TwoShotRun:

@@ -25,7 +25,7 @@ def test_bound_formula():
 def test_pad_model():
     import numpy as np
     f = oracle.pad_after_reset(3, 40, 0b101)
-    assert f.shape == (3, 3)
+    assert f.shape == (3, 10)  # ceil(40 / 4) flag tiles
     assert (f[0] == 0xFFFFFFFF).all() and (f[1] == 0).all() and (f[2] == 0xFFFFFFFF).all()
     g = oracle.pad_after_calls(f, 1, 5)
     assert (g[1] == 5).all() and np.array_equal(g[[0, 2]], f[[0, 2]])
@@ -36,4 +36,4 @@ def test_pad_model():
     tiles, first = oracle.expected_timeouts(h, 1)
     assert tiles == [1] and first == (1, 2)
     tiles, first = oracle.expected_timeouts(oracle.pad_after_reset(4, 33, 0b0001), 1)
-    assert tiles == [0, 1, 2] and first == (0, 2)
+    assert tiles == list(range(9)) and first == (0, 2)
