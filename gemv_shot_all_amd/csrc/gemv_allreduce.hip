@@ -123,14 +123,14 @@ __device__ __forceinline__ uint32_t* flag_ptr(const GemvArgs& a, int r, int64_t 
 __device__ __forceinline__ uint32_t* flag2_ptr(const GemvArgs& a, int r, int64_t t) {
   return a.pad + GSA_PAD_HEADER_WORDS + (int64_t)(a.W + r) * a.row_stride + flag_word(t);
 }
-// The rank that reduces workgroup tile t: the calling rank, or in the
-// two-shot variant (TS, 16-row tiles only) the owner of the tile's chunk.
-// The kernels take TS as a template argument so that the one-shot instances
-// carry none of this code.
-template <bool TS>
+// The rank that reduces workgroup tile t of TR rows: the calling rank, or in
+// the two-shot variant (TS) the owner of the tile's chunk (chunks are whole
+// 16-row blocks, so a tile has one owner).  The kernels take TS as a template
+// argument so that the one-shot instances carry none of this code.
+template <bool TS, int TR>
 __device__ __forceinline__ int tile_owner(const GemvArgs& a, int64_t t) {
   if constexpr (TS)
-    return min(a.W - 1, (int)((uint32_t)t / (uint32_t)a.chunk_tiles));
+    return min(a.W - 1, (int)((uint32_t)t / (uint32_t)(a.chunk_tiles * (kBigTile / TR))));
   else
     return a.rank;
 }
@@ -172,7 +172,7 @@ __device__ __forceinline__ void issue_peer_tile(const GemvArgs& a, int lane, int
   const int per_lane = (TR * a.B + 63) / 64;  // 1, 2 or 4
   const int64_t first = tile * TR * a.B;      // first element of the tile in a slot
   const int64_t last = NB - 1;
-  const int owner = tile_owner<TS>(a, tile);
+  const int owner = tile_owner<TS, TR>(a, tile);
   // Two-shot, a chunk another rank reduces: its published values, held in
   // v[0] (store_peer_tile puts them at the owner's place in the peer tile).
   const bool copy = TS && owner != a.rank;
@@ -192,7 +192,7 @@ __device__ __forceinline__ void store_peer_tile(const GemvArgs& a, int lane, int
                                                 const float (&v)[kMaxW][kPerLane<TR>], float* pe) {
   const int tb = TR * a.B;  // elements of one rank's tile
   const int per_lane = (tb + 63) / 64;
-  const int owner = tile_owner<TS>(a, tile);
+  const int owner = tile_owner<TS, TR>(a, tile);
   const bool copy = TS && owner != a.rank;  // v[0] holds the owner's values
 #pragma unroll
   for (int r = 0; r < kMaxW; ++r) {
@@ -212,7 +212,7 @@ __device__ __forceinline__ void store_peer_tile(const GemvArgs& a, int lane, int
 // flag tile q and s_ctl[1] = kMustWait / kPeersReady / kBadOwnRow; returns
 // s_ctl[1].  A workgroup with an unusable own flag (marked published, or its
 // epochs exhausted) records the first such flag tile and does nothing else.
-template <bool TS>
+template <bool TS, int TR>
 __device__ __forceinline__ uint32_t comm_decide(const GemvArgs& a, int lane, int64_t tile,
                                                 const FlagSpan& fs, uint32_t fl, uint32_t* s_ctl) {
   const int q = lane_q(fs, lane);
@@ -231,7 +231,7 @@ __device__ __forceinline__ uint32_t comm_decide(const GemvArgs& a, int lane, int
   }
   const uint32_t epoch = own + 1u;
   if (in_span && p == a.rank) s_ctl[4 + q] = epoch;
-  const int owner = tile_owner<TS>(a, tile);
+  const int owner = tile_owner<TS, TR>(a, tile);
   bool lane_ok = !in_span || p == a.rank || fl >= epoch;
   if (TS && owner != a.rank) {  // two-shot: only the owner's reduced chunk is needed
     const uint32_t e2 = __shfl(fl, min(lane, fs.nf - 1) * 8 + a.rank) + 1u;
@@ -246,11 +246,11 @@ __device__ __forceinline__ uint32_t comm_decide(const GemvArgs& a, int lane, int
 // Bounded wait for every peer's flag >= the epoch of each of the workgroup's
 // flag tiles.  Returns the mask of complete flag tiles (bit q); on expiry
 // records the smallest missing (flag tile, peer) in the pad header.
-template <bool TS>
+template <bool TS, int TR>
 __device__ uint32_t wait_peers(const GemvArgs& a, int lane, int64_t tile, const FlagSpan& fs,
                                const uint32_t* s_ctl) {
   const uint64_t start = wall_clock64();
-  const int owner = tile_owner<TS>(a, tile);
+  const int owner = tile_owner<TS, TR>(a, tile);
   const bool copy = TS && owner != a.rank;  // two-shot: the owner's reduced-chunk flags
   const int q = copy ? min(lane, fs.nf - 1) : lane_q(fs, lane);
   const bool in_span = copy ? lane < fs.nf : lane_in_span(a, fs, lane);
@@ -324,7 +324,7 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
   if (kEpi && a.epi && lane == 0)
     before = __hip_atomic_fetch_add(epi_count(a, epi_started_off(a.tiles), grp), 1ull,
                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint32_t state = comm_decide<TS>(a, lane, tile, fs, fl, s_ctl);
+  const uint32_t state = comm_decide<TS, TR>(a, lane, tile, fs, fl, s_ctl);
   float v[kMaxW][kPerLane<TR>];
   if (state == kPeersReady) issue_peer_tile<TS, TR>(a, lane, tile, v);  // after the flags returned
   __syncthreads();  // B1
@@ -332,7 +332,7 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
   __syncthreads();  // B2
   if (state == kMustWait) {
     // The own flags went out after B2.
-    const uint32_t done = wait_peers<TS>(a, lane, tile, fs, s_ctl);
+    const uint32_t done = wait_peers<TS, TR>(a, lane, tile, fs, s_ctl);
     if (done != 0) {
       // After the flags returned; rows of incomplete flag tiles are never read.
       issue_peer_tile<TS, TR>(a, lane, tile, v);
@@ -344,7 +344,7 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
     }
     __syncthreads();  // B3
   }
-  if (TS && tile_owner<TS>(a, tile) == a.rank) __syncthreads();  // B5
+  if (TS && tile_owner<TS, TR>(a, tile) == a.rank) __syncthreads();  // B5
   if (kEpi && a.epi) {
     // The call's index k (every tile of a call is counted once per group).
     const unsigned long long k =
@@ -439,7 +439,7 @@ __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t ti
   bool ok[OPL];
 #pragma unroll
   for (int e = 0; e < OPL; ++e) ok[e] = ((done >> (n[e] / kFlagRows)) & 1u) != 0;
-  const int owner = tile_owner<TS>(a, tile);
+  const int owner = tile_owner<TS, TR>(a, tile);
   float o[OPL];
 #pragma unroll
   for (int e = 0; e < OPL; ++e) {
@@ -809,8 +809,8 @@ __device__ __forceinline__ void valu_stream(float (&acc)[R][B], uint4 (&ring)[D]
 // once).  WPE is the occupancy (waves per SIMD) the register budget must
 // allow.  NCH > 0 builds a fully unrolled instance for
 // exactly NCH chunks per lane; MASKED instances zero chunks past the row end.
-// TR = NW * (64 / G) * R rows per workgroup (4 or 16; the two-shot variant and
-// the fused epilogue run on 16).  XM: XCD-contiguous tile order (block_tile).
+// TR = NW * (64 / G) * R rows per workgroup (4 or 16; the fused epilogue runs
+// on 16).  XM: XCD-contiguous tile order (block_tile).
 // LDS: x chunks [b][c], one zero chunk, one sink chunk, then the peer tile.
 template <int B, int G, int R, int NW, int NCH, int D, int XPT, int WPE, bool MASKED, bool TS,
           bool XM>
@@ -818,8 +818,7 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   constexpr int NT = NW * 64;
   constexpr int GPW = 64 / G;
   constexpr int TR = NW * GPW * R;
-  static_assert(TR == kBigTile || (TR == kFlagRows && !TS),
-                "16-row tiles, or 4-row tiles of the plain one-shot call");
+  static_assert(TR == kBigTile || TR == kFlagRows, "16-row or 4-row tiles");
   constexpr int V = R * B;
   static_assert(V <= G, "one owner lane per output of a row group");
 
@@ -1152,9 +1151,9 @@ ValuChoice valu_tier(int C) {
 }
 
 // VALU tiers by chunks per row C = Ks / 8 (plus the communication wave):
-//   C <= 64, plain one-shot call: 4 rows per workgroup, 1 wave, half a wave
-//            per row, 2 x 2 rows (more, smaller workgroups: on the Llama-3-8B
-//            o_proj shape 4.05 against 4.49 us per call with 16-row tiles)
+//   C <= 64, no epilogue: 4 rows per workgroup, 1 wave, half a wave per row,
+//            2 x 2 rows (more, smaller workgroups: on the Llama-3-8B o_proj
+//            shape 4.05 against 4.49 us per call with 16-row tiles)
 //   C <= 64 : 16 rows, 4 waves, a full wave per row, 4 rows per wave
 //   C <= 224: 16 rows, 4 waves, half a wave per row, 2 x 2 rows per wave
 //   larger  : 16 rows, 8 waves, a full wave per row, 2 rows per wave
@@ -1163,9 +1162,7 @@ ValuChoice valu_tier(int C) {
 // of rows up to C = 224 go to the XCDs in contiguous runs (block_tile).
 template <int B, bool TS>
 ValuChoice valu_kernel(int C, bool small_tiles) {
-  if constexpr (!TS) {
-    if (small_tiles && C <= 64) return valu_tier<B, 32, 2, 1, 2, 2, 1, false, true>(C);
-  }
+  if (small_tiles && C <= 64) return valu_tier<B, 32, 2, 1, 2, 2, 1, TS, true>(C);
   if (C <= 64) return valu_tier<B, 64, 4, 4, 1, 1, 1, TS, true>(C);
   if (C <= 224) return valu_tier<B, 32, 2, 4, 7, 4, 1, TS, true>(C);
   return valu_tier<B, 64, 2, 8, 7, 3, 5, TS, false>(C);
@@ -1208,9 +1205,9 @@ bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, Launch* ou
   if (W < 1 || W > GSA_MAX_W || B < 1 || B > GSA_MAX_B || C < 1) return false;
   if (B <= 8 && (size_t)B * C * 16 > GSA_MAX_X_LDS_BYTES) return false;  // x staged in LDS
   if (epi && two_shot) return false;  // separate entry points
-  const bool small_tiles = !epi && !two_shot;  // 4-row tiles only for the plain call
+  const bool small_tiles = !epi;  // the fused epilogue counts 16-row tiles
   const ValuChoice k =
-      two_shot ? pick_kernel<true>(B, C, false) : pick_kernel<false>(B, C, small_tiles);
+      two_shot ? pick_kernel<true>(B, C, small_tiles) : pick_kernel<false>(B, C, small_tiles);
   const unsigned block = (unsigned)(k.waves + 1) * 64;
   *out = {k.kernel, block, gemv_lds_bytes(W, B, C, epi, k.tile_rows), k.tile_rows};
   return true;

@@ -58,8 +58,8 @@ struct GemvArgs {
   int row_stride;         // words between flag rows
   int tiles;              // workgroup tiles: ceil(N / tile rows of the kernel)
   uint64_t timeout_ticks; // device wall-clock ticks a wait may take
-  // Two-shot variant (the kernels' TS instances, 16-row tiles): rank p owns
-  // tiles [p * chunk_tiles, (p + 1) * chunk_tiles), reduces them into gathered
+  // Two-shot variant (the kernels' TS instances): rank p owns the 16-row
+  // blocks [p * chunk_tiles, (p + 1) * chunk_tiles), reduces them into gathered
   // (N x B) and raises its reduced-chunk flag (pad row W + p); other rows are
   // copied from their owner's gathered rows once its flag shows the epoch.
   int chunk_tiles;
