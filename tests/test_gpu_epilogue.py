@@ -223,14 +223,14 @@ def test_graph_replays_match_eager():
         er.close()
 
 
-@pytest.mark.parametrize("K", [256, 6400])
-def test_plain_and_epilogue_calls_share_a_buffer(K):
+@pytest.mark.parametrize("Ks", [256, 6400])
+def test_plain_and_epilogue_calls_share_a_buffer(Ks):
     """Plain calls (4-row workgroups on short rows) and epilogue calls (16-row
     workgroups) alternate on one buffer: every call raises each 4-row flag
     tile once, so the epochs stay in step and every result is right."""
-    _say(f"[epilogue] plain and epilogue calls on one buffer, K={K}")
+    _say(f"[epilogue] plain and epilogue calls on one buffer, Ks={Ks}")
     W, rank = 4, 2
-    d = gi.make_shard_inputs(W, 200, K, 3, seed=21, rank=rank)
+    d = gi.make_shard_inputs(W, 200, Ks, 3, seed=21, rank=rank)
     er = EpiRun(d, rank=rank, seed=21)
     try:
         for i, kind in enumerate(["plain", "epilogue", "plain", "epilogue", "plain"]):

@@ -46,6 +46,8 @@ EDGE = [
     (8, 40, 65536, 12, 3),    # MFMA, 1.5 MB of x, ragged N
     (4, 24, 72, 10, 0),       # MFMA, C = 9: fewer k-steps than waves
     (8, 4096, 512, 6, 4),     # short tier, B = 6
+    (4, 123, 512, 8, 2),      # 4-row tiles, B = 8, the last tile 3 rows
+    (2, 6, 64, 7, 1),         # 4-row tiles, C = 8, the second tile 2 rows
     (8, 300, 1024, 7, 6),     # long tier, B = 7
 ]
 

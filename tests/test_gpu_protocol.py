@@ -203,18 +203,18 @@ def test_timeout_reports_missing_peer_and_skips_out():
     assert np.array_equal(flags, oracle.pad_after_calls(before, rank, 1))
 
 
-@pytest.mark.parametrize("K,t_bad", [
+@pytest.mark.parametrize("Ks,t_bad", [
     (128, 3),    # short rows: 4-row workgroups, one flag tile each
     (3200, 5),   # longer rows: 16-row workgroups; flag tile 5 is the second of its workgroup
     (128, 19),   # the last flag tile
 ])
-def test_timeout_single_tile(K, t_bad):
+def test_timeout_single_tile(Ks, t_bad):
     """One flag word of peer 2 overwritten with 0 from the host: only the rows
     of that flag tile stay unwritten, whatever the workgroup size; every other
     row is correct."""
-    _say(f"[protocol] timeout, one flag tile withheld, K={K} t={t_bad}")
+    _say(f"[protocol] timeout, one flag tile withheld, Ks={Ks} t={t_bad}")
     W, rank, N, B = 4, 0, 80, 3
-    d = gi.make_shard_inputs(W, N, K, B, seed=11, rank=rank)
+    d = gi.make_shard_inputs(W, N, Ks, B, seed=11, rank=rank)
     gsa.gsa_set_wait_timeout_us(200)
     try:
         r = Run(d["A"], d["x"], d["slots"].copy(), rank)
