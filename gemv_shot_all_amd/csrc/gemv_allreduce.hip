@@ -364,6 +364,7 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
       s_ctl[3] = all_started ? 1u : 0u;
     }
     __syncthreads();  // E1
+    __syncthreads();  // E1b
     __syncthreads();  // E2
     if (s_ctl[3] || s_ctl[2]) {
       __syncthreads();  // E3
@@ -578,20 +579,22 @@ __device__ __forceinline__ void store_y(const GemvArgs& a, int64_t i, float v) {
 // completes that count is the last.  Every count (and the started counts
 // taken at entry) only grows, so call k is complete when a count reaches
 // (k + 1) times its number of members.  The last tile folds every partial
-// (fold_inv_rms), then publishes inv and a flag holding k + 1 (after the
-// inv stores completed) in kEpiGroups copies, one per group.
+// (fold_inv_rms), then publishes inv in kEpiGroups copies, one per group, as
+// one 64-bit word per column holding k + 1 and the bits of inv (a word is
+// written and read whole, so it needs no separate flag).
 //  - A tile that saw every tile of its call started (s_ctl[3], looked up by
 //    the communication wave) may wait: every other tile is resident or done
-//    and finishes on its own.  It marks its record with k + 1, waits
-//    (bounded) for its group's copy of the flag, reads inv from that copy and
-//    normalises its own rows from registers.
+//    and finishes on its own.  It marks its record with k + 1, polls
+//    (bounded) its group's copy until every column shows k + 1, takes inv
+//    from it and normalises its own rows from registers.
 //  - Any other tile marks 0 and leaves; the last tile also normalises the
 //    rows of every tile not marked k + 1, re-reading out (stored coherently
 //    for this).
 // A row that failed (its flag tile's wait expired, or a bad own row)
-// contributes NaN, so y comes out NaN for that call.  Barriers: E1 (squares in LDS, out stores
-// completed), E2 (count taken), then, in the last tile and in waiting tiles,
-// E3 (wave sums in LDS, or the flag seen) and E4 (inv in LDS).
+// contributes NaN, so y comes out NaN for that call.  Barriers: E1 (squares
+// in LDS), E1b (out stores and the record completed), E2 (count taken), then,
+// in the last tile and in waiting tiles, E3 (wave sums in LDS, or inv seen)
+// and E4 (inv in LDS).
 template <int BM, int OPL>
 __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
                                const bool (&own)[OPL], const bool (&live)[OPL],
@@ -615,16 +618,16 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
       zz[n[e] * 16 + b] = ok[e] ? sq : __builtin_nanf("");
     }
   }
-  wait_vm_all();    // this wave's out stores are at the coherence point ...
-  __syncthreads();  // E1 ... in every compute wave, and the squares are in LDS
+  __syncthreads();  // E1: the squares are in LDS
   const unsigned long long k = *s_epi_k;
   const uint32_t mark = (uint32_t)(k + 1ull);
   const bool waits = s_ctl[3] != 0;
   const int grp = (int)(tile % kEpiGroups);
   float* rec = a.ssq + tile * kEpiRecordWords;
-  // This tile's group copy of the published inv and flag.
-  float* inv_copy = a.ssq + epi_inv_off(a.tiles) + (int64_t)grp * kEpiRecordWords;
-  uint32_t* inv_flag = reinterpret_cast<uint32_t*>(inv_copy + 16);
+  // This tile's group copy of the published inv: per column one 64-bit word
+  // (mark in the high half, the fp32 bits of inv in the low half).
+  const unsigned long long* inv_copy = reinterpret_cast<const unsigned long long*>(
+      a.ssq + epi_inv_off(a.tiles) + (int64_t)grp * kEpiRecordWords);
   if (wave == 0) {
     if (lane < a.B) {
       float part = 0.0f;
@@ -634,7 +637,12 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
     if (lane == 16)
       __hip_atomic_store(reinterpret_cast<uint32_t*>(rec + 16), waits ? mark : 0u,
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    wait_vm_all();  // the record is at the coherence point before the count
+  }
+  // One wait covers each wave's out stores and wave 0's record: both are at
+  // the coherence point in every compute wave before the count.
+  wait_vm_all();
+  __syncthreads();  // E1b
+  if (wave == 0) {
     if (lane == 0) {
       uint32_t last = 0;
       const unsigned long long g_before =
@@ -657,37 +665,46 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
   if (!last && !waits) return;
 
   if (last) {
-    // Every tile has published: fold, then publish inv and the flag.
+    // Every tile has published: fold, then publish inv.
     fold_inv_rms<BM>(a, wave, lane, nt, wsum, s_inv);  // contains E3
     if (wave == 0) {
-      // Lane g writes group g's copy: inv, then (once inv completed) the flag.
-      float* copy = a.ssq + epi_inv_off(a.tiles) + (int64_t)lane * kEpiRecordWords;
-      for (int c = 0; c < a.B; ++c) store_coherent(&copy[c], s_inv[c]);
+      // Lane g writes group g's copy, one self-validating 64-bit word per
+      // column, so no wait has to separate the values from a flag.
+      unsigned long long* copy = reinterpret_cast<unsigned long long*>(
+          a.ssq + epi_inv_off(a.tiles) + (int64_t)lane * kEpiRecordWords);
+      for (int c = 0; c < a.B; ++c)
+        __hip_atomic_store(&copy[c],
+                           ((unsigned long long)mark << 32) | __float_as_uint(s_inv[c]),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (a.inv_rms && lane < a.B) a.inv_rms[lane] = s_inv[lane];
-      wait_vm_all();  // inv at the coherence point before the flag
-      __hip_atomic_store(reinterpret_cast<uint32_t*>(copy + 16), mark, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
     }
   } else {
-    if (wave == 0 && lane == 0) {
-      bool seen = true;
+    if (wave == 0) {
+      // Lane c < B polls column c's word until every column shows this call's
+      // mark; its low half is then inv.  Other tiles may still be in their
+      // bounded peer waits: allow twice that.
       const uint64_t start = wall_clock64();
-      // Other tiles may still be in their bounded peer waits: allow twice that.
-      while (__hip_atomic_load(inv_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != mark) {
+      float inv = __builtin_nanf("");
+      for (;;) {
+        const unsigned long long w = __hip_atomic_load(
+            &inv_copy[min(lane, a.B - 1)], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool seen = lane >= a.B || (uint32_t)(w >> 32) == mark;
+        if (__ballot(!seen) == 0) {
+          inv = __uint_as_float((uint32_t)w);
+          break;
+        }
         if (wall_clock64() - start > 2 * a.timeout_ticks + 1000000ull) {
-          atomicOr(a.pad + kHdrErrorBits, kErrEpiWait);
-          atomicMin(a.pad + kHdrEpiWaitTile, (uint32_t)(tile * (kBigTile / kFlagRows)));
-          seen = false;
+          if (lane == 0) {
+            atomicOr(a.pad + kHdrErrorBits, kErrEpiWait);
+            atomicMin(a.pad + kHdrEpiWaitTile, (uint32_t)(tile * (kBigTile / kFlagRows)));
+          }
           break;
         }
         __builtin_amdgcn_s_sleep(2);
       }
-      s_ctl[1] = seen ? 1u : 0u;  // the protocol state is no longer needed
+      if (lane < a.B) s_inv[lane] = inv;
     }
-    __syncthreads();  // E3: the flag seen (or the wait expired)
-    // inv is loaded only after the flag showed it published.
-    if (wave == 0 && lane < a.B)
-      s_inv[lane] = s_ctl[1] ? load_coherent(&inv_copy[lane]) : __builtin_nanf("");
+    __syncthreads();  // E3: inv in LDS (NaN if the wait expired)
   }
   __syncthreads();  // E4: inv in LDS
   if (waits) {

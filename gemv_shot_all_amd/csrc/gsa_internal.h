@@ -19,7 +19,7 @@ enum : int {
 };
 // The epilogue's scratch (fp32 / uint32 words, 128-byte lines of 32 words):
 //   records   tiles lines: 16 partial sums of squares, the call mark at word 16
-//   inv       kEpiGroups lines: 16 x 1/rms, the published flag at word 16
+//   inv       kEpiGroups lines: 16 64-bit words, column c = (mark << 32) | bits of 1/rms
 //   started   kEpiGroups lines: a 64-bit count at word 0
 //   done      kEpiGroups lines: a 64-bit count at word 0
 //   top       1 line: a 64-bit count of completed groups at word 0
