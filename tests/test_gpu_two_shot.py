@@ -155,13 +155,14 @@ def test_edge_two_shot(W, N, Ks, B, rank):
     run_two_shot_and_check(d, f"W={W} N={N} Ks={Ks} B={B} rank={rank}", seed=3)
 
 
-def test_repeats_and_mixed_with_plain_calls():
+@pytest.mark.parametrize("cfg", ["c3b4", "c2"])  # 16-row and 4-row workgroups
+def test_repeats_and_mixed_with_plain_calls(cfg):
     """two-shot, plain, two-shot, plain, two-shot on one buffer: every
     two-shot call gives the same bits; slot flags count every call; the
     reduced-chunk flags of the own chunk carry the last two-shot call's
     epoch."""
-    _say("[two-shot] repeats mixed with plain calls")
-    d = gi.make_inputs("c3b4", seed=2, rank=3)
+    _say(f"[two-shot] repeats mixed with plain calls, {cfg}")
+    d = gi.make_inputs(cfg, seed=2, rank=3)
     ts = TwoShotRun(d, seed=2)
     W, N = ts.r.W, ts.r.N
     try:
