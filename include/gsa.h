@@ -21,8 +21,8 @@
  * One call of gsa_gemv_allreduce on rank `rank`:
  *   1. y_r[n][b] = sum_k A_r[n][k] x_r[b][k]   (bf16 in, fp32 accumulate)
  *   2. slot[rank][n][b] = y_r[n][b]            (publish)
- *   3. flag[rank][t] = e_t                     (release, per tile t)
- *   4. wait flag[p][t] >= e_t for every p      (acquire, per tile, bounded)
+ *   3. flag[rank][t] = e_t                     (release, per flag tile t of 4 rows)
+ *   4. wait flag[p][t] >= e_t for every p      (acquire, per flag tile, bounded)
  *   5. out[n][b] = ((0 + s_0) + s_1) ... + s_{W-1}, s_r = slot[r][n][b],
  *      fp32 round-to-nearest, s_rank being the value published in step 2.
  * On one GPU the W-1 peer slots are ordinary device memory filled by the
