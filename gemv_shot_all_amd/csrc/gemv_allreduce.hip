@@ -311,7 +311,10 @@ __device__ __forceinline__ unsigned long long* epi_count(const GemvArgs& a, int6
 // its group (after B0) and, once its protocol work is done, looks whether
 // every tile of the call has started (s_ctl[3]: lane g reads group g's
 // count); s_epi_k gets the call's index.
-template <bool TS, int TR>
+// PE: whether the compute waves take the peer tile from LDS when every peer
+// had published at the start (the VALU one-shot kernels load their own peer
+// values instead; a late peer tile always goes through LDS).
+template <bool TS, int TR, bool PE>
 __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
                           uint32_t* s_ctl, unsigned long long* s_epi_k) {
   const FlagSpan fs = flag_span<TR>(a, tile);
@@ -326,9 +329,10 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t state = comm_decide<TS, TR>(a, lane, tile, fs, fl, s_ctl);
   float v[kMaxW][kPerLane<TR>];
-  if (state == kPeersReady) issue_peer_tile<TS, TR>(a, lane, tile, v);  // after the flags returned
+  const bool early_tile = PE && state == kPeersReady;
+  if (early_tile) issue_peer_tile<TS, TR>(a, lane, tile, v);  // after the flags returned
   __syncthreads();  // B1
-  if (state == kPeersReady) store_peer_tile<TS, TR>(a, lane, tile, v, pe);
+  if (early_tile) store_peer_tile<TS, TR>(a, lane, tile, v, pe);
   __syncthreads();  // B2
   if (state == kMustWait) {
     // The own flags went out after B2.
@@ -410,12 +414,20 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
 // for its own slot stores to complete before B2, so the flag stores that
 // follow B2 are ordered after all of them.  nt: compute threads of the
 // workgroup.
+//
+// own_peers (the VALU one-shot kernels, every peer published at the start):
+// the lane already holds its output's peer values in pv (loaded after B1),
+// so out is summed and stored right behind the published value, and the
+// wait before B2 covers only the published value (stores complete in issue
+// order); the out store's round trip overlaps it.
 template <int BM, int OPL, bool TS, int TR>
 __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
                                    const bool (&own)[OPL], const float (&y)[OPL],
                                    const float* pe, float* elds, uint32_t* s_ctl,
                                    const unsigned long long* s_epi_k, uint32_t state, int wave,
-                                   int lane, int nt) {
+                                   int lane, int nt, bool own_peers,
+                                   const float (&pv)[kMaxW]) {
+  static_assert(OPL == 1, "one output per lane");
   const int64_t NB = a.N * a.B;
   const int64_t row0 = tile * TR;
   const FlagSpan fs = flag_span<TR>(a, tile);
@@ -423,12 +435,44 @@ __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t ti
   bool live[OPL];
 #pragma unroll
   for (int e = 0; e < OPL; ++e) live[e] = own[e] && row0 + n[e] < a.N;
+  float o[OPL];
+  bool ok[OPL];
+  if (own_peers) {
+    // out = ((0 + s_0) + s_1) ... + s_{W-1}, the own term being y (as
+    // published); the same order and operations as one_shot_sum.  Summed
+    // before the published value is stored, so that waiting for the peer
+    // values cannot wait for that store.
+    float acc = 0.0f;
+#pragma unroll
+    for (int r = 0; r < kMaxW; ++r) {
+      const float t = r == a.rank ? y[0] : pv[r];
+      acc = acc + (r < a.W ? t : 0.0f);
+    }
+    o[0] = acc;
+    ok[0] = true;
+  }
+  // Nothing may move across: the waits below count on every load being
+  // complete here and on the published value being issued before the out
+  // store.
+  __builtin_amdgcn_sched_barrier(0);
   if (state != kBadOwnRow) {
 #pragma unroll
     for (int e = 0; e < OPL; ++e)
       if (live[e]) store_coherent(&own_slot[(row0 + n[e]) * a.B + b], y[e]);
   }
-  wait_vm_all();    // the published values are at the coherence point ...
+  __builtin_amdgcn_sched_barrier(0);
+  if (own_peers) {
+    if (live[0]) {
+      const int64_t i = (row0 + n[0]) * a.B + b;
+      if (a.epi)
+        store_coherent(&a.out[i], o[0]);  // read back by the workgroup that finishes last
+      else
+        a.out[i] = o[0];
+    }
+    wait_vm_le<1>();  // the published value is at the coherence point ...
+  } else {
+    wait_vm_all();    // the published values are at the coherence point ...
+  }
   __syncthreads();  // B2 ... in every compute wave
   if (state != kBadOwnRow && wave == 0 && lane < fs.nf)
     store_flag(flag_ptr(a, a.rank, fs.f0 + lane), s_ctl[4 + lane]);
@@ -437,13 +481,11 @@ __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t ti
     __syncthreads();  // B3
     done = s_ctl[0];  // a wait expired: those flag tiles' out rows stay unwritten
   }
-  bool ok[OPL];
-#pragma unroll
-  for (int e = 0; e < OPL; ++e) ok[e] = ((done >> (n[e] / kFlagRows)) & 1u) != 0;
   const int owner = tile_owner<TS, TR>(a, tile);
-  float o[OPL];
 #pragma unroll
   for (int e = 0; e < OPL; ++e) {
+    if (own_peers) break;  // out already stored
+    ok[e] = ((done >> (n[e] / kFlagRows)) & 1u) != 0;
     o[e] = 0.0f;
     if (ok[e] && live[e]) {
       const int64_t i = (row0 + n[e]) * a.B + b;
@@ -864,7 +906,7 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   float* elds = pe + a.W * TR * B + 1;  // the epilogue's LDS
 
   if (wave == NW) {
-    comm_wave<TS, TR>(a, lane, tile, pe, s_ctl, &s_epi_k);
+    comm_wave<TS, TR, TS>(a, lane, tile, pe, s_ctl, &s_epi_k);
     return;
   }
 
@@ -904,6 +946,25 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   if (tid == 0) lds_x[zidx] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();  // B1
   const uint32_t state = s_ctl[1];
+  // Every peer published at the start (one-shot call): each lane uses the
+  // peer values of the output it will own (lane li < V: row nloc0 + li / B,
+  // column li % B; other lanes repeat the last owner's addresses), loaded
+  // here, after the flags were seen (B1): they queue behind this wave's A
+  // loads and land as the stream ends.  The loads are unconditional (ranks
+  // past W - 1 repeat rank W - 1's word, and when a peer had not published
+  // the values are never used), so no branch join forces an early wait.
+  const bool own_peers = !TS && state == kPeersReady;
+  const int vidx = min(li, V - 1);
+  float pv[kMaxW];
+  if constexpr (!TS) {
+    const int64_t NB = a.N * a.B;
+    const int64_t oi = min((row0 + vidx / B) * a.B + vidx % B, NB - 1);
+#pragma unroll
+    for (int r = 0; r < kMaxW; ++r) pv[r] = load_coherent(&a.slots[min(r, a.W - 1) * NB + oi]);
+  } else {
+#pragma unroll
+    for (int r = 0; r < kMaxW; ++r) pv[r] = 0.0f;
+  }
 
   float acc[R][B];
 #pragma unroll
@@ -920,12 +981,11 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
     const float t = group_sum<G>(acc[i / B][i % B]);
     yv = li == i ? t : yv;
   }
-  const int vidx = min(li, V - 1);
   const int n[1] = {nloc0 + vidx / B};
   const bool own[1] = {li < V};
   const float y[1] = {yv};
   publish_and_reduce<B, 1, TS, TR>(a, tile, n, vidx % B, own, y, pe, elds, s_ctl, &s_epi_k,
-                                   state, wave, lane, NT);
+                                   state, wave, lane, NT, own_peers, pv);
 }
 
 // MFMA epilogue: each wave's 16 x 16 partial goes to red[wave][n][b]; after
@@ -949,8 +1009,10 @@ __device__ __forceinline__ void mfma_finish(const GemvArgs& a, int64_t tile, int
   const int n[1] = {nl};
   const bool own[1] = {bl < a.B};
   const float yv[1] = {y};
+  const float no_pv[kMaxW] = {};
   publish_and_reduce<GSA_MAX_B, 1, TS, kBigTile>(a, tile, n, bl, own, yv, pe, elds, s_ctl,
-                                                 s_epi_k, state, wave, lane, NW * 64);
+                                                 s_epi_k, state, wave, lane, NW * 64, false,
+                                                 no_pv);
 }
 
 // MFMA path, 8 < B <= 16 (batch padded to 16 with zeros).  The tile's 16 rows
@@ -984,7 +1046,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs a) {
   float* elds = pe + a.W * kBigTile * a.B + 1;  // the epilogue's LDS
 
   if (wave == NW) {
-    comm_wave<TS, kBigTile>(a, lane, tile, pe, s_ctl, &s_epi_k);
+    comm_wave<TS, kBigTile, true>(a, lane, tile, pe, s_ctl, &s_epi_k);
     return;
   }
 
@@ -1078,7 +1140,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a
   float* elds = pe + a.W * kBigTile * a.B + 1;  // the epilogue's LDS
 
   if (wave == NW) {
-    comm_wave<TS, kBigTile>(a, lane, tile, pe, s_ctl, &s_epi_k);
+    comm_wave<TS, kBigTile, true>(a, lane, tile, pe, s_ctl, &s_epi_k);
     return;
   }
 
