@@ -905,8 +905,12 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   float* pe = reinterpret_cast<float*>(lds_x + xchunks + 2);
   float* elds = pe + a.W * TR * B + 1;  // the epilogue's LDS
 
+  // The one-shot kernels with B <= 4 load their own peer values (see below);
+  // at B = 8 that measured slower (8B down_proj shape 6.16 against 5.85 us),
+  // so larger batches take the peer tile from LDS.
+  constexpr bool kOwnPeers = !TS && B <= 4;
   if (wave == NW) {
-    comm_wave<TS, TR, TS>(a, lane, tile, pe, s_ctl, &s_epi_k);
+    comm_wave<TS, TR, !kOwnPeers>(a, lane, tile, pe, s_ctl, &s_epi_k);
     return;
   }
 
@@ -946,17 +950,17 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   if (tid == 0) lds_x[zidx] = make_uint4(0u, 0u, 0u, 0u);
   __syncthreads();  // B1
   const uint32_t state = s_ctl[1];
-  // Every peer published at the start (one-shot call): each lane uses the
+  // Every peer published at the start (one-shot call, B <= 4): each lane uses the
   // peer values of the output it will own (lane li < V: row nloc0 + li / B,
   // column li % B; other lanes repeat the last owner's addresses), loaded
   // here, after the flags were seen (B1): they queue behind this wave's A
   // loads and land as the stream ends.  The loads are unconditional (ranks
   // past W - 1 repeat rank W - 1's word, and when a peer had not published
   // the values are never used), so no branch join forces an early wait.
-  const bool own_peers = !TS && state == kPeersReady;
+  const bool own_peers = kOwnPeers && state == kPeersReady;
   const int vidx = min(li, V - 1);
   float pv[kMaxW];
-  if constexpr (!TS) {
+  if constexpr (kOwnPeers) {
     const int64_t NB = a.N * a.B;
     const int64_t oi = min((row0 + vidx / B) * a.B + vidx % B, NB - 1);
 #pragma unroll
