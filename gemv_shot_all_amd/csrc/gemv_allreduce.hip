@@ -60,7 +60,11 @@ static_assert(kBigTile % kFlagRows == 0 && kBigTile / kFlagRows * kMaxW <= 64,
 //            kBadOwnRow), after a late wait kPeersReady if every flag tile is complete
 //   s_ctl[2], s_ctl[3] the fused epilogue's (see fused_epilogue)
 //   s_ctl[4 + q] the epoch of flag tile q
-constexpr int kCtlWords = 8;
+//   s_ctl[8] 0 from B1 (the VALU compute waves clear it before B1, so that no
+//            LDS store delays B0), 1 once the communication wave has stored
+//            the peer tile it loaded at the start (the compute waves may wait
+//            for it without a barrier)
+constexpr int kCtlWords = 9;
 enum : uint32_t { kMustWait = 0u, kPeersReady = 1u, kBadOwnRow = 2u };
 
 // The workgroup tile of this block.  The dispatcher deals consecutive block
@@ -332,7 +336,12 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
   const bool early_tile = PE && state == kPeersReady;
   if (early_tile) issue_peer_tile<TS, TR>(a, lane, tile, v);  // after the flags returned
   __syncthreads();  // B1
-  if (early_tile) store_peer_tile<TS, TR>(a, lane, tile, v, pe);
+  if (early_tile) {
+    store_peer_tile<TS, TR>(a, lane, tile, v, pe);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the peer tile is in LDS ...
+    if (lane == 0)                       // ... before its mark
+      __hip_atomic_store(&s_ctl[8], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
   __syncthreads();  // B2
   if (state == kMustWait) {
     // The own flags went out after B2.
@@ -905,10 +914,16 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   float* pe = reinterpret_cast<float*>(lds_x + xchunks + 2);
   float* elds = pe + a.W * TR * B + 1;  // the epilogue's LDS
 
-  // The one-shot kernels with B <= 4 load their own peer values (see below);
-  // at B = 8 that measured slower (8B down_proj shape 6.16 against 5.85 us),
-  // so larger batches take the peer tile from LDS.
-  constexpr bool kOwnPeers = !TS && B <= 4;
+  // The one-shot kernels with B <= 4 sum out before publishing (see
+  // publish_and_reduce): the 8-wave tier from the communication wave's peer
+  // tile, which it marks in s_ctl[8] (70B-class shape 12.06 against 12.20 us
+  // with own loads), the others from peer values each lane loads itself
+  // (from the tile: W=2 case 3.37 against 2.92 us, o_proj 4.04 against 3.46).
+  // At B = 8 either measured slower than summing after B2 (8B down_proj shape
+  // 6.16 against 5.85 us with own loads), so larger batches do that.
+  constexpr bool kEarlyOut = !TS && B <= 4;
+  constexpr bool kPeersFromTile = kEarlyOut && NW == 8;
+  constexpr bool kOwnPeers = kEarlyOut && !kPeersFromTile;
   if (wave == NW) {
     comm_wave<TS, TR, !kOwnPeers>(a, lane, tile, pe, s_ctl, &s_epi_k);
     return;
@@ -947,7 +962,10 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
     lds_x[idx < xchunks ? idx : xchunks + 1] = xr[i];  // out-of-range lanes: sink
   }
   for (int idx = tid + XPT * NT; idx < xchunks; idx += NT) lds_x[idx] = xg[idx];
-  if (tid == 0) lds_x[zidx] = make_uint4(0u, 0u, 0u, 0u);
+  if (tid == 0) {
+    lds_x[zidx] = make_uint4(0u, 0u, 0u, 0u);
+    s_ctl[8] = 0u;
+  }
   __syncthreads();  // B1
   const uint32_t state = s_ctl[1];
   // Every peer published at the start (one-shot call, B <= 4): each lane uses the
@@ -957,7 +975,7 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   // loads and land as the stream ends.  The loads are unconditional (ranks
   // past W - 1 repeat rank W - 1's word, and when a peer had not published
   // the values are never used), so no branch join forces an early wait.
-  const bool own_peers = kOwnPeers && state == kPeersReady;
+  const bool own_peers = kEarlyOut && state == kPeersReady;
   const int vidx = min(li, V - 1);
   float pv[kMaxW];
   if constexpr (kOwnPeers) {
@@ -984,6 +1002,15 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   for (int i = 0; i < V; ++i) {
     const float t = group_sum<G>(acc[i / B][i % B]);
     yv = li == i ? t : yv;
+  }
+  if (kPeersFromTile && own_peers) {
+    // The communication wave marks the peer tile stored without waiting for
+    // the compute waves, so this wait ends.
+    while (__hip_atomic_load(&s_ctl[8], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u)
+      __builtin_amdgcn_s_sleep(1);
+    const int idx = (nloc0 + vidx / B) * B + vidx % B;
+#pragma unroll
+    for (int r = 0; r < kMaxW; ++r) pv[r] = pe[min(r, a.W - 1) * (TR * B) + idx];
   }
   const int n[1] = {nloc0 + vidx / B};
   const bool own[1] = {li < V};
