@@ -1,15 +1,27 @@
 """Benchmark: µs per gemv_allreduce call and achieved HBM GB/s on one MI355X.
 
 One step = one fused call (GEMV of this rank's shard, publish, flag release,
-one-shot reduce) on one batch of resident inputs.  Inputs rotate over enough
-independent sets (>= 1 GiB in total) that every call reads A from HBM, not
-from the 256 MB Infinity Cache.
+one-shot reduce) on one batch of resident inputs.  The default workload is
+the 70B-class MLP down_proj (W=8 N=8192 K=28672 B=4), the largest decode
+shape of the workload table.
 
-The timed region replays a HIP graph of K calls (the way a decode loop issues
-them), bracketed by HIP events on the launch stream: the mean launch duration
-is the µs/call value and the denominator of the roofline figure (kernels of
-a graph run back to back, so this matches the kernel trace).  Reported beside
-it: an eager pass of host-issued launches, a warm pass over one resident set
+Inputs rotate over R independent sets whose total exceeds 1 GiB, so that a
+call reads its set from HBM and not from the 256 MB Infinity Cache.  Order of
+work (rank 0, N = 1):
+  1. exactly --warmup untimed calls, on sets 0, 1, ... (mod R);
+  2. a HIP graph is captured holding the K = --steps timed calls, which
+     continue the rotation (call j on set (warmup + j) mod R);
+  3. a 1 GiB read pass over a separate buffer evicts every set
+     from the caches, and a bounded spin kernel keeps the GPU busy while the
+     host queues the replay;
+  4. the timed region: one graph replay between two HIP events recorded on
+     the stream the kernels run on, between two device syncs.  The mean
+     launch duration is the µs/call value and the denominator of the
+     roofline figure.
+So every timed call reads a set that has been untouched for at least 1 GiB
+of other traffic, whatever K is.  Reported beside it, all measured after the
+timed region: a second cold replay of the same graph (steps 3-4 again), an
+eager pass of host-issued launches, a warm pass over one resident set
 (Infinity-Cache resident, not HBM), and the HBM read bandwidth a plain
 streaming-read kernel achieves over 1 GiB on the same GPU.  The CPU oracle
 is timed on a bounded sample of the same workload, on one thread and on all
@@ -37,7 +49,7 @@ import gsa_inputs as gi  # noqa: E402
 
 METRIC = "µs per gemv_allreduce call and achieved HBM GB/s (% of peak), 1 MI355X"
 HBM_PEAK_GBPS = 8000.0
-DEFAULT_CONFIG = "c2"  # Llama-3-8B o_proj decode, W=8 N=4096 K=4096 B=1
+DEFAULT_CONFIG = "c4"  # 70B-class MLP down_proj, W=8 N=8192 K=28672 B=4
 KERNEL_SOURCE = os.path.join(ROOT, "gemv_shot_all_amd", "csrc", "gemv_allreduce.hip")
 MOE_KERNEL_SOURCE = os.path.join(ROOT, "gemv_shot_all_amd", "csrc", "moe_a2a.hip")
 MOE_METRIC = "µs per MoE GEMM + combine all-to-all call and achieved HBM GB/s (% of peak), 1 MI355X"
@@ -110,10 +122,11 @@ class Sets:
         self.two_shot = two_shot
         foot = d["A"].nbytes + d["x"].nbytes + d["slots"].nbytes + 4 * N * B * (2 if two_shot
                                                                                  else 1)
-        R = max(1, -(-rotate_bytes // foot))
+        R = max(1, -(-rotate_bytes // foot) + 1)  # other sets between two uses >= rotate_bytes
         if max_sets:
             R = min(R, max_sets)
         self.R = R
+        self.touched = set()  # sets called at least once
         A0 = torch.from_numpy(d["A"].view(np.int16)).cuda()
         x0 = torch.from_numpy(d["x"].view(np.int16)).cuda()
         s0 = torch.from_numpy(d["slots"]).cuda()
@@ -154,6 +167,7 @@ class Sets:
 
     def call(self, i):
         j = i % self.R
+        self.touched.add(j)
         b = self.bufs[j]
         if self.epilogue:
             self.gsa.gsa_gemv_allreduce_rmsnorm(self.A[j], self.x[j], b.slots, b.pad,
@@ -179,9 +193,10 @@ def check_consistency(sets):
     two-shot variant every row outside the own chunk is the other ranks'
     seeded chunk, copied exactly.  Parity against the oracle at these sizes
     is the GPU tests' job."""
-    out0 = sets.out[0].cpu().numpy()
+    used = sorted(sets.touched)
+    out0 = sets.out[used[0]].cpu().numpy()
     ok = bool(np.all(np.isfinite(out0)))
-    for j in range(1, sets.R, max(1, sets.R // 8)):
+    for j in used[1::max(1, len(used) // 8)]:
         ok = ok and np.array_equal(sets.out[j].cpu().numpy().view(np.uint32),
                                    out0.view(np.uint32))
     if sets.two_shot:
@@ -191,9 +206,71 @@ def check_consistency(sets):
         ok = ok and np.array_equal(out0[rest].view(np.uint32),
                                    sets.gathered_in[rest].view(np.uint32))
     if sets.epilogue:
-        y = sets.epi_tensors[0][2].float().cpu().numpy()
+        y = sets.epi_tensors[used[0]][2].float().cpu().numpy()
         ok = ok and bool(np.all(np.isfinite(y)))
     return ok
+
+
+class ColdTimer:
+    """The timed region's surroundings: a 1 GiB buffer whose read pass
+    evicts the input sets from the caches (L2 and the 256 MB Infinity Cache),
+    and the bounded spin kernel of libgsa_probe.so that keeps the GPU busy
+    while the host queues the graph replay.  The pass only reads (a sum), so
+    it leaves no dirty lines whose write-back would land in the timed region
+    (a read-and-write pass measured 15.2 against 12.7 us per call for the
+    70B-class shape at K = 20: about 50 us of write-back per replay)."""
+
+    def __init__(self, flush_mib):
+        import ctypes
+
+        import torch
+
+        from gemv_shot_all_amd import build as gbuild
+        if not os.path.exists(gbuild.PROBE_LIBRARY):
+            raise RuntimeError(f"{gbuild.PROBE_LIBRARY} is missing; build first")
+        self.L = ctypes.CDLL(gbuild.PROBE_LIBRARY)
+        self.L.gsa_probe_spin.argtypes = [ctypes.c_uint32, ctypes.c_void_p]
+        self.L.gsa_probe_spin.restype = ctypes.c_int
+        # flush_mib == 0 (the --warm mode): no eviction pass.
+        self.flush_buf = (torch.ones((flush_mib << 20) // 4, dtype=torch.float32,
+                                     device="cuda") if flush_mib > 0 else None)
+        self.flush_sum = None
+
+    def replay(self, graph, calls, spin_us=20000):
+        """Flush, spin, then time one replay of `graph` (holding `calls`
+        calls) with HIP events on the current stream.  Returns µs per call."""
+        import ctypes
+
+        import torch
+        stream = torch.cuda.current_stream()
+        if self.flush_buf is not None:
+            self.flush_sum = self.flush_buf.sum()
+        rc = self.L.gsa_probe_spin(spin_us, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"gsa_probe_spin: {rc}")
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        graph.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * ev0.elapsed_time(ev1) / calls
+
+    def close(self):
+        self.flush_buf = self.flush_sum = None
+
+
+def capture(calls_fn):
+    """A HIP graph of the calls that calls_fn() enqueues (captured on a side
+    stream; a replay runs on the current stream)."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            calls_fn()
+    torch.cuda.synchronize()
+    return g
 
 
 def time_cpu_oracle(d, seconds, threads=1, gathered=None):
@@ -300,63 +377,47 @@ def run_config(cfg, args):
     W, N, K, B = d["W"], d["N"], d["K"], d["B"]
     sets = Sets(d, args.rotate_mib << 20 if not args.warm else 1, args.max_sets, args.epilogue,
                 args.two_shot)
+    timer = ColdTimer(args.flush_mib if not args.warm else 0)
     try:
-        # Warm-up; it also touches every set once, which the consistency check reads.
-        for i in range(max(args.warmup, sets.R)):
+        # Warm-up: exactly args.warmup untimed calls.
+        for i in range(args.warmup):
             sets.call(i)
         torch.cuda.synchronize()
+
+        # Timed region: K calls continuing the rotation, in one graph replay
+        # after a cache-evicting pass (see the module docstring).
+        K_ = args.steps
+        g = capture(lambda: [sets.call(args.warmup + j) for j in range(K_)])
+        us_per_call = timer.replay(g, K_)
         consistent = check_consistency(sets)
 
-        # Eager pass (host-issued launches): wall-clock rate, for reference.
+        # For reference, after the timed region: the same replay again (cold
+        # again; shows whether the first replay of a graph costs extra), host-
+        # issued launches, and a warm pass over one resident set (its inputs
+        # stay in the Infinity Cache and L2: not HBM).
+        second_us = timer.replay(g, K_)
         torch.cuda.synchronize()
         t_e0 = time.perf_counter()
-        for i in range(args.steps):
-            sets.call(i)
+        for j in range(K_):
+            sets.call(args.warmup + j)
         torch.cuda.synchronize()
-        eager_us = 1e6 * (time.perf_counter() - t_e0) / args.steps
-
-        # Timed region: replay of a graph holding K calls, bracketed by HIP
-        # events on the stream the kernels run on (a graph replays on the
-        # current stream), between two device syncs.
-        g = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(g, stream=cap):
-                for i in range(args.steps):
-                    sets.call(i)
-        g.replay()
+        eager_us = 1e6 * (time.perf_counter() - t_e0) / K_
+        gw = capture(lambda: [sets.call(0) for _ in range(K_)])
+        gw.replay()
         torch.cuda.synchronize()
         stream = torch.cuda.current_stream()
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
         ev0.record(stream)
-        g.replay()
+        gw.replay()
         ev1.record(stream)
         torch.cuda.synchronize()
-        wall_us = 1e6 * (time.perf_counter() - t0) / args.steps
-        us_per_call = 1e3 * ev0.elapsed_time(ev1) / args.steps
-        # The graph replays left every set in the same state.
+        warm_us = 1e3 * ev0.elapsed_time(ev1) / K_
         consistent = consistent and check_consistency(sets)
-
-        # Warm: the same number of calls on set 0 only (its inputs stay in
-        # the Infinity Cache and L2): not HBM, reported for reference.
-        gw = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(gw, stream=cap):
-                for _ in range(args.steps):
-                    sets.call(0)
-        gw.replay()
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        gw.replay()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        warm_us = 1e3 * ev0.elapsed_time(ev1) / args.steps
         del g, gw
     finally:
         gathered_in = getattr(sets, "gathered_in", None)
+        timer.close()
         sets.close()
 
     nbytes = alg_bytes(W, N, K, B, args.epilogue, args.two_shot)
@@ -378,9 +439,12 @@ def run_config(cfg, args):
         "config": {
             "workload": gi.CONFIGS[cfg]["name"], "id": cfg, "W": W, "rank": 0, "N": N,
             "K": K, "B": B, "accumulate": "f32",
-            "inputs": "cold: rotated over %d resident sets" % sets.R if not args.warm
-                      else "warm: one set (Infinity-Cache resident, not HBM)",
-            "timing": "hipGraph replay of K calls between two device syncs",
+            "inputs": ("cold: %d resident sets rotated, %d MiB read between the warm-up "
+                       "and the timed replay" % (sets.R, args.flush_mib))
+                      if not args.warm else "warm: one set (Infinity-Cache resident, not HBM)",
+            "timing": "hipGraph replay of K calls, HIP events on the launch stream, between "
+                      "two device syncs",
+            "untimed_calls_before_timed_region": args.warmup,
             "epilogue": ("bias + RMSNorm over rows (eps 1e-5), y in bf16" if args.epilogue
                          else "none"),
             "all_reduce": "two-shot" if args.two_shot else "one-shot",
@@ -393,7 +457,7 @@ def run_config(cfg, args):
             "launch_us_mean": round(us_per_call, 4),
         },
         "extra": {
-            "wall_us_per_call": round(wall_us, 4),
+            "second_cold_replay_us_per_call": round(second_us, 4),
             "eager_us_per_call": round(eager_us, 4),
             "warm_us_per_call": round(warm_us, 4),
             "sets_consistent": consistent,
@@ -438,10 +502,11 @@ class MoeSets:
         import gemv_shot_all_amd as gsa
         self.gsa, self.d = gsa, d
         foot = d["Wd"].nbytes + d["X"].nbytes + d["bufs"].nbytes
-        R = max(1, -(-rotate_bytes // foot))
+        R = max(1, -(-rotate_bytes // foot) + 1)  # other sets between two uses >= rotate_bytes
         if max_sets:
             R = min(R, max_sets)
         self.R = R
+        self.touched = set()  # sets called at least once
         Wd0 = torch.from_numpy(d["Wd"].view(np.int16)).cuda()
         X0 = torch.from_numpy(d["X"].view(np.int16)).cuda()
         b0 = torch.from_numpy(d["bufs"]).cuda()
@@ -465,19 +530,21 @@ class MoeSets:
 
     def call(self, i):
         j = i % self.R
+        self.touched.add(j)
         d, b = self.d, self.bufs[j]
         self.gsa.gsa_moe_gemm_all_to_all(self.X[j], self.Wd[j], self.splits[j], self.dst[j],
                                          b.bufs, b.pads, d["W"], d["rank"], d["ne"], d["H"],
                                          d["F"], d["rows_in"], d["rows_out"])
 
     def check_consistency(self):
-        """Every set's combine buffers bit-identical to set 0's, finite where
-        the combine writes; every set's status OK."""
-        out0 = self.bufs[0].bufs_view().cpu().numpy()
+        """Every called set's combine buffers bit-identical to the first
+        one's, finite where the combine writes; every set's status OK."""
+        used = sorted(self.touched)
+        out0 = self.bufs[used[0]].bufs_view().cpu().numpy()
         ok = bool(np.all(np.isfinite(out0)))
         for j in range(self.R):
             ok = ok and self.bufs[j].status(self.d["rank"]) == (0, -1, -1)
-        for j in range(1, self.R, max(1, self.R // 8)):
+        for j in used[1::max(1, len(used) // 8)]:
             ok = ok and np.array_equal(self.bufs[j].bufs_view().cpu().numpy().view(np.uint32),
                                        out0.view(np.uint32))
         return ok
@@ -520,34 +587,21 @@ def run_moe_config(cfg, args):
 
     d = gi.make_moe_inputs(cfg, seed=args.seed, rank=0)
     sets = MoeSets(d, args.rotate_mib << 20 if not args.warm else 1, args.max_sets)
+    timer = ColdTimer(args.flush_mib if not args.warm else 0)
     try:
-        for i in range(max(args.warmup, sets.R)):
+        for i in range(args.warmup):
             sets.call(i)
         torch.cuda.synchronize()
+        K_ = args.steps
+        g = capture(lambda: [sets.call(args.warmup + j) for j in range(K_)])
+        us_per_call = timer.replay(g, K_)
         consistent = sets.check_consistency()
-        g = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(g, stream=cap):
-                for i in range(args.steps):
-                    sets.call(i)
-        g.replay()
-        torch.cuda.synchronize()
-        stream = torch.cuda.current_stream()
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        ev0.record(stream)
-        g.replay()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        wall_us = 1e6 * (time.perf_counter() - t0) / args.steps
-        us_per_call = 1e3 * ev0.elapsed_time(ev1) / args.steps
+        second_us = timer.replay(g, K_)
         consistent = consistent and sets.check_consistency()
         del g
     finally:
         R = sets.R
+        timer.close()
         sets.close()
     nbytes = moe_alg_bytes(d)
     achieved = nbytes / (us_per_call * 1e-6) / 1e9
@@ -572,9 +626,12 @@ def run_moe_config(cfg, args):
             "H": d["H"], "F": d["F"], "top_k": c["top_k"], "tokens_per_rank": c["T"],
             "tokens_received": int(M.sum()), "experts_with_tokens": int((M > 0).sum()),
             "accumulate": "f32", "out": "f32",
-            "inputs": "cold: rotated over %d resident sets" % R if not args.warm
-                      else "warm: one set (Infinity-Cache resident, not HBM)",
-            "timing": "hipGraph replay of K calls between two device syncs",
+            "inputs": ("cold: %d resident sets rotated, %d MiB read between the warm-up "
+                       "and the timed replay" % (R, args.flush_mib))
+                      if not args.warm else "warm: one set (Infinity-Cache resident, not HBM)",
+            "timing": "hipGraph replay of K calls, HIP events on the launch stream, between "
+                      "two device syncs",
+            "untimed_calls_before_timed_region": args.warmup,
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
@@ -584,7 +641,7 @@ def run_moe_config(cfg, args):
             "launch_us_mean": round(us_per_call, 4),
         },
         "extra": {
-            "wall_us_per_call": round(wall_us, 4),
+            "second_cold_replay_us_per_call": round(second_us, 4),
             "sets_consistent": consistent,
             "alg_flops_per_call": int(2 * d["H"] * d["F"] * M.sum()),
         },
@@ -610,7 +667,7 @@ def main():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=2000)
-    p.add_argument("--warmup", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default=DEFAULT_CONFIG,
                    choices=sorted(gi.CONFIGS) + sorted(gi.MOE_CONFIGS),
                    help="a GEMV + AllReduce workload, or m0/m1/m2 for the MoE GEMM + "
@@ -621,6 +678,9 @@ def main():
     p.add_argument("--rotate-mib", type=int, default=1024,
                    help="total size of the rotated input sets (MiB)")
     p.add_argument("--max-sets", type=int, default=None)
+    p.add_argument("--flush-mib", type=int, default=1024,
+                   help="size of the buffer read between the warm-up and the "
+                        "timed replay (MiB)")
     p.add_argument("--warm", action="store_true", help="one resident set (cache-warm)")
     p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="CPU-oracle wall-time budget, split between one thread and all "

@@ -41,6 +41,7 @@
 // GPUs the same scheme runs at system scope.
 
 #include <algorithm>
+#include <type_traits>
 
 #include "gsa_device.h"
 #include "gsa_internal.h"
@@ -555,6 +556,94 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// The value that lane l ^ D holds (D = 8, 4, 2 or 1; partners stay within a
+// 16-lane row).  D = 8 and 4 take two DPP row shifts, each writing only the
+// 4-lane banks whose partner lies in its direction; D = 2 and 1 one quad
+// permutation.
+template <int D>
+__device__ __forceinline__ float partner_value(float v) {
+  auto dpp = [](float old, float src, auto ctrl, auto bank) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                           __builtin_bit_cast(int, src), decltype(ctrl)::value,
+                                           0xF, decltype(bank)::value, false));
+  };
+  using I = int;
+  if constexpr (D == 8) {
+    const float t = dpp(0.0f, v, std::integral_constant<I, 0x108>{},   // row_shl:8
+                        std::integral_constant<I, 0x3>{});             // banks 0, 1
+    return dpp(t, v, std::integral_constant<I, 0x118>{},               // row_shr:8
+               std::integral_constant<I, 0xC>{});                      // banks 2, 3
+  } else if constexpr (D == 4) {
+    const float t = dpp(0.0f, v, std::integral_constant<I, 0x104>{},   // row_shl:4
+                        std::integral_constant<I, 0x5>{});             // banks 0, 2
+    return dpp(t, v, std::integral_constant<I, 0x114>{},               // row_shr:4
+               std::integral_constant<I, 0xA>{});                      // banks 1, 3
+  } else if constexpr (D == 2) {
+    return dpp(0.0f, v, std::integral_constant<I, 0x4E>{},             // quad_perm [2,3,0,1]
+               std::integral_constant<I, 0xF>{});
+  } else {
+    static_assert(D == 1, "partner distance 8, 4, 2 or 1");
+    return dpp(0.0f, v, std::integral_constant<I, 0xB1>{},             // quad_perm [1,0,3,2]
+               std::integral_constant<I, 0xF>{});
+  }
+}
+
+// One stage of a reduce-scatter at lane distance D over V values per lane:
+// lane l keeps the upper half of the values if bit D of l is set, else the
+// lower half, and adds the partner's copy of the half it keeps.  V == 1: a
+// plain pairwise sum (both lanes end with the same total).
+template <int D, int V, int N>
+__device__ __forceinline__ void rs_stage(float (&v)[N], int lane) {
+  static_assert(V <= N, "stage over the array's first V values");
+  if constexpr (V == 1) {
+    if constexpr (D >= 16) {
+      const unsigned u = __builtin_bit_cast(unsigned, v[0]);
+      const auto p = D == 32 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                             : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+      v[0] = __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
+    } else {
+      v[0] = v[0] + partner_value<D>(v[0]);
+    }
+  } else if constexpr (D >= 16) {
+    // The swap pairs rows (16 or 32 lanes) so that each lane ends with its own
+    // and its partner's copy of the half it keeps.
+#pragma unroll
+    for (int j = 0; j < V / 2; ++j) {
+      const unsigned lo = __builtin_bit_cast(unsigned, v[j]);
+      const unsigned hi = __builtin_bit_cast(unsigned, v[j + V / 2]);
+      const auto p = D == 32 ? __builtin_amdgcn_permlane32_swap(lo, hi, false, false)
+                             : __builtin_amdgcn_permlane16_swap(lo, hi, false, false);
+      v[j] = __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
+    }
+  } else {
+    const bool upper = (lane & D) != 0;
+#pragma unroll
+    for (int j = 0; j < V / 2; ++j) {
+      const float keep = upper ? v[j + V / 2] : v[j];
+      const float give = upper ? v[j] : v[j + V / 2];
+      v[j] = keep + partner_value<D>(give);
+    }
+  }
+}
+
+// Reduce-scatter over the 64 lanes of a wave: v[0..V) are every lane's
+// partials of V outputs (V a power of two, at most 64); afterwards v[0] of
+// lane l holds the total over all 64 lanes of output l >> (6 - log2 V), in
+// every lane of that output's aligned group of 64 / V lanes.  A fixed tree
+// (bit-identical in every lane of a group, and from call to call).
+template <int V>
+__device__ __forceinline__ float reduce_scatter64(float (&v)[V], int lane) {
+  static_assert(V >= 1 && V <= 64 && (V & (V - 1)) == 0, "a power of two up to 64");
+  rs_stage<32, (V >= 2 ? V : 1)>(v, lane);
+  rs_stage<16, (V >= 4 ? V / 2 : 1)>(v, lane);
+  rs_stage<8, (V >= 8 ? V / 4 : 1)>(v, lane);
+  rs_stage<4, (V >= 16 ? V / 8 : 1)>(v, lane);
+  rs_stage<2, (V >= 32 ? V / 16 : 1)>(v, lane);
+  rs_stage<1, (V >= 64 ? V / 32 : 1)>(v, lane);
+  return v[0];
+}
+
 // fp32 -> bf16 bits, round to nearest, ties to even; a NaN stays a quiet NaN.
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -1019,6 +1108,167 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
                                    state, wave, lane, NT, own_peers, pv);
 }
 
+// Long rows (C > 224 chunks, B <= 8), the plain one-shot call.  One
+// workgroup of kLongWaves waves owns kLongRows = 32 rows; wave w takes rows
+// 2w and 2w + 1 of the tile, a full wave per row: lane l streams chunks
+// l, l + 64, ... of both rows with D chunk steps in flight.  Every x load of
+// the workgroup goes out ahead of every A load (a scheduling barrier keeps
+// that order; x is small and read by every workgroup, so it returns first,
+// and the workgroup barrier that publishes x in LDS then waits for x alone,
+// never for A).  Wave 0 also runs the signal-pad protocol: its flag loads go
+// out before anything else, it takes the start decision (comm_decide) before
+// that barrier, and after the publish it raises the tile's flags (and, if a
+// peer had not published at the start, waits for it).  The 2 B partial sums
+// of a lane are combined across the wave with one reduce-scatter, which
+// leaves each output in one aligned lane group; its first lane loads that
+// output's peer values right after the barrier (they queue behind the A
+// stream), sums out in rank order, publishes y and stores out.
+// Measured on the 70B-class down_proj shape (cold inputs, no protocol):
+// 10.55 us per call against 10.9-12.0 us for 16-row workgroups of 8 waves
+// with 2-7 steps in flight or x staged by LDS DMA (whose LDS writes the
+// compiler orders behind every outstanding load), and against 9.9 us for a
+// plain read of the same rows.
+constexpr int kLongWaves = 16;
+constexpr int kLongRows = 2 * kLongWaves;
+constexpr int kLongCtlWords = 4 + kLongRows / kFlagRows;  // s_ctl[4 + q]: epoch of flag tile q
+
+constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 * pow2_at_least((v + 1) / 2); }
+constexpr int log2_exact(int v) { return v <= 1 ? 0 : 1 + log2_exact(v / 2); }
+
+template <int B, int NCH, int D, int XPT, bool MASKED>
+__global__ __launch_bounds__(kLongWaves * 64, kLongWaves / 4) void gemv_ar_long(GemvArgs a) {
+  constexpr int R = 2;
+  constexpr int NT = kLongWaves * 64;
+  constexpr int TR = kLongRows;
+  constexpr int V = R * B;                 // outputs of a wave: row s, column b at s * B + b
+  constexpr int VP = pow2_at_least(V);     // padded for the reduce-scatter
+  constexpr int SH = 6 - log2_exact(VP);   // output o sits in lanes [o << SH, (o + 1) << SH)
+  static_assert(kLongRows / kFlagRows * kMaxW <= 64, "one wave-0 lane per (flag tile, rank)");
+
+  extern __shared__ uint4 lds_x[];         // x chunks [b][c], one zero chunk, one sink chunk
+  __shared__ uint32_t s_ctl[kLongCtlWords];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t tile = blockIdx.x;
+  const FlagSpan fs = flag_span<TR>(a, tile);
+  const int C = a.C;
+  const int xchunks = B * C;
+  const int zidx = xchunks;
+  const int nch = NCH > 0 ? NCH : (C + 63) / 64;
+
+  // Protocol state first: wave 0's flag loads lead every other load of the wave.
+  uint32_t fl = 0;
+  if (wave == 0) fl = load_flag(a, fs, lane);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // x into registers (XPT <= 8 chunks per thread; indexes past x repeat the
+  // last chunk and are written to the sink), then A.  Named registers, not
+  // an array: across the scheduling barrier an array was kept in scratch.
+  static_assert(XPT >= 1 && XPT <= 8, "x staged in at most 8 chunks per thread");
+  const uint4* xg = reinterpret_cast<const uint4*>(a.x);
+  uint4 x0, x1, x2, x3, x4, x5, x6, x7;
+#define GSA_X_LOAD(k) \
+  if constexpr (XPT > k) x##k = xg[min(tid + k * NT, xchunks - 1)];
+  GSA_X_LOAD(0) GSA_X_LOAD(1) GSA_X_LOAD(2) GSA_X_LOAD(3)
+  GSA_X_LOAD(4) GSA_X_LOAD(5) GSA_X_LOAD(6) GSA_X_LOAD(7)
+#undef GSA_X_LOAD
+  __builtin_amdgcn_sched_barrier(0);
+
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, (uint32_t)(a.N * C * 16));
+  const int64_t row0 = tile * TR + wave * R;
+  uint32_t voff[R];
+#pragma unroll
+  for (int s = 0; s < R; ++s) voff[s] = ((uint32_t)(row0 + s) * (uint32_t)C + lane) * 16u;
+  uint4 ring[D][R];
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+    if (NCH > 0 ? u < NCH : u < nch) load_chunk<R>(ring[u], ra, voff, (uint32_t)u * 1024u);
+
+  if (wave == 0) comm_decide<false, TR>(a, lane, tile, fs, fl, s_ctl);
+#define GSA_X_PUT(k)                                    \
+  if constexpr (XPT > k) {                              \
+    const int idx = tid + k * NT;                       \
+    lds_x[idx < xchunks ? idx : xchunks + 1] = x##k;    \
+  }
+  GSA_X_PUT(0) GSA_X_PUT(1) GSA_X_PUT(2) GSA_X_PUT(3)
+  GSA_X_PUT(4) GSA_X_PUT(5) GSA_X_PUT(6) GSA_X_PUT(7)
+#undef GSA_X_PUT
+  if (tid == 0) lds_x[zidx] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();  // B1: x in LDS, the start decision in s_ctl
+  const uint32_t state = s_ctl[1];
+
+  // The output this lane group owns: o = lane >> SH (row o / B, column o % B).
+  const int o = min(lane >> SH, V - 1);
+  const bool owner = (lane & ((1 << SH) - 1)) == 0 && (lane >> SH) < V;
+  const int64_t orow = row0 + o / B;
+  const int64_t NB = a.N * a.B;
+  const int64_t oi = min(orow * B + o % B, NB - 1);
+  // Peer values of that output, loaded after the flags were seen (B1) when
+  // every peer had published then; the loads are unconditional (ranks past
+  // W - 1 repeat rank W - 1's word) and their values unused otherwise.  They
+  // queue behind the lane's first A steps.  (Issued instead right behind the
+  // lane's last A load, with each refill pinned to its step, they measured
+  // no faster: 11.93 against 11.86 us per call on the 70B-class shape.)
+  float pv[kMaxW];
+#pragma unroll
+  for (int r = 0; r < kMaxW; ++r) pv[r] = load_coherent(&a.slots[min(r, a.W - 1) * NB + oi]);
+
+  float acc[R][B];
+#pragma unroll
+  for (int s = 0; s < R; ++s)
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[s][b] = 0.0f;
+  valu_stream<MASKED, NCH, D, B, 64, R>(acc, ring, ra, voff, lds_x, C, zidx, lane, nch, 0);
+
+  float v[VP];
+#pragma unroll
+  for (int i = 0; i < VP; ++i) v[i] = i < V ? acc[i / B][i % B] : 0.0f;
+  const float y = reduce_scatter64<VP>(v, lane);
+
+  const bool live = owner && orow < a.N;
+  float* own_slot = a.slots + a.rank * NB;
+  float outv = 0.0f;
+  if (state == kPeersReady) {
+    // out = ((0 + s_0) + s_1) ... + s_{W-1}, the own term being y as
+    // published; ranks past W - 1 add +0 (acc is never -0).
+#pragma unroll
+    for (int r = 0; r < kMaxW; ++r) outv = outv + (r < a.W ? (r == a.rank ? y : pv[r]) : 0.0f);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (state != kBadOwnRow && live) store_coherent(&own_slot[oi], y);
+  __builtin_amdgcn_sched_barrier(0);
+  if (state == kPeersReady) {
+    if (live) a.out[oi] = outv;
+    wait_vm_le<1>();  // the published value is at the coherence point (stores complete in order)
+  } else {
+    wait_vm_all();
+  }
+  __syncthreads();  // B2: every published value of the tile is at the coherence point
+  if (state != kBadOwnRow && wave == 0 && lane < fs.nf)
+    store_flag(flag_ptr(a, a.rank, fs.f0 + lane), s_ctl[4 + lane]);
+  if (state == kMustWait) {
+    // A peer had not published at the start: wait for it (bounded), then
+    // load the peer values of the complete flag tiles and write out.
+    if (wave == 0) {
+      const uint32_t done = wait_peers<false, TR>(a, lane, tile, fs, s_ctl);
+      if (lane == 0) s_ctl[0] = done;
+    }
+    __syncthreads();  // B3
+    const uint32_t done = s_ctl[0];
+    const int q = (int)(orow - tile * TR) / kFlagRows;
+    if (live && ((done >> q) & 1u)) {
+      float acc2 = 0.0f;
+#pragma unroll
+      for (int r = 0; r < kMaxW; ++r) {
+        if (r < a.W) acc2 = acc2 + (r == a.rank ? y : load_coherent(&a.slots[r * NB + oi]));
+      }
+      a.out[oi] = acc2;
+    }
+  }
+}
+
 // MFMA epilogue: each wave's 16 x 16 partial goes to red[wave][n][b]; after
 // B1 wave w sums rows 4w .. 4w+3 over the waves in wave order (lane l: row
 // 4w + (l >> 4), column l & 15), publishes them and reduces.
@@ -1251,7 +1501,7 @@ bool mfma_x_in_lds(int C) { return (size_t)16 * (C + 1) * 16 <= GSA_MAX_X_LDS_BY
 
 struct ValuChoice {
   const void* kernel;
-  int waves;      // compute waves (the communication wave comes on top)
+  int threads;    // per workgroup (compute waves, plus the communication wave if the kernel has one)
   int tile_rows;  // rows per workgroup
 };
 
@@ -1273,7 +1523,22 @@ ValuChoice valu_tier(int C) {
         &gemv_ar_valu<B, G, R, NW, NCH, DE, XPT, WPE, false, TS, XM>);
   else
     k = reinterpret_cast<const void*>(&gemv_ar_valu<B, G, R, NW, 0, D, XPT, WPE, true, TS, XM>);
-  return {k, NW, NW * (64 / G) * R};
+  return {k, (NW + 1) * 64, NW * (64 / G) * R};
+}
+
+// The long-row kernel: an unrolled instance for rows of exactly 448 chunks
+// (the 70B-class down_proj shard), a masked streaming one for the others;
+// 4 chunk steps in flight (measured: 10.55 us on the 70B-class shape against
+// 11.1 at 3 and 10.6-12.0 at 5-7, cold, without the protocol).
+template <int B>
+ValuChoice long_tier(int C) {
+  constexpr int kExactNch = 7;
+  constexpr int XPT = ceil_div(B * 64 * kExactNch, kLongWaves * 64);
+  constexpr int D = 4;
+  const void* k = C == 64 * kExactNch
+                      ? reinterpret_cast<const void*>(&gemv_ar_long<B, kExactNch, D, XPT, false>)
+                      : reinterpret_cast<const void*>(&gemv_ar_long<B, 0, D, 8, true>);
+  return {k, kLongWaves * 64, kLongRows};
 }
 
 // VALU tiers by chunks per row C = Ks / 8 (plus the communication wave):
@@ -1288,6 +1553,7 @@ ValuChoice valu_tier(int C) {
 // of rows up to C = 224 go to the XCDs in contiguous runs (block_tile).
 template <int B, bool TS>
 ValuChoice valu_kernel(int C, bool small_tiles) {
+  if (small_tiles && !TS && C > 224) return long_tier<B>(C);
   if (small_tiles && C <= 64) return valu_tier<B, 32, 2, 1, 2, 2, 1, TS, true>(C);
   if (C <= 64) return valu_tier<B, 64, 4, 4, 1, 1, 1, TS, true>(C);
   if (C <= 224) return valu_tier<B, 32, 2, 4, 7, 4, 1, TS, true>(C);
@@ -1308,15 +1574,16 @@ ValuChoice pick_kernel(int B, int C, bool small_tiles) {
     default:
       return mfma_x_in_lds(C)
                  ? ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma<kMfmaWaves, 8, TS>),
-                              kMfmaWaves, kBigTile}
+                              (kMfmaWaves + 1) * 64, kBigTile}
                  : ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma_xmem<kMfmaWaves, 8, TS>),
-                              kMfmaWaves, kBigTile};
+                              (kMfmaWaves + 1) * 64, kBigTile};
   }
 }
 
 }  // namespace
 
 size_t gemv_lds_bytes(int W, int B, int C, bool epi, int tile_rows) {
+  if (tile_rows == kLongRows) return ((size_t)B * C + 2) * 16;  // x, zero and sink chunks
   // The peer tile, then (with the epilogue) 16 x 16 squares, 16 1/rms and
   // up to 8 waves x 16 partial sums.
   const size_t tail = ((size_t)W * tile_rows * B + 1) * sizeof(float) +
@@ -1334,8 +1601,7 @@ bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, Launch* ou
   const bool small_tiles = !epi;  // the fused epilogue counts 16-row tiles
   const ValuChoice k =
       two_shot ? pick_kernel<true>(B, C, small_tiles) : pick_kernel<false>(B, C, small_tiles);
-  const unsigned block = (unsigned)(k.waves + 1) * 64;
-  *out = {k.kernel, block, gemv_lds_bytes(W, B, C, epi, k.tile_rows), k.tile_rows};
+  *out = {k.kernel, (unsigned)k.threads, gemv_lds_bytes(W, B, C, epi, k.tile_rows), k.tile_rows};
   return true;
 }
 

@@ -1,5 +1,6 @@
-// hbm_read_probe.hip -- the streaming-read kernel behind include/gsa_probe.h
-// (a measurement aid for the achievable HBM read bandwidth).
+// hbm_read_probe.hip -- the measurement aids behind include/gsa_probe.h: a
+// streaming-read kernel (the achievable HBM read bandwidth) and a bounded
+// spin kernel (keeps the GPU busy while the host queues a timed region).
 #include <hip/hip_runtime.h>
 
 #include "gsa_probe.h"
@@ -35,7 +36,26 @@ __global__ __launch_bounds__(kBlock) void read_probe(const u32x4_t* __restrict__
   if (acc == 0x9E3779B9u) sink[blockIdx.x] = acc;
 }
 
+// One wave spins until `ticks` wall-clock ticks have passed since it started.
+// The bound is the argument itself, so the kernel always ends.
+__global__ __launch_bounds__(64) void spin_probe(uint64_t ticks) {
+  const uint64_t t0 = wall_clock64();
+  while (wall_clock64() - t0 < ticks) __builtin_amdgcn_s_sleep(32);
+}
+
 }  // namespace
+
+extern "C" int gsa_probe_spin(uint32_t us, void* stream) {
+  if (us == 0 || us > 1000000u) return -1;
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+      khz <= 0)
+    return -3;
+  const uint64_t ticks = (uint64_t)us * (uint64_t)khz / 1000u;
+  hipLaunchKernelGGL(spin_probe, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), ticks);
+  return hipGetLastError() == hipSuccess ? 0 : -3;
+}
 
 extern "C" int gsa_probe_read(const void* src, size_t bytes, uint32_t* sink, int grid,
                               void* stream) {
