@@ -339,9 +339,11 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
   __syncthreads();  // B1
   if (early_tile) {
     store_peer_tile<TS, TR>(a, lane, tile, v, pe);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the peer tile is in LDS ...
-    if (lane == 0)                       // ... before its mark
-      __hip_atomic_store(&s_ctl[8], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    // The mark is a workgroup-scope release: every lane's peer-tile stores
+    // above happen before it, for the compiler and for the hardware alike
+    // (its acquire load is in the compute waves).
+    if (lane == 0)
+      __hip_atomic_store(&s_ctl[8], 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
   __syncthreads();  // B2
   if (state == kMustWait) {
@@ -1095,8 +1097,8 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   if (kPeersFromTile && own_peers) {
     // The communication wave marks the peer tile stored without waiting for
     // the compute waves, so this wait ends.
-    while (__hip_atomic_load(&s_ctl[8], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u)
-      __builtin_amdgcn_s_sleep(1);
+    while (__hip_atomic_load(&s_ctl[8], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) == 0u)
+      __builtin_amdgcn_s_sleep(1);  // acquire: the peer tile's LDS loads below stay after it
     const int idx = (nloc0 + vidx / B) * B + vidx % B;
 #pragma unroll
     for (int r = 0; r < kMaxW; ++r) pv[r] = pe[min(r, a.W - 1) * (TR * B) + idx];

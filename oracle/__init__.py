@@ -18,7 +18,8 @@ protocol state.  Sources followed (restated, not quoted):
   "PyTorch Symmetric Memory" documentation, writing-your-own-kernel section
   (Triton one_shot_all_reduce_kernel);
 * fp32 accumulation of bf16 inputs -- same documentation, higher-precision
-  reduction section;
+  reduction section; read for the all-reduce itself: bf16 partials in the
+  slots widened and summed in fp32, the sum handed back in bf16;
 * bias then RMSNorm fused behind the all-reduce -- "PyTorch Symmetric Memory"
   talk, real-model example (RMSNorm itself: its textbook definition, the
   pages do not write it out); bf16 output of an fp32 accumulation -- the
@@ -83,6 +84,10 @@ class Oracle:
         lib.gsa_oracle_gemv_allreduce.restype = ctypes.c_int
         lib.gsa_oracle_fold_f32.argtypes = [_f32p, ctypes.c_int, ctypes.c_int64, _f32p]
         lib.gsa_oracle_fold_f32.restype = None
+        lib.gsa_oracle_fold_bf16.argtypes = [_u16p, ctypes.c_int, ctypes.c_int64, _f32p]
+        lib.gsa_oracle_fold_bf16.restype = None
+        lib.gsa_oracle_f32_to_bf16.argtypes = [_f32p, ctypes.c_int64, _u16p]
+        lib.gsa_oracle_f32_to_bf16.restype = None
         lib.gsa_oracle_bias_rmsnorm.argtypes = [_f32p, _f32p, _f32p, ctypes.c_double,
                                                 ctypes.c_int64, ctypes.c_int, _f32p, _f64p,
                                                 _f64p]
@@ -245,10 +250,38 @@ class Oracle:
         self._lib.gsa_oracle_fold_f32(_ptr(slots, _f32p), W, nb, _ptr(out, _f32p))
         return out
 
+    def fold_bf16(self, slots):
+        """fp32 one-shot sum of bf16 slots (uint16 bits, W x ...), each
+        widened exactly, in rank order from +0.0f."""
+        slots = np.ascontiguousarray(slots, dtype=np.uint16)
+        W = slots.shape[0]
+        rest = slots.shape[1:]
+        nb = int(np.prod(rest)) if rest else 1
+        out = np.empty(rest, np.float32)
+        self._lib.gsa_oracle_fold_bf16(_ptr(slots, _u16p), W, nb, _ptr(out, _f32p))
+        return out
+
+    def to_bf16(self, v):
+        """bf16 bits (uint16) of float32 values, round to nearest, ties to even."""
+        v = np.ascontiguousarray(v, dtype=np.float32)
+        out = np.empty(v.shape, np.uint16)
+        self._lib.gsa_oracle_f32_to_bf16(_ptr(v, _f32p), int(v.size), _ptr(out, _u16p))
+        return out
+
 
 def bound(abs64):
     """Allowed |fp32 result - fp64 value| for each element."""
     return BOUND_REL * np.asarray(abs64, np.float64) + BOUND_ABS
+
+
+def bound_bf16(abs64, y64):
+    """Allowed |bf16 result - fp64 value| when an fp32 result within bound()
+    is then rounded to bf16: a bf16 value carries 8 significant bits, so
+    round-to-nearest moves v by at most half a unit in its last place, which
+    is at most 2^-8 |v|; with |v| <= |y64| + bound this adds
+    2^-8 (|y64| + bound) to bound()."""
+    b = bound(abs64)
+    return b + 2.0 ** -8 * (np.abs(np.asarray(y64, np.float64)) + b)
 
 
 def flag_tiles(N):

@@ -43,7 +43,10 @@
  *    the other chunks from their owners (gsa_oracle_two_shot).
  *  - "PyTorch Symmetric Memory" documentation, higher-precision reduction:
  *    accumulate in fp32, hand the result back in the input precision (bf16),
- *    which gsa_oracle_scale_f32 rounds to nearest, ties to even.
+ *    which gsa_oracle_scale_f32 rounds to nearest, ties to even.  The same
+ *    section read for the all-reduce itself: bf16 partials in the slots are
+ *    widened and summed in fp32 (gsa_oracle_fold_bf16), and the sum is
+ *    handed back in bf16 (gsa_oracle_f32_to_bf16).
  *
  *  - "Overlapping Collective Communication ..." (the fused-operators page),
  *    Abstract: a third fused operator, GEMM + All-to-All for mixture-of-
@@ -190,6 +193,36 @@ static uint16_t f32_to_bf16_rne(float f)
         return (uint16_t)((u >> 16) | 0x0040u);
     uint32_t lsb = (u >> 16) & 1u;
     return (uint16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+
+/*
+ * fp32 to bf16 for a whole array: out[i] = round-to-nearest-even of in[i]
+ * to the bf16 grid (a quiet NaN stays a quiet NaN).
+ */
+void gsa_oracle_f32_to_bf16(const float *in, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = f32_to_bf16_rne(in[i]);
+}
+
+/*
+ * The one-shot sum over bf16 slots with fp32 accumulation, in the pages'
+ * order: sum = +0.0f; for r = 0..W-1: sum = fl32(sum + widen(slots[r][i]));
+ * out[i] = sum.  Widening bf16 to fp32 is exact.  Given the bf16 partials a
+ * GPU published, this result (and its bf16 rounding) is unique.
+ */
+void gsa_oracle_fold_bf16(const uint16_t *slots, int W, int64_t NB, float *out)
+{
+    for (int64_t i = 0; i < NB; ++i) {
+        float sum = 0.0f;
+        for (int r = 0; r < W; ++r) {
+            uint32_t word = (uint32_t)slots[(int64_t)r * NB + i] << 16;
+            float v;
+            memcpy(&v, &word, sizeof v);
+            sum = sum + v;
+        }
+        out[i] = sum;
+    }
 }
 
 /*

@@ -24,6 +24,12 @@ What pins what:
   scale_exact      fp32 evaluation of the normalised output against exact
                    rational arithmetic with IEEE round-to-nearest-even
   bf16_rne         fp32 -> bf16 rounding, hand-chosen bit patterns
+  bf16_reduce_*    the all-reduce over bf16 slots with fp32 accumulation and
+                   bf16 output: a hand-worked golden file (cases where bf16
+                   accumulation, another order or another start would give
+                   other bits), numpy float32 scalar adds in rank order, and
+                   the rounding built from the definition (the nearer of the
+                   two neighbouring bf16 values, ties to the even one)
   two_shot_*       chunk partition (hand values and its defining properties),
                    ownership of every row for every rank against numpy
                    float32 sums in rank order and plain copies
@@ -369,6 +375,69 @@ def pin_bf16_rne(o):
         f"NaN stays a quiet NaN, got {hex(v)}"
 
 
+def pin_bf16_reduce_golden(o):
+    with open(os.path.join(GOLDEN, "bf16_allreduce_hand.json")) as f:
+        g = json.load(f)
+    for c in g["cases"]:
+        bits = np.array([int(b, 16) for b in c["bits"]], np.uint16).reshape(-1, 1)
+        fold = o.fold_bf16(bits)
+        want = np.float32(c["fold_f32"])
+        assert fold[0].view(np.uint32) == want.view(np.uint32), (
+            f"bf16 slots {c['slots']}: fp32 fold {fold[0]!r}, want {want!r}")
+        got = int(o.to_bf16(fold)[0])
+        assert got == int(c["out_bits"], 16), (
+            f"bf16 slots {c['slots']}: out bits {hex(got)}, want {c['out_bits']}")
+
+
+def pin_bf16_reduce_sequence(o):
+    # Random bf16 slots: widen each exactly (bits << 16) and add them in rank
+    # order with numpy float32 scalar adds (IEEE round-to-nearest).
+    rng = np.random.default_rng(12)
+    W, NB = 8, 301
+    vals = (rng.normal(0, 1, (W, NB)) * rng.choice([1e-3, 1, 1e3], (W, NB))).astype(np.float32)
+    bits = gi.bf16_bits(vals)
+    out = o.fold_bf16(bits)
+    wide = (bits.astype(np.uint32) << 16).view(np.float32)
+    for i in range(NB):
+        acc = np.float32(0.0)
+        for r in range(W):
+            acc = np.float32(acc + wide[r, i])
+        assert out[i].view(np.uint32) == acc.view(np.uint32), f"bf16 fold element {i}"
+
+
+def _bf16_nearest_by_definition(v):
+    """bf16 bits of the bf16 value nearest to the finite float32 v (ties: the
+    one whose last stored bit is 0), found by comparing the distances to the
+    two neighbours in exact arithmetic -- not by the rounding bit trick."""
+    u = int(np.float32(v).view(np.uint32))
+    lo = u >> 16                           # toward zero: the upper half of the word
+    hi = lo + 1                            # the next bf16 value away from zero
+    def val(b):
+        return Fraction(float(np.uint32(b << 16).view(np.float32)))
+    x = Fraction(float(v))
+    d_lo, d_hi = abs(x - val(lo)), abs(val(hi) - x)
+    if d_lo < d_hi:
+        return lo
+    if d_hi < d_lo:
+        return hi
+    return lo if lo % 2 == 0 else hi
+
+
+def pin_bf16_reduce_rounding(o):
+    rng = np.random.default_rng(13)
+    v = (rng.normal(0, 1, 400) * rng.choice([1e-30, 1e-3, 1, 1e5, 1e30], 400)).astype(np.float32)
+    # exact ties and their neighbours: upper halves with the low 16 bits
+    # 0x8000 (halfway) and 0x7FFF / 0x8001
+    base = rng.integers(0x0080, 0x7F00, 60).astype(np.uint32) << 16
+    sign = rng.integers(0, 2, 60).astype(np.uint32) << 31
+    for low in (0x8000, 0x7FFF, 0x8001):
+        v = np.concatenate([v, ((base | sign) + low).view(np.float32)])
+    got = o.to_bf16(v)
+    for i, f in enumerate(v):
+        want = _bf16_nearest_by_definition(f)
+        assert int(got[i]) == want, f"bf16 of {f!r}: {hex(int(got[i]))}, want {hex(want)}"
+
+
 def pin_two_shot_chunks(o):
     # Hand values: ceil(N / W) rounded up to whole 16-row tiles.
     for N, W, want in [(4096, 8, 512), (17, 8, 16), (1000, 3, 336), (33, 2, 32), (1, 1, 16),
@@ -536,6 +605,7 @@ PINS = [pin_brute_force, pin_single_rank, pin_shard_sum, pin_identity, pin_one_h
         pin_fold_order, pin_fold_zero_start, pin_fold_fp32, pin_fold_matches_sequence,
         pin_rms_golden, pin_rms_constant_column, pin_rms_unit_rms, pin_rms_scale_invariant,
         pin_rms_bias_cancels, pin_rms_columns_independent, pin_scale_exact, pin_bf16_rne,
+        pin_bf16_reduce_golden, pin_bf16_reduce_sequence, pin_bf16_reduce_rounding,
         pin_two_shot_chunks, pin_two_shot_rows, pin_moe_numpy, pin_moe_identity,
         pin_moe_one_hot, pin_moe_golden, pin_moe_rejects]
 

@@ -24,24 +24,28 @@ def _bits(a):
     return np.ascontiguousarray(a).view(np.uint32)
 
 
-@pytest.mark.parametrize("cfg", ["c2", "c3b8", "c5"])
+REPEATS = 100
+
+
+@pytest.mark.parametrize("cfg", ["c2", "c3b8", "c4", "c5"])
 def test_repeats_bit_identical_and_flag_epochs(cfg):
+    """REPEATS calls on one buffer: out and every slot byte-identical to the
+    first call's, and the own flags count the calls."""
     _say(f"[protocol] repeats {cfg}")
     d = gi.make_inputs(cfg, seed=3)
     r = Run(d["A"], d["x"], d["slots"].copy(), 0)
     try:
-        outs, slots = [], []
-        for _ in range(5):
+        r.call()
+        out0, sl0, _, _ = r.results()
+        for i in range(1, REPEATS):
+            r.out.fill_(float("nan"))
             r.call()
             out, sl, flags, status = r.results()
-            outs.append(out.copy())
-            slots.append(sl.copy())
+            assert np.array_equal(_bits(out), _bits(out0)), f"out differs at call {i}"
+            assert np.array_equal(_bits(sl), _bits(sl0)), f"slots differ at call {i}"
         assert status == (gsa.GSA_OK, -1, -1)
-        for o, s in zip(outs[1:], slots[1:]):
-            assert np.array_equal(_bits(o), _bits(outs[0])), "out differs between calls"
-            assert np.array_equal(_bits(s), _bits(slots[0])), "slots differ between calls"
         expect = oracle.pad_after_calls(oracle.pad_after_reset(d["W"], d["N"], all_but(d["W"], 0)),
-                                        0, 5)
+                                        0, REPEATS)
         assert np.array_equal(flags, expect), "own flags must count the calls"
     finally:
         r.close()
@@ -205,7 +209,9 @@ def test_timeout_reports_missing_peer_and_skips_out():
 
 @pytest.mark.parametrize("Ks,t_bad", [
     (128, 3),    # short rows: 4-row workgroups, one flag tile each
-    (3200, 5),   # longer rows: 16-row workgroups; flag tile 5 is the second of its workgroup
+    (1024, 6),   # middle rows: 16-row workgroups of 4 waves; the third flag tile of the second
+    (3200, 5),   # long rows: 32-row workgroups; flag tile 5 is the sixth of its workgroup
+    (3200, 13),  # long rows: a flag tile of the second (ragged) 32-row workgroup
     (128, 19),   # the last flag tile
 ])
 def test_timeout_single_tile(Ks, t_bad):

@@ -64,6 +64,21 @@ MUTANTS = {
     "moe_first_row_only": ("const uint16_t *xr = X + (src + i) * F;", "const uint16_t *xr = X + src * F;"),
     "moe_abs_dropped": ("acc_abs += fabs(q);", "acc_abs += q;"),
     "moe_overlap_unchecked": ("if (written[orow])\n                    return -2;\n", ""),
+    "bf16_fold_in_bf16": ("            sum = sum + v;\n",
+                          "            sum = sum + v;\n            { uint32_t t; memcpy(&t, &sum, 4);"
+                          " t = (t + 0x7FFFu + ((t >> 16) & 1u)) & 0xFFFF0000u; memcpy(&sum, &t, 4); }\n"),
+    "bf16_fold_reversed": ("            uint32_t word = (uint32_t)slots[(int64_t)r * NB + i] << 16;",
+                           "            uint32_t word = (uint32_t)slots[(int64_t)(W - 1 - r) * NB + i] << 16;"),
+    "bf16_fold_widen_shift": ("            uint32_t word = (uint32_t)slots[(int64_t)r * NB + i] << 16;",
+                              "            uint32_t word = (uint32_t)slots[(int64_t)r * NB + i] << 15;"),
+    "bf16_fold_stride": ("            uint32_t word = (uint32_t)slots[(int64_t)r * NB + i] << 16;",
+                         "            uint32_t word = (uint32_t)slots[(int64_t)r * W + i] << 16;"),
+    "bf16_fold_starts_at_slot0": ("        float sum = 0.0f;\n        for (int r = 0; r < W; ++r) {",
+                                  "        float sum = 0.0f;\n        for (int r = 0; r < W; ++r) {\n            if (r == 0) sum = -0.0f;"),
+    "bf16_fold_skips_last": ("        for (int r = 0; r < W; ++r) {\n            uint32_t word",
+                             "        for (int r = 0; r < W - 1; ++r) {\n            uint32_t word"),
+    "bf16_out_truncates": ("        out[i] = f32_to_bf16_rne(in[i]);",
+                           "        { uint32_t t; memcpy(&t, &in[i], 4); out[i] = (uint16_t)(t >> 16); }"),
     "nan_branch_dropped": ("if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0)\n        return (uint16_t)((u >> 16) | 0x0040u);\n", ""),
 }
 
