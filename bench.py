@@ -60,19 +60,22 @@ def two_shot_chunk_rows(N, W):
     return -(-(-(-N // W)) // 16) * 16
 
 
-def alg_bytes(W, N, K, B, epilogue=False, two_shot=False, rank=0):
+def alg_bytes(W, N, K, B, epilogue=False, two_shot=False, rank=0, slot_bytes=4, out_bytes=4):
     """Bytes the method itself must move per call: A_r, x_r, the published
     slot, the W-1 peer slots and out (flags excluded); with the fused
     epilogue also the bias and RMSNorm weight (N fp32 each) and y (bf16).
     Two-shot: the peer slots only over the own chunk's c rows, plus the
-    published chunk (c rows) and the N - c rows copied from their owners."""
+    published chunk (c rows) and the N - c rows copied from their owners.
+    slot_bytes / out_bytes: element sizes of the slots and of out (4 for
+    fp32, 2 for bf16; the two-shot and epilogue calls take fp32)."""
     Ks = K // W
     if two_shot:
         c = max(0, min(N, (rank + 1) * two_shot_chunk_rows(N, W)) -
                 rank * two_shot_chunk_rows(N, W))
         return (2 * N * Ks + 2 * B * Ks + 4 * N * B + 4 * (W - 1) * c * B + 4 * c * B +
                 4 * (N - c) * B + 4 * N * B)
-    base = 2 * N * Ks + 2 * B * Ks + 4 * N * B + 4 * (W - 1) * N * B + 4 * N * B
+    base = (2 * N * Ks + 2 * B * Ks + slot_bytes * N * B + slot_bytes * (W - 1) * N * B +
+            out_bytes * N * B)
     return base + (8 * N + 2 * N * B if epilogue else 0)
 
 
@@ -86,9 +89,11 @@ def kernel_source_digest(path=KERNEL_SOURCE):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def profile_name(cfg, epilogue=False, two_shot=False):
+def profile_name(cfg, epilogue=False, two_shot=False, slot_dtype="f32", out_dtype="f32"):
     """Base name of the committed rocprofv3 summaries for a bench line."""
     variant = "_rmsnorm" if epilogue else "_two_shot" if two_shot else ""
+    if slot_dtype != "f32" or out_dtype != "f32":
+        variant += f"_slots_{slot_dtype}_out_{out_dtype}"
     return f"gemv_allreduce{variant}_{cfg}"
 
 
@@ -111,7 +116,8 @@ class Sets:
     """R independent input sets on the device, each with its own symmetric
     buffer (peers published) and output."""
 
-    def __init__(self, d, rotate_bytes, max_sets=None, epilogue=False, two_shot=False):
+    def __init__(self, d, rotate_bytes, max_sets=None, epilogue=False, two_shot=False,
+                 slot_dtype="f32", out_dtype="f32"):
         import torch
 
         import gemv_shot_all_amd as gsa
@@ -120,6 +126,9 @@ class Sets:
         self.W, self.N, self.K, self.B, self.rank = W, N, K, B, d["rank"]
         self.epilogue = epilogue
         self.two_shot = two_shot
+        self.slot_bf16 = slot_dtype == "bf16"
+        self.out_bf16 = out_dtype == "bf16"
+        self.typed = self.slot_bf16 or self.out_bf16
         foot = d["A"].nbytes + d["x"].nbytes + d["slots"].nbytes + 4 * N * B * (2 if two_shot
                                                                                  else 1)
         R = max(1, -(-rotate_bytes // foot) + 1)  # other sets between two uses >= rotate_bytes
@@ -129,7 +138,15 @@ class Sets:
         self.touched = set()  # sets called at least once
         A0 = torch.from_numpy(d["A"].view(np.int16)).cuda()
         x0 = torch.from_numpy(d["x"].view(np.int16)).cuda()
-        s0 = torch.from_numpy(d["slots"]).cuda()
+        if self.slot_bf16:
+            # the peers' values rounded to bf16 (bits); the own slot is written by the call
+            sb = np.zeros(d["slots"].shape, np.uint16)
+            for p in range(W):
+                if p != self.rank:
+                    sb[p] = gi.bf16_bits(d["slots"][p])
+            s0 = torch.from_numpy(sb.view(np.int16)).cuda()
+        else:
+            s0 = torch.from_numpy(d["slots"]).cuda()
         mask = ((1 << W) - 1) & ~(1 << self.rank)
         if two_shot:
             # the other ranks' reduced chunks; the own chunk's rows NaN
@@ -142,9 +159,13 @@ class Sets:
         for _ in range(R):
             self.A.append(A0.clone())
             self.x.append(x0.clone())
-            self.out.append(torch.full((N, B), float("nan"), dtype=torch.float32,
-                                       device="cuda"))
-            buf = gsa.SymmBuffer(W, N, B)
+            if self.out_bf16:
+                self.out.append(torch.full((N, B), 0x7FC0, dtype=torch.int16, device="cuda"))
+            else:
+                self.out.append(torch.full((N, B), float("nan"), dtype=torch.float32,
+                                           device="cuda"))
+            buf = gsa.SymmBuffer(W, N, B, gsa.GSA_DTYPE_BF16 if self.slot_bf16
+                                 else gsa.GSA_DTYPE_F32)
             buf.slots_view().copy_(s0)
             if two_shot:
                 buf.gathered_view().copy_(g0)
@@ -177,6 +198,11 @@ class Sets:
             self.gsa.gsa_gemv_allreduce_two_shot(self.A[j], self.x[j], b.slots, b.pad,
                                                  b.gathered, self.out[j], self.W, self.rank,
                                                  self.N, self.K, self.B)
+        elif self.typed:
+            self.gsa.gsa_gemv_allreduce_dtype(
+                self.A[j], self.x[j], b.slots, b.pad, self.out[j],
+                self.gsa.GSA_DTYPE_BF16 if self.out_bf16 else self.gsa.GSA_DTYPE_F32, self.W,
+                self.rank, self.N, self.K, self.B)
         else:
             self.gsa.gsa_gemv_allreduce(self.A[j], self.x[j], b.slots, b.pad, self.out[j],
                                         self.W, self.rank, self.N, self.K, self.B)
@@ -194,17 +220,20 @@ def check_consistency(sets):
     seeded chunk, copied exactly.  Parity against the oracle at these sizes
     is the GPU tests' job."""
     used = sorted(sets.touched)
-    out0 = sets.out[used[0]].cpu().numpy()
-    ok = bool(np.all(np.isfinite(out0)))
+
+    def bits(t):
+        return t.cpu().numpy().view(np.uint16 if sets.out_bf16 else np.uint32)
+    out0 = bits(sets.out[used[0]])
+    vals = ((out0.astype(np.uint32) << 16).view(np.float32) if sets.out_bf16
+            else out0.view(np.float32))
+    ok = bool(np.all(np.isfinite(vals)))
     for j in used[1::max(1, len(used) // 8)]:
-        ok = ok and np.array_equal(sets.out[j].cpu().numpy().view(np.uint32),
-                                   out0.view(np.uint32))
+        ok = ok and np.array_equal(bits(sets.out[j]), out0)
     if sets.two_shot:
         c = two_shot_chunk_rows(sets.N, sets.W)
         rest = np.ones(sets.N, bool)
         rest[sets.rank * c:(sets.rank + 1) * c] = False
-        ok = ok and np.array_equal(out0[rest].view(np.uint32),
-                                   sets.gathered_in[rest].view(np.uint32))
+        ok = ok and np.array_equal(out0[rest], sets.gathered_in[rest].view(np.uint32))
     if sets.epilogue:
         y = sets.epi_tensors[used[0]][2].float().cpu().numpy()
         ok = ok and bool(np.all(np.isfinite(y)))
@@ -376,7 +405,7 @@ def run_config(cfg, args):
     d = gi.make_inputs(cfg, seed=args.seed, rank=0)
     W, N, K, B = d["W"], d["N"], d["K"], d["B"]
     sets = Sets(d, args.rotate_mib << 20 if not args.warm else 1, args.max_sets, args.epilogue,
-                args.two_shot)
+                args.two_shot, args.slot_dtype, args.out_dtype)
     timer = ColdTimer(args.flush_mib if not args.warm else 0)
     try:
         # Warm-up: exactly args.warmup untimed calls.
@@ -420,9 +449,12 @@ def run_config(cfg, args):
         timer.close()
         sets.close()
 
-    nbytes = alg_bytes(W, N, K, B, args.epilogue, args.two_shot)
+    nbytes = alg_bytes(W, N, K, B, args.epilogue, args.two_shot,
+                       slot_bytes=2 if args.slot_dtype == "bf16" else 4,
+                       out_bytes=2 if args.out_dtype == "bf16" else 4)
     achieved = nbytes / (us_per_call * 1e-6) / 1e9
-    traffic = traffic_from_profile(cfg, args.epilogue, args.two_shot)
+    traffic = traffic_from_profile(cfg, name=profile_name(cfg, args.epilogue, args.two_shot,
+                                                          args.slot_dtype, args.out_dtype))
     line = {
         "metric": METRIC,
         "value": round(us_per_call, 4),
@@ -448,6 +480,7 @@ def run_config(cfg, args):
             "epilogue": ("bias + RMSNorm over rows (eps 1e-5), y in bf16" if args.epilogue
                          else "none"),
             "all_reduce": "two-shot" if args.two_shot else "one-shot",
+            "slots": args.slot_dtype, "out": args.out_dtype,
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
@@ -690,6 +723,11 @@ def main():
     p.add_argument("--two-shot", action="store_true",
                    help="time gsa_gemv_allreduce_two_shot (reduce the own chunk, copy the "
                         "others) instead")
+    p.add_argument("--slot-dtype", choices=("f32", "bf16"), default="f32",
+                   help="element type of the slots (bf16: published and summed as bf16 "
+                        "values, fp32 accumulation)")
+    p.add_argument("--out-dtype", choices=("f32", "bf16"), default="f32",
+                   help="element type of out")
     p.add_argument("--no-probe", action="store_true",
                    help="skip the 1 GiB streaming-read bandwidth reference")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -698,6 +736,8 @@ def main():
     args = p.parse_args()
     if args.epilogue and args.two_shot:
         p.error("--epilogue and --two-shot are separate entry points; pick one")
+    if (args.epilogue or args.two_shot) and (args.slot_dtype != "f32" or args.out_dtype != "f32"):
+        p.error("the epilogue and two-shot calls take fp32 slots and out")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's share of the operator on one MI355X; "
               "multi-GPU runs are not implemented (each rank would run this same "

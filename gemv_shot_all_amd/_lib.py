@@ -27,9 +27,10 @@ GSA_DTYPE_BF16 = 1
 GSA_MOE_MAX_TOKENS = 16
 GSA_MOE_MAX_F = 4088
 
-EXPORTS = ("gsa_symm_alloc", "gsa_symm_free", "gsa_symm_slots", "gsa_symm_signal_pad",
+EXPORTS = ("gsa_symm_alloc", "gsa_symm_alloc_dtype", "gsa_symm_free", "gsa_symm_slots", "gsa_symm_signal_pad",
            "gsa_symm_gathered", "gsa_signal_pad_row_stride", "gsa_signal_pad_reset",
-           "gsa_gemv_allreduce", "gsa_gemv_allreduce_two_shot", "gsa_gemv_allreduce_rmsnorm",
+           "gsa_gemv_allreduce", "gsa_gemv_allreduce_dtype", "gsa_gemv_allreduce_two_shot",
+           "gsa_gemv_allreduce_rmsnorm",
            "gsa_signal_pad_status", "gsa_set_wait_timeout_us", "gsa_strerror",
            "gsa_a2a_pad_words", "gsa_a2a_alloc", "gsa_a2a_free", "gsa_a2a_buffers",
            "gsa_a2a_signal_pads", "gsa_a2a_reset", "gsa_moe_gemm_all_to_all", "gsa_a2a_status")
@@ -67,6 +68,8 @@ def lib():
         ci = ctypes.c_int
         L.gsa_symm_alloc.argtypes = [ci, i64, ci, ctypes.POINTER(vp)]
         L.gsa_symm_alloc.restype = ci
+        L.gsa_symm_alloc_dtype.argtypes = [ci, i64, ci, ci, ctypes.POINTER(vp)]
+        L.gsa_symm_alloc_dtype.restype = ci
         L.gsa_symm_free.argtypes = [vp]
         L.gsa_symm_free.restype = ci
         L.gsa_symm_slots.argtypes = [vp]
@@ -81,6 +84,8 @@ def lib():
         L.gsa_signal_pad_reset.restype = ci
         L.gsa_gemv_allreduce.argtypes = [vp, vp, vp, vp, vp, ci, ci, i64, i64, ci, vp]
         L.gsa_gemv_allreduce.restype = ci
+        L.gsa_gemv_allreduce_dtype.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, i64, i64, ci, vp]
+        L.gsa_gemv_allreduce_dtype.restype = ci
         L.gsa_gemv_allreduce_two_shot.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, i64, i64, ci,
                                                   vp]
         L.gsa_gemv_allreduce_two_shot.restype = ci
@@ -155,6 +160,13 @@ def gsa_symm_alloc(W, N, B):
     return h.value
 
 
+def gsa_symm_alloc_dtype(W, N, B, slot_dtype):
+    h = ctypes.c_void_p()
+    _check(lib().gsa_symm_alloc_dtype(W, N, B, slot_dtype, ctypes.byref(h)),
+           "gsa_symm_alloc_dtype")
+    return h.value
+
+
 def gsa_symm_free(h):
     _check(lib().gsa_symm_free(h), "gsa_symm_free")
 
@@ -199,6 +211,12 @@ def gsa_gemv_allreduce(A_r, x, slots, pad, out, W, rank, N, K, B, stream=None):
     _check(lib().gsa_gemv_allreduce(_ptr(A_r), _ptr(x), _ptr(slots), _ptr(pad), _ptr(out),
                                     W, rank, N, K, B, _stream(stream)),
            "gsa_gemv_allreduce")
+
+
+def gsa_gemv_allreduce_dtype(A_r, x, slots, pad, out, out_dtype, W, rank, N, K, B, stream=None):
+    _check(lib().gsa_gemv_allreduce_dtype(_ptr(A_r), _ptr(x), _ptr(slots), _ptr(pad), _ptr(out),
+                                          out_dtype, W, rank, N, K, B, _stream(stream)),
+           "gsa_gemv_allreduce_dtype")
 
 
 def gsa_gemv_allreduce_two_shot(A_r, x, slots, pad, gathered, out, W, rank, N, K, B,
@@ -262,7 +280,7 @@ def device_view(ptr, shape, dtype):
     import numpy as np
     import torch
     typestr = {torch.float32: "<f4", torch.int32: "<i4", torch.uint8: "|u1",
-               torch.int64: "<i8"}[dtype]
+               torch.int64: "<i8", torch.int16: "<i2"}[dtype]
     del np
     return torch.as_tensor(_DeviceArray(ptr, shape, typestr), device="cuda")
 
@@ -272,9 +290,10 @@ class SymmBuffer:
     variant's gathered chunks), freed on close().  Convenience wrapper over
     gsa_symm_alloc / gsa_symm_free."""
 
-    def __init__(self, W, N, B):
+    def __init__(self, W, N, B, slot_dtype=GSA_DTYPE_F32):
         self.W, self.N, self.B = W, N, B
-        self.handle = gsa_symm_alloc(W, N, B)
+        self.slot_dtype = slot_dtype
+        self.handle = gsa_symm_alloc_dtype(W, N, B, slot_dtype)
         self.slots = gsa_symm_slots(self.handle)
         self.pad = gsa_symm_signal_pad(self.handle)
         self.gathered = gsa_symm_gathered(self.handle)
@@ -282,9 +301,11 @@ class SymmBuffer:
         self.tiles = (N + GSA_FLAG_TILE_ROWS - 1) // GSA_FLAG_TILE_ROWS
 
     def slots_view(self):
-        """torch float32 view (W, N, B) of the slots."""
+        """torch view (W, N, B) of the slots: float32, or int16 holding the
+        bf16 bits for a buffer with bf16 slots."""
         import torch
-        return device_view(self.slots, (self.W, self.N, self.B), torch.float32)
+        dt = torch.int16 if self.slot_dtype == GSA_DTYPE_BF16 else torch.float32
+        return device_view(self.slots, (self.W, self.N, self.B), dt)
 
     def gathered_view(self):
         """torch float32 view (N, B) of the gathered chunks."""

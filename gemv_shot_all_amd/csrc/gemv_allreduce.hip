@@ -116,6 +116,52 @@ __device__ __forceinline__ float dot8(const uint4& a, const uint4& x, float acc)
   return acc;
 }
 
+// fp32 -> bf16 bits, round to nearest, ties to even; a NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0)
+    return (uint16_t)((u >> 16) | 0x0040u);
+  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Slot and output element types.  A buffer's slots hold fp32 or bf16 values
+// (a.slot_bf16) and out is fp32 or bf16 (a.out_bf16); every sum is taken in
+// fp32 either way.  Both flags are uniform over the launch, so each access
+// below is one branch of a uniform condition.
+//   publish_value: y as published into the own slot (its bf16 rounding for
+//                  bf16 slots), which is also the own term of the rank-order
+//                  sum, so that out is the fold of the slots as published;
+//   load_slot:     element i of the slots (i = r * N * B + n * B + b),
+//                  widened exactly to fp32; a device-coherent load;
+//   store_slot:    the device-coherent store of a published value;
+//   store_out:     out[i], rounded to bf16 for a bf16 out.
+__device__ __forceinline__ float bf16_widen(uint16_t bits) {
+  return __uint_as_float((uint32_t)bits << 16);
+}
+__device__ __forceinline__ float publish_value(const GemvArgs& a, float y) {
+  return a.slot_bf16 ? bf16_widen(bf16_rne(y)) : y;
+}
+__device__ __forceinline__ float load_slot(const GemvArgs& a, int64_t i) {
+  if (a.slot_bf16)
+    return bf16_widen(__hip_atomic_load(reinterpret_cast<const uint16_t*>(a.slots) + i,
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  return load_coherent(a.slots + i);
+}
+__device__ __forceinline__ void store_slot(const GemvArgs& a, int64_t i, float yp) {
+  if (a.slot_bf16)
+    __hip_atomic_store(reinterpret_cast<uint16_t*>(a.slots) + i,
+                       (uint16_t)(__float_as_uint(yp) >> 16), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  else
+    store_coherent(a.slots + i, yp);
+}
+__device__ __forceinline__ void store_out(const GemvArgs& a, int64_t i, float o) {
+  if (a.out_bf16)
+    reinterpret_cast<uint16_t*>(a.out)[i] = bf16_rne(o);
+  else
+    a.out[i] = o;
+}
+
 // Word of flag tile t within a rank's row: groups of 4 flag tiles (one
 // 16-row tile), one group per 128-byte line.
 __device__ __forceinline__ int64_t flag_word(int64_t t) {
@@ -184,10 +230,11 @@ __device__ __forceinline__ void issue_peer_tile(const GemvArgs& a, int lane, int
 #pragma unroll
   for (int r = 0; r < kMaxW; ++r) {
     if (copy ? r == 0 : (r < a.W && r != a.rank)) {
-      const float* src = copy ? a.gathered : a.slots + r * NB;
 #pragma unroll
-      for (int i = 0; i < kPerLane<TR>; ++i)
-        if (i < per_lane) v[r][i] = load_coherent(&src[min(first + lane + 64 * i, last)]);
+      for (int i = 0; i < kPerLane<TR>; ++i) {
+        const int64_t e = min(first + lane + 64 * i, last);
+        if (i < per_lane) v[r][i] = copy ? load_coherent(&a.gathered[e]) : load_slot(a, r * NB + e);
+      }
     }
   }
 }
@@ -443,21 +490,24 @@ __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t ti
   const int64_t NB = a.N * a.B;
   const int64_t row0 = tile * TR;
   const FlagSpan fs = flag_span<TR>(a, tile);
-  float* own_slot = a.slots + a.rank * NB;
   bool live[OPL];
+  float yp[OPL];  // y as published (the own term of the sum)
 #pragma unroll
-  for (int e = 0; e < OPL; ++e) live[e] = own[e] && row0 + n[e] < a.N;
+  for (int e = 0; e < OPL; ++e) {
+    live[e] = own[e] && row0 + n[e] < a.N;
+    yp[e] = publish_value(a, y[e]);
+  }
   float o[OPL];
   bool ok[OPL];
   if (own_peers) {
-    // out = ((0 + s_0) + s_1) ... + s_{W-1}, the own term being y (as
-    // published); the same order and operations as one_shot_sum.  Summed
+    // out = ((0 + s_0) + s_1) ... + s_{W-1}, the own term being y as
+    // published; the same order and operations as one_shot_sum.  Summed
     // before the published value is stored, so that waiting for the peer
     // values cannot wait for that store.
     float acc = 0.0f;
 #pragma unroll
     for (int r = 0; r < kMaxW; ++r) {
-      const float t = r == a.rank ? y[0] : pv[r];
+      const float t = r == a.rank ? yp[0] : pv[r];
       acc = acc + (r < a.W ? t : 0.0f);
     }
     o[0] = acc;
@@ -470,7 +520,7 @@ __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t ti
   if (state != kBadOwnRow) {
 #pragma unroll
     for (int e = 0; e < OPL; ++e)
-      if (live[e]) store_coherent(&own_slot[(row0 + n[e]) * a.B + b], y[e]);
+      if (live[e]) store_slot(a, a.rank * NB + (row0 + n[e]) * a.B + b, yp[e]);
   }
   __builtin_amdgcn_sched_barrier(0);
   if (own_peers) {
@@ -479,7 +529,7 @@ __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t ti
       if (a.epi)
         store_coherent(&a.out[i], o[0]);  // read back by the workgroup that finishes last
       else
-        a.out[i] = o[0];
+        store_out(a, i, o[0]);
     }
     wait_vm_le<1>();  // the published value is at the coherence point ...
   } else {
@@ -502,7 +552,7 @@ __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t ti
     if (ok[e] && live[e]) {
       const int64_t i = (row0 + n[e]) * a.B + b;
       if (!TS || owner == a.rank) {
-        o[e] = one_shot_sum<TR>(a, y[e], pe, n[e], b);
+        o[e] = one_shot_sum<TR>(a, yp[e], pe, n[e], b);
         if (TS) store_coherent(&a.gathered[i], o[e]);  // this rank's reduced chunk
       } else {
         o[e] = pe[owner * TR * a.B + n[e] * a.B + b];  // the owner's reduced chunk
@@ -510,7 +560,7 @@ __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t ti
       if (a.epi)
         store_coherent(&a.out[i], o[e]);  // read back by the workgroup that finishes last
       else
-        a.out[i] = o[e];
+        store_out(a, i, o[e]);
     }
   }
   if (TS && owner == a.rank) {
@@ -644,14 +694,6 @@ __device__ __forceinline__ float reduce_scatter64(float (&v)[V], int lane) {
   rs_stage<2, (V >= 32 ? V / 16 : 1)>(v, lane);
   rs_stage<1, (V >= 64 ? V / 32 : 1)>(v, lane);
   return v[0];
-}
-
-// fp32 -> bf16 bits, round to nearest, ties to even; a NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0)
-    return (uint16_t)((u >> 16) | 0x0040u);
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
 // 1 / rms per column from every tile's published partials, computed by the
@@ -1073,7 +1115,7 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
     const int64_t NB = a.N * a.B;
     const int64_t oi = min((row0 + vidx / B) * a.B + vidx % B, NB - 1);
 #pragma unroll
-    for (int r = 0; r < kMaxW; ++r) pv[r] = load_coherent(&a.slots[min(r, a.W - 1) * NB + oi]);
+    for (int r = 0; r < kMaxW; ++r) pv[r] = load_slot(a, min(r, a.W - 1) * NB + oi);
   } else {
 #pragma unroll
     for (int r = 0; r < kMaxW; ++r) pv[r] = 0.0f;
@@ -1215,7 +1257,7 @@ __global__ __launch_bounds__(kLongWaves * 64, kLongWaves / 4) void gemv_ar_long(
   // no faster: 11.93 against 11.86 us per call on the 70B-class shape.)
   float pv[kMaxW];
 #pragma unroll
-  for (int r = 0; r < kMaxW; ++r) pv[r] = load_coherent(&a.slots[min(r, a.W - 1) * NB + oi]);
+  for (int r = 0; r < kMaxW; ++r) pv[r] = load_slot(a, min(r, a.W - 1) * NB + oi);
 
   float acc[R][B];
 #pragma unroll
@@ -1230,19 +1272,19 @@ __global__ __launch_bounds__(kLongWaves * 64, kLongWaves / 4) void gemv_ar_long(
   const float y = reduce_scatter64<VP>(v, lane);
 
   const bool live = owner && orow < a.N;
-  float* own_slot = a.slots + a.rank * NB;
+  const float yp = publish_value(a, y);  // y as published: the own term of the sum
   float outv = 0.0f;
   if (state == kPeersReady) {
     // out = ((0 + s_0) + s_1) ... + s_{W-1}, the own term being y as
     // published; ranks past W - 1 add +0 (acc is never -0).
 #pragma unroll
-    for (int r = 0; r < kMaxW; ++r) outv = outv + (r < a.W ? (r == a.rank ? y : pv[r]) : 0.0f);
+    for (int r = 0; r < kMaxW; ++r) outv = outv + (r < a.W ? (r == a.rank ? yp : pv[r]) : 0.0f);
   }
   __builtin_amdgcn_sched_barrier(0);
-  if (state != kBadOwnRow && live) store_coherent(&own_slot[oi], y);
+  if (state != kBadOwnRow && live) store_slot(a, a.rank * NB + oi, yp);
   __builtin_amdgcn_sched_barrier(0);
   if (state == kPeersReady) {
-    if (live) a.out[oi] = outv;
+    if (live) store_out(a, oi, outv);
     wait_vm_le<1>();  // the published value is at the coherence point (stores complete in order)
   } else {
     wait_vm_all();
@@ -1264,9 +1306,9 @@ __global__ __launch_bounds__(kLongWaves * 64, kLongWaves / 4) void gemv_ar_long(
       float acc2 = 0.0f;
 #pragma unroll
       for (int r = 0; r < kMaxW; ++r) {
-        if (r < a.W) acc2 = acc2 + (r == a.rank ? y : load_coherent(&a.slots[r * NB + oi]));
+        if (r < a.W) acc2 = acc2 + (r == a.rank ? yp : load_slot(a, r * NB + oi));
       }
-      a.out[oi] = acc2;
+      store_out(a, oi, acc2);
     }
   }
 }

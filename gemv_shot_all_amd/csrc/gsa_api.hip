@@ -20,6 +20,7 @@ struct gsa_symm {
   int W;
   int64_t N;
   int B;
+  int slot_dtype;   // GSA_DTYPE_F32 or GSA_DTYPE_BF16
   int64_t row_stride;
   int64_t tiles;
   size_t bytes;
@@ -120,12 +121,14 @@ int64_t gsa_signal_pad_row_stride(int64_t N) {
   return (int64_t)round_up((size_t)groups * GSA_FLAG_GROUP_WORDS, 64);
 }
 
-int gsa_symm_alloc(int W, int64_t N, int B, gsa_symm** out) {
+int gsa_symm_alloc_dtype(int W, int64_t N, int B, int slot_dtype, gsa_symm** out) {
   if (!out || W < 1 || W > GSA_MAX_W || N < 1 || B < 1 || B > GSA_MAX_B) return GSA_EINVAL;
+  if (slot_dtype != GSA_DTYPE_F32 && slot_dtype != GSA_DTYPE_BF16) return GSA_EINVAL;
   if (N > ((int64_t)1 << 40)) return GSA_EINVAL;
   *out = nullptr;
   const int64_t stride = gsa_signal_pad_row_stride(N);
-  const size_t slot_bytes = round_up((size_t)W * (size_t)N * (size_t)B * sizeof(float), kAlign);
+  const size_t elem = slot_dtype == GSA_DTYPE_BF16 ? sizeof(uint16_t) : sizeof(float);
+  const size_t slot_bytes = round_up((size_t)W * (size_t)N * (size_t)B * elem, kAlign);
   const size_t pad_words = GSA_PAD_HEADER_WORDS + 2 * (size_t)W * (size_t)stride;
   const size_t gathered_bytes = round_up((size_t)N * (size_t)B * sizeof(float), kAlign);
   const size_t pad_bytes = round_up(pad_words * sizeof(uint32_t), kAlign);
@@ -154,7 +157,7 @@ int gsa_symm_alloc(int W, int64_t N, int B, gsa_symm** out) {
   float* gathered = reinterpret_cast<float*>(static_cast<char*>(base) + slot_bytes + pad_bytes);
   float* ssq = reinterpret_cast<float*>(static_cast<char*>(base) + slot_bytes + pad_bytes +
                                         gathered_bytes);
-  gsa_symm* h = new gsa_symm{W, N, B, stride, big_tiles_of(N), bytes, base,
+  gsa_symm* h = new gsa_symm{W, N, B, slot_dtype, stride, big_tiles_of(N), bytes, base,
                              static_cast<float*>(base), pad, gathered, ssq, dev};
   std::lock_guard<std::mutex> lk(g_mu);
   g_by_slots[(uintptr_t)h->slots] = h;
@@ -162,6 +165,10 @@ int gsa_symm_alloc(int W, int64_t N, int B, gsa_symm** out) {
   g_handles.insert(h);
   *out = h;
   return GSA_OK;
+}
+
+int gsa_symm_alloc(int W, int64_t N, int B, gsa_symm** out) {
+  return gsa_symm_alloc_dtype(W, N, B, GSA_DTYPE_F32, out);
 }
 
 int gsa_symm_free(gsa_symm* h) {
@@ -223,10 +230,16 @@ namespace {
 
 bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
-// Both entry points: validate, fill the launch arguments, enqueue one kernel.
-int enqueue_call(const uint16_t* A_r, const uint16_t* x, float* slots, uint32_t* pad,
-                 float* gathered, float* out, int W, int rank, int64_t N, int64_t K, int B,
-                 const gsa_epilogue* ep, void* stream) {
+// Every GEMV entry point: validate, fill the launch arguments, enqueue one
+// kernel.  out_dtype is the element type of out; bf16_slots_ok whether the
+// entry point accepts a buffer whose slots are bf16 (the plain one-shot call
+// with element types only; the others take fp32 slots).
+int enqueue_call(const uint16_t* A_r, const uint16_t* x, void* slots_any, uint32_t* pad,
+                 float* gathered, void* out_any, int out_dtype, bool bf16_slots_ok, int W,
+                 int rank, int64_t N, int64_t K, int B, const gsa_epilogue* ep, void* stream) {
+  float* slots = static_cast<float*>(slots_any);
+  float* out = static_cast<float*>(out_any);
+  if (out_dtype != GSA_DTYPE_F32 && out_dtype != GSA_DTYPE_BF16) return GSA_EINVAL;
   // Scalars first: these checks touch no HIP state.
   if (W < 1 || W > GSA_MAX_W || rank < 0 || rank >= W) return GSA_EINVAL;
   if (N < 1 || B < 1 || B > GSA_MAX_B || K < 1 || K % W != 0) return GSA_EINVAL;
@@ -259,6 +272,8 @@ int enqueue_call(const uint16_t* A_r, const uint16_t* x, float* slots, uint32_t*
     std::lock_guard<std::mutex> lk(g_mu);
     gsa_symm* h = find_by_slots(slots);
     if (!h || h->pad != pad || h->W != W || h->N != N || h->B != B) return GSA_EINVAL;
+    if (h->slot_dtype == GSA_DTYPE_BF16 && !bf16_slots_ok) return GSA_EINVAL;
+    a.slot_bf16 = h->slot_dtype == GSA_DTYPE_BF16 ? 1 : 0;
     if (gathered && h->gathered != gathered) return GSA_EINVAL;
     a.row_stride = (int)h->row_stride;
     a.tiles = (int)((N + l.tile_rows - 1) / l.tile_rows);  // == h->tiles for 16-row tiles
@@ -277,6 +292,7 @@ int enqueue_call(const uint16_t* A_r, const uint16_t* x, float* slots, uint32_t*
   a.slots = slots;
   a.pad = pad;
   a.out = out;
+  a.out_bf16 = out_dtype == GSA_DTYPE_BF16 ? 1 : 0;
   a.N = N;
   a.C = C;
   a.B = B;
@@ -307,21 +323,31 @@ extern "C" {
 
 int gsa_gemv_allreduce(const uint16_t* A_r, const uint16_t* x, float* slots, uint32_t* pad,
                        float* out, int W, int rank, int64_t N, int64_t K, int B, void* stream) {
-  return enqueue_call(A_r, x, slots, pad, nullptr, out, W, rank, N, K, B, nullptr, stream);
+  return enqueue_call(A_r, x, slots, pad, nullptr, out, GSA_DTYPE_F32, false, W, rank, N, K, B,
+                      nullptr, stream);
+}
+
+int gsa_gemv_allreduce_dtype(const uint16_t* A_r, const uint16_t* x, void* slots, uint32_t* pad,
+                             void* out, int out_dtype, int W, int rank, int64_t N, int64_t K,
+                             int B, void* stream) {
+  return enqueue_call(A_r, x, slots, pad, nullptr, out, out_dtype, true, W, rank, N, K, B,
+                      nullptr, stream);
 }
 
 int gsa_gemv_allreduce_two_shot(const uint16_t* A_r, const uint16_t* x, float* slots,
                                 uint32_t* pad, float* gathered, float* out, int W, int rank,
                                 int64_t N, int64_t K, int B, void* stream) {
   if (!gathered || !aligned16(gathered)) return GSA_EINVAL;
-  return enqueue_call(A_r, x, slots, pad, gathered, out, W, rank, N, K, B, nullptr, stream);
+  return enqueue_call(A_r, x, slots, pad, gathered, out, GSA_DTYPE_F32, false, W, rank, N, K, B,
+                      nullptr, stream);
 }
 
 int gsa_gemv_allreduce_rmsnorm(const uint16_t* A_r, const uint16_t* x, float* slots,
                                uint32_t* pad, float* out, int W, int rank, int64_t N, int64_t K,
                                int B, const gsa_epilogue* ep, void* stream) {
   if (!ep) return GSA_EINVAL;
-  return enqueue_call(A_r, x, slots, pad, nullptr, out, W, rank, N, K, B, ep, stream);
+  return enqueue_call(A_r, x, slots, pad, nullptr, out, GSA_DTYPE_F32, false, W, rank, N, K, B,
+                      ep, stream);
 }
 
 int gsa_signal_pad_status(const uint32_t* pad, void* stream, int* code, int64_t* tile,

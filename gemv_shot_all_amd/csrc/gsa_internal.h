@@ -47,9 +47,11 @@ enum : uint32_t { kErrTimeout = 1u, kErrState = 2u, kErrEpiWait = 4u, kErrSplit 
 struct GemvArgs {
   const uint16_t* A;      // N x Ks bf16 bits
   const uint16_t* x;      // B x Ks bf16 bits
-  float* slots;           // W x N x B fp32
+  float* slots;           // W x N x B fp32, or bf16 bits if slot_bf16
   uint32_t* pad;          // header + W flag rows
-  float* out;             // N x B fp32
+  float* out;             // N x B fp32, or bf16 bits if out_bf16
+  int slot_bf16;          // the slots hold bf16 values (published y rounded to bf16)
+  int out_bf16;           // out is bf16 (the fp32 sum rounded to nearest, ties to even)
   int64_t N;
   int C;                  // 16-byte chunks per row = Ks / 8
   int B;

@@ -84,6 +84,11 @@ extern "C" {
  * when that fits under this bound and read from memory otherwise. */
 #define GSA_MAX_X_LDS_BYTES (128 * 1024)
 
+/* Element types: of a buffer's slots (gsa_symm_alloc_dtype), of out
+ * (gsa_gemv_allreduce_dtype) and of the fused epilogue's y. */
+#define GSA_DTYPE_F32 0
+#define GSA_DTYPE_BF16 1
+
 typedef struct gsa_symm gsa_symm; /* opaque host-side handle */
 
 /* Allocate one symmetric buffer: W fp32 slots of N x B (n-major) followed by
@@ -94,12 +99,21 @@ typedef struct gsa_symm gsa_symm; /* opaque host-side handle */
  * *out [host] receives the handle.  Errors: GSA_EINVAL, GSA_ENOMEM, GSA_EHIP. */
 int gsa_symm_alloc(int W, int64_t N, int B, gsa_symm **out);
 
+/* gsa_symm_alloc with the slots' element type: GSA_DTYPE_F32 (the slots of
+ * gsa_symm_alloc) or GSA_DTYPE_BF16, W bf16 slots of N x B (n-major, half
+ * the bytes).  A buffer with bf16 slots is used through
+ * gsa_gemv_allreduce_dtype only (the other calls take fp32 slots and reject
+ * it with GSA_EINVAL).  Errors as gsa_symm_alloc; an unknown type is
+ * GSA_EINVAL. */
+int gsa_symm_alloc_dtype(int W, int64_t N, int B, int slot_dtype, gsa_symm **out);
+
 /* Free a handle and its device memory (host-blocking: synchronizes the
  * device first).  NULL is a no-op.  Errors: GSA_EINVAL (unknown handle). */
 int gsa_symm_free(gsa_symm *h);
 
-/* [device] slot 0 of the buffer; slot r starts r*N*B floats later.  NULL for
- * an unknown handle.  The library owns this memory. */
+/* [device] slot 0 of the buffer; slot r starts r*N*B elements later (fp32,
+ * or the 16 bits of each bf16 value for a buffer whose slots are bf16).
+ * NULL for an unknown handle.  The library owns this memory. */
 float *gsa_symm_slots(const gsa_symm *h);
 
 /* [device] signal pad of the buffer (header + flags).  NULL if unknown. */
@@ -148,6 +162,24 @@ int gsa_gemv_allreduce(const uint16_t *A_r, const uint16_t *x, float *slots,
                        uint32_t *pad, float *out, int W, int rank, int64_t N,
                        int64_t K, int B, void *stream);
 
+/* gsa_gemv_allreduce with element types: the "PyTorch Symmetric Memory"
+ * documentation, higher-precision reduction section, takes bf16 values,
+ * accumulates them in fp32 and hands the result back in bf16.  Here:
+ *   - slots [device]: a buffer from gsa_symm_alloc_dtype; if its slots are
+ *     bf16, step 2 publishes y_r rounded to bf16 (to nearest, ties to even)
+ *     and step 5 widens every slot value exactly and sums in fp32 -- the own
+ *     term being the value as published, so out is the fold of the slots as
+ *     they stand after the call;
+ *   - out [device]: N x B of out_dtype (GSA_DTYPE_F32, or GSA_DTYPE_BF16:
+ *     the fp32 sum rounded to nearest, ties to even), 16-byte aligned.
+ * Step 1 accumulates in fp32 in every case.  Everything else (arguments,
+ * limits, protocol, errors) as gsa_gemv_allreduce; GSA_EINVAL also for an
+ * unknown out_dtype.  With fp32 slots and an fp32 out the result is the
+ * same as gsa_gemv_allreduce's, bit for bit. */
+int gsa_gemv_allreduce_dtype(const uint16_t *A_r, const uint16_t *x, void *slots,
+                             uint32_t *pad, void *out, int out_dtype, int W, int rank,
+                             int64_t N, int64_t K, int B, void *stream);
+
 /* The two-stage variant of the same operator: the documentation's op
  * reference lists a two-stage all-reduce (two_shot_all_reduce_) beside the
  * one-shot one, read here as reduce-scatter then all-gather.  Each rank owns
@@ -165,10 +197,6 @@ int gsa_gemv_allreduce(const uint16_t *A_r, const uint16_t *x, float *slots,
 int gsa_gemv_allreduce_two_shot(const uint16_t *A_r, const uint16_t *x, float *slots,
                                 uint32_t *pad, float *gathered, float *out, int W, int rank,
                                 int64_t N, int64_t K, int B, void *stream);
-
-/* Output element types of the fused epilogue. */
-#define GSA_DTYPE_F32 0
-#define GSA_DTYPE_BF16 1
 
 /* What gsa_gemv_allreduce_rmsnorm does after the one-shot sum.  The
  * "PyTorch Symmetric Memory" talk's real-model example follows the

@@ -17,6 +17,16 @@ def test_alg_bytes_one_shot_by_hand():
             bench.alg_bytes(8, 4096, 4096, 1)) == 8 * 4096 + 2 * 4096
 
 
+def test_alg_bytes_bf16_slots_and_out_by_hand():
+    # 70B-class shape with bf16 slots and bf16 out: A 8192 x 3584 bf16, x 4 x
+    # 3584 bf16, own slot, 7 peer slots and out at 2 bytes per element
+    assert bench.alg_bytes(8, 8192, 28672, 4, slot_bytes=2, out_bytes=2) == (
+        8192 * 3584 * 2 + 4 * 3584 * 2 + 8192 * 4 * 2 + 7 * 8192 * 4 * 2 + 8192 * 4 * 2)
+    # bf16 out alone saves 2 bytes per output element
+    assert (bench.alg_bytes(8, 4096, 4096, 1) - bench.alg_bytes(8, 4096, 4096, 1, out_bytes=2)
+            == 2 * 4096)
+
+
 def test_alg_bytes_two_shot_by_hand():
     # rank 0 of 8 owns 512 rows: 7 peers x 512 rows, its 512 published rows,
     # 3584 copied rows
