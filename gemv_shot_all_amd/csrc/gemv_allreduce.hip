@@ -1520,6 +1520,35 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a
   mfma_finish<NW, TS>(a, tile, wave, lane, acc, red, pe, elds, s_ctl, &s_epi_k);
 }
 
+// One-GPU stand-in for a peer's zero-copy push (the fused-operators page:
+// results written straight into peer memory, then signalled): one
+// workgroup spins `delay_ticks` of device wall-clock time, stores `values`
+// into slot `peer` with device-coherent stores, waits until every store of
+// the workgroup is complete (vmcnt(0), then the barrier), and only then
+// stores `epoch` into each of peer's flags.  The spin is bounded by its
+// argument, so the kernel always ends.
+__global__ __launch_bounds__(256) void peer_publish_kernel(float* slots, uint32_t* pad,
+                                                           const void* values, int peer,
+                                                           int64_t NB, int slot_bf16,
+                                                           int row_stride, int64_t nflags,
+                                                           uint32_t epoch, uint64_t delay_ticks) {
+  const uint64_t t0 = wall_clock64();
+  while (wall_clock64() - t0 < delay_ticks) __builtin_amdgcn_s_sleep(32);
+  const int64_t base = (int64_t)peer * NB;
+  for (int64_t i = threadIdx.x; i < NB; i += blockDim.x) {
+    if (slot_bf16)
+      __hip_atomic_store(reinterpret_cast<uint16_t*>(slots) + base + i,
+                         static_cast<const uint16_t*>(values)[i], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    else
+      store_coherent(slots + base + i, static_cast<const float*>(values)[i]);
+  }
+  wait_vm_all();
+  __syncthreads();  // every value is at the coherence point before any flag
+  uint32_t* row = pad + GSA_PAD_HEADER_WORDS + (int64_t)peer * row_stride;
+  for (int64_t t = threadIdx.x; t < nflags; t += blockDim.x) store_flag(row + flag_word(t), epoch);
+}
+
 __global__ void pad_reset_kernel(uint32_t* pad, int W, int row_stride, uint32_t mask,
                                  uint32_t* epi_tail, int64_t tail_words) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1652,6 +1681,14 @@ bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, Launch* ou
 hipError_t launch_gemv(const Launch& l, const GemvArgs& a, hipStream_t s) {
   void* args[] = {const_cast<GemvArgs*>(&a)};
   return hipLaunchKernel(l.kernel, dim3((unsigned)a.tiles), dim3(l.block), args, l.lds_bytes, s);
+}
+
+hipError_t launch_peer_publish(float* slots, uint32_t* pad, const void* values, int peer,
+                               int64_t NB, bool slot_bf16, int row_stride, int64_t nflags,
+                               uint32_t epoch, uint64_t delay_ticks, hipStream_t s) {
+  hipLaunchKernelGGL(peer_publish_kernel, dim3(1), dim3(256), 0, s, slots, pad, values, peer, NB,
+                     slot_bf16 ? 1 : 0, row_stride, nflags, epoch, delay_ticks);
+  return hipGetLastError();
 }
 
 hipError_t launch_pad_reset(uint32_t* pad, int W, int row_stride, int tiles,

@@ -350,6 +350,36 @@ int gsa_gemv_allreduce_rmsnorm(const uint16_t* A_r, const uint16_t* x, float* sl
                       ep, stream);
 }
 
+int gsa_peer_publish(void* slots, uint32_t* pad, const void* values, int W, int peer, int64_t N,
+                     int B, uint32_t epoch, uint32_t delay_us, void* stream) {
+  if (!slots || !pad || !values || W < 1 || W > GSA_MAX_W || peer < 0 || peer >= W || N < 1 ||
+      B < 1 || B > GSA_MAX_B || delay_us > 1000000u)
+    return GSA_EINVAL;
+  bool bf16;
+  int64_t stride;
+  {
+    std::lock_guard<std::mutex> lk(g_mu);
+    gsa_symm* h = find_by_slots(slots);
+    if (!h || h->pad != pad || h->W != W || h->N != N || h->B != B) return GSA_EINVAL;
+    bf16 = h->slot_dtype == GSA_DTYPE_BF16;
+    stride = h->row_stride;
+  }
+  if (((uintptr_t)values & (bf16 ? 1u : 3u)) != 0) return GSA_EINVAL;
+  uint64_t ticks = 0;
+  if (delay_us > 0) {
+    const int rc = ticks_for(delay_us, &ticks);
+    if (rc != GSA_OK) return rc;
+  }
+  const hipError_t e = gsa::launch_peer_publish(
+      static_cast<float*>(slots), pad, values, peer, N * (int64_t)B, bf16, (int)stride,
+      tiles_of(N), epoch, ticks, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return GSA_EHIP;
+  }
+  return GSA_OK;
+}
+
 int gsa_signal_pad_status(const uint32_t* pad, void* stream, int* code, int64_t* tile,
                           int* peer) {
   if (!pad || !code || !tile || !peer) return GSA_EINVAL;

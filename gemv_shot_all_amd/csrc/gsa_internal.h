@@ -98,6 +98,10 @@ bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, Launch* ou
 size_t gemv_lds_bytes(int W, int B, int C, bool epi, int tile_rows);
 
 hipError_t launch_gemv(const Launch& l, const GemvArgs& a, hipStream_t s);
+// The one-GPU stand-in for a peer's push (see gsa_peer_publish).
+hipError_t launch_peer_publish(float* slots, uint32_t* pad, const void* values, int peer,
+                               int64_t NB, bool slot_bf16, int row_stride, int64_t nflags,
+                               uint32_t epoch, uint64_t delay_ticks, hipStream_t s);
 // Also clears the fused epilogue's scratch after its records (flags and
 // counts), so the next call starts counting from zero.
 hipError_t launch_pad_reset(uint32_t* pad, int W, int row_stride, int tiles,

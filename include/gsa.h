@@ -237,6 +237,23 @@ int gsa_gemv_allreduce_rmsnorm(const uint16_t *A_r, const uint16_t *x, float *sl
                                uint32_t *pad, float *out, int W, int rank, int64_t N,
                                int64_t K, int B, const gsa_epilogue *ep, void *stream);
 
+/* One-GPU stand-in for a peer's zero-copy push, for tests of the signal-pad
+ * protocol.  The fused-operators page has each rank write its finished
+ * results straight into the peers' memory and signal them; the
+ * documentation's custom-kernel section asks that a peer's writes be visible
+ * before it signals.  On `stream`, one workgroup spins for delay_us
+ * microseconds of device wall-clock time (0 <= delay_us <= 1000000), stores
+ * `values` [device] (N x B, n-major, of the buffer's slot element type: fp32,
+ * or bf16 bits) into slot `peer` with device-coherent stores, waits until
+ * they are complete, and then stores `epoch` into every flag of pad row
+ * `peer` (flag tiles 0..ceil(N/4)-1).  Run on a second stream it publishes
+ * while a fused call on another stream is already waiting.  slots, pad [device]:
+ * one buffer of (W, N, B); `values` must stay valid until the kernel ran.
+ * The kernel always ends.  Errors: GSA_EINVAL (unknown buffer, sizes, peer
+ * out of range, misaligned values, delay too long), GSA_EHIP. */
+int gsa_peer_publish(void *slots, uint32_t *pad, const void *values, int W, int peer,
+                     int64_t N, int B, uint32_t epoch, uint32_t delay_us, void *stream);
+
 /* Read the pad's status words after the work queued on `stream` has finished
  * (synchronizes `stream`).  *code [host] := GSA_ESTATE if any call found its
  * own flag row unusable (then *tile := the smallest such flag tile, *peer :=

@@ -1,0 +1,148 @@
+"""A peer publishes while the fused call is already waiting for it (needs an
+MI355X).
+
+The documentation's custom-kernel section asks that a kernel synchronise with
+its peers' writes before it reads them, and the symmetric-memory talk names
+visibility of every read and write as the hard part.  Here one peer is
+withheld at the reset (flags 0, its slot poisoned with NaN).  On a second
+stream of the same priority, gsa_peer_publish -- the one-GPU stand-in for
+that peer's push -- spins a few milliseconds, writes the peer's slot and then
+raises its flags; the fused call, launched on another stream right after,
+finds the flags down, waits (bounded) and must then read the late values:
+out has to be the oracle's fold of the slots as they stand after both
+kernels, with no NaN from the poisoned slot, and the call's own duration on
+its stream shows that it waited.  Small grids, so both kernels are resident
+together; every wait is bounded, so every kernel ends either way."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import gemv_shot_all_amd as gsa
+import gsa_inputs as gi
+import oracle
+from tests.gpu_util import all_but, to_dev
+
+pytestmark = pytest.mark.gpu
+
+DELAY_US = 5000
+
+
+def _say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def streams():
+    """Two default-priority streams that the GPU runs at the same time.  The
+    runtime maps streams onto a few hardware queues, and two streams on one
+    queue run one after the other; a pair is kept only if a small kernel on
+    the second completes while a bounded sleep on the first still runs."""
+    for _ in range(8):
+        s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            torch.cuda._sleep(50_000_000)          # bounded: ~20 ms of shader clock
+        with torch.cuda.stream(s2):
+            torch.ones(1, device="cuda").add_(1.0)
+        s2.synchronize()
+        concurrent = not s1.query()
+        torch.cuda.synchronize()
+        if concurrent:
+            return s1, s2
+    pytest.skip("no two streams ran concurrently on this device")
+
+
+CASES = [
+    # (Ks, B, slot dtype): one per kernel tier
+    (128, 2, gsa.GSA_DTYPE_F32),     # 4-row tiles
+    (1024, 3, gsa.GSA_DTYPE_F32),    # 16-row middle tier, 4 waves
+    (1024, 8, gsa.GSA_DTYPE_F32),    # 16-row middle tier, peer tile through LDS
+    (3584, 4, gsa.GSA_DTYPE_F32),    # 32-row long tier
+    (512, 16, gsa.GSA_DTYPE_F32),    # MFMA
+    (3584, 4, gsa.GSA_DTYPE_BF16),   # long tier, bf16 slots
+    (128, 1, gsa.GSA_DTYPE_BF16),    # 4-row tiles, bf16 slots
+]
+
+
+@pytest.mark.parametrize("Ks,B,slot_dtype", CASES)
+def test_late_peer_values_are_read(Ks, B, slot_dtype, streams):
+    W, rank, late, N = 4, 1, 3, 64
+    bf16 = slot_dtype == gsa.GSA_DTYPE_BF16
+    _say(f"[late peer] Ks={Ks} B={B} slots={'bf16' if bf16 else 'f32'}")
+    d = gi.make_shard_inputs(W, N, Ks, B, seed=21, cfg_id=4000 + Ks + B, rank=rank)
+    if bf16:
+        slots_in = np.zeros(d["slots"].shape, np.uint16)
+        for p in range(W):
+            slots_in[p] = gi.bf16_bits(d["slots"][p]) if p != rank else 0x7FC0
+        slots_in[late] = 0x7FC0                      # poisoned until the late push
+        late_vals = gi.bf16_bits(d["slots"][late])
+        dev_slots = torch.from_numpy(slots_in.view(np.int16)).cuda()
+        dev_late = torch.from_numpy(late_vals.view(np.int16)).cuda()
+        out = torch.full((N, B), 0x7FC0, dtype=torch.int16, device="cuda")
+        out_dtype = gsa.GSA_DTYPE_BF16
+    else:
+        slots_in = d["slots"].copy()
+        slots_in[late] = np.nan
+        late_vals = d["slots"][late].copy()
+        dev_slots = torch.from_numpy(slots_in).cuda()
+        dev_late = torch.from_numpy(late_vals).cuda()
+        out = torch.full((N, B), float("nan"), dtype=torch.float32, device="cuda")
+        out_dtype = gsa.GSA_DTYPE_F32
+    A, x = to_dev(d["A"]), to_dev(d["x"])
+    mask = all_but(W, rank) & ~(1 << late)
+    with gsa.SymmBuffer(W, N, B, slot_dtype) as buf:
+        buf.slots_view().copy_(dev_slots)
+        buf.reset(mask)
+        torch.cuda.synchronize()
+        s_peer, s_call = streams
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        # the epoch this rank's call will wait for: its own flag (0) + 1
+        gsa.gsa_peer_publish(buf.slots, buf.pad, dev_late, W, late, N, B, 1, DELAY_US,
+                             stream=s_peer)
+        ev0.record(s_call)
+        gsa.gsa_gemv_allreduce_dtype(A, x, buf.slots, buf.pad, out, out_dtype, W, rank, N,
+                                     Ks * W, B, stream=s_call)
+        ev1.record(s_call)
+        torch.cuda.synchronize()
+        waited_ms = ev0.elapsed_time(ev1)
+        status = buf.status()
+        slots_out = buf.slots_view().cpu().numpy()
+        flags = buf.flags()
+    got = out.cpu().numpy()
+    assert status == (gsa.GSA_OK, -1, -1), f"status {status}"
+    o = oracle.load()
+    if bf16:
+        slots_out = slots_out.view(np.uint16)
+        got = got.view(np.uint16)
+        assert np.array_equal(slots_out[late], late_vals), "the late values must be in the slot"
+        want = o.to_bf16(o.fold_bf16(slots_out))
+        assert np.array_equal(got, want), "out must be the fold with the late values"
+        assert not np.any(got == 0x7FC0), "a poisoned (stale) value reached out"
+        widened = (slots_in.astype(np.uint32) << 16).view(np.float32).copy()
+        widened[late] = (late_vals.astype(np.uint32) << 16).view(np.float32)
+        y64, abs64, out64 = o.gemv_allreduce(d["A"], d["x"], widened, rank)
+        own = ((slots_out[rank].astype(np.uint32) << 16).view(np.float32)).astype(np.float64)
+        assert np.all(np.abs(own - y64) <= oracle.bound_bf16(abs64, y64))
+    else:
+        assert np.array_equal(slots_out[late].view(np.uint32), late_vals.view(np.uint32))
+        fold = o.fold_f32(slots_out)
+        assert np.array_equal(got.view(np.uint32), fold.view(np.uint32)), (
+            "out must be the fold of the slots with the late values")
+        assert np.all(np.isfinite(got)), "a poisoned (stale) value reached out"
+        full = slots_in.copy()
+        full[late] = late_vals
+        y64, abs64, out64 = o.gemv_allreduce(d["A"], d["x"], full, rank)
+        bnd = oracle.bound(abs64)
+        mag = np.abs(np.delete(full, rank, axis=0)).astype(np.float64).sum(0) + np.abs(y64)
+        assert np.all(np.abs(got - out64) <= bnd + W * 2.0 ** -24 * mag)
+    expect = oracle.pad_after_reset(W, N, mask)
+    expect[rank, :] = 1
+    expect[late, :] = 1
+    assert np.array_equal(flags, expect), "flags: own row 1, the late peer's row 1"
+    # The call found the peer's flags down and waited for the push: its
+    # duration on its own stream spans part of the delay.
+    assert waited_ms >= 0.2, f"the call did not wait for the late peer ({waited_ms:.3f} ms)"
+    _say(f"[late peer] waited {waited_ms:.2f} ms")
