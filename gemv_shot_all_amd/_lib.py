@@ -30,7 +30,7 @@ GSA_MOE_MAX_F = 4088
 EXPORTS = ("gsa_symm_alloc", "gsa_symm_alloc_dtype", "gsa_symm_free", "gsa_symm_slots", "gsa_symm_signal_pad",
            "gsa_symm_gathered", "gsa_signal_pad_row_stride", "gsa_signal_pad_reset",
            "gsa_gemv_allreduce", "gsa_gemv_allreduce_dtype", "gsa_gemv_allreduce_two_shot",
-           "gsa_gemv_allreduce_rmsnorm",
+           "gsa_gemv_allreduce_rmsnorm", "gsa_gemv_allreduce_rmsnorm_noalloc",
            "gsa_peer_publish", "gsa_signal_pad_status", "gsa_set_wait_timeout_us",
            "gsa_strerror",
            "gsa_a2a_pad_words", "gsa_a2a_alloc", "gsa_a2a_free", "gsa_a2a_buffers",
@@ -93,6 +93,8 @@ def lib():
         L.gsa_gemv_allreduce_rmsnorm.argtypes = [vp, vp, vp, vp, vp, ci, ci, i64, i64, ci,
                                                  ctypes.POINTER(gsa_epilogue), vp]
         L.gsa_gemv_allreduce_rmsnorm.restype = ci
+        L.gsa_gemv_allreduce_rmsnorm_noalloc.argtypes = L.gsa_gemv_allreduce_rmsnorm.argtypes
+        L.gsa_gemv_allreduce_rmsnorm_noalloc.restype = ci
         L.gsa_peer_publish.argtypes = [vp, vp, vp, ci, ci, i64, ci, u32, u32, vp]
         L.gsa_peer_publish.restype = ci
         L.gsa_signal_pad_status.argtypes = [vp, vp, ctypes.POINTER(ci),
@@ -255,6 +257,17 @@ def gsa_gemv_allreduce_rmsnorm(A_r, x, slots, pad, out, W, rank, N, K, B, ep, st
 def gsa_peer_publish(slots, pad, values, W, peer, N, B, epoch, delay_us, stream=None):
     _check(lib().gsa_peer_publish(_ptr(slots), _ptr(pad), _ptr(values), W, peer, N, B, epoch,
                                   delay_us, _stream(stream)), "gsa_peer_publish")
+
+
+def gsa_gemv_allreduce_rmsnorm_noalloc(A_r, x, slots, pad, out, W, rank, N, K, B, ep,
+                                       stream=None):
+    """As gsa_gemv_allreduce_rmsnorm, with the epilogue's scratch in the
+    library's static device array (no allocation)."""
+    _check(lib().gsa_gemv_allreduce_rmsnorm_noalloc(_ptr(A_r), _ptr(x), _ptr(slots), _ptr(pad),
+                                                    _ptr(out), W, rank, N, K, B,
+                                                    None if ep is None else ctypes.byref(ep),
+                                                    _stream(stream)),
+           "gsa_gemv_allreduce_rmsnorm_noalloc")
 
 
 def gsa_signal_pad_status(pad, stream=None):

@@ -1691,6 +1691,17 @@ hipError_t launch_peer_publish(float* slots, uint32_t* pad, const void* values, 
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+hipError_t launch_clear_words(uint32_t* p, int64_t n, hipStream_t s) {
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL(clear_words_kernel, dim3(grid), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_pad_reset(uint32_t* pad, int W, int row_stride, int tiles,
                             uint32_t published_mask, float* epi_scratch, hipStream_t s) {
   uint32_t* epi_tail = reinterpret_cast<uint32_t*>(epi_scratch + epi_inv_off(tiles));

@@ -113,6 +113,44 @@ int ticks_for(uint32_t us, uint64_t* ticks) {
 
 }  // namespace
 
+// The entry point that allocates nothing (gsa_gemv_allreduce_rmsnorm_noalloc)
+// keeps the fused epilogue's scratch -- one record of partial sums per
+// 16-row tile, then the 1/rms copies and the completion counts -- in this
+// file-scope device array instead of the buffer's own scratch.  Each device
+// holds its own copy until the process ends.  Host code never uses the
+// array's name as an address: the address comes from hipGetSymbolAddress,
+// once per device (g_scratch_ptr), with that device current.
+namespace {
+constexpr int64_t kNoAllocMaxTiles = 2048;  // 16-row tiles: N <= 32768
+constexpr int64_t kNoAllocScratchWords = gsa::epi_scratch_words(kNoAllocMaxTiles);
+}  // namespace
+static __device__ __align__(256) float scratch[kNoAllocScratchWords];
+
+namespace {
+std::unordered_map<int, float*> g_scratch_ptr;  // device -> address of its `scratch`
+
+// The address of this device's `scratch` (looked up on the first call on
+// the device).  No allocation.
+int scratch_of_current_device(float** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GSA_EHIP;
+  std::lock_guard<std::mutex> lk(g_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it != g_scratch_ptr.end()) {
+    *out = it->second;
+    return GSA_OK;
+  }
+  void* ptr = nullptr;
+  if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+    (void)hipGetLastError();
+    return GSA_EHIP;
+  }
+  g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  *out = static_cast<float*>(ptr);
+  return GSA_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int64_t gsa_signal_pad_row_stride(int64_t N) {
@@ -234,9 +272,13 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 // kernel.  out_dtype is the element type of out; bf16_slots_ok whether the
 // entry point accepts a buffer whose slots are bf16 (the plain one-shot call
 // with element types only; the others take fp32 slots).
+// epi_scratch: the epilogue's scratch to use instead of the buffer's own
+// (the no-allocation entry point); its counts and 1/rms copies are cleared
+// by a small kernel ahead of the call.
 int enqueue_call(const uint16_t* A_r, const uint16_t* x, void* slots_any, uint32_t* pad,
                  float* gathered, void* out_any, int out_dtype, bool bf16_slots_ok, int W,
-                 int rank, int64_t N, int64_t K, int B, const gsa_epilogue* ep, void* stream) {
+                 int rank, int64_t N, int64_t K, int B, const gsa_epilogue* ep, void* stream,
+                 float* epi_scratch = nullptr) {
   float* slots = static_cast<float*>(slots_any);
   float* out = static_cast<float*>(out_any);
   if (out_dtype != GSA_DTYPE_F32 && out_dtype != GSA_DTYPE_BF16) return GSA_EINVAL;
@@ -309,7 +351,18 @@ int enqueue_call(const uint16_t* A_r, const uint16_t* x, void* slots_any, uint32
   a.inv_rms = ep ? ep->inv_rms : nullptr;
   int rc = ticks_for(g_timeout_us.load(std::memory_order_relaxed), &a.timeout_ticks);
   if (rc != GSA_OK) return rc;
-  hipError_t e = gsa::launch_gemv(l, a, static_cast<hipStream_t>(stream));
+  hipError_t e = hipSuccess;
+  if (epi_scratch) {
+    // The shared scratch's counts start at zero for every call (the
+    // buffer's own scratch counts calls instead); the records are written
+    // whole by every call.
+    a.ssq = epi_scratch;
+    const int64_t tiles = a.tiles;
+    e = gsa::launch_clear_words(reinterpret_cast<uint32_t*>(epi_scratch + gsa::epi_inv_off(tiles)),
+                                gsa::epi_scratch_words(tiles) - gsa::epi_inv_off(tiles),
+                                static_cast<hipStream_t>(stream));
+  }
+  if (e == hipSuccess) e = gsa::launch_gemv(l, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     (void)hipGetLastError();
     return GSA_EHIP;
@@ -378,6 +431,19 @@ int gsa_peer_publish(void* slots, uint32_t* pad, const void* values, int W, int 
     return GSA_EHIP;
   }
   return GSA_OK;
+}
+
+int gsa_gemv_allreduce_rmsnorm_noalloc(const uint16_t* A_r, const uint16_t* x, float* slots,
+                                       uint32_t* pad, float* out, int W, int rank, int64_t N,
+                                       int64_t K, int B, const gsa_epilogue* ep, void* stream) {
+  if (!ep) return GSA_EINVAL;
+  // The epilogue's 16-row tiles must fit the static scratch.
+  if (N < 1 || big_tiles_of(N) > kNoAllocMaxTiles) return GSA_EINVAL;
+  float* sc = nullptr;
+  const int rc = scratch_of_current_device(&sc);
+  if (rc != GSA_OK) return rc;
+  return enqueue_call(A_r, x, slots, pad, nullptr, out, GSA_DTYPE_F32, false, W, rank, N, K, B,
+                      ep, stream, sc);
 }
 
 int gsa_signal_pad_status(const uint32_t* pad, void* stream, int* code, int64_t* tile,

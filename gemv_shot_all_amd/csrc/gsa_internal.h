@@ -98,6 +98,8 @@ bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, Launch* ou
 size_t gemv_lds_bytes(int W, int B, int C, bool epi, int tile_rows);
 
 hipError_t launch_gemv(const Launch& l, const GemvArgs& a, hipStream_t s);
+// Zero n words at p with a small kernel (graph-capturable, unlike a memset node).
+hipError_t launch_clear_words(uint32_t* p, int64_t n, hipStream_t s);
 // The one-GPU stand-in for a peer's push (see gsa_peer_publish).
 hipError_t launch_peer_publish(float* slots, uint32_t* pad, const void* values, int peer,
                                int64_t NB, bool slot_bf16, int row_stride, int64_t nflags,

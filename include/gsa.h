@@ -254,6 +254,23 @@ int gsa_gemv_allreduce_rmsnorm(const uint16_t *A_r, const uint16_t *x, float *sl
 int gsa_peer_publish(void *slots, uint32_t *pad, const void *values, int W, int peer,
                      int64_t N, int B, uint32_t epoch, uint32_t delay_us, void *stream);
 
+/* gsa_gemv_allreduce_rmsnorm for callers that cannot allocate device memory
+ * or have the library hold any per buffer for them: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  Same
+ * arguments, contract and results (bit for bit) as
+ * gsa_gemv_allreduce_rmsnorm; the difference is the epilogue's scratch (the
+ * partial sums of squares per 16-row tile, the published 1/rms and the
+ * completion counts).  It lives in one file-scope device array of the
+ * library, at most 2048 tiles' worth (N <= 32768; larger N: GSA_EINVAL),
+ * 280 KiB, which every GPU the library runs on holds until the process
+ * ends.  Every call first clears the array's counts with a small kernel (so
+ * a call is two kernels on `stream`) and allocates nothing.  All calls on
+ * one GPU share the array, which keeps the last call's contents: calls that
+ * overlap on one GPU (other streams) race and must not be issued. */
+int gsa_gemv_allreduce_rmsnorm_noalloc(const uint16_t *A_r, const uint16_t *x, float *slots,
+                                       uint32_t *pad, float *out, int W, int rank, int64_t N,
+                                       int64_t K, int B, const gsa_epilogue *ep, void *stream);
+
 /* Read the pad's status words after the work queued on `stream` has finished
  * (synchronizes `stream`).  *code [host] := GSA_ESTATE if any call found its
  * own flag row unusable (then *tile := the smallest such flag tile, *peer :=
