@@ -24,7 +24,7 @@ GSA_MAX_B = 16
 GSA_MAX_X_LDS_BYTES = 128 * 1024
 GSA_DTYPE_F32 = 0
 GSA_DTYPE_BF16 = 1
-GSA_MOE_MAX_TOKENS = 16
+GSA_MOE_MAX_TOKENS = 256
 GSA_MOE_MAX_F = 4088
 
 EXPORTS = ("gsa_symm_alloc", "gsa_symm_alloc_dtype", "gsa_symm_free", "gsa_symm_slots", "gsa_symm_signal_pad",

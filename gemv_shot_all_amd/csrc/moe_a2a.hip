@@ -4,13 +4,15 @@
 // Rank `rank` holds ne experts.  A workgroup owns local expert e and TPW
 // consecutive 16-feature tiles t0 .. t0 + TPW - 1.  Inside one launch it
 //   a. reads the expert's split table (one segment per source rank), checks
-//      it, and lays out its M <= 16 tokens: token j's row in X and the row
-//      of its source rank's combine buffer that receives it;
-//   b. copies the tokens' rows of X into LDS (each compute wave its own
-//      k-slice, straight from memory with LDS DMA) and streams each tile's
+//      it, and lays out its M <= GSA_MOE_MAX_TOKENS tokens: token j's row in X
+//      and the row of its source rank's combine buffer that receives it;
+//   b. for each tile of 16 tokens (the B operand's 16 columns): copies the
+//      tokens' rows of X into LDS (each compute wave its own k-slice,
+//      straight from memory with LDS DMA) and streams each feature tile's
 //      16 weight rows with v_mfma_f32_16x16x32_bf16 (weights as the A
 //      operand, tokens as the B operand, fp32 accumulation), the waves'
-//      partials summed in wave order;
+//      partials summed in wave order -- the weights of a later token tile
+//      come back from L2, where the first one left them;
 //   c. stores each token's results into its source rank's combine buffer,
 //      waits for the stores, raises flag (rank, e, t) of each tile in every
 //      rank's pad, and waits (bounded) for flag (p, e, t) of every other
@@ -37,9 +39,10 @@
 namespace gsa {
 namespace {
 
-constexpr int kTok = GSA_MOE_MAX_TOKENS;  // the MFMA B operand's 16 columns
-constexpr int kWaves = 4;                 // compute waves per workgroup
-static_assert(kTok == 16, "one 16 x 16 x 32 MFMA tile of tokens");
+constexpr int kTok = 16;                     // tokens per MFMA tile: the B operand's 16 columns
+constexpr int kMaxTok = GSA_MOE_MAX_TOKENS;  // tokens one local expert takes per call
+constexpr int kWaves = 4;                    // compute waves per workgroup
+static_assert(kMaxTok % kTok == 0, "whole token tiles");
 
 __device__ __forceinline__ uint32_t* moe_flag(const MoeArgs& a, int pad, int src, int e, int t) {
   return a.pads + (int64_t)pad * a.pad_words + GSA_PAD_HEADER_WORDS +
@@ -82,8 +85,8 @@ __device__ void moe_wait_peers(const MoeArgs& a, int lane, int e, int t0, int nt
 template <int TPW, int RING>
 __global__ __launch_bounds__(kWaves * 64) void moe_gemm_a2a(MoeArgs a) {
   extern __shared__ uint4 lds[];
-  __shared__ int64_t s_xrow[kTok];  // token j: its row of X
-  __shared__ int64_t s_dst[kTok];   // token j: first element of its combine row
+  __shared__ int64_t s_xrow[kMaxTok];  // token j: its row of X
+  __shared__ int64_t s_dst[kMaxTok];   // token j: first element of its combine row
   __shared__ uint32_t s_ctl[4];     // -, ok, M
   __shared__ uint32_t s_ep[TPW];    // epoch of each tile
 
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(kWaves * 64) void moe_gemm_a2a(MoeArgs a) {
     const int64_t len = a.splits[e * a.W + s];
     const int64_t ioff = a.splits[(int64_t)a.ne * a.W + e * a.W + s];
     const int64_t doff = a.dst_off[(int64_t)s * a.ne + e];
-    const bool bad = lane < a.W && (len < 0 || ioff < 0 || doff < 0 || len > kTok ||
+    const bool bad = lane < a.W && (len < 0 || ioff < 0 || doff < 0 || len > kMaxTok ||
                                     ioff + len > a.rows_in || doff + len > a.rows_out);
     const int mine = (lane < a.W && !bad) ? (int)len : 0;
     int before = 0, M = 0;  // rows of the lanes below this one, and in total
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(kWaves * 64) void moe_gemm_a2a(MoeArgs a) {
       before += r < lane ? lr : 0;
       M += lr;
     }
-    const bool splits_ok = __ballot(bad) == 0 && M <= kTok;
+    const bool splits_ok = __ballot(bad) == 0 && M <= kMaxTok;
     const uint32_t own = __hip_atomic_load(moe_flag(a, a.rank, a.rank, e, t0 + min(lane, nt - 1)),
                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // tiles whose own flag row is marked published or has its epochs exhausted
@@ -154,13 +157,7 @@ __global__ __launch_bounds__(kWaves * 64) void moe_gemm_a2a(MoeArgs a) {
     const int c_begin = min(4 * s_begin, C);
     const int c_end = min(4 * (s_begin + n_steps), C);
 
-    // This wave's k-slice of every token row, straight into LDS.
     const uint4* xg = reinterpret_cast<const uint4*>(a.X);
-    for (int c0 = c_begin; c0 < c_end; c0 += 64) {
-      if (c0 + lane < c_end) {
-        for (int j = 0; j < M; ++j) lds_dma16(xg + s_xrow[j] * C + c0 + lane, lds + j * CP + c0);
-      }
-    }
     const uint16_t* w_e = a.Wd + (int64_t)e * a.H * a.F;
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(w_e, (uint32_t)(a.H * a.F * 2));
     const int kq = lane >> 4;
@@ -170,72 +167,86 @@ __global__ __launch_bounds__(kWaves * 64) void moe_gemm_a2a(MoeArgs a) {
     // bytes (half a 128-byte line) of each of 16 rows, and the next step
     // reads the other halves; without the non-temporal hint those lines are
     // still in L2 when it asks (measured 204 -> 182 us on the DeepSeek-V3-like
-    // shape, 17.0 -> 16.6 us on the Qwen3-30B-A3B-like one).
+    // shape, 17.0 -> 16.6 us on the Qwen3-30B-A3B-like one), and a second
+    // token tile finds them there too.
     const uint32_t kOutOfRange = 0x80000000u;  // past any weight: reads zeros
     auto a_off = [&](int j, int q) {
       return j < n_steps ? a_row + (uint32_t)q * tile_bytes + (uint32_t)(s_begin + j) * 64u : kOutOfRange;
     };
-    uint4 ring[RING][TPW];
-#pragma unroll
-    for (int u = 0; u < RING; ++u)
-#pragma unroll
-      for (int q = 0; q < TPW; ++q) ring[u][q] = buf_load16_cached(ra, a_off(u, q));
-    // The x copies went out before the ring loads: once at most RING loads
-    // are outstanding they have landed.
-    wait_vm_le<RING * TPW>();
-    for (int c = c_begin + lane; c < c_end; c += 64)
-      for (int j = M; j < kTok; ++j) lds[j * CP + c] = make_uint4(0u, 0u, 0u, 0u);
-    if (lane < kTok) lds[lane * CP + C] = make_uint4(0u, 0u, 0u, 0u);
-
     const int xrow = (lane & 15) * CP;
-    f32x4_t acc[TPW];
-#pragma unroll
-    for (int q = 0; q < TPW; ++q) acc[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int j0 = 0; j0 < n_steps; j0 += RING) {
-      uint4 xv[RING];
-#pragma unroll
-      for (int u = 0; u < RING; ++u) {
-        const int j = j0 + u;
-        const int chunk = 4 * (s_begin + j) + kq;
-        xv[u] = lds[xrow + (j < n_steps && chunk < C ? chunk : C)];
-      }
-#pragma unroll
-      for (int u = 0; u < RING; ++u) {
-#pragma unroll
-        for (int q = 0; q < TPW; ++q) {
-          acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ring[u][q]),
-                                                           __builtin_bit_cast(bf16x8_t, xv[u]),
-                                                           acc[q], 0, 0, 0);
-          ring[u][q] = buf_load16_cached(ra, a_off(j0 + u + RING, q));
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // Partials: feature 4 * (lane >> 4) + q, token lane & 15.
-    // red[wave][q*16 + feature][token]
-#pragma unroll
-    for (int q = 0; q < TPW; ++q)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        red[(wave * 16 * TPW + q * 16 + 4 * (lane >> 4) + r) * 16 + (lane & 15)] = acc[q][r];
-    __syncthreads();  // B1
-#pragma unroll
-    for (int q = 0; q < TPW; ++q) {
-      const int nl = q * 16 + 4 * wave + (lane >> 4);
-      const int bl = lane & 15;
-      float y = red[nl * 16 + bl];
-#pragma unroll
-      for (int w = 1; w < kWaves; ++w) y = y + red[(w * 16 * TPW + nl) * 16 + bl];
-      yt[bl * 16 * TPW + nl] = y;
-    }
-    __syncthreads();  // B2: results token-major
-    const int j = tid >> 4;
+    const int j = tid >> 4;  // the store phase: token j of the tile, feature n of each feature tile
     const int n = tid & 15;
+
+    for (int jt = 0; jt < M; jt += kTok) {
+      // Tokens jt .. jt + mt - 1 in LDS rows 0 .. mt - 1.  Each wave reads
+      // only its own k-slice of the rows (and the zero column C), so no
+      // barrier guards them; the partials' buffers are guarded by B1 / B2.
+      const int mt = min(kTok, M - jt);
+      for (int c0 = c_begin; c0 < c_end; c0 += 64) {
+        if (c0 + lane < c_end) {
+          for (int t = 0; t < mt; ++t)
+            lds_dma16(xg + s_xrow[jt + t] * C + c0 + lane, lds + t * CP + c0);
+        }
+      }
+      uint4 ring[RING][TPW];
 #pragma unroll
-    for (int q = 0; q < TPW; ++q) {
-      const int64_t feat = (int64_t)(t0 + q) * 16 + n;
-      if (j < M && q < nt && feat < a.H)
-        store_coherent(&a.bufs[s_dst[j] + feat], yt[j * 16 * TPW + q * 16 + n]);
+      for (int u = 0; u < RING; ++u)
+#pragma unroll
+        for (int q = 0; q < TPW; ++q) ring[u][q] = buf_load16_cached(ra, a_off(u, q));
+      // The x copies went out before the ring loads: once at most RING * TPW
+      // loads are outstanding they have landed.
+      wait_vm_le<RING * TPW>();
+      for (int c = c_begin + lane; c < c_end; c += 64)
+        for (int t = mt; t < kTok; ++t) lds[t * CP + c] = make_uint4(0u, 0u, 0u, 0u);
+      if (lane < kTok) lds[lane * CP + C] = make_uint4(0u, 0u, 0u, 0u);
+
+      f32x4_t acc[TPW];
+#pragma unroll
+      for (int q = 0; q < TPW; ++q) acc[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int j0 = 0; j0 < n_steps; j0 += RING) {
+        uint4 xv[RING];
+#pragma unroll
+        for (int u = 0; u < RING; ++u) {
+          const int js = j0 + u;
+          const int chunk = 4 * (s_begin + js) + kq;
+          xv[u] = lds[xrow + (js < n_steps && chunk < C ? chunk : C)];
+        }
+#pragma unroll
+        for (int u = 0; u < RING; ++u) {
+#pragma unroll
+          for (int q = 0; q < TPW; ++q) {
+            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ring[u][q]),
+                                                             __builtin_bit_cast(bf16x8_t, xv[u]),
+                                                             acc[q], 0, 0, 0);
+            ring[u][q] = buf_load16_cached(ra, a_off(j0 + u + RING, q));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      // Partials: feature 4 * (lane >> 4) + q, token lane & 15.
+      // red[wave][q*16 + feature][token]
+#pragma unroll
+      for (int q = 0; q < TPW; ++q)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          red[(wave * 16 * TPW + q * 16 + 4 * (lane >> 4) + r) * 16 + (lane & 15)] = acc[q][r];
+      __syncthreads();  // B1
+#pragma unroll
+      for (int q = 0; q < TPW; ++q) {
+        const int nl = q * 16 + 4 * wave + (lane >> 4);
+        const int bl = lane & 15;
+        float y = red[nl * 16 + bl];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) y = y + red[(w * 16 * TPW + nl) * 16 + bl];
+        yt[bl * 16 * TPW + nl] = y;
+      }
+      __syncthreads();  // B2: results token-major
+#pragma unroll
+      for (int q = 0; q < TPW; ++q) {
+        const int64_t feat = (int64_t)(t0 + q) * 16 + n;
+        if (j < mt && q < nt && feat < a.H)
+          store_coherent(&a.bufs[s_dst[jt + j] + feat], yt[j * 16 * TPW + q * 16 + n]);
+      }
     }
   }
   wait_vm_all();    // this wave's result rows are at the coherence point ...

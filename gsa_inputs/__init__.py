@@ -127,40 +127,43 @@ def shard(A, x, W, r):
 # Mixture-of-experts workloads: the expert down-projection fused with the
 # combine all-to-all, at one rank's share.  W ranks hold ne experts each
 # (global expert g = rank * ne + e); every rank has T tokens, each routed to
-# top_k distinct experts drawn uniformly; an expert accepts at most
-# `capacity` tokens per call (assignments past it are dropped, in rank and
-# token order).  Weights ~ N(0, sigma), dispatched token rows ~ N(0, 1), bf16.
+# top_k distinct experts drawn uniformly; every assignment is kept (the pages
+# name no capacity limit).  Weights ~ N(0, sigma), dispatched token rows
+# ~ N(0, 1), bf16.
 #
 #   m0  W=4 ne=4  H=256  F=128  top-2 of 16,  T=8   small case
 #   m1  W=8 ne=16 H=2048 F=768  top-8 of 128, T=16  Qwen3-30B-A3B-like down_proj
 #   m2  W=8 ne=32 H=7168 F=2048 top-8 of 256, T=16  DeepSeek-V3-like down_proj
+#   m3  W=8 ne=16 H=2048 F=768  top-8 of 128, T=64  the Qwen3-like shape with 64
+#                                                   tokens per rank (about 32 per
+#                                                   expert)
 MOE_CONFIGS = {
-    "m0": dict(cfg_id=20, W=4, ne=4, H=256, F=128, top_k=2, T=8, capacity=16, sigma=0.05,
+    "m0": dict(cfg_id=20, W=4, ne=4, H=256, F=128, top_k=2, T=8, sigma=0.05,
                name="small MoE, W=4 ne=4 H=256 F=128 top-2 of 16, 8 tokens per rank"),
-    "m1": dict(cfg_id=21, W=8, ne=16, H=2048, F=768, top_k=8, T=16, capacity=16, sigma=0.02,
+    "m1": dict(cfg_id=21, W=8, ne=16, H=2048, F=768, top_k=8, T=16, sigma=0.02,
                name="Qwen3-30B-A3B-like MoE down_proj, W=8 ne=16 H=2048 F=768 top-8 of 128, "
                     "16 tokens per rank"),
-    "m2": dict(cfg_id=22, W=8, ne=32, H=7168, F=2048, top_k=8, T=16, capacity=16, sigma=0.02,
+    "m2": dict(cfg_id=22, W=8, ne=32, H=7168, F=2048, top_k=8, T=16, sigma=0.02,
                name="DeepSeek-V3-like MoE down_proj, W=8 ne=32 H=7168 F=2048 top-8 of 256, "
                     "16 tokens per rank"),
+    "m3": dict(cfg_id=23, W=8, ne=16, H=2048, F=768, top_k=8, T=64, sigma=0.02,
+               name="Qwen3-30B-A3B-like MoE down_proj, W=8 ne=16 H=2048 F=768 top-8 of 128, "
+                    "64 tokens per rank"),
 }
 
 
-def moe_routing(W, ne, T, top_k, capacity, seed=0, cfg_id=0):
-    """Seeded routing of every rank's T tokens: counts[s][g] = tokens of rank
-    s accepted by global expert g (int64, W x W*ne)."""
+def moe_routing(W, ne, T, top_k, seed=0, cfg_id=0):
+    """Seeded routing of every rank's T tokens to top_k distinct experts each:
+    counts[s][g] = tokens of rank s routed to global expert g (int64,
+    W x W*ne); every row sums to T * top_k."""
     E = W * ne
     ss = np.random.SeedSequence([int(seed), int(cfg_id), 7])
     g = np.random.Generator(np.random.PCG64(ss))
-    load = np.zeros(E, np.int64)
     counts = np.zeros((W, E), np.int64)
     for s in range(W):
         for _ in range(T):
             experts = np.argsort(g.random(E))[:top_k]
-            for ex in experts:
-                if load[ex] < capacity:
-                    load[ex] += 1
-                    counts[s, ex] += 1
+            counts[s, experts] += 1
     return counts
 
 
@@ -168,7 +171,7 @@ def make_moe_inputs(cfg, seed=0, rank=0, gap=0):
     """One rank's inputs for a MoE workload (see MOE_CONFIGS): the seeded
     routing of moe_routing, then make_moe_from_counts."""
     c = MOE_CONFIGS[cfg] if isinstance(cfg, str) else cfg
-    counts = moe_routing(c["W"], c["ne"], c["T"], c["top_k"], c["capacity"], seed, c["cfg_id"])
+    counts = moe_routing(c["W"], c["ne"], c["T"], c["top_k"], seed, c["cfg_id"])
     return make_moe_from_counts(counts, c["ne"], c["H"], c["F"], c["sigma"], seed, c["cfg_id"],
                                 rank, gap, rows_out=c["T"] * c["top_k"])
 

@@ -314,8 +314,10 @@ const char *gsa_strerror(int code);
  * caller, their flags marked published by gsa_a2a_reset.
  * ---------------------------------------------------------------------- */
 
-/* Tokens one local expert may take per call (its capacity). */
-#define GSA_MOE_MAX_TOKENS 16
+/* Tokens one local expert may take per call: the kernel runs them in tiles of
+ * 16 tokens (one MFMA operand of 16 columns each); a split table that gives
+ * an expert more is reported as GSA_ESPLIT for that expert. */
+#define GSA_MOE_MAX_TOKENS 256
 /* Largest input width F of the expert GEMM (the dispatched rows of one
  * expert are staged in LDS). */
 #define GSA_MOE_MAX_F 4088

@@ -105,7 +105,7 @@ def run_moe_and_check(d, what):
                                                 all_but(d["W"], d["rank"]), 1)), f"{what}: flags"
 
 
-@pytest.mark.parametrize("cfg", ["m0", "m1", "m2"])
+@pytest.mark.parametrize("cfg", ["m0", "m1", "m2", "m3"])
 def test_config_moe(cfg):
     _say(f"[moe] config {cfg}")
     run_moe_and_check(gi.make_moe_inputs(cfg, seed=0, rank=0), cfg)
@@ -139,6 +139,10 @@ EDGE = [
     (3, 5, 33, 32, 2, [0], 0),              # no tokens at all
     (2, 2, 48, 2048, 1, [16, 2], 0),        # wide experts: two tiles per workgroup, 3 tiles
     (4, 2, 80, 1024, 3, [5], 1),            # four tiles per workgroup, 5 tiles
+    (2, 2, 64, 256, 0, [17, 32], 0),        # one token past a 16-token tile; two whole tiles
+    (4, 1, 80, 768, 2, [48], 1),            # three token tiles, gaps between segments
+    (2, 2, 48, 2048, 1, [33, 0], 0),        # wide experts, three token tiles (the last of 1)
+    (2, 1, 40, 64, 1, [256], 0),            # the most tokens an expert takes
 ]
 
 

@@ -38,21 +38,22 @@ def test_distribution_roughly_as_stated():
     assert abs(x.std() - 1.0) < 0.1
 
 
-def test_moe_routing_respects_top_k_and_capacity():
-    c = gi.MOE_CONFIGS["m1"]
-    counts = gi.moe_routing(c["W"], c["ne"], c["T"], c["top_k"], c["capacity"], seed=0,
-                            cfg_id=c["cfg_id"])
-    E = c["W"] * c["ne"]
-    assert counts.shape == (c["W"], E)
-    # every expert takes at most its capacity; no token is counted twice for
-    # one expert, so a rank sends at most T tokens to any expert
-    assert counts.sum(axis=0).max() <= c["capacity"]
-    assert counts.max() <= c["T"]
-    # each rank routes T * top_k assignments before capacity drops
-    assert np.all(counts.sum(axis=1) <= c["T"] * c["top_k"])
-    again = gi.moe_routing(c["W"], c["ne"], c["T"], c["top_k"], c["capacity"], seed=0,
-                           cfg_id=c["cfg_id"])
-    assert np.array_equal(counts, again)
+def test_moe_routing_keeps_every_assignment():
+    for name in ("m1", "m3"):
+        c = gi.MOE_CONFIGS[name]
+        counts = gi.moe_routing(c["W"], c["ne"], c["T"], c["top_k"], seed=0, cfg_id=c["cfg_id"])
+        E = c["W"] * c["ne"]
+        assert counts.shape == (c["W"], E)
+        # every token goes to top_k distinct experts: each rank routes exactly
+        # T * top_k assignments and sends at most T tokens to any one expert
+        assert np.all(counts.sum(axis=1) == c["T"] * c["top_k"])
+        assert counts.max() <= c["T"]
+        again = gi.moe_routing(c["W"], c["ne"], c["T"], c["top_k"], seed=0, cfg_id=c["cfg_id"])
+        assert np.array_equal(counts, again)
+    # the 64-token workload gives some expert more than one 16-token tile
+    c = gi.MOE_CONFIGS["m3"]
+    d = gi.make_moe_inputs("m3", seed=0, rank=0)
+    assert d["length"].sum(axis=1).max() > 32
 
 
 def test_moe_layout_is_expert_major_and_combine_ordered():
