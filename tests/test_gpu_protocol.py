@@ -2,6 +2,8 @@
 determinism, flag state, the W = 1 and shard-sum identities, closed-form
 inputs with exact results, rank sweep, timeouts and a bad own flag row
 (forced from the host with a short wait bound), graph replays."""
+import os
+import subprocess
 import sys
 
 import numpy as np
@@ -68,6 +70,43 @@ def test_bit_identical_across_buffers_and_streams():
     finally:
         r1.close()
         r2.close()
+
+
+_CHILD = """
+import sys
+import numpy as np
+import gsa_inputs as gi
+from tests.gpu_util import Run
+d = gi.make_inputs("c3b4", seed=4)
+r = Run(d["A"], d["x"], d["slots"].copy(), 0)
+r.call()
+out, sl, flags, status = r.results()
+r.close()
+np.savez(sys.argv[1], out=out, slots=sl, flags=flags, status=np.array(status))
+"""
+
+
+def test_bit_identical_across_processes(tmp_path):
+    """The same call in a second process (started after this one's calls):
+    out, every slot and the flags byte-identical, status clean in both."""
+    _say("[protocol] across processes")
+    d = gi.make_inputs("c3b4", seed=4)
+    r = Run(d["A"], d["x"], d["slots"].copy(), 0)
+    try:
+        r.call()
+        out, sl, flags, status = r.results()
+    finally:
+        r.close()
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    path = str(tmp_path / "child.npz")
+    child = subprocess.run([sys.executable, "-c", _CHILD, path], cwd=root, timeout=300,
+                           capture_output=True, text=True)
+    assert child.returncode == 0, child.stderr[-2000:]
+    got = np.load(path)
+    assert status == (gsa.GSA_OK, -1, -1) and tuple(got["status"]) == status
+    assert np.array_equal(_bits(got["out"]), _bits(out)), "out differs between processes"
+    assert np.array_equal(_bits(got["slots"]), _bits(sl)), "slots differ between processes"
+    assert np.array_equal(got["flags"], flags)
 
 
 @pytest.mark.parametrize("cfg", ["c1", "c2"])
