@@ -133,6 +133,13 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 //                  sum, so that out is the fold of the slots as published;
 //   load_slot:     element i of the slots (i = r * N * B + n * B + b),
 //                  widened exactly to fp32; a device-coherent load;
+//   load_slot_bits / slot_value: the same in two halves, for loads issued
+//                  well before their use: one coherent 32-bit load with no
+//                  branch (for bf16 slots the aligned word that holds
+//                  element i; the slot region is padded to whole words), and
+//                  the element's widening from that word.  A 16-bit load in
+//                  a dtype branch has its zero-extension inside the branch,
+//                  which waits for that load before the next one issues;
 //   store_slot:    the device-coherent store of a published value;
 //   store_out:     out[i], rounded to bf16 for a bf16 out.
 __device__ __forceinline__ float bf16_widen(uint16_t bits) {
@@ -141,11 +148,16 @@ __device__ __forceinline__ float bf16_widen(uint16_t bits) {
 __device__ __forceinline__ float publish_value(const GemvArgs& a, float y) {
   return a.slot_bf16 ? bf16_widen(bf16_rne(y)) : y;
 }
+__device__ __forceinline__ uint32_t load_slot_bits(const GemvArgs& a, int64_t i) {
+  return __hip_atomic_load(reinterpret_cast<const uint32_t*>(a.slots) + (a.slot_bf16 ? i >> 1 : i),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float slot_value(const GemvArgs& a, int64_t i, uint32_t bits) {
+  if (a.slot_bf16) bits = (i & 1) ? bits & 0xFFFF0000u : bits << 16;  // little-endian halves
+  return __uint_as_float(bits);
+}
 __device__ __forceinline__ float load_slot(const GemvArgs& a, int64_t i) {
-  if (a.slot_bf16)
-    return bf16_widen(__hip_atomic_load(reinterpret_cast<const uint16_t*>(a.slots) + i,
-                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  return load_coherent(a.slots + i);
+  return slot_value(a, i, load_slot_bits(a, i));
 }
 __device__ __forceinline__ void store_slot(const GemvArgs& a, int64_t i, float yp) {
   if (a.slot_bf16)
@@ -1110,15 +1122,15 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   // the values are never used), so no branch join forces an early wait.
   const bool own_peers = kEarlyOut && state == kPeersReady;
   const int vidx = min(li, V - 1);
-  float pv[kMaxW];
+  const int64_t NB = a.N * a.B;
+  const int64_t oi = min((row0 + vidx / B) * a.B + vidx % B, NB - 1);
+  uint32_t pvb[kMaxW];
   if constexpr (kOwnPeers) {
-    const int64_t NB = a.N * a.B;
-    const int64_t oi = min((row0 + vidx / B) * a.B + vidx % B, NB - 1);
 #pragma unroll
-    for (int r = 0; r < kMaxW; ++r) pv[r] = load_slot(a, min(r, a.W - 1) * NB + oi);
+    for (int r = 0; r < kMaxW; ++r) pvb[r] = load_slot_bits(a, min(r, a.W - 1) * NB + oi);
   } else {
 #pragma unroll
-    for (int r = 0; r < kMaxW; ++r) pv[r] = 0.0f;
+    for (int r = 0; r < kMaxW; ++r) pvb[r] = 0u;
   }
 
   float acc[R][B];
@@ -1127,6 +1139,9 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[s][b] = 0.0f;
   valu_stream<MASKED, NCH, D, B, G, R>(acc, ring, ra, voff, lds_x, C, zidx, li, nch, rot);
+  float pv[kMaxW];
+#pragma unroll
+  for (int r = 0; r < kMaxW; ++r) pv[r] = slot_value(a, min(r, a.W - 1) * NB + oi, pvb[r]);
 
   // Every lane of the row group gets every total; lane li < V owns output
   // li = s * B + b (row nloc0 + s, column b): consecutive floats of the slot.
@@ -1255,9 +1270,9 @@ __global__ __launch_bounds__(kLongWaves * 64, kLongWaves / 4) void gemv_ar_long(
   // queue behind the lane's first A steps.  (Issued instead right behind the
   // lane's last A load, with each refill pinned to its step, they measured
   // no faster: 11.93 against 11.86 us per call on the 70B-class shape.)
-  float pv[kMaxW];
+  uint32_t pv[kMaxW];
 #pragma unroll
-  for (int r = 0; r < kMaxW; ++r) pv[r] = load_slot(a, min(r, a.W - 1) * NB + oi);
+  for (int r = 0; r < kMaxW; ++r) pv[r] = load_slot_bits(a, min(r, a.W - 1) * NB + oi);
 
   float acc[R][B];
 #pragma unroll
@@ -1278,7 +1293,8 @@ __global__ __launch_bounds__(kLongWaves * 64, kLongWaves / 4) void gemv_ar_long(
     // out = ((0 + s_0) + s_1) ... + s_{W-1}, the own term being y as
     // published; ranks past W - 1 add +0 (acc is never -0).
 #pragma unroll
-    for (int r = 0; r < kMaxW; ++r) outv = outv + (r < a.W ? (r == a.rank ? yp : pv[r]) : 0.0f);
+    for (int r = 0; r < kMaxW; ++r)
+      outv = outv + (r < a.W ? (r == a.rank ? yp : slot_value(a, r * NB + oi, pv[r])) : 0.0f);
   }
   __builtin_amdgcn_sched_barrier(0);
   if (state != kBadOwnRow && live) store_slot(a, a.rank * NB + oi, yp);
@@ -1549,6 +1565,181 @@ __global__ __launch_bounds__(256) void peer_publish_kernel(float* slots, uint32_
   for (int64_t t = threadIdx.x; t < nflags; t += blockDim.x) store_flag(row + flag_word(t), epoch);
 }
 
+// MFMA path with x in registers: 8 < B <= 16 (batch padded to 16 with
+// zeros), rows of exactly 16 * NS chunks, the plain one-shot call.  One
+// workgroup of 4 waves owns 32 rows, two 16-row blocks of
+// v_mfma_f32_16x16x32_bf16 (A rows as the A operand, x as the B operand);
+// wave w owns k-steps [w NS, (w + 1) NS) of both blocks.  Operand layout per
+// lane l: A row (l & 15), batch column (l & 15), k-chunk (l >> 4) of the
+// step's four 8-element chunks; result rows 4 (l >> 4) + e, column (l & 15).
+// Each lane's x operand of every one of its steps is loaded once, into
+// registers, ahead of every A load (a scheduling barrier keeps the order):
+// no LDS copy of x and no barrier before the first MFMA, where the
+// 16-row kernel copies all of x into LDS in every workgroup (by LDS DMA,
+// whose LDS reads the compiler then orders behind every outstanding load).
+// The A stream is fully unrolled, D steps in flight, so its waits count
+// exactly.  The waves' partials are summed in wave order through LDS; each
+// thread then owns two outputs, whose peer values it loads right behind its
+// last A load, and publishes and sums as the long-row kernel does; wave 0
+// runs the signal-pad protocol.
+// Measured on the skinny GEMM (W = 4, 8192 x 2048 share, B = 16; cold, per
+// call): 10.7 us against 13.3 us for the 16-row kernel.  A plain read of the
+// same rows takes 6.4 us, and 8.3 us with the MFMA operand's access pattern
+// (64 bytes of each of 16 rows per load instruction).
+constexpr int kMfmaXWaves = 4;
+constexpr int kMfmaXRows = 32;
+
+template <int NS, int D>
+__global__ __launch_bounds__(kMfmaXWaves * 64) void gemv_ar_mfma_xreg(GemvArgs a) {
+  constexpr int RB = kMfmaXRows / 16;  // 16-row MFMA blocks
+  constexpr int NT = kMfmaXWaves * 64;
+  constexpr int TR = kMfmaXRows;
+  constexpr int OPT = TR * 16 / NT;    // outputs per thread (batch padded to 16)
+  static_assert(kMfmaXRows / kFlagRows * kMaxW <= 64, "one wave-0 lane per (flag tile, rank)");
+  static_assert(NS > D, "the peer loads follow the last A refill");
+  __shared__ float red[kMfmaXWaves][RB][16][16];
+  __shared__ uint32_t s_ctl[kLongCtlWords];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t tile = blockIdx.x;
+  const FlagSpan fs = flag_span<TR>(a, tile);
+  const int C = a.C;  // == 16 * NS
+  const int s0 = wave * NS;
+  const int kq = lane >> 4;
+  const int l16 = lane & 15;
+  const uint32_t kOutOfRange = 0x80000000u;  // past any buffer: reads zeros
+
+  uint32_t fl = 0;
+  if (wave == 0) fl = load_flag(a, fs, lane);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // x: batch l16 (zeros past B), chunk 4 (s0 + s) + kq of every step s.
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(a.B * C * 16));
+  uint4 xv[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+    xv[s] = buf_load16_cached(
+        rx, l16 < a.B ? ((uint32_t)l16 * (uint32_t)C + 4u * (s0 + s) + kq) * 16u : kOutOfRange);
+  __builtin_amdgcn_sched_barrier(0);
+
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, (uint32_t)(a.N * C * 16));
+  const int64_t row0 = tile * TR;
+  uint32_t arow[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+    arow[r] = ((uint32_t)(row0 + 16 * r + l16) * (uint32_t)C + 4u * s0 + kq) * 16u;
+  uint4 ring[D][RB];
+#pragma unroll
+  for (int u = 0; u < D; ++u)
+#pragma unroll
+    for (int r = 0; r < RB; ++r) ring[u][r] = buf_load16(ra, arow[r] + u * 64u);
+
+  if (wave == 0) comm_decide<false, TR>(a, lane, tile, fs, fl, s_ctl);
+  __syncthreads();  // B1: the start decision in s_ctl
+  const uint32_t state = s_ctl[1];
+
+  // This thread's outputs: o = tid + NT i, local row o / 16, column o % 16.
+  const int64_t NB = a.N * a.B;
+  int64_t oi[OPT];
+  bool live[OPT];
+#pragma unroll
+  for (int i = 0; i < OPT; ++i) {
+    const int o = tid + NT * i;
+    const int64_t row = row0 + o / 16;
+    const int b = o % 16;
+    live[i] = b < a.B && row < a.N;
+    oi[i] = min(row * a.B + min(b, a.B - 1), NB - 1);
+  }
+  uint32_t pv[OPT][kMaxW];
+
+  f32x4_t acc[RB];
+#pragma unroll
+  for (int r = 0; r < RB; ++r) acc[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ring[s % D][r]),
+                                                       __builtin_bit_cast(bf16x8_t, xv[s]), acc[r],
+                                                       0, 0, 0);
+      if (s + D < NS) ring[s % D][r] = buf_load16(ra, arow[r] + (s + D) * 64u);
+    }
+    if (s == NS - D - 1) {
+      // The peer values, right behind the lane's last A load: unconditional
+      // (clamped) loads, unused unless every peer had published at the
+      // start.  Issued after B1 instead, ahead of the A refills, they held
+      // the stream up: 11.5 against 10.7 us per call on the skinny GEMM.
+#pragma unroll
+      for (int i = 0; i < OPT; ++i)
+#pragma unroll
+        for (int r = 0; r < kMaxW; ++r) pv[i][r] = load_slot_bits(a, min(r, a.W - 1) * NB + oi[i]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[wave][r][4 * kq + e][l16] = acc[r][e];
+  __syncthreads();  // every wave's partials in LDS
+
+  float yp[OPT], outv[OPT];
+#pragma unroll
+  for (int i = 0; i < OPT; ++i) {
+    const int o = tid + NT * i;
+    const int lr = o / 16, b = o % 16;
+    float y = red[0][lr / 16][lr % 16][b];
+#pragma unroll
+    for (int w = 1; w < kMfmaXWaves; ++w) y = y + red[w][lr / 16][lr % 16][b];
+    yp[i] = publish_value(a, y);  // y as published: the own term of the sum
+    outv[i] = 0.0f;
+    if (state == kPeersReady) {
+#pragma unroll
+      for (int r = 0; r < kMaxW; ++r)
+        outv[i] = outv[i] +
+                  (r < a.W ? (r == a.rank ? yp[i] : slot_value(a, r * NB + oi[i], pv[i][r])) : 0.0f);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (state != kBadOwnRow) {
+#pragma unroll
+    for (int i = 0; i < OPT; ++i)
+      if (live[i]) store_slot(a, a.rank * NB + oi[i], yp[i]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (state == kPeersReady) {
+#pragma unroll
+    for (int i = 0; i < OPT; ++i)
+      if (live[i]) store_out(a, oi[i], outv[i]);
+    wait_vm_le<OPT>();  // the published values are at the coherence point (in-order completion)
+  } else {
+    wait_vm_all();
+  }
+  __syncthreads();  // B2: every published value of the tile is at the coherence point
+  if (state != kBadOwnRow && wave == 0 && lane < fs.nf)
+    store_flag(flag_ptr(a, a.rank, fs.f0 + lane), s_ctl[4 + lane]);
+  if (state == kMustWait) {
+    if (wave == 0) {
+      const uint32_t done = wait_peers<false, TR>(a, lane, tile, fs, s_ctl);
+      if (lane == 0) s_ctl[0] = done;
+    }
+    __syncthreads();  // B3
+    const uint32_t done = s_ctl[0];
+#pragma unroll
+    for (int i = 0; i < OPT; ++i) {
+      const int q = ((tid + NT * i) / 16) / kFlagRows;
+      if (live[i] && ((done >> q) & 1u)) {
+        float acc2 = 0.0f;
+#pragma unroll
+        for (int r = 0; r < kMaxW; ++r)
+          if (r < a.W) acc2 = acc2 + (r == a.rank ? yp[i] : load_slot(a, r * NB + oi[i]));
+        store_out(a, oi[i], acc2);
+      }
+    }
+  }
+}
+
 __global__ void pad_reset_kernel(uint32_t* pad, int W, int row_stride, uint32_t mask,
                                  uint32_t* epi_tail, int64_t tail_words) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -1576,6 +1767,7 @@ struct ValuChoice {
   const void* kernel;
   int threads;    // per workgroup (compute waves, plus the communication wave if the kernel has one)
   int tile_rows;  // rows per workgroup
+  bool no_dynamic_lds = false;  // the kernel's LDS is all static
 };
 
 constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -1645,6 +1837,10 @@ ValuChoice pick_kernel(int B, int C, bool small_tiles) {
     case 7: return valu_kernel<7, TS>(C, small_tiles);
     case 8: return valu_kernel<8, TS>(C, small_tiles);
     default:
+      // Rows of exactly 256 chunks (4 waves x 16 k-steps), plain call: x in registers.
+      if (!TS && small_tiles && C == 16 * 16)
+        return ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma_xreg<16, 4>),
+                          kMfmaXWaves * 64, kMfmaXRows, true};
       return mfma_x_in_lds(C)
                  ? ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma<kMfmaWaves, 8, TS>),
                               (kMfmaWaves + 1) * 64, kBigTile}
@@ -1674,7 +1870,8 @@ bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, Launch* ou
   const bool small_tiles = !epi;  // the fused epilogue counts 16-row tiles
   const ValuChoice k =
       two_shot ? pick_kernel<true>(B, C, small_tiles) : pick_kernel<false>(B, C, small_tiles);
-  *out = {k.kernel, (unsigned)k.threads, gemv_lds_bytes(W, B, C, epi, k.tile_rows), k.tile_rows};
+  *out = {k.kernel, (unsigned)k.threads,
+          k.no_dynamic_lds ? 0 : gemv_lds_bytes(W, B, C, epi, k.tile_rows), k.tile_rows};
   return true;
 }
 

@@ -246,19 +246,21 @@ def test_timeout_reports_missing_peer_and_skips_out():
     assert np.array_equal(flags, oracle.pad_after_calls(before, rank, 1))
 
 
-@pytest.mark.parametrize("Ks,t_bad", [
-    (128, 3),    # short rows: 4-row workgroups, one flag tile each
-    (1024, 6),   # middle rows: 16-row workgroups of 4 waves; the third flag tile of the second
-    (3200, 5),   # long rows: 32-row workgroups; flag tile 5 is the sixth of its workgroup
-    (3200, 13),  # long rows: a flag tile of the second (ragged) 32-row workgroup
-    (128, 19),   # the last flag tile
+@pytest.mark.parametrize("Ks,t_bad,B", [
+    (128, 3, 3),     # short rows: 4-row workgroups, one flag tile each
+    (1024, 6, 3),    # middle rows: 16-row workgroups of 4 waves; the third flag tile of the second
+    (3200, 5, 3),    # long rows: 32-row workgroups; flag tile 5 is the sixth of its workgroup
+    (3200, 13, 3),   # long rows: a flag tile of the second (ragged) 32-row workgroup
+    (128, 19, 3),    # the last flag tile
+    (2048, 5, 16),   # MFMA, x in registers: 32-row workgroups
+    (2048, 13, 12),  # the same, a flag tile of the second (ragged) workgroup
 ])
-def test_timeout_single_tile(Ks, t_bad):
+def test_timeout_single_tile(Ks, t_bad, B):
     """One flag word of peer 2 overwritten with 0 from the host: only the rows
     of that flag tile stay unwritten, whatever the workgroup size; every other
     row is correct."""
-    _say(f"[protocol] timeout, one flag tile withheld, Ks={Ks} t={t_bad}")
-    W, rank, N, B = 4, 0, 80, 3
+    _say(f"[protocol] timeout, one flag tile withheld, Ks={Ks} t={t_bad} B={B}")
+    W, rank, N = 4, 0, 80
     d = gi.make_shard_inputs(W, N, Ks, B, seed=11, rank=rank)
     gsa.gsa_set_wait_timeout_us(200)
     try:
