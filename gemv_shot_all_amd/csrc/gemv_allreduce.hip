@@ -174,6 +174,21 @@ __device__ __forceinline__ void store_out(const GemvArgs& a, int64_t i, float o)
     a.out[i] = o;
 }
 
+// The launch arguments as a kernel instance sees them: an fp32 instance (DT
+// false) takes slots and out as fp32 whatever the fields say, so every test
+// of the element types above folds away at compile time (the runtime tests
+// cost 0.2-0.4 us per call on the short rows, through the publish chain);
+// calls with bf16 slots or a bf16 out launch the DT instance.
+template <bool DT>
+__device__ __forceinline__ GemvArgs typed_args(const GemvArgs& args) {
+  GemvArgs a = args;
+  if constexpr (!DT) {
+    a.slot_bf16 = 0;
+    a.out_bf16 = 0;
+  }
+  return a;
+}
+
 // Word of flag tile t within a rank's row: groups of 4 flag tiles (one
 // 16-row tile), one group per 128-byte line.
 __device__ __forceinline__ int64_t flag_word(int64_t t) {
@@ -221,16 +236,17 @@ __device__ __forceinline__ uint32_t load_flag2(const GemvArgs& a, const FlagSpan
 
 // Peer tiles: rank r's TR x B tile of slot r lands at pe[(r * TR + n) * B + b]
 // for every peer r != rank.  issue_peer_tile loads up to kPerLane values per
-// lane per peer into registers (rows past N are clamped to a valid address;
-// their values are never read); store_peer_tile writes them to LDS.  The peer
-// loop is unrolled over GSA_MAX_W with a uniform guard, so no load sits under
-// divergent control.
+// lane per peer into registers, as raw bits (rows past N are clamped to a
+// valid address; their values are never read); store_peer_tile widens them
+// and writes them to LDS.  The peer loop is unrolled over GSA_MAX_W with a
+// uniform guard, so no load sits under divergent control; nothing uses a
+// loaded value inside its guard, so no load waits for the one before it.
 template <int TR>
 constexpr int kPerLane = (TR * GSA_MAX_B + 63) / 64;  // 4 (TR = 16) or 1 (TR = 4)
 
 template <bool TS, int TR>
 __device__ __forceinline__ void issue_peer_tile(const GemvArgs& a, int lane, int64_t tile,
-                                                float (&v)[kMaxW][kPerLane<TR>]) {
+                                                uint32_t (&v)[kMaxW][kPerLane<TR>]) {
   const int64_t NB = a.N * a.B;
   const int per_lane = (TR * a.B + 63) / 64;  // 1, 2 or 4
   const int64_t first = tile * TR * a.B;      // first element of the tile in a slot
@@ -245,7 +261,9 @@ __device__ __forceinline__ void issue_peer_tile(const GemvArgs& a, int lane, int
 #pragma unroll
       for (int i = 0; i < kPerLane<TR>; ++i) {
         const int64_t e = min(first + lane + 64 * i, last);
-        if (i < per_lane) v[r][i] = copy ? load_coherent(&a.gathered[e]) : load_slot(a, r * NB + e);
+        if (i < per_lane)
+          v[r][i] = copy ? __float_as_uint(load_coherent(&a.gathered[e]))
+                         : load_slot_bits(a, r * NB + e);
       }
     }
   }
@@ -253,9 +271,12 @@ __device__ __forceinline__ void issue_peer_tile(const GemvArgs& a, int lane, int
 
 template <bool TS, int TR>
 __device__ __forceinline__ void store_peer_tile(const GemvArgs& a, int lane, int64_t tile,
-                                                const float (&v)[kMaxW][kPerLane<TR>], float* pe) {
+                                                const uint32_t (&v)[kMaxW][kPerLane<TR>],
+                                                float* pe) {
+  const int64_t NB = a.N * a.B;
   const int tb = TR * a.B;  // elements of one rank's tile
   const int per_lane = (tb + 63) / 64;
+  const int64_t first = tile * tb;
   const int owner = tile_owner<TS, TR>(a, tile);
   const bool copy = TS && owner != a.rank;  // v[0] holds the owner's values
 #pragma unroll
@@ -265,7 +286,9 @@ __device__ __forceinline__ void store_peer_tile(const GemvArgs& a, int lane, int
 #pragma unroll
       for (int i = 0; i < kPerLane<TR>; ++i) {
         const int e = lane + 64 * i;
-        if (i < per_lane && e < tb) dst[e] = v[r][i];
+        const int64_t g = min(first + e, NB - 1);  // the element issue_peer_tile loaded
+        if (i < per_lane && e < tb)
+          dst[e] = copy ? __uint_as_float(v[r][i]) : slot_value(a, r * NB + g, v[r][i]);
       }
     }
   }
@@ -392,7 +415,7 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
     before = __hip_atomic_fetch_add(epi_count(a, epi_started_off(a.tiles), grp), 1ull,
                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint32_t state = comm_decide<TS, TR>(a, lane, tile, fs, fl, s_ctl);
-  float v[kMaxW][kPerLane<TR>];
+  uint32_t v[kMaxW][kPerLane<TR>];
   const bool early_tile = PE && state == kPeersReady;
   if (early_tile) issue_peer_tile<TS, TR>(a, lane, tile, v);  // after the flags returned
   __syncthreads();  // B1
@@ -990,10 +1013,13 @@ __device__ __forceinline__ int rotated(int j, int rot) {
 
 // The lane's chunks as a stream with D chunks in flight: step j handles
 // chunk li + rotated(j) * G of each row, ring[j % D] holds it, steps 0..D-1
-// were issued before the LDS barrier.  NCH > 0: exactly NCH chunks, fully
+// were issued before the LDS barrier.  A scheduling barrier closes each step:
+// left free, the scheduler has hoisted later steps' x reads and sunk the
+// refills behind them, draining the ring (twice the time on B = 8 rows of
+// 224 chunks).  NCH > 0: exactly NCH chunks, fully
 // unrolled, starting at the tile's rotation rot; NCH == 0: nch chunks in
 // order, unrolled by D.
-template <bool MASKED, int NCH, int D, int B, int G, int R>
+template <bool MASKED, int NCH, int D, int B, int G, int R, bool PIN>
 __device__ __forceinline__ void valu_stream(float (&acc)[R][B], uint4 (&ring)[D][R],
                                             __amdgpu_buffer_rsrc_t ra, const uint32_t (&voff)[R],
                                             const uint4* lds_x, int C, int zidx, int li, int nch,
@@ -1004,6 +1030,7 @@ __device__ __forceinline__ void valu_stream(float (&acc)[R][B], uint4 (&ring)[D]
       mac_chunk<MASKED, B, R>(acc, ring[j % D], lds_x, C, zidx, li + rotated<NCH>(j, rot) * G);
       if (j + D < NCH)
         load_chunk<R>(ring[j % D], ra, voff, (uint32_t)(rotated<NCH>(j + D, rot) * G) * 16u);
+      if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);  // the refill stays in its step
     }
   } else {
     for (int j0 = 0; j0 < nch; j0 += D) {
@@ -1014,6 +1041,7 @@ __device__ __forceinline__ void valu_stream(float (&acc)[R][B], uint4 (&ring)[D]
           mac_chunk<MASKED, B, R>(acc, ring[u], lds_x, C, zidx, li + j * G);
           if (j + D < nch) load_chunk<R>(ring[u], ra, voff, (uint32_t)((j + D) * G) * 16u);
         }
+        if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
       }
     }
   }
@@ -1036,8 +1064,9 @@ __device__ __forceinline__ void valu_stream(float (&acc)[R][B], uint4 (&ring)[D]
 // on 16).  XM: XCD-contiguous tile order (block_tile).
 // LDS: x chunks [b][c], one zero chunk, one sink chunk, then the peer tile.
 template <int B, int G, int R, int NW, int NCH, int D, int XPT, int WPE, bool MASKED, bool TS,
-          bool XM>
-__global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
+          bool XM, bool DT>
+__global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs args) {
+  const GemvArgs a = typed_args<DT>(args);
   constexpr int NT = NW * 64;
   constexpr int GPW = 64 / G;
   constexpr int TR = NW * GPW * R;
@@ -1067,6 +1096,11 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   // At B = 8 either measured slower than summing after B2 (8B down_proj shape
   // 6.16 against 5.85 us with own loads), so larger batches do that.
   constexpr bool kEarlyOut = !TS && B <= 4;
+#ifndef X_PIN
+  constexpr bool kPinSteps = G == 32 && B > 4;  // rows up to 224 chunks, B > 4
+#else
+  constexpr bool kPinSteps = X_PIN;
+#endif
   constexpr bool kPeersFromTile = kEarlyOut && NW == 8;
   constexpr bool kOwnPeers = kEarlyOut && !kPeersFromTile;
   if (wave == NW) {
@@ -1138,7 +1172,8 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs a) {
   for (int s = 0; s < R; ++s)
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[s][b] = 0.0f;
-  valu_stream<MASKED, NCH, D, B, G, R>(acc, ring, ra, voff, lds_x, C, zidx, li, nch, rot);
+  valu_stream<MASKED, NCH, D, B, G, R, kPinSteps>(acc, ring, ra, voff, lds_x, C, zidx, li, nch,
+                                                 rot);
   float pv[kMaxW];
 #pragma unroll
   for (int r = 0; r < kMaxW; ++r) pv[r] = slot_value(a, min(r, a.W - 1) * NB + oi, pvb[r]);
@@ -1194,8 +1229,9 @@ constexpr int kLongCtlWords = 4 + kLongRows / kFlagRows;  // s_ctl[4 + q]: epoch
 constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 * pow2_at_least((v + 1) / 2); }
 constexpr int log2_exact(int v) { return v <= 1 ? 0 : 1 + log2_exact(v / 2); }
 
-template <int B, int NCH, int D, int XPT, bool MASKED>
-__global__ __launch_bounds__(kLongWaves * 64, kLongWaves / 4) void gemv_ar_long(GemvArgs a) {
+template <int B, int NCH, int D, int XPT, bool MASKED, bool DT>
+__global__ __launch_bounds__(kLongWaves * 64, kLongWaves / 4) void gemv_ar_long(GemvArgs args) {
+  const GemvArgs a = typed_args<DT>(args);
   constexpr int R = 2;
   constexpr int NT = kLongWaves * 64;
   constexpr int TR = kLongRows;
@@ -1279,7 +1315,7 @@ __global__ __launch_bounds__(kLongWaves * 64, kLongWaves / 4) void gemv_ar_long(
   for (int s = 0; s < R; ++s)
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[s][b] = 0.0f;
-  valu_stream<MASKED, NCH, D, B, 64, R>(acc, ring, ra, voff, lds_x, C, zidx, lane, nch, 0);
+  valu_stream<MASKED, NCH, D, B, 64, R, false>(acc, ring, ra, voff, lds_x, C, zidx, lane, nch, 0);
 
   float v[VP];
 #pragma unroll
@@ -1369,8 +1405,9 @@ __device__ __forceinline__ void mfma_finish(const GemvArgs& a, int64_t tile, int
 // is finite).  The per-wave 16 x 16 fp32 partials are summed in wave order
 // through LDS.  One more wave runs the signal-pad protocol.
 // LDS: x [16][C + 1] chunks (column C zero); NW 16 x 16 partials; peer tile.
-template <int NW, int D, bool TS>
-__global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs a) {
+template <int NW, int D, bool TS, bool DT>
+__global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs args) {
+  const GemvArgs a = typed_args<DT>(args);
   static_assert(NW * 4 == kBigTile, "each compute wave finishes 4 rows of the tile");
   extern __shared__ uint4 lds[];
   __shared__ uint32_t s_ctl[kCtlWords];
@@ -1464,8 +1501,9 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs a) {
 // wave's steps start at a rotation that differs between the workgroups of
 // one XCD so that they do not all read the same lines of x at once.
 // LDS: NW 16 x 16 partials, then the peer tile.
-template <int NW, int D, bool TS>
-__global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a) {
+template <int NW, int D, bool TS, bool DT>
+__global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs args) {
+  const GemvArgs a = typed_args<DT>(args);
   static_assert(NW * 4 == kBigTile, "each compute wave finishes 4 rows of the tile");
   extern __shared__ uint4 lds[];
   __shared__ uint32_t s_ctl[kCtlWords];
@@ -1589,8 +1627,9 @@ __global__ __launch_bounds__(256) void peer_publish_kernel(float* slots, uint32_
 constexpr int kMfmaXWaves = 4;
 constexpr int kMfmaXRows = 32;
 
-template <int NS, int D>
-__global__ __launch_bounds__(kMfmaXWaves * 64) void gemv_ar_mfma_xreg(GemvArgs a) {
+template <int NS, int D, bool DT>
+__global__ __launch_bounds__(kMfmaXWaves * 64) void gemv_ar_mfma_xreg(GemvArgs args) {
+  const GemvArgs a = typed_args<DT>(args);
   constexpr int RB = kMfmaXRows / 16;  // 16-row MFMA blocks
   constexpr int NT = kMfmaXWaves * 64;
   constexpr int TR = kMfmaXRows;
@@ -1777,7 +1816,7 @@ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // exact instance; any other C the masked streaming instance.  XPT covers
 // B * G * NCH chunks of x (at most 8 per thread; the rest of a longer x is
 // staged by a plain loop).
-template <int B, int G, int R, int NW, int NCH, int D, int WPE, bool TS, bool XM>
+template <int B, int G, int R, int NW, int NCH, int D, int WPE, bool TS, bool XM, bool DT>
 ValuChoice valu_tier(int C) {
   constexpr int XPT0 = ceil_div(B * G * NCH, NW * 64);
   constexpr int XPT = XPT0 > 8 ? 8 : XPT0;
@@ -1785,9 +1824,10 @@ ValuChoice valu_tier(int C) {
   const void* k;
   if (C == G * NCH)
     k = reinterpret_cast<const void*>(
-        &gemv_ar_valu<B, G, R, NW, NCH, DE, XPT, WPE, false, TS, XM>);
+        &gemv_ar_valu<B, G, R, NW, NCH, DE, XPT, WPE, false, TS, XM, DT>);
   else
-    k = reinterpret_cast<const void*>(&gemv_ar_valu<B, G, R, NW, 0, D, XPT, WPE, true, TS, XM>);
+    k = reinterpret_cast<const void*>(
+        &gemv_ar_valu<B, G, R, NW, 0, D, XPT, WPE, true, TS, XM, DT>);
   return {k, (NW + 1) * 64, NW * (64 / G) * R};
 }
 
@@ -1795,14 +1835,14 @@ ValuChoice valu_tier(int C) {
 // (the 70B-class down_proj shard), a masked streaming one for the others;
 // 4 chunk steps in flight (measured: 10.55 us on the 70B-class shape against
 // 11.1 at 3 and 10.6-12.0 at 5-7, cold, without the protocol).
-template <int B>
+template <int B, bool DT>
 ValuChoice long_tier(int C) {
   constexpr int kExactNch = 7;
   constexpr int XPT = ceil_div(B * 64 * kExactNch, kLongWaves * 64);
   constexpr int D = 4;
   const void* k = C == 64 * kExactNch
-                      ? reinterpret_cast<const void*>(&gemv_ar_long<B, kExactNch, D, XPT, false>)
-                      : reinterpret_cast<const void*>(&gemv_ar_long<B, 0, D, 8, true>);
+                      ? reinterpret_cast<const void*>(&gemv_ar_long<B, kExactNch, D, XPT, false, DT>)
+                      : reinterpret_cast<const void*>(&gemv_ar_long<B, 0, D, 8, true, DT>);
   return {k, kLongWaves * 64, kLongRows};
 }
 
@@ -1816,36 +1856,45 @@ ValuChoice long_tier(int C) {
 // (4-row tiles on the longer rows measured slower: 5.4-5.5 against 5.25 us on
 // the 8B down_proj shape, 14.9 against 12.3 us on the 70B-class one.)  Tiles
 // of rows up to C = 224 go to the XCDs in contiguous runs (block_tile).
-template <int B, bool TS>
+// DT (bf16 slots or out) comes only with small tiles and one-shot: the
+// instances it takes are the ones those calls reach.
+template <int B, bool TS, bool DT>
 ValuChoice valu_kernel(int C, bool small_tiles) {
-  if (small_tiles && !TS && C > 224) return long_tier<B>(C);
-  if (small_tiles && C <= 64) return valu_tier<B, 32, 2, 1, 2, 2, 1, TS, true>(C);
-  if (C <= 64) return valu_tier<B, 64, 4, 4, 1, 1, 1, TS, true>(C);
-  if (C <= 224) return valu_tier<B, 32, 2, 4, 7, 4, 1, TS, true>(C);
-  return valu_tier<B, 64, 2, 8, 7, 3, 5, TS, false>(C);
+  static_assert(!(DT && TS), "element types are for the one-shot call");
+  if (small_tiles && !TS && C > 224) return long_tier<B, DT>(C);
+  if (small_tiles && C <= 64) return valu_tier<B, 32, 2, 1, 2, 2, 1, TS, true, DT>(C);
+  if constexpr (!DT) {
+    if (C <= 64) return valu_tier<B, 64, 4, 4, 1, 1, 1, TS, true, false>(C);
+  }
+  if (C <= 224) return valu_tier<B, 32, 2, 4, 7, 4, 1, TS, true, DT>(C);
+  if constexpr (DT)
+    return ValuChoice{nullptr, 0, 0};  // not reached: small tiles take the long tier
+  else
+    return valu_tier<B, 64, 2, 8, 7, 3, 5, TS, false, false>(C);
 }
 
-template <bool TS>
+template <bool TS, bool DT>
 ValuChoice pick_kernel(int B, int C, bool small_tiles) {
   switch (B) {
-    case 1: return valu_kernel<1, TS>(C, small_tiles);
-    case 2: return valu_kernel<2, TS>(C, small_tiles);
-    case 3: return valu_kernel<3, TS>(C, small_tiles);
-    case 4: return valu_kernel<4, TS>(C, small_tiles);
-    case 5: return valu_kernel<5, TS>(C, small_tiles);
-    case 6: return valu_kernel<6, TS>(C, small_tiles);
-    case 7: return valu_kernel<7, TS>(C, small_tiles);
-    case 8: return valu_kernel<8, TS>(C, small_tiles);
+    case 1: return valu_kernel<1, TS, DT>(C, small_tiles);
+    case 2: return valu_kernel<2, TS, DT>(C, small_tiles);
+    case 3: return valu_kernel<3, TS, DT>(C, small_tiles);
+    case 4: return valu_kernel<4, TS, DT>(C, small_tiles);
+    case 5: return valu_kernel<5, TS, DT>(C, small_tiles);
+    case 6: return valu_kernel<6, TS, DT>(C, small_tiles);
+    case 7: return valu_kernel<7, TS, DT>(C, small_tiles);
+    case 8: return valu_kernel<8, TS, DT>(C, small_tiles);
     default:
       // Rows of exactly 256 chunks (4 waves x 16 k-steps), plain call: x in registers.
       if (!TS && small_tiles && C == 16 * 16)
-        return ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma_xreg<16, 4>),
+        return ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma_xreg<16, 4, DT>),
                           kMfmaXWaves * 64, kMfmaXRows, true};
       return mfma_x_in_lds(C)
-                 ? ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma<kMfmaWaves, 8, TS>),
+                 ? ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma<kMfmaWaves, 8, TS, DT>),
                               (kMfmaWaves + 1) * 64, kBigTile}
-                 : ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma_xmem<kMfmaWaves, 8, TS>),
-                              (kMfmaWaves + 1) * 64, kBigTile};
+                 : ValuChoice{
+                       reinterpret_cast<const void*>(&gemv_ar_mfma_xmem<kMfmaWaves, 8, TS, DT>),
+                       (kMfmaWaves + 1) * 64, kBigTile};
   }
 }
 
@@ -1863,13 +1912,16 @@ size_t gemv_lds_bytes(int W, int B, int C, bool epi, int tile_rows) {
   return partials + tail;
 }
 
-bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, Launch* out) {
+bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, bool typed, Launch* out) {
   if (W < 1 || W > GSA_MAX_W || B < 1 || B > GSA_MAX_B || C < 1) return false;
   if (B <= 8 && (size_t)B * C * 16 > GSA_MAX_X_LDS_BYTES) return false;  // x staged in LDS
   if (epi && two_shot) return false;  // separate entry points
+  if (typed && (epi || two_shot)) return false;  // element types: the plain one-shot call only
   const bool small_tiles = !epi;  // the fused epilogue counts 16-row tiles
-  const ValuChoice k =
-      two_shot ? pick_kernel<true>(B, C, small_tiles) : pick_kernel<false>(B, C, small_tiles);
+  const ValuChoice k = two_shot ? pick_kernel<true, false>(B, C, small_tiles)
+                       : typed  ? pick_kernel<false, true>(B, C, small_tiles)
+                                : pick_kernel<false, false>(B, C, small_tiles);
+  if (!k.kernel) return false;
   *out = {k.kernel, (unsigned)k.threads,
           k.no_dynamic_lds ? 0 : gemv_lds_bytes(W, B, C, epi, k.tile_rows), k.tile_rows};
   return true;
