@@ -643,6 +643,19 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Sum of v over the 8 lanes whose index agrees with this lane's mod 8, in
+// every one of them: row_ror:8 within each 16-lane row, then the two
+// permlane swaps of group_sum (a fixed tree, bit-identical in the 8 lanes).
+__device__ __forceinline__ float sum_mod8(float v) {
+  v = v + dpp_f32<0x128>(v);  // row_ror:8
+  unsigned u = __builtin_bit_cast(unsigned, v);
+  auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
+  u = __builtin_bit_cast(unsigned, v);
+  p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
+}
+
 // The value that lane l ^ D holds (D = 8, 4, 2 or 1; partners stay within a
 // 16-lane row).  D = 8 and 4 take two DPP row shifts, each writing only the
 // 4-lane banks whose partner lies in its direction; D = 2 and 1 one quad
@@ -732,42 +745,47 @@ __device__ __forceinline__ float reduce_scatter64(float (&v)[V], int lane) {
 }
 
 // 1 / rms per column from every tile's published partials, computed by the
-// compute waves of the last tile in a fixed order: thread j (nt threads)
-// takes tiles j, j + nt, ... in ascending order, each wave sums its lanes
-// with the fixed lane tree, and the waves' sums are added in wave order.
-// Result in s_inv[0..B).  Contains the barrier E3.  BM >= B bounds the
-// registers it holds (the epilogue runs where the GEMV's registers are free,
-// and must not raise the kernel's register count).
+// compute waves of the last tile in a fixed order.  A record's 16 partial
+// words are read by 8 consecutive lanes, 8 bytes each (coherent 64-bit
+// loads; a wave reads 8 records per load, whole lines, not one request per
+// value): lane l of thread group j = (wave * 64 + l) / 8 holds columns
+// 2 (l % 8) and 2 (l % 8) + 1 and takes tiles j, j + nt / 8, ... in
+// ascending order, 8 tiles' loads ahead of their additions.  The lanes of a
+// wave with the same l % 8 are then summed by a fixed butterfly (xor 8, 16,
+// 32: sum_mod8) and the waves' sums are added in wave order.  Result in s_inv[0..B).
+// Contains the barrier E3.  BM >= B bounds the columns it sums.
 template <int BM>
 __device__ void fold_inv_rms(const GemvArgs& a, int wave, int lane, int nt, float* wsum,
                              float* s_inv) {
-  float acc[BM];
+  constexpr int kLoads = 8;  // tiles per thread group in flight
+  const int sub = lane & 7;  // columns 2 sub, 2 sub + 1
+  const int groups = nt / 8;
+  float acc0 = 0.0f, acc1 = 0.0f;
+  if (2 * sub < BM) {
+    for (int t0 = (wave * 64 + lane) >> 3; t0 < a.tiles; t0 += kLoads * groups) {
+      unsigned long long w[kLoads];
 #pragma unroll
-  for (int c = 0; c < BM; ++c) acc[c] = 0.0f;
-  // The partials of two tiles are loaded before they are added.
-  for (int t0 = wave * 64 + lane; t0 < a.tiles; t0 += 2 * nt) {
-    float pv[2][BM];
+      for (int u = 0; u < kLoads; ++u) {
+        const int t = min(t0 + u * groups, a.tiles - 1);
+        w[u] = __hip_atomic_load(
+            reinterpret_cast<const unsigned long long*>(a.ssq + (int64_t)t * kEpiRecordWords) +
+                sub,
+            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int t = min(t0 + u * nt, a.tiles - 1);
-#pragma unroll
-      for (int c = 0; c < BM; ++c)
-        pv[u][c] = c < a.B ? load_coherent(&a.ssq[(int64_t)t * kEpiRecordWords + c]) : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (t0 + u * nt < a.tiles) {
-#pragma unroll
-        for (int c = 0; c < BM; ++c) acc[c] = acc[c] + pv[u][c];
+      for (int u = 0; u < kLoads; ++u) {
+        if (t0 + u * groups < a.tiles) {
+          acc0 = acc0 + __uint_as_float((uint32_t)w[u]);
+          acc1 = acc1 + __uint_as_float((uint32_t)(w[u] >> 32));
+        }
       }
     }
   }
-#pragma unroll
-  for (int c = 0; c < BM; ++c) {
-    if (c < a.B) {
-      const float ws = group_sum<64>(acc[c]);
-      if (lane == 0) wsum[wave * 16 + c] = ws;
-    }
+  acc0 = sum_mod8(acc0);
+  acc1 = sum_mod8(acc1);
+  if (lane < 8) {
+    wsum[wave * 16 + 2 * lane] = acc0;
+    wsum[wave * 16 + 2 * lane + 1] = acc1;
   }
   __syncthreads();  // E3: every wave's sums in LDS
   if (wave == 0 && lane < a.B) {
@@ -887,14 +905,20 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
     // Every tile has published: fold, then publish inv.
     fold_inv_rms<BM>(a, wave, lane, nt, wsum, s_inv);  // contains E3
     if (wave == 0) {
-      // Lane g writes group g's copy, one self-validating 64-bit word per
-      // column, so no wait has to separate the values from a flag.
-      unsigned long long* copy = reinterpret_cast<unsigned long long*>(
-          a.ssq + epi_inv_off(a.tiles) + (int64_t)lane * kEpiRecordWords);
-      for (int c = 0; c < a.B; ++c)
-        __hip_atomic_store(&copy[c],
-                           ((unsigned long long)mark << 32) | __float_as_uint(s_inv[c]),
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // Every group's copy, one self-validating 64-bit word per column (so no
+      // wait has to separate the values from a flag): P = B rounded up to a
+      // power of two lanes per copy, consecutive lanes on consecutive words.
+      const int lp = a.B <= 1 ? 0 : 32 - __builtin_clz((unsigned)(a.B - 1));  // log2 P
+      const int c = lane & ((1 << lp) - 1);
+      const unsigned long long word =
+          ((unsigned long long)mark << 32) | __float_as_uint(s_inv[min(c, a.B - 1)]);
+      if (c < a.B) {
+        for (int g = lane >> lp; g < kEpiGroups; g += 64 >> lp)
+          __hip_atomic_store(reinterpret_cast<unsigned long long*>(
+                                 a.ssq + epi_inv_off(a.tiles) + (int64_t)g * kEpiRecordWords) +
+                                 c,
+                             word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       if (a.inv_rms && lane < a.B) a.inv_rms[lane] = s_inv[lane];
     }
   } else {
