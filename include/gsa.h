@@ -220,16 +220,17 @@ typedef struct gsa_epilogue {
 /* gsa_gemv_allreduce (same arguments, same contract, `out` written as
  * there), followed in the same kernel by the epilogue `ep` [host, read
  * before return].  The sum over n crosses tiles: each tile publishes its
- * partial sums of squares and counts itself done in the pad header (a count
- * that only grows, cleared by gsa_signal_pad_reset); 1/rms is the fold of
- * the partials in one fixed order, so repeated calls are bit-identical.
- * When the whole grid fits on the GPU at once (the occupancy the library
- * queries), every tile waits for the count, folds and normalises its own
- * rows; otherwise the tile that completes the count normalises all N rows.
- * Both give the same bits.  The tile-side wait is bounded (twice the
- * timeout of gsa_set_wait_timeout_us); if it expires, gsa_signal_pad_status
- * reports GSA_ETIMEOUT with that tile's first flag tile and peer -1.  If any tile of the call
- * failed, y and inv_rms are NaN.
+ * partial sums of squares and counts itself done in the buffer's epilogue
+ * scratch (counts that only grow, cleared by gsa_signal_pad_reset); 1/rms
+ * is the fold of the partials in one fixed order, so repeated calls are
+ * bit-identical.  A tile that finds every tile of the call started once its
+ * own rows are done waits for 1/rms and normalises its own rows (started
+ * tiles always finish, so that wait cannot deadlock); the rows of every
+ * other tile are normalised by the tile that completes the count.  Both
+ * give the same bits.  The tile-side wait is bounded (twice the timeout of
+ * gsa_set_wait_timeout_us); if it expires, gsa_signal_pad_status reports
+ * GSA_ETIMEOUT with that tile's first flag tile and peer -1.  If any tile
+ * of the call failed, y and inv_rms are NaN.
  * Requires N <= 2^24 in addition.  Errors: GSA_EINVAL (also: ep or y NULL,
  * unknown y_dtype, misaligned pointer, eps negative or not finite),
  * GSA_EHIP. */
