@@ -174,17 +174,23 @@ __device__ __forceinline__ void store_out(const GemvArgs& a, int64_t i, float o)
     a.out[i] = o;
 }
 
-// The launch arguments as a kernel instance sees them: an fp32 instance (DT
-// false) takes slots and out as fp32 whatever the fields say, so every test
-// of the element types above folds away at compile time (the runtime tests
-// cost 0.2-0.4 us per call on the short rows, through the publish chain);
-// calls with bf16 slots or a bf16 out launch the DT instance.
-template <bool DT>
+// Element types of a kernel instance: fp32 slots and out, bf16 slots and
+// out, or either (tested at run time).
+constexpr int kDtF32 = 0;
+constexpr int kDtMixed = 1;
+constexpr int kDtBf16 = 2;
+
+// The launch arguments as a kernel instance sees them: an fp32 or bf16
+// instance fixes both element types, so every test of them above folds away
+// at compile time (the run-time tests cost 0.2-0.4 us per call on the short
+// rows, through the publish chain); calls with one of the two in bf16
+// launch the mixed instance.
+template <int DT>
 __device__ __forceinline__ GemvArgs typed_args(const GemvArgs& args) {
   GemvArgs a = args;
-  if constexpr (!DT) {
-    a.slot_bf16 = 0;
-    a.out_bf16 = 0;
+  if constexpr (DT != kDtMixed) {
+    a.slot_bf16 = DT == kDtBf16 ? 1 : 0;
+    a.out_bf16 = DT == kDtBf16 ? 1 : 0;
   }
   return a;
 }
@@ -1088,7 +1094,7 @@ __device__ __forceinline__ void valu_stream(float (&acc)[R][B], uint4 (&ring)[D]
 // on 16).  XM: XCD-contiguous tile order (block_tile).
 // LDS: x chunks [b][c], one zero chunk, one sink chunk, then the peer tile.
 template <int B, int G, int R, int NW, int NCH, int D, int XPT, int WPE, bool MASKED, bool TS,
-          bool XM, bool DT>
+          bool XM, int DT>
 __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs args) {
   const GemvArgs a = typed_args<DT>(args);
   constexpr int NT = NW * 64;
@@ -1253,7 +1259,7 @@ constexpr int kLongCtlWords = 4 + kLongRows / kFlagRows;  // s_ctl[4 + q]: epoch
 constexpr int pow2_at_least(int v) { return v <= 1 ? 1 : 2 * pow2_at_least((v + 1) / 2); }
 constexpr int log2_exact(int v) { return v <= 1 ? 0 : 1 + log2_exact(v / 2); }
 
-template <int B, int NCH, int D, int XPT, bool MASKED, bool DT>
+template <int B, int NCH, int D, int XPT, bool MASKED, int DT>
 __global__ __launch_bounds__(kLongWaves * 64, kLongWaves / 4) void gemv_ar_long(GemvArgs args) {
   const GemvArgs a = typed_args<DT>(args);
   constexpr int R = 2;
@@ -1429,7 +1435,7 @@ __device__ __forceinline__ void mfma_finish(const GemvArgs& a, int64_t tile, int
 // is finite).  The per-wave 16 x 16 fp32 partials are summed in wave order
 // through LDS.  One more wave runs the signal-pad protocol.
 // LDS: x [16][C + 1] chunks (column C zero); NW 16 x 16 partials; peer tile.
-template <int NW, int D, bool TS, bool DT>
+template <int NW, int D, bool TS, int DT>
 __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs args) {
   const GemvArgs a = typed_args<DT>(args);
   static_assert(NW * 4 == kBigTile, "each compute wave finishes 4 rows of the tile");
@@ -1525,7 +1531,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs args) 
 // wave's steps start at a rotation that differs between the workgroups of
 // one XCD so that they do not all read the same lines of x at once.
 // LDS: NW 16 x 16 partials, then the peer tile.
-template <int NW, int D, bool TS, bool DT>
+template <int NW, int D, bool TS, int DT>
 __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs args) {
   const GemvArgs a = typed_args<DT>(args);
   static_assert(NW * 4 == kBigTile, "each compute wave finishes 4 rows of the tile");
@@ -1651,7 +1657,7 @@ __global__ __launch_bounds__(256) void peer_publish_kernel(float* slots, uint32_
 constexpr int kMfmaXWaves = 4;
 constexpr int kMfmaXRows = 32;
 
-template <int NS, int D, bool DT>
+template <int NS, int D, int DT>
 __global__ __launch_bounds__(kMfmaXWaves * 64) void gemv_ar_mfma_xreg(GemvArgs args) {
   const GemvArgs a = typed_args<DT>(args);
   constexpr int RB = kMfmaXRows / 16;  // 16-row MFMA blocks
@@ -1840,7 +1846,7 @@ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // exact instance; any other C the masked streaming instance.  XPT covers
 // B * G * NCH chunks of x (at most 8 per thread; the rest of a longer x is
 // staged by a plain loop).
-template <int B, int G, int R, int NW, int NCH, int D, int WPE, bool TS, bool XM, bool DT>
+template <int B, int G, int R, int NW, int NCH, int D, int WPE, bool TS, bool XM, int DT>
 ValuChoice valu_tier(int C) {
   constexpr int XPT0 = ceil_div(B * G * NCH, NW * 64);
   constexpr int XPT = XPT0 > 8 ? 8 : XPT0;
@@ -1859,7 +1865,7 @@ ValuChoice valu_tier(int C) {
 // (the 70B-class down_proj shard), a masked streaming one for the others;
 // 4 chunk steps in flight (measured: 10.55 us on the 70B-class shape against
 // 11.1 at 3 and 10.6-12.0 at 5-7, cold, without the protocol).
-template <int B, bool DT>
+template <int B, int DT>
 ValuChoice long_tier(int C) {
   constexpr int kExactNch = 7;
   constexpr int XPT = ceil_div(B * 64 * kExactNch, kLongWaves * 64);
@@ -1880,24 +1886,24 @@ ValuChoice long_tier(int C) {
 // (4-row tiles on the longer rows measured slower: 5.4-5.5 against 5.25 us on
 // the 8B down_proj shape, 14.9 against 12.3 us on the 70B-class one.)  Tiles
 // of rows up to C = 224 go to the XCDs in contiguous runs (block_tile).
-// DT (bf16 slots or out) comes only with small tiles and one-shot: the
-// instances it takes are the ones those calls reach.
-template <int B, bool TS, bool DT>
+// DT other than fp32 (bf16 slots or out) comes only with small tiles and
+// one-shot: the instances it takes are the ones those calls reach.
+template <int B, bool TS, int DT>
 ValuChoice valu_kernel(int C, bool small_tiles) {
-  static_assert(!(DT && TS), "element types are for the one-shot call");
+  static_assert(!(DT != kDtF32 && TS), "element types are for the one-shot call");
   if (small_tiles && !TS && C > 224) return long_tier<B, DT>(C);
   if (small_tiles && C <= 64) return valu_tier<B, 32, 2, 1, 2, 2, 1, TS, true, DT>(C);
-  if constexpr (!DT) {
-    if (C <= 64) return valu_tier<B, 64, 4, 4, 1, 1, 1, TS, true, false>(C);
+  if constexpr (DT == kDtF32) {
+    if (C <= 64) return valu_tier<B, 64, 4, 4, 1, 1, 1, TS, true, kDtF32>(C);
   }
   if (C <= 224) return valu_tier<B, 32, 2, 4, 7, 4, 1, TS, true, DT>(C);
-  if constexpr (DT)
+  if constexpr (DT != kDtF32)
     return ValuChoice{nullptr, 0, 0};  // not reached: small tiles take the long tier
   else
-    return valu_tier<B, 64, 2, 8, 7, 3, 5, TS, false, false>(C);
+    return valu_tier<B, 64, 2, 8, 7, 3, 5, TS, false, kDtF32>(C);
 }
 
-template <bool TS, bool DT>
+template <bool TS, int DT>
 ValuChoice pick_kernel(int B, int C, bool small_tiles) {
   switch (B) {
     case 1: return valu_kernel<1, TS, DT>(C, small_tiles);
@@ -1936,15 +1942,18 @@ size_t gemv_lds_bytes(int W, int B, int C, bool epi, int tile_rows) {
   return partials + tail;
 }
 
-bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, bool typed, Launch* out) {
+bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, bool slot_bf16,
+                        bool out_bf16, Launch* out) {
   if (W < 1 || W > GSA_MAX_W || B < 1 || B > GSA_MAX_B || C < 1) return false;
   if (B <= 8 && (size_t)B * C * 16 > GSA_MAX_X_LDS_BYTES) return false;  // x staged in LDS
   if (epi && two_shot) return false;  // separate entry points
+  const bool typed = slot_bf16 || out_bf16;
   if (typed && (epi || two_shot)) return false;  // element types: the plain one-shot call only
   const bool small_tiles = !epi;  // the fused epilogue counts 16-row tiles
-  const ValuChoice k = two_shot ? pick_kernel<true, false>(B, C, small_tiles)
-                       : typed  ? pick_kernel<false, true>(B, C, small_tiles)
-                                : pick_kernel<false, false>(B, C, small_tiles);
+  const ValuChoice k = two_shot                 ? pick_kernel<true, kDtF32>(B, C, small_tiles)
+                       : slot_bf16 && out_bf16 ? pick_kernel<false, kDtBf16>(B, C, small_tiles)
+                       : typed                 ? pick_kernel<false, kDtMixed>(B, C, small_tiles)
+                                               : pick_kernel<false, kDtF32>(B, C, small_tiles);
   if (!k.kernel) return false;
   *out = {k.kernel, (unsigned)k.threads,
           k.no_dynamic_lds ? 0 : gemv_lds_bytes(W, B, C, epi, k.tile_rows), k.tile_rows};

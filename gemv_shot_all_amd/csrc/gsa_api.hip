@@ -314,10 +314,10 @@ int enqueue_call(const uint16_t* A_r, const uint16_t* x, void* slots_any, uint32
     if (h->slot_dtype == GSA_DTYPE_BF16 && !bf16_slots_ok) return GSA_EINVAL;
     a.slot_bf16 = h->slot_dtype == GSA_DTYPE_BF16 ? 1 : 0;
     if (gathered && h->gathered != gathered) return GSA_EINVAL;
-    // fp32 slots and out take the fp32 kernel instances; either in bf16 the
-    // instances that handle both element types
-    const bool typed = a.slot_bf16 || out_dtype == GSA_DTYPE_BF16;
-    if (!gsa::select_gemv_kernel(W, B, C, ep != nullptr, gathered != nullptr, typed, &l))
+    // kernel instances with the element types fixed (both fp32 or both
+    // bf16), or tested at run time (mixed)
+    if (!gsa::select_gemv_kernel(W, B, C, ep != nullptr, gathered != nullptr, a.slot_bf16 != 0,
+                                 out_dtype == GSA_DTYPE_BF16, &l))
       return GSA_EINVAL;
     a.row_stride = (int)h->row_stride;
     a.tiles = (int)((N + l.tile_rows - 1) / l.tile_rows);  // == h->tiles for 16-row tiles

@@ -93,7 +93,8 @@ struct Launch {
 // Pick the kernel for W ranks, batch B (1..16) and C chunks per row (with
 // the epilogue's extra LDS if epi).  Returns false if the shape exceeds the
 // LDS staging bound.
-bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, bool typed, Launch* out);
+bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, bool slot_bf16,
+                        bool out_bf16, Launch* out);
 // Dynamic LDS bytes a kernel of tile_rows rows per workgroup needs for (W, B, C, epi).
 size_t gemv_lds_bytes(int W, int B, int C, bool epi, int tile_rows);
 
