@@ -33,6 +33,8 @@
 // agent-scope (sc1) accesses; every result store of the workgroup completes
 // (s_waitcnt vmcnt(0), then a barrier) before its flags are stored.
 
+#include <type_traits>
+
 #include "gsa_device.h"
 #include "gsa_internal.h"
 
@@ -42,6 +44,9 @@ namespace {
 constexpr int kTok = 16;                     // tokens per MFMA tile: the B operand's 16 columns
 constexpr int kMaxTok = GSA_MOE_MAX_TOKENS;  // tokens one local expert takes per call
 constexpr int kWaves = 4;                    // compute waves per workgroup
+// Largest chunks per row (F / 8) for which two token tiles of x and the
+// partials of four feature tiles fit in 80 KB of LDS.
+constexpr int kTwoTileMaxC = (80 * 1024 - (kWaves * 256 * 4 + 256 * 4) * 4) / (2 * 16 * 16) - 1;
 static_assert(kMaxTok % kTok == 0, "whole token tiles");
 
 __device__ __forceinline__ uint32_t* moe_flag(const MoeArgs& a, int pad, int src, int e, int t) {
@@ -78,11 +83,12 @@ __device__ void moe_wait_peers(const MoeArgs& a, int lane, int e, int t0, int nt
   }
 }
 
-// LDS (dynamic): x [16][C + 1] chunks (column C and rows >= M zero), the
-// waves' 16 x (16 TPW) partials, the results token-major [16][16 TPW].
-// TPW: 16-feature tiles per workgroup (each x chunk read from LDS serves TPW
-// MFMAs); RING: weight steps in flight per lane.
-template <int TPW, int RING>
+// LDS (dynamic): x [16 NTT][C + 1] chunks (column C and rows past the
+// tokens zero), the waves' 16 x (16 TPW) partials, the results token-major
+// [16][16 TPW].  TPW: 16-feature tiles per workgroup (each x chunk read from
+// LDS serves TPW MFMAs); RING: weight steps in flight per lane; NTT: token
+// tiles one pass of the weights serves (each weight operand feeds NTT MFMAs).
+template <int TPW, int RING, int NTT>
 __global__ __launch_bounds__(kWaves * 64) void moe_gemm_a2a(MoeArgs a) {
   extern __shared__ uint4 lds[];
   __shared__ int64_t s_xrow[kMaxTok];  // token j: its row of X
@@ -99,7 +105,7 @@ __global__ __launch_bounds__(kWaves * 64) void moe_gemm_a2a(MoeArgs a) {
   const int nt = min(TPW, a.tiles - t0);
   const int C = a.C;
   const int CP = C + 1;  // padded LDS row: the 16 token rows of one chunk hit distinct banks
-  float* red = reinterpret_cast<float*>(lds + 16 * CP);
+  float* red = reinterpret_cast<float*>(lds + NTT * 16 * CP);
   float* yt = red + kWaves * 256 * TPW;
   uint32_t* own_pad = a.pads + (int64_t)a.rank * a.pad_words;
 
@@ -177,15 +183,23 @@ __global__ __launch_bounds__(kWaves * 64) void moe_gemm_a2a(MoeArgs a) {
     const int j = tid >> 4;  // the store phase: token j of the tile, feature n of each feature tile
     const int n = tid & 15;
 
-    for (int jt = 0; jt < M; jt += kTok) {
-      // Tokens jt .. jt + mt - 1 in LDS rows 0 .. mt - 1.  Each wave reads
-      // only its own k-slice of the rows (and the zero column C), so no
-      // barrier guards them; the partials' buffers are guarded by B1 / B2.
-      const int mt = min(kTok, M - jt);
+    // One pass of the weights over NT token tiles (tokens jt .. jt + 16 NT - 1,
+    // tile u in LDS rows 16 u ..): every weight operand feeds NT MFMAs, so the
+    // expert's weights are streamed once per NT tiles.  Each wave reads only
+    // its own k-slice of the rows (and the zero column C), so no barrier
+    // guards them; the partials' buffers are guarded by B1 / B2.
+    auto pass = [&](auto nt_const, int jt) {
+      constexpr int NT = decltype(nt_const)::value;
+      int mt[NT];
+#pragma unroll
+      for (int u = 0; u < NT; ++u) mt[u] = max(0, min(kTok, M - jt - u * kTok));
       for (int c0 = c_begin; c0 < c_end; c0 += 64) {
         if (c0 + lane < c_end) {
-          for (int t = 0; t < mt; ++t)
-            lds_dma16(xg + s_xrow[jt + t] * C + c0 + lane, lds + t * CP + c0);
+#pragma unroll
+          for (int u = 0; u < NT; ++u)
+            for (int t = 0; t < mt[u]; ++t)
+              lds_dma16(xg + s_xrow[jt + u * kTok + t] * C + c0 + lane,
+                        lds + (u * kTok + t) * CP + c0);
         }
       }
       uint4 ring[RING][TPW];
@@ -196,56 +210,78 @@ __global__ __launch_bounds__(kWaves * 64) void moe_gemm_a2a(MoeArgs a) {
       // The x copies went out before the ring loads: once at most RING * TPW
       // loads are outstanding they have landed.
       wait_vm_le<RING * TPW>();
-      for (int c = c_begin + lane; c < c_end; c += 64)
-        for (int t = mt; t < kTok; ++t) lds[t * CP + c] = make_uint4(0u, 0u, 0u, 0u);
-      if (lane < kTok) lds[lane * CP + C] = make_uint4(0u, 0u, 0u, 0u);
-
-      f32x4_t acc[TPW];
 #pragma unroll
-      for (int q = 0; q < TPW; ++q) acc[q] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int u = 0; u < NT; ++u)
+        for (int c = c_begin + lane; c < c_end; c += 64)
+          for (int t = mt[u]; t < kTok; ++t) lds[(u * kTok + t) * CP + c] = make_uint4(0u, 0u, 0u, 0u);
+      if (lane < NT * kTok) lds[lane * CP + C] = make_uint4(0u, 0u, 0u, 0u);
+
+      f32x4_t acc[TPW][NT];
+#pragma unroll
+      for (int q = 0; q < TPW; ++q)
+#pragma unroll
+        for (int u = 0; u < NT; ++u) acc[q][u] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
       for (int j0 = 0; j0 < n_steps; j0 += RING) {
-        uint4 xv[RING];
+        uint4 xv[RING][NT];
 #pragma unroll
         for (int u = 0; u < RING; ++u) {
           const int js = j0 + u;
           const int chunk = 4 * (s_begin + js) + kq;
-          xv[u] = lds[xrow + (js < n_steps && chunk < C ? chunk : C)];
+#pragma unroll
+          for (int v = 0; v < NT; ++v)
+            xv[u][v] = lds[v * kTok * CP + xrow + (js < n_steps && chunk < C ? chunk : C)];
         }
 #pragma unroll
         for (int u = 0; u < RING; ++u) {
 #pragma unroll
           for (int q = 0; q < TPW; ++q) {
-            acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ring[u][q]),
-                                                             __builtin_bit_cast(bf16x8_t, xv[u]),
-                                                             acc[q], 0, 0, 0);
+#pragma unroll
+            for (int v = 0; v < NT; ++v)
+              acc[q][v] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, ring[u][q]), __builtin_bit_cast(bf16x8_t, xv[u][v]),
+                  acc[q][v], 0, 0, 0);
             ring[u][q] = buf_load16_cached(ra, a_off(j0 + u + RING, q));
           }
           __builtin_amdgcn_sched_barrier(0);
         }
       }
-      // Partials: feature 4 * (lane >> 4) + q, token lane & 15.
-      // red[wave][q*16 + feature][token]
 #pragma unroll
-      for (int q = 0; q < TPW; ++q)
+      for (int v = 0; v < NT; ++v) {
+        // Partials: feature 4 * (lane >> 4) + q, token lane & 15.
+        // red[wave][q*16 + feature][token]
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          red[(wave * 16 * TPW + q * 16 + 4 * (lane >> 4) + r) * 16 + (lane & 15)] = acc[q][r];
-      __syncthreads();  // B1
+        for (int q = 0; q < TPW; ++q)
 #pragma unroll
-      for (int q = 0; q < TPW; ++q) {
-        const int nl = q * 16 + 4 * wave + (lane >> 4);
-        const int bl = lane & 15;
-        float y = red[nl * 16 + bl];
+          for (int r = 0; r < 4; ++r)
+            red[(wave * 16 * TPW + q * 16 + 4 * (lane >> 4) + r) * 16 + (lane & 15)] = acc[q][v][r];
+        __syncthreads();  // B1
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) y = y + red[(w * 16 * TPW + nl) * 16 + bl];
-        yt[bl * 16 * TPW + nl] = y;
+        for (int q = 0; q < TPW; ++q) {
+          const int nl = q * 16 + 4 * wave + (lane >> 4);
+          const int bl = lane & 15;
+          float y = red[nl * 16 + bl];
+#pragma unroll
+          for (int w = 1; w < kWaves; ++w) y = y + red[(w * 16 * TPW + nl) * 16 + bl];
+          yt[bl * 16 * TPW + nl] = y;
+        }
+        __syncthreads();  // B2: results token-major (and red free again)
+#pragma unroll
+        for (int q = 0; q < TPW; ++q) {
+          const int64_t feat = (int64_t)(t0 + q) * 16 + n;
+          if (j < mt[v] && q < nt && feat < a.H)
+            store_coherent(&a.bufs[s_dst[jt + v * kTok + j] + feat], yt[j * 16 * TPW + q * 16 + n]);
+        }
       }
-      __syncthreads();  // B2: results token-major
-#pragma unroll
-      for (int q = 0; q < TPW; ++q) {
-        const int64_t feat = (int64_t)(t0 + q) * 16 + n;
-        if (j < mt && q < nt && feat < a.H)
-          store_coherent(&a.bufs[s_dst[jt + j] + feat], yt[j * 16 * TPW + q * 16 + n]);
+    };
+    // Two token tiles per pass where the launch staged room for them and
+    // more than one tile's tokens remain; one otherwise.
+    for (int jt = 0; jt < M;) {
+      if (NTT >= 2 && M - jt > kTok) {
+        pass(std::integral_constant<int, (NTT >= 2 ? 2 : 1)>{}, jt);
+        jt += (NTT >= 2 ? 2 : 1) * kTok;
+      } else {
+        pass(std::integral_constant<int, 1>{}, jt);
+        jt += kTok;
       }
     }
   }
@@ -281,23 +317,25 @@ __global__ void a2a_reset_kernel(uint32_t* pads, int ne, int row_stride, int64_t
 
 namespace {
 
-template <int TPW>
+template <int TPW, int NTT>
 size_t lds_bytes(int C) {
-  return (size_t)16 * (C + 1) * 16 + (size_t)(kWaves * 256 * TPW + 256 * TPW) * sizeof(float);
+  return (size_t)16 * NTT * (C + 1) * 16 +
+         (size_t)(kWaves * 256 * TPW + 256 * TPW) * sizeof(float);
 }
 
-template <int TPW, int RING>
+template <int TPW, int RING, int NTT>
 hipError_t launch(const MoeArgs& a, hipStream_t s) {
-  const size_t lds = lds_bytes<TPW>(a.C);
+  const size_t lds = lds_bytes<TPW, NTT>(a.C);
   if (lds > 65536) {
     // Opt in to the largest dynamic LDS this instance may use (cheap, idempotent).
     const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&moe_gemm_a2a<TPW, RING>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes<TPW>(GSA_MOE_MAX_F / 8));
+        reinterpret_cast<const void*>(&moe_gemm_a2a<TPW, RING, NTT>),
+        hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)lds_bytes<TPW, NTT>(NTT > 1 ? kTwoTileMaxC : GSA_MOE_MAX_F / 8));
     if (e != hipSuccess) return e;
   }
   const unsigned grid = (unsigned)(a.ne * ((a.tiles + TPW - 1) / TPW));
-  hipLaunchKernelGGL((moe_gemm_a2a<TPW, RING>), dim3(grid), dim3(kWaves * 64), lds, s, a);
+  hipLaunchKernelGGL((moe_gemm_a2a<TPW, RING, NTT>), dim3(grid), dim3(kWaves * 64), lds, s, a);
   return hipGetLastError();
 }
 
@@ -310,8 +348,16 @@ hipError_t launch(const MoeArgs& a, hipStream_t s) {
 // Measured on the Qwen3-30B-A3B-like (F = 768) and DeepSeek-V3-like
 // (F = 2048) shapes: one tile per workgroup 21.7 / 236 us, two 18.7 / 205,
 // four 17.0 / 230.
+//
+// Experts narrow enough that two token tiles of x stay within 80 KB of LDS
+// with the partials (two workgroups per CU) take two token tiles per pass of
+// their weights: an expert with more than 16 tokens streams its weights half
+// as often (the host does not know the token counts, which live on the
+// device; an expert with at most 16 takes the one-tile pass, at the price of
+// the second tile's LDS).
 hipError_t launch_moe(const MoeArgs& a, hipStream_t s) {
-  return a.F <= 1024 ? launch<4, 4>(a, s) : launch<2, 8>(a, s);
+  if (a.F > 1024) return launch<2, 8, 1>(a, s);
+  return a.C <= kTwoTileMaxC ? launch<4, 4, 2>(a, s) : launch<4, 4, 1>(a, s);
 }
 
 hipError_t launch_a2a_reset(uint32_t* pads, int W, int ne, int row_stride, int64_t pad_words,

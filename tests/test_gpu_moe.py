@@ -143,6 +143,8 @@ EDGE = [
     (4, 1, 80, 768, 2, [48], 1),            # three token tiles, gaps between segments
     (2, 2, 48, 2048, 1, [33, 0], 0),        # wide experts, three token tiles (the last of 1)
     (2, 1, 40, 64, 1, [256], 0),            # the most tokens an expert takes
+    (2, 1, 48, 512, 0, [33], 0),            # two token tiles per weight pass, then a tile of 1
+    (2, 1, 32, 960, 1, [40], 0),            # C = 120: one token tile per pass (LDS bound)
 ]
 
 
