@@ -1633,40 +1633,67 @@ __global__ __launch_bounds__(256) void peer_publish_kernel(float* slots, uint32_
   for (int64_t t = threadIdx.x; t < nflags; t += blockDim.x) store_flag(row + flag_word(t), epoch);
 }
 
-// MFMA path with x in registers: 8 < B <= 16 (batch padded to 16 with
-// zeros), rows of exactly 16 * NS chunks, the plain one-shot call.  One
-// workgroup of 4 waves owns 32 rows, two 16-row blocks of
-// v_mfma_f32_16x16x32_bf16 (A rows as the A operand, x as the B operand);
-// wave w owns k-steps [w NS, (w + 1) NS) of both blocks.  Operand layout per
-// lane l: A row (l & 15), batch column (l & 15), k-chunk (l >> 4) of the
-// step's four 8-element chunks; result rows 4 (l >> 4) + e, column (l & 15).
-// Each lane's x operand of every one of its steps is loaded once, into
-// registers, ahead of every A load (a scheduling barrier keeps the order):
-// no LDS copy of x and no barrier before the first MFMA, where the
-// 16-row kernel copies all of x into LDS in every workgroup (by LDS DMA,
-// whose LDS reads the compiler then orders behind every outstanding load).
-// The A stream is fully unrolled, D steps in flight, so its waits count
-// exactly.  The waves' partials are summed in wave order through LDS; each
-// thread then owns two outputs, whose peer values it loads right behind its
-// last A load, and publishes and sums as the long-row kernel does; wave 0
-// runs the signal-pad protocol.
-// Measured on the skinny GEMM (W = 4, 8192 x 2048 share, B = 16; cold, per
-// call): 10.7 us against 13.3 us for the 16-row kernel.  A plain read of the
-// same rows takes 6.4 us, and 8.3 us with the MFMA operand's access pattern
-// (64 bytes of each of 16 rows per load instruction).
-constexpr int kMfmaXWaves = 4;
-constexpr int kMfmaXRows = 32;
+// MFMA path with A staged through LDS: 8 < B <= 16, rows of exactly 256
+// chunks, the plain one-shot call (the skinny GEMM).  One workgroup owns 32
+// rows (two 16-row blocks of v_mfma_f32_16x16x32_bf16) with 4 consumer waves
+// and 2 producer waves.  Consumer wave w owns chunks [64 w, 64 w + 64) of
+// every row, in 8 stages of 8 chunks.  The producers copy A into LDS with
+// direct-to-LDS loads, 4 stages in flight: each copy instruction reads 8 rows
+// x 128 bytes (whole lines; the MFMA operand itself reads 64 bytes of each of
+// 16 rows per instruction, half a line, which measured 8.3 us against 6.4
+// for the same bytes read whole), laid out in 1 KB blocks with the chunk
+// index XOR-ed with the row, so that a consumer's 16-row operand read hits
+// 16 distinct banks.  Stage j is complete when its producer's counted wait
+// returns; a plain s_barrier then hands it over (a barrier with a fence
+// would wait for every copy in flight).  The consumers issue no A loads, so
+// their LDS reads carry no wait for the copies; they load their x operands
+// a stage at a time, two stages ahead (all of x at the start, 64 KB per
+// workgroup at once, cost 1.1 us), and the peer values of their two outputs
+// right behind their last x loads.  Wave 0 runs the signal-pad protocol and
+// takes the start decision before the first stage barrier.  The waves'
+// partials are summed in wave order through LDS; each consumer thread then
+// owns two outputs, sums them with their peer values in rank order and
+// publishes them (the long-row kernel's scheme).  Measured on the skinny
+// GEMM (cold, per call): without the protocol 7.9 us against 9.6 for the
+// same MFMAs with every lane loading its own A operands and all of x in
+// registers; with it 9.0 against 10.4.
+constexpr int kMfmaLCons = 4;     // consumer waves (MFMA)
+constexpr int kMfmaLProd = 2;     // producer waves (A into LDS)
+constexpr int kMfmaLRows = 32;
+constexpr int kMfmaLStages = 8;   // stages per workgroup: 8 chunks of each consumer's 64
+constexpr int kMfmaLInFlight = 4; // stages in LDS at once
+constexpr int kMfmaLBlocks = kMfmaLCons * (kMfmaLRows / 8);  // 1 KB blocks per stage
+constexpr int kMfmaLStageBytes = kMfmaLBlocks * 1024;
+constexpr size_t kMfmaLLdsBytes = (size_t)kMfmaLInFlight * kMfmaLStageBytes +
+                                  (size_t)kMfmaLCons * kMfmaLRows * 16 * sizeof(float);
 
-template <int NS, int D, int DT>
-__global__ __launch_bounds__(kMfmaXWaves * 64) void gemv_ar_mfma_xreg(GemvArgs args) {
+// s_waitcnt vmcnt(n) for a count known only after unrolling (0 <= n <= 63).
+template <int K>
+__device__ __forceinline__ void wait_vm_le_n(int n) {
+  if constexpr (K >= 0) {
+    if (n == K)
+      wait_vm_le<K>();
+    else
+      wait_vm_le_n<K - 1>(n);
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__((kMfmaLCons + kMfmaLProd) * 64) void gemv_ar_mfma_lds(GemvArgs args) {
   const GemvArgs a = typed_args<DT>(args);
-  constexpr int RB = kMfmaXRows / 16;  // 16-row MFMA blocks
-  constexpr int NT = kMfmaXWaves * 64;
-  constexpr int TR = kMfmaXRows;
-  constexpr int OPT = TR * 16 / NT;    // outputs per thread (batch padded to 16)
-  static_assert(kMfmaXRows / kFlagRows * kMaxW <= 64, "one wave-0 lane per (flag tile, rank)");
-  static_assert(NS > D, "the peer loads follow the last A refill");
-  __shared__ float red[kMfmaXWaves][RB][16][16];
+  constexpr int RB = kMfmaLRows / 16;
+  constexpr int NT = kMfmaLCons * 64;  // consumer threads
+  constexpr int TR = kMfmaLRows;
+  constexpr int OPT = TR * 16 / NT;    // outputs per consumer thread
+  constexpr int NS = kMfmaLStages;
+  constexpr int S = kMfmaLInFlight;
+  constexpr int PER = kMfmaLBlocks / kMfmaLProd;  // copies per producer per stage
+  constexpr int XPF = 2;                          // stages of x loaded ahead
+  static_assert(PER * S <= 63, "a producer's copies in flight fit the vmcnt counter");
+  static_assert(kMfmaLRows / kFlagRows * kMaxW <= 64, "one wave-0 lane per (flag tile, rank)");
+  static_assert(NS > XPF, "the peer loads follow the last x loads");
+  extern __shared__ __align__(16) unsigned char lds_a[];
+  float* red = reinterpret_cast<float*>(lds_a + S * kMfmaLStageBytes);  // [wave][RB][16][16]
   __shared__ uint32_t s_ctl[kLongCtlWords];
 
   const int tid = threadIdx.x;
@@ -1674,8 +1701,40 @@ __global__ __launch_bounds__(kMfmaXWaves * 64) void gemv_ar_mfma_xreg(GemvArgs a
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t tile = blockIdx.x;
   const FlagSpan fs = flag_span<TR>(a, tile);
-  const int C = a.C;  // == 16 * NS
-  const int s0 = wave * NS;
+  const int C = a.C;  // == 256
+  const int64_t row0 = tile * TR;
+
+  if (wave >= kMfmaLCons) {
+    // Producer p: blocks b = 2 i + p of every stage; block b holds rows
+    // 8 (b % 4) .. + 7 of consumer wave b / 4's 8 chunks; lane l copies row
+    // l / 8, chunk (l % 8) ^ (l / 8) of it (rows past N repeat row N - 1).
+    const int p = wave - kMfmaLCons;
+    auto issue = [&](int j, int buf) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int b = 2 * i + p;
+        const int64_t r = min(row0 + (b & 3) * 8 + (lane >> 3), a.N - 1);
+        const int chunk = 64 * (b >> 2) + 8 * j + ((lane & 7) ^ (lane >> 3));
+        lds_dma16<2>(a.A + (r * C + chunk) * 8, lds_a + buf * kMfmaLStageBytes + b * 1024);
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < S; ++j) issue(j, j);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      // stage j complete: only the copies of later stages may be in flight
+      const int last = min(NS - 1, S - 1 + max(0, j - 1));
+      wait_vm_le_n<63>((last - j) * PER);
+      asm volatile("s_barrier" ::: "memory");  // stage j handed over
+      if (j >= 1 && j - 1 + S < NS) issue(j - 1 + S, (j - 1) % S);  // the buffer of stage j - 1
+    }
+    __syncthreads();  // R: partials
+    const uint32_t state = s_ctl[1];
+    __syncthreads();  // B2
+    if (state == kMustWait) __syncthreads();  // B3
+    return;
+  }
+
   const int kq = lane >> 4;
   const int l16 = lane & 15;
   const uint32_t kOutOfRange = 0x80000000u;  // past any buffer: reads zeros
@@ -1684,32 +1743,18 @@ __global__ __launch_bounds__(kMfmaXWaves * 64) void gemv_ar_mfma_xreg(GemvArgs a
   if (wave == 0) fl = load_flag(a, fs, lane);
   __builtin_amdgcn_sched_barrier(0);
 
-  // x: batch l16 (zeros past B), chunk 4 (s0 + s) + kq of every step s.
+  // x: batch l16 (zeros past B), chunk 64 wave + 4 s + kq of MFMA step s.
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(a.B * C * 16));
-  uint4 xv[NS];
+  auto x_off = [&](int s2) {
+    return l16 < a.B ? ((uint32_t)l16 * (uint32_t)C + 64u * wave + 4u * s2 + kq) * 16u
+                     : kOutOfRange;
+  };
+  uint4 xv[2 * NS];
 #pragma unroll
-  for (int s = 0; s < NS; ++s)
-    xv[s] = buf_load16_cached(
-        rx, l16 < a.B ? ((uint32_t)l16 * (uint32_t)C + 4u * (s0 + s) + kq) * 16u : kOutOfRange);
-  __builtin_amdgcn_sched_barrier(0);
-
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, (uint32_t)(a.N * C * 16));
-  const int64_t row0 = tile * TR;
-  uint32_t arow[RB];
-#pragma unroll
-  for (int r = 0; r < RB; ++r)
-    arow[r] = ((uint32_t)(row0 + 16 * r + l16) * (uint32_t)C + 4u * s0 + kq) * 16u;
-  uint4 ring[D][RB];
-#pragma unroll
-  for (int u = 0; u < D; ++u)
-#pragma unroll
-    for (int r = 0; r < RB; ++r) ring[u][r] = buf_load16(ra, arow[r] + u * 64u);
+  for (int s2 = 0; s2 < 2 * XPF; ++s2) xv[s2] = buf_load16_cached(rx, x_off(s2));
 
   if (wave == 0) comm_decide<false, TR>(a, lane, tile, fs, fl, s_ctl);
-  __syncthreads();  // B1: the start decision in s_ctl
-  const uint32_t state = s_ctl[1];
 
-  // This thread's outputs: o = tid + NT i, local row o / 16, column o % 16.
   const int64_t NB = a.N * a.B;
   int64_t oi[OPT];
   bool live[OPT];
@@ -1727,40 +1772,56 @@ __global__ __launch_bounds__(kMfmaXWaves * 64) void gemv_ar_mfma_xreg(GemvArgs a
 #pragma unroll
   for (int r = 0; r < RB; ++r) acc[r] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
+  for (int j = 0; j < NS; ++j) {
+    // this wave's reads of stage j - 1 are complete; stage j is in LDS
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (j + XPF < NS) {
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      acc[r] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, ring[s % D][r]),
-                                                       __builtin_bit_cast(bf16x8_t, xv[s]), acc[r],
-                                                       0, 0, 0);
-      if (s + D < NS) ring[s % D][r] = buf_load16(ra, arow[r] + (s + D) * 64u);
+      for (int m = 0; m < 2; ++m) xv[2 * (j + XPF) + m] = buf_load16_cached(rx, x_off(2 * (j + XPF) + m));
     }
-    if (s == NS - D - 1) {
-      // The peer values, right behind the lane's last A load: unconditional
-      // (clamped) loads, unused unless every peer had published at the
-      // start.  Issued after B1 instead, ahead of the A refills, they held
-      // the stream up: 11.5 against 10.7 us per call on the skinny GEMM.
+    if (j == NS - 1 - XPF) {
+      // The peer values, right behind the last x loads: unconditional
+      // (clamped) loads, unused unless every peer had published at the start.
 #pragma unroll
       for (int i = 0; i < OPT; ++i)
 #pragma unroll
         for (int r = 0; r < kMaxW; ++r) pv[i][r] = load_slot_bits(a, min(r, a.W - 1) * NB + oi[i]);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    const unsigned char* st = lds_a + (j % S) * kMfmaLStageBytes;
+    uint4 av[2][RB];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        const int row = rb * 16 + l16;
+        const int c = 4 * m + kq;  // chunk within the wave's 8 of this stage
+        const int off = (wave * 4 + (row >> 3)) * 1024 + (row & 7) * 128 + ((c ^ (row & 7)) * 16);
+        av[m][rb] = *reinterpret_cast<const uint4*>(st + off);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[m][rb]),
+                                                          __builtin_bit_cast(bf16x8_t, xv[2 * j + m]),
+                                                          acc[rb], 0, 0, 0);
   }
 #pragma unroll
   for (int r = 0; r < RB; ++r)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) red[wave][r][4 * kq + e][l16] = acc[r][e];
-  __syncthreads();  // every wave's partials in LDS
+    for (int e = 0; e < 4; ++e) red[((wave * RB + r) * 16 + 4 * kq + e) * 16 + l16] = acc[r][e];
+  __syncthreads();  // R: every wave's partials in LDS, the start decision in s_ctl
+  const uint32_t state = s_ctl[1];
 
   float yp[OPT], outv[OPT];
 #pragma unroll
   for (int i = 0; i < OPT; ++i) {
     const int o = tid + NT * i;
     const int lr = o / 16, b = o % 16;
-    float y = red[0][lr / 16][lr % 16][b];
+    float y = red[((0 * RB + lr / 16) * 16 + lr % 16) * 16 + b];
 #pragma unroll
-    for (int w = 1; w < kMfmaXWaves; ++w) y = y + red[w][lr / 16][lr % 16][b];
+    for (int w = 1; w < kMfmaLCons; ++w) y = y + red[((w * RB + lr / 16) * 16 + lr % 16) * 16 + b];
     yp[i] = publish_value(a, y);  // y as published: the own term of the sum
     outv[i] = 0.0f;
     if (state == kPeersReady) {
@@ -1836,7 +1897,8 @@ struct ValuChoice {
   const void* kernel;
   int threads;    // per workgroup (compute waves, plus the communication wave if the kernel has one)
   int tile_rows;  // rows per workgroup
-  bool no_dynamic_lds = false;  // the kernel's LDS is all static
+  bool fixed_lds = false;  // dynamic LDS of a fixed size (lds_bytes), not from the shape
+  size_t lds_bytes = 0;
 };
 
 constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -1915,10 +1977,10 @@ ValuChoice pick_kernel(int B, int C, bool small_tiles) {
     case 7: return valu_kernel<7, TS, DT>(C, small_tiles);
     case 8: return valu_kernel<8, TS, DT>(C, small_tiles);
     default:
-      // Rows of exactly 256 chunks (4 waves x 16 k-steps), plain call: x in registers.
+      // Rows of exactly 256 chunks, plain call: A staged through LDS.
       if (!TS && small_tiles && C == 16 * 16)
-        return ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma_xreg<16, 4, DT>),
-                          kMfmaXWaves * 64, kMfmaXRows, true};
+        return ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma_lds<DT>),
+                          (kMfmaLCons + kMfmaLProd) * 64, kMfmaLRows, true, kMfmaLLdsBytes};
       return mfma_x_in_lds(C)
                  ? ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma<kMfmaWaves, 8, TS, DT>),
                               (kMfmaWaves + 1) * 64, kBigTile}
@@ -1956,7 +2018,7 @@ bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, bool slot_
                                                : pick_kernel<false, kDtF32>(B, C, small_tiles);
   if (!k.kernel) return false;
   *out = {k.kernel, (unsigned)k.threads,
-          k.no_dynamic_lds ? 0 : gemv_lds_bytes(W, B, C, epi, k.tile_rows), k.tile_rows};
+          k.fixed_lds ? k.lds_bytes : gemv_lds_bytes(W, B, C, epi, k.tile_rows), k.tile_rows};
   return true;
 }
 

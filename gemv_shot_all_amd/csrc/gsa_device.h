@@ -61,11 +61,13 @@ __device__ __forceinline__ void wait_vm_all() { wait_vm_le<0>(); }
 
 // Copy 16 bytes per active lane from global memory straight into LDS: lane l
 // writes lds_base + 16 * l (lds_base is wave-uniform).  Completion is counted
-// by vmcnt like any other vector load.
+// by vmcnt like any other vector load.  CPOL: cache policy (2: the
+// non-temporal hint, for data streamed once).
+template <int CPOL = 0>
 __device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
   __builtin_amdgcn_global_load_lds(
       (const void __attribute__((address_space(1)))*)src,
-      (void __attribute__((address_space(3)))*)lds_base, 16, 0, 0);
+      (void __attribute__((address_space(3)))*)lds_base, 16, 0, CPOL);
 }
 
 }  // namespace
