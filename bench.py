@@ -60,14 +60,16 @@ def two_shot_chunk_rows(N, W):
     return -(-(-(-N // W)) // 16) * 16
 
 
-def alg_bytes(W, N, K, B, epilogue=False, two_shot=False, rank=0, slot_bytes=4, out_bytes=4):
+def alg_bytes(W, N, K, B, epilogue=False, two_shot=False, rank=0, slot_bytes=4, out_bytes=4,
+              unfused=False):
     """Bytes the method itself must move per call: A_r, x_r, the published
     slot, the W-1 peer slots and out (flags excluded); with the fused
     epilogue also the bias and RMSNorm weight (N fp32 each) and y (bf16).
     Two-shot: the peer slots only over the own chunk's c rows, plus the
     published chunk (c rows) and the N - c rows copied from their owners.
     slot_bytes / out_bytes: element sizes of the slots and of out (4 for
-    fp32, 2 for bf16; the two-shot and epilogue calls take fp32)."""
+    fp32, 2 for bf16; the two-shot and epilogue calls take fp32).  unfused: the
+    epilogue as a second kernel, which reads out back (4 N B more)."""
     Ks = K // W
     if two_shot:
         c = max(0, min(N, (rank + 1) * two_shot_chunk_rows(N, W)) -
@@ -76,7 +78,7 @@ def alg_bytes(W, N, K, B, epilogue=False, two_shot=False, rank=0, slot_bytes=4, 
                 4 * (N - c) * B + 4 * N * B)
     base = (2 * N * Ks + 2 * B * Ks + slot_bytes * N * B + slot_bytes * (W - 1) * N * B +
             out_bytes * N * B)
-    return base + (8 * N + 2 * N * B if epilogue else 0)
+    return base + (8 * N + 2 * N * B if epilogue else 0) + (4 * N * B if unfused else 0)
 
 
 def alg_flops(W, N, K, B):
@@ -89,9 +91,11 @@ def kernel_source_digest(path=KERNEL_SOURCE):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def profile_name(cfg, epilogue=False, two_shot=False, slot_dtype="f32", out_dtype="f32"):
+def profile_name(cfg, epilogue=False, two_shot=False, slot_dtype="f32", out_dtype="f32",
+                 unfused=False):
     """Base name of the committed rocprofv3 summaries for a bench line."""
-    variant = "_rmsnorm" if epilogue else "_two_shot" if two_shot else ""
+    variant = ("_rmsnorm_unfused" if unfused else "_rmsnorm" if epilogue else
+               "_two_shot" if two_shot else "")
     if slot_dtype != "f32" or out_dtype != "f32":
         variant += f"_slots_{slot_dtype}_out_{out_dtype}"
     return f"gemv_allreduce{variant}_{cfg}"
@@ -117,7 +121,7 @@ class Sets:
     buffer (peers published) and output."""
 
     def __init__(self, d, rotate_bytes, max_sets=None, epilogue=False, two_shot=False,
-                 slot_dtype="f32", out_dtype="f32"):
+                 slot_dtype="f32", out_dtype="f32", unfused=False):
         import torch
 
         import gemv_shot_all_amd as gsa
@@ -125,6 +129,7 @@ class Sets:
         W, N, K, B = d["W"], d["N"], d["K"], d["B"]
         self.W, self.N, self.K, self.B, self.rank = W, N, K, B, d["rank"]
         self.epilogue = epilogue
+        self.unfused = unfused  # the epilogue as a second kernel after the plain call
         self.two_shot = two_shot
         self.slot_bf16 = slot_dtype == "bf16"
         self.out_bf16 = out_dtype == "bf16"
@@ -190,7 +195,11 @@ class Sets:
         j = i % self.R
         self.touched.add(j)
         b = self.bufs[j]
-        if self.epilogue:
+        if self.epilogue and self.unfused:
+            self.gsa.gsa_gemv_allreduce(self.A[j], self.x[j], b.slots, b.pad, self.out[j],
+                                        self.W, self.rank, self.N, self.K, self.B)
+            self.gsa.gsa_bias_rmsnorm(self.out[j], self.N, self.B, self.eps[j])
+        elif self.epilogue:
             self.gsa.gsa_gemv_allreduce_rmsnorm(self.A[j], self.x[j], b.slots, b.pad,
                                                 self.out[j], self.W, self.rank, self.N, self.K,
                                                 self.B, self.eps[j])
@@ -405,7 +414,7 @@ def run_config(cfg, args):
     d = gi.make_inputs(cfg, seed=args.seed, rank=0)
     W, N, K, B = d["W"], d["N"], d["K"], d["B"]
     sets = Sets(d, args.rotate_mib << 20 if not args.warm else 1, args.max_sets, args.epilogue,
-                args.two_shot, args.slot_dtype, args.out_dtype)
+                args.two_shot, args.slot_dtype, args.out_dtype, args.epilogue_unfused)
     timer = ColdTimer(args.flush_mib if not args.warm else 0)
     try:
         # Warm-up: exactly args.warmup untimed calls.
@@ -449,12 +458,13 @@ def run_config(cfg, args):
         timer.close()
         sets.close()
 
-    nbytes = alg_bytes(W, N, K, B, args.epilogue, args.two_shot,
+    nbytes = alg_bytes(W, N, K, B, args.epilogue, args.two_shot, unfused=args.epilogue_unfused,
                        slot_bytes=2 if args.slot_dtype == "bf16" else 4,
                        out_bytes=2 if args.out_dtype == "bf16" else 4)
     achieved = nbytes / (us_per_call * 1e-6) / 1e9
     traffic = traffic_from_profile(cfg, name=profile_name(cfg, args.epilogue, args.two_shot,
-                                                          args.slot_dtype, args.out_dtype))
+                                                          args.slot_dtype, args.out_dtype,
+                                                          unfused=args.epilogue_unfused))
     line = {
         "metric": METRIC,
         "value": round(us_per_call, 4),
@@ -477,7 +487,9 @@ def run_config(cfg, args):
             "timing": "hipGraph replay of K calls, HIP events on the launch stream, between "
                       "two device syncs",
             "untimed_calls_before_timed_region": args.warmup,
-            "epilogue": ("bias + RMSNorm over rows (eps 1e-5), y in bf16" if args.epilogue
+            "epilogue": ("bias + RMSNorm over rows (eps 1e-5), y in bf16, as a second kernel "
+                         "(gsa_bias_rmsnorm) after the plain call" if args.epilogue_unfused else
+                         "bias + RMSNorm over rows (eps 1e-5), y in bf16" if args.epilogue
                          else "none"),
             "all_reduce": "two-shot" if args.two_shot else "one-shot",
             "slots": args.slot_dtype, "out": args.out_dtype,
@@ -720,6 +732,9 @@ def main():
                         "host threads (0 = skip)")
     p.add_argument("--epilogue", action="store_true",
                    help="time gsa_gemv_allreduce_rmsnorm (bias + RMSNorm, y in bf16) instead")
+    p.add_argument("--epilogue-unfused", action="store_true",
+                   help="time the plain call followed by gsa_bias_rmsnorm (the same epilogue "
+                        "as a second kernel) in the same graph")
     p.add_argument("--two-shot", action="store_true",
                    help="time gsa_gemv_allreduce_two_shot (reduce the own chunk, copy the "
                         "others) instead")
@@ -734,6 +749,8 @@ def main():
                    help="also run a plain device copy of this many MiB five times "
                         "(reference kernel for scaling HBM byte counters)")
     args = p.parse_args()
+    if args.epilogue_unfused:
+        args.epilogue = True
     if args.epilogue and args.two_shot:
         p.error("--epilogue and --two-shot are separate entry points; pick one")
     if (args.epilogue or args.two_shot) and (args.slot_dtype != "f32" or args.out_dtype != "f32"):

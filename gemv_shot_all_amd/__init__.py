@@ -14,7 +14,8 @@ from ._lib import (  # noqa: F401
     GSA_FLAG_TILE_ROWS, flag_word,
     GSA_MOE_TILE_ROWS, GSA_MAX_B, GSA_MAX_W,
     GSA_MAX_X_LDS_BYTES, GSA_OK, GSA_PAD_HEADER_WORDS, GsaError, SymmBuffer, device_view,
-    gsa_epilogue, gsa_gemv_allreduce, gsa_gemv_allreduce_dtype, gsa_gemv_allreduce_rmsnorm, gsa_gemv_allreduce_rmsnorm_noalloc,
+    gsa_bias_rmsnorm, gsa_epilogue, gsa_gemv_allreduce, gsa_gemv_allreduce_dtype,
+    gsa_gemv_allreduce_rmsnorm, gsa_gemv_allreduce_rmsnorm_noalloc,
     gsa_gemv_allreduce_two_shot,
     gsa_peer_publish, gsa_set_wait_timeout_us, gsa_signal_pad_reset, gsa_signal_pad_row_stride,
     gsa_signal_pad_status, gsa_strerror, gsa_symm_alloc, gsa_symm_alloc_dtype, gsa_symm_free, gsa_symm_gathered,

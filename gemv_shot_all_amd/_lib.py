@@ -30,7 +30,7 @@ GSA_MOE_MAX_F = 4088
 EXPORTS = ("gsa_symm_alloc", "gsa_symm_alloc_dtype", "gsa_symm_free", "gsa_symm_slots", "gsa_symm_signal_pad",
            "gsa_symm_gathered", "gsa_signal_pad_row_stride", "gsa_signal_pad_reset",
            "gsa_gemv_allreduce", "gsa_gemv_allreduce_dtype", "gsa_gemv_allreduce_two_shot",
-           "gsa_gemv_allreduce_rmsnorm", "gsa_gemv_allreduce_rmsnorm_noalloc",
+           "gsa_gemv_allreduce_rmsnorm", "gsa_gemv_allreduce_rmsnorm_noalloc", "gsa_bias_rmsnorm",
            "gsa_peer_publish", "gsa_signal_pad_status", "gsa_set_wait_timeout_us",
            "gsa_strerror",
            "gsa_a2a_pad_words", "gsa_a2a_alloc", "gsa_a2a_free", "gsa_a2a_buffers",
@@ -95,6 +95,8 @@ def lib():
         L.gsa_gemv_allreduce_rmsnorm.restype = ci
         L.gsa_gemv_allreduce_rmsnorm_noalloc.argtypes = L.gsa_gemv_allreduce_rmsnorm.argtypes
         L.gsa_gemv_allreduce_rmsnorm_noalloc.restype = ci
+        L.gsa_bias_rmsnorm.argtypes = [vp, i64, ci, ctypes.POINTER(gsa_epilogue), vp]
+        L.gsa_bias_rmsnorm.restype = ci
         L.gsa_peer_publish.argtypes = [vp, vp, vp, ci, ci, i64, ci, u32, u32, vp]
         L.gsa_peer_publish.restype = ci
         L.gsa_signal_pad_status.argtypes = [vp, vp, ctypes.POINTER(ci),
@@ -268,6 +270,14 @@ def gsa_gemv_allreduce_rmsnorm_noalloc(A_r, x, slots, pad, out, W, rank, N, K, B
                                                     None if ep is None else ctypes.byref(ep),
                                                     _stream(stream)),
            "gsa_gemv_allreduce_rmsnorm_noalloc")
+
+
+def gsa_bias_rmsnorm(out, N, B, ep, stream=None):
+    """The epilogue of gsa_gemv_allreduce_rmsnorm as a kernel of its own,
+    over an out (N x B float32) already written; ep: a gsa_epilogue."""
+    _check(lib().gsa_bias_rmsnorm(_ptr(out), N, B, ctypes.byref(ep) if ep is not None else None,
+                                  _stream(stream)),
+           "gsa_bias_rmsnorm")
 
 
 def gsa_signal_pad_status(pad, stream=None):

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libgsa.so")
-SOURCES = ["gsa_api.hip", "gemv_allreduce.hip", "moe_a2a.hip"]
+SOURCES = ["gsa_api.hip", "gemv_allreduce.hip", "moe_a2a.hip", "bias_rmsnorm.hip"]
 # The benchmark's achievable-bandwidth reference (include/gsa_probe.h).
 PROBE_LIBRARY = os.path.join(PKG, "libgsa_probe.so")
 PROBE_SOURCES = ["hbm_read_probe.hip"]

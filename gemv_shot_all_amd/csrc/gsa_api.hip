@@ -405,6 +405,24 @@ int gsa_gemv_allreduce_rmsnorm(const uint16_t* A_r, const uint16_t* x, float* sl
                       ep, stream);
 }
 
+int gsa_bias_rmsnorm(const float* out, int64_t N, int B, const gsa_epilogue* ep, void* stream) {
+  if (!out || !ep || !ep->y || N < 1 || N > ((int64_t)1 << 24) || B < 1 || B > GSA_MAX_B)
+    return GSA_EINVAL;
+  if (ep->y_dtype != GSA_DTYPE_F32 && ep->y_dtype != GSA_DTYPE_BF16) return GSA_EINVAL;
+  if (!aligned(out, 4) || !aligned(ep->y, ep->y_dtype == GSA_DTYPE_F32 ? 4 : 2)) return GSA_EINVAL;
+  if ((ep->bias && !aligned(ep->bias, 4)) || (ep->rms_weight && !aligned(ep->rms_weight, 4)) ||
+      (ep->inv_rms && !aligned(ep->inv_rms, 4)))
+    return GSA_EINVAL;
+  if (!std::isfinite(ep->eps) || ep->eps < 0.0f) return GSA_EINVAL;
+  if (gsa::launch_bias_rmsnorm(out, N, B, ep->bias, ep->rms_weight, ep->eps, ep->y,
+                               ep->y_dtype == GSA_DTYPE_BF16, ep->inv_rms,
+                               static_cast<hipStream_t>(stream)) != hipSuccess) {
+    (void)hipGetLastError();
+    return GSA_EHIP;
+  }
+  return GSA_OK;
+}
+
 int gsa_peer_publish(void* slots, uint32_t* pad, const void* values, int W, int peer, int64_t N,
                      int B, uint32_t epoch, uint32_t delay_us, void* stream) {
   if (!slots || !pad || !values || W < 1 || W > GSA_MAX_W || peer < 0 || peer >= W || N < 1 ||

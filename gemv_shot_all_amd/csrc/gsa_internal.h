@@ -93,6 +93,12 @@ struct Launch {
 // Pick the kernel for W ranks, batch B (1..16) and C chunks per row (with
 // the epilogue's extra LDS if epi).  Returns false if the shape exceeds the
 // LDS staging bound.
+// The fused epilogue's bias + RMSNorm as a kernel of its own, over an out
+// already written (B workgroups).
+hipError_t launch_bias_rmsnorm(const float* out, int64_t N, int B, const float* bias,
+                               const float* w, float eps, void* y, bool y_bf16, float* inv_rms,
+                               hipStream_t s);
+
 bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, bool slot_bf16,
                         bool out_bf16, Launch* out);
 // Dynamic LDS bytes a kernel of tile_rows rows per workgroup needs for (W, B, C, epi).

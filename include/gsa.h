@@ -238,6 +238,21 @@ int gsa_gemv_allreduce_rmsnorm(const uint16_t *A_r, const uint16_t *x, float *sl
                                uint32_t *pad, float *out, int W, int rank, int64_t N,
                                int64_t K, int B, const gsa_epilogue *ep, void *stream);
 
+/* The epilogue of gsa_gemv_allreduce_rmsnorm as a kernel of its own, over
+ * an `out` [device] (N x B fp32, n-major) already written, e.g. by a
+ * gsa_gemv_allreduce call earlier on the same stream: the unfused form of the
+ * talk's real-model example ("PyTorch Symmetric Memory: A New Programming
+ * Paradigm for Distributed AI"), where the reduction, a bias addition and an
+ * RMSNorm run in one kernel.  Same definition as there (bias, rms_weight,
+ * eps, y, inv_rms of `ep` [host, read before return]); one kernel of B
+ * workgroups, no host sync, no allocation.  inv_rms is the fold of the
+ * squares in one fixed order (its bits may differ from the fused call's, which
+ * sums in another order); y is computed from it exactly as there.
+ * Errors: GSA_EINVAL (out, ep or y NULL, N < 1, N > 2^24, B outside
+ * 1..GSA_MAX_B, unknown y_dtype, misaligned pointer, eps negative or not
+ * finite), GSA_EHIP. */
+int gsa_bias_rmsnorm(const float *out, int64_t N, int B, const gsa_epilogue *ep, void *stream);
+
 /* One-GPU stand-in for a peer's zero-copy push, for tests of the signal-pad
  * protocol.  The fused-operators page has each rank write its finished
  * results straight into the peers' memory and signal them; the

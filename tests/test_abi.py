@@ -117,6 +117,26 @@ def test_rmsnorm_entry_point_rejects_bad_arguments():
     assert L.gsa_gemv_allreduce_rmsnorm(*big, ep(), None) == gsa.GSA_EINVAL
 
 
+def test_unfused_rmsnorm_rejects_bad_arguments():
+    """gsa_bias_rmsnorm validates every argument before any HIP call."""
+    L = _lib.lib()
+
+    def ep(**kw):
+        e = _lib.gsa_epilogue(None, None, 1e-5, gsa.GSA_DTYPE_F32, P, None)
+        for k, v in kw.items():
+            setattr(e, k, v)
+        return ctypes.byref(e)
+
+    assert L.gsa_bias_rmsnorm(P, 16, 1, None, None) == gsa.GSA_EINVAL  # no epilogue
+    assert L.gsa_bias_rmsnorm(None, 16, 1, ep(), None) == gsa.GSA_EINVAL
+    for N, B in [(0, 1), (-1, 1), ((1 << 24) + 1, 1), (16, 0), (16, gsa.GSA_MAX_B + 1)]:
+        assert L.gsa_bias_rmsnorm(P, N, B, ep(), None) == gsa.GSA_EINVAL, (N, B)
+    assert L.gsa_bias_rmsnorm(P + 2, 16, 1, ep(), None) == gsa.GSA_EINVAL  # misaligned out
+    for bad in [dict(y=None), dict(y_dtype=2), dict(eps=-1.0), dict(eps=float("nan")),
+                dict(y=P + 2), dict(bias=P + 2), dict(rms_weight=P + 1), dict(inv_rms=P + 3)]:
+        assert L.gsa_bias_rmsnorm(P, 16, 1, ep(**bad), None) == gsa.GSA_EINVAL, bad
+
+
 def test_two_shot_entry_point_rejects_bad_arguments():
     L = _lib.lib()
     A, x, slots, pad, out = P, P, P, P, P

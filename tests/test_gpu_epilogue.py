@@ -252,3 +252,84 @@ def test_plain_and_epilogue_calls_share_a_buffer(Ks):
             assert np.array_equal(flags, expect), f"{kind} {i}: flag state"
     finally:
         er.close()
+
+
+def unfused_inv_rel_bound(N):
+    """The same bound for gsa_bias_rmsnorm, whose sum runs ceil(N / 1024)
+    sequential adds per thread, a 6-level lane butterfly and the 16 waves in
+    order."""
+    d = math.ceil(N / 1024) + 6 + 16
+    return ((d + 3) / 2 + 3) * U
+
+
+UNFUSED = [
+    # (N, B, bias, weight, eps, y dtype)
+    (4096, 1, True, True, 1e-5, torch.bfloat16),    # the o_proj shape
+    (8192, 4, True, True, 1e-5, torch.float32),     # the 70B-class shape
+    (8192, 16, True, True, 1e-5, torch.bfloat16),   # the skinny GEMM
+    (1, 1, True, True, 1e-5, torch.float32),        # one row
+    (1025, 3, False, True, 0.0, torch.float32),     # past one batch of rows, no bias, eps = 0
+    (9000, 7, True, False, 1e-3, torch.float32),    # two batches, ragged, no weight
+    (70000, 2, True, True, 1e-5, torch.bfloat16),   # many batches
+]
+
+
+@pytest.mark.parametrize("N,B,bias,weight,eps,y_dtype", UNFUSED)
+def test_unfused_bias_rmsnorm(N, B, bias, weight, eps, y_dtype):
+    """gsa_bias_rmsnorm on a seeded out: inv_rms within its bound of the fp64
+    value, y bit-identical to (z * inv) * w given the kernel's inv_rms, and
+    every call bit-identical."""
+    _say(f"[epilogue] unfused N={N} B={B} bias={bias} weight={weight} eps={eps} y={y_dtype}")
+    rng = np.random.default_rng(N * 31 + B)
+    out = rng.normal(0, 1, (N, B)).astype(np.float32)
+    b = rng.normal(0, 0.5, N).astype(np.float32) if bias else None
+    w = rng.normal(1, 0.1, N).astype(np.float32) if weight else None
+    out_t = torch.from_numpy(out).cuda()
+    b_t = None if b is None else torch.from_numpy(b).cuda()
+    w_t = None if w is None else torch.from_numpy(w).cuda()
+    ys, invs = [], []
+    for _ in range(2):
+        y = torch.full((N, B), float("nan"), dtype=y_dtype, device="cuda")
+        inv = torch.full((B,), float("nan"), dtype=torch.float32, device="cuda")
+        gsa.gsa_bias_rmsnorm(out_t, N, B, gsa.make_epilogue(y, b_t, w_t, eps, inv))
+        torch.cuda.synchronize()
+        yc = y.cpu()
+        ys.append(yc.view(torch.int16).numpy().view(np.uint16) if y_dtype == torch.bfloat16
+                  else yc.numpy())
+        invs.append(inv.cpu().numpy())
+    assert np.array_equal(ys[0].view(np.uint8), ys[1].view(np.uint8))
+    assert np.array_equal(invs[0].view(np.uint32), invs[1].view(np.uint32))
+    o = oracle.load()
+    z, inv64, y64 = o.bias_rmsnorm(out, b, w, eps)
+    rel = unfused_inv_rel_bound(N)
+    err = np.abs(invs[0].astype(np.float64) - inv64) / inv64
+    assert np.all(err <= rel), f"inv_rms rel err {err.max():.3g} > {rel:.3g}"
+    y32, ybf = o.scale_f32(z, invs[0], w)
+    if y_dtype == torch.bfloat16:
+        assert np.array_equal(ys[0], ybf)
+    else:
+        assert np.array_equal(ys[0].view(np.uint32), y32.view(np.uint32))
+
+
+def test_plain_call_then_unfused_matches_fused_definition():
+    """The unfused form of the epilogue on the o_proj shape: a plain call,
+    then gsa_bias_rmsnorm on its out (same stream); out meets the usual bar
+    and y the epilogue's."""
+    d = gi.make_inputs("c2", seed=0, rank=0)
+    er = EpiRun(d, y_dtype=torch.bfloat16)
+    try:
+        r = er.r
+        gsa.gsa_gemv_allreduce(r.A, r.x, r.buf.slots, r.buf.pad, r.out, r.W, er.rank, r.N, r.K,
+                               r.B)
+        gsa.gsa_bias_rmsnorm(r.out, r.N, r.B, er.ep)
+        out, sl, y, inv, status, hdr = er.results()
+    finally:
+        er.close()
+    assert status == (gsa.GSA_OK, -1, -1)
+    check_against_oracle(d["A"], d["x"], er.slots_in, er.rank, out, sl, "c2 plain")
+    o = oracle.load()
+    z, inv64, y64 = o.bias_rmsnorm(out, er.bias, er.w, er.eps)
+    rel = unfused_inv_rel_bound(out.shape[0])
+    assert np.all(np.abs(inv.astype(np.float64) - inv64) / inv64 <= rel)
+    y32, ybf = o.scale_f32(z, inv, er.w)
+    assert np.array_equal(y, ybf)
