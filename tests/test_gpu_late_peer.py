@@ -61,7 +61,7 @@ CASES = [
     (1024, 8, gsa.GSA_DTYPE_F32),    # 16-row middle tier, peer tile through LDS
     (3584, 4, gsa.GSA_DTYPE_F32),    # 32-row long tier
     (512, 16, gsa.GSA_DTYPE_F32),    # MFMA
-    (2048, 16, gsa.GSA_DTYPE_F32),   # MFMA, x in registers (rows of 256 chunks)
+    (2048, 16, gsa.GSA_DTYPE_F32),   # MFMA, A staged through LDS (rows of 256 chunks)
     (2048, 11, gsa.GSA_DTYPE_BF16),  # the same, bf16 slots
     (3584, 4, gsa.GSA_DTYPE_BF16),   # long tier, bf16 slots
     (128, 1, gsa.GSA_DTYPE_BF16),    # 4-row tiles, bf16 slots

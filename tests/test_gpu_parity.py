@@ -37,7 +37,7 @@ EDGE = [
     (2, 48, 16384, 1, 0),     # multi-pass long rows
     (2, 32, 8192, 8, 1),      # x at the LDS bound (128 KB)
     (2, 33, 5000, 5, 0),      # masked multi-pass, B = 5
-    (4, 50, 2048, 9, 3),      # MFMA path, x in registers, B = 9, ragged N
+    (4, 50, 2048, 9, 3),      # MFMA path, A staged through LDS, B = 9, ragged N
     (8, 4099, 2048, 16, 7),   # the same, W = 8, last rank, 129 workgroups, the last of 3 rows
     (1, 31, 2048, 13, 0),     # the same, W = 1, one partial workgroup
     (2, 33, 2048, 16, 1),     # the same, a second workgroup of one row

@@ -252,7 +252,7 @@ def test_timeout_reports_missing_peer_and_skips_out():
     (3200, 5, 3),    # long rows: 32-row workgroups; flag tile 5 is the sixth of its workgroup
     (3200, 13, 3),   # long rows: a flag tile of the second (ragged) 32-row workgroup
     (128, 19, 3),    # the last flag tile
-    (2048, 5, 16),   # MFMA, x in registers: 32-row workgroups
+    (2048, 5, 16),   # MFMA, A staged through LDS: 32-row workgroups
     (2048, 13, 12),  # the same, a flag tile of the second (ragged) workgroup
 ])
 def test_timeout_single_tile(Ks, t_bad, B):
