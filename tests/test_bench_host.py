@@ -27,6 +27,13 @@ def test_alg_bytes_bf16_slots_and_out_by_hand():
             == 2 * 4096)
 
 
+def test_alg_bytes_unfused_epilogue_by_hand():
+    # the epilogue as a second kernel reads out back: 4 N B more than fused
+    assert (bench.alg_bytes(8, 4096, 4096, 1, epilogue=True, unfused=True) -
+            bench.alg_bytes(8, 4096, 4096, 1, epilogue=True)) == 4 * 4096
+    assert bench.profile_name("c2", epilogue=True, unfused=True) == "gemv_allreduce_rmsnorm_unfused_c2"
+
+
 def test_alg_bytes_two_shot_by_hand():
     # rank 0 of 8 owns 512 rows: 7 peers x 512 rows, its 512 published rows,
     # 3584 copied rows
