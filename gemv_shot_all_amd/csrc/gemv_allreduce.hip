@@ -1656,7 +1656,13 @@ __global__ __launch_bounds__(256) void peer_publish_kernel(float* slots, uint32_
 // publishes them (the long-row kernel's scheme).  Measured on the skinny
 // GEMM (cold, per call): without the protocol 7.9 us against 9.6 for the
 // same MFMAs with every lane loading its own A operands and all of x in
-// registers; with it 9.0 against 10.4.
+// registers; with it 9.0 against 10.4.  Each workgroup starts its walk over
+// the 8 stages at a stage of its own ((t ^ (t >> 3)) mod 8 for tile t): 8.7
+// against 9.05 us with every workgroup in the same order.  Not taken
+// (same box, us per call): 5-7 stages in flight 9.3-9.6; a stage of 512
+// contiguous bytes of each row 10.2-10.4; a stage of 16 whole 1 KB row
+// pieces 10.1 (9.2 with the rotation); a workgroup's 4-row groups spread
+// over the matrix instead of contiguous, no gain.
 constexpr int kMfmaLCons = 4;     // consumer waves (MFMA)
 constexpr int kMfmaLProd = 2;     // producer waves (A into LDS)
 constexpr int kMfmaLRows = 32;
@@ -1676,6 +1682,17 @@ __device__ __forceinline__ void wait_vm_le_n(int n) {
     else
       wait_vm_le_n<K - 1>(n);
   }
+}
+
+// The stage a workgroup of tile t starts its walk at: position j holds stage
+// (j + rot) mod NS of the row, so that neighbouring workgroups, on one XCD
+// (t >> 3) and across XCDs (t & 7), do not request the same offsets of their
+// rows at once.  (Computed where it is used: kept in a register from the
+// kernel's start, the same value measured 0.4 us slower per call, from a
+// different schedule of the x loads.)
+template <int NS>
+__device__ __forceinline__ int lds_stage_rot(int64_t t) {
+  return (int)((t ^ (t >> 3)) & (NS - 1));
 }
 
 template <int DT>
@@ -1710,11 +1727,12 @@ __global__ __launch_bounds__((kMfmaLCons + kMfmaLProd) * 64) void gemv_ar_mfma_l
     // l / 8, chunk (l % 8) ^ (l / 8) of it (rows past N repeat row N - 1).
     const int p = wave - kMfmaLCons;
     auto issue = [&](int j, int buf) {
+      const int st = (j + lds_stage_rot<NS>(tile)) & (NS - 1);
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
         const int b = 2 * i + p;
         const int64_t r = min(row0 + (b & 3) * 8 + (lane >> 3), a.N - 1);
-        const int chunk = 64 * (b >> 2) + 8 * j + ((lane & 7) ^ (lane >> 3));
+        const int chunk = 64 * (b >> 2) + 8 * st + ((lane & 7) ^ (lane >> 3));
         lds_dma16<2>(a.A + (r * C + chunk) * 8, lds_a + buf * kMfmaLStageBytes + b * 1024);
       }
     };
@@ -1745,8 +1763,9 @@ __global__ __launch_bounds__((kMfmaLCons + kMfmaLProd) * 64) void gemv_ar_mfma_l
 
   // x: batch l16 (zeros past B), chunk 64 wave + 4 s + kq of MFMA step s.
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(a.B * C * 16));
-  auto x_off = [&](int s2) {
-    return l16 < a.B ? ((uint32_t)l16 * (uint32_t)C + 64u * wave + 4u * s2 + kq) * 16u
+  auto x_off = [&](int j2) {  // MFMA step j2 = 2 j + m of position j: step s of the row
+    const int s = 2 * (((j2 >> 1) + lds_stage_rot<NS>(tile)) & (NS - 1)) + (j2 & 1);
+    return l16 < a.B ? ((uint32_t)l16 * (uint32_t)C + 64u * wave + 4u * s + kq) * 16u
                      : kOutOfRange;
   };
   uint4 xv[2 * NS];
