@@ -141,7 +141,8 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 //                  a dtype branch has its zero-extension inside the branch,
 //                  which waits for that load before the next one issues;
 //   store_slot:    the device-coherent store of a published value;
-//   store_out:     out[i], rounded to bf16 for a bf16 out.
+//   store_out:     out[i], rounded to bf16 for a bf16 out (store_out_wt:
+//                  the same, written through).
 __device__ __forceinline__ float bf16_widen(uint16_t bits) {
   return __uint_as_float((uint32_t)bits << 16);
 }
@@ -172,6 +173,19 @@ __device__ __forceinline__ void store_out(const GemvArgs& a, int64_t i, float o)
     reinterpret_cast<uint16_t*>(a.out)[i] = bf16_rne(o);
   else
     a.out[i] = o;
+}
+// out[i] written through to the coherence point like a published value,
+// instead of left in L2 for the kernel's closing write-back; used by the
+// publish path of the VALU and 16-row MFMA kernels (the small, o_proj and 8B
+// down_proj shapes, fp32 or bf16 out: 0.05-0.16 us per call faster).  The
+// long-row kernel measured no change with it and the LDS-staged MFMA kernel
+// 0.45 us slower, so both keep store_out.
+__device__ __forceinline__ void store_out_wt(const GemvArgs& a, int64_t i, float o) {
+  if (a.out_bf16)
+    __hip_atomic_store(reinterpret_cast<uint16_t*>(a.out) + i, bf16_rne(o), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  else
+    store_coherent(a.out + i, o);
 }
 
 // Element types of a kernel instance: fp32 slots and out, bf16 slots and
@@ -570,7 +584,7 @@ __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t ti
       if (a.epi)
         store_coherent(&a.out[i], o[0]);  // read back by the workgroup that finishes last
       else
-        store_out(a, i, o[0]);
+        store_out_wt(a, i, o[0]);
     }
     wait_vm_le<1>();  // the published value is at the coherence point ...
   } else {
@@ -601,7 +615,7 @@ __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t ti
       if (a.epi)
         store_coherent(&a.out[i], o[e]);  // read back by the workgroup that finishes last
       else
-        store_out(a, i, o[e]);
+        store_out_wt(a, i, o[e]);
     }
   }
   if (TS && owner == a.rank) {
