@@ -483,8 +483,7 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
     }
     __syncthreads();  // E1
     __syncthreads();  // E1b
-    __syncthreads();  // E2
-    if (s_ctl[3] || s_ctl[2]) {
+    if (s_ctl[3] || tile == a.tiles - 1) {  // a waiting tile, or the reducing workgroup
       __syncthreads();  // E3
       __syncthreads();  // E4
     }
@@ -663,19 +662,6 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// Sum of v over the 8 lanes whose index agrees with this lane's mod 8, in
-// every one of them: row_ror:8 within each 16-lane row, then the two
-// permlane swaps of group_sum (a fixed tree, bit-identical in the 8 lanes).
-__device__ __forceinline__ float sum_mod8(float v) {
-  v = v + dpp_f32<0x128>(v);  // row_ror:8
-  unsigned u = __builtin_bit_cast(unsigned, v);
-  auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  v = __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
-  u = __builtin_bit_cast(unsigned, v);
-  p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
-}
-
 // The value that lane l ^ D holds (D = 8, 4, 2 or 1; partners stay within a
 // 16-lane row).  D = 8 and 4 take two DPP row shifts, each writing only the
 // 4-lane banks whose partner lies in its direction; D = 2 and 1 one quad
@@ -764,54 +750,126 @@ __device__ __forceinline__ float reduce_scatter64(float (&v)[V], int lane) {
   return v[0];
 }
 
-// 1 / rms per column from every tile's published partials, computed by the
-// compute waves of the last tile in a fixed order.  A record's 16 partial
-// words are read by 8 consecutive lanes, 8 bytes each (coherent 64-bit
-// loads; a wave reads 8 records per load, whole lines, not one request per
-// value): lane l of thread group j = (wave * 64 + l) / 8 holds columns
-// 2 (l % 8) and 2 (l % 8) + 1 and takes tiles j, j + nt / 8, ... in
-// ascending order, 8 tiles' loads ahead of their additions.  The lanes of a
-// wave with the same l % 8 are then summed by a fixed butterfly (xor 8, 16,
-// 32: sum_mod8) and the waves' sums are added in wave order.  Result in s_inv[0..B).
-// Contains the barrier E3.  BM >= B bounds the columns it sums.
-template <int BM>
-__device__ void fold_inv_rms(const GemvArgs& a, int wave, int lane, int nt, float* wsum,
-                             float* s_inv) {
-  constexpr int kLoads = 8;  // tiles per thread group in flight
-  const int sub = lane & 7;  // columns 2 sub, 2 sub + 1
-  const int groups = nt / 8;
-  float acc0 = 0.0f, acc1 = 0.0f;
-  if (2 * sub < BM) {
-    for (int t0 = (wave * 64 + lane) >> 3; t0 < a.tiles; t0 += kLoads * groups) {
+// The call's mark in the epilogue's scratch: 1 + k mod (2^31 - 1) for call
+// index k, never 0 (cleared scratch reads 0) and below 2^31, so that the top
+// bit of a record's tag can say that the tile left its rows to the reducing
+// workgroup (kEpiLeft).
+constexpr uint32_t kEpiLeft = 0x80000000u;
+__device__ __forceinline__ uint32_t epi_mark(unsigned long long k) {
+  return (uint32_t)(k % 0x7FFFFFFFull) + 1u;
+}
+__device__ __forceinline__ unsigned long long* epi_record(const GemvArgs& a, int64_t t) {
+  return reinterpret_cast<unsigned long long*>(a.ssq + t * kEpiRecordWords);
+}
+
+// Sum of v over the lanes of the wave whose index agrees with this lane's
+// modulo 2^lp (0 <= lp <= 5, wave-uniform, every lane active): a fixed
+// butterfly at lane distances 2^lp, ..., 32 (DPP within 16-lane rows, then
+// the two permlane swaps); every lane of a class ends with the same bits.
+__device__ __forceinline__ float sum_lane_class(float v, int lp) {
+  if (lp <= 0) v = v + partner_value<1>(v);
+  if (lp <= 1) v = v + partner_value<2>(v);
+  if (lp <= 2) v = v + partner_value<4>(v);
+  if (lp <= 3) v = v + partner_value<8>(v);
+  if (lp <= 4) {
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    v = __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
+  }
+  const unsigned u = __builtin_bit_cast(unsigned, v);
+  const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (unsigned)p[0]) + __builtin_bit_cast(float, (unsigned)p[1]);
+}
+
+// 1 / rms per column, folded by the reducing workgroup from every tile's
+// record as the records arrive.  Record t holds B 64-bit words; word c is
+// (tag << 32) | the fp32 bits of tile t's sum of squares of column c, with
+// tag = the call's mark, plus kEpiLeft if the tile left its rows.  A word is
+// written and read whole, so it carries its own validity: no flag and no
+// wait stand between a tile's sums and the fold.  P = B rounded up to a
+// power of two lanes read one record (lane class c = lane mod P: column c);
+// thread group j = (wave * 64 + lane) / P takes tiles j, j + nt / P, ... in
+// ascending order, kLoads tiles' loads in flight, and re-reads the words that
+// do not show this call's mark yet, together, until all do (bounded: twice
+// the wait timeout).  The lanes of
+// a class are summed by a fixed butterfly (sum_lane_class) and the waves'
+// sums in wave order, so the result has the same bits on every call.
+// Result in s_inv[0..B), NaN in every column if the wait expired (then the
+// pad header records kErrEpiWait with this tile's first flag tile).
+// s_ctl[2] must be 0 on entry.  Contains the barrier E3.
+__device__ void fold_records(const GemvArgs& a, uint32_t mark, int64_t tile, int wave, int lane,
+                             int nt, float* wsum, float* s_inv, uint32_t* s_ctl) {
+  constexpr int kLoads = 16;
+  const int lp = a.B <= 1 ? 0 : 32 - __builtin_clz((unsigned)(a.B - 1));  // log2 P
+  const int c = lane & ((1 << lp) - 1);
+  const int groups = nt >> lp;
+  const uint64_t limit = 2 * a.timeout_ticks + 1000000ull;
+  const uint64_t start = wall_clock64();
+  float acc = 0.0f;
+  bool expired = false;
+  if (lp > 0 && lp <= 3) {
+    // 2 <= B <= 8: first the column-0 word of every record this wave reads
+    // below, the P lanes of a thread group sharing its tiles.  A record's
+    // words are stored by one instruction, so once these show the mark the
+    // reads below rarely find a word without it, each of which would cost a
+    // round trip of its own there (8B down_proj shape, B = 8: 11.1 against
+    // 12.2 us per call; at B = 16, 32 words a lane, it measured slower).
+    const int j = (wave * 64 + lane) >> lp;
+    for (int t = j + c * groups; t < a.tiles && !expired; t += groups << lp) {
+      unsigned long long v =
+          __hip_atomic_load(epi_record(a, t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      while (((uint32_t)(v >> 32) & ~kEpiLeft) != mark) {
+        if (wall_clock64() - start > limit) {
+          expired = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        v = __hip_atomic_load(epi_record(a, t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+  if (c < a.B) {
+    for (int t0 = (wave * 64 + lane) >> lp; t0 < a.tiles; t0 += kLoads * groups) {
       unsigned long long w[kLoads];
 #pragma unroll
       for (int u = 0; u < kLoads; ++u) {
         const int t = min(t0 + u * groups, a.tiles - 1);
-        w[u] = __hip_atomic_load(
-            reinterpret_cast<const unsigned long long*>(a.ssq + (int64_t)t * kEpiRecordWords) +
-                sub,
-            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        w[u] = __hip_atomic_load(epi_record(a, t) + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
 #pragma unroll
       for (int u = 0; u < kLoads; ++u) {
-        if (t0 + u * groups < a.tiles) {
-          acc0 = acc0 + __uint_as_float((uint32_t)w[u]);
-          acc1 = acc1 + __uint_as_float((uint32_t)(w[u] >> 32));
+        const int t = t0 + u * groups;
+        if (t < a.tiles) {
+          unsigned long long v = w[u];
+          while (((uint32_t)(v >> 32) & ~kEpiLeft) != mark && !expired) {
+            if (wall_clock64() - start > limit) {
+              expired = true;
+            } else {
+              __builtin_amdgcn_s_sleep(1);
+              v = __hip_atomic_load(epi_record(a, t) + c, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+          acc = acc + (expired ? __builtin_nanf("") : __uint_as_float((uint32_t)v));
         }
       }
     }
   }
-  acc0 = sum_mod8(acc0);
-  acc1 = sum_mod8(acc1);
-  if (lane < 8) {
-    wsum[wave * 16 + 2 * lane] = acc0;
-    wsum[wave * 16 + 2 * lane + 1] = acc1;
-  }
+  acc = sum_lane_class(acc, lp);
+  if (lane < (1 << lp)) wsum[wave * 16 + lane] = acc;
+  if (__ballot(expired) != 0 && lane == 0) s_ctl[2] = 1u;
   __syncthreads();  // E3: every wave's sums in LDS
-  if (wave == 0 && lane < a.B) {
-    float tot = 0.0f;
-    for (int w = 0; w < nt / 64; ++w) tot = tot + wsum[w * 16 + lane];
-    s_inv[lane] = 1.0f / sqrtf(tot / (float)a.N + a.eps);
+  if (wave == 0) {
+    const bool failed = s_ctl[2] != 0;
+    if (failed && lane == 0) {
+      atomicOr(a.pad + kHdrErrorBits, kErrEpiWait);
+      atomicMin(a.pad + kHdrEpiWaitTile, (uint32_t)(tile * (kBigTile / kFlagRows)));
+    }
+    if (lane < a.B) {
+      float tot = 0.0f;
+      for (int w = 0; w < nt / 64; ++w) tot = tot + wsum[w * 16 + lane];
+      s_inv[lane] = failed ? __builtin_nanf("") : 1.0f / sqrtf(tot / (float)a.N + a.eps);
+    }
   }
 }
 
@@ -830,28 +888,37 @@ __device__ __forceinline__ void store_y(const GemvArgs& a, int64_t i, float v) {
 //   z = out + bias[n]; inv[b] = 1 / sqrtf(sum_n z^2 / N + eps);
 //   y = (z * inv[b]) * w[n]
 // The sum over n crosses workgroups.  Each tile sums its 16 squares per
-// column in row order and publishes the partials (coherent stores) in its
-// record, then adds one to its group's done count; the tile that completes
-// its group adds one to the count of completed groups, and the tile that
-// completes that count is the last.  Every count (and the started counts
-// taken at entry) only grows, so call k is complete when a count reaches
-// (k + 1) times its number of members.  The last tile folds every partial
-// (fold_inv_rms), then publishes inv in kEpiGroups copies, one per group, as
-// one 64-bit word per column holding k + 1 and the bits of inv (a word is
-// written and read whole, so it needs no separate flag).
+// column in row order and publishes them as its record (fold_records: one
+// self-validating 64-bit word per column, tagged with the call's mark).  The
+// reducing workgroup, the last tile's (dispatched last, so most records are
+// out when it starts reading them), folds every record as it arrives and
+// publishes inv in kEpiGroups copies, one per group of tiles (t %
+// kEpiGroups), as one 64-bit word per column holding the mark and the bits
+// of inv.  No count stands between a record and the fold: against the
+// earlier scheme (each tile counting itself done in its group, the tile that
+// completed the count of groups folding), one wait for the records'
+// acknowledgement and two atomic round trips fewer (us per call: c1 8.6 ->
+// 7.5, o_proj 8.6 -> 7.8, 8B down_proj B = 1 9.9 -> 9.1, B = 4 10.2 -> 9.9;
+// B = 8, the 70B-class shape and the skinny GEMM within their run-to-run
+// spread).  The call index k comes from the started
+// counts, which only grow (taken by the communication wave at entry), so no
+// host state is needed (graph replays work).
 //  - A tile that saw every tile of its call started (s_ctl[3], looked up by
 //    the communication wave) may wait: every other tile is resident or done
-//    and finishes on its own.  It marks its record with k + 1, polls
-//    (bounded) its group's copy until every column shows k + 1, takes inv
-//    from it and normalises its own rows from registers.
-//  - Any other tile marks 0 and leaves; the last tile also normalises the
-//    rows of every tile not marked k + 1, re-reading out (stored coherently
-//    for this).
-// A row that failed (its flag tile's wait expired, or a bad own row)
-// contributes NaN, so y comes out NaN for that call.  Barriers: E1 (squares
-// in LDS), E1b (out stores and the record completed), E2 (count taken), then,
-// in the last tile and in waiting tiles, E3 (wave sums in LDS, or inv seen)
-// and E4 (inv in LDS).
+//    and finishes on its own.  It polls (bounded) its group's copy until
+//    every column shows the mark, takes inv from it and normalises its own
+//    rows from registers.
+//  - Any other tile first waits until its out stores are at the coherence
+//    point, tags its record kEpiLeft and leaves; the reducing workgroup, once
+//    it has inv, also normalises the rows of every tile tagged so, re-reading
+//    out (stored coherently for this).
+// The reducing workgroup waits whatever it saw at its start: it holds one
+// workgroup's place, and every tile it waits for has started or will start
+// in a place that tiles leaving free up.  A row that failed (its flag tile's
+// wait expired, or a bad own row) contributes NaN, so y comes out NaN for
+// that call.  Barriers: E1 (squares in LDS), E1b (out stores complete in a
+// tile that leaves), then, in the reducing and the waiting tiles, E3 (wave
+// sums in LDS, or inv seen) and E4 (inv in LDS).
 template <int BM, int OPL>
 __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
                                const bool (&own)[OPL], const bool (&live)[OPL],
@@ -876,54 +943,29 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
     }
   }
   __syncthreads();  // E1: the squares are in LDS
-  const unsigned long long k = *s_epi_k;
-  const uint32_t mark = (uint32_t)(k + 1ull);
+  const uint32_t mark = epi_mark(*s_epi_k);
   const bool waits = s_ctl[3] != 0;
-  const int grp = (int)(tile % kEpiGroups);
-  float* rec = a.ssq + tile * kEpiRecordWords;
+  const bool reducer = tile == a.tiles - 1;
   // This tile's group copy of the published inv: per column one 64-bit word
   // (mark in the high half, the fp32 bits of inv in the low half).
   const unsigned long long* inv_copy = reinterpret_cast<const unsigned long long*>(
-      a.ssq + epi_inv_off(a.tiles) + (int64_t)grp * kEpiRecordWords);
-  if (wave == 0) {
-    if (lane < a.B) {
-      float part = 0.0f;
-      for (int r = 0; r < kBigTile; ++r) part = part + zz[r * 16 + lane];
-      store_coherent(&rec[lane], part);
-    }
-    if (lane == 16)
-      __hip_atomic_store(reinterpret_cast<uint32_t*>(rec + 16), waits ? mark : 0u,
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  // One wait covers each wave's out stores and wave 0's record: both are at
-  // the coherence point in every compute wave before the count.
-  wait_vm_all();
+      a.ssq + epi_inv_off(a.tiles) + (int64_t)(tile % kEpiGroups) * kEpiRecordWords);
+  // A tile that leaves its rows to the reducing workgroup has its out at the
+  // coherence point in every compute wave before its record goes out.
+  if (!waits) wait_vm_all();
+  if (reducer && wave == 0 && lane == 0) s_ctl[2] = 0u;
   __syncthreads();  // E1b
-  if (wave == 0) {
-    if (lane == 0) {
-      uint32_t last = 0;
-      const unsigned long long g_before =
-          __hip_atomic_fetch_add(epi_count(a, epi_done_off(a.tiles), grp), 1ull,
-                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (g_before + 1ull == (k + 1ull) * (unsigned)epi_group_tiles(a, grp)) {
-        // This tile completed its group (whose members all counted after
-        // their records were published): count the group.
-        const unsigned groups = (unsigned)min(a.tiles, kEpiGroups);
-        const unsigned long long t_before =
-            __hip_atomic_fetch_add(epi_count(a, epi_top_off(a.tiles), 0), 1ull,
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = t_before + 1ull == (k + 1ull) * groups ? 1u : 0u;
-      }
-      s_ctl[2] = last;
-    }
+  if (wave == 0 && lane < a.B) {
+    float part = 0.0f;
+    for (int r = 0; r < kBigTile; ++r) part = part + zz[r * 16 + lane];
+    const unsigned long long tag = mark | (waits ? 0u : kEpiLeft);
+    __hip_atomic_store(epi_record(a, tile) + lane, (tag << 32) | __float_as_uint(part),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  __syncthreads();  // E2
-  const bool last = s_ctl[2] != 0;
-  if (!last && !waits) return;
+  if (!reducer && !waits) return;
 
-  if (last) {
-    // Every tile has published: fold, then publish inv.
-    fold_inv_rms<BM>(a, wave, lane, nt, wsum, s_inv);  // contains E3
+  if (reducer) {
+    fold_records(a, mark, tile, wave, lane, nt, wsum, s_inv, s_ctl);  // contains E3
     if (wave == 0) {
       // Every group's copy, one self-validating 64-bit word per column (so no
       // wait has to separate the values from a flag): P = B rounded up to a
@@ -944,8 +986,9 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
   } else {
     if (wave == 0) {
       // Lane c < B polls column c's word until every column shows this call's
-      // mark; its low half is then inv.  Other tiles may still be in their
-      // bounded peer waits: allow twice that.
+      // mark; its low half is then inv.  The reducing workgroup may itself
+      // sit in its bounded peer wait and then in its bounded record wait:
+      // allow four times the timeout.
       const uint64_t start = wall_clock64();
       float inv = __builtin_nanf("");
       for (;;) {
@@ -956,7 +999,7 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
           inv = __uint_as_float((uint32_t)w);
           break;
         }
-        if (wall_clock64() - start > 2 * a.timeout_ticks + 1000000ull) {
+        if (wall_clock64() - start > 4 * a.timeout_ticks + 2000000ull) {
           if (lane == 0) {
             atomicOr(a.pad + kHdrErrorBits, kErrEpiWait);
             atomicMin(a.pad + kHdrEpiWaitTile, (uint32_t)(tile * (kBigTile / kFlagRows)));
@@ -970,32 +1013,29 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
     __syncthreads();  // E3: inv in LDS (NaN if the wait expired)
   }
   __syncthreads();  // E4: inv in LDS
-  if (waits) {
 #pragma unroll
-    for (int e = 0; e < OPL; ++e) {
-      if (live[e]) {
-        float v = z[e] * s_inv[b];
-        if (a.rms_w) v = v * a.rms_w[row0 + n[e]];
-        if (!ok[e]) v = __builtin_nanf("");
-        store_y(a, (row0 + n[e]) * a.B + b, v);
-      }
+  for (int e = 0; e < OPL; ++e) {
+    if (live[e]) {
+      float v = z[e] * s_inv[b];
+      if (a.rms_w) v = v * a.rms_w[row0 + n[e]];
+      if (!ok[e]) v = __builtin_nanf("");
+      store_y(a, (row0 + n[e]) * a.B + b, v);
     }
   }
-  if (!last) return;
+  if (!reducer) return;
 
-  // The last tile: the rows of every tile not marked k + 1 (in the common
-  // case, where every tile saw all tiles started, there are none).  Thread j
-  // takes tiles j, j + nt, ...; a tile's outputs go four at a time, all
-  // loads of a batch before its stores.  The loads of marks and outputs are
-  // issued only after the count this tile took showed every tile done (they
-  // sit behind a branch on that value).
+  // The reducing workgroup: the rows of every other tile tagged kEpiLeft in
+  // this call (in the common case, where every tile saw all tiles started,
+  // there are none).  Thread j takes tiles j, j + nt, ...; a tile's outputs
+  // go four at a time, all loads of a batch before its stores.  The tags and
+  // outputs are read only after the fold saw every record (E3, E4).
   constexpr int kBatch = 4;
   const int64_t NB = a.N * a.B;
   for (int t = wave * 64 + lane; t < a.tiles; t += nt) {
-    const uint32_t m = __hip_atomic_load(
-        reinterpret_cast<const uint32_t*>(a.ssq + (int64_t)t * kEpiRecordWords + 16),
-        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (m == mark) continue;
+    if (t == tile) continue;
+    const uint32_t tag = (uint32_t)(__hip_atomic_load(epi_record(a, t), __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT) >> 32);
+    if (tag != (mark | kEpiLeft)) continue;
     const int64_t lo = (int64_t)t * kBigTile * a.B;
     const int64_t hi = min(NB, lo + (int64_t)kBigTile * a.B);
     for (int64_t i0 = lo; i0 < hi; i0 += kBatch) {
@@ -1904,9 +1944,9 @@ __global__ __launch_bounds__((kMfmaLCons + kMfmaLProd) * 64) void gemv_ar_mfma_l
 }
 
 __global__ void pad_reset_kernel(uint32_t* pad, int W, int row_stride, uint32_t mask,
-                                 uint32_t* epi_tail, int64_t tail_words) {
+                                 uint32_t* epi, int64_t epi_words) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < tail_words) epi_tail[i] = 0u;  // the epilogue's flags and counts
+  if (i < epi_words) epi[i] = 0u;  // the epilogue's records, 1/rms copies and counts
   // Header, then 2W flag rows: rank r's slot flags (row r) and reduced-chunk
   // flags of the two-shot variant (row W + r).
   const int64_t total = GSA_PAD_HEADER_WORDS + 2 * (int64_t)W * row_stride;
@@ -2081,14 +2121,14 @@ hipError_t launch_clear_words(uint32_t* p, int64_t n, hipStream_t s) {
 
 hipError_t launch_pad_reset(uint32_t* pad, int W, int row_stride, int tiles,
                             uint32_t published_mask, float* epi_scratch, hipStream_t s) {
-  uint32_t* epi_tail = reinterpret_cast<uint32_t*>(epi_scratch + epi_inv_off(tiles));
-  const int64_t tail_words = epi_scratch_words(tiles) - epi_inv_off(tiles);
+  uint32_t* epi = reinterpret_cast<uint32_t*>(epi_scratch);
+  const int64_t epi_words = epi_scratch_words(tiles);
   const int64_t total =
-      std::max<int64_t>(GSA_PAD_HEADER_WORDS + 2 * (int64_t)W * row_stride, tail_words);
+      std::max<int64_t>(GSA_PAD_HEADER_WORDS + 2 * (int64_t)W * row_stride, epi_words);
   const unsigned block = 256;
   const unsigned grid = (unsigned)((total + block - 1) / block);
   hipLaunchKernelGGL(pad_reset_kernel, dim3(grid), dim3(block), 0, s, pad, W, row_stride,
-                     published_mask, epi_tail, tail_words);
+                     published_mask, epi, epi_words);
   return hipGetLastError();
 }
 

@@ -115,7 +115,7 @@ int ticks_for(uint32_t us, uint64_t* ticks) {
 
 // The entry point that allocates nothing (gsa_gemv_allreduce_rmsnorm_noalloc)
 // keeps the fused epilogue's scratch -- one record of partial sums per
-// 16-row tile, then the 1/rms copies and the completion counts -- in this
+// 16-row tile, then the 1/rms copies and the started counts -- in this
 // file-scope device array instead of the buffer's own scratch.  Each device
 // holds its own copy until the process ends.  Host code never uses the
 // array's name as an address: the address comes from hipGetSymbolAddress,
@@ -170,7 +170,8 @@ int gsa_symm_alloc_dtype(int W, int64_t N, int B, int slot_dtype, gsa_symm** out
   const size_t pad_words = GSA_PAD_HEADER_WORDS + 2 * (size_t)W * (size_t)stride;
   const size_t gathered_bytes = round_up((size_t)N * (size_t)B * sizeof(float), kAlign);
   const size_t pad_bytes = round_up(pad_words * sizeof(uint32_t), kAlign);
-  // The epilogue's scratch: one record per 16-row tile, then flags and counts.
+  // The epilogue's scratch: one record per 16-row tile, then the 1/rms copies and
+  // the started counts.
   const size_t ssq_bytes =
       round_up((size_t)gsa::epi_scratch_words(big_tiles_of(N)) * sizeof(float), kAlign);
   const size_t bytes = slot_bytes + pad_bytes + gathered_bytes + ssq_bytes;
@@ -355,14 +356,13 @@ int enqueue_call(const uint16_t* A_r, const uint16_t* x, void* slots_any, uint32
   if (rc != GSA_OK) return rc;
   hipError_t e = hipSuccess;
   if (epi_scratch) {
-    // The shared scratch's counts start at zero for every call (the
-    // buffer's own scratch counts calls instead); the records are written
-    // whole by every call.
+    // The shared scratch starts cleared for every call (the buffer's own
+    // scratch counts calls instead, so its records and 1/rms copies carry
+    // each call's mark): the counts, the records and the copies, so that no
+    // word a previous call left can pass for one of this call.
     a.ssq = epi_scratch;
-    const int64_t tiles = a.tiles;
-    e = gsa::launch_clear_words(reinterpret_cast<uint32_t*>(epi_scratch + gsa::epi_inv_off(tiles)),
-                                gsa::epi_scratch_words(tiles) - gsa::epi_inv_off(tiles),
-                                static_cast<hipStream_t>(stream));
+    e = gsa::launch_clear_words(reinterpret_cast<uint32_t*>(epi_scratch),
+                                gsa::epi_scratch_words(a.tiles), static_cast<hipStream_t>(stream));
   }
   if (e == hipSuccess) e = gsa::launch_gemv(l, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {

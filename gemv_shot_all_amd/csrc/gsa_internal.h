@@ -18,28 +18,22 @@ enum : int {
   kHdrSplitExpert = 7, // MoE: atomicMin of a local expert with a bad split table
 };
 // The epilogue's scratch (fp32 / uint32 words, 128-byte lines of 32 words):
-//   records   tiles lines: 16 partial sums of squares, the call mark at word 16
+//   records   tiles lines: 16 64-bit words, column c = (tag << 32) | bits of
+//             the tile's sum of squares (tag: the call's mark, top bit set if
+//             the tile left its rows to the reducing workgroup)
 //   inv       kEpiGroups lines: 16 64-bit words, column c = (mark << 32) | bits of 1/rms
 //   started   kEpiGroups lines: a 64-bit count at word 0
-//   done      kEpiGroups lines: a 64-bit count at word 0
-//   top       1 line: a 64-bit count of completed groups at word 0
-// Tile t belongs to group t % kEpiGroups; spreading the counts and the flag
-// over separate lines keeps the tiles' atomics and polls from queueing on one
-// address.  Everything after the records is cleared by the pad reset.
+// Tile t belongs to group t % kEpiGroups; spreading the counts and the 1/rms
+// copies over separate lines keeps the tiles' atomics and polls from queueing
+// on one address.  The pad reset clears all of it.
 constexpr int kEpiRecordWords = 32;
 constexpr int kEpiGroups = 64;
 __host__ __device__ constexpr int64_t epi_inv_off(int64_t tiles) { return tiles * kEpiRecordWords; }
 __host__ __device__ constexpr int64_t epi_started_off(int64_t tiles) {
   return epi_inv_off(tiles) + kEpiGroups * kEpiRecordWords;
 }
-__host__ __device__ constexpr int64_t epi_done_off(int64_t tiles) {
-  return epi_started_off(tiles) + kEpiGroups * kEpiRecordWords;
-}
-__host__ __device__ constexpr int64_t epi_top_off(int64_t tiles) {
-  return epi_done_off(tiles) + kEpiGroups * kEpiRecordWords;
-}
 __host__ __device__ constexpr int64_t epi_scratch_words(int64_t tiles) {
-  return epi_top_off(tiles) + kEpiRecordWords;
+  return epi_started_off(tiles) + kEpiGroups * kEpiRecordWords;
 }
 enum : uint32_t { kErrTimeout = 1u, kErrState = 2u, kErrEpiWait = 4u, kErrSplit = 8u };
 
@@ -75,7 +69,7 @@ struct GemvArgs {
   const float* rms_w;     // N fp32 or null
   void* y;                // N x B
   float* inv_rms;         // B fp32 or null
-  float* ssq;             // tiles x kEpiRecordWords: partial sums of squares + mark (scratch)
+  float* ssq;             // the epilogue's scratch (records, 1/rms copies, started counts)
 };
 
 // Rows per flag tile of the pad (GSA_FLAG_TILE_ROWS) and per workgroup of the

@@ -220,17 +220,19 @@ typedef struct gsa_epilogue {
 /* gsa_gemv_allreduce (same arguments, same contract, `out` written as
  * there), followed in the same kernel by the epilogue `ep` [host, read
  * before return].  The sum over n crosses tiles: each tile publishes its
- * partial sums of squares and counts itself done in the buffer's epilogue
- * scratch (counts that only grow, cleared by gsa_signal_pad_reset); 1/rms
- * is the fold of the partials in one fixed order, so repeated calls are
- * bit-identical.  A tile that finds every tile of the call started once its
- * own rows are done waits for 1/rms and normalises its own rows (started
- * tiles always finish, so that wait cannot deadlock); the rows of every
- * other tile are normalised by the tile that completes the count.  Both
- * give the same bits.  The tile-side wait is bounded (twice the timeout of
- * gsa_set_wait_timeout_us); if it expires, gsa_signal_pad_status reports
- * GSA_ETIMEOUT with that tile's first flag tile and peer -1.  If any tile
- * of the call failed, y and inv_rms are NaN.
+ * partial sums of squares in the buffer's epilogue scratch, each value
+ * tagged with the call's index (taken from counts that only grow, cleared
+ * with the scratch by gsa_signal_pad_reset); one workgroup folds them in
+ * one fixed order as they arrive, so repeated calls are bit-identical, and
+ * publishes 1/rms.  A tile that finds every tile of the call started once
+ * its own rows are done waits for 1/rms and normalises its own rows
+ * (started tiles always finish, so that wait cannot deadlock); the rows of
+ * every other tile are normalised by the folding workgroup.  Both give the
+ * same bits.  The waits are bounded (the fold's by twice, a tile's wait for
+ * 1/rms by four times the timeout of gsa_set_wait_timeout_us); if one
+ * expires, gsa_signal_pad_status reports GSA_ETIMEOUT with that tile's first
+ * flag tile and peer -1.  If any tile of the call failed, y and inv_rms are
+ * NaN.
  * Requires N <= 2^24 in addition.  Errors: GSA_EINVAL (also: ep or y NULL,
  * unknown y_dtype, misaligned pointer, eps negative or not finite),
  * GSA_EHIP. */
@@ -276,11 +278,12 @@ int gsa_peer_publish(void *slots, uint32_t *pad, const void *values, int W, int 
  * arguments, contract and results (bit for bit) as
  * gsa_gemv_allreduce_rmsnorm; the difference is the epilogue's scratch (the
  * partial sums of squares per 16-row tile, the published 1/rms and the
- * completion counts).  It lives in one file-scope device array of the
+ * started counts).  It lives in one file-scope device array of the
  * library, at most 2048 tiles' worth (N <= 32768; larger N: GSA_EINVAL),
- * 280 KiB, which every GPU the library runs on holds until the process
- * ends.  Every call first clears the array's counts with a small kernel (so
- * a call is two kernels on `stream`) and allocates nothing.  All calls on
+ * 272 KiB, which every GPU the library runs on holds until the process
+ * ends.  Every call first clears the part of the array it uses with a small
+ * kernel (so a call is two kernels on `stream`) and allocates nothing.  All
+ * calls on
  * one GPU share the array, which keeps the last call's contents: calls that
  * overlap on one GPU (other streams) race and must not be issued. */
 int gsa_gemv_allreduce_rmsnorm_noalloc(const uint16_t *A_r, const uint16_t *x, float *slots,

@@ -164,7 +164,7 @@ def test_repeats_bit_identical_and_mixed_with_plain_calls():
 
 def test_timeout_poisons_y_then_recovers():
     """A withheld peer: the waits expire, y and inv_rms come out NaN (every
-    tile still counts itself done, so nothing hangs); after a reset with the
+    tile still publishes its sums, so nothing hangs); after a reset with the
     peer published the next calls are correct."""
     _say("[epilogue] timeout")
     W, rank = 4, 1
