@@ -29,12 +29,14 @@ def _say(msg):
 
 def inv_rel_bound(N):
     """Relative bound on the kernel's fp32 1/rms: the sum of squares runs 16
-    sequential adds per tile, ceil(T/64) per lane of the fold and a 6-level
-    lane tree (depth d), after one rounding per square; then a division by
-    N, the +eps, the square root (which halves the relative error) and the
+    sequential adds per tile, then at most ceil(T/16) per lane of the fold
+    (a lane takes every (nt/P)-th record, nt >= 256 threads, P <= 16 lanes
+    per record), a lane tree of at most 6 levels and at most 8 wave sums in
+    order (depth d), after one rounding per square; then a division by N,
+    the +eps, the square root (which halves the relative error) and the
     reciprocal each round once."""
     T = (N + 15) // 16
-    d = 16 + math.ceil(T / 64) + 6
+    d = 16 + math.ceil(T / 16) + 6 + 8
     return ((d + 3) / 2 + 3) * U
 
 
