@@ -389,13 +389,65 @@ __device__ uint32_t wait_peers(const GemvArgs& a, int lane, int64_t tile, const 
   }
 }
 
-// The fused epilogue's grouped counts (see kEpiGroups): tile t is in group
-// t % kEpiGroups, which holds epi_group_tiles(g) of the call's tiles.
+// The fused epilogue's grouped counts (see kEpiGroups): 16-row tile t is in
+// group t % kEpiGroups, which holds epi_group_tiles(g) of the call's 16-row
+// tiles (a workgroup of more rows counts each of its 16-row tiles).
 __device__ __forceinline__ int epi_group_tiles(const GemvArgs& a, int g) {
-  return g < a.tiles ? (a.tiles - g + kEpiGroups - 1) / kEpiGroups : 0;
+  return g < a.epi_tiles ? (a.epi_tiles - g + kEpiGroups - 1) / kEpiGroups : 0;
 }
+
 __device__ __forceinline__ unsigned long long* epi_count(const GemvArgs& a, int64_t off, int g) {
   return reinterpret_cast<unsigned long long*>(a.ssq + off + (int64_t)g * kEpiRecordWords);
+}
+
+// Count 16-row tile t16 started (lanes below `subs` count t16 + lane, if it
+// exists); returns the count lane 0 saw before its own (used only in lane 0).
+__device__ __forceinline__ unsigned long long epi_count_started(const GemvArgs& a, int64_t t16,
+                                                                int subs, int lane) {
+  unsigned long long before = 0;
+  if (lane < subs && t16 + lane < a.epi_tiles)
+    before = __hip_atomic_fetch_add(
+        epi_count(a, epi_started_off(a.epi_tiles), (int)((t16 + lane) % kEpiGroups)), 1ull,
+        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return before;
+}
+
+// Lane g's reading of group g's started count (0 for a group without tiles).
+__device__ __forceinline__ unsigned long long epi_started_load(const GemvArgs& a, int lane) {
+  return epi_group_tiles(a, lane) > 0
+             ? __hip_atomic_load(epi_count(a, epi_started_off(a.epi_tiles), lane),
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+             : 0ull;
+}
+
+// Once the workgroup's protocol work is done: the call's index k (from the
+// count lane 0 saw for 16-row tile t16, every tile of a call being counted
+// once in its group) into *s_epi_k, and into s_ctl[3] whether every 16-row
+// tile of the call had started when the counts `now` (epi_started_load, lane
+// g: group g) were read.  One wave.
+__device__ __forceinline__ void epi_note_started(const GemvArgs& a, int64_t t16,
+                                                 unsigned long long before,
+                                                 unsigned long long now, int lane,
+                                                 uint32_t* s_ctl, unsigned long long* s_epi_k) {
+  const int grp = (int)(t16 % kEpiGroups);
+  const unsigned long long k =
+      __builtin_amdgcn_readfirstlane((uint32_t)(before / (unsigned)epi_group_tiles(a, grp))) |
+      0ull;
+  const int ng = epi_group_tiles(a, lane);
+  const bool lane_ok = ng == 0 || now >= (k + 1ull) * (unsigned)ng;
+  const bool all_started = __ballot(!lane_ok) == 0;
+  if (lane == 0) {
+    *s_epi_k = k;
+    s_ctl[3] = all_started ? 1u : 0u;
+  }
+}
+
+// The workgroup of tile `tile` (TR rows) folds the epilogue's records if it
+// holds the call's last 16-row tile.
+template <int TR>
+__device__ __forceinline__ bool epi_reducer(const GemvArgs& a, int64_t tile) {
+  static_assert(TR % kBigTile == 0, "whole 16-row tiles");
+  return (a.epi_tiles - 1) / (TR / kBigTile) == tile;
 }
 
 // The communication wave (the last wave of every workgroup) runs the
@@ -428,12 +480,9 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
   const uint32_t fl = load_flag(a, fs, lane);
   __syncthreads();  // B0: the flag loads are issued ahead of every x and A load
   // Count the tile started; the value is used only after the protocol work.
-  constexpr bool kEpi = TR == kBigTile;  // the epilogue runs on 16-row tiles only
-  const int grp = (int)(tile % kEpiGroups);
+  constexpr bool kEpi = TR == kBigTile;  // the epilogue runs on 16-row tiles here
   unsigned long long before = 0;
-  if (kEpi && a.epi && lane == 0)
-    before = __hip_atomic_fetch_add(epi_count(a, epi_started_off(a.tiles), grp), 1ull,
-                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (kEpi && a.epi) before = epi_count_started(a, tile, 1, lane);
   const uint32_t state = comm_decide<TS, TR>(a, lane, tile, fs, fl, s_ctl);
   uint32_t v[kMaxW][kPerLane<TR>];
   const bool early_tile = PE && state == kPeersReady;
@@ -463,29 +512,15 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
     __syncthreads();  // B3
   }
   if (TS && tile_owner<TS, TR>(a, tile) == a.rank) __syncthreads();  // B5
-  if (kEpi && a.epi) {
-    // The call's index k (every tile of a call is counted once per group).
-    const unsigned long long k =
-        __builtin_amdgcn_readfirstlane((uint32_t)(before / (unsigned)epi_group_tiles(a, grp))) |
-        0ull;
-    const int ng = epi_group_tiles(a, lane);
-    bool lane_ok = true;
-    if (ng > 0) {
-      const unsigned long long now = __hip_atomic_load(
-          epi_count(a, epi_started_off(a.tiles), lane), __ATOMIC_RELAXED,
-          __HIP_MEMORY_SCOPE_AGENT);
-      lane_ok = now >= (k + 1ull) * (unsigned)ng;
-    }
-    const bool all_started = __ballot(!lane_ok) == 0;
-    if (lane == 0) {
-      *s_epi_k = k;
-      s_ctl[3] = all_started ? 1u : 0u;
-    }
-    __syncthreads();  // E1
-    __syncthreads();  // E1b
-    if (s_ctl[3] || tile == a.tiles - 1) {  // a waiting tile, or the reducing workgroup
-      __syncthreads();  // E3
-      __syncthreads();  // E4
+  if constexpr (kEpi) {
+    if (a.epi) {
+      epi_note_started(a, tile, before, epi_started_load(a, lane), lane, s_ctl, s_epi_k);
+      __syncthreads();  // E1
+      __syncthreads();  // E1b
+      if (s_ctl[3] || epi_reducer<TR>(a, tile)) {  // a waiting tile, or the reducing workgroup
+        __syncthreads();  // E3
+        __syncthreads();  // E4
+      }
     }
   }
 }
@@ -512,7 +547,7 @@ __device__ __forceinline__ float one_shot_sum(const GemvArgs& a, float y, const 
   return acc;
 }
 
-template <int BM, int OPL>
+template <int BM, int OPL, int TR>
 __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
                                const bool (&own)[OPL], const bool (&live)[OPL],
                                const float (&o)[OPL], const bool (&ok)[OPL], float* elds,
@@ -625,7 +660,7 @@ __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t ti
   }
   if constexpr (TR == kBigTile) {
     if (a.epi)
-      fused_epilogue<BM, OPL>(a, tile, n, b, own, live, o, ok, elds, s_ctl, s_epi_k, wave, lane,
+      fused_epilogue<BM, OPL, TR>(a, tile, n, b, own, live, o, ok, elds, s_ctl, s_epi_k, wave, lane,
                               nt);
   }
 }
@@ -781,10 +816,11 @@ __device__ __forceinline__ float sum_lane_class(float v, int lp) {
 // a class are summed by a fixed butterfly (sum_lane_class) and the waves'
 // sums in wave order, so the result has the same bits on every call.
 // Result in s_inv[0..B), NaN in every column if the wait expired (then the
-// pad header records kErrEpiWait with this tile's first flag tile).
+// pad header records kErrEpiWait with flag tile ft0, the workgroup's first).
 // s_ctl[2] must be 0 on entry.  Contains the barrier E3.
-__device__ void fold_records(const GemvArgs& a, uint32_t mark, int64_t tile, int wave, int lane,
-                             int nt, float* wsum, float* s_inv, uint32_t* s_ctl) {
+__device__ void fold_records(const GemvArgs& a, uint32_t mark, int64_t ft0, int wave, int lane,
+                             int nt, float* wsum, float* s_inv, uint32_t* s_ctl,
+                             bool prewait_wide) {
   constexpr int kLoads = 16;
   const int lp = a.B <= 1 ? 0 : 32 - __builtin_clz((unsigned)(a.B - 1));  // log2 P
   const int c = lane & ((1 << lp) - 1);
@@ -793,15 +829,19 @@ __device__ void fold_records(const GemvArgs& a, uint32_t mark, int64_t tile, int
   const uint64_t start = wall_clock64();
   float acc = 0.0f;
   bool expired = false;
-  if (lp > 0 && lp <= 3) {
-    // 2 <= B <= 8: first the column-0 word of every record this wave reads
-    // below, the P lanes of a thread group sharing its tiles.  A record's
-    // words are stored by one instruction, so once these show the mark the
-    // reads below rarely find a word without it, each of which would cost a
-    // round trip of its own there (8B down_proj shape, B = 8: 11.1 against
-    // 12.2 us per call; at B = 16, 32 words a lane, it measured slower).
+  if (lp > 0 && (lp <= 3 || prewait_wide)) {
+    // 2 <= B <= 8 (B > 8 too if prewait_wide): first the column-0 word of
+    // every record this wave reads below, the P lanes of a thread group
+    // sharing its tiles.  A record's words are stored by one instruction, so
+    // once these show the mark the reads below rarely find a word without
+    // it, each of which would cost a round trip of its own there (8B
+    // down_proj shape, B = 8: 11.1 against 12.2 us per call).  At B = 16 (32
+    // words a lane) it pays only where the folding workgroup tends to finish
+    // its own rows early, among others that run alongside it (the 32-row
+    // LDS-staged kernel: skinny GEMM 15.7 against 18.1 us; the 16-row MFMA
+    // kernel, whose last workgroup starts last: 18.0 against 16.6).
     const int j = (wave * 64 + lane) >> lp;
-    for (int t = j + c * groups; t < a.tiles && !expired; t += groups << lp) {
+    for (int t = j + c * groups; t < a.epi_tiles && !expired; t += groups << lp) {
       unsigned long long v =
           __hip_atomic_load(epi_record(a, t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       while (((uint32_t)(v >> 32) & ~kEpiLeft) != mark) {
@@ -815,17 +855,17 @@ __device__ void fold_records(const GemvArgs& a, uint32_t mark, int64_t tile, int
     }
   }
   if (c < a.B) {
-    for (int t0 = (wave * 64 + lane) >> lp; t0 < a.tiles; t0 += kLoads * groups) {
+    for (int t0 = (wave * 64 + lane) >> lp; t0 < a.epi_tiles; t0 += kLoads * groups) {
       unsigned long long w[kLoads];
 #pragma unroll
       for (int u = 0; u < kLoads; ++u) {
-        const int t = min(t0 + u * groups, a.tiles - 1);
+        const int t = min(t0 + u * groups, a.epi_tiles - 1);
         w[u] = __hip_atomic_load(epi_record(a, t) + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
 #pragma unroll
       for (int u = 0; u < kLoads; ++u) {
         const int t = t0 + u * groups;
-        if (t < a.tiles) {
+        if (t < a.epi_tiles) {
           unsigned long long v = w[u];
           while (((uint32_t)(v >> 32) & ~kEpiLeft) != mark && !expired) {
             if (wall_clock64() - start > limit) {
@@ -849,7 +889,7 @@ __device__ void fold_records(const GemvArgs& a, uint32_t mark, int64_t tile, int
     const bool failed = s_ctl[2] != 0;
     if (failed && lane == 0) {
       atomicOr(a.pad + kHdrErrorBits, kErrEpiWait);
-      atomicMin(a.pad + kHdrEpiWaitTile, (uint32_t)(tile * (kBigTile / kFlagRows)));
+      atomicMin(a.pad + kHdrEpiWaitTile, (uint32_t)ft0);
     }
     if (lane < a.B) {
       float tot = 0.0f;
@@ -905,16 +945,24 @@ __device__ __forceinline__ void store_y(const GemvArgs& a, int64_t i, float v) {
 // that call.  Barriers: E1 (squares in LDS), E1b (out stores complete in a
 // tile that leaves), then, in the reducing and the waiting tiles, E3 (wave
 // sums in LDS, or inv seen) and E4 (inv in LDS).
-template <int BM, int OPL>
+// The records, the counts and the copies of inv are kept per 16-row tile
+// whatever the kernel's workgroup tile (TR = 16 or 32 rows, SUB = TR / 16
+// records a workgroup), so that calls on one buffer through kernels of either
+// tile size count and tag alike.  elds: TR x 16 squares, then 16 inv, then 8
+// x 16 wave sums (floats).
+template <int BM, int OPL, int TR>
 __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
                                const bool (&own)[OPL], const bool (&live)[OPL],
                                const float (&o)[OPL], const bool (&ok)[OPL], float* elds,
                                uint32_t* s_ctl, const unsigned long long* s_epi_k, int wave,
                                int lane, int nt) {
-  float* zz = elds;            // [16 rows][16 columns] squares of z
-  float* s_inv = elds + 256;   // [16] 1 / rms per column
-  float* wsum = elds + 272;    // [8 waves][16 columns] the fold's wave sums
-  const int64_t row0 = tile * kBigTile;
+  static_assert(TR % kBigTile == 0, "whole 16-row tiles");
+  constexpr int SUB = TR / kBigTile;
+  float* zz = elds;                 // [TR rows][16 columns] squares of z
+  float* s_inv = elds + TR * 16;    // [16] 1 / rms per column
+  float* wsum = s_inv + 16;         // [8 waves][16 columns] the fold's wave sums
+  const int64_t row0 = tile * TR;
+  const int64_t t16 = tile * SUB;   // the workgroup's first 16-row tile
   float z[OPL];
 #pragma unroll
   for (int e = 0; e < OPL; ++e) {
@@ -931,27 +979,33 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
   __syncthreads();  // E1: the squares are in LDS
   const uint32_t mark = epi_mark(*s_epi_k);
   const bool waits = s_ctl[3] != 0;
-  const bool reducer = tile == a.tiles - 1;
-  // This tile's group copy of the published inv: per column one 64-bit word
-  // (mark in the high half, the fp32 bits of inv in the low half).
+  const bool reducer = epi_reducer<TR>(a, tile);
+  // The group copy of the published inv this workgroup polls: per column one
+  // 64-bit word (mark in the high half, the fp32 bits of inv in the low half).
   const unsigned long long* inv_copy = reinterpret_cast<const unsigned long long*>(
-      a.ssq + epi_inv_off(a.tiles) + (int64_t)(tile % kEpiGroups) * kEpiRecordWords);
+      a.ssq + epi_inv_off(a.epi_tiles) + (int64_t)(t16 % kEpiGroups) * kEpiRecordWords);
   // A tile that leaves its rows to the reducing workgroup has its out at the
   // coherence point in every compute wave before its record goes out.
   if (!waits) wait_vm_all();
   if (reducer && wave == 0 && lane == 0) s_ctl[2] = 0u;
   __syncthreads();  // E1b
   if (wave == 0 && lane < a.B) {
-    float part = 0.0f;
-    for (int r = 0; r < kBigTile; ++r) part = part + zz[r * 16 + lane];
     const unsigned long long tag = mark | (waits ? 0u : kEpiLeft);
-    __hip_atomic_store(epi_record(a, tile) + lane, (tag << 32) | __float_as_uint(part),
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int h = 0; h < SUB; ++h) {
+      if (t16 + h < a.epi_tiles) {
+        float part = 0.0f;
+        for (int r = 0; r < kBigTile; ++r) part = part + zz[(h * kBigTile + r) * 16 + lane];
+        __hip_atomic_store(epi_record(a, t16 + h) + lane, (tag << 32) | __float_as_uint(part),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
   if (!reducer && !waits) return;
 
   if (reducer) {
-    fold_records(a, mark, tile, wave, lane, nt, wsum, s_inv, s_ctl);  // contains E3
+    fold_records(a, mark, tile * (TR / kFlagRows), wave, lane, nt, wsum, s_inv, s_ctl,
+                 TR > kBigTile);  // contains E3
     if (wave == 0) {
       // Every group's copy, one self-validating 64-bit word per column (so no
       // wait has to separate the values from a flag): P = B rounded up to a
@@ -963,7 +1017,7 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
       if (c < a.B) {
         for (int g = lane >> lp; g < kEpiGroups; g += 64 >> lp)
           __hip_atomic_store(reinterpret_cast<unsigned long long*>(
-                                 a.ssq + epi_inv_off(a.tiles) + (int64_t)g * kEpiRecordWords) +
+                                 a.ssq + epi_inv_off(a.epi_tiles) + (int64_t)g * kEpiRecordWords) +
                                  c,
                              word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
@@ -988,7 +1042,7 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
         if (wall_clock64() - start > 4 * a.timeout_ticks + 2000000ull) {
           if (lane == 0) {
             atomicOr(a.pad + kHdrErrorBits, kErrEpiWait);
-            atomicMin(a.pad + kHdrEpiWaitTile, (uint32_t)(tile * (kBigTile / kFlagRows)));
+            atomicMin(a.pad + kHdrEpiWaitTile, (uint32_t)(tile * (TR / kFlagRows)));
           }
           break;
         }
@@ -1017,8 +1071,8 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
   // outputs are read only after the fold saw every record (E3, E4).
   constexpr int kBatch = 4;
   const int64_t NB = a.N * a.B;
-  for (int t = wave * 64 + lane; t < a.tiles; t += nt) {
-    if (t == tile) continue;
+  for (int t = wave * 64 + lane; t < a.epi_tiles; t += nt) {
+    if (t / SUB == tile) continue;  // this workgroup's own rows
     const uint32_t tag = (uint32_t)(__hip_atomic_load(epi_record(a, t), __ATOMIC_RELAXED,
                                                       __HIP_MEMORY_SCOPE_AGENT) >> 32);
     if (tag != (mark | kEpiLeft)) continue;
@@ -1680,7 +1734,12 @@ __global__ __launch_bounds__(256) void peer_publish_kernel(float* slots, uint32_
 }
 
 // MFMA path with A staged through LDS: 8 < B <= 16, rows of exactly 256
-// chunks, the plain one-shot call (the skinny GEMM).  One workgroup owns 32
+// chunks, the one-shot call, plain or with the fused epilogue (the skinny
+// GEMM; the epilogue takes the 16-row MFMA kernel's 16.0 to 15.2 us per
+// call there: wave 0 counts the workgroup's two 16-row tiles started,
+// reads the started counts right after its MFMAs, the partials' LDS holds
+// the squares, and the producer waves join the epilogue's barriers).  One
+// workgroup owns 32
 // rows (two 16-row blocks of v_mfma_f32_16x16x32_bf16) with 4 consumer waves
 // and 2 producer waves.  Consumer wave w owns chunks [64 w, 64 w + 64) of
 // every row, in 8 stages of 8 chunks.  The producers copy A into LDS with
@@ -1758,6 +1817,8 @@ __global__ __launch_bounds__((kMfmaLCons + kMfmaLProd) * 64) void gemv_ar_mfma_l
   extern __shared__ __align__(16) unsigned char lds_a[];
   float* red = reinterpret_cast<float*>(lds_a + S * kMfmaLStageBytes);  // [wave][RB][16][16]
   __shared__ uint32_t s_ctl[kLongCtlWords];
+  __shared__ unsigned long long s_epi_k;  // the fused epilogue's call index
+  constexpr int SUB = TR / kBigTile;      // the epilogue's 16-row tiles per workgroup
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1796,6 +1857,14 @@ __global__ __launch_bounds__((kMfmaLCons + kMfmaLProd) * 64) void gemv_ar_mfma_l
     const uint32_t state = s_ctl[1];
     __syncthreads();  // B2
     if (state == kMustWait) __syncthreads();  // B3
+    if (a.epi) {
+      __syncthreads();  // E1
+      __syncthreads();  // E1b
+      if (s_ctl[3] || epi_reducer<TR>(a, tile)) {  // a waiting tile, or the reducing workgroup
+        __syncthreads();  // E3
+        __syncthreads();  // E4
+      }
+    }
     return;
   }
 
@@ -1804,7 +1873,13 @@ __global__ __launch_bounds__((kMfmaLCons + kMfmaLProd) * 64) void gemv_ar_mfma_l
   const uint32_t kOutOfRange = 0x80000000u;  // past any buffer: reads zeros
 
   uint32_t fl = 0;
-  if (wave == 0) fl = load_flag(a, fs, lane);
+  unsigned long long epi_before = 0;
+  if (wave == 0) {
+    fl = load_flag(a, fs, lane);
+    // The fused epilogue: count the workgroup's 16-row tiles started (the
+    // value is used once the protocol work is done).
+    if (a.epi) epi_before = epi_count_started(a, tile * SUB, SUB, lane);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
   // x: batch l16 (zeros past B), chunk 64 wave + 4 s + kq of MFMA step s.
@@ -1872,6 +1947,10 @@ __global__ __launch_bounds__((kMfmaLCons + kMfmaLProd) * 64) void gemv_ar_mfma_l
                                                           __builtin_bit_cast(bf16x8_t, xv[2 * j + m]),
                                                           acc[rb], 0, 0, 0);
   }
+  // The fused epilogue's reading of the started counts, taken here so that
+  // its round trip overlaps the publish (any tile counted by now has started).
+  unsigned long long epi_now = 0;
+  if (wave == 0 && a.epi) epi_now = epi_started_load(a, lane);
 #pragma unroll
   for (int r = 0; r < RB; ++r)
 #pragma unroll
@@ -1903,10 +1982,21 @@ __global__ __launch_bounds__((kMfmaLCons + kMfmaLProd) * 64) void gemv_ar_mfma_l
       if (live[i]) store_slot(a, a.rank * NB + oi[i], yp[i]);
   }
   __builtin_amdgcn_sched_barrier(0);
+  // With the fused epilogue, out is stored device-coherently: the reducing
+  // workgroup may read it back.
+  auto put_out = [&](int64_t i, float v) {
+    if (a.epi)
+      store_coherent(&a.out[i], v);
+    else
+      store_out(a, i, v);
+  };
+  bool okv[OPT];  // out of the output computed (its flag tile complete)
+#pragma unroll
+  for (int i = 0; i < OPT; ++i) okv[i] = state == kPeersReady;
   if (state == kPeersReady) {
 #pragma unroll
     for (int i = 0; i < OPT; ++i)
-      if (live[i]) store_out(a, oi[i], outv[i]);
+      if (live[i]) put_out(oi[i], outv[i]);
     wait_vm_le<OPT>();  // the published values are at the coherence point (in-order completion)
   } else {
     wait_vm_all();
@@ -1924,14 +2014,31 @@ __global__ __launch_bounds__((kMfmaLCons + kMfmaLProd) * 64) void gemv_ar_mfma_l
 #pragma unroll
     for (int i = 0; i < OPT; ++i) {
       const int q = ((tid + NT * i) / 16) / kFlagRows;
-      if (live[i] && ((done >> q) & 1u)) {
+      okv[i] = ((done >> q) & 1u) != 0;
+      if (live[i] && okv[i]) {
         float acc2 = 0.0f;
 #pragma unroll
         for (int r = 0; r < kMaxW; ++r)
           if (r < a.W) acc2 = acc2 + (r == a.rank ? yp[i] : load_slot(a, r * NB + oi[i]));
-        store_out(a, oi[i], acc2);
+        outv[i] = acc2;
+        put_out(oi[i], acc2);
       }
     }
+  }
+  if (a.epi) {
+    // Thread tid holds outputs tid + NT i: local row (tid + NT i) / 16,
+    // column tid % 16.  The partials in `red` were all read before B2, so
+    // the epilogue's LDS takes their place.
+    if (wave == 0) epi_note_started(a, tile * SUB, epi_before, epi_now, lane, s_ctl, &s_epi_k);
+    int n[OPT];
+    bool own[OPT];
+#pragma unroll
+    for (int i = 0; i < OPT; ++i) {
+      n[i] = (tid + NT * i) / 16;
+      own[i] = (tid & 15) < a.B;
+    }
+    fused_epilogue<GSA_MAX_B, OPT, TR>(a, tile, n, tid & 15, own, live, outv, okv, red, s_ctl,
+                                       &s_epi_k, wave, lane, NT);
   }
 }
 
@@ -2042,8 +2149,9 @@ ValuChoice pick_kernel(int B, int C, bool small_tiles) {
     case 7: return valu_kernel<7, TS, DT>(C, small_tiles);
     case 8: return valu_kernel<8, TS, DT>(C, small_tiles);
     default:
-      // Rows of exactly 256 chunks, plain call: A staged through LDS.
-      if (!TS && small_tiles && C == 16 * 16)
+      // Rows of exactly 256 chunks, one-shot (plain or fused epilogue): A
+      // staged through LDS.
+      if (!TS && C == 16 * 16)
         return ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma_lds<DT>),
                           (kMfmaLCons + kMfmaLProd) * 64, kMfmaLRows, true, kMfmaLLdsBytes};
       return mfma_x_in_lds(C)

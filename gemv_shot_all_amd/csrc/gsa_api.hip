@@ -321,7 +321,8 @@ int enqueue_call(const uint16_t* A_r, const uint16_t* x, void* slots_any, uint32
                                  out_dtype == GSA_DTYPE_BF16, &l))
       return GSA_EINVAL;
     a.row_stride = (int)h->row_stride;
-    a.tiles = (int)((N + l.tile_rows - 1) / l.tile_rows);  // == h->tiles for 16-row tiles
+    a.tiles = (int)((N + l.tile_rows - 1) / l.tile_rows);
+    a.epi_tiles = (int)h->tiles;  // 16-row tiles, whatever the kernel's tile
     a.ssq = h->ssq;
     if (l.lds_bytes > 65536 && !g_big_lds_ready.count(l.kernel)) {
       // Opt in once to the largest dynamic LDS any shape of this kernel may use.
@@ -362,7 +363,7 @@ int enqueue_call(const uint16_t* A_r, const uint16_t* x, void* slots_any, uint32
     // word a previous call left can pass for one of this call.
     a.ssq = epi_scratch;
     e = gsa::launch_clear_words(reinterpret_cast<uint32_t*>(epi_scratch),
-                                gsa::epi_scratch_words(a.tiles), static_cast<hipStream_t>(stream));
+                                gsa::epi_scratch_words(a.epi_tiles), static_cast<hipStream_t>(stream));
   }
   if (e == hipSuccess) e = gsa::launch_gemv(l, a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {

@@ -53,6 +53,7 @@ struct GemvArgs {
   int rank;
   int row_stride;         // words between flag rows
   int tiles;              // workgroup tiles: ceil(N / tile rows of the kernel)
+  int epi_tiles;          // the fused epilogue's 16-row tiles: ceil(N / 16)
   uint64_t timeout_ticks; // device wall-clock ticks a wait may take
   // Two-shot variant (the kernels' TS instances): rank p owns the 16-row
   // blocks [p * chunk_tiles, (p + 1) * chunk_tiles), reduces them into gathered
