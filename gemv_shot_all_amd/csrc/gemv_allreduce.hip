@@ -473,16 +473,16 @@ __device__ __forceinline__ bool epi_reducer(const GemvArgs& a, int64_t tile) {
 // PE: whether the compute waves take the peer tile from LDS when every peer
 // had published at the start (the VALU one-shot kernels load their own peer
 // values instead; a late peer tile always goes through LDS).
-template <bool TS, int TR, bool PE>
+template <bool TS, int TR, bool PE, bool EPI>
 __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
                           uint32_t* s_ctl, unsigned long long* s_epi_k) {
   const FlagSpan fs = flag_span<TR>(a, tile);
   const uint32_t fl = load_flag(a, fs, lane);
   __syncthreads();  // B0: the flag loads are issued ahead of every x and A load
   // Count the tile started; the value is used only after the protocol work.
-  constexpr bool kEpi = TR == kBigTile;  // the epilogue runs on 16-row tiles here
+  constexpr bool kEpi = EPI && TR == kBigTile;  // the epilogue runs on 16-row tiles here
   unsigned long long before = 0;
-  if (kEpi && a.epi) before = epi_count_started(a, tile, 1, lane);
+  if constexpr (kEpi) before = epi_count_started(a, tile, 1, lane);
   const uint32_t state = comm_decide<TS, TR>(a, lane, tile, fs, fl, s_ctl);
   uint32_t v[kMaxW][kPerLane<TR>];
   const bool early_tile = PE && state == kPeersReady;
@@ -513,14 +513,12 @@ __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
   }
   if (TS && tile_owner<TS, TR>(a, tile) == a.rank) __syncthreads();  // B5
   if constexpr (kEpi) {
-    if (a.epi) {
-      epi_note_started(a, tile, before, epi_started_load(a, lane), lane, s_ctl, s_epi_k);
-      __syncthreads();  // E1
-      __syncthreads();  // E1b
-      if (s_ctl[3] || epi_reducer<TR>(a, tile)) {  // a waiting tile, or the reducing workgroup
-        __syncthreads();  // E3
-        __syncthreads();  // E4
-      }
+    epi_note_started(a, tile, before, epi_started_load(a, lane), lane, s_ctl, s_epi_k);
+    __syncthreads();  // E1
+    __syncthreads();  // E1b
+    if (s_ctl[3] || epi_reducer<TR>(a, tile)) {  // a waiting tile, or the reducing workgroup
+      __syncthreads();  // E3
+      __syncthreads();  // E4
     }
   }
 }
@@ -568,7 +566,7 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
 // so out is summed and stored right behind the published value, and the
 // wait before B2 covers only the published value (stores complete in issue
 // order); the out store's round trip overlaps it.
-template <int BM, int OPL, bool TS, int TR>
+template <int BM, int OPL, bool TS, int TR, bool EPI>
 __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
                                    const bool (&own)[OPL], const float (&y)[OPL],
                                    const float* pe, float* elds, uint32_t* s_ctl,
@@ -615,8 +613,8 @@ __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t ti
   if (own_peers) {
     if (live[0]) {
       const int64_t i = (row0 + n[0]) * a.B + b;
-      if (a.epi)
-        store_coherent(&a.out[i], o[0]);  // read back by the workgroup that finishes last
+      if constexpr (EPI)
+        store_coherent(&a.out[i], o[0]);  // the reducing workgroup may read it back
       else
         store_out_wt(a, i, o[0]);
     }
@@ -646,8 +644,8 @@ __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t ti
       } else {
         o[e] = pe[owner * TR * a.B + n[e] * a.B + b];  // the owner's reduced chunk
       }
-      if (a.epi)
-        store_coherent(&a.out[i], o[e]);  // read back by the workgroup that finishes last
+      if constexpr (EPI)
+        store_coherent(&a.out[i], o[e]);  // the reducing workgroup may read it back
       else
         store_out_wt(a, i, o[e]);
     }
@@ -658,11 +656,9 @@ __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t ti
     if (wave == 0 && lane < fs.nf && ((done >> lane) & 1u))
       store_flag(flag2_ptr(a, a.rank, fs.f0 + lane), s_ctl[4 + lane]);
   }
-  if constexpr (TR == kBigTile) {
-    if (a.epi)
-      fused_epilogue<BM, OPL, TR>(a, tile, n, b, own, live, o, ok, elds, s_ctl, s_epi_k, wave, lane,
-                              nt);
-  }
+  if constexpr (EPI && TR == kBigTile)
+    fused_epilogue<BM, OPL, TR>(a, tile, n, b, own, live, o, ok, elds, s_ctl, s_epi_k, wave, lane,
+                                nt);
 }
 
 // The value that lane l ^ D holds (D = 8, 4, 2 or 1; partners stay within a
@@ -1137,10 +1133,12 @@ __device__ __forceinline__ int rotated(int j, int rot) {
 
 // The lane's chunks as a stream with D chunks in flight: step j handles
 // chunk li + rotated(j) * G of each row, ring[j % D] holds it, steps 0..D-1
-// were issued before the LDS barrier.  A scheduling barrier closes each step:
-// left free, the scheduler has hoisted later steps' x reads and sunk the
-// refills behind them, draining the ring (twice the time on B = 8 rows of
-// 224 chunks).  NCH > 0: exactly NCH chunks, fully
+// were issued before the LDS barrier.  A scheduling barrier closes each step
+// (PIN): left free, the scheduler has hoisted later steps' x reads and sunk
+// the refills behind them, draining the ring (twice the time on B = 8 rows
+// of 224 chunks; after an unrelated change elsewhere in the kernel, the
+// two-shot call on the 70B-class shape 14.7 against 12.4 us, the 8B
+// down_proj at B = 4 5.71 against 5.41).  NCH > 0: exactly NCH chunks, fully
 // unrolled, starting at the tile's rotation rot; NCH == 0: nch chunks in
 // order, unrolled by D.
 template <bool MASKED, int NCH, int D, int B, int G, int R, bool PIN>
@@ -1188,7 +1186,7 @@ __device__ __forceinline__ void valu_stream(float (&acc)[R][B], uint4 (&ring)[D]
 // on 16).  XM: XCD-contiguous tile order (block_tile).
 // LDS: x chunks [b][c], one zero chunk, one sink chunk, then the peer tile.
 template <int B, int G, int R, int NW, int NCH, int D, int XPT, int WPE, bool MASKED, bool TS,
-          bool XM, int DT>
+          bool XM, int DT, bool EPI>
 __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs args) {
   const GemvArgs a = typed_args<DT>(args);
   constexpr int NT = NW * 64;
@@ -1220,15 +1218,13 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs args
   // At B = 8 either measured slower than summing after B2 (8B down_proj shape
   // 6.16 against 5.85 us with own loads), so larger batches do that.
   constexpr bool kEarlyOut = !TS && B <= 4;
-#ifndef X_PIN
-  constexpr bool kPinSteps = G == 32 && B > 4;  // rows up to 224 chunks, B > 4
-#else
-  constexpr bool kPinSteps = X_PIN;
-#endif
+  // Every step of the A stream pinned (valu_stream), except in the 8-wave
+  // tier at B = 8, where the pins make the registers spill.
+  constexpr bool kPinSteps = !(G == 64 && NW == 8 && B == 8);
   constexpr bool kPeersFromTile = kEarlyOut && NW == 8;
   constexpr bool kOwnPeers = kEarlyOut && !kPeersFromTile;
   if (wave == NW) {
-    comm_wave<TS, TR, !kOwnPeers>(a, lane, tile, pe, s_ctl, &s_epi_k);
+    comm_wave<TS, TR, !kOwnPeers, EPI>(a, lane, tile, pe, s_ctl, &s_epi_k);
     return;
   }
 
@@ -1330,7 +1326,7 @@ __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs args
   const int n[1] = {nloc0 + vidx / B};
   const bool own[1] = {vown};
   const float y[1] = {yv};
-  publish_and_reduce<B, 1, TS, TR>(a, tile, n, vidx % B, own, y, pe, elds, s_ctl, &s_epi_k,
+  publish_and_reduce<B, 1, TS, TR, EPI>(a, tile, n, vidx % B, own, y, pe, elds, s_ctl, &s_epi_k,
                                    state, wave, lane, NT, own_peers, pv);
 }
 
@@ -1498,7 +1494,7 @@ __global__ __launch_bounds__(kLongWaves * 64, kLongWaves / 4) void gemv_ar_long(
 // MFMA epilogue: each wave's 16 x 16 partial goes to red[wave][n][b]; after
 // B1 wave w sums rows 4w .. 4w+3 over the waves in wave order (lane l: row
 // 4w + (l >> 4), column l & 15), publishes them and reduces.
-template <int NW, bool TS>
+template <int NW, bool TS, bool EPI>
 __device__ __forceinline__ void mfma_finish(const GemvArgs& a, int64_t tile, int wave, int lane,
                                             f32x4_t acc, float* red, const float* pe,
                                             float* elds, uint32_t* s_ctl,
@@ -1517,7 +1513,7 @@ __device__ __forceinline__ void mfma_finish(const GemvArgs& a, int64_t tile, int
   const bool own[1] = {bl < a.B};
   const float yv[1] = {y};
   const float no_pv[kMaxW] = {};
-  publish_and_reduce<GSA_MAX_B, 1, TS, kBigTile>(a, tile, n, bl, own, yv, pe, elds, s_ctl,
+  publish_and_reduce<GSA_MAX_B, 1, TS, kBigTile, EPI>(a, tile, n, bl, own, yv, pe, elds, s_ctl,
                                                  s_epi_k, state, wave, lane, NW * 64, false,
                                                  no_pv);
 }
@@ -1535,7 +1531,7 @@ __device__ __forceinline__ void mfma_finish(const GemvArgs& a, int64_t tile, int
 // is finite).  The per-wave 16 x 16 fp32 partials are summed in wave order
 // through LDS.  One more wave runs the signal-pad protocol.
 // LDS: x [16][C + 1] chunks (column C zero); NW 16 x 16 partials; peer tile.
-template <int NW, int D, bool TS, int DT>
+template <int NW, int D, bool TS, int DT, bool EPI>
 __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs args) {
   const GemvArgs a = typed_args<DT>(args);
   static_assert(NW * 4 == kBigTile, "each compute wave finishes 4 rows of the tile");
@@ -1554,7 +1550,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs args) 
   float* elds = pe + a.W * kBigTile * a.B + 1;  // the epilogue's LDS
 
   if (wave == NW) {
-    comm_wave<TS, kBigTile, true>(a, lane, tile, pe, s_ctl, &s_epi_k);
+    comm_wave<TS, kBigTile, true, EPI>(a, lane, tile, pe, s_ctl, &s_epi_k);
     return;
   }
 
@@ -1621,7 +1617,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs args) 
     }
   }
 
-  mfma_finish<NW, TS>(a, tile, wave, lane, acc, red, pe, elds, s_ctl, &s_epi_k);
+  mfma_finish<NW, TS, EPI>(a, tile, wave, lane, acc, red, pe, elds, s_ctl, &s_epi_k);
 }
 
 // MFMA path for x beyond the LDS bound (8 < B <= 16, 16 * (C + 1) chunks over
@@ -1631,7 +1627,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs args) 
 // wave's steps start at a rotation that differs between the workgroups of
 // one XCD so that they do not all read the same lines of x at once.
 // LDS: NW 16 x 16 partials, then the peer tile.
-template <int NW, int D, bool TS, int DT>
+template <int NW, int D, bool TS, int DT, bool EPI>
 __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs args) {
   const GemvArgs a = typed_args<DT>(args);
   static_assert(NW * 4 == kBigTile, "each compute wave finishes 4 rows of the tile");
@@ -1649,7 +1645,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a
   float* elds = pe + a.W * kBigTile * a.B + 1;  // the epilogue's LDS
 
   if (wave == NW) {
-    comm_wave<TS, kBigTile, true>(a, lane, tile, pe, s_ctl, &s_epi_k);
+    comm_wave<TS, kBigTile, true, EPI>(a, lane, tile, pe, s_ctl, &s_epi_k);
     return;
   }
 
@@ -1701,7 +1697,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs a
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-  mfma_finish<NW, TS>(a, tile, wave, lane, acc, red, pe, elds, s_ctl, &s_epi_k);
+  mfma_finish<NW, TS, EPI>(a, tile, wave, lane, acc, red, pe, elds, s_ctl, &s_epi_k);
 }
 
 // One-GPU stand-in for a peer's zero-copy push (the fused-operators page:
@@ -1800,7 +1796,7 @@ __device__ __forceinline__ int lds_stage_rot(int64_t t) {
   return (int)((t ^ (t >> 3)) & (NS - 1));
 }
 
-template <int DT>
+template <int DT, bool EPI>
 __global__ __launch_bounds__((kMfmaLCons + kMfmaLProd) * 64) void gemv_ar_mfma_lds(GemvArgs args) {
   const GemvArgs a = typed_args<DT>(args);
   constexpr int RB = kMfmaLRows / 16;
@@ -1857,7 +1853,7 @@ __global__ __launch_bounds__((kMfmaLCons + kMfmaLProd) * 64) void gemv_ar_mfma_l
     const uint32_t state = s_ctl[1];
     __syncthreads();  // B2
     if (state == kMustWait) __syncthreads();  // B3
-    if (a.epi) {
+    if constexpr (EPI) {
       __syncthreads();  // E1
       __syncthreads();  // E1b
       if (s_ctl[3] || epi_reducer<TR>(a, tile)) {  // a waiting tile, or the reducing workgroup
@@ -1878,7 +1874,7 @@ __global__ __launch_bounds__((kMfmaLCons + kMfmaLProd) * 64) void gemv_ar_mfma_l
     fl = load_flag(a, fs, lane);
     // The fused epilogue: count the workgroup's 16-row tiles started (the
     // value is used once the protocol work is done).
-    if (a.epi) epi_before = epi_count_started(a, tile * SUB, SUB, lane);
+    if constexpr (EPI) epi_before = epi_count_started(a, tile * SUB, SUB, lane);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -1950,7 +1946,9 @@ __global__ __launch_bounds__((kMfmaLCons + kMfmaLProd) * 64) void gemv_ar_mfma_l
   // The fused epilogue's reading of the started counts, taken here so that
   // its round trip overlaps the publish (any tile counted by now has started).
   unsigned long long epi_now = 0;
-  if (wave == 0 && a.epi) epi_now = epi_started_load(a, lane);
+  if constexpr (EPI) {
+    if (wave == 0) epi_now = epi_started_load(a, lane);
+  }
 #pragma unroll
   for (int r = 0; r < RB; ++r)
 #pragma unroll
@@ -1985,7 +1983,7 @@ __global__ __launch_bounds__((kMfmaLCons + kMfmaLProd) * 64) void gemv_ar_mfma_l
   // With the fused epilogue, out is stored device-coherently: the reducing
   // workgroup may read it back.
   auto put_out = [&](int64_t i, float v) {
-    if (a.epi)
+    if constexpr (EPI)
       store_coherent(&a.out[i], v);
     else
       store_out(a, i, v);
@@ -2025,7 +2023,7 @@ __global__ __launch_bounds__((kMfmaLCons + kMfmaLProd) * 64) void gemv_ar_mfma_l
       }
     }
   }
-  if (a.epi) {
+  if constexpr (EPI) {
     // Thread tid holds outputs tid + NT i: local row (tid + NT i) / 16,
     // column tid % 16.  The partials in `red` were all read before B2, so
     // the epilogue's LDS takes their place.
@@ -2080,7 +2078,7 @@ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // exact instance; any other C the masked streaming instance.  XPT covers
 // B * G * NCH chunks of x (at most 8 per thread; the rest of a longer x is
 // staged by a plain loop).
-template <int B, int G, int R, int NW, int NCH, int D, int WPE, bool TS, bool XM, int DT>
+template <int B, int G, int R, int NW, int NCH, int D, int WPE, bool TS, bool XM, int DT, bool EPI>
 ValuChoice valu_tier(int C) {
   constexpr int XPT0 = ceil_div(B * G * NCH, NW * 64);
   constexpr int XPT = XPT0 > 8 ? 8 : XPT0;
@@ -2088,10 +2086,10 @@ ValuChoice valu_tier(int C) {
   const void* k;
   if (C == G * NCH)
     k = reinterpret_cast<const void*>(
-        &gemv_ar_valu<B, G, R, NW, NCH, DE, XPT, WPE, false, TS, XM, DT>);
+        &gemv_ar_valu<B, G, R, NW, NCH, DE, XPT, WPE, false, TS, XM, DT, EPI>);
   else
     k = reinterpret_cast<const void*>(
-        &gemv_ar_valu<B, G, R, NW, 0, D, XPT, WPE, true, TS, XM, DT>);
+        &gemv_ar_valu<B, G, R, NW, 0, D, XPT, WPE, true, TS, XM, DT, EPI>);
   return {k, (NW + 1) * 64, NW * (64 / G) * R};
 }
 
@@ -2122,44 +2120,53 @@ ValuChoice long_tier(int C) {
 // of rows up to C = 224 go to the XCDs in contiguous runs (block_tile).
 // DT other than fp32 (bf16 slots or out) comes only with small tiles and
 // one-shot: the instances it takes are the ones those calls reach.
-template <int B, bool TS, int DT>
-ValuChoice valu_kernel(int C, bool small_tiles) {
-  static_assert(!(DT != kDtF32 && TS), "element types are for the one-shot call");
-  if (small_tiles && !TS && C > 224) return long_tier<B, DT>(C);
-  if (small_tiles && C <= 64) return valu_tier<B, 32, 2, 1, 2, 2, 1, TS, true, DT>(C);
-  if constexpr (DT == kDtF32) {
-    if (C <= 64) return valu_tier<B, 64, 4, 4, 1, 1, 1, TS, true, kDtF32>(C);
+template <int B, bool TS, int DT, bool EPI>
+ValuChoice valu_kernel(int C) {
+  static_assert(!(DT != kDtF32 && (TS || EPI)), "element types are for the plain one-shot call");
+  static_assert(!(TS && EPI), "no fused epilogue in the two-shot call");
+  if constexpr (!EPI) {
+    if (!TS && C > 224) return long_tier<B, DT>(C);
+    if (C <= 64) return valu_tier<B, 32, 2, 1, 2, 2, 1, TS, true, DT, false>(C);
+  } else {
+    // The fused epilogue counts 16-row tiles.
+    if (C <= 64) return valu_tier<B, 64, 4, 4, 1, 1, 1, false, true, kDtF32, true>(C);
   }
-  if (C <= 224) return valu_tier<B, 32, 2, 4, 7, 4, 1, TS, true, DT>(C);
+  if (C <= 224) return valu_tier<B, 32, 2, 4, 7, 4, 1, TS, true, DT, EPI>(C);
   if constexpr (DT != kDtF32)
-    return ValuChoice{nullptr, 0, 0};  // not reached: small tiles take the long tier
+    return ValuChoice{nullptr, 0, 0};  // not reached: the plain call takes the long tier
   else
-    return valu_tier<B, 64, 2, 8, 7, 3, 5, TS, false, kDtF32>(C);
+    return valu_tier<B, 64, 2, 8, 7, 3, 5, TS, false, kDtF32, EPI>(C);
 }
 
-template <bool TS, int DT>
-ValuChoice pick_kernel(int B, int C, bool small_tiles) {
+// EPI: the kernels of the fused epilogue, instances of their own, so that the
+// plain and two-shot instances carry none of its code (the compiler's
+// schedule of their A stream has moved with changes to it).
+template <bool TS, int DT, bool EPI>
+ValuChoice pick_kernel(int B, int C) {
   switch (B) {
-    case 1: return valu_kernel<1, TS, DT>(C, small_tiles);
-    case 2: return valu_kernel<2, TS, DT>(C, small_tiles);
-    case 3: return valu_kernel<3, TS, DT>(C, small_tiles);
-    case 4: return valu_kernel<4, TS, DT>(C, small_tiles);
-    case 5: return valu_kernel<5, TS, DT>(C, small_tiles);
-    case 6: return valu_kernel<6, TS, DT>(C, small_tiles);
-    case 7: return valu_kernel<7, TS, DT>(C, small_tiles);
-    case 8: return valu_kernel<8, TS, DT>(C, small_tiles);
+    case 1: return valu_kernel<1, TS, DT, EPI>(C);
+    case 2: return valu_kernel<2, TS, DT, EPI>(C);
+    case 3: return valu_kernel<3, TS, DT, EPI>(C);
+    case 4: return valu_kernel<4, TS, DT, EPI>(C);
+    case 5: return valu_kernel<5, TS, DT, EPI>(C);
+    case 6: return valu_kernel<6, TS, DT, EPI>(C);
+    case 7: return valu_kernel<7, TS, DT, EPI>(C);
+    case 8: return valu_kernel<8, TS, DT, EPI>(C);
     default:
       // Rows of exactly 256 chunks, one-shot (plain or fused epilogue): A
       // staged through LDS.
-      if (!TS && C == 16 * 16)
-        return ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma_lds<DT>),
-                          (kMfmaLCons + kMfmaLProd) * 64, kMfmaLRows, true, kMfmaLLdsBytes};
+      if constexpr (!TS) {
+        if (C == 16 * 16)
+          return ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma_lds<DT, EPI>),
+                            (kMfmaLCons + kMfmaLProd) * 64, kMfmaLRows, true, kMfmaLLdsBytes};
+      }
       return mfma_x_in_lds(C)
-                 ? ValuChoice{reinterpret_cast<const void*>(&gemv_ar_mfma<kMfmaWaves, 8, TS, DT>),
+                 ? ValuChoice{reinterpret_cast<const void*>(
+                                  &gemv_ar_mfma<kMfmaWaves, 8, TS, DT, EPI>),
                               (kMfmaWaves + 1) * 64, kBigTile}
-                 : ValuChoice{
-                       reinterpret_cast<const void*>(&gemv_ar_mfma_xmem<kMfmaWaves, 8, TS, DT>),
-                       (kMfmaWaves + 1) * 64, kBigTile};
+                 : ValuChoice{reinterpret_cast<const void*>(
+                                  &gemv_ar_mfma_xmem<kMfmaWaves, 8, TS, DT, EPI>),
+                              (kMfmaWaves + 1) * 64, kBigTile};
   }
 }
 
@@ -2184,11 +2191,12 @@ bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, bool slot_
   if (epi && two_shot) return false;  // separate entry points
   const bool typed = slot_bf16 || out_bf16;
   if (typed && (epi || two_shot)) return false;  // element types: the plain one-shot call only
-  const bool small_tiles = !epi;  // the fused epilogue counts 16-row tiles
-  const ValuChoice k = two_shot                 ? pick_kernel<true, kDtF32>(B, C, small_tiles)
-                       : slot_bf16 && out_bf16 ? pick_kernel<false, kDtBf16>(B, C, small_tiles)
-                       : typed                 ? pick_kernel<false, kDtMixed>(B, C, small_tiles)
-                                               : pick_kernel<false, kDtF32>(B, C, small_tiles);
+  if (epi && two_shot) return false;
+  const ValuChoice k = two_shot                 ? pick_kernel<true, kDtF32, false>(B, C)
+                       : epi                   ? pick_kernel<false, kDtF32, true>(B, C)
+                       : slot_bf16 && out_bf16 ? pick_kernel<false, kDtBf16, false>(B, C)
+                       : typed                 ? pick_kernel<false, kDtMixed, false>(B, C)
+                                               : pick_kernel<false, kDtF32, false>(B, C);
   if (!k.kernel) return false;
   *out = {k.kernel, (unsigned)k.threads,
           k.fixed_lds ? k.lds_bytes : gemv_lds_bytes(W, B, C, epi, k.tile_rows), k.tile_rows};
