@@ -442,6 +442,12 @@ __device__ __forceinline__ void epi_note_started(const GemvArgs& a, int64_t t16,
   }
 }
 
+// The kernels' epilogue parameter EPI: none, the fused bias + RMSNorm with
+// 1/rms folded by one workgroup and polled by the others, or folded by every
+// workgroup that waits (few records: no copy of 1/rms to publish and poll).
+constexpr int kEpiNone = 0, kEpiFoldOne = 1, kEpiFoldAll = 2;
+constexpr int64_t kEpiFoldAllWords = 64;  // kEpiFoldAll up to this many record words a call
+
 // The workgroup of tile `tile` (TR rows) folds the epilogue's records if it
 // holds the call's last 16-row tile.
 template <int TR>
@@ -473,14 +479,14 @@ __device__ __forceinline__ bool epi_reducer(const GemvArgs& a, int64_t tile) {
 // PE: whether the compute waves take the peer tile from LDS when every peer
 // had published at the start (the VALU one-shot kernels load their own peer
 // values instead; a late peer tile always goes through LDS).
-template <bool TS, int TR, bool PE, bool EPI>
+template <bool TS, int TR, bool PE, int EPI>
 __device__ void comm_wave(const GemvArgs& a, int lane, int64_t tile, float* pe,
                           uint32_t* s_ctl, unsigned long long* s_epi_k) {
   const FlagSpan fs = flag_span<TR>(a, tile);
   const uint32_t fl = load_flag(a, fs, lane);
   __syncthreads();  // B0: the flag loads are issued ahead of every x and A load
   // Count the tile started; the value is used only after the protocol work.
-  constexpr bool kEpi = EPI && TR == kBigTile;  // the epilogue runs on 16-row tiles here
+  constexpr bool kEpi = EPI != 0 && TR == kBigTile;  // the epilogue runs on 16-row tiles here
   unsigned long long before = 0;
   if constexpr (kEpi) before = epi_count_started(a, tile, 1, lane);
   const uint32_t state = comm_decide<TS, TR>(a, lane, tile, fs, fl, s_ctl);
@@ -545,7 +551,7 @@ __device__ __forceinline__ float one_shot_sum(const GemvArgs& a, float y, const 
   return acc;
 }
 
-template <int BM, int OPL, int TR>
+template <int BM, int OPL, int TR, bool ALL>
 __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
                                const bool (&own)[OPL], const bool (&live)[OPL],
                                const float (&o)[OPL], const bool (&ok)[OPL], float* elds,
@@ -566,7 +572,7 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
 // so out is summed and stored right behind the published value, and the
 // wait before B2 covers only the published value (stores complete in issue
 // order); the out store's round trip overlaps it.
-template <int BM, int OPL, bool TS, int TR, bool EPI>
+template <int BM, int OPL, bool TS, int TR, int EPI>
 __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
                                    const bool (&own)[OPL], const float (&y)[OPL],
                                    const float* pe, float* elds, uint32_t* s_ctl,
@@ -656,9 +662,9 @@ __device__ __forceinline__ void publish_and_reduce(const GemvArgs& a, int64_t ti
     if (wave == 0 && lane < fs.nf && ((done >> lane) & 1u))
       store_flag(flag2_ptr(a, a.rank, fs.f0 + lane), s_ctl[4 + lane]);
   }
-  if constexpr (EPI && TR == kBigTile)
-    fused_epilogue<BM, OPL, TR>(a, tile, n, b, own, live, o, ok, elds, s_ctl, s_epi_k, wave, lane,
-                                nt);
+  if constexpr (EPI != kEpiNone && TR == kBigTile)
+    fused_epilogue<BM, OPL, TR, EPI == kEpiFoldAll>(a, tile, n, b, own, live, o, ok, elds, s_ctl,
+                                                    s_epi_k, wave, lane, nt);
 }
 
 // The value that lane l ^ D holds (D = 8, 4, 2 or 1; partners stay within a
@@ -929,7 +935,13 @@ __device__ __forceinline__ void store_y(const GemvArgs& a, int64_t i, float v) {
 //    the communication wave) may wait: every other tile is resident or done
 //    and finishes on its own.  It polls (bounded) its group's copy until
 //    every column shows the mark, takes inv from it and normalises its own
-//    rows from registers.
+//    rows from registers.  With ALL (calls of at most 64 record words) it
+//    folds the records itself instead, as the reducing workgroup does and
+//    with the same bits, and no copy of inv is published: one store and one
+//    poll fewer after the last record (c1 shape: 6.9 against 7.4 us per call
+//    with one folding workgroup); from 256 tiles on, every tile reading
+//    every record costs more than it saves (o_proj shape 8.0 against 7.8,
+//    70B-class shape 21.3 against 16.8).
 //  - Any other tile first waits until its out stores are at the coherence
 //    point, tags its record kEpiLeft and leaves; the reducing workgroup, once
 //    it has inv, also normalises the rows of every tile tagged so, re-reading
@@ -946,7 +958,7 @@ __device__ __forceinline__ void store_y(const GemvArgs& a, int64_t i, float v) {
 // records a workgroup), so that calls on one buffer through kernels of either
 // tile size count and tag alike.  elds: TR x 16 squares, then 16 inv, then 8
 // x 16 wave sums (floats).
-template <int BM, int OPL, int TR>
+template <int BM, int OPL, int TR, bool ALL>
 __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[OPL], int b,
                                const bool (&own)[OPL], const bool (&live)[OPL],
                                const float (&o)[OPL], const bool (&ok)[OPL], float* elds,
@@ -976,6 +988,7 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
   const uint32_t mark = epi_mark(*s_epi_k);
   const bool waits = s_ctl[3] != 0;
   const bool reducer = epi_reducer<TR>(a, tile);
+  const bool folds = reducer || (ALL && waits);
   // The group copy of the published inv this workgroup polls: per column one
   // 64-bit word (mark in the high half, the fp32 bits of inv in the low half).
   const unsigned long long* inv_copy = reinterpret_cast<const unsigned long long*>(
@@ -983,7 +996,7 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
   // A tile that leaves its rows to the reducing workgroup has its out at the
   // coherence point in every compute wave before its record goes out.
   if (!waits) wait_vm_all();
-  if (reducer && wave == 0 && lane == 0) s_ctl[2] = 0u;
+  if (folds && wave == 0 && lane == 0) s_ctl[2] = 0u;
   __syncthreads();  // E1b
   if (wave == 0 && lane < a.B) {
     const unsigned long long tag = mark | (waits ? 0u : kEpiLeft);
@@ -999,10 +1012,10 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
   }
   if (!reducer && !waits) return;
 
-  if (reducer) {
+  if (folds) {
     fold_records(a, mark, tile * (TR / kFlagRows), wave, lane, nt, wsum, s_inv, s_ctl,
                  TR > kBigTile);  // contains E3
-    if (wave == 0) {
+    if (reducer && wave == 0) {
       // Every group's copy, one self-validating 64-bit word per column (so no
       // wait has to separate the values from a flag): P = B rounded up to a
       // power of two lanes per copy, consecutive lanes on consecutive words.
@@ -1010,7 +1023,7 @@ __device__ void fused_epilogue(const GemvArgs& a, int64_t tile, const int (&n)[O
       const int c = lane & ((1 << lp) - 1);
       const unsigned long long word =
           ((unsigned long long)mark << 32) | __float_as_uint(s_inv[min(c, a.B - 1)]);
-      if (c < a.B) {
+      if (!ALL && c < a.B) {
         for (int g = lane >> lp; g < kEpiGroups; g += 64 >> lp)
           __hip_atomic_store(reinterpret_cast<unsigned long long*>(
                                  a.ssq + epi_inv_off(a.epi_tiles) + (int64_t)g * kEpiRecordWords) +
@@ -1186,7 +1199,7 @@ __device__ __forceinline__ void valu_stream(float (&acc)[R][B], uint4 (&ring)[D]
 // on 16).  XM: XCD-contiguous tile order (block_tile).
 // LDS: x chunks [b][c], one zero chunk, one sink chunk, then the peer tile.
 template <int B, int G, int R, int NW, int NCH, int D, int XPT, int WPE, bool MASKED, bool TS,
-          bool XM, int DT, bool EPI>
+          bool XM, int DT, int EPI>
 __global__ __launch_bounds__((NW + 1) * 64, WPE) void gemv_ar_valu(GemvArgs args) {
   const GemvArgs a = typed_args<DT>(args);
   constexpr int NT = NW * 64;
@@ -1494,7 +1507,7 @@ __global__ __launch_bounds__(kLongWaves * 64, kLongWaves / 4) void gemv_ar_long(
 // MFMA epilogue: each wave's 16 x 16 partial goes to red[wave][n][b]; after
 // B1 wave w sums rows 4w .. 4w+3 over the waves in wave order (lane l: row
 // 4w + (l >> 4), column l & 15), publishes them and reduces.
-template <int NW, bool TS, bool EPI>
+template <int NW, bool TS, int EPI>
 __device__ __forceinline__ void mfma_finish(const GemvArgs& a, int64_t tile, int wave, int lane,
                                             f32x4_t acc, float* red, const float* pe,
                                             float* elds, uint32_t* s_ctl,
@@ -1531,7 +1544,7 @@ __device__ __forceinline__ void mfma_finish(const GemvArgs& a, int64_t tile, int
 // is finite).  The per-wave 16 x 16 fp32 partials are summed in wave order
 // through LDS.  One more wave runs the signal-pad protocol.
 // LDS: x [16][C + 1] chunks (column C zero); NW 16 x 16 partials; peer tile.
-template <int NW, int D, bool TS, int DT, bool EPI>
+template <int NW, int D, bool TS, int DT, int EPI>
 __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs args) {
   const GemvArgs a = typed_args<DT>(args);
   static_assert(NW * 4 == kBigTile, "each compute wave finishes 4 rows of the tile");
@@ -1627,7 +1640,7 @@ __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma(GemvArgs args) 
 // wave's steps start at a rotation that differs between the workgroups of
 // one XCD so that they do not all read the same lines of x at once.
 // LDS: NW 16 x 16 partials, then the peer tile.
-template <int NW, int D, bool TS, int DT, bool EPI>
+template <int NW, int D, bool TS, int DT, int EPI>
 __global__ __launch_bounds__((NW + 1) * 64, 3) void gemv_ar_mfma_xmem(GemvArgs args) {
   const GemvArgs a = typed_args<DT>(args);
   static_assert(NW * 4 == kBigTile, "each compute wave finishes 4 rows of the tile");
@@ -1796,7 +1809,7 @@ __device__ __forceinline__ int lds_stage_rot(int64_t t) {
   return (int)((t ^ (t >> 3)) & (NS - 1));
 }
 
-template <int DT, bool EPI>
+template <int DT, int EPI>
 __global__ __launch_bounds__((kMfmaLCons + kMfmaLProd) * 64) void gemv_ar_mfma_lds(GemvArgs args) {
   const GemvArgs a = typed_args<DT>(args);
   constexpr int RB = kMfmaLRows / 16;
@@ -2035,7 +2048,7 @@ __global__ __launch_bounds__((kMfmaLCons + kMfmaLProd) * 64) void gemv_ar_mfma_l
       n[i] = (tid + NT * i) / 16;
       own[i] = (tid & 15) < a.B;
     }
-    fused_epilogue<GSA_MAX_B, OPT, TR>(a, tile, n, tid & 15, own, live, outv, okv, red, s_ctl,
+    fused_epilogue<GSA_MAX_B, OPT, TR, false>(a, tile, n, tid & 15, own, live, outv, okv, red, s_ctl,
                                        &s_epi_k, wave, lane, NT);
   }
 }
@@ -2078,7 +2091,7 @@ constexpr int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // exact instance; any other C the masked streaming instance.  XPT covers
 // B * G * NCH chunks of x (at most 8 per thread; the rest of a longer x is
 // staged by a plain loop).
-template <int B, int G, int R, int NW, int NCH, int D, int WPE, bool TS, bool XM, int DT, bool EPI>
+template <int B, int G, int R, int NW, int NCH, int D, int WPE, bool TS, bool XM, int DT, int EPI>
 ValuChoice valu_tier(int C) {
   constexpr int XPT0 = ceil_div(B * G * NCH, NW * 64);
   constexpr int XPT = XPT0 > 8 ? 8 : XPT0;
@@ -2120,28 +2133,32 @@ ValuChoice long_tier(int C) {
 // of rows up to C = 224 go to the XCDs in contiguous runs (block_tile).
 // DT other than fp32 (bf16 slots or out) comes only with small tiles and
 // one-shot: the instances it takes are the ones those calls reach.
-template <int B, bool TS, int DT, bool EPI>
+template <int B, bool TS, int DT, int EPI>
 ValuChoice valu_kernel(int C) {
   static_assert(!(DT != kDtF32 && (TS || EPI)), "element types are for the plain one-shot call");
   static_assert(!(TS && EPI), "no fused epilogue in the two-shot call");
   if constexpr (!EPI) {
     if (!TS && C > 224) return long_tier<B, DT>(C);
-    if (C <= 64) return valu_tier<B, 32, 2, 1, 2, 2, 1, TS, true, DT, false>(C);
+    if (C <= 64) return valu_tier<B, 32, 2, 1, 2, 2, 1, TS, true, DT, kEpiNone>(C);
   } else {
     // The fused epilogue counts 16-row tiles.
-    if (C <= 64) return valu_tier<B, 64, 4, 4, 1, 1, 1, false, true, kDtF32, true>(C);
+    if (C <= 64) return valu_tier<B, 64, 4, 4, 1, 1, 1, false, true, kDtF32, EPI>(C);
   }
-  if (C <= 224) return valu_tier<B, 32, 2, 4, 7, 4, 1, TS, true, DT, EPI>(C);
-  if constexpr (DT != kDtF32)
-    return ValuChoice{nullptr, 0, 0};  // not reached: the plain call takes the long tier
-  else
-    return valu_tier<B, 64, 2, 8, 7, 3, 5, TS, false, kDtF32, EPI>(C);
+  if constexpr (EPI == kEpiFoldAll) {
+    return ValuChoice{nullptr, 0, 0};  // not reached: chosen for rows of at most 64 chunks
+  } else {
+    if (C <= 224) return valu_tier<B, 32, 2, 4, 7, 4, 1, TS, true, DT, EPI>(C);
+    if constexpr (DT != kDtF32)
+      return ValuChoice{nullptr, 0, 0};  // not reached: the plain call takes the long tier
+    else
+      return valu_tier<B, 64, 2, 8, 7, 3, 5, TS, false, kDtF32, EPI>(C);
+  }
 }
 
 // EPI: the kernels of the fused epilogue, instances of their own, so that the
 // plain and two-shot instances carry none of its code (the compiler's
 // schedule of their A stream has moved with changes to it).
-template <bool TS, int DT, bool EPI>
+template <bool TS, int DT, int EPI>
 ValuChoice pick_kernel(int B, int C) {
   switch (B) {
     case 1: return valu_kernel<1, TS, DT, EPI>(C);
@@ -2153,6 +2170,7 @@ ValuChoice pick_kernel(int B, int C) {
     case 7: return valu_kernel<7, TS, DT, EPI>(C);
     case 8: return valu_kernel<8, TS, DT, EPI>(C);
     default:
+      if constexpr (EPI == kEpiFoldAll) return ValuChoice{nullptr, 0, 0};  // B <= 8 only
       // Rows of exactly 256 chunks, one-shot (plain or fused epilogue): A
       // staged through LDS.
       if constexpr (!TS) {
@@ -2184,19 +2202,20 @@ size_t gemv_lds_bytes(int W, int B, int C, bool epi, int tile_rows) {
   return partials + tail;
 }
 
-bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, bool slot_bf16,
-                        bool out_bf16, Launch* out) {
+bool select_gemv_kernel(int W, int B, int C, int64_t tiles16, bool epi, bool two_shot,
+                        bool slot_bf16, bool out_bf16, Launch* out) {
   if (W < 1 || W > GSA_MAX_W || B < 1 || B > GSA_MAX_B || C < 1) return false;
   if (B <= 8 && (size_t)B * C * 16 > GSA_MAX_X_LDS_BYTES) return false;  // x staged in LDS
   if (epi && two_shot) return false;  // separate entry points
   const bool typed = slot_bf16 || out_bf16;
   if (typed && (epi || two_shot)) return false;  // element types: the plain one-shot call only
-  if (epi && two_shot) return false;
-  const ValuChoice k = two_shot                 ? pick_kernel<true, kDtF32, false>(B, C)
-                       : epi                   ? pick_kernel<false, kDtF32, true>(B, C)
-                       : slot_bf16 && out_bf16 ? pick_kernel<false, kDtBf16, false>(B, C)
-                       : typed                 ? pick_kernel<false, kDtMixed, false>(B, C)
-                                               : pick_kernel<false, kDtF32, false>(B, C);
+  const bool fold_all = epi && B <= 8 && C <= 64 && tiles16 * B <= kEpiFoldAllWords;
+  const ValuChoice k = two_shot                 ? pick_kernel<true, kDtF32, kEpiNone>(B, C)
+                       : fold_all              ? pick_kernel<false, kDtF32, kEpiFoldAll>(B, C)
+                       : epi                   ? pick_kernel<false, kDtF32, kEpiFoldOne>(B, C)
+                       : slot_bf16 && out_bf16 ? pick_kernel<false, kDtBf16, kEpiNone>(B, C)
+                       : typed                 ? pick_kernel<false, kDtMixed, kEpiNone>(B, C)
+                                               : pick_kernel<false, kDtF32, kEpiNone>(B, C);
   if (!k.kernel) return false;
   *out = {k.kernel, (unsigned)k.threads,
           k.fixed_lds ? k.lds_bytes : gemv_lds_bytes(W, B, C, epi, k.tile_rows), k.tile_rows};

@@ -317,8 +317,8 @@ int enqueue_call(const uint16_t* A_r, const uint16_t* x, void* slots_any, uint32
     if (gathered && h->gathered != gathered) return GSA_EINVAL;
     // kernel instances with the element types fixed (both fp32 or both
     // bf16), or tested at run time (mixed)
-    if (!gsa::select_gemv_kernel(W, B, C, ep != nullptr, gathered != nullptr, a.slot_bf16 != 0,
-                                 out_dtype == GSA_DTYPE_BF16, &l))
+    if (!gsa::select_gemv_kernel(W, B, C, h->tiles, ep != nullptr, gathered != nullptr,
+                                 a.slot_bf16 != 0, out_dtype == GSA_DTYPE_BF16, &l))
       return GSA_EINVAL;
     a.row_stride = (int)h->row_stride;
     a.tiles = (int)((N + l.tile_rows - 1) / l.tile_rows);

@@ -94,8 +94,9 @@ hipError_t launch_bias_rmsnorm(const float* out, int64_t N, int B, const float* 
                                const float* w, float eps, void* y, bool y_bf16, float* inv_rms,
                                hipStream_t s);
 
-bool select_gemv_kernel(int W, int B, int C, bool epi, bool two_shot, bool slot_bf16,
-                        bool out_bf16, Launch* out);
+// tiles16: the call's 16-row tiles (the epilogue's record count).
+bool select_gemv_kernel(int W, int B, int C, int64_t tiles16, bool epi, bool two_shot,
+                        bool slot_bf16, bool out_bf16, Launch* out);
 // Dynamic LDS bytes a kernel of tile_rows rows per workgroup needs for (W, B, C, epi).
 size_t gemv_lds_bytes(int W, int B, int C, bool epi, int tile_rows);
 

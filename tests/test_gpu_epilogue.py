@@ -134,14 +134,16 @@ def test_edge_epilogue(W, N, Ks, B, rank, bias, weight, eps):
     run_epi_and_check(d, f"W={W} N={N} Ks={Ks} B={B}", bias=bias, weight=weight, eps=eps)
 
 
-def test_repeats_bit_identical_and_mixed_with_plain_calls():
+@pytest.mark.parametrize("cfg", ["c1", "c2"])
+def test_repeats_bit_identical_and_mixed_with_plain_calls(cfg):
     """Three epilogue calls with plain calls in between (which leave the
     epilogue's counts alone): y and inv_rms are right and bit-identical every
-    time.  (On this shape the plain call runs 4-row workgroups and the
+    time.  (On these shapes the plain call runs 4-row workgroups and the
     epilogue call 16-row ones, so their partial sums may round differently:
-    each call's results are checked right after it.)"""
-    _say("[epilogue] repeats")
-    d = gi.make_inputs("c2", seed=4, rank=0)
+    each call's results are checked right after it.)  c1 has 64 records a
+    call, so every waiting workgroup folds them; c2 256, folded by one."""
+    _say(f"[epilogue] repeats {cfg}")
+    d = gi.make_inputs(cfg, seed=4, rank=0)
     er = EpiRun(d, seed=4)
     try:
         ys, invs = [], []
@@ -197,11 +199,12 @@ def test_timeout_poisons_y_then_recovers():
         gsa.gsa_set_wait_timeout_us(100000)
 
 
-def test_graph_replays_match_eager():
+@pytest.mark.parametrize("cfg", ["c1", "c3b4"])
+def test_graph_replays_match_eager(cfg):
     """Calls captured in a HIP graph (no host-held state: the epilogue's
     counts only grow): every replay gives the eager result, bit for bit."""
-    _say("[epilogue] graph replays")
-    d = gi.make_inputs("c3b4", seed=5, rank=0)
+    _say(f"[epilogue] graph replays {cfg}")
+    d = gi.make_inputs(cfg, seed=5, rank=0)
     er = EpiRun(d, seed=5, y_dtype=torch.bfloat16)
     try:
         er.call()

@@ -54,9 +54,10 @@ def _one(d, y_dtype, noalloc):
 
 @pytest.mark.parametrize("y_dtype", [torch.float32, torch.bfloat16])
 def test_noalloc_matches_rmsnorm_entry_point(y_dtype):
-    # two calls in a row, the second smaller: the 70B-class shape, then the
-    # Llama-3-8B o_proj shape
-    for cfg in ("c4", "c2"):
+    # calls in a row, each smaller: the 70B-class shape, the Llama-3-8B
+    # o_proj shape, then the smallest one (whose 64 records every waiting
+    # workgroup folds itself)
+    for cfg in ("c4", "c2", "c1"):
         _say(f"[no-alloc] {cfg} y={y_dtype}")
         d = gi.make_inputs(cfg, seed=9, rank=0)
         got = _one(d, y_dtype, noalloc=True)
