@@ -226,10 +226,12 @@ typedef struct gsa_epilogue {
  * one fixed order as they arrive, so repeated calls are bit-identical, and
  * publishes 1/rms.  A tile that finds every tile of the call started once
  * its own rows are done waits for 1/rms and normalises its own rows
- * (started tiles always finish, so that wait cannot deadlock); the rows of
- * every other tile are normalised by the folding workgroup.  Both give the
- * same bits.  The waits are bounded (the fold's by twice, a tile's wait for
- * 1/rms by four times the timeout of gsa_set_wait_timeout_us); if one
+ * (started tiles always finish, so that wait cannot deadlock); on calls of
+ * at most 64 partial sums (16-row tiles x B) such a tile folds them itself,
+ * in the same order, instead of waiting for 1/rms.  The rows of every other
+ * tile are normalised by the folding workgroup.  All give the same bits.
+ * The waits are bounded (a fold's by twice, a tile's wait for 1/rms by four
+ * times the timeout of gsa_set_wait_timeout_us); if one
  * expires, gsa_signal_pad_status reports GSA_ETIMEOUT with that tile's first
  * flag tile and peer -1.  If any tile of the call failed, y and inv_rms are
  * NaN.
