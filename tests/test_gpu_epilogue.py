@@ -123,6 +123,9 @@ EDGE = [
     (4, 4000, 256, 16, 1, True, True, 1e-5),     # MFMA, 250 tiles: several per fold lane
     (8, 8192 + 16 * 65, 64, 2, 5, True, True, 1e-5),  # 577 tiles, short rows
     (2, 65536, 64, 1, 0, True, True, 1e-5),     # 4096 tiles: more than fit at once
+    # 2048 tiles of 4 columns: more than fit at once, so tiles that finish
+    # early leave their rows to the folding workgroup
+    (2, 2048 * 16 - 5, 512, 4, 1, True, True, 1e-5),
     (2, 16 * 6000 + 5, 64, 3, 1, True, False, 1e-4),  # 6001 tiles, ragged
 ]
 
