@@ -2127,7 +2127,9 @@ ValuChoice long_tier(int C) {
 //            shape 4.05 against 4.49 us per call with 16-row tiles)
 //   C <= 64 : 16 rows, 4 waves, a full wave per row, 4 rows per wave
 //   C <= 224: 16 rows, 4 waves, half a wave per row, 2 x 2 rows per wave
-//   larger  : 16 rows, 8 waves, a full wave per row, 2 rows per wave
+//   larger, plain call: the long-row kernel (32 rows, 16 waves)
+//   larger, epilogue or two-shot: 16 rows, 8 waves, a full wave per row,
+//            2 rows per wave
 // (4-row tiles on the longer rows measured slower: 5.4-5.5 against 5.25 us on
 // the 8B down_proj shape, 14.9 against 12.3 us on the 70B-class one.)  Tiles
 // of rows up to C = 224 go to the XCDs in contiguous runs (block_tile).
