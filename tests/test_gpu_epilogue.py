@@ -119,6 +119,12 @@ EDGE = [
     (2, 1000, 512, 1, 1, True, True, 1e-6),      # ragged N
     (8, 17, 512, 3, 7, True, False, 1e-5),       # 2 tiles, the second with one row
     (1, 1, 8, 1, 0, False, False, 1e-3),         # one row
+    # calls of at most 64 records x columns, where every waiting workgroup
+    # folds the records itself, and the first call past that bound
+    (4, 256, 512, 4, 2, True, True, 1e-5),       # 16 tiles x 4 columns: 64
+    (2, 100, 256, 2, 0, True, False, 1e-5),      # 7 tiles x 2, the last ragged
+    (8, 64 * 16, 512, 1, 3, False, True, 1e-5),  # 64 tiles x 1
+    (8, 65 * 16, 512, 1, 3, True, True, 1e-5),   # 65 tiles: one workgroup folds
     (4, 50, 2048, 9, 3, False, True, 0.0),       # MFMA, ragged, eps = 0
     (4, 4000, 256, 16, 1, True, True, 1e-5),     # MFMA, 250 tiles: several per fold lane
     (8, 8192 + 16 * 65, 64, 2, 5, True, True, 1e-5),  # 577 tiles, short rows
